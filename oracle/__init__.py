@@ -1,0 +1,283 @@
+"""CPU oracle for SageAttention-style quantized attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  The product path (``quantized_attention_quantize_amd``) never imports it and shares
+no code with it.  Arithmetic lives in ``sage_oracle.c`` (plain C loops, fp64 where the method's
+definition calls for it); this module only compiles that file with gcc and marshals numpy arrays
+through ctypes.
+
+Entry points (all inputs are host numpy arrays; bf16 tensors travel as their uint16 bit patterns):
+
+* codecs: ``f32_to_f16``, ``f16_to_f32``, ``f32_to_bf16``, ``f32_to_e4m3``, ``e4m3_to_f32``
+* ``kmean(K)``                      -- per-(b,h,channel) token mean of K, fp64 sum -> fp32
+* ``quant_qk(Q, K, kmean, ...)``    -- per-64-token-block INT8 Q and smoothed K, scales, LSE shift
+* ``prep_v(V, pv)``                 -- fp16 V or per-channel e4m3 V with its scales
+* ``scores(q8, k8, ...)``           -- exact int32 Q8 . K8^T window of one head
+* ``attn_qe(...)``                  -- the quantized emulation (online softmax over BN-key tiles)
+* ``attn_ex(...)``                  -- fp64 exact attention on the unquantized bf16 inputs
+* ``run_qe(...)``                   -- convenience: all the steps above for given rows
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.c")
+_LIB = os.path.join(_HERE, "libsage_oracle.so")
+QBLK = 64
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile sage_oracle.c into libsage_oracle.so with gcc (OpenMP, no fast-math, no FP contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        i32 = ctypes.c_int
+        f32 = ctypes.c_float
+        f64 = ctypes.c_double
+        L.orc_num_threads.restype = i32
+        for name in ("orc_f32_to_f16_n", "orc_f16_to_f32_n", "orc_f32_to_bf16_n", "orc_f32_to_e4m3_n",
+                     "orc_e4m3_to_f32_n"):
+            getattr(L, name).argtypes = [P, P, I]
+            getattr(L, name).restype = None
+        L.orc_kmean.argtypes = [P, I, I, I, I, P]
+        L.orc_quant_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P]
+        L.orc_prep_v_fp16.argtypes = [P, I, I, I, I, P]
+        L.orc_prep_v_fp8.argtypes = [P, I, I, I, I, P, P]
+        L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, P, I, P, P, P]
+        L.orc_attn_ex.argtypes = [P, P, P, P, I, i32, f64, I, I, I, I, I, P, I, P, P]
+        for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
+                     "orc_attn_qe", "orc_attn_ex"):
+            getattr(L, name).restype = None
+        _lib = L
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------------------------------------
+# codecs
+# ---------------------------------------------------------------------------------------------
+def f32_to_f16(x):
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_f16_n(_p(x), _p(y), x.size)
+    return y
+
+
+def f16_to_f32(x):
+    x = _c(x, np.uint16)
+    y = np.empty(x.shape, np.float32)
+    lib().orc_f16_to_f32_n(_p(x), _p(y), x.size)
+    return y
+
+
+def f32_to_bf16(x):
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16_n(_p(x), _p(y), x.size)
+    return y
+
+
+def bf16_to_f32(x):
+    """bf16 bits -> fp32: the bf16 pattern is the upper half of the binary32 pattern."""
+    x = _c(x, np.uint16)
+    return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_e4m3(x):
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint8)
+    lib().orc_f32_to_e4m3_n(_p(x), _p(y), x.size)
+    return y
+
+
+def e4m3_to_f32(x):
+    x = _c(x, np.uint8)
+    y = np.empty(x.shape, np.float32)
+    lib().orc_e4m3_to_f32_n(_p(x), _p(y), x.size)
+    return y
+
+
+# ---------------------------------------------------------------------------------------------
+# the method's steps
+# ---------------------------------------------------------------------------------------------
+def pad_n(n: int) -> int:
+    """Padded token extent used for the int8 / prepared-V buffers: a multiple of 128."""
+    return (n + 127) // 128 * 128
+
+
+def kmean(K):
+    """K: uint16 bf16 bits [B,H,Nk,d] -> fp32 [B,H,d]."""
+    K = _c(K, np.uint16)
+    B, H, Nk, d = K.shape
+    out = np.empty((B, H, d), np.float32)
+    lib().orc_kmean(_p(K), B, H, Nk, d, _p(out))
+    return out
+
+
+@dataclass
+class QuantQK:
+    q8: np.ndarray  # int8 [B,H,Nq_pad,d]
+    k8: np.ndarray  # int8 [B,H,Nk_pad,d]
+    qs: np.ndarray  # fp32 [B,H,ceil(Nq/64)]
+    ks: np.ndarray  # fp32 [B,H,ceil(Nk/64)]
+    kmean: np.ndarray  # fp32 [B,H,d]
+    corr: np.ndarray  # fp32 [B,H,Nq]
+
+
+def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None) -> QuantQK:
+    Q = _c(Q, np.uint16)
+    K = _c(K, np.uint16)
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    if km is None:
+        km = kmean(K)
+    km = _c(km, np.float32)
+    Nq_pad = pad_n(Nq) if Nq_pad is None else Nq_pad
+    Nk_pad = pad_n(Nk) if Nk_pad is None else Nk_pad
+    q8 = np.empty((B, H, Nq_pad, d), np.int8)
+    k8 = np.empty((B, H, Nk_pad, d), np.int8)
+    qs = np.empty((B, H, (Nq + QBLK - 1) // QBLK), np.float32)
+    ks = np.empty((B, H, (Nk + QBLK - 1) // QBLK), np.float32)
+    corr = np.empty((B, H, Nq), np.float32)
+    lib().orc_quant_qk(_p(Q), _p(K), _p(km), B, H, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
+                       _p(corr))
+    return QuantQK(q8, k8, qs, ks, km, corr)
+
+
+def prep_v(V, pv: str = "fp16"):
+    """Returns (vhat, vs): fp16 bits uint16 [B,H,Nk,d] and None, or e4m3 uint8 [B,H,Nk,d] and fp32 [B,H,d]."""
+    V = _c(V, np.uint16)
+    B, H, Nk, d = V.shape
+    if pv == "fp16":
+        out = np.empty(V.shape, np.uint16)
+        lib().orc_prep_v_fp16(_p(V), B, H, Nk, d, _p(out))
+        return out, None
+    if pv == "fp8":
+        out = np.empty(V.shape, np.uint8)
+        vs = np.empty((B, H, d), np.float32)
+        lib().orc_prep_v_fp8(_p(V), B, H, Nk, d, _p(out), _p(vs))
+        return out, vs
+    raise ValueError(pv)
+
+
+def scores(q8, k8, b, h, row0, nrows, col0, ncols):
+    """Exact int32 scores for rows [row0,row0+nrows) x keys [col0,col0+ncols) of head (b,h)."""
+    d = q8.shape[3]
+    qh = np.ascontiguousarray(q8[b, h])
+    kh = np.ascontiguousarray(k8[b, h])
+    assert row0 + nrows <= qh.shape[0] and col0 + ncols <= kh.shape[0]
+    out = np.empty((nrows, ncols), np.int32)
+    lib().orc_scores(_p(qh), _p(kh), d, row0, nrows, col0, ncols, _p(out))
+    return out
+
+
+def default_sm_scale(d: int) -> float:
+    """sm_scale default 1/sqrt(head_dim), rounded to fp32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _mask_arg(mask, B, H, Nq, Nk):
+    if mask is None:
+        return None, 0
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert m.ndim == 4 and m.shape[0] == B and m.shape[2] == Nq and m.shape[3] == Nk and m.shape[1] in (1, H)
+    return m, m.shape[1]
+
+
+def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_scale=None, BN=64, rows=None):
+    """Quantized emulation.  Returns (o32 [R,d] fp32, obf [R,d] bf16 bits, lse [R] fp32)."""
+    B, H, Nq_pad, d = qk.q8.shape
+    Nk_pad = qk.k8.shape[2]
+    sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
+    m, mh = _mask_arg(mask, B, H, Nq, Nk)
+    if rows is None:
+        R = B * H * Nq
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rows.size
+        rp = rows
+    o32 = np.empty((R, d), np.float32)
+    obf = np.empty((R, d), np.uint16)
+    lse = np.empty((R,), np.float32)
+    lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
+                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mh, 1 if causal else 0, sm, B, H, Nq, Nk, d, Nq_pad,
+                      Nk_pad, BN, _p(rp), R, _p(o32), _p(obf), _p(lse))
+    return o32, obf, lse
+
+
+def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
+    """fp64 exact attention on the bf16 inputs.  Returns (out [R,d] fp64, lse [R] fp64)."""
+    Q = _c(Q, np.uint16)
+    K = _c(K, np.uint16)
+    V = _c(V, np.uint16)
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
+    m, mh = _mask_arg(mask, B, H, Nq, Nk)
+    if rows is None:
+        R = B * H * Nq
+        rp = None
+    else:
+        rp = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rp.size
+    out = np.empty((R, d), np.float64)
+    lse = np.empty((R,), np.float64)
+    lib().orc_attn_ex(_p(Q), _p(K), _p(V), _p(m), mh, 1 if causal else 0, sm, B, H, Nq, Nk, d, _p(rp), R,
+                      _p(out), _p(lse))
+    return out, lse
+
+
+@dataclass
+class QEResult:
+    qk: QuantQK
+    vhat: np.ndarray
+    vs: np.ndarray | None
+    o32: np.ndarray
+    obf: np.ndarray
+    lse: np.ndarray
+
+
+def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, rows=None) -> QEResult:
+    """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe."""
+    qk = quant_qk(Q, K)
+    vhat, vs = prep_v(V, pv)
+    Nq, Nk = Q.shape[2], K.shape[2]
+    o32, obf, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, rows=rows)
+    return QEResult(qk, vhat, vs, o32, obf, lse)

@@ -1,0 +1,459 @@
+/*
+ * sage_oracle.c -- plain, slow CPU oracle for SageAttention-style quantized attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this file:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header, table or constant generator with the HIP library; it is written from the
+ * method's description and from the number-format definitions, one step at a time.
+ *
+ * What it follows (page title, section):
+ *  - "SageAttention docs digest (context7 llms.txt)", section "sageattn_qk_int8_pv_fp16_triton --
+ *    Triton INT8/FP16 kernel (Ampere/Ada)": per-block INT8 quantization of Q and K, key smoothing
+ *    (smooth_k), boolean mask, FP16 PV.
+ *  - same page, section "SageAttention CUDA INT8/FP16 Kernel (Ampere sm80)": pv_accum_dtype="fp32"
+ *    (FP16 products, FP32 accumulation), return_lse.
+ *  - same page, section "sageattn_qk_int8_pv_fp8_cuda": INT8 Q/K with per-channel FP8 V.
+ *  - same page, section "sageattn3_blackwell" usage: smoothing by the *global* mean of K over tokens.
+ *  - same page, section "sageattn -- Auto-selecting attention kernel": sm_scale default, LSE shape.
+ *  - "flashinfer.nvfp4_attention_sm120_fwd" (FlashInfer API doc), parameters sm_scale
+ *    (default 1/sqrt(head_dim)), unpadded_k_len (keys at or beyond the logical length are masked
+ *    before the softmax), out / lse buffers.
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *  - quantization block = 64 tokens for Q and K; symmetric scale = absmax/127, codes in [-127,127];
+ *    an all-zero block has scale 0 and codes 0;
+ *  - every rounding is round-to-nearest-even (int8 codes, fp16, e4m3, bf16 output);
+ *  - the K mean is summed in fp64 over all Nk tokens (mask and causality ignored), divided by Nk
+ *    in fp64 and rounded once to fp32;
+ *  - P for FP8 PV is quantized as e4m3(448 * p) with saturation, V per channel as
+ *    e4m3(V * 448 / max_t |V|);
+ *  - the softmax denominator l sums the unquantized fp32 p;
+ *  - the online softmax runs over key tiles of BN keys in increasing key order with an exact
+ *    running maximum;
+ *  - a row with no valid key gives O = 0 and LSE = -inf;
+ *  - LSE is natural-log and adds back the smoothing shift sm_scale * (q_i . kmean), so it is the
+ *    LSE of the unsmoothed scores.
+ *
+ * Index arithmetic is 64-bit throughout.  Compile without -ffast-math and with -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_QBLK 64 /* tokens per quantization block */
+
+/* ------------------------------------------------------------------------------------------ */
+/* Number formats, written from their definitions.                                            */
+/* ------------------------------------------------------------------------------------------ */
+
+/* bfloat16 is the upper half of an IEEE binary32 pattern. */
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; subnormal unit 2^-24. */
+float orc_f16_to_f32(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -24);
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return (float)(s ? -v : v);
+}
+
+/* fp32 -> binary16, round to nearest, ties to even; overflow to infinity. */
+uint16_t orc_f32_to_f16(float x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return sign | 0x7e00;
+  if (isinf(x)) return sign | 0x7c00;
+  double a = fabs((double)x);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int E = e - 1; /* a in [2^E, 2^(E+1)) */
+  if (E < -14) {
+    /* subnormal range: count units of 2^-24; a result of 1024 is the smallest normal */
+    double r = nearbyint(ldexp(a, 24));
+    return sign | (uint16_t)r;
+  }
+  double r = nearbyint(ldexp(a, 10 - E)); /* 11 significant bits, in [1024, 2048] */
+  if (r == 2048.0) {
+    r = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return sign | 0x7c00;
+  return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(r - 1024.0);
+}
+
+/* fp32 -> bfloat16 (8 significant bits, binary32 exponent range), round to nearest even. */
+uint16_t orc_f32_to_bf16(float x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return sign | 0x7fc0;
+  if (isinf(x)) return sign | 0x7f80;
+  double a = fabs((double)x);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < -126) {
+    double r = nearbyint(ldexp(a, 133)); /* subnormal unit 2^-133; 128 = smallest normal */
+    return sign | (uint16_t)r;
+  }
+  double r = nearbyint(ldexp(a, 7 - E)); /* in [128, 256] */
+  if (r == 256.0) {
+    r = 128.0;
+    E += 1;
+  }
+  if (E > 127) return sign | 0x7f80;
+  return sign | (uint16_t)((E + 127) << 7) | (uint16_t)(r - 128.0);
+}
+
+/* OCP 8-bit floating point, E4M3 ("fn" flavour): bias 7, no infinities, S.1111.111 = NaN,
+ * largest finite 448 = 1.75 * 2^8, subnormal unit 2^-9. */
+float orc_e4m3_to_f32(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (float)(s ? -v : v);
+}
+
+/* fp32 -> E4M3, round to nearest even, saturating: finite magnitudes that would round past 448
+ * (and infinities) give +-448; NaN gives NaN. */
+uint8_t orc_f32_to_e4m3(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return sign | 0x7f;
+  if (isinf(x)) return sign | 0x7e;
+  double a = fabs((double)x);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < -6) {
+    double r = nearbyint(ldexp(a, 9)); /* units of 2^-9; 8 = smallest normal 2^-6 */
+    return sign | (uint8_t)r;
+  }
+  double r = nearbyint(ldexp(a, 3 - E)); /* 4 significant bits, in [8, 16] */
+  if (r == 16.0) {
+    r = 8.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && r > 14.0)) return sign | 0x7e;
+  return sign | (uint8_t)(((E + 7) << 3) | ((int)r - 8));
+}
+
+/* Vector forms for the codec tests. */
+void orc_f32_to_f16_n(const float* x, uint16_t* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_f16(x[i]);
+}
+void orc_f16_to_f32_n(const uint16_t* x, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f16_to_f32(x[i]);
+}
+void orc_f32_to_bf16_n(const float* x, uint16_t* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_bf16(x[i]);
+}
+void orc_f32_to_e4m3_n(const float* x, uint8_t* y, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_e4m3(x[i]);
+}
+void orc_e4m3_to_f32_n(const uint8_t* x, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_e4m3_to_f32(x[i]);
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Step 1: K mean over tokens (smooth_k).                                                     */
+/* K is bf16 [B][H][Nk][d]; kmean is fp32 [B][H][d].                                          */
+/* ------------------------------------------------------------------------------------------ */
+void orc_kmean(const uint16_t* K, int64_t B, int64_t H, int64_t Nk, int64_t d, float* kmean) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    for (int64_t c = 0; c < d; ++c) {
+      double s = 0.0;
+      for (int64_t t = 0; t < Nk; ++t) s += (double)orc_bf16_to_f32(K[(bh * Nk + t) * d + c]);
+      kmean[bh * d + c] = (float)(s / (double)Nk);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Step 2: per-block symmetric INT8 quantization of an fp32 matrix X [N][d] (one head).       */
+/* Block u covers rows [64u, min(64u+64, N)) and all d channels.                              */
+/* x8 gets N_pad rows (rows >= N are zero); scale gets ceil(N/64) entries.                    */
+/* ------------------------------------------------------------------------------------------ */
+static void quantize_blocks(const float* X, int64_t N, int64_t N_pad, int64_t d, int8_t* x8, float* scale) {
+  int64_t nblk = (N + ORC_QBLK - 1) / ORC_QBLK;
+  for (int64_t u = 0; u < nblk; ++u) {
+    int64_t r0 = u * ORC_QBLK, r1 = r0 + ORC_QBLK < N ? r0 + ORC_QBLK : N;
+    float amax = 0.0f;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = 0; c < d; ++c) {
+        float a = fabsf(X[r * d + c]);
+        if (a > amax) amax = a;
+      }
+    float sc = 0.0f, inv = 0.0f;
+    if (amax > 0.0f) {
+      sc = amax / 127.0f; /* IEEE binary32 division */
+      inv = 127.0f / amax;
+    }
+    scale[u] = sc;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = 0; c < d; ++c) {
+        float y = X[r * d + c] * inv; /* one binary32 rounding */
+        float q = nearbyintf(y);      /* ties to even */
+        if (q > 127.0f) q = 127.0f;
+        if (q < -127.0f) q = -127.0f;
+        x8[r * d + c] = (int8_t)q;
+      }
+  }
+  memset(x8 + N * d, 0, (size_t)((N_pad - N) * d));
+}
+
+/* Q, K bf16 [B][H][N][d]; kmean fp32 [B][H][d] (from orc_kmean).
+ * Outputs: q8 [B][H][Nq_pad][d], k8 [B][H][Nk_pad][d], qs [B][H][ceil(Nq/64)],
+ *          ks [B][H][ceil(Nk/64)], corr [B][H][Nq] = fp32(sum_c fp64(Q_ic) * fp64(kmean_c)).
+ * K is smoothed as fp32(K - kmean) (one rounding) before quantizing. */
+void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int64_t B, int64_t H, int64_t Nq,
+                  int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8, int8_t* k8, float* qs,
+                  float* ks, float* corr) {
+  int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    float* xq = (float*)malloc((size_t)(Nq * d) * sizeof(float));
+    float* xk = (float*)malloc((size_t)(Nk * d) * sizeof(float));
+    const float* km = kmean + bh * d;
+    for (int64_t i = 0; i < Nq * d; ++i) xq[i] = orc_bf16_to_f32(Q[bh * Nq * d + i]);
+    for (int64_t t = 0; t < Nk; ++t)
+      for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_bf16_to_f32(K[(bh * Nk + t) * d + c]) - km[c];
+    quantize_blocks(xq, Nq, Nq_pad, d, q8 + bh * Nq_pad * d, qs + bh * nbq);
+    quantize_blocks(xk, Nk, Nk_pad, d, k8 + bh * Nk_pad * d, ks + bh * nbk);
+    for (int64_t i = 0; i < Nq; ++i) {
+      double s = 0.0;
+      for (int64_t c = 0; c < d; ++c) s += (double)xq[i * d + c] * (double)km[c];
+      corr[bh * Nq + i] = (float)s;
+    }
+    free(xq);
+    free(xk);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Step 3: V preparation.  Output keeps V's own layout [B][H][Nk][d].                         */
+/* fp16: vhat = fp16_rne(V).                                                                  */
+/* fp8:  vmax_c = max_t |V_tc|; vs_c = fp32(vmax_c / 448); vinv_c = fp32(448 / vmax_c)        */
+/*       (0 when vmax_c = 0); vhat = e4m3_rne_sat(fp32(V * vinv_c)).                          */
+/* ------------------------------------------------------------------------------------------ */
+void orc_prep_v_fp16(const uint16_t* V, int64_t B, int64_t H, int64_t Nk, int64_t d, uint16_t* vhat) {
+  int64_t n = B * H * Nk * d;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) vhat[i] = orc_f32_to_f16(orc_bf16_to_f32(V[i]));
+}
+
+void orc_prep_v_fp8(const uint16_t* V, int64_t B, int64_t H, int64_t Nk, int64_t d, uint8_t* vhat, float* vs) {
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    for (int64_t c = 0; c < d; ++c) {
+      float vmax = 0.0f;
+      for (int64_t t = 0; t < Nk; ++t) {
+        float a = fabsf(orc_bf16_to_f32(V[(bh * Nk + t) * d + c]));
+        if (a > vmax) vmax = a;
+      }
+      float sc = 0.0f, inv = 0.0f;
+      if (vmax > 0.0f) {
+        sc = vmax / 448.0f;
+        inv = 448.0f / vmax;
+      }
+      vs[bh * d + c] = sc;
+      for (int64_t t = 0; t < Nk; ++t) {
+        int64_t idx = (bh * Nk + t) * d + c;
+        vhat[idx] = orc_f32_to_e4m3(orc_bf16_to_f32(V[idx]) * inv);
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Step 4: exact int32 scores acc_ij = sum_c q8_ic * k8_jc for a window of one head.          */
+/* q8h = q8 + bh*Nq_pad*d, k8h = k8 + bh*Nk_pad*d; out is [nrows][ncols].                     */
+/* ------------------------------------------------------------------------------------------ */
+void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, int64_t nrows, int64_t col0,
+                int64_t ncols, int32_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int8_t* q = q8h + (row0 + r) * d;
+    for (int64_t j = 0; j < ncols; ++j) {
+      const int8_t* k = k8h + (col0 + j) * d;
+      int32_t acc = 0;
+      for (int64_t c = 0; c < d; ++c) acc += (int32_t)q[c] * (int32_t)k[c];
+      out[r * ncols + j] = acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Step 5: quantized attention forward (the emulation the GPU path must reproduce).           */
+/*                                                                                            */
+/* rows: flattened row ids (b*H + h)*Nq + i to evaluate; NULL = all B*H*Nq rows in order.     */
+/* mask: uint8 [B][mask_h][Nq][Nk], nonzero = attend; mask_h is 1 (broadcast over heads) or H; */
+/*       mask == NULL means no mask.                                                          */
+/* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
+/* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
+/* Outputs per requested row: o32 [nrows][d] (fp32 O before the bf16 rounding, may be NULL),  */
+/* obf [nrows][d] (bf16 bits), lse [nrows] (natural log, fp32).                               */
+/* ------------------------------------------------------------------------------------------ */
+void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
+                 const void* vhat, const float* vs, int pv_fp8, const uint8_t* mask, int64_t mask_h, int causal,
+                 float sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
+                 int64_t Nk_pad, int64_t BN, const int64_t* rows, int64_t nrows, float* o32, uint16_t* obf,
+                 float* lse) {
+  int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
+  if (rows == NULL) nrows = B * H * Nq;
+#pragma omp parallel
+  {
+    float* o = (float*)malloc((size_t)d * sizeof(float));
+    float* s = (float*)malloc((size_t)BN * sizeof(float));
+    float* pq = (float*)malloc((size_t)BN * sizeof(float));
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int64_t rid = rows ? rows[r] : r;
+      int64_t bh = rid / Nq, i = rid % Nq, b = bh / H, h = bh % H;
+      const int8_t* q = q8 + (bh * Nq_pad + i) * d;
+      const int8_t* kh = k8 + bh * Nk_pad * d;
+      const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
+      float qscale = qs[bh * nbq + i / ORC_QBLK];
+      float m = -INFINITY, l = 0.0f;
+      for (int64_t c = 0; c < d; ++c) o[c] = 0.0f;
+      for (int64_t j0 = 0; j0 < Nk; j0 += BN) {
+        int64_t j1 = j0 + BN < Nk ? j0 + BN : Nk;
+        /* scores of this key tile */
+        float tmax = -INFINITY;
+        for (int64_t j = j0; j < j1; ++j) {
+          int valid = 1;
+          if (causal && j > i) valid = 0;
+          if (mrow && mrow[j] == 0) valid = 0;
+          if (!valid) {
+            s[j - j0] = -INFINITY;
+            continue;
+          }
+          const int8_t* k = kh + j * d;
+          int32_t acc = 0;
+          for (int64_t c = 0; c < d; ++c) acc += (int32_t)q[c] * (int32_t)k[c];
+          float cst = (qscale * ks[bh * nbk + j / ORC_QBLK]) * sm_scale;
+          s[j - j0] = (float)acc * cst;
+          if (s[j - j0] > tmax) tmax = s[j - j0];
+        }
+        float mnew = m > tmax ? m : tmax;
+        if (mnew == -INFINITY) continue; /* nothing valid so far */
+        float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mnew));
+        float psum = 0.0f;
+        for (int64_t j = j0; j < j1; ++j) {
+          float p = (s[j - j0] == -INFINITY) ? 0.0f : (float)exp((double)(s[j - j0] - mnew));
+          psum += p;
+          if (pv_fp8)
+            pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(448.0f * p));
+          else
+            pq[j - j0] = orc_f16_to_f32(orc_f32_to_f16(p));
+        }
+        l = alpha * l + psum;
+        for (int64_t c = 0; c < d; ++c) {
+          float acc = alpha * o[c];
+          for (int64_t j = j0; j < j1; ++j) {
+            int64_t vidx = (bh * Nk + j) * d + c;
+            float v = pv_fp8 ? orc_e4m3_to_f32(((const uint8_t*)vhat)[vidx])
+                             : orc_f16_to_f32(((const uint16_t*)vhat)[vidx]);
+            acc += pq[j - j0] * v;
+          }
+          o[c] = acc;
+        }
+        m = mnew;
+      }
+      for (int64_t c = 0; c < d; ++c) {
+        float out;
+        if (l == 0.0f)
+          out = 0.0f;
+        else if (pv_fp8)
+          out = (float)((double)o[c] * (double)vs[bh * d + c] / (448.0 * (double)l));
+        else
+          out = o[c] / l;
+        if (o32) o32[r * d + c] = out;
+        if (obf) obf[r * d + c] = orc_f32_to_bf16(out);
+      }
+      if (lse) {
+        if (l == 0.0f)
+          lse[r] = -INFINITY;
+        else
+          lse[r] = (float)((double)m + log((double)l) + (double)sm_scale * (double)corr[bh * Nq + i]);
+      }
+    }
+    free(o);
+    free(s);
+    free(pq);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Exact attention in fp64 on the original bf16 inputs: no smoothing, no quantization.        */
+/* s_ij = sm_scale * sum_c Q_ic K_jc; invalid entries -inf; two-pass softmax; O = P V;        */
+/* LSE_i = log sum_j exp(s_ij).  A row with no valid key gives O = 0, LSE = -inf.             */
+/* ------------------------------------------------------------------------------------------ */
+void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint8_t* mask, int64_t mask_h,
+                 int causal, double sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 const int64_t* rows, int64_t nrows, double* out, double* lse) {
+  if (rows == NULL) nrows = B * H * Nq;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc((size_t)Nk * sizeof(double));
+    double* q = (double*)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int64_t rid = rows ? rows[r] : r;
+      int64_t bh = rid / Nq, i = rid % Nq, b = bh / H, h = bh % H;
+      const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
+      for (int64_t c = 0; c < d; ++c) q[c] = (double)orc_bf16_to_f32(Q[(bh * Nq + i) * d + c]);
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < Nk; ++j) {
+        if ((causal && j > i) || (mrow && mrow[j] == 0)) {
+          s[j] = -INFINITY;
+          continue;
+        }
+        double acc = 0.0;
+        for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_bf16_to_f32(K[(bh * Nk + j) * d + c]);
+        s[j] = sm_scale * acc;
+        if (s[j] > mx) mx = s[j];
+      }
+      double* o = out + r * d;
+      for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+      if (mx == -INFINITY) {
+        if (lse) lse[r] = -INFINITY;
+        continue;
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j < Nk; ++j) {
+        if (s[j] == -INFINITY) continue;
+        double p = exp(s[j] - mx);
+        den += p;
+        for (int64_t c = 0; c < d; ++c) o[c] += p * (double)orc_bf16_to_f32(V[(bh * Nk + j) * d + c]);
+      }
+      for (int64_t c = 0; c < d; ++c) o[c] /= den;
+      if (lse) lse[r] = mx + log(den);
+    }
+    free(s);
+    free(q);
+  }
+}

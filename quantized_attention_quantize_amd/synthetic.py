@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs for the quantized-attention workloads.
+
+This module holds the workload shapes and the random-input recipe and nothing of the method's
+arithmetic; both the HIP path's tests/benchmark and the CPU oracle consume what it produces.
+
+The recipe follows the examples on the SageAttention docs digest (context7 llms.txt), sections
+"SageAttention Triton INT8/FP16 Kernel Examples" and "sageattn -- Auto-selecting attention kernel":
+plain ``torch.randn`` bf16 tensors in HND layout, and a boolean mask that keeps the first half of
+the keys.  Keys additionally carry a per-(batch, head, channel) bias of standard deviation sigma, the
+channel-wise offset that key smoothing exists to remove.
+
+Draw order (fp32, one CPU generator seeded with ``seed``):
+    Q  = randn(B, H, Nq, d)
+    Kn = randn(B, H, Nk, d)
+    Kb = sigma * randn(B, H, 1, d)
+    V  = randn(B, H, Nk, d)
+then K = bf16(Kn + Kb), Q = bf16(Q), V = bf16(V).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    sigma: float
+    causal: bool = False
+    mask: str | None = None  # None or "half_keys" ([B,1,Nq,Nk] bool, True for keys < Nk/2)
+    pv: str = "fp16"  # "fp16" or "fp8"
+    lse: bool = True
+    note: str = field(default="", compare=False)
+
+    @property
+    def ops(self) -> float:
+        """Throughput numerator 4*B*H*Nq*Nk*d, halved for causal."""
+        o = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return o / 2 if self.causal else o
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 256, 256, 64, 4.0, pv="fp16",
+                     note="B=1 H=2 N=256 d=64, INT8 QK (64-token blocks) + FP16 PV, seed 0"),
+    "n8k": Workload("n8k", 2, 32, 8192, 8192, 128, 4.0, pv="fp16",
+                    note="B=2 H=32 N=8192 d=128 bf16, non-causal, INT8 QK + FP16 PV, bf16 out + fp32 LSE"),
+    "n8k_causal": Workload("n8k_causal", 2, 32, 8192, 8192, 128, 4.0, causal=True, pv="fp16",
+                           note="B=2 H=32 N=8192 d=128 bf16, causal, INT8 QK + FP16 PV"),
+    "n8k_mask": Workload("n8k_mask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys", pv="fp16",
+                         note="B=2 H=32 N=8192 d=128 bf16, bool mask [B,1,N,N] keeping keys < N/2, LSE"),
+    "n17776_fp8": Workload("n17776_fp8", 1, 24, 17776, 17776, 128, 8.0, pv="fp8",
+                           note="B=1 H=24 N=17776 d=128 bf16, non-causal, INT8 QK + FP8 e4m3 PV"),
+}
+
+
+@dataclass
+class Inputs:
+    q: torch.Tensor  # bf16 [B,H,Nq,d] (CPU)
+    k: torch.Tensor
+    v: torch.Tensor
+    mask: torch.Tensor | None  # bool [B,1,Nq,Nk] (CPU) or None
+
+    def bits(self, t: torch.Tensor) -> np.ndarray:
+        """bf16 tensor -> numpy uint16 bit patterns (what the oracle consumes)."""
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    @property
+    def mask_u8(self):
+        return None if self.mask is None else self.mask.numpy().astype(np.uint8)
+
+
+def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None) -> Inputs:
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, Nq, d, generator=g, dtype=torch.float32)
+    kn = torch.randn(B, H, Nk, d, generator=g, dtype=torch.float32)
+    kb = sigma * torch.randn(B, H, 1, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, Nk, d, generator=g, dtype=torch.float32)
+    k = (kn + kb).to(torch.bfloat16)
+    del kn
+    m = None
+    if mask == "half_keys":
+        m = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+        m[:, :, :, Nk // 2:] = False
+    elif mask is not None:
+        raise ValueError(mask)
+    return Inputs(q.to(torch.bfloat16), k, v.to(torch.bfloat16), m)
+
+
+def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
+    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.sigma, seed, w.mask)
+
+
+def random_mask(B, Hm, Nq, Nk, p_keep=0.7, seed=1) -> torch.Tensor:
+    """Element-wise random boolean mask (True = attend) for edge-case tests."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.rand(B, Hm, Nq, Nk, generator=g) < p_keep
