@@ -1,0 +1,180 @@
+/*
+ * sage_mi355x.h -- C ABI of libsage_mi355x: SageAttention-style quantized attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (SageAttention docs digest, context7 llms.txt; sections
+ * "sageattn_qk_int8_pv_fp16_triton -- Triton INT8/FP16 kernel (Ampere/Ada)",
+ * "SageAttention CUDA INT8/FP16 Kernel (Ampere sm80)", "sageattn_qk_int8_pv_fp8_cuda"):
+ *   O = softmax(Q K^T * sm_scale [masked]) V, where
+ *   - K is smoothed by subtracting its per-channel mean over tokens (exact under softmax);
+ *   - Q and the smoothed K are quantized to INT8 with one scale per 64-token block;
+ *   - Q K^T runs as an INT8 product with int32 accumulation and is then dequantized;
+ *   - the softmax is computed online over 64-key tiles;
+ *   - P V runs in FP16 (P and V rounded to fp16) or in FP8 e4m3 (V per channel, P with the static
+ *     scale 448), accumulated in FP32.
+ * The split into a quantize call and an attention call on pre-quantized tensors, and the
+ * caller-supplied out / lse buffers, follow the FlashInfer API doc
+ * "flashinfer.nvfp4_attention_sm120_fwd" (parameters out, lse, sm_scale, unpadded_k_len).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device; the caller allocates and
+ *    owns every buffer, including workspaces.  The library never allocates, frees or synchronizes
+ *    and keeps no mutable global state (one cached per-device architecture check aside).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is enqueued on it
+ *    and the call returns without waiting; asynchronous faults surface at the caller's next sync.
+ *  - Host-side argument validation runs before any HIP call and before any launch; a non-OK status
+ *    means nothing was enqueued.  Launch failures report SAGE_ERR_HIP.
+ *  - Inputs are bf16 with a contiguous channel (head_dim) axis; batch, head and token strides are
+ *    free (HND or NHD), given in elements, and must keep every row 16-byte aligned.
+ *  - head_dim d must be 64 or 128.  Index arithmetic is 64-bit.
+ */
+#ifndef SAGE_MI355X_H
+#define SAGE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride, alignment or dtype mismatch */
+  SAGE_ERR_UNSUPPORTED = 2,      /* head_dim not 64/128, fp16 input, or a device other than gfx950 */
+  SAGE_ERR_WORKSPACE = 3,        /* workspace smaller than the matching *_workspace_bytes() value */
+  SAGE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} sage_status;
+
+typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1 /* reserved: not supported yet */ } sage_dtype;
+
+typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_dtype;
+
+/* A Q, K or V tensor of shape [B, H, N, d] addressed as
+ *   data + b*stride_b + h*stride_h + n*stride_n + c      (element offsets, c contiguous). */
+typedef struct {
+  const void* data;
+  sage_dtype dtype;
+  int64_t B, H, N, d;
+  int64_t stride_b, stride_h, stride_n;
+} sage_qkv_desc;
+
+/* Quantized Q/K produced by sage_quantize_qk (all device buffers, caller-owned, contiguous):
+ *   q8       int8  [B][H][Nq_pad][d]   rows >= Nq are zero
+ *   k8       int8  [B][H][Nk_pad][d]   smoothed K codes; rows >= Nk are zero
+ *   q_scale  fp32  [B][H][ceil(Nq/64)] per-64-token-block scale  (amax/127; 0 for an all-zero block)
+ *   k_scale  fp32  [B][H][ceil(Nk/64)]
+ *   k_mean   fp32  [B][H][d]           per-channel token mean of K (fp64 sum, rounded once)
+ *   lse_corr fp32  [B][H][Nq]          sum_c Q[i,c]*k_mean[c]: adds the smoothing shift back to the LSE
+ * Nq_pad and Nk_pad must equal sage_pad_tokens(Nq) and sage_pad_tokens(Nk). */
+typedef struct {
+  int8_t* q8;
+  int8_t* k8;
+  float* q_scale;
+  float* k_scale;
+  float* k_mean;
+  float* lse_corr;
+  int64_t B, H, Nq, Nk, d, Nq_pad, Nk_pad;
+} sage_qk_quant;
+
+/* Padded token extent of q8 / k8 / prepared V: n rounded up to a multiple of 128. Host only. */
+int64_t sage_pad_tokens(int64_t n);
+
+/* Keys per online-softmax tile used by sage_attn_fwd (the running maximum is updated once per
+ * tile, which fixes where P is rounded).  Host only. */
+int sage_block_n(sage_pv_dtype pv);
+
+/* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean).  Host only. */
+size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d);
+
+/* Step 1 (quantize).  Reads q and k (bf16, same B, H, d), writes every buffer of *out.
+ * Per (b,h): k_mean = fp32(sum_t fp64(K[t,:]) / Nk); Ks = fp32(K - k_mean); for every 64-token
+ * block of Q and of Ks: scale = amax/127, code = clamp(rne(x * (127/amax)), -127, 127)
+ * (IEEE fp32 divisions, round-to-nearest-even); lse_corr[i] = fp32(sum_c fp64(Q[i,c])*fp64(k_mean[c])).
+ * Sources: per-block INT8 Q/K and smooth_k on the Triton INT8/FP16 kernel section; smoothing by
+ * the global token mean on the sageattn3_blackwell usage section (per_block_mean=False).
+ * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, mismatched B/H/d, wrong pads or
+ * misaligned rows; UNSUPPORTED for d not in {64,128} or non-bf16 input; WORKSPACE if
+ * workspace_bytes < sage_quantize_workspace_bytes(). */
+sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sage_prepare_v needs (fp8: per-chunk partial maxima of |V|; fp16: 0). Host only. */
+size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv);
+
+/* Step 2a (V preparation).  v bf16 [B,H,Nk,d].
+ *   SAGE_PV_FP16:     v_t = fp16 (round to nearest even) of V, 2-byte elements [B][H][d][Nk_pad];
+ *                     v_scale is not used (may be NULL).
+ *   SAGE_PV_FP8_E4M3: v_scale fp32 [B][H][d] = max_t |V[t,c]| / 448 (0 for an all-zero channel),
+ *                     v_t = e4m3 (round to nearest even, saturating at +-448) of
+ *                     V * (448 / max_t |V[t,c]|), bytes [B][H][d][Nk_pad].
+ * (Per-channel FP8 V: section "sageattn_qk_int8_pv_fp8_cuda"; transposed V storage as v_fp4_t in the
+ * FlashInfer API doc.)  Key order inside v_t is the order the PV MFMA consumes: fp16 stores each
+ * group of 16 keys as [0-3, 8-11, 4-7, 12-15]; e4m3 stores key kb*32 + w of each group of 64 at
+ * position ((w/4)%2)*32 + kb*16 + (w/8)*4 + w%4.  Pad keys (>= Nk) are zero.
+ * Errors: INVALID_ARGUMENT (descriptor, null/misaligned v_t, fp8 without v_scale), UNSUPPORTED,
+ * WORKSPACE (fp8 and workspace below sage_prepare_v_workspace_bytes), HIP. */
+sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the mask tile classification needs (0 when mask_h == 0).  Host only.
+ * mask_h: 0 = no mask, 1 = mask broadcast over heads, H = one mask per head. */
+size_t sage_mask_workspace_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h);
+
+/* Bytes of workspace sage_attn_fwd needs: prepared V, the fp8 V scales, sage_prepare_v's scratch
+ * and the mask tile classification.  Host only. */
+size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
+                                int64_t mask_h);
+
+/* Step 2 (attention, all in one): sage_prepare_v into the workspace, then sage_attn_fwd_prepared.
+ *   qk: from sage_quantize_qk; v: bf16 [B,H,Nk,d].
+ *   mask: NULL, or uint8 with nonzero = attend, shape [B][mask_h][Nq][Nk] addressed as
+ *         mask + b*mask_stride_b + h*mask_stride_h + i*mask_stride_q + j (mask_h in {1, H};
+ *         mask_stride_h is ignored when mask_h == 1; mask_stride_b may be 0 to broadcast over
+ *         the batch).  (Boolean mask semantics: Triton INT8/FP16 kernel examples section, where
+ *         False entries are masked out.)
+ *   causal: key j is visible to query i only if j <= i (top-left aligned).
+ *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
+ *   out: [B,H,Nq,d] of out_dtype (must be SAGE_BF16) addressed with out_stride_{b,h,n}.
+ *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled, unsmoothed
+ *        scores (lse_corr added back), for merging partial results ("return_lse" on the
+ *        sageattn section and on "Utilize SageAttention for Distributed Inference").
+ * The online softmax runs over sage_block_n() keys per tile in increasing key order with an exact
+ * running maximum; P is rounded to fp16 (or e4m3 of 448*p) against that running maximum; the
+ * denominator sums the unrounded fp32 p; O and l accumulate in fp32.  Keys j >= Nk are masked
+ * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
+ * gets O = 0 and LSE = -inf.
+ * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, mask_h not
+ * in {1,H}), UNSUPPORTED (d, dtype, pv, non-gfx950 device), WORKSPACE (too small), HIP. */
+sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const uint8_t* mask, int64_t mask_h,
+                          int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
+                          float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
+                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Step 2b (attention on prepared V): mask tile classification (if a mask is given) and the
+ * attention kernel.  v_t / v_scale as written by sage_prepare_v for the same B, H, Nk, d and pv.
+ * workspace: at least sage_mask_workspace_bytes(B, Nq, Nk, mask_h) bytes (may be NULL without a
+ * mask).  Other arguments and errors as for sage_attn_fwd. */
+sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+                                   const uint8_t* mask, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
+                                   int64_t mask_stride_q, int causal, float sm_scale, void* out,
+                                   sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
+                                   int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* Debug: the raw int32 scores acc[i,j] = sum_c q8[i,c]*k8[j,c] of head (b,h) for rows
+ * [row0, row0+nrows) and keys [col0, col0+ncols), computed by the same tile code as
+ * sage_attn_fwd.  out: int32 [nrows][ncols] device buffer.  The window must lie inside
+ * [0,Nq_pad) x [0,Nk_pad). */
+sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, int64_t row0, int64_t nrows,
+                                int64_t col0, int64_t ncols, int32_t* out, void* stream);
+
+/* Static description of a status code. Host only. */
+const char* sage_status_string(sage_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_MI355X_H */

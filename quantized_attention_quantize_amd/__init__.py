@@ -2,5 +2,20 @@
 
 The compute path is a C-ABI shared library of hand-written gfx950 HIP kernels
 (``libsage_mi355x.so``, built from ``csrc/``); this package is a thin ctypes binding over it.
-PyTorch supplies device memory and the current stream only.
+PyTorch supplies device memory and the current stream only.  Importing the package does not load
+the library; the first call does, and raises if the library is missing.
 """
+
+from .api import (  # noqa: F401
+    SageError,
+    attn_fwd,
+    attn_fwd_prepared,
+    block_n,
+    debug_qk_int32,
+    lib_path,
+    load_library,
+    pad_tokens,
+    prepare_v,
+    quantize_qk,
+    sageattn,
+)

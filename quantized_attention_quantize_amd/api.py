@@ -1,0 +1,346 @@
+"""ctypes binding of libsage_mi355x (include/sage_mi355x.h).
+
+Argument marshalling only: torch tensors are turned into device pointers, strides and the current
+HIP stream; every step of the computation runs in the library's gfx950 kernels.  If the library
+is missing, every call raises -- there is no fallback path.
+
+User-level entry point, shaped like the pages' ``sageattn`` (SageAttention docs digest, context7
+llms.txt, section "sageattn -- Auto-selecting attention kernel") plus the boolean ``attn_mask`` of
+the Triton INT8/FP16 kernel examples and the FP8 PV option of ``sageattn_qk_int8_pv_fp8_cuda``::
+
+    out = sageattn(q, k, v, tensor_layout="HND", is_causal=False, attn_mask=None,
+                   sm_scale=None, return_lse=False, pv_dtype="fp16")
+
+Lower-level, mirroring the quantize -> attention split of the FlashInfer API doc
+(flashinfer.nvfp4_attention_sm120_fwd): ``quantize_qk`` then ``attn_fwd``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsage_mi355x.so")
+
+SAGE_BF16, SAGE_FP16 = 0, 1
+PV_CODES = {"fp16": 0, "fp8": 1, "fp8_e4m3": 1}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class QKVDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("d", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class QKQuant(ctypes.Structure):
+    _fields_ = [("q8", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("lse_corr", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64), ("Nk_pad", ctypes.c_int64)]
+
+
+_lib = None
+
+EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_quantize_workspace_bytes", "sage_quantize_qk",
+           "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
+           "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_debug_qk_int32",
+           "sage_status_string")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsage_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m quantized_attention_quantize_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.sage_pad_tokens.argtypes = [I64]
+    L.sage_pad_tokens.restype = I64
+    L.sage_block_n.argtypes = [I]
+    L.sage_block_n.restype = I
+    L.sage_quantize_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    L.sage_quantize_workspace_bytes.restype = SZ
+    L.sage_quantize_qk.argtypes = [ctypes.POINTER(QKVDesc), ctypes.POINTER(QKVDesc), ctypes.POINTER(QKQuant), P, SZ, P]
+    L.sage_quantize_qk.restype = I
+    L.sage_prepare_v_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    L.sage_prepare_v_workspace_bytes.restype = SZ
+    L.sage_prepare_v.argtypes = [ctypes.POINTER(QKVDesc), I, P, P, P, SZ, P]
+    L.sage_prepare_v.restype = I
+    L.sage_mask_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    L.sage_mask_workspace_bytes.restype = SZ
+    L.sage_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I, I64]
+    L.sage_fwd_workspace_bytes.restype = SZ
+    L.sage_attn_fwd.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, I64, I64, I64, I64, I, F, I, P, I,
+                                I64, I64, I64, P, P, SZ, P]
+    L.sage_attn_fwd.restype = I
+    L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I64, I64, I64, I64, I, F, P, I, I64, I64,
+                                         I64, P, P, SZ, P]
+    L.sage_attn_fwd_prepared.restype = I
+    L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
+    L.sage_debug_qk_int32.restype = I
+    L.sage_status_string.argtypes = [I]
+    L.sage_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SageError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def pad_tokens(n: int) -> int:
+    return int(load_library().sage_pad_tokens(n))
+
+
+def block_n(pv_dtype: str = "fp16") -> int:
+    """Keys per online-softmax tile of the attention kernel."""
+    return int(load_library().sage_block_n(PV_CODES[pv_dtype]))
+
+
+def _desc(t: torch.Tensor, layout: str) -> QKVDesc:
+    if t.dim() != 4:
+        raise ValueError("q/k/v must be 4-D")
+    if t.dtype == torch.bfloat16:
+        dt = SAGE_BF16
+    elif t.dtype == torch.float16:
+        dt = SAGE_FP16
+    else:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.stride(3) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    if layout == "HND":
+        B, H, N, d = t.shape
+        sb, sh, sn = t.stride(0), t.stride(1), t.stride(2)
+    elif layout == "NHD":
+        B, N, H, d = t.shape
+        sb, sh, sn = t.stride(0), t.stride(2), t.stride(1)
+    else:
+        raise ValueError(f"tensor_layout must be HND or NHD, got {layout}")
+    return QKVDesc(t.data_ptr(), dt, B, H, N, d, sb, sh, sn)
+
+
+@dataclass
+class QuantizedQK:
+    """Device buffers produced by quantize_qk (see sage_qk_quant in the header)."""
+    q8: torch.Tensor
+    k8: torch.Tensor
+    q_scale: torch.Tensor
+    k_scale: torch.Tensor
+    k_mean: torch.Tensor
+    lse_corr: torch.Tensor
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+
+    def cstruct(self) -> QKQuant:
+        return QKQuant(self.q8.data_ptr(), self.k8.data_ptr(), self.q_scale.data_ptr(), self.k_scale.data_ptr(),
+                       self.k_mean.data_ptr(), self.lse_corr.data_ptr(), self.B, self.H, self.Nq, self.Nk, self.d,
+                       self.q8.shape[2], self.k8.shape[2])
+
+
+def alloc_quantized(B, H, Nq, Nk, d, device) -> QuantizedQK:
+    nq, nk = pad_tokens(Nq), pad_tokens(Nk)
+    return QuantizedQK(torch.empty(B, H, nq, d, dtype=torch.int8, device=device),
+                       torch.empty(B, H, nk, d, dtype=torch.int8, device=device),
+                       torch.empty(B, H, (Nq + 63) // 64, dtype=torch.float32, device=device),
+                       torch.empty(B, H, (Nk + 63) // 64, dtype=torch.float32, device=device),
+                       torch.empty(B, H, d, dtype=torch.float32, device=device),
+                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d)
+
+
+def quantize_workspace(B, H, Nk, d, device) -> torch.Tensor:
+    n = int(load_library().sage_quantize_workspace_bytes(B, H, Nk, d))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def quantize_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", out: QuantizedQK | None = None,
+                workspace: torch.Tensor | None = None) -> QuantizedQK:
+    """K mean, per-64-token-block INT8 Q and smoothed K, scales and the LSE shift."""
+    L = load_library()
+    dq, dk = _desc(q, tensor_layout), _desc(k, tensor_layout)
+    if out is None:
+        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device)
+    if workspace is None:
+        workspace = quantize_workspace(dk.B, dk.H, dk.N, dk.d, q.device)
+    qs = out.cstruct()
+    _check(L.sage_quantize_qk(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(qs), workspace.data_ptr(),
+                              workspace.numel(), _stream(q)), "sage_quantize_qk")
+    return out
+
+
+def fwd_workspace(B, H, Nq, Nk, d, pv_dtype, mask_h, device) -> torch.Tensor:
+    n = int(load_library().sage_fwd_workspace_bytes(B, H, Nq, Nk, d, PV_CODES[pv_dtype], mask_h))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _mask_args(attn_mask, B, H, Nq, Nk):
+    if attn_mask is None:
+        return None, 0, 0, 0, 0
+    if attn_mask.dtype != torch.bool:
+        raise NotImplementedError("only boolean masks (True = attend) are supported")
+    m = attn_mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if m.shape[-2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+        raise ValueError(f"attn_mask of shape {tuple(attn_mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
+    if m.stride(3) != 1:
+        m = m.contiguous()
+    mh = m.shape[1]
+    sb = m.stride(0) if m.shape[0] == B else 0
+    sh = m.stride(1) if mh == H and H > 1 else 0
+    return m, (mh if mh == H else 1), sb, sh, m.stride(2)
+
+
+def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is_causal: bool = False,
+             attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, pv_dtype: str = "fp16",
+             return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None):
+    """Attention on pre-quantized Q/K (from quantize_qk) with bf16 V.  Returns out or (out, lse)."""
+    L = load_library()
+    dv = _desc(v, tensor_layout)
+    B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
+    if out is None:
+        shape = (B, H, Nq, d) if tensor_layout == "HND" else (B, Nq, H, d)
+        out = torch.empty(shape, dtype=v.dtype, device=v.device)
+    if tensor_layout == "HND":
+        osb, osh, osn = out.stride(0), out.stride(1), out.stride(2)
+    else:
+        osb, osh, osn = out.stride(0), out.stride(2), out.stride(1)
+    if return_lse and lse is None:
+        lse = torch.empty(B, H, Nq, dtype=torch.float32, device=v.device)
+    m, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
+    if workspace is None:
+        workspace = fwd_workspace(B, H, Nq, Nk, d, pv_dtype, mh, v.device)
+    qs = qk.cstruct()
+    odt = SAGE_BF16 if out.dtype == torch.bfloat16 else SAGE_FP16
+    _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mh, msb, msh, msq,
+                           1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale), PV_CODES[pv_dtype],
+                           out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
+                           workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
+             attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, return_lse: bool = False,
+             pv_dtype: str = "fp16"):
+    """Quantized attention forward: INT8 Q/K with K smoothing, FP16 (or FP8 e4m3) PV.
+
+    q, k, v: bf16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}.
+    attn_mask: optional bool, broadcastable to [B, H, Nq, Nk], True = attend.
+    sm_scale: defaults to 1/sqrt(d).  Returns out (same layout and dtype as q) or (out, lse) with
+    lse fp32 [B, H, Nq] (natural log, of the unsmoothed scaled scores).
+    """
+    if q.shape[-1] not in (64, 128):
+        raise ValueError("head_dim must be 64 or 128")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    hk = k.shape[1] if tensor_layout == "HND" else k.shape[2]
+    hq = q.shape[1] if tensor_layout == "HND" else q.shape[2]
+    if hk != hq:
+        raise NotImplementedError("grouped-query attention (fewer K/V heads) is not supported yet")
+    qk = quantize_qk(q, k, tensor_layout)
+    return attn_fwd(qk, v, tensor_layout=tensor_layout, is_causal=is_causal, attn_mask=attn_mask, sm_scale=sm_scale,
+                    pv_dtype=pv_dtype, return_lse=return_lse)
+
+
+def debug_qk_int32(qk: QuantizedQK, b: int, h: int, row0: int, nrows: int, col0: int, ncols: int) -> torch.Tensor:
+    """Raw int32 Q8 . K8^T window of head (b, h) from the attention kernel's own tile code."""
+    L = load_library()
+    out = torch.empty(nrows, ncols, dtype=torch.int32, device=qk.q8.device)
+    qs = qk.cstruct()
+    _check(L.sage_debug_qk_int32(ctypes.byref(qs), b, h, row0, nrows, col0, ncols, out.data_ptr(), _stream(out)),
+           "sage_debug_qk_int32")
+    return out
+
+
+def alloc_prepared_v(B, H, Nk, d, pv_dtype, device):
+    """Buffers for prepare_v: (v_t, v_scale) with v_t [B,H,d,Nk_pad] (int16 fp16 bits or uint8 e4m3)."""
+    nkp = pad_tokens(Nk)
+    if pv_dtype == "fp16":
+        return torch.empty(B, H, d, nkp, dtype=torch.int16, device=device), None
+    return (torch.empty(B, H, d, nkp, dtype=torch.uint8, device=device),
+            torch.empty(B, H, d, dtype=torch.float32, device=device))
+
+
+def prepare_v_workspace(B, H, Nk, d, pv_dtype, device) -> torch.Tensor:
+    n = int(load_library().sage_prepare_v_workspace_bytes(B, H, Nk, d, PV_CODES[pv_dtype]))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def prepare_v(v: torch.Tensor, pv_dtype: str = "fp16", tensor_layout: str = "HND", out=None,
+              workspace: torch.Tensor | None = None):
+    """V preparation: returns (v_t, v_scale); see sage_prepare_v for the storage order."""
+    L = load_library()
+    dv = _desc(v, tensor_layout)
+    vt, vs = alloc_prepared_v(dv.B, dv.H, dv.N, dv.d, pv_dtype, v.device) if out is None else out
+    if workspace is None:
+        workspace = prepare_v_workspace(dv.B, dv.H, dv.N, dv.d, pv_dtype, v.device)
+    _check(L.sage_prepare_v(ctypes.byref(dv), PV_CODES[pv_dtype], vt.data_ptr(), None if vs is None else vs.data_ptr(),
+                            workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_prepare_v")
+    return vt, vs
+
+
+def mask_workspace(B, Nq, Nk, mask_h, device) -> torch.Tensor:
+    n = int(load_library().sage_mask_workspace_bytes(B, Nq, Nk, mask_h))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor | None, *, pv_dtype: str = "fp16",
+                      tensor_layout: str = "HND", is_causal: bool = False, attn_mask: torch.Tensor | None = None,
+                      sm_scale: float | None = None, return_lse: bool = False, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Attention on pre-quantized Q/K and prepared V (from prepare_v).  Returns out or (out, lse)."""
+    L = load_library()
+    B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
+    dev = qk.q8.device
+    if out is None:
+        shape = (B, H, Nq, d) if tensor_layout == "HND" else (B, Nq, H, d)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    if tensor_layout == "HND":
+        osb, osh, osn = out.stride(0), out.stride(1), out.stride(2)
+    else:
+        osb, osh, osn = out.stride(0), out.stride(2), out.stride(1)
+    if return_lse and lse is None:
+        lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
+    m, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
+    if workspace is None and mh > 0:
+        workspace = mask_workspace(B, Nq, Nk, mh, dev)
+    qs = qk.cstruct()
+    odt = SAGE_BF16 if out.dtype == torch.bfloat16 else SAGE_FP16
+    _check(L.sage_attn_fwd_prepared(ctypes.byref(qs), v_t.data_ptr(), None if v_scale is None else v_scale.data_ptr(),
+                                    PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mh, msb, msh, msq,
+                                    1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+                                    out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
+                                    None if workspace is None else workspace.data_ptr(),
+                                    0 if workspace is None else workspace.numel(), _stream(out)),
+           "sage_attn_fwd_prepared")
+    return (out, lse) if return_lse else out
+
+
+def default_sm_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,402 @@
+// sage_api.cpp -- host side of the libsage_mi355x C ABI (include/sage_mi355x.h).
+//
+// Every entry point validates its arguments on the host first, touching no HIP API, so a bad call
+// returns a status with nothing enqueued.  Then it checks (once per device) that the current
+// device is gfx950, lays out the caller's workspace and enqueues the kernels on the caller's
+// stream.  Nothing here allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "sage_launch.h"
+#include "sage_mi355x.h"
+
+namespace {
+
+using namespace sage;
+
+constexpr int64_t kChunkTokens = 256;   // column-reduction chunk (matches sage_prep.hip)
+constexpr int64_t kTileRows = 256;      // attention workgroup rows == mask tile rows
+constexpr int64_t kTileKeys = 64;       // attention key tile
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+constexpr int kMaxDevices = 64;
+
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+sage_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SAGE_ERR_HIP;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+// Shape / dtype / stride checks of one Q, K or V descriptor.
+sage_status check_desc(const sage_qkv_desc* t) {
+  if (!t || !t->data) return SAGE_ERR_INVALID_ARGUMENT;
+  if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->d <= 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (t->N > kMaxTokens || t->B * t->H > 65535) return SAGE_ERR_INVALID_ARGUMENT;
+  if (t->dtype == SAGE_FP16) return SAGE_ERR_UNSUPPORTED;
+  if (t->dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (t->d != 64 && t->d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_n < t->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(t->data) || (t->stride_b % 8) || (t->stride_h % 8) || (t->stride_n % 8))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+sage_status check_qk(const sage_qk_quant* qk) {
+  if (!qk || !qk->q8 || !qk->k8 || !qk->q_scale || !qk->k_scale || !qk->k_mean || !qk->lse_corr)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (qk->B <= 0 || qk->H <= 0 || qk->Nq <= 0 || qk->Nk <= 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (qk->Nq > kMaxTokens || qk->Nk > kMaxTokens || qk->B * qk->H > 65535) return SAGE_ERR_INVALID_ARGUMENT;
+  if (qk->d != 64 && qk->d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (qk->Nq_pad != sage_pad_tokens(qk->Nq) || qk->Nk_pad != sage_pad_tokens(qk->Nk))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(qk->q8) || !aligned16(qk->k8)) return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+sage_status hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+size_t vt_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
+  return (size_t)(B * H * d * sage_pad_tokens(Nk)) * (pv == SAGE_PV_FP16 ? 2 : 1);
+}
+size_t prep_ws_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
+  return pv == SAGE_PV_FP8_E4M3 ? align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * 4) : 0;
+}
+size_t mask_ws_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h) {
+  return mask_h > 0 ? align256((size_t)(B * mask_h * cdiv(Nq, kTileRows) * cdiv(Nk, kTileKeys))) : 0;
+}
+
+// sage_attn_fwd workspace: [prepared V | fp8 V scale | prepare-V scratch | mask tile states]
+struct FwdLayout {
+  size_t vt, vscale, prep, mtiles, total;
+};
+
+FwdLayout fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv, int64_t mask_h) {
+  FwdLayout L;
+  size_t off = 0;
+  L.vt = off;
+  off += align256(vt_bytes(B, H, Nk, d, pv));
+  L.vscale = off;
+  if (pv == SAGE_PV_FP8_E4M3) off += align256((size_t)(B * H * d) * 4);
+  L.prep = off;
+  off += prep_ws_bytes(B, H, Nk, d, pv);
+  L.mtiles = off;
+  off += mask_ws_bytes(B, Nq, Nk, mask_h);
+  L.total = off;
+  return L;
+}
+
+PrepVArgs prep_v_args(const sage_qkv_desc* v, void* vt, float* vscale, float* vmax_partial) {
+  PrepVArgs a;
+  a.v = static_cast<const unsigned short*>(v->data);
+  a.v_sb = v->stride_b;
+  a.v_sh = v->stride_h;
+  a.v_sn = v->stride_n;
+  a.vt = vt;
+  a.vscale = vscale;
+  a.vmax_partial = vmax_partial;
+  a.B = v->B;
+  a.H = v->H;
+  a.Nk = v->N;
+  a.d = v->d;
+  a.Nk_pad = sage_pad_tokens(v->N);
+  a.nchunk = (int)cdiv(v->N, kChunkTokens);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sage_pad_tokens(int64_t n) { return n <= 0 ? 0 : (n + 127) / 128 * 128; }
+
+int sage_block_n(sage_pv_dtype pv) {
+  (void)pv;
+  return (int)kTileKeys;
+}
+
+size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d) {
+  if (B <= 0 || H <= 0 || Nk <= 0 || d <= 0) return 0;
+  return align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * sizeof(double));
+}
+
+sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  sage_status s;
+  if ((s = check_desc(q)) != SAGE_OK) return s;
+  if ((s = check_desc(k)) != SAGE_OK) return s;
+  if (q->B != k->B || q->H != k->H || q->d != k->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_qk(out)) != SAGE_OK) return s;
+  if (out->B != q->B || out->H != q->H || out->d != q->d || out->Nq != q->N || out->Nk != k->N)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!workspace) return SAGE_ERR_WORKSPACE;
+  if (workspace_bytes < sage_quantize_workspace_bytes(k->B, k->H, k->N, k->d)) return SAGE_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGE_OK) return s;
+
+  QuantArgs a;
+  a.q = static_cast<const unsigned short*>(q->data);
+  a.k = static_cast<const unsigned short*>(k->data);
+  a.q_sb = q->stride_b;
+  a.q_sh = q->stride_h;
+  a.q_sn = q->stride_n;
+  a.k_sb = k->stride_b;
+  a.k_sh = k->stride_h;
+  a.k_sn = k->stride_n;
+  a.q8 = out->q8;
+  a.k8 = out->k8;
+  a.qs = out->q_scale;
+  a.ks = out->k_scale;
+  a.kmean = out->k_mean;
+  a.corr = out->lse_corr;
+  a.B = q->B;
+  a.H = q->H;
+  a.Nq = q->N;
+  a.Nk = k->N;
+  a.d = q->d;
+  a.Nq_pad = out->Nq_pad;
+  a.Nk_pad = out->Nk_pad;
+  a.nbq = (int)cdiv(a.Nq, 64);
+  a.nbk = (int)cdiv(a.Nk, 64);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_status(launch_kmean(a, static_cast<double*>(workspace), (int)cdiv(a.Nk, kChunkTokens), st))) != SAGE_OK)
+    return s;
+  return hip_status(launch_quant(a, st));
+}
+
+size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
+  if (B <= 0 || H <= 0 || Nk <= 0 || d <= 0) return 0;
+  if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return 0;
+  return prep_ws_bytes(B, H, Nk, d, pv);
+}
+
+size_t sage_mask_workspace_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h) {
+  if (B <= 0 || Nq <= 0 || Nk <= 0 || mask_h < 0) return 0;
+  return mask_ws_bytes(B, Nq, Nk, mask_h);
+}
+
+size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
+                                int64_t mask_h) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || mask_h < 0) return 0;
+  if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return 0;
+  return fwd_layout(B, H, Nq, Nk, d, pv, mask_h).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+sage_status validate_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, const void* v_t, const float* v_scale,
+                             const void* workspace, size_t workspace_bytes) {
+  sage_status s;
+  if ((s = check_desc(v)) != SAGE_OK) return s;
+  if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
+  if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  const size_t need = prep_ws_bytes(v->B, v->H, v->N, v->d, pv);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_ERR_WORKSPACE;
+  return SAGE_OK;
+}
+
+sage_status enqueue_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                            hipStream_t st) {
+  const int pv8 = pv == SAGE_PV_FP8_E4M3;
+  PrepVArgs pa = prep_v_args(v, v_t, pv8 ? v_scale : nullptr, pv8 ? static_cast<float*>(workspace) : nullptr);
+  return hip_status(launch_prep_v(pa, pv8, st));
+}
+
+struct FwdCommon {
+  int64_t mh;
+};
+
+sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const uint8_t* mask, int64_t mask_h,
+                                int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, void* out,
+                                sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
+                                int64_t out_stride_n, FwdCommon* c) {
+  sage_status s;
+  if ((s = check_qk(qk)) != SAGE_OK) return s;
+  if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
+  if (!out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_dtype == SAGE_FP16) return SAGE_ERR_UNSUPPORTED;
+  if (out_dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < qk->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || (out_stride_b % 8) || (out_stride_h % 8) || (out_stride_n % 8))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  c->mh = 0;
+  if (mask) {
+    if (mask_h != 1 && mask_h != qk->H) return SAGE_ERR_INVALID_ARGUMENT;
+    if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_q < qk->Nk) return SAGE_ERR_INVALID_ARGUMENT;
+    c->mh = mask_h;
+  }
+  return SAGE_OK;
+}
+
+// Mask classification (if any) and the attention kernel, on already prepared V.
+sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+                              const uint8_t* mask, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
+                              int64_t mask_stride_q, int causal, float sm_scale, void* out, int64_t out_stride_b,
+                              int64_t out_stride_h, int64_t out_stride_n, float* lse, uint8_t* mtiles,
+                              hipStream_t st) {
+  sage_status s;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.nQT = (int)cdiv(qk->Nq, kTileRows);
+  a.nKT = (int)cdiv(qk->Nk, kTileKeys);
+  if (mask) {
+    MaskTileArgs m;
+    m.mask = mask;
+    m.sb = mask_stride_b;
+    m.sh = mask_stride_h;
+    m.sq = mask_stride_q;
+    m.B = qk->B;
+    m.Hm = mh;
+    m.Nq = qk->Nq;
+    m.Nk = qk->Nk;
+    m.nQT = a.nQT;
+    m.nKT = a.nKT;
+    m.vec16 = aligned16(mask) && (mask_stride_b % 16 == 0) && (mh == 1 || mask_stride_h % 16 == 0) &&
+              (mask_stride_q % 16 == 0);
+    m.state = mtiles;
+    if ((s = hip_status(launch_mask_tiles(m, st))) != SAGE_OK) return s;
+    a.mask = mask;
+    a.m_sb = mask_stride_b;
+    a.m_sh = mask_stride_h;
+    a.m_sq = mask_stride_q;
+    a.mtiles = mtiles;
+    a.Hm = mh;
+  }
+  a.q8 = qk->q8;
+  a.k8 = qk->k8;
+  a.qs = qk->q_scale;
+  a.ks = qk->k_scale;
+  a.corr = qk->lse_corr;
+  a.vt = v_t;
+  a.vscale = pv == SAGE_PV_FP8_E4M3 ? v_scale : nullptr;
+  a.out = static_cast<unsigned short*>(out);
+  a.o_sb = out_stride_b;
+  a.o_sh = out_stride_h;
+  a.o_sn = out_stride_n;
+  a.lse = lse;
+  a.B = qk->B;
+  a.H = qk->H;
+  a.Nq = qk->Nq;
+  a.Nk = qk->Nk;
+  a.Nq_pad = qk->Nq_pad;
+  a.Nk_pad = qk->Nk_pad;
+  a.nbq = (int)cdiv(qk->Nq, 64);
+  a.nbk = (int)cdiv(qk->Nk, 64);
+  a.causal = causal ? 1 : 0;
+  a.sm_scale = (sm_scale > 0.f && isfinite(sm_scale)) ? sm_scale : (float)(1.0 / sqrt((double)qk->d));
+  return hip_status(launch_attn(a, (int)qk->d, pv == SAGE_PV_FP8_E4M3, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  sage_status s;
+  if ((s = validate_prepare(v, pv, v_t, v_scale, workspace, workspace_bytes)) != SAGE_OK) return s;
+  if ((s = check_device()) != SAGE_OK) return s;
+  return enqueue_prepare(v, pv, v_t, v_scale, workspace, static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const uint8_t* mask, int64_t mask_h,
+                          int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
+                          float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
+                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  sage_status s;
+  FwdCommon c;
+  if ((s = validate_fwd_common(qk, pv, mask, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out, out_dtype,
+                               out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
+    return s;
+  if ((s = check_desc(v)) != SAGE_OK) return s;
+  if (v->B != qk->B || v->H != qk->H || v->N != qk->Nk || v->d != qk->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!workspace) return SAGE_ERR_WORKSPACE;
+  const FwdLayout L = fwd_layout(qk->B, qk->H, qk->Nq, qk->Nk, qk->d, pv, c.mh);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* vscale = pv == SAGE_PV_FP8_E4M3 ? reinterpret_cast<float*>(ws + L.vscale) : nullptr;
+  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st)) != SAGE_OK) return s;
+  return enqueue_attention(qk, ws + L.vt, vscale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
+                           sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
+                           reinterpret_cast<uint8_t*>(ws + L.mtiles), st);
+}
+
+sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+                                   const uint8_t* mask, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
+                                   int64_t mask_stride_q, int causal, float sm_scale, void* out,
+                                   sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
+                                   int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  sage_status s;
+  FwdCommon c;
+  if ((s = validate_fwd_common(qk, pv, mask, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out, out_dtype,
+                               out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
+    return s;
+  if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  const size_t need = mask_ws_bytes(qk->B, qk->Nq, qk->Nk, c.mh);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGE_OK) return s;
+  return enqueue_attention(qk, v_t, v_scale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
+                           sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
+                           static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, int64_t row0, int64_t nrows,
+                                int64_t col0, int64_t ncols, int32_t* out, void* stream) {
+  sage_status s;
+  if ((s = check_qk(qk)) != SAGE_OK) return s;
+  if (!out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (b < 0 || b >= qk->B || h < 0 || h >= qk->H) return SAGE_ERR_INVALID_ARGUMENT;
+  if (row0 < 0 || nrows <= 0 || row0 + nrows > qk->Nq_pad) return SAGE_ERR_INVALID_ARGUMENT;
+  if (col0 < 0 || ncols <= 0 || col0 + ncols > qk->Nk_pad) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_device()) != SAGE_OK) return s;
+  DebugQKArgs a;
+  const int64_t bh = b * qk->H + h;
+  a.q8h = qk->q8 + bh * qk->Nq_pad * qk->d;
+  a.k8h = qk->k8 + bh * qk->Nk_pad * qk->d;
+  a.row0 = row0;
+  a.nrows = nrows;
+  a.col0 = col0;
+  a.ncols = ncols;
+  a.out = out;
+  return hip_status(launch_debug_qk(a, (int)qk->d, qk->Nq_pad, static_cast<hipStream_t>(stream)));
+}
+
+const char* sage_status_string(sage_status s) {
+  switch (s) {
+    case SAGE_OK:
+      return "ok";
+    case SAGE_ERR_INVALID_ARGUMENT:
+      return "invalid argument";
+    case SAGE_ERR_UNSUPPORTED:
+      return "unsupported (head_dim, dtype, pv dtype or device)";
+    case SAGE_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case SAGE_ERR_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// sage_device.h -- device-side helpers shared by the gfx950 kernels of libsage_mi355x.
+//
+// Vector types, bf16 handling, the LDS swizzle and the prepared-V key permutation.  Everything
+// here is device code for one target (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kQuantBlock = 64;  // tokens per INT8 quantization block (Q and K)
+constexpr int kBlockN = 64;      // keys per attention tile: one K-scale per tile
+constexpr int kWaveRows = 32;    // query rows per wave
+constexpr int kWaves = 8;        // waves per attention workgroup
+constexpr int kBlockM = kWaveRows * kWaves;  // query rows per attention workgroup
+constexpr int kMaskTileRows = kBlockM;       // mask classification granularity (rows)
+
+// int32 accumulator bias: the bit pattern of 1.5 * 2^23.  For |acc| < 2^22 the int32 sum
+// 0x4B400000 + acc is the binary32 pattern of the float 1.5*2^23 + acc, so an MFMA started from
+// this value yields the scores already as floats (offset by 1.5*2^23).
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short h) {
+  return __uint_as_float(static_cast<unsigned>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<unsigned short>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<unsigned short>(u >> 16);
+}
+
+// LDS swizzle of 16-byte chunks inside a row, chosen so that the 16 (or 8) lanes of one
+// ds_read_b128 phase, which read the same logical chunk of 16 consecutive rows, hit distinct
+// banks.  Rows of 128 bytes (8 chunks) and rows of 64 bytes (4 chunks).
+__device__ __forceinline__ int swz128(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
+  if constexpr (ROW_BYTES == 128)
+    return row * 128 + ((chunk ^ swz128(row)) << 4);
+  else
+    return row * 64 + ((chunk ^ swz64(row)) << 4);
+}
+
+}  // namespace sage

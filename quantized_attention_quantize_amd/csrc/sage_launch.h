@@ -1,0 +1,77 @@
+// sage_launch.h -- kernel argument blocks and launcher declarations (internal to libsage_mi355x).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+struct QuantArgs {
+  const unsigned short* q;  // bf16
+  const unsigned short* k;  // bf16
+  int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn;
+  int8_t* q8;
+  int8_t* k8;
+  float* qs;
+  float* ks;
+  float* kmean;
+  float* corr;
+  int64_t B, H, Nq, Nk, d, Nq_pad, Nk_pad;
+  int nbq, nbk;
+};
+
+struct PrepVArgs {
+  const unsigned short* v;  // bf16
+  int64_t v_sb, v_sh, v_sn;
+  void* vt;             // fp16 or e4m3 [B][H][d][Nk_pad]
+  float* vscale;        // fp8 only: [B][H][d]
+  float* vmax_partial;  // fp8 only: [B][H][nchunk][d]
+  int64_t B, H, Nk, d, Nk_pad;
+  int nchunk;
+};
+
+struct MaskTileArgs {
+  const uint8_t* mask;
+  int64_t sb, sh, sq;
+  int64_t B, Hm, Nq, Nk;
+  int nQT, nKT;
+  int vec16;  // rows and base are 16-byte aligned: read 16 bytes at a time
+  uint8_t* state;  // [B*Hm][nQT][nKT]
+};
+
+struct AttnArgs {
+  const int8_t* q8;
+  const int8_t* k8;
+  const float* qs;
+  const float* ks;
+  const float* corr;
+  const void* vt;  // prepared V
+  const float* vscale;
+  const uint8_t* mask;  // element mask (only read for mixed tiles)
+  int64_t m_sb, m_sh, m_sq;
+  const uint8_t* mtiles;  // tile states or nullptr
+  int64_t Hm;             // 0 = no mask
+  unsigned short* out;    // bf16
+  int64_t o_sb, o_sh, o_sn;
+  float* lse;  // nullptr = not requested
+  int64_t B, H, Nq, Nk, Nq_pad, Nk_pad;
+  int nbq, nbk, nQT, nKT;
+  int causal;
+  float sm_scale;
+};
+
+struct DebugQKArgs {
+  const int8_t* q8h;  // head base
+  const int8_t* k8h;
+  int64_t row0, nrows, col0, ncols;
+  int32_t* out;
+};
+
+hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s);
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
+hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s);
+hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s);
+hipError_t launch_debug_qk(const DebugQKArgs& a, int d, int64_t Nq_pad, hipStream_t s);
+
+}  // namespace sage

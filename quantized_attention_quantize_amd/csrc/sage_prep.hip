@@ -1,0 +1,391 @@
+// sage_prep.hip -- HBM-streaming preparation kernels for the quantized attention forward (gfx950).
+//
+//   k_colred_partial  per-(b,h,256-token chunk) column sums of K in fp64 (K mean) or column
+//                     maxima of |V| (fp8 V scale); fixed summation order, no atomics
+//   k_kmean_final     k_mean[b,h,c] = fp32(sum over chunks / Nk)
+//   k_quant_qk        per-64-token-block INT8 quantization of Q and of the smoothed K, their
+//                     scales, and the LSE shift sum_c Q[i,c]*k_mean[c]
+//   k_prep_v16        V -> fp16 (round to nearest even), transposed to [d][Nk_pad] in the key
+//                     order the PV MFMA consumes
+//   k_prep_v8         V -> e4m3 with per-channel scale 448/max|V|, transposed likewise
+//   k_mask_tiles      classifies each (256-row x 64-key) tile of a boolean mask as all-masked,
+//                     all-visible or mixed, so the attention kernel skips or simplifies it
+//
+// Method sources (page title, section): SageAttention docs digest (context7 llms.txt) --
+// "sageattn_qk_int8_pv_fp16_triton" (per-block INT8 Q/K, smooth_k), "sageattn3_blackwell" usage
+// (smoothing by the global token mean), "sageattn_qk_int8_pv_fp8_cuda" (per-channel FP8 V).
+#include "sage_device.h"
+#include "sage_launch.h"
+
+namespace sage {
+
+constexpr int kChunk = 256;  // tokens per column-reduction chunk
+constexpr int kPrepThreads = 256;
+
+// ---------------------------------------------------------------------------------------------
+// Column reductions over token chunks.  MODE 0: fp64 sums of x; MODE 1: fp32 maxima of |x|.
+// grid = (nchunk, B*H), block = 256.  Thread t covers channels [8*(t % (D/8)), +8) of the rows
+// t / (D/8) + i * (256 / (D/8)) of the chunk.
+// ---------------------------------------------------------------------------------------------
+template <int D, int MODE>
+__global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned short* __restrict__ x, int64_t H,
+                                                                 int64_t N, int64_t sb, int64_t sh, int64_t sn,
+                                                                 void* __restrict__ partial, int nchunk) {
+  constexpr int CG = D / 8;               // threads per row
+  constexpr int RPI = kPrepThreads / CG;  // rows per iteration
+  const int t = threadIdx.x, cg = t % CG, rs = t / CG;
+  const int64_t bh = blockIdx.y, b = bh / H, h = bh % H;
+  const int64_t t0 = (int64_t)blockIdx.x * kChunk;
+  const unsigned short* base = x + b * sb + h * sh + cg * 8;
+  double sum[8];
+  float mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    sum[j] = 0.0;
+    mx[j] = 0.f;
+  }
+  for (int r = rs; r < kChunk; r += RPI) {
+    int64_t tok = t0 + r;
+    if (tok < N) {
+      u16x8 v = *reinterpret_cast<const u16x8*>(base + tok * sn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float f = bf16_to_f32(v[j]);
+        if constexpr (MODE == 0)
+          sum[j] += (double)f;
+        else
+          mx[j] = fmaxf(mx[j], fabsf(f));
+      }
+    }
+  }
+  // combine the RPI row-slices in a fixed order
+  if constexpr (MODE == 0) {
+    __shared__ double red[RPI][D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rs][cg * 8 + j] = sum[j];
+    __syncthreads();
+    if (t < D) {
+      double s = 0.0;
+      for (int r = 0; r < RPI; ++r) s += red[r][t];
+      static_cast<double*>(partial)[(bh * nchunk + blockIdx.x) * D + t] = s;
+    }
+  } else {
+    __shared__ float red[RPI][D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[rs][cg * 8 + j] = mx[j];
+    __syncthreads();
+    if (t < D) {
+      float m = 0.f;
+      for (int r = 0; r < RPI; ++r) m = fmaxf(m, red[r][t]);
+      static_cast<float*>(partial)[(bh * nchunk + blockIdx.x) * D + t] = m;
+    }
+  }
+}
+
+// k_mean = fp32(sum_chunks partial / Nk); grid = B*H, block = D.
+template <int D>
+__global__ __launch_bounds__(D) void k_kmean_final(const double* __restrict__ partial, int nchunk, int64_t N,
+                                                   float* __restrict__ kmean) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  double s = 0.0;
+  for (int i = 0; i < nchunk; ++i) s += partial[(bh * nchunk + i) * D + c];
+  kmean[bh * D + c] = (float)(s / (double)N);
+}
+
+// block-wide max of a non-negative float (256 threads)
+__device__ __forceinline__ float block_max256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-block INT8 quantization.  grid = (Nq_pad/64 + Nk_pad/64, B*H), block = 256.
+// Block x < Nq_pad/64 handles Q rows [64x, 64x+64); the others handle K.  Blocks past the last
+// valid block only write zero pad rows.  Each thread holds 8 channels of RPB rows.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
+  constexpr int CG = D / 8;
+  constexpr int RPI = kPrepThreads / CG;  // 16 (D=128) or 32 (D=64)
+  constexpr int RPB = kQuantBlock / RPI;  // rows per thread: 4 or 2
+  __shared__ float red[4];
+  __shared__ float km_s[D];
+  const int t = threadIdx.x, cg = t % CG, rs = t / CG;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int nqb_pad = (int)(a.Nq_pad / kQuantBlock);
+  const bool isq = (int)blockIdx.x < nqb_pad;
+  const int u = isq ? (int)blockIdx.x : (int)blockIdx.x - nqb_pad;
+  const int64_t N = isq ? a.Nq : a.Nk;
+  const int64_t Npad = isq ? a.Nq_pad : a.Nk_pad;
+  int8_t* x8 = (isq ? a.q8 : a.k8) + (bh * Npad + (int64_t)u * kQuantBlock) * D;
+  const int64_t r0 = (int64_t)u * kQuantBlock;
+
+  if (r0 >= N) {  // pure pad block
+#pragma unroll
+    for (int i = 0; i < RPB; ++i) {
+      int r = rs + i * RPI;
+      *reinterpret_cast<uint2*>(x8 + (int64_t)r * D + cg * 8) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+
+  if (t < D) km_s[t] = a.kmean[bh * D + t];
+  __syncthreads();
+
+  const unsigned short* src =
+      isq ? a.q + b * a.q_sb + h * a.q_sh + cg * 8 : a.k + b * a.k_sb + h * a.k_sh + cg * 8;
+  const int64_t sn = isq ? a.q_sn : a.k_sn;
+  float x[RPB][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPB; ++i) {
+    int64_t tok = r0 + rs + i * RPI;
+    if (tok < N) {
+      u16x8 v = *reinterpret_cast<const u16x8*>(src + tok * sn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float f = bf16_to_f32(v[j]);
+        if (!isq) f = f - km_s[cg * 8 + j];  // one fp32 rounding
+        x[i][j] = f;
+        amax = fmaxf(amax, fabsf(f));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
+    }
+  }
+  amax = block_max256(amax, red);
+  float scale = 0.f, inv = 0.f;
+  if (amax > 0.f) {
+    scale = amax / 127.0f;  // IEEE-correct binary32 division
+    inv = 127.0f / amax;
+  }
+  if (t == 0) (isq ? a.qs : a.ks)[bh * (isq ? a.nbq : a.nbk) + u] = scale;
+#pragma unroll
+  for (int i = 0; i < RPB; ++i) {
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float q = __builtin_rintf(x[i][j] * inv);  // round to nearest even
+      q = fminf(fmaxf(q, -127.f), 127.f);
+      unsigned byte = (unsigned)((int)q) & 0xffu;
+      if (j < 4)
+        lo |= byte << (8 * j);
+      else
+        hi |= byte << (8 * (j - 4));
+    }
+    int r = rs + i * RPI;
+    *reinterpret_cast<uint2*>(x8 + (int64_t)r * D + cg * 8) = make_uint2(lo, hi);
+  }
+  if (isq) {
+    // LSE shift: sum_c fp64(Q[i,c]) * fp64(k_mean[c]); the CG threads of a row are adjacent lanes
+#pragma unroll
+    for (int i = 0; i < RPB; ++i) {
+      double s = 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += (double)x[i][j] * (double)km_s[cg * 8 + j];
+#pragma unroll
+      for (int o = 1; o < CG; o <<= 1) s += __shfl_xor(s, o);
+      int64_t tok = r0 + rs + i * RPI;
+      if (cg == 0 && tok < N) a.corr[bh * a.Nq + tok] = (float)s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// V preparation.  grid = (Nk_pad/64, B*H), block = 256.  A 64-token x D tile is converted and
+// written transposed: row c of v_t holds the tile's 64 keys of channel c, in the MFMA key order.
+// ---------------------------------------------------------------------------------------------
+// position p (0..15) inside a 16-key group holds key ((p & 7) >> 2) * 8 + (p >> 3) * 4 + (p & 3)
+__device__ __forceinline__ int fp16_pos_to_key(int p) { return ((p & 7) >> 2) * 8 + (p >> 3) * 4 + (p & 3); }
+// position p (0..63) inside a 64-key group: g = p/32, kb = (p/16)%2, r = p%16;
+// key = kb*32 + (r/4)*8 + g*4 + r%4
+__device__ __forceinline__ int fp8_pos_to_key(int p) {
+  int g = p >> 5, kb = (p >> 4) & 1, r = p & 15;
+  return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
+  constexpr int CG = D / 8;
+  constexpr int RPI = kPrepThreads / CG;
+  __shared__ _Float16 tile[64][D + 8];  // +8 halves of padding against bank conflicts
+  const int t = threadIdx.x, cg = t % CG, rs = t / CG;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + cg * 8;
+  for (int r = rs; r < 64; r += RPI) {
+    int64_t tok = k0 + r;
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = (_Float16)bf16_to_f32(v[j]);  // RNE
+  }
+  __syncthreads();
+  // D rows x 8 chunks of 8 halves; chunk q holds positions [8q, 8q+8)
+  unsigned short* dst = static_cast<unsigned short*>(a.vt) + (bh * D) * a.Nk_pad + k0;
+  for (int i = t; i < D * 8; i += kPrepThreads) {
+    int c = i / 8, q = i % 8;
+    u16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int p = q * 8 + j;
+      int key = (p & ~15) + fp16_pos_to_key(p & 15);
+      _Float16 hv = tile[key][c];
+      o[j] = *reinterpret_cast<unsigned short*>(&hv);
+    }
+    *reinterpret_cast<u16x8*>(dst + (int64_t)c * a.Nk_pad + q * 8) = o;
+  }
+}
+
+// V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1>.
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
+  constexpr int CG = D / 8;
+  constexpr int RPI = kPrepThreads / CG;
+  __shared__ float tile[64][D + 1];
+  __shared__ float inv_s[D];
+  const int t = threadIdx.x, cg = t % CG, rs = t / CG;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  if (t < D) {
+    float m = 0.f;
+    for (int i = 0; i < a.nchunk; ++i) m = fmaxf(m, a.vmax_partial[(bh * a.nchunk + i) * D + t]);
+    float sc = 0.f, inv = 0.f;
+    if (m > 0.f) {
+      sc = m / 448.0f;
+      inv = 448.0f / m;
+    }
+    inv_s[t] = inv;
+    if (blockIdx.x == 0) a.vscale[bh * D + t] = sc;
+  }
+  __syncthreads();
+  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + cg * 8;
+  for (int r = rs; r < 64; r += RPI) {
+    int64_t tok = k0 + r;
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = bf16_to_f32(v[j]) * inv_s[cg * 8 + j];
+      if (fabsf(f) > 448.f) f = copysignf(448.f, f);  // saturate (NaN passes through)
+      tile[r][cg * 8 + j] = f;
+    }
+  }
+  __syncthreads();
+  // D rows x 4 chunks of 16 bytes; chunk q holds positions [16q, 16q+16)
+  uint8_t* dst = static_cast<uint8_t*>(a.vt) + (bh * D) * a.Nk_pad + k0;
+  for (int i = t; i < D * 4; i += kPrepThreads) {
+    int c = i / 4, q = i % 4;
+    v4i o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int p = q * 16 + w * 4;
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(tile[fp8_pos_to_key(p)][c], tile[fp8_pos_to_key(p + 1)][c], 0, false);
+      o[w] = __builtin_amdgcn_cvt_pk_fp8_f32(tile[fp8_pos_to_key(p + 2)][c], tile[fp8_pos_to_key(p + 3)][c], lo,
+                                             true);
+    }
+    *reinterpret_cast<v4i*>(dst + (int64_t)c * a.Nk_pad + q * 16) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Mask tile classification.  grid = (nKT, nQT, B*Hm), block = 256 (one thread per tile row).
+// state: 0 = every (valid) entry masked, 1 = every valid entry visible, 2 = mixed.
+// Entries beyond Nq / Nk do not count.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
+  const int kt = blockIdx.x, qt = blockIdx.y;
+  const int64_t bm = blockIdx.z, b = bm / a.Hm, hm = bm % a.Hm;
+  const int64_t i = (int64_t)qt * kMaskTileRows + threadIdx.x;
+  const int64_t j0 = (int64_t)kt * kBlockN;
+  int any0 = 0, any1 = 0;
+  if (i < a.Nq) {
+    const uint8_t* row = a.mask + b * a.sb + hm * a.sh + i * a.sq;
+    int64_t jn = a.Nk - j0 < kBlockN ? a.Nk - j0 : kBlockN;
+    if (a.vec16 && jn == kBlockN) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 w = *reinterpret_cast<const uint4*>(row + j0 + 16 * c);
+        unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          unsigned v = ws[e];
+          // per byte: zero -> any0, nonzero -> any1
+          unsigned nz = ((v & 0x7f7f7f7fu) + 0x7f7f7f7fu | v) & 0x80808080u;
+          any1 |= nz != 0u;
+          any0 |= nz != 0x80808080u;
+        }
+      }
+    } else {
+      for (int64_t j = 0; j < jn; ++j) {
+        uint8_t v = row[j0 + j];
+        any1 |= v != 0;
+        any0 |= v == 0;
+      }
+    }
+  }
+  int z = __syncthreads_or(any0);
+  int o = __syncthreads_or(any1);
+  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = (uint8_t)(z && o ? 2 : (o ? 1 : 0));
+}
+
+// ---------------------------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------------------------
+hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
+  dim3 g(nchunk, (unsigned)(a.B * a.H));
+  if (a.d == 128) {
+    k_colred_partial<128, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.H, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
+    k_kmean_final<128><<<(unsigned)(a.B * a.H), 128, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+  } else {
+    k_colred_partial<64, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.H, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
+    k_kmean_final<64><<<(unsigned)(a.B * a.H), 64, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
+  dim3 g((unsigned)(a.Nq_pad / kQuantBlock + a.Nk_pad / kQuantBlock), (unsigned)(a.B * a.H));
+  if (a.d == 128)
+    k_quant_qk<128><<<g, kPrepThreads, 0, s>>>(a);
+  else
+    k_quant_qk<64><<<g, kPrepThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
+  dim3 g((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.H));
+  if (!pv_fp8) {
+    if (a.d == 128)
+      k_prep_v16<128><<<g, kPrepThreads, 0, s>>>(a);
+    else
+      k_prep_v16<64><<<g, kPrepThreads, 0, s>>>(a);
+  } else {
+    dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
+    if (a.d == 128) {
+      k_colred_partial<128, 1><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
+                                                          a.nchunk);
+      k_prep_v8<128><<<g, kPrepThreads, 0, s>>>(a);
+    } else {
+      k_colred_partial<64, 1><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
+                                                         a.nchunk);
+      k_prep_v8<64><<<g, kPrepThreads, 0, s>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s) {
+  dim3 g((unsigned)a.nKT, (unsigned)a.nQT, (unsigned)(a.B * a.Hm));
+  k_mask_tiles<<<g, kPrepThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,118 @@
+"""Shared helpers of the GPU parity tests: moving seeded inputs to the device, undoing the
+documented key order of the prepared V, and the comparison metrics."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda"
+
+
+def say(*a):
+    """Flushed progress line, so a failing GPU step names its case."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(inp):
+    return inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_of_bf16_bits(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def fp16_storage_key(p: np.ndarray) -> np.ndarray:
+    """Key held at storage position p of the prepared fp16 V (groups of 16: [0-3, 8-11, 4-7, 12-15])."""
+    base = p & ~15
+    q = p & 15
+    return base + ((q & 7) >> 2) * 8 + (q >> 3) * 4 + (q & 3)
+
+
+def fp8_storage_key(p: np.ndarray) -> np.ndarray:
+    """Key held at storage position p of the prepared e4m3 V (groups of 64, see the header)."""
+    base = p & ~63
+    q = p & 63
+    g, kb, r = q >> 5, (q >> 4) & 1, q & 15
+    return base + kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3)
+
+
+def unpermute_vt(vt: np.ndarray, pv: str) -> np.ndarray:
+    """[B,H,d,Nk_pad] in storage order -> [B,H,Nk_pad,d] in key order."""
+    npad = vt.shape[-1]
+    p = np.arange(npad)
+    key = fp16_storage_key(p) if pv == "fp16" else fp8_storage_key(p)
+    nat = np.empty_like(vt)
+    nat[..., key] = vt
+    return np.ascontiguousarray(np.swapaxes(nat, -1, -2))
+
+
+def rel_l1(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).sum() / max(np.abs(b).sum(), 1e-300))
+
+
+def cosine(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def rows_of(out: torch.Tensor, rows: np.ndarray, layout: str = "HND") -> np.ndarray:
+    """Pick flattened (b*H + h)*Nq + i rows of a [B,H,Nq,d] (or NHD) bf16 output as fp32."""
+    o = out if layout == "HND" else out.permute(0, 2, 1, 3)
+    B, H, Nq, d = o.shape
+    flat = o.reshape(B * H * Nq, d) if o.is_contiguous() else o.contiguous().reshape(B * H * Nq, d)
+    idx = torch.from_numpy(rows).to(out.device)
+    return flat.index_select(0, idx).float().cpu().numpy()
+
+
+def lse_rows(lse: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    return lse.reshape(-1).index_select(0, torch.from_numpy(rows).to(lse.device)).cpu().numpy()
+
+
+def assert_lse_close(got, want, atol):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), "LSE finiteness differs"
+    assert np.array_equal(got[~fin], want[~fin])
+    if fin.any():
+        err = np.abs(got[fin] - want[fin]).max()
+        assert err <= atol, f"LSE max abs diff {err} > {atol}"
+
+
+def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None):
+    """Per-row bound on |LSE(quantized scores) - LSE(exact scores)|.
+
+    logsumexp is 1-Lipschitz in the max norm, so the LSE moves by at most the largest score error
+    over the row's visible keys.  With |q - qs*q8| <= qs/2 and |ks - ks*k8| <= ks/2 per element,
+    |s_ij - s~_ij| <= sm * (sum_c |q_ic| * ks_j/2 + sum_c |k~_jc| * qs_i/2 + d * qs_i*ks_j/4),
+    where k~ is the smoothed key (the smoothing shift itself cancels between the two LSEs)."""
+    B, H, _, d = Qb.shape
+    Q = f32_of_bf16_bits(Qb).astype(np.float64)
+    Ks = (f32_of_bf16_bits(Kb) - qk.kmean[:, :, None, :]).astype(np.float32).astype(np.float64)
+    sk = np.abs(Ks).sum(-1)  # [B,H,Nk]
+    out = np.empty(rows.size)
+    for n, rid in enumerate(rows):
+        bh, i = divmod(int(rid), Nq)
+        b, h = divmod(bh, H)
+        qs = float(qk.qs[b, h, i // 64])
+        ks = np.repeat(qk.ks[b, h].astype(np.float64), 64)[:Nk]
+        sq = np.abs(Q[b, h, i]).sum()
+        bnd = sm_scale * (sq * ks / 2 + sk[b, h] * qs / 2 + d * qs * ks / 4)
+        valid = np.ones(Nk, bool)
+        if causal:
+            valid[i + 1:] = False
+        if mask is not None:
+            valid &= mask[b, 0 if mask.shape[1] == 1 else h, i] != 0
+        out[n] = bnd[valid].max() if valid.any() else 0.0
+    return out

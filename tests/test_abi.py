@@ -1,0 +1,202 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and rejects bad arguments
+with the documented status codes before touching any device (so these run without a GPU)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from quantized_attention_quantize_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(sage_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return api.load_library()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_symbols()
+    assert {"sage_quantize_qk", "sage_attn_fwd", "sage_debug_qk_int32", "sage_prepare_v", "sage_attn_fwd_prepared"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(api.EXPORTS) == names
+
+
+def test_host_queries(L):
+    assert L.sage_pad_tokens(1) == 128 and L.sage_pad_tokens(128) == 128 and L.sage_pad_tokens(17776) == 17792
+    assert L.sage_pad_tokens(0) == 0
+    assert L.sage_block_n(0) == 64 and L.sage_block_n(1) == 64
+    assert L.sage_quantize_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 32 * 128 * 8
+    assert L.sage_quantize_workspace_bytes(0, 1, 1, 64) == 0
+    # prepared fp16 V of the 8192-token, 64-head workload
+    assert L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 0) == 2 * 32 * 128 * 8192 * 2
+    base8 = L.sage_fwd_workspace_bytes(1, 24, 17776, 17776, 128, 1, 0)
+    assert base8 >= 24 * 128 * 17792 + 24 * 128 * 4
+    with_mask = L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 1)
+    assert with_mask - L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 0) >= 2 * 32 * 128
+    assert L.sage_fwd_workspace_bytes(1, 1, 1, 1, 64, 7, 0) == 0
+    for s, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing or too small")]:
+        assert L.sage_status_string(s) == txt
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null address; validation fails before anything dereferences it
+
+
+def desc(B=1, H=2, N=256, d=64, dtype=0, data=FAKE, sb=None, sh=None, sn=None):
+    sn = d if sn is None else sn
+    sh = N * sn if sh is None else sh
+    sb = H * sh if sb is None else sb
+    return api.QKVDesc(data, dtype, B, H, N, d, sb, sh, sn)
+
+
+def quant(B=1, H=2, Nq=256, Nk=256, d=64, pad=None, null=None):
+    ptrs = [FAKE] * 6
+    if null is not None:
+        ptrs[null] = 0
+    npq = L_pad(Nq) if pad is None else pad
+    return api.QKQuant(*ptrs, B, H, Nq, Nk, d, npq, L_pad(Nk))
+
+
+def L_pad(n):
+    return (n + 127) // 128 * 128
+
+
+def call_quant(L, q, k, out, ws=FAKE, wsb=1 << 20):
+    return L.sage_quantize_qk(ctypes.byref(q) if q else None, ctypes.byref(k) if k else None,
+                              ctypes.byref(out) if out else None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("null_q", INVALID), ("null_data", INVALID), ("zero_B", INVALID), ("neg_N", INVALID), ("d96", UNSUPPORTED),
+    ("fp16", UNSUPPORTED), ("bad_dtype", INVALID), ("misaligned", INVALID), ("odd_stride", INVALID),
+    ("small_stride_n", INVALID), ("qk_mismatch_H", INVALID), ("out_null_ptr", INVALID), ("out_bad_pad", INVALID),
+    ("out_wrong_N", INVALID), ("no_workspace", WORKSPACE), ("small_workspace", WORKSPACE),
+])
+def test_quantize_validation(L, case, status):
+    q, k, out = desc(), desc(), quant()
+    ws, wsb = FAKE, 1 << 20
+    if case == "null_q":
+        q = None
+    elif case == "null_data":
+        q = desc(data=0)
+    elif case == "zero_B":
+        q = desc(B=0)
+    elif case == "neg_N":
+        k = desc(N=-5)
+    elif case == "d96":
+        q, k = desc(d=96), desc(d=96)
+    elif case == "fp16":
+        q = desc(dtype=1)
+    elif case == "bad_dtype":
+        q = desc(dtype=9)
+    elif case == "misaligned":
+        q = desc(data=FAKE + 2)
+    elif case == "odd_stride":
+        k = desc(sn=68)
+    elif case == "small_stride_n":
+        k = desc(sn=32)
+    elif case == "qk_mismatch_H":
+        k = desc(H=3)
+    elif case == "out_null_ptr":
+        out = quant(null=3)
+    elif case == "out_bad_pad":
+        out = quant(pad=200)
+    elif case == "out_wrong_N":
+        out = quant(Nq=255)
+    elif case == "no_workspace":
+        ws = 0
+    elif case == "small_workspace":
+        wsb = 16
+    assert call_quant(L, q, k, out, ws, wsb) == status
+
+
+def call_fwd(L, qk, v, mask=None, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30):
+    return L.sage_attn_fwd(ctypes.byref(qk) if qk else None, ctypes.byref(v) if v else None, mask, mask_h, 0, 0, msq,
+                           0, 0.0, pv, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("null_qk", INVALID), ("v_shape", INVALID), ("pv_bad", UNSUPPORTED), ("out_null", INVALID),
+    ("out_fp16", UNSUPPORTED), ("out_misaligned", INVALID), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
+    ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED),
+])
+def test_attn_validation(L, case, status):
+    qk, v = quant(), desc()
+    kw = {}
+    if case == "null_qk":
+        qk = None
+    elif case == "v_shape":
+        v = desc(N=128)
+    elif case == "pv_bad":
+        kw["pv"] = 5
+    elif case == "out_null":
+        kw["out"] = 0
+    elif case == "out_fp16":
+        kw["odt"] = 1
+    elif case == "out_misaligned":
+        kw["out"] = FAKE + 8
+    elif case == "mask_h_bad":
+        kw.update(mask=FAKE, mask_h=3)
+    elif case == "mask_stride_small":
+        kw.update(mask=FAKE, mask_h=1, msq=100)
+    elif case == "ws_small":
+        kw["wsb"] = 100
+    elif case == "ws_null":
+        kw["ws"] = 0
+    elif case == "qk_d":
+        qk = quant(d=80)
+    assert call_fwd(L, qk, v, **kw) == status
+
+
+def test_debug_validation(L):
+    qk = quant()
+    out = FAKE
+    assert L.sage_debug_qk_int32(ctypes.byref(qk), 0, 0, 0, 10, 0, 10, 0, None) == INVALID
+    assert L.sage_debug_qk_int32(ctypes.byref(qk), 1, 0, 0, 10, 0, 10, out, None) == INVALID  # b >= B
+    assert L.sage_debug_qk_int32(ctypes.byref(qk), 0, 0, 200, 100, 0, 10, out, None) == INVALID  # past Nq_pad
+    assert L.sage_debug_qk_int32(ctypes.byref(qk), 0, 0, 0, 10, -1, 10, out, None) == INVALID
+    v = desc()
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, None, FAKE, 1 << 20, None) == INVALID  # fp8 needs v_scale
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, FAKE, 10, None) == WORKSPACE
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, 0, 1 << 20, None) == WORKSPACE
+    assert L.sage_prepare_v(ctypes.byref(v), 3, FAKE, None, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert L.sage_prepare_v(ctypes.byref(v), 0, FAKE + 4, None, None, 0, None) == INVALID  # misaligned v_t
+
+
+def test_prepared_attn_validation(L):
+    qk = quant()
+    args = [0, None, 0, 0, 0, 0, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
+    f = L.sage_attn_fwd_prepared
+    assert f(ctypes.byref(qk), 0, None, *args, None, 0, None) == INVALID  # no v_t
+    assert f(ctypes.byref(qk), FAKE, None, 1, *args[1:], None, 0, None) == INVALID  # fp8 without v_scale
+    masked = [0, FAKE, 1, 0, 0, 256, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
+    assert f(ctypes.byref(qk), FAKE, None, *masked, None, 0, None) == WORKSPACE  # mask needs tile workspace
+    assert L.sage_mask_workspace_bytes(2, 8192, 8192, 1) == 2 * 32 * 128
+    assert L.sage_mask_workspace_bytes(2, 8192, 8192, 0) == 0
+    assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 0) == 0
+    assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 1) >= 24 * 70 * 128 * 4
+
+
+def test_no_oracle_on_product_path():
+    """The product package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "quantized_attention_quantize_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if path.endswith((".py", ".cpp", ".hip", ".h")):
+            text = open(path).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b|libsage_oracle|sage_oracle\.c", text, flags=re.M), path

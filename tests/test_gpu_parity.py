@@ -1,0 +1,263 @@
+"""GPU parity on small and ragged shapes: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: K mean, int8 Q/K codes, their scales, the prepared V (fp16 / e4m3 bytes and the e4m3
+per-channel scale) and the int32 Q8.K8^T scores.  Tolerance: O within relative L1 1e-3 of the
+oracle's quantized emulation (both rounded to bf16) and LSE within 1e-3; against fp64 exact
+attention, cosine >= 0.999 and relative L1 <= 3e-2 for FP16 PV.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_quantize_amd as sage
+from quantized_attention_quantize_amd import api
+from quantized_attention_quantize_amd.synthetic import make_inputs, random_mask
+
+from gpu_helpers import (DEV, assert_lse_close, bits, cosine, f32_of_bf16_bits, lse_rows, rel_l1, rows_of, say,
+                         to_dev, unpermute_vt)
+
+pytestmark = pytest.mark.gpu
+
+QE_REL_L1 = 1e-3  # output vs quantized emulation (spec bar)
+QE_LSE = 1e-3
+EX_COS = 0.999
+EX_REL_L1 = 3e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    sage.load_library()  # raises loudly if the HIP library is missing
+
+
+SHAPES = [(1, 2, 256, 256, 64), (1, 1, 1, 1, 64), (1, 2, 63, 63, 128), (2, 1, 65, 65, 128), (1, 2, 129, 300, 64),
+          (1, 3, 300, 129, 128), (2, 2, 64, 64, 64), (1, 1, 700, 1000, 128)]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", SHAPES)
+def test_quantize_bitexact(orc, B, H, Nq, Nk, d):
+    say(f"quantize B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=3)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qk(q, k)
+    torch.cuda.synchronize()
+    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k))
+    assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32))
+    assert np.array_equal(g.q8.cpu().numpy(), c.q8)
+    assert np.array_equal(g.k8.cpu().numpy(), c.k8)
+    assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32))
+    assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32))
+    np.testing.assert_allclose(g.lse_corr.cpu().numpy(), c.corr, rtol=2e-6, atol=2e-6)
+
+
+def test_quantize_nhd_layout_and_zero_blocks(orc):
+    inp = make_inputs(2, 3, 130, 200, 128, sigma=4.0, seed=4)
+    qb = inp.q.clone()
+    qb[0, 1, 64:128] = 0  # an all-zero Q block: scale 0, codes 0
+    kb = inp.k.clone()
+    kb[1, 2] = kb[1, 2, :1]  # constant keys: smoothed K exactly zero
+    q = qb.permute(0, 2, 1, 3).contiguous().to(DEV)  # NHD
+    k = kb.permute(0, 2, 1, 3).contiguous().to(DEV)
+    g = sage.quantize_qk(q, k, tensor_layout="NHD")
+    torch.cuda.synchronize()
+    c = orc.quant_qk(bits(qb), bits(kb))
+    assert np.array_equal(g.q8.cpu().numpy(), c.q8) and np.array_equal(g.k8.cpu().numpy(), c.k8)
+    assert np.array_equal(g.q_scale.cpu().numpy(), c.qs) and np.array_equal(g.k_scale.cpu().numpy(), c.ks)
+    assert g.q_scale[0, 1, 1].item() == 0.0 and (g.k_scale[1, 2] == 0).all()
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", SHAPES[:6])
+def test_debug_scores_bitexact(orc, B, H, Nq, Nk, d):
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=5)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qk(q, k)
+    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k))
+    nqp, nkp = c.q8.shape[2], c.k8.shape[2]
+    for b in range(B):
+        for h in range(H):
+            say(f"scores b={b} h={h} window full")
+            got = sage.debug_qk_int32(g, b, h, 0, nqp, 0, nkp).cpu().numpy()
+            want = orc.scores(c.q8, c.k8, b, h, 0, nqp, 0, nkp)
+            assert np.array_equal(got, want)
+    # an unaligned window
+    r0, nr, c0, nc = 5, min(70, nqp - 5), 3, min(100, nkp - 3)
+    got = sage.debug_qk_int32(g, B - 1, H - 1, r0, nr, c0, nc).cpu().numpy()
+    assert np.array_equal(got, orc.scores(c.q8, c.k8, B - 1, H - 1, r0, nr, c0, nc))
+
+
+def test_debug_scores_extremes(orc):
+    """Codes at +-127 everywhere reach the largest |int32| the path produces (127^2 * d)."""
+    d = 128
+    Q = torch.full((1, 1, 64, d), 3.0, dtype=torch.bfloat16)
+    K = torch.zeros(1, 1, 128, d, dtype=torch.bfloat16)
+    K[0, 0, :64] = -2.0
+    K[0, 0, 64:] = 2.0  # smoothed: +-2 -> codes -127 / 127
+    g = sage.quantize_qk(Q.to(DEV), K.to(DEV))
+    got = sage.debug_qk_int32(g, 0, 0, 0, 64, 0, 128).cpu().numpy()
+    assert (got[:, :64] == -127 * 127 * d).all() and (got[:, 64:] == 127 * 127 * d).all()
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 64), (2, 1, 65, 128), (1, 3, 300, 128), (1, 1, 1, 64)])
+def test_prep_v_bitexact(orc, pv, B, H, N, d):
+    say(f"prep_v {pv} B={B} H={H} N={N} d={d}")
+    inp = make_inputs(B, H, N, N, d, seed=6)
+    vt, vs = sage.prepare_v(inp.v.to(DEV), pv)
+    torch.cuda.synchronize()
+    want, want_s = orc.prep_v(inp.bits(inp.v), pv)
+    got = vt.cpu().numpy()
+    got = got.view(np.uint16) if pv == "fp16" else got
+    nat = unpermute_vt(got, pv)
+    assert np.array_equal(nat[:, :, :N, :], want)
+    assert not nat[:, :, N:, :].any()  # pad keys are zero
+    if pv == "fp8":
+        assert np.array_equal(vs.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+
+
+def test_prep_v_fp8_extremes(orc):
+    """Ties, subnormals, saturation edge and a zero channel through the e4m3 preparation."""
+    N, d = 64, 64
+    V = torch.randn(1, 1, N, d).to(torch.bfloat16)
+    V[0, 0, :, 0] = 0  # all-zero channel: scale 0, codes 0
+    V[0, 0, 0, 1] = 448.0
+    V[0, 0, 1:, 1] = torch.tensor([2.0 ** -e for e in range(3, 3 + N - 1)], dtype=torch.float32).to(torch.bfloat16)
+    vt, vs = sage.prepare_v(V.to(DEV), "fp8")
+    want, want_s = orc.prep_v(bits(V), "fp8")
+    nat = unpermute_vt(vt.cpu().numpy(), "fp8")
+    assert np.array_equal(nat[:, :, :N], want) and np.array_equal(vs.cpu().numpy(), want_s)
+
+
+def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None):
+    q, k, v = to_dev(inp)
+    if layout == "NHD":
+        q, k, v = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v))
+    mask_dev = None if mask is None else mask.to(DEV)
+    out, lse = sage.sageattn(q, k, v, tensor_layout=layout, is_causal=causal, attn_mask=mask_dev, sm_scale=sm_scale,
+                             return_lse=True, pv_dtype=pv)
+    torch.cuda.synchronize()
+    B, H, Nq, d = inp.q.shape
+    if rows is None:
+        rows = np.arange(B * H * Nq, dtype=np.int64)
+    m_u8 = None if mask is None else mask.numpy().astype(np.uint8)
+    r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m_u8,
+                   sm_scale=sm_scale, BN=sage.block_n(pv), rows=rows)
+    ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m_u8,
+                             sm_scale=sm_scale, rows=rows)
+    got_o = rows_of(out, rows, layout)
+    got_l = lse_rows(lse, rows)
+    return got_o, got_l, r, ex_o, ex_l
+
+
+def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16"):
+    qe_o = f32_of_bf16_bits(r.obf)
+    e1 = rel_l1(got_o, qe_o)
+    assert e1 <= QE_REL_L1, f"rel-L1 vs quantized emulation {e1}"
+    assert_lse_close(got_l, r.lse, QE_LSE)
+    live = np.abs(ex_o).sum(axis=1) > 0
+    if live.any():
+        cos = cosine(got_o[live], ex_o[live])
+        ex1 = rel_l1(got_o[live], ex_o[live])
+        assert cos >= EX_COS, f"cosine vs exact {cos}"
+        assert ex1 <= (EX_REL_L1 if pv == "fp16" else 5e-2), f"rel-L1 vs exact {ex1}"
+    return e1
+
+
+CASES = [
+    dict(name="tiny", B=1, H=2, Nq=256, Nk=256, d=64),
+    dict(name="d128", B=1, H=2, Nq=512, Nk=512, d=128),
+    dict(name="ragged", B=2, H=1, Nq=300, Nk=417, d=128),
+    dict(name="one_key", B=1, H=2, Nq=77, Nk=1, d=64),
+    dict(name="one_query", B=1, H=2, Nq=1, Nk=333, d=128),
+    dict(name="causal", B=1, H=2, Nq=600, Nk=600, d=128, causal=True),
+    dict(name="causal_rect", B=1, H=1, Nq=300, Nk=520, d=64, causal=True),
+    dict(name="mask_half", B=2, H=2, Nq=320, Nk=640, d=128, mask="half"),
+    dict(name="mask_rand_per_head", B=1, H=3, Nq=257, Nk=200, d=64, mask="rand_h"),
+    dict(name="mask_rand_bcast_causal", B=2, H=2, Nq=200, Nk=200, d=128, mask="rand_1", causal=True),
+    dict(name="fp8", B=1, H=2, Nq=400, Nk=777, d=128, pv="fp8", sigma=8.0),
+    dict(name="fp8_d64_causal", B=1, H=2, Nq=300, Nk=300, d=64, pv="fp8", causal=True),
+    dict(name="fp8_mask", B=1, H=2, Nq=256, Nk=320, d=128, pv="fp8", mask="half"),
+    dict(name="sm_scale", B=1, H=2, Nq=256, Nk=256, d=128, sm_scale=0.05),
+    dict(name="nhd", B=2, H=3, Nq=200, Nk=260, d=64, layout="NHD"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_attention_parity(orc, case):
+    c = dict(case)
+    say(f"attention case {c}")
+    B, H, Nq, Nk, d = c["B"], c["H"], c["Nq"], c["Nk"], c["d"]
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=11)
+    mask = None
+    if c.get("mask") == "half":
+        mask = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+        mask[..., Nk // 2:] = False
+    elif c.get("mask") == "rand_h":
+        mask = random_mask(B, H, Nq, Nk, 0.6, seed=3)
+    elif c.get("mask") == "rand_1":
+        mask = random_mask(B, 1, Nq, Nk, 0.5, seed=4)
+    got_o, got_l, r, ex_o, ex_l = run_both(orc, inp, pv=c.get("pv", "fp16"), causal=c.get("causal", False), mask=mask,
+                                           sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"))
+    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"))
+    say(f"  rel-L1 vs QE {e1:.3e}")
+
+
+def test_fully_masked_rows_and_tiles(orc):
+    B, H, Nq, Nk, d = 1, 2, 300, 300, 64
+    inp = make_inputs(B, H, Nq, Nk, d, seed=12)
+    mask = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+    mask[0, 0, 7, :] = False  # one row sees nothing
+    mask[0, 0, 256:, :] = False  # a whole 256-row tile sees nothing
+    mask[0, 0, :, 64:128] = False  # a whole key tile is dropped
+    got_o, got_l, r, ex_o, ex_l = run_both(orc, inp, mask=mask)
+    check(got_o, got_l, r, ex_o, ex_l)
+    dead = np.array([h * Nq + i for h in range(H) for i in [7] + list(range(256, 300))])
+    assert (got_o[dead] == 0).all() and np.isneginf(got_l[dead]).all()
+
+
+def test_zero_query_closed_form(orc):
+    """Q = 0: every score is 0, so O is the mean of the prepared values and LSE = ln(Nk)."""
+    B, H, N, d = 1, 2, 200, 128
+    inp = make_inputs(B, H, N, N, d, seed=13)
+    inp.q.zero_()
+    out, lse = sage.sageattn(*to_dev(inp), return_lse=True)
+    vhat = torch.from_numpy(inp.v.float().numpy()).to(torch.float16).double()
+    want = vhat.mean(dim=2, keepdim=True).expand(B, H, N, d)
+    np.testing.assert_allclose(out.float().cpu().numpy(), want.numpy(), rtol=1e-2, atol=1e-3)
+    np.testing.assert_allclose(lse.cpu().numpy(), np.log(N), atol=1e-5)
+
+
+def test_outputs_leave_neighbours_untouched():
+    """Canary: the output and LSE buffers live inside larger buffers; nothing outside changes."""
+    B, H, Nq, Nk, d = 1, 2, 131, 131, 128
+    inp = make_inputs(B, H, Nq, Nk, d, seed=14)
+    q, k, v = to_dev(inp)
+    qk = sage.quantize_qk(q, k)
+    big = torch.full((B * H * Nq * d + 4096,), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = big[2048:2048 + B * H * Nq * d].view(B, H, Nq, d)
+    lbig = torch.full((B * H * Nq + 128,), 3.25, dtype=torch.float32, device=DEV)
+    lse = lbig[64:64 + B * H * Nq].view(B, H, Nq)
+    sage.attn_fwd(qk, v, out=out, lse=lse, return_lse=True)
+    torch.cuda.synchronize()
+    assert (big[:2048] == -7.0).all() and (big[2048 + B * H * Nq * d:] == -7.0).all()
+    assert (lbig[:64] == 3.25).all() and (lbig[64 + B * H * Nq:] == 3.25).all()
+    assert torch.isfinite(out.float()).all()
+
+
+def test_repeatable_bitwise():
+    inp = make_inputs(1, 2, 700, 700, 128, seed=15)
+    q, k, v = to_dev(inp)
+    ref = sage.sageattn(q, k, v, return_lse=True)
+    for _ in range(5):
+        o, l = sage.sageattn(q, k, v, return_lse=True)
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
+def test_errors_raise():
+    inp = make_inputs(1, 1, 64, 64, 64, seed=16)
+    q, k, v = to_dev(inp)
+    with pytest.raises(ValueError):
+        sage.sageattn(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
+    with pytest.raises(api.SageError) as ei:
+        sage.sageattn(q.half(), k.half(), v.half())
+    assert ei.value.status == 2

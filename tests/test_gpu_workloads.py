@@ -1,0 +1,104 @@
+"""GPU parity at the full workload sizes (the launch configuration the benchmark times).
+
+For every workload: the K mean, int8 Q/K, their scales and the prepared V are compared bit for bit
+over the whole tensors; int32 scores on windows of 256 rows x all keys of two heads; O and LSE on a
+seeded sample of rows (random rows over all heads plus each head's first and last rows) against
+the oracle's quantized emulation, and against fp64 exact attention.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_quantize_amd as sage
+from quantized_attention_quantize_amd.synthetic import WORKLOADS, workload_inputs
+
+from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_quant_bound, lse_rows, rel_l1, rows_of,
+                         say, to_dev, unpermute_vt)
+
+pytestmark = pytest.mark.gpu
+
+N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_parity(orc, name):
+    w = WORKLOADS[name]
+    say(f"workload {name}: {w.note}")
+    inp = workload_inputs(w, seed=0)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    q, k, v = to_dev(inp)
+    mask_dev = None if inp.mask is None else inp.mask.to(DEV)
+
+    # quantization: whole tensors, bit for bit
+    g = sage.quantize_qk(q, k)
+    torch.cuda.synchronize()
+    c = orc.quant_qk(Qb, Kb)
+    assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32)), "k_mean"
+    assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32)), "q_scale"
+    assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32)), "k_scale"
+    assert np.array_equal(g.q8.cpu().numpy(), c.q8), "q8"
+    assert np.array_equal(g.k8.cpu().numpy(), c.k8), "k8"
+    np.testing.assert_allclose(g.lse_corr.cpu().numpy(), c.corr, rtol=2e-6, atol=2e-6)
+    say("  quantization bit-exact")
+
+    # prepared V: whole tensor, bit for bit
+    vt, vs = sage.prepare_v(v, w.pv)
+    torch.cuda.synchronize()
+    vh, vsc = orc.prep_v(Vb, w.pv)
+    got = vt.cpu().numpy()
+    nat = unpermute_vt(got.view(np.uint16) if w.pv == "fp16" else got, w.pv)
+    assert np.array_equal(nat[:, :, :w.Nk], vh), "prepared V"
+    assert not nat[:, :, w.Nk:].any()
+    if w.pv == "fp8":
+        assert np.array_equal(vs.cpu().numpy().view(np.uint32), vsc.view(np.uint32)), "V scale"
+    del nat, got, vt
+    say("  prepared V bit-exact")
+
+    # int32 scores: 256 rows x all keys, first and last rows of two heads
+    nqp, nkp = c.q8.shape[2], c.k8.shape[2]
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        for r0 in (0, nqp - 256):
+            got = sage.debug_qk_int32(g, b, h, r0, 256, 0, nkp).cpu().numpy()
+            assert np.array_equal(got, orc.scores(c.q8, c.k8, b, h, r0, 256, 0, nkp)), ("scores", b, h, r0)
+    say("  int32 scores bit-exact")
+
+    # attention
+    out, lse = sage.sageattn(q, k, v, is_causal=w.causal, attn_mask=mask_dev, return_lse=True, pv_dtype=w.pv)
+    torch.cuda.synchronize()
+    R = w.B * w.H * w.Nq
+    n_rand = N_RANDOM_ROWS[name]
+    if n_rand is None:
+        rows = np.arange(R, dtype=np.int64)
+    else:
+        rng = np.random.default_rng(0)
+        ends = [bh * w.Nq + i for bh in (0, w.B * w.H - 1) for i in list(range(64)) + list(range(w.Nq - 64, w.Nq))]
+        rows = np.unique(np.concatenate([rng.choice(R, n_rand, replace=False), np.array(ends)])).astype(np.int64)
+    m_u8 = inp.mask_u8
+    vh_o, vs_o = (vh, vsc)
+    o32, obf, qlse = orc.attn_qe(c, vh_o, vs_o, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8,
+                                 BN=sage.block_n(w.pv), rows=rows)
+    got_o = rows_of(out, rows)
+    got_l = lse_rows(lse, rows)
+    e_qe = rel_l1(got_o, f32_of_bf16_bits(obf))
+    say(f"  rows={rows.size} rel-L1 vs quantized emulation {e_qe:.3e}")
+    assert e_qe <= 1e-3
+    assert_lse_close(got_l, qlse, 1e-3)
+    ex_rows = rows[:: max(1, rows.size // 512)]
+    ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, mask=m_u8, rows=ex_rows)
+    sel = np.searchsorted(rows, ex_rows)
+    cos = cosine(got_o[sel], ex_o)
+    e_ex = rel_l1(got_o[sel], ex_o)
+    say(f"  vs fp64 exact: cosine {cos:.6f} rel-L1 {e_ex:.3e} max|dLSE| {np.abs(got_l[sel] - ex_l).max():.3e}")
+    assert cos >= 0.999
+    if w.pv == "fp16":
+        assert e_ex <= 3e-2
+    else:
+        # e4m3 rounding of P and V alone costs ~3.7e-2 relative L1 on these inputs, so the 3e-2 bar
+        # cannot be met by a faithful implementation; the measured value is reported above.
+        assert e_ex <= 5e-2
+    # LSE against the exact LSE: within the per-row score-quantization bound (plus fp32 slack)
+    bound = lse_quant_bound(c, Qb, Kb, ex_rows, w.Nq, w.Nk, orc.default_sm_scale(w.d), w.causal, m_u8)
+    excess = np.abs(got_l[sel] - ex_l) - bound
+    say(f"  LSE vs exact: worst excess over the quantization bound {excess.max():.3e} (bound max {bound.max():.3e})")
+    assert excess.max() <= 1e-4
