@@ -28,14 +28,18 @@
  *  - P for FP8 PV is quantized as e4m3(448 * p) with saturation, V per channel as
  *    e4m3(V * 448 / max_t |V|);
  *  - the softmax denominator l sums the unquantized fp32 p;
- *  - the online softmax runs over key tiles of BN keys in increasing key order with an exact
- *    running maximum;
+ *  - the online softmax runs over key tiles of BN keys in increasing key order.  Its reference
+ *    maximum m starts at -inf and, after each tile, is replaced by the running maximum whenever
+ *    that exceeds m by more than tau*ln(2) (tau = 0: the exact running maximum); p = exp(s - m)
+ *    is then at most 2^tau.  The normalized result does not depend on tau; only where P is
+ *    rounded does;
  *  - a row with no valid key gives O = 0 and LSE = -inf;
  *  - LSE is natural-log and adds back the smoothing shift sm_scale * (q_i . kmean), so it is the
  *    LSE of the unsmoothed scores.
  *
  * Index arithmetic is 64-bit throughout.  Compile without -ffast-math and with -ffp-contract=off.
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -314,14 +318,15 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /*       mask == NULL means no mask.                                                          */
 /* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
 /* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
+/* BN: keys per online-softmax tile; tau: lazy-maximum threshold in log2 units (0 = exact).    */
 /* Outputs per requested row: o32 [nrows][d] (fp32 O before the bf16 rounding, may be NULL),  */
 /* obf [nrows][d] (bf16 bits), lse [nrows] (natural log, fp32).                               */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
                  const void* vhat, const float* vs, int pv_fp8, const uint8_t* mask, int64_t mask_h, int causal,
                  float sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
-                 int64_t Nk_pad, int64_t BN, const int64_t* rows, int64_t nrows, float* o32, uint16_t* obf,
-                 float* lse) {
+                 int64_t Nk_pad, int64_t BN, double tau, const int64_t* rows, int64_t nrows, float* o32,
+                 uint16_t* obf, float* lse) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
   if (rows == NULL) nrows = B * H * Nq;
 #pragma omp parallel
@@ -358,7 +363,8 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           s[j - j0] = (float)acc * cst;
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
-        float mnew = m > tmax ? m : tmax;
+        float mnew = m;
+        if (m == -INFINITY || (double)tmax > (double)m + tau * M_LN2) mnew = m > tmax ? m : tmax;
         if (mnew == -INFINITY) continue; /* nothing valid so far */
         float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mnew));
         float psum = 0.0f;

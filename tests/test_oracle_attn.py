@@ -223,3 +223,22 @@ def test_qe_smoothing_is_what_buys_accuracy(orc):
     o_s = orc.attn_qe(qk, vh, vs, "fp16", N, N)[0]
     o_r = orc.attn_qe(raw, vh, vs, "fp16", N, N)[0]
     assert _rel_l1(o_s, eo) < 0.5 * _rel_l1(o_r, eo)
+
+
+@pytest.mark.parametrize("sm", [None, 0.6])
+def test_qe_lazy_maximum_only_moves_rounding(orc, sm):
+    """Raising the reference maximum only when a tile exceeds it by more than tau (log2 units)
+    leaves the normalized result unchanged up to the fp16 rounding of P: against the exact running
+    maximum the outputs agree to fp16-rounding noise, the LSE to fp32 rounding.  sm_scale = 0.6
+    makes the scores peaked enough that p reaches 2^tau."""
+    inp = make_inputs(1, 2, 300, 900, 128, seed=16)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    a = orc.run_qe(Qb, Kb, Vb, BN=64, tau=0.0, sm_scale=sm)
+    b = orc.run_qe(Qb, Kb, Vb, BN=64, tau=8.0, sm_scale=sm)
+    assert _rel_l1(b.o32, a.o32) < 1e-3
+    np.testing.assert_allclose(b.lse, a.lse, atol=2e-5)
+    eo, _ = orc.attn_ex(Qb, Kb, Vb, sm_scale=sm)
+    assert abs(_rel_l1(b.o32, eo) - _rel_l1(a.o32, eo)) < 1e-3
+    # with tau = 0 the emulation is the exact running maximum: identical to tau = 1e-30
+    c = orc.run_qe(Qb, Kb, Vb, BN=64, tau=1e-30, sm_scale=sm)
+    assert np.array_equal(c.obf, a.obf)
