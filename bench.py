@@ -10,7 +10,7 @@ sage_attn_fwd_prepared (mask classification if any, attention with LSE).
 Prints one JSON line.  ``value`` is attention TOPS = 4*B*H*Nq*Nk*d / (time per step), halved for
 causal, over the whole step.  ``roofline`` reports the attention kernel alone: its algorithmic
 ops per launch over its average duration, measured with HIP events recorded on the stream the
-kernel runs on, against the dense INT8 MFMA peak.  ``cpu_baseline`` times the CPU oracle (the
+kernel runs on, against the MFMA peak of its own dtypes (INT8 for QK^T, FP16 or FP8 for PV).  ``cpu_baseline`` times the CPU oracle (the
 plain reference implementation used by the tests) on a bounded sample of the same workload.
 """
 
@@ -28,7 +28,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention TOPS (4·B·H·N²·d/t) and % of dense INT8 MFMA peak, 1×MI355X"
-INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA (datasheet, no sparsity)
+INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA (datasheet, no sparsity); FP8 is the same
+FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 MFMA
+
+
+def mfma_peak(pv: str) -> float:
+    """MFMA ceiling of the attention kernel for its own dtypes: half its counted ops are INT8 QK^T,
+    half are PV in FP16 (or FP8), so the ceiling is the harmonic combination of the two peaks."""
+    pv_peak = FP16_PEAK_TOPS if pv == "fp16" else INT8_PEAK_TOPS
+    return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
 KERNEL_SOURCES = ["quantized_attention_quantize_amd/csrc/sage_attn.hip",
                   "quantized_attention_quantize_amd/csrc/sage_device.h"]
 
@@ -54,30 +62,38 @@ def traffic_from_profile(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, rows_target: int):
-    """The oracle (never tuned) on one head of the workload: K mean, quantization and V preparation
-    of that head, then the quantized emulation for `rows_target` query rows of it."""
+def cpu_baseline(w, work_target: float, tau: float):
+    """The oracle (never tuned) on a bounded sample of the workload: whole heads (B=1) of the same
+    shape and input recipe -- K mean, INT8 quantization and V preparation of those heads, then the
+    quantized emulation of evenly spaced query rows -- sized to about `work_target` row x key
+    pairs (~15 s on 16 host cores at the default)."""
+    import math
+
     import numpy as np
 
     import oracle
     from quantized_attention_quantize_amd.synthetic import make_inputs
 
     oracle.build(force=False)
-    inp = make_inputs(1, 1, w.Nq, w.Nk, w.d, w.sigma, seed=0, mask=w.mask)
+    heads = max(1, min(w.B * w.H, math.ceil(work_target / (w.Nq * w.Nk))))
+    per_head = max(1, min(w.Nq, int(work_target / (heads * w.Nk))))
+    inp = make_inputs(1, heads, w.Nq, w.Nk, w.d, w.sigma, seed=0, mask=w.mask)
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
-    rows = np.linspace(0, w.Nq - 1, min(rows_target, w.Nq)).astype(np.int64)
+    local = np.linspace(0, w.Nq - 1, per_head).astype(np.int64)
+    rows = np.concatenate([h * w.Nq + local for h in range(heads)])
     t0 = time.perf_counter()
     qk = oracle.quant_qk(Qb, Kb)
     vh, vs = oracle.prep_v(Vb, w.pv)
-    oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, rows=rows)
+    oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, tau=tau, rows=rows)
     dt = time.perf_counter() - t0
     if w.causal:
-        ops = float(sum(4.0 * (int(i) + 1) * w.d for i in rows))
+        ops = heads * float(sum(4.0 * (int(i) + 1) * w.d for i in local))
     else:  # the mask workload counts formula ops too, as the GPU metric does
         ops = 4.0 * rows.size * w.Nk * w.d
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"1 head (B=1,H=1) of {w.name}: K mean + INT8 quantization + V prep of the head, quantized "
-                      f"emulation of {rows.size} evenly spaced query rows x {w.Nk} keys; {dt:.2f} s"}
+            "sample": f"{heads} head(s) (B=1) of {w.name}: K mean + INT8 quantization + V prep of the heads, "
+                      f"quantized emulation of {per_head} evenly spaced query rows per head x {w.Nk} keys; "
+                      f"{dt:.2f} s"}
 
 
 def main():
@@ -86,7 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n8k")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows in the CPU-baseline sample")
+    ap.add_argument("--cpu-work", type=float, default=2.7e8,
+                    help="query-row x key pairs in the CPU-baseline sample (oracle on the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -174,12 +191,15 @@ def main():
                    "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
                    "gpu_ms_per_step": round(gpu_ms_step, 4)},
         "roofline": {"kernel": "k_attn_fwd", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                     "peak": round(mfma_peak(w.pv), 1), "unit": "TOPS", "frac": round(achieved / mfma_peak(w.pv), 4),
+                     "peak_basis": "dense MFMA: INT8 5000 TOPS for QK^T, " +
+                                   ("FP16 2500 TFLOP/s" if w.pv == "fp16" else "FP8 5000 TFLOP/s") +
+                                   " for PV, each half of the counted ops",
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
                      "min_ms": round(attn_ms[0], 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv))
     print(json.dumps(line), flush=True)
 
 

@@ -84,6 +84,12 @@ int64_t sage_pad_tokens(int64_t n);
  * tile, which fixes where P is rounded).  Host only. */
 int sage_block_n(sage_pv_dtype pv);
 
+/* Lazy-maximum threshold of the online softmax, in log2 units: sage_attn_fwd moves a row's
+ * reference maximum only when a tile's maximum exceeds it by more than this (0 = the exact running
+ * maximum).  The normalized result does not depend on it; only the point at which P is rounded
+ * does.  8 for SAGE_PV_FP16 (P <= 256 fits fp16), 0 for SAGE_PV_FP8_E4M3.  Host only. */
+double sage_softmax_tau(sage_pv_dtype pv);
+
 /* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean).  Host only. */
 size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d);
 
@@ -139,9 +145,10 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled, unsmoothed
  *        scores (lse_corr added back), for merging partial results ("return_lse" on the
  *        sageattn section and on "Utilize SageAttention for Distributed Inference").
- * The online softmax runs over sage_block_n() keys per tile in increasing key order with an exact
- * running maximum; P is rounded to fp16 (or e4m3 of 448*p) against that running maximum; the
- * denominator sums the unrounded fp32 p; O and l accumulate in fp32.  Keys j >= Nk are masked
+ * The online softmax runs over sage_block_n() keys per tile in increasing key order; a row's
+ * reference maximum moves when a tile's maximum exceeds it by more than sage_softmax_tau() (log2
+ * units); P is rounded to fp16 (or e4m3 of 448*p) against the reference maximum; the denominator
+ * sums P as rounded (fp16) or the unrounded fp32 448*p (e4m3); O and l accumulate in fp32.  Keys j >= Nk are masked
  * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
  * gets O = 0 and LSE = -inf.
  * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, mask_h not

@@ -18,4 +18,5 @@ from .api import (  # noqa: F401
     prepare_v,
     quantize_qk,
     sageattn,
+    softmax_tau,
 )

@@ -78,7 +78,7 @@ size_t prep_ws_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype 
   return pv == SAGE_PV_FP8_E4M3 ? align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * 4) : 0;
 }
 size_t mask_ws_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h) {
-  return mask_h > 0 ? align256((size_t)(B * mask_h * cdiv(Nq, kTileRows) * cdiv(Nk, kTileKeys))) : 0;
+  return mask_h > 0 ? align256((size_t)(B * mask_h * cdiv(Nq, kTileRows) * cdiv(Nk, kTileKeys)) * sizeof(int)) : 0;
 }
 
 // sage_attn_fwd workspace: [prepared V | fp8 V scale | prepare-V scratch | mask tile states]
@@ -129,6 +129,8 @@ int sage_block_n(sage_pv_dtype pv) {
   (void)pv;
   return (int)kTileKeys;
 }
+
+double sage_softmax_tau(sage_pv_dtype pv) { return kSoftmaxTau[pv == SAGE_PV_FP8_E4M3 ? 1 : 0]; }
 
 size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d) {
   if (B <= 0 || H <= 0 || Nk <= 0 || d <= 0) return 0;
@@ -249,7 +251,7 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
 sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
                               const uint8_t* mask, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
                               int64_t mask_stride_q, int causal, float sm_scale, void* out, int64_t out_stride_b,
-                              int64_t out_stride_h, int64_t out_stride_n, float* lse, uint8_t* mtiles,
+                              int64_t out_stride_h, int64_t out_stride_n, float* lse, int* mtiles,
                               hipStream_t st) {
   sage_status s;
   AttnArgs a;
@@ -278,6 +280,8 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
     a.m_sq = mask_stride_q;
     a.mtiles = mtiles;
     a.Hm = mh;
+    a.mask_vec4 = ((uintptr_t)mask % 4 == 0) && (mask_stride_b % 4 == 0) && (mask_stride_h % 4 == 0) &&
+                  (mask_stride_q % 4 == 0);
   }
   a.q8 = qk->q8;
   a.k8 = qk->k8;
@@ -338,7 +342,7 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
   if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st)) != SAGE_OK) return s;
   return enqueue_attention(qk, ws + L.vt, vscale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
                            sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
-                           reinterpret_cast<uint8_t*>(ws + L.mtiles), st);
+                           reinterpret_cast<int*>(ws + L.mtiles), st);
 }
 
 sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
@@ -359,7 +363,7 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
   if ((s = check_device()) != SAGE_OK) return s;
   return enqueue_attention(qk, v_t, v_scale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
                            sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
-                           static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+                           static_cast<int*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, int64_t row0, int64_t nrows,
@@ -375,6 +379,7 @@ sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, i
   const int64_t bh = b * qk->H + h;
   a.q8h = qk->q8 + bh * qk->Nq_pad * qk->d;
   a.k8h = qk->k8 + bh * qk->Nk_pad * qk->d;
+  a.Nk_pad = qk->Nk_pad;
   a.row0 = row0;
   a.nrows = nrows;
   a.col0 = col0;

@@ -9,8 +9,10 @@
 // "flashinfer.nvfp4_attention_sm120_fwd", parameter unpadded_k_len).
 //
 // Design (MI355X / CDNA4):
-//  * One workgroup = 8 waves = 256 query rows of one (b,h); each wave owns 32 rows.  Two waves
-//    share a SIMD, so one wave's MFMAs overlap the other's softmax VALU work.
+//  * One workgroup = 4 waves = 256 query rows of one (b,h), one wave per SIMD; each wave owns 64
+//    rows as two 32-row MFMA blocks that share every K and V fragment read from LDS.  Inside a
+//    wave the key loop is software-pipelined (QK of the next tile, softmax of this tile and PV of
+//    the previous tile are interleaved), so MFMA and VALU work of one wave overlap.
 //  * S^T = K8 . Q8^T on v_mfma_i32_32x32x32_i8: the K tile (A operand) comes from LDS, the
 //    wave's Q8 rows (B operand) stay in registers for the whole key loop.  In the 32x32 output
 //    layout each lane holds one query row and 16 of every 32 keys, so the row max and row sum are
@@ -19,18 +21,22 @@
 //    for e4m3): P goes from the QK accumulator registers straight into the B operand.  The
 //    prepared V is stored transposed with its keys permuted to match that register layout, so
 //    each A-operand fetch is one 16-byte LDS read.
-//  * K and V tiles (64 keys) are double-buffered in LDS through registers with one barrier per
-//    tile; 16-byte chunks are XOR-swizzled so ds_read_b128 phases are bank-conflict free.
+//  * K and V tiles (64 keys) stream into a four-stage LDS ring by direct buffer-to-LDS loads issued
+//    two tiles ahead, one barrier per tile; 16-byte chunks are XOR-swizzled so ds_read_b128
+//    phases are bank-conflict free.
 //  * Workgroup ids are remapped so each XCD (own L2) works through whole heads; causal q-tiles
 //    run longest first.  Fully masked key tiles (causal or mask classification) are skipped;
 //    only diagonal, tail and mixed-mask tiles evaluate per-element predicates.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "sage_device.h"
 #include "sage_launch.h"
 
 namespace sage {
 
+constexpr int kWaves = kBlockM / 32;  // waves per attention workgroup, 32 query rows each
 constexpr int kAttnThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -47,59 +53,93 @@ struct TileGeom {
   static constexpr int V_CPR = V_ROW / 16;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int V_ESZ = PV == 0 ? 2 : 1;
+  static constexpr int K_SEGS_ALL = K_BYTES / 1024;
+  static constexpr int V_SEGS_ALL = V_BYTES / 1024;
 };
 
-// Cooperative global -> register -> LDS staging of one key tile by NT threads.
-template <int D, int PV, int NT>
+// Direct global -> LDS staging of key tiles with buffer loads (buffer_load_dwordx4 ... lds: lane l
+// of a wave writes the 16 bytes at LDS base + 16*l).  Each wave fills whole 1 KiB segments of the
+// tile buffer; a lane fetches the global chunk that belongs at its swizzled LDS position.  The
+// per-head tensors are addressed through buffer resources (SGPRs).  The swizzle depends on the row
+// modulo 16 only, so a lane's offset inside a segment depends on the segment's parity alone: one
+// per-lane offset register serves every segment of a wave, and the segment and tile offsets are
+// wave-uniform (SGPR soffset).
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer resource word 3: 32-bit data format
+
+// Offset (relative to its segment's first row) of the global chunk that lane `lane` stores, for a
+// segment of parity `par` of a buffer with ROW_BYTES-byte LDS rows and global row stride gstride.
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_lane_source(int par, int lane, int gstride) {
+  constexpr int CPR = ROW_BYTES / 16, RPS = 1024 / ROW_BYTES;
+  const int r = lane / CPR;                // row inside the segment
+  const int row16 = (r + RPS * par) & 15;  // row of the buffer modulo 16
+  const int lc = (lane % CPR) ^ (ROW_BYTES == 128 ? swz128(row16) : swz64(row16));
+  return r * gstride + lc * 16;
+}
+
+template <int D, int PV, int NW>
 struct Stager {
   using G = TileGeom<D, PV>;
-  static constexpr int KN = (G::K_CHUNKS + NT - 1) / NT;
-  static constexpr int VN = (G::V_CHUNKS + NT - 1) / NT;
-  v4i kreg[KN];
-  v4i vreg[VN];
+  static constexpr int K_SEGS = G::K_BYTES / 1024;
+  static constexpr int V_SEGS = G::V_BYTES / 1024;
+  static constexpr int KN = (K_SEGS + NW - 1) / NW;
+  static constexpr int VN = (V_SEGS + NW - 1) / NW;
+  static constexpr int NP = NW % 2 == 0 ? 1 : 2;  // segment parities one wave sees
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  int kx[NP], vx[NP];  // per-lane source offsets by segment parity
+  int wu;              // wave index (SGPR)
+  int vseg;            // global bytes between V segments (SGPR)
 
-  __device__ __forceinline__ void load_k(const int8_t* k8h, int kt, int tid) {
+  // k8h: K8 rows of one head ([Nk_pad][D] bytes); vth: prepared V of one head ([D][Nk_pad])
+  __device__ __forceinline__ void init(const int8_t* k8h, const uint8_t* vth, int64_t Nk_pad, int wave, int lane) {
+    wu = __builtin_amdgcn_readfirstlane(wave);
+    const int vrow = (int)Nk_pad * G::V_ESZ;
+    vseg = (1024 / G::V_ROW) * vrow;
+    krs = __builtin_amdgcn_make_buffer_rsrc((void*)k8h, (short)0, (int)(Nk_pad * D), kBufferWord3);
+    vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vth, (short)0, vrow * D, kBufferWord3);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int par = NP == 1 ? (wu & 1) : p;
+      kx[p] = lds_lane_source<D>(par, lane, D);
+      vx[p] = lds_lane_source<G::V_ROW>(par, lane, vrow);
+    }
+  }
+  __device__ __forceinline__ int px(const int (&x)[NP], int i) const { return NP == 1 ? x[0] : x[(i * NW) & 1]; }
+  // K tile kt into the LDS buffer sK
+  __device__ __forceinline__ void load_k(int kt, char* sK) const {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
-      int c = tid + i * NT;
-      if (c < G::K_CHUNKS) {
-        int row = c / G::K_CPR, ch = c % G::K_CPR;
-        kreg[i] = *reinterpret_cast<const v4i*>(k8h + ((int64_t)kt * kBlockN + row) * D + ch * 16);
-      }
+      const int seg = wu + i * NW;
+      if (K_SEGS % NW == 0 || seg < K_SEGS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(sK + seg * 1024), 16, px(kx, i),
+                                                 kt * kBlockN * D + seg * 1024, 0, 0);
     }
   }
-  __device__ __forceinline__ void store_k(char* sK, int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      int c = tid + i * NT;
-      if (c < G::K_CHUNKS) {
-        int row = c / G::K_CPR, ch = c % G::K_CPR;
-        *reinterpret_cast<v4i*>(sK + lds_chunk_offset<D>(row, ch)) = kreg[i];
-      }
-    }
-  }
-  __device__ __forceinline__ void load_v(const uint8_t* vth, int64_t Nk_pad, int kt, int tid) {
+  // V tile kt (columns [64kt, 64kt+64) of every channel row) into sV
+  __device__ __forceinline__ void load_v(int kt, char* sV) const {
 #pragma unroll
     for (int i = 0; i < VN; ++i) {
-      int c = tid + i * NT;
-      if (c < G::V_CHUNKS) {
-        int row = c / G::V_CPR, ch = c % G::V_CPR;
-        vreg[i] = *reinterpret_cast<const v4i*>(vth + ((int64_t)row * Nk_pad + (int64_t)kt * kBlockN) * G::V_ESZ +
-                                                ch * 16);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_v(char* sV, int tid) {
-#pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      int c = tid + i * NT;
-      if (c < G::V_CHUNKS) {
-        int row = c / G::V_CPR, ch = c % G::V_CPR;
-        *reinterpret_cast<v4i*>(sV + lds_chunk_offset<G::V_ROW>(row, ch)) = vreg[i];
-      }
+      const int seg = wu + i * NW;
+      if (V_SEGS % NW == 0 || seg < V_SEGS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(sV + seg * 1024), 16, px(vx, i),
+                                                 kt * kBlockN * G::V_ESZ + seg * vseg, 0, 0);
     }
   }
 };
+
+// s_waitcnt with vmcnt = N (other counters untouched): all but this wave's N most recent vector
+// memory operations -- here the direct-to-LDS loads -- have completed
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+}
+// loads one wave issues for a tile buffer of SEGS 1 KiB segments shared by NW waves
+template <int SEGS, int NW>
+__device__ __forceinline__ int segs_of_wave(int w) {
+  return SEGS / NW + (w < SEGS % NW ? 1 : 0);
+}
 
 // B operand of S^T = K Q^T for one wave: lane (lr, g) holds bytes [32*cs + 16*g, +16) of its row.
 template <int D>
@@ -134,11 +174,344 @@ __device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32],
 
 __device__ __forceinline__ int key_of(int kb, int r, int g) { return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3); }
 
+// Wave-uniform read-only scalars (k-scales, mask-tile states) are read through the constant
+// address space so they become scalar loads: a vector load here would be counted by vmcnt, whose
+// in-order wait would also drain the in-flight direct-to-LDS prefetches.
+typedef __attribute__((address_space(4))) const float cfloat_t;
+typedef __attribute__((address_space(4))) const int cint_t;
+__device__ __forceinline__ float scalar_ld(const float* p, int i) { return ((cfloat_t*)p)[i]; }
+__device__ __forceinline__ int scalar_ld(const int* p, int i) { return ((cint_t*)p)[i]; }
+
+// P^T fragments of one tile in the PV MFMA's B-operand layout (one 32-row block).
+template <int PV>
+struct PFrag;
+template <>
+struct PFrag<0> {  // fp16: 4 steps of 16 keys, 8 halves per lane each
+  v8h s[4];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[i][j] = (_Float16)0.f;
+  }
+};
+template <>
+struct PFrag<1> {  // e4m3: 64 keys, 32 bytes per lane
+  v8i b;
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = 0;
+  }
+};
+
+// Per-lane LDS address bases.  The swizzles depend on the row modulo 16 only, so the fragment at
+// row 32*k + lr of a tile lies at  (per-lane base for its chunk) + k * 32 * ROW_BYTES.  Lane
+// (lr, g) reads chunks 2*c + g of 128-byte rows (K with d = 128, FP16 V), chunks 2*c + g of
+// 64-byte rows (K with d = 64) and chunks 2*g + h of 64-byte rows (e4m3 V); every base is a
+// register of its own, so no fragment address indexes an array by lane.
+struct LaneBases {
+  int b128[4];  // 128-byte rows, chunk 2*c + g
+  int k64[2];   // 64-byte rows, chunk 2*c + g
+  int v64[2];   // 64-byte rows, chunk 2*g + h
+  __device__ __forceinline__ void init(int lr, int g) {
+    const int x = g ^ swz128(lr);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b128[c] = lr * 128 + ((x ^ (2 * c)) << 4);
+    const int y = swz64(lr);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      k64[c] = lr * 64 + (((2 * c + g) ^ y) << 4);
+      v64[c] = lr * 64 + (((2 * g + c) ^ y) << 4);
+    }
+  }
+};
+// fragment at row 32*k + lr, chunk 2*c + g of a 128-byte-row tile starting at base
+__device__ __forceinline__ v4i frag128(const char* base, const LaneBases& lb, int k, int c) {
+  return *reinterpret_cast<const v4i*>(base + lb.b128[c] + 4096 * k);
+}
+// fragment at row 32*k + lr of a 64-byte-row tile: chunk 2*c + g (K) or 2*g + c (e4m3 V)
+__device__ __forceinline__ v4i frag64k(const char* base, const LaneBases& lb, int k, int c) {
+  return *reinterpret_cast<const v4i*>(base + lb.k64[c] + 2048 * k);
+}
+__device__ __forceinline__ v4i frag64v(const char* base, const LaneBases& lb, int k, int c) {
+  return *reinterpret_cast<const v4i*>(base + lb.v64[c] + 2048 * k);
+}
+
+// Softmax state of a wave's rows.  Lane (lr, g) holds row lr; both halves of the wave carry the
+// same reference maximum, and each holds the partial denominator of its half of the keys.
+struct RowState {
+  float m;      // reference maximum (log2 units) of the newest scored tile
+  float pm;     // exponent offset of the tile being exponentiated (m, or m - log2(448) for e4m3 P)
+  float l;      // partial denominator
+  float alpha;  // 2^(previous m - m) for the tile being exponentiated; O takes it after the
+                // previous tile's PV
+};
+
+// Scores of a tile that fall outside the visible region become INT_MIN: key jr of the tile is
+// visible iff jr <= lim and (mtile == nullptr or mtile[jr] != 0).
+__device__ __forceinline__ void mask_scores(v16i (&acc)[2], int g, int lim, const uint8_t* mtile, bool mvec4) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int j4 = kb * 32 + rq * 8 + g * 4;
+      unsigned mb = 0x01010101u;
+      if (mtile) {
+        if (mvec4 && j4 + 3 <= lim) {
+          mb = *reinterpret_cast<const unsigned*>(mtile + j4);
+        } else {
+          mb = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j4 + e <= lim) mb |= (unsigned)mtile[j4 + e] << (8 * e);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = (j4 + e <= lim) && ((mb >> (8 * e)) & 0xffu) != 0;
+        if (!valid) acc[kb][rq * 4 + e] = INT_MIN;
+      }
+    }
+}
+
+// Row maximum of a tile's scores in four independent chains of eight: piece p (0..7) advances
+// chain p/2 by two max3/max steps.
+__device__ __forceinline__ int score_at(const v16i (&acc)[2], int i) { return acc[i >> 4][i & 15]; }
+__device__ __forceinline__ void max_piece(const v16i (&acc)[2], int (&ch)[4], int p) {
+  const int c = p >> 1, e = 8 * c;
+  if ((p & 1) == 0) {
+    ch[c] = max(max(score_at(acc, e), score_at(acc, e + 1)), score_at(acc, e + 2));
+    ch[c] = max(max(ch[c], score_at(acc, e + 3)), score_at(acc, e + 4));
+  } else {
+    ch[c] = max(max(ch[c], score_at(acc, e + 5)), score_at(acc, e + 6));
+    ch[c] = max(ch[c], score_at(acc, e + 7));
+  }
+}
+// Combines the chains across the wave's halves and moves the reference maximum (lazy by
+// kSoftmaxTau[PV] log2 units).  Returns 2^(m_old - m_new); the new exponent offset goes to pm_new.
+template <int PV, bool MASKED>
+__device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowState& rs, float& pm_new) {
+  constexpr float kTau = kSoftmaxTau[PV];
+  int im = max(max(ch[0], ch[1]), max(ch[2], ch[3]));
+  const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);  // lanes l and l ^ 32
+  im = max((int)sw[0], (int)sw[1]);
+  float mt;
+  if constexpr (MASKED)
+    mt = im == INT_MIN ? -INFINITY : (float)im * c;
+  else
+    mt = (float)im * c;
+  const float m_new = (mt > rs.m + kTau) ? mt : rs.m;
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(rs.m - m_use);
+  rs.m = m_new;
+  pm_new = PV == 1 ? m_use - kLog2_448 : m_use;  // the e4m3 path carries P as 448 * p
+  return alpha;
+}
+
+// MFMA operand geometry of one tile step.
+template <int D, int PV>
+struct StepGeom {
+  static constexpr int NB = D / 32;                   // 32-wide blocks of the head dimension
+  static constexpr int NQ = 2 * NB;                   // QK MFMAs: key block q / NB, chunk step q % NB
+  static constexpr int NPV = PV == 0 ? 4 * NB : NB;  // PV MFMAs
+  static constexpr int NM = NPV + NQ;                 // MFMA k < NPV is PV MFMA k, else QK MFMA k - NPV
+  static constexpr int LA = PV == 0 ? 2 : 1;          // operands read from LDS ahead of the MFMA stream
+  using VFrag = typename std::conditional<PV == 0, v4i, v8i>::type;
+};
+
+// A operand of PV MFMA j from the V tile at sV: fp16 -- channels 32*(j % NB) + lr, keys of step
+// j / NB; e4m3 -- channel block j, the lane's 32 keys (two 16-byte chunks)
+template <int D, int PV>
+__device__ __forceinline__ typename StepGeom<D, PV>::VFrag vfrag(const char* sV, const LaneBases& lb, int g, int j) {
+  constexpr int NB = D / 32;
+  if constexpr (PV == 0) {
+    return frag128(sV, lb, j % NB, j / NB);
+  } else {
+    const v4i v0 = frag64v(sV, lb, j, 0), v1 = frag64v(sV, lb, j, 1);
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// One software-pipelined tile step of a wave.  At step n the tile T[n] has been scored (acc) and
+// the row maxima of its first key block are in ch[0..1]; T[n-1]'s probabilities are in P; T[n+1]
+// is to be scored.  The step interleaves three independent streams:
+//   MFMA: PV of T[n-1] (P, V from sVp; its first LA operands arrive in vpre) into O first, then QK
+//         of T[n+1] (K from sKn) into acc;
+//   VALU: the rest of T[n]'s row maxima and its reference maximum (first slots), the
+//         exponentials of T[n] into P -- each group once the MFMAs reading its registers have been
+//         issued -- with the row sums, and the row maxima of T[n+1]'s first key block.
+// Ordered this way, P and the scores are overwritten in place and no VALU work waits for a
+// just-issued MFMA.  Every MFMA is issued with a slice of VALU work and the LDS reads LA operands
+// ahead; sched_barrier fences keep that order.  At the end vpre receives the first operands of the
+// next step's PV (V tile sVn).  With SLOW, T[n]'s scores may be masked (INT_MIN) and T[n+1] is
+// masked by lim / mtile (mask_scores).  Returns 2^(m_{n-1} - m_n), the factor O takes after the
+// PV of T[n-1].
+template <int D, int PV, bool SLOW>
+__device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<PV>& P,
+                                           typename StepGeom<D, PV>::VFrag (&vpre)[StepGeom<D, PV>::LA],
+                                           const char* sKn, const char* sVp, const char* sVn, const v4i (&qf)[D / 32],
+                                           v16f (&o)[D / 32], float c_cur, RowState& rs, const LaneBases& lb, int g,
+                                           int lim, const uint8_t* mtile, bool mvec4) {
+  using SG = StepGeom<D, PV>;
+  constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = SG::NM, LA = SG::LA;
+  constexpr int NG = PV == 0 ? 16 : 8;  // exponential groups of 2 (fp16) or 4 (e4m3) scores
+  constexpr int FIN = 1;                // slot of the reference-maximum update (pieces 4-7 in slot 0)
+  using VFrag = typename SG::VFrag;
+
+  // A operand of QK MFMA q: K rows 32*kb + lr, chunk 2*cs + g
+  auto kfrag = [&](int q) -> v4i {
+    const int kb = q / NB, cs = q % NB;
+    if constexpr (D == 128)
+      return frag128(sKn, lb, kb, cs);
+    else
+      return frag64k(sKn, lb, kb, cs);
+  };
+  // Slot of exponential group gi, after the reference maximum.  FP16: after the PV MFMAs that
+  // read the P registers it overwrites, spread so that each key block's scores are consumed
+  // before the QK of T[n+1] overwrites them.  e4m3: every PV MFMA reads all of P, so P is written
+  // into fresh registers, spread over the slots before the second key block's QK.
+  auto exp_slot = [](int gi) {
+    if (PV == 1) return FIN + 1 + gi * (NPV + NB - FIN - 1) / NG;
+    const int first = ((gi >> 2) + 1) * NB > FIN + 1 ? ((gi >> 2) + 1) * NB : FIN + 1;
+    const int s = NB + gi * NPV / NG;
+    return s > first ? s : first;
+  };
+  // slot of row-max piece p < 4 of T[n+1] (key block 0): two MFMAs after that block's last QK
+  auto max_slot = [](int p) { return NPV + NB + 1 + p / 2 < NM - 1 ? NPV + NB + 1 + p / 2 : NM - 1; };
+
+  const v16i sc[2] = {acc[0], acc[1]};  // scores of T[n]
+  const PFrag<PV> pin = P;              // probabilities of T[n-1]
+  VFrag vf[NPV];
+  v4i kf[NQ];
+#pragma unroll
+  for (int r = 0; r < LA; ++r) vf[r] = vpre[r];
+  auto read = [&](int r) {  // operand r of the MFMA stream
+    if (r < NPV)
+      vf[r] = vfrag<D, PV>(sVp, lb, g, r);
+    else
+      kf[r - NPV] = kfrag(r - NPV);
+  };
+  float psum = 0.f, alpha = 1.f;
+  const v2h ones = {(_Float16)1.f, (_Float16)1.f};
+
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    if (k + LA < NM) read(k + LA);  // LDS reads for a later MFMA
+    if (k < NPV) {
+      if constexpr (PV == 0)
+        o[k % NB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, vf[k]), pin.s[k / NB], o[k % NB], 0,
+                                                          0, 0);
+      else
+        o[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[k], pin.b, o[k], 0, 0, 0, 127, 0, 127);
+    } else {
+      const int q = k - NPV, kb = q / NB, cs = q % NB;
+      if (cs == 0) {
+        const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+        acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[q], qf[cs], z, 0, 0, 0);
+      } else {
+        acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[q], qf[cs], acc[kb], 0, 0, 0);
+      }
+    }
+    // T[n]'s row maxima over its second key block, then its reference maximum
+    if (k == 0) {
+#pragma unroll
+      for (int p = 4; p < 8; ++p) max_piece(sc, ch, p);
+    }
+    if (k == FIN) {
+      float pm_new;
+      alpha = finish_max<PV, SLOW>(ch, c_cur, rs, pm_new);
+      rs.pm = pm_new;
+    }
+    // exponentials of T[n] assigned to slot k
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (exp_slot(gi) != k) continue;
+      constexpr int GS = 32 / NG;
+      float x[GS];
+#pragma unroll
+      for (int e = 0; e < GS; ++e) {
+        const int idx = gi * GS + e, kb = idx >> 4, r = idx & 15;
+        float t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[kb][r], c_cur, -rs.pm));
+        if constexpr (SLOW) t = sc[kb][r] == INT_MIN ? 0.f : t;
+        x[e] = t;
+      }
+      if constexpr (PV == 0) {
+        const int idx = gi * 2, kb = idx >> 4, r = idx & 15;
+        const int s2 = kb * 2 + (r >> 3), jj = (r & 7) >> 1;
+        const v2h hh = __builtin_convertvector((v2f{x[0], x[1]}), v2h);  // round to nearest even
+        P.s[s2][2 * jj] = hh[0];
+        P.s[s2][2 * jj + 1] = hh[1];
+        psum = __builtin_amdgcn_fdot2(hh, ones, psum, false);  // the row sum takes the rounded P
+      } else {
+        psum += (x[0] + x[1]) + (x[2] + x[3]);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        P.b[gi] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+      }
+    }
+    // row maxima of T[n+1]'s first key block (a tile that needs masking takes them after the slots)
+    if constexpr (!SLOW) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (max_slot(p) == k) max_piece(acc, ch, p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (SLOW) {
+    mask_scores(acc, g, lim, mtile, mvec4);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) max_piece(acc, ch, p);
+  }
+  rs.l = alpha * rs.l + psum;
+#pragma unroll
+  for (int r = 0; r < LA; ++r) vpre[r] = vfrag<D, PV>(sVn, lb, g, r);
+  return alpha;
+}
+
+// O^T += V^T P^T for one tile (V tile from LDS); used for the last tile after the loop.
+template <int D, int PV>
+__device__ __forceinline__ void pv_tile(const char* sV, const PFrag<PV>& pf, const LaneBases& lb, int g,
+                                        v16f (&o)[D / 32]) {
+  if constexpr (PV == 0) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, frag128(sV, lb, db, s)), pf.s[s], o[db],
+                                                      0, 0, 0);
+  } else {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const v4i v0 = frag64v(sV, lb, db, 0), v1 = frag64v(sV, lb, db, 1);
+      const v8i vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf.b, o[db], 0, 0, 0, 127, 0, 127);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+}
+
+// Main loop, software-pipelined inside each wave (see tile_step).  One workgroup = 8 waves = 256
+// query rows; wave w owns rows 32w..32w+31.  LDS holds a four-stage ring of K tiles and one of V
+// tiles; processed tiles are numbered T[0], T[1], ...: K of T[i] lives in kslot i%4, V of T[i] in
+// vslot i%4.  Step n consumes K of T[n+1] and V of T[n-1], issues the loads of V of T[n+2] and K
+// of T[n+3] into slots freed two steps earlier, and waits at its end only for the loads of the
+// previous step.  The loop is unrolled four times so every slot is a compile-time offset.  One
+// barrier per tile.
 template <int D, int PV>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   using G = TileGeom<D, PV>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, g = lane >> 5;
+  constexpr int kNS = 4;
+  __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
+  char* const kring = smem;
+  char* const vring = smem + kNS * G::K_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int w = tid >> 6;
 
   // workgroup -> (head, q-tile); consecutive logical ids land on the same XCD
   const int total = gridDim.x, bid = blockIdx.x;
@@ -148,26 +521,26 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   int qt = L % a.nQT;
   if (a.causal) qt = a.nQT - 1 - qt;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const int64_t q0 = (int64_t)qt * kBlockM;
-  const int64_t r0w = q0 + (int64_t)w * kWaveRows;
-  const int64_t row = r0w + lr;
+  const int q0 = qt * kBlockM;
+  const int r0w = q0 + w * 32;  // first row of this wave (token counts are < 2^30)
+  const int row = r0w + lr;
+  const int nk = (int)a.Nk, nq = (int)a.Nq;
 
   int kt_end = a.nKT;
   if (a.causal) {
-    int64_t lim = (q0 + kBlockM + kBlockN - 1) / kBlockN;
-    if (lim < kt_end) kt_end = (int)lim;
+    const int lim = (q0 + kBlockM + kBlockN - 1) / kBlockN;
+    if (lim < kt_end) kt_end = lim;
   }
-  const uint8_t* mt = a.mtiles ? a.mtiles + ((b * a.Hm + (a.Hm == 1 ? 0 : h)) * a.nQT + qt) * a.nKT : nullptr;
-  const uint8_t* mrow = nullptr;
-  if (a.mask && row < a.Nq) mrow = a.mask + b * a.m_sb + (a.Hm == 1 ? 0 : h) * a.m_sh + row * a.m_sq;
+  const int* mt = a.mtiles ? a.mtiles + ((b * a.Hm + (a.Hm == 1 ? 0 : h)) * a.nQT + qt) * a.nKT : nullptr;
+  const uint8_t* mrow =
+      (a.mask && row < nq) ? a.mask + b * a.m_sb + (a.Hm == 1 ? 0 : h) * a.m_sh + (int64_t)row * a.m_sq : nullptr;
 
   const int8_t* q8h = a.q8 + bh * a.Nq_pad * D;
   const int8_t* k8h = a.k8 + bh * a.Nk_pad * D;
   const uint8_t* vth = static_cast<const uint8_t*>(a.vt) + bh * D * a.Nk_pad * G::V_ESZ;
-  v4i qf[D / 32];
-  load_q_frags<D>(q8h, row, a.Nq_pad, g, qf);
-  const int qblk = (int)(r0w / kQuantBlock);
-  const float qsw = qblk < a.nbq ? a.qs[bh * a.nbq + qblk] : 0.f;
+  const int r0u = __builtin_amdgcn_readfirstlane(r0w);  // the same value, held in an SGPR
+  const int qblk = r0u / kQuantBlock;                   // a wave's rows lie in one quantization block
+  const float cq = qblk < a.nbq ? scalar_ld(a.qs + bh * a.nbq, qblk) : 0.f;
   const float* ksh = a.ks + bh * a.nbk;
 
   v16f o[D / 32];
@@ -175,150 +548,176 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_state = -INFINITY, l_lane = 0.f;
 
-  Stager<D, PV, kAttnThreads> st;
-  int kt = 0;
-  while (kt < kt_end && mt && mt[kt] == 0) ++kt;
-  if (kt < kt_end) {
-    st.load_k(k8h, kt, tid);
-    st.load_v(vth, a.Nk_pad, kt, tid);
-    st.store_k(smem, tid);
-    st.store_v(smem + G::K_BYTES, tid);
+  // The first step multiplies a zero P by the V slot of "T[-1]": clear it so uninitialized LDS
+  // (possibly NaN patterns) cannot leak in through 0 * NaN.
+  for (int i = tid; i < G::V_BYTES / 16; i += kAttnThreads)
+    *reinterpret_cast<v4i*>(vring + (kNS - 1) * G::V_BYTES + i * 16) = v4i{0, 0, 0, 0};
+
+  Stager<D, PV, kWaves> st;
+  st.init(k8h, vth, a.Nk_pad, w, lane);
+  auto dropped = [&](int t) { return mt != nullptr && scalar_ld(mt, t) == 0; };
+  auto next_tile = [&](int t) {
+    if (t >= kt_end) return kt_end;
+    ++t;
+    while (t < kt_end && dropped(t)) ++t;
+    return t;
+  };
+  int t0 = 0;
+  while (t0 < kt_end && dropped(t0)) ++t0;
+  const int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
+  const int tstand = t0 < kt_end ? t0 : 0;  // a valid tile to stand in for loads past the end
+  auto clampt = [&](int t) { return t < kt_end ? t : tstand; };
+  if (t0 < kt_end) {
+    st.load_k(t0, kring);
+    st.load_k(clampt(t1), kring + G::K_BYTES);
+    st.load_k(clampt(t2), kring + 2 * G::K_BYTES);
+    st.load_v(t0, vring);
+    st.load_v(clampt(t1), vring + G::V_BYTES);
   }
+  v4i qf[D / 32];
+  load_q_frags<D>(q8h, row, a.Nq_pad, g, qf);
+  __builtin_amdgcn_s_waitcnt(0);  // Q fragments and the prologue tiles resident
   __syncthreads();
-  int buf = 0;
-  while (kt < kt_end) {
-    int ktn = kt + 1;
-    while (ktn < kt_end && mt && mt[ktn] == 0) ++ktn;
-    if (ktn < kt_end) {
-      st.load_k(k8h, ktn, tid);
-      st.load_v(vth, a.Nk_pad, ktn, tid);
-    }
-    const char* sK = smem + buf * G::STAGE_BYTES;
-    const char* sV = sK + G::K_BYTES;
-    const int64_t j0 = (int64_t)kt * kBlockN;
-    const bool wave_skip = a.causal && j0 > r0w + kWaveRows - 1;
-    if (!wave_skip) {
-      const bool mixed = mt && mt[kt] == 2;
-      const bool partial = (j0 + kBlockN > a.Nk) || (a.causal && j0 + kBlockN - 1 > r0w) || mixed;
-      v16i acc[2];
-      qk_tile<D>(sK, qf, lr, g, acc);
-      const float c = ((qsw * ksh[kt]) * a.sm_scale) * kLog2e;
-      if (partial) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t j = j0 + key_of(kb, r, g);
-            bool valid = j < a.Nk;
-            if (a.causal) valid = valid && j <= row;
-            if (mixed && mrow && valid) valid = mrow[j] != 0;
-            if (!valid) acc[kb][r] = INT_MIN;
-          }
-      }
-      int imax = INT_MIN;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) imax = max(imax, acc[kb][r]);
-      imax = max(imax, __shfl_xor(imax, 32));
-      const float mt_ = imax == INT_MIN ? -INFINITY : (float)imax * c;
-      const float m_new = fmaxf(m_state, mt_);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_state - m_use);
-      const float pm = PV == 1 ? m_use - kLog2_448 : m_use;  // e4m3 path carries P as 448 * p
-      float p[2][16];
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)acc[kb][r], c, -pm));
-          if (partial) e = acc[kb][r] == INT_MIN ? 0.f : e;
-          p[kb][r] = e;
-          psum += e;
-        }
-      l_lane = alpha * l_lane + psum;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      m_state = m_new;
 
-      if constexpr (PV == 0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kb = s >> 1, rb = (s & 1) * 8;
-          v8h pf;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            v2f two = {p[kb][rb + 2 * jj], p[kb][rb + 2 * jj + 1]};
-            v2h hh = __builtin_convertvector(two, v2h);  // round to nearest even
-            pf[2 * jj] = hh[0];
-            pf[2 * jj + 1] = hh[1];
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            v8h vf = *reinterpret_cast<const v8h*>(sV + lds_chunk_offset<128>(db * 32 + lr, 2 * s + g));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
-          }
-        }
-      } else {
-        v8i pf;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int kb = q >> 2, r0 = (q & 3) * 4;
-          int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r0], p[kb][r0 + 1], 0, false);
-          pf[q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r0 + 2], p[kb][r0 + 3], lo, true);
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          v4i v0 = *reinterpret_cast<const v4i*>(sV + lds_chunk_offset<64>(db * 32 + lr, 2 * g));
-          v4i v1 = *reinterpret_cast<const v4i*>(sV + lds_chunk_offset<64>(db * 32 + lr, 2 * g + 1));
-          v8i vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 127, 0, 127);
-        }
-      }
+  // per-tile scale, and whether a tile needs per-element visibility (past the end, ragged tail,
+  // causal diagonal, mixed mask tile); lim / mtile describe the visible keys of such a tile
+  auto scale_of = [&](int t) { return t < kt_end ? ((cq * scalar_ld(ksh, t)) * a.sm_scale) * kLog2e : 0.f; };
+  auto partial = [&](int t) {
+    if (t >= kt_end) return true;
+    // The test runs on a vector-register copy of the tile index (v_mbcnt_lo with an empty mask
+    // adds 0): the compiler then keeps the masked/unmasked step choice as a per-lane branch, which
+    // it compiles without spills, and holds no row index in a vector register across the loop.
+    const int j0 = __builtin_amdgcn_mbcnt_lo(0u, t) * kBlockN;
+    return j0 + kBlockN > nk || (a.causal && j0 + kBlockN - 1 > r0u) || (mt != nullptr && scalar_ld(mt, t) == 2);
+  };
+  auto visible = [&](int t, int& lim, const uint8_t*& mtile) {
+    if (t >= kt_end) {
+      lim = -1;
+      mtile = nullptr;
+      return;
     }
-    if (ktn < kt_end) {
-      char* nK = smem + (buf ^ 1) * G::STAGE_BYTES;
-      st.store_k(nK, tid);
-      st.store_v(nK + G::K_BYTES, tid);
+    const int j0 = t * kBlockN;
+    lim = j0 + kBlockN > nk ? nk - j0 - 1 : kBlockN - 1;
+    if (a.causal) {
+      const int dr = row - j0;
+      lim = dr < lim ? (dr < -1 ? -1 : dr) : lim;
     }
-    __syncthreads();
-    buf ^= 1;
-    kt = ktn;
+    mtile = (mt != nullptr && scalar_ld(mt, t) == 2 && mrow) ? mrow + j0 : nullptr;
+  };
+
+  LaneBases lb;
+  lb.init(lr, g);
+  RowState rs;
+  rs.m = -INFINITY;
+  rs.pm = 0.f;
+  rs.l = 0.f;
+  v16i acc[2];
+  int ch[4];
+  PFrag<PV> P;
+  P.zero();
+  typename StepGeom<D, PV>::VFrag vpre[StepGeom<D, PV>::LA];
+  float c_cur = scale_of(t0);
+  bool part_cur = partial(t0);
+  {  // scores of T[0] and the row maxima of its first key block; the first PV operands
+    qk_tile<D>(kring, qf, lr, g, acc);
+    int lim;
+    const uint8_t* mtile;
+    visible(t0, lim, mtile);
+    if (part_cur) mask_scores(acc, g, lim, mtile, a.mask_vec4);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) max_piece(acc, ch, p);
+#pragma unroll
+    for (int r = 0; r < StepGeom<D, PV>::LA; ++r) vpre[r] = vfrag<D, PV>(vring + (kNS - 1) * G::V_BYTES, lb, g, r);
   }
+  // loads this wave issues per step (its share of one V and one K tile), for the vmcnt waits
+  const int nload = segs_of_wave<G::V_SEGS_ALL, kWaves>(w) + segs_of_wave<G::K_SEGS_ALL, kWaves>(w);
+
+  int n = 0;
+  int tc = t0, tn = t1, tnn = t2, tnnn = t3;  // T[n] .. T[n+3]
+  auto step = [&](auto slot) -> bool {
+    constexpr int Q = decltype(slot)::value;  // n % kNS
+    if (tc >= kt_end) return false;
+    __syncthreads();
+    st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
+    st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
+    const char* sVp = vring + ((Q + kNS - 1) % kNS) * G::V_BYTES;  // V of T[n-1]
+    const char* sVn = vring + Q * G::V_BYTES;                      // V of T[n]
+    const char* sKn = kring + ((Q + 1) % kNS) * G::K_BYTES;        // K of T[n+1]
+    const bool part_nxt = partial(tn);
+    float alpha;
+    if (part_cur || part_nxt) {
+      int lim;
+      const uint8_t* mtile;
+      visible(tn, lim, mtile);
+      alpha = tile_step<D, PV, true>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mtile,
+                                     a.mask_vec4);
+    } else {
+      alpha = tile_step<D, PV, false>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, kBlockN - 1, nullptr,
+                                      false);
+    }
+    // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare for the lazy FP16 maximum)
+    if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
+    c_cur = scale_of(tn);
+    part_cur = part_nxt;
+    // the loads of the previous steps must have landed before the next barrier
+    switch (nload) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 5: wait_vmcnt<5>(); break;
+      default: wait_vmcnt<6>(); break;
+    }
+    tc = tn;
+    tn = tnn;
+    tnn = tnnn;
+    tnnn = next_tile(tnnn);
+    ++n;
+    return true;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  while (step(I0{}) && step(I1{}) && step(I2{}) && step(I3{})) {
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
 
   // epilogue: normalize, store bf16 O and the LSE
-  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
-  if (row < a.Nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    unsigned short* orow = a.out + b * a.o_sb + h * a.o_sh + row * a.o_sn;
+  const float l_tot = rs.l + __shfl_xor(rs.l, 32);
+  if (row < nq) {
     const float* vsh = PV == 1 ? a.vscale + bh * D : nullptr;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    unsigned short* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int d0 = db * 32 + rq * 8 + g * 4;
-        unsigned short hv[4];
+        float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float f = o[db][rq * 4 + e] * inv;
-          if constexpr (PV == 1) f = o[db][rq * 4 + e] * (vsh[d0 + e] * inv);
-          hv[e] = f32_to_bf16(f);
+          if constexpr (PV == 1)
+            f[e] = o[db][rq * 4 + e] * (vsh[d0 + e] * inv);
+          else
+            f[e] = o[db][rq * 4 + e] * inv;
         }
-        uint2 pk = make_uint2((unsigned)hv[0] | ((unsigned)hv[1] << 16), (unsigned)hv[2] | ((unsigned)hv[3] << 16));
+        const v2bf lo = __builtin_convertvector((v2f{f[0], f[1]}), v2bf);  // round to nearest even
+        const v2bf hi = __builtin_convertvector((v2f{f[2], f[3]}), v2bf);
+        uint2 pk;
+        pk.x = __builtin_bit_cast(unsigned, lo);
+        pk.y = __builtin_bit_cast(unsigned, hi);
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
     if (g == 0 && a.lse) {
       float v = -INFINITY;
       if (l_tot > 0.f) {
-        float m2 = PV == 1 ? m_state - kLog2_448 : m_state;
-        v = (m2 + log2f(l_tot)) * kLn2 + a.sm_scale * a.corr[bh * a.Nq + row];
+        // l_tot sums 2^(s - pm) over the row (e4m3 P carries the 448 inside pm)
+        v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.corr[bh * a.Nq + row];
       }
       a.lse[bh * a.Nq + row] = v;
     }
@@ -331,14 +730,15 @@ template <int D>
 __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) {
   __shared__ __attribute__((aligned(16))) char sK[kBlockN * D];
   const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
-  const int64_t rb = a.row0 / kWaveRows + blockIdx.x;
+  const int64_t rb = a.row0 / 32 + blockIdx.x;
   const int kt = (int)(a.col0 / kBlockN) + (int)blockIdx.y;
-  Stager<D, 0, 64> st;
-  st.load_k(a.k8h, kt, lane);
-  st.store_k(sK, lane);
+  Stager<D, 0, 1> st;
+  st.init(a.k8h, reinterpret_cast<const uint8_t*>(a.k8h), a.Nk_pad, 0, lane);
+  st.load_k(kt, sK);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v4i qf[D / 32];
-  const int64_t row = rb * kWaveRows + lr;
+  const int64_t row = rb * 32 + lr;
   load_q_frags<D>(a.q8h, row, Nq_pad, g, qf);
   v16i acc[2];
   qk_tile<D>(sK, qf, lr, g, acc);
@@ -352,24 +752,29 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
     }
 }
 
+template <int D, int PV>
+static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  k_attn_fwd<D, PV><<<grid, kAttnThreads, 0, s>>>(a);
+}
+
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nQT * a.B * a.H);
   if (d == 128) {
     if (pv_fp8)
-      k_attn_fwd<128, 1><<<grid, kAttnThreads, 0, s>>>(a);
+      launch_attn_t<128, 1>(a, grid, s);
     else
-      k_attn_fwd<128, 0><<<grid, kAttnThreads, 0, s>>>(a);
+      launch_attn_t<128, 0>(a, grid, s);
   } else {
     if (pv_fp8)
-      k_attn_fwd<64, 1><<<grid, kAttnThreads, 0, s>>>(a);
+      launch_attn_t<64, 1>(a, grid, s);
     else
-      k_attn_fwd<64, 0><<<grid, kAttnThreads, 0, s>>>(a);
+      launch_attn_t<64, 0>(a, grid, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_debug_qk(const DebugQKArgs& a, int d, int64_t Nq_pad, hipStream_t s) {
-  const int64_t rb0 = a.row0 / kWaveRows, rb1 = (a.row0 + a.nrows + kWaveRows - 1) / kWaveRows;
+  const int64_t rb0 = a.row0 / 32, rb1 = (a.row0 + a.nrows + 31) / 32;
   const int64_t kt0 = a.col0 / kBlockN, kt1 = (a.col0 + a.ncols + kBlockN - 1) / kBlockN;
   dim3 grid((unsigned)(rb1 - rb0), (unsigned)(kt1 - kt0));
   if (d == 128)

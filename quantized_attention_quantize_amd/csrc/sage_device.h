@@ -16,13 +16,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kQuantBlock = 64;  // tokens per INT8 quantization block (Q and K)
 constexpr int kBlockN = 64;      // keys per attention tile: one K-scale per tile
-constexpr int kWaveRows = 32;    // query rows per wave
-constexpr int kWaves = 8;        // waves per attention workgroup
-constexpr int kBlockM = kWaveRows * kWaves;  // query rows per attention workgroup
+constexpr int kBlockM = 256;     // query rows per attention workgroup
 constexpr int kMaskTileRows = kBlockM;       // mask classification granularity (rows)
 
 // int32 accumulator bias: the bit pattern of 1.5 * 2^23.  For |acc| < 2^22 the int32 sum
@@ -43,10 +42,13 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   return static_cast<unsigned short>(u >> 16);
 }
 
-// LDS swizzle of 16-byte chunks inside a row, chosen so that the 16 (or 8) lanes of one
-// ds_read_b128 phase, which read the same logical chunk of 16 consecutive rows, hit distinct
-// banks.  Rows of 128 bytes (8 chunks) and rows of 64 bytes (4 chunks).
-__device__ __forceinline__ int swz128(int row) { return (row ^ (row >> 3)) & 7; }
+// LDS swizzle of 16-byte chunks inside a row.  A fragment read (ds_read_b128) fetches one logical
+// chunk from each of 32 consecutive rows, and LDS serves it 16 lanes (16 rows) at a time.  With
+// 128-byte rows the 16 rows of such a group hit distinct banks iff the even rows land on 8
+// distinct chunks and so do the odd rows; with 64-byte rows iff the rows of each residue modulo 4
+// land on 4 distinct chunks.  The swizzles below meet that (and keep every 8 consecutive rows on
+// distinct chunks) while depending on the row modulo 16 only.
+__device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 template <int ROW_BYTES>
 __device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {

@@ -6,6 +6,11 @@
 
 namespace sage {
 
+// Lazy online-softmax maximum (log2 units) by PV type: the reference maximum moves only when a
+// tile's maximum exceeds it by more than this, so FP16 P stays <= 2^8 (no overflow) while O is
+// rarely rescaled; e4m3 P (448 * p <= 448) needs the exact running maximum.
+constexpr float kSoftmaxTau[2] = {8.f, 0.f};
+
 struct QuantArgs {
   const unsigned short* q;  // bf16
   const unsigned short* k;  // bf16
@@ -36,7 +41,7 @@ struct MaskTileArgs {
   int64_t B, Hm, Nq, Nk;
   int nQT, nKT;
   int vec16;  // rows and base are 16-byte aligned: read 16 bytes at a time
-  uint8_t* state;  // [B*Hm][nQT][nKT]
+  int* state;  // [B*Hm][nQT][nKT]: 0 all masked, 1 all visible, 2 mixed
 };
 
 struct AttnArgs {
@@ -49,7 +54,7 @@ struct AttnArgs {
   const float* vscale;
   const uint8_t* mask;  // element mask (only read for mixed tiles)
   int64_t m_sb, m_sh, m_sq;
-  const uint8_t* mtiles;  // tile states or nullptr
+  const int* mtiles;  // tile states or nullptr
   int64_t Hm;             // 0 = no mask
   unsigned short* out;    // bf16
   int64_t o_sb, o_sh, o_sn;
@@ -57,12 +62,14 @@ struct AttnArgs {
   int64_t B, H, Nq, Nk, Nq_pad, Nk_pad;
   int nbq, nbk, nQT, nKT;
   int causal;
+  int mask_vec4;  // mask rows 4-byte aligned: read 4 mask bytes at a time
   float sm_scale;
 };
 
 struct DebugQKArgs {
   const int8_t* q8h;  // head base
   const int8_t* k8h;
+  int64_t Nk_pad;
   int64_t row0, nrows, col0, ncols;
   int32_t* out;
 };

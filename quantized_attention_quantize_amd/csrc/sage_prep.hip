@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
   }
   int z = __syncthreads_or(any0);
   int o = __syncthreads_or(any1);
-  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = (uint8_t)(z && o ? 2 : (o ? 1 : 0));
+  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = z && o ? 2 : (o ? 1 : 0);
 }
 
 // ---------------------------------------------------------------------------------------------

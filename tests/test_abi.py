@@ -187,7 +187,7 @@ def test_prepared_attn_validation(L):
     assert f(ctypes.byref(qk), FAKE, None, 1, *args[1:], None, 0, None) == INVALID  # fp8 without v_scale
     masked = [0, FAKE, 1, 0, 0, 256, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
     assert f(ctypes.byref(qk), FAKE, None, *masked, None, 0, None) == WORKSPACE  # mask needs tile workspace
-    assert L.sage_mask_workspace_bytes(2, 8192, 8192, 1) == 2 * 32 * 128
+    assert L.sage_mask_workspace_bytes(2, 8192, 8192, 1) == 2 * 32 * 128 * 4  # one int32 state per tile
     assert L.sage_mask_workspace_bytes(2, 8192, 8192, 0) == 0
     assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 0) == 0
     assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 1) >= 24 * 70 * 128 * 4
