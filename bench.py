@@ -62,7 +62,7 @@ def traffic_from_profile(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, work_target: float, tau: float):
+def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     """The oracle (never tuned) on a bounded sample of the workload: whole heads (B=1) of the same
     shape and input recipe -- K mean, INT8 quantization and V preparation of those heads, then the
     quantized emulation of evenly spaced query rows -- sized to about `work_target` row x key
@@ -84,7 +84,8 @@ def cpu_baseline(w, work_target: float, tau: float):
     t0 = time.perf_counter()
     qk = oracle.quant_qk(Qb, Kb)
     vh, vs = oracle.prep_v(Vb, w.pv)
-    oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, tau=tau, rows=rows)
+    oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, tau=tau,
+                   lsum_rounded=lsum_rounded, rows=rows)
     dt = time.perf_counter() - t0
     if w.causal:
         ops = heads * float(sum(4.0 * (int(i) + 1) * w.d for i in local))
@@ -199,7 +200,7 @@ def main():
                      "min_ms": round(attn_ms[0], 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv))
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
     print(json.dumps(line), flush=True)
 
 

@@ -90,6 +90,11 @@ int sage_block_n(sage_pv_dtype pv);
  * does.  8 for SAGE_PV_FP16 (P <= 256 fits fp16), 0 for SAGE_PV_FP8_E4M3.  Host only. */
 double sage_softmax_tau(sage_pv_dtype pv);
 
+/* 1 if sage_attn_fwd's softmax denominator sums P as rounded for the PV product (fp16 P), 0 if it
+ * sums the unrounded fp32 p (e4m3 P, where it sums 448*p).  Either way O = (sum P V) / l with l
+ * over the same keys; the choice moves l by at most the relative rounding error of P.  Host only. */
+int sage_rowsum_rounded(sage_pv_dtype pv);
+
 /* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean).  Host only. */
 size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d);
 
@@ -148,7 +153,7 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, in
  * The online softmax runs over sage_block_n() keys per tile in increasing key order; a row's
  * reference maximum moves when a tile's maximum exceeds it by more than sage_softmax_tau() (log2
  * units); P is rounded to fp16 (or e4m3 of 448*p) against the reference maximum; the denominator
- * sums P as rounded (fp16) or the unrounded fp32 448*p (e4m3); O and l accumulate in fp32.  Keys j >= Nk are masked
+ * sums P as rounded or unrounded per sage_rowsum_rounded(); O and l accumulate in fp32.  Keys j >= Nk are masked
  * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
  * gets O = 0 and LSE = -inf.
  * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, mask_h not

@@ -68,7 +68,7 @@ def lib():
         L.orc_prep_v_fp16.argtypes = [P, I, I, I, I, P]
         L.orc_prep_v_fp8.argtypes = [P, I, I, I, I, P, P]
         L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
-        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, f64, P, I, P, P, P]
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, f64, i32, P, I, P, P, P]
         L.orc_attn_ex.argtypes = [P, P, P, P, I, i32, f64, I, I, I, I, I, P, I, P, P]
         for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
                      "orc_attn_qe", "orc_attn_ex"):
@@ -221,11 +221,12 @@ def _mask_arg(mask, B, H, Nq, Nk):
 
 
 def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_scale=None, BN=64, tau=0.0,
-            rows=None):
+            lsum_rounded=False, rows=None):
     """Quantized emulation.  Returns (o32 [R,d] fp32, obf [R,d] bf16 bits, lse [R] fp32).
 
     BN: keys per online-softmax tile; tau: the reference maximum is raised only when a tile's
-    maximum exceeds it by more than tau (log2 units); 0 = exact running maximum."""
+    maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.
+    lsum_rounded: the denominator sums P as rounded for the PV product instead of the fp32 p."""
     B, H, Nq_pad, d = qk.q8.shape
     Nk_pad = qk.k8.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
@@ -242,7 +243,7 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     lse = np.empty((R,), np.float32)
     lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
                       _p(vs), 1 if pv == "fp8" else 0, _p(m), mh, 1 if causal else 0, sm, B, H, Nq, Nk, d, Nq_pad,
-                      Nk_pad, BN, float(tau), _p(rp), R, _p(o32), _p(obf), _p(lse))
+                      Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32), _p(obf), _p(lse))
     return o32, obf, lse
 
 
@@ -278,11 +279,12 @@ class QEResult:
     lse: np.ndarray
 
 
-def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, tau=0.0, rows=None) -> QEResult:
+def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, tau=0.0, lsum_rounded=False,
+           rows=None) -> QEResult:
     """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe."""
     qk = quant_qk(Q, K)
     vhat, vs = prep_v(V, pv)
     Nq, Nk = Q.shape[2], K.shape[2]
     o32, obf, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, tau=tau,
-                            rows=rows)
+                            lsum_rounded=lsum_rounded, rows=rows)
     return QEResult(qk, vhat, vs, o32, obf, lse)

@@ -27,7 +27,8 @@
  *    in fp64 and rounded once to fp32;
  *  - P for FP8 PV is quantized as e4m3(448 * p) with saturation, V per channel as
  *    e4m3(V * 448 / max_t |V|);
- *  - the softmax denominator l sums the unquantized fp32 p;
+ *  - the softmax denominator l sums, per the lsum_rounded argument, either the unquantized fp32 p
+ *    (0) or P as rounded for the PV product (1: the fp16 value, or e4m3(448*p)/448);
  *  - the online softmax runs over key tiles of BN keys in increasing key order.  Its reference
  *    maximum m starts at -inf and, after each tile, is replaced by the running maximum whenever
  *    that exceeds m by more than tau*ln(2) (tau = 0: the exact running maximum); p = exp(s - m)
@@ -319,13 +320,15 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
 /* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
 /* BN: keys per online-softmax tile; tau: lazy-maximum threshold in log2 units (0 = exact).    */
+/* lsum_rounded: 0 = l sums the fp32 p, 1 = l sums P as rounded for PV.                       */
 /* Outputs per requested row: o32 [nrows][d] (fp32 O before the bf16 rounding, may be NULL),  */
 /* obf [nrows][d] (bf16 bits), lse [nrows] (natural log, fp32).                               */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
                  const void* vhat, const float* vs, int pv_fp8, const uint8_t* mask, int64_t mask_h, int causal,
                  float sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
-                 int64_t Nk_pad, int64_t BN, double tau, const int64_t* rows, int64_t nrows, float* o32,
+                 int64_t Nk_pad, int64_t BN, double tau, int lsum_rounded, const int64_t* rows, int64_t nrows,
+                 float* o32,
                  uint16_t* obf, float* lse) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
   if (rows == NULL) nrows = B * H * Nq;
@@ -370,11 +373,14 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         float psum = 0.0f;
         for (int64_t j = j0; j < j1; ++j) {
           float p = (s[j - j0] == -INFINITY) ? 0.0f : (float)exp((double)(s[j - j0] - mnew));
-          psum += p;
           if (pv_fp8)
             pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(448.0f * p));
           else
             pq[j - j0] = orc_f16_to_f32(orc_f32_to_f16(p));
+          if (!lsum_rounded)
+            psum += p;
+          else
+            psum += pv_fp8 ? pq[j - j0] / 448.0f : pq[j - j0];
         }
         l = alpha * l + psum;
         for (int64_t c = 0; c < d; ++c) {

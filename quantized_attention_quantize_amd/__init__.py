@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     pad_tokens,
     prepare_v,
     quantize_qk,
+    rowsum_rounded,
     sageattn,
     softmax_tau,
 )

@@ -53,7 +53,7 @@ class QKQuant(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_quantize_workspace_bytes", "sage_quantize_qk",
+EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_rounded", "sage_quantize_workspace_bytes", "sage_quantize_qk",
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
            "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_debug_qk_int32",
            "sage_status_string")
@@ -78,6 +78,8 @@ def load_library():
     L.sage_block_n.restype = I
     L.sage_softmax_tau.argtypes = [I]
     L.sage_softmax_tau.restype = ctypes.c_double
+    L.sage_rowsum_rounded.argtypes = [I]
+    L.sage_rowsum_rounded.restype = I
     L.sage_quantize_workspace_bytes.argtypes = [I64, I64, I64, I64]
     L.sage_quantize_workspace_bytes.restype = SZ
     L.sage_quantize_qk.argtypes = [ctypes.POINTER(QKVDesc), ctypes.POINTER(QKVDesc), ctypes.POINTER(QKQuant), P, SZ, P]
@@ -125,6 +127,11 @@ def block_n(pv_dtype: str = "fp16") -> int:
 def softmax_tau(pv_dtype: str = "fp16") -> float:
     """Lazy-maximum threshold (log2 units) of the attention kernel's online softmax."""
     return float(load_library().sage_softmax_tau(PV_CODES[pv_dtype]))
+
+
+def rowsum_rounded(pv_dtype: str = "fp16") -> bool:
+    """Whether the attention kernel's softmax denominator sums P as rounded for the PV product."""
+    return bool(load_library().sage_rowsum_rounded(PV_CODES[pv_dtype]))
 
 
 def _desc(t: torch.Tensor, layout: str) -> QKVDesc:

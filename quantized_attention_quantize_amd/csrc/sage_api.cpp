@@ -132,6 +132,8 @@ int sage_block_n(sage_pv_dtype pv) {
 
 double sage_softmax_tau(sage_pv_dtype pv) { return kSoftmaxTau[pv == SAGE_PV_FP8_E4M3 ? 1 : 0]; }
 
+int sage_rowsum_rounded(sage_pv_dtype pv) { return kRowsumRounded[pv == SAGE_PV_FP8_E4M3 ? 1 : 0]; }
+
 size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d) {
   if (B <= 0 || H <= 0 || Nk <= 0 || d <= 0) return 0;
   return align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * sizeof(double));

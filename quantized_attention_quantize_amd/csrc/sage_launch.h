@@ -10,6 +10,9 @@ namespace sage {
 // tile's maximum exceeds it by more than this, so FP16 P stays <= 2^8 (no overflow) while O is
 // rarely rescaled; e4m3 P (448 * p <= 448) needs the exact running maximum.
 constexpr float kSoftmaxTau[2] = {8.f, 0.f};
+// Whether the softmax denominator sums P as rounded for the PV product (FP16: one v_dot2 per two
+// probabilities) rather than the fp32 p (e4m3), by PV type.
+constexpr int kRowsumRounded[2] = {1, 0};
 
 struct QuantArgs {
   const unsigned short* q;  // bf16

@@ -42,6 +42,9 @@ def test_host_queries(L):
     assert L.sage_pad_tokens(1) == 128 and L.sage_pad_tokens(128) == 128 and L.sage_pad_tokens(17776) == 17792
     assert L.sage_pad_tokens(0) == 0
     assert L.sage_block_n(0) == 64 and L.sage_block_n(1) == 64
+    L.sage_softmax_tau.restype = ctypes.c_double
+    assert L.sage_softmax_tau(0) == 8.0 and L.sage_softmax_tau(1) == 0.0  # FP16 P <= 2^8; e4m3 exact max
+    assert L.sage_rowsum_rounded(0) == 1 and L.sage_rowsum_rounded(1) == 0
     assert L.sage_quantize_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_quantize_workspace_bytes(0, 1, 1, 64) == 0
     # prepared fp16 V of the 8192-token, 64-head workload

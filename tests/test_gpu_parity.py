@@ -141,7 +141,8 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
         rows = np.arange(B * H * Nq, dtype=np.int64)
     m_u8 = None if mask is None else mask.numpy().astype(np.uint8)
     r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m_u8,
-                   sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv), rows=rows)
+                   sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv),
+                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows)
     ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m_u8,
                              sm_scale=sm_scale, rows=rows)
     got_o = rows_of(out, rows, layout)

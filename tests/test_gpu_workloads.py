@@ -77,7 +77,8 @@ def test_workload_parity(orc, name):
     m_u8 = inp.mask_u8
     vh_o, vs_o = (vh, vsc)
     o32, obf, qlse = orc.attn_qe(c, vh_o, vs_o, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8,
-                                 BN=sage.block_n(w.pv), tau=sage.softmax_tau(w.pv), rows=rows)
+                                 BN=sage.block_n(w.pv), tau=sage.softmax_tau(w.pv),
+                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows)
     got_o = rows_of(out, rows)
     got_l = lse_rows(lse, rows)
     e_qe = rel_l1(got_o, f32_of_bf16_bits(obf))

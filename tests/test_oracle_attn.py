@@ -242,3 +242,23 @@ def test_qe_lazy_maximum_only_moves_rounding(orc, sm):
     # with tau = 0 the emulation is the exact running maximum: identical to tau = 1e-30
     c = orc.run_qe(Qb, Kb, Vb, BN=64, tau=1e-30, sm_scale=sm)
     assert np.array_equal(c.obf, a.obf)
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_qe_rounded_rowsum_is_a_per_row_rescale(orc, pv):
+    """Summing the rounded P instead of the fp32 p changes only the denominator l: the accumulated
+    o is the same, so per row O_rounded / O_fp32 = l_fp32 / l_rounded = exp(LSE_fp32 - LSE_rounded)
+    to fp32 rounding, and |LSE_rounded - LSE_fp32| stays within the relative rounding error of one
+    P element (2^-11 for fp16, 2^-4 for e4m3)."""
+    inp = make_inputs(1, 2, 200, 333, 128, sigma=8.0 if pv == "fp8" else 4.0, seed=21)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    tau = 8.0 if pv == "fp16" else 0.0
+    a = orc.run_qe(Qb, Kb, Vb, pv=pv, BN=64, tau=tau)
+    b = orc.run_qe(Qb, Kb, Vb, pv=pv, BN=64, tau=tau, lsum_rounded=True)
+    dl = b.lse.astype(np.float64) - a.lse.astype(np.float64)
+    assert np.abs(dl).max() <= (2.0 ** -11 if pv == "fp16" else 2.0 ** -4)
+    assert np.abs(dl).max() > 0  # the flag does change the denominator
+    ratio = np.exp(-dl)[:, None]
+    nz = np.abs(a.o32) > 1e-30
+    rel = np.abs(b.o32[nz] - (a.o32 * ratio)[nz]) / np.abs(a.o32[nz])
+    assert rel.max() < 2e-6
