@@ -52,7 +52,7 @@ def kernel_source_hash() -> str:
 def traffic_from_profile(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"k_attn_fwd_{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="n8k")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (5 launches): a kernel of "
+                         "known traffic for calibrating HBM byte counters")
     ap.add_argument("--cpu-work", type=float, default=2.7e8,
                     help="query-row x key pairs in the CPU-baseline sample (oracle on the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -116,6 +119,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 5}), flush=True)
+        return
 
     import quantized_attention_quantize_amd as sage
     from quantized_attention_quantize_amd import api
