@@ -64,12 +64,13 @@ def lib():
             getattr(L, name).argtypes = [P, P, I]
             getattr(L, name).restype = None
         L.orc_kmean.argtypes = [P, I, I, I, I, P]
-        L.orc_quant_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P]
+        L.orc_quant_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P]
         L.orc_prep_v_fp16.argtypes = [P, I, I, I, I, P]
         L.orc_prep_v_fp8.argtypes = [P, I, I, I, I, P, P]
         L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
-        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, f64, i32, P, I, P, P, P]
-        L.orc_attn_ex.argtypes = [P, P, P, P, I, i32, f64, I, I, I, I, I, P, I, P, P]
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32, P, I, P, P,
+                                  P]
+        L.orc_attn_ex.argtypes = [P, P, P, P, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
         for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
                      "orc_attn_qe", "orc_attn_ex"):
             getattr(L, name).restype = None
@@ -153,29 +154,31 @@ def kmean(K):
 @dataclass
 class QuantQK:
     q8: np.ndarray  # int8 [B,H,Nq_pad,d]
-    k8: np.ndarray  # int8 [B,H,Nk_pad,d]
+    k8: np.ndarray  # int8 [B,Hkv,Nk_pad,d]
     qs: np.ndarray  # fp32 [B,H,ceil(Nq/64)]
-    ks: np.ndarray  # fp32 [B,H,ceil(Nk/64)]
-    kmean: np.ndarray  # fp32 [B,H,d]
+    ks: np.ndarray  # fp32 [B,Hkv,ceil(Nk/64)]
+    kmean: np.ndarray  # fp32 [B,Hkv,d]
     corr: np.ndarray  # fp32 [B,H,Nq]
 
 
 def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None) -> QuantQK:
+    """Q [B,H,Nq,d], K [B,Hkv,Nk,d] (Hkv divides H; query head h reads key head h // (H // Hkv))."""
     Q = _c(Q, np.uint16)
     K = _c(K, np.uint16)
     B, H, Nq, d = Q.shape
-    Nk = K.shape[2]
+    Hkv, Nk = K.shape[1], K.shape[2]
+    assert K.shape[0] == B and K.shape[3] == d and H % Hkv == 0
     if km is None:
         km = kmean(K)
     km = _c(km, np.float32)
     Nq_pad = pad_n(Nq) if Nq_pad is None else Nq_pad
     Nk_pad = pad_n(Nk) if Nk_pad is None else Nk_pad
     q8 = np.empty((B, H, Nq_pad, d), np.int8)
-    k8 = np.empty((B, H, Nk_pad, d), np.int8)
+    k8 = np.empty((B, Hkv, Nk_pad, d), np.int8)
     qs = np.empty((B, H, (Nq + QBLK - 1) // QBLK), np.float32)
-    ks = np.empty((B, H, (Nk + QBLK - 1) // QBLK), np.float32)
+    ks = np.empty((B, Hkv, (Nk + QBLK - 1) // QBLK), np.float32)
     corr = np.empty((B, H, Nq), np.float32)
-    lib().orc_quant_qk(_p(Q), _p(K), _p(km), B, H, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
+    lib().orc_quant_qk(_p(Q), _p(K), _p(km), B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
                        _p(corr))
     return QuantQK(q8, k8, qs, ks, km, corr)
 
@@ -228,7 +231,7 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.
     lsum_rounded: the denominator sums P as rounded for the PV product instead of the fp32 p."""
     B, H, Nq_pad, d = qk.q8.shape
-    Nk_pad = qk.k8.shape[2]
+    Hkv, Nk_pad = qk.k8.shape[1], qk.k8.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
     m, mh = _mask_arg(mask, B, H, Nq, Nk)
     if rows is None:
@@ -242,7 +245,7 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     obf = np.empty((R, d), np.uint16)
     lse = np.empty((R,), np.float32)
     lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
-                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mh, 1 if causal else 0, sm, B, H, Nq, Nk, d, Nq_pad,
+                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d, Nq_pad,
                       Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32), _p(obf), _p(lse))
     return o32, obf, lse
 
@@ -253,7 +256,8 @@ def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
     K = _c(K, np.uint16)
     V = _c(V, np.uint16)
     B, H, Nq, d = Q.shape
-    Nk = K.shape[2]
+    Hkv, Nk = K.shape[1], K.shape[2]
+    assert H % Hkv == 0 and V.shape[1] == Hkv
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
     m, mh = _mask_arg(mask, B, H, Nq, Nk)
     if rows is None:
@@ -264,7 +268,7 @@ def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
         R = rp.size
     out = np.empty((R, d), np.float64)
     lse = np.empty((R,), np.float64)
-    lib().orc_attn_ex(_p(Q), _p(K), _p(V), _p(m), mh, 1 if causal else 0, sm, B, H, Nq, Nk, d, _p(rp), R,
+    lib().orc_attn_ex(_p(Q), _p(K), _p(V), _p(m), mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d, _p(rp), R,
                       _p(out), _p(lse))
     return out, lse
 

@@ -230,31 +230,37 @@ static void quantize_blocks(const float* X, int64_t N, int64_t N_pad, int64_t d,
   memset(x8 + N * d, 0, (size_t)((N_pad - N) * d));
 }
 
-/* Q, K bf16 [B][H][N][d]; kmean fp32 [B][H][d] (from orc_kmean).
- * Outputs: q8 [B][H][Nq_pad][d], k8 [B][H][Nk_pad][d], qs [B][H][ceil(Nq/64)],
- *          ks [B][H][ceil(Nk/64)], corr [B][H][Nq] = fp32(sum_c fp64(Q_ic) * fp64(kmean_c)).
+/* Q bf16 [B][H][Nq][d]; K bf16 [B][Hkv][Nk][d]; kmean fp32 [B][Hkv][d] (from orc_kmean).
+ * Hkv divides H; query head h reads key/value head h / (H / Hkv) (group-query attention).
+ * Outputs: q8 [B][H][Nq_pad][d], k8 [B][Hkv][Nk_pad][d], qs [B][H][ceil(Nq/64)],
+ *          ks [B][Hkv][ceil(Nk/64)], corr [B][H][Nq] = fp32(sum_c fp64(Q_ic) * fp64(kmean_c)) with
+ *          the K mean of the query head's key/value head.
  * K is smoothed as fp32(K - kmean) (one rounding) before quantizing. */
-void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int64_t B, int64_t H, int64_t Nq,
-                  int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8, int8_t* k8, float* qs,
-                  float* ks, float* corr) {
+void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int64_t B, int64_t H, int64_t Hkv,
+                  int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8, int8_t* k8,
+                  float* qs, float* ks, float* corr) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * Hkv; ++bh) {
+    float* xk = (float*)malloc((size_t)(Nk * d) * sizeof(float));
+    const float* km = kmean + bh * d;
+    for (int64_t t = 0; t < Nk; ++t)
+      for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_bf16_to_f32(K[(bh * Nk + t) * d + c]) - km[c];
+    quantize_blocks(xk, Nk, Nk_pad, d, k8 + bh * Nk_pad * d, ks + bh * nbk);
+    free(xk);
+  }
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bh = 0; bh < B * H; ++bh) {
     float* xq = (float*)malloc((size_t)(Nq * d) * sizeof(float));
-    float* xk = (float*)malloc((size_t)(Nk * d) * sizeof(float));
-    const float* km = kmean + bh * d;
+    const float* km = kmean + ((bh / H) * Hkv + (bh % H) / (H / Hkv)) * d;
     for (int64_t i = 0; i < Nq * d; ++i) xq[i] = orc_bf16_to_f32(Q[bh * Nq * d + i]);
-    for (int64_t t = 0; t < Nk; ++t)
-      for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_bf16_to_f32(K[(bh * Nk + t) * d + c]) - km[c];
     quantize_blocks(xq, Nq, Nq_pad, d, q8 + bh * Nq_pad * d, qs + bh * nbq);
-    quantize_blocks(xk, Nk, Nk_pad, d, k8 + bh * Nk_pad * d, ks + bh * nbk);
     for (int64_t i = 0; i < Nq; ++i) {
       double s = 0.0;
       for (int64_t c = 0; c < d; ++c) s += (double)xq[i * d + c] * (double)km[c];
       corr[bh * Nq + i] = (float)s;
     }
     free(xq);
-    free(xk);
   }
 }
 
@@ -326,7 +332,7 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
                  const void* vhat, const float* vs, int pv_fp8, const uint8_t* mask, int64_t mask_h, int causal,
-                 float sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
+                 float sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
                  int64_t Nk_pad, int64_t BN, double tau, int lsum_rounded, const int64_t* rows, int64_t nrows,
                  float* o32,
                  uint16_t* obf, float* lse) {
@@ -341,8 +347,9 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
     for (int64_t r = 0; r < nrows; ++r) {
       int64_t rid = rows ? rows[r] : r;
       int64_t bh = rid / Nq, i = rid % Nq, b = bh / H, h = bh % H;
+      int64_t bhk = b * Hkv + h / (H / Hkv); /* key/value head of this query head */
       const int8_t* q = q8 + (bh * Nq_pad + i) * d;
-      const int8_t* kh = k8 + bh * Nk_pad * d;
+      const int8_t* kh = k8 + bhk * Nk_pad * d;
       const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
       float qscale = qs[bh * nbq + i / ORC_QBLK];
       float m = -INFINITY, l = 0.0f;
@@ -362,7 +369,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           const int8_t* k = kh + j * d;
           int32_t acc = 0;
           for (int64_t c = 0; c < d; ++c) acc += (int32_t)q[c] * (int32_t)k[c];
-          float cst = (qscale * ks[bh * nbk + j / ORC_QBLK]) * sm_scale;
+          float cst = (qscale * ks[bhk * nbk + j / ORC_QBLK]) * sm_scale;
           s[j - j0] = (float)acc * cst;
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
@@ -386,7 +393,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         for (int64_t c = 0; c < d; ++c) {
           float acc = alpha * o[c];
           for (int64_t j = j0; j < j1; ++j) {
-            int64_t vidx = (bh * Nk + j) * d + c;
+            int64_t vidx = (bhk * Nk + j) * d + c;
             float v = pv_fp8 ? orc_e4m3_to_f32(((const uint8_t*)vhat)[vidx])
                              : orc_f16_to_f32(((const uint16_t*)vhat)[vidx]);
             acc += pq[j - j0] * v;
@@ -400,7 +407,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         if (l == 0.0f)
           out = 0.0f;
         else if (pv_fp8)
-          out = (float)((double)o[c] * (double)vs[bh * d + c] / (448.0 * (double)l));
+          out = (float)((double)o[c] * (double)vs[bhk * d + c] / (448.0 * (double)l));
         else
           out = o[c] / l;
         if (o32) o32[r * d + c] = out;
@@ -425,7 +432,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
 /* LSE_i = log sum_j exp(s_ij).  A row with no valid key gives O = 0, LSE = -inf.             */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint8_t* mask, int64_t mask_h,
-                 int causal, double sm_scale, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 int causal, double sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                  const int64_t* rows, int64_t nrows, double* out, double* lse) {
   if (rows == NULL) nrows = B * H * Nq;
 #pragma omp parallel
@@ -436,6 +443,7 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     for (int64_t r = 0; r < nrows; ++r) {
       int64_t rid = rows ? rows[r] : r;
       int64_t bh = rid / Nq, i = rid % Nq, b = bh / H, h = bh % H;
+      int64_t bhk = b * Hkv + h / (H / Hkv); /* key/value head of this query head */
       const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
       for (int64_t c = 0; c < d; ++c) q[c] = (double)orc_bf16_to_f32(Q[(bh * Nq + i) * d + c]);
       double mx = -INFINITY;
@@ -445,7 +453,7 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
           continue;
         }
         double acc = 0.0;
-        for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_bf16_to_f32(K[(bh * Nk + j) * d + c]);
+        for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_bf16_to_f32(K[(bhk * Nk + j) * d + c]);
         s[j] = sm_scale * acc;
         if (s[j] > mx) mx = s[j];
       }
@@ -460,7 +468,7 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
         if (s[j] == -INFINITY) continue;
         double p = exp(s[j] - mx);
         den += p;
-        for (int64_t c = 0; c < d; ++c) o[c] += p * (double)orc_bf16_to_f32(V[(bh * Nk + j) * d + c]);
+        for (int64_t c = 0; c < d; ++c) o[c] += p * (double)orc_bf16_to_f32(V[(bhk * Nk + j) * d + c]);
       }
       for (int64_t c = 0; c < d; ++c) o[c] /= den;
       if (lse) lse[r] = mx + log(den);

@@ -262,3 +262,25 @@ def test_qe_rounded_rowsum_is_a_per_row_rescale(orc, pv):
     nz = np.abs(a.o32) > 1e-30
     rel = np.abs(b.o32[nz] - (a.o32 * ratio)[nz]) / np.abs(a.o32[nz])
     assert rel.max() < 2e-6
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_gqa_equals_repeated_kv_heads(orc, pv):
+    """Group-query attention (query head h reads key/value head h // (H // Hkv)) is the same
+    computation as ordinary attention on K and V with each head repeated H // Hkv times: every
+    quantized tensor, output bit and LSE agrees exactly, in the emulation and in exact attention."""
+    inp = make_inputs(1, 4, 150, 170, 64, sigma=4.0, seed=23)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    Kg, Vg = np.ascontiguousarray(Kb[:, ::2]), np.ascontiguousarray(Vb[:, ::2])  # 2 key/value heads
+    Kr, Vr = np.repeat(Kg, 2, axis=1), np.repeat(Vg, 2, axis=1)
+    tau = 8.0 if pv == "fp16" else 0.0
+    g = orc.run_qe(Qb, Kg, Vg, pv=pv, tau=tau, causal=True)
+    r = orc.run_qe(Qb, Kr, Vr, pv=pv, tau=tau, causal=True)
+    assert g.qk.k8.shape[1] == 2 and r.qk.k8.shape[1] == 4
+    assert np.array_equal(np.repeat(g.qk.k8, 2, axis=1), r.qk.k8)
+    assert np.array_equal(np.repeat(g.qk.ks, 2, axis=1), r.qk.ks)
+    assert np.array_equal(g.qk.q8, r.qk.q8) and np.array_equal(g.qk.corr, r.qk.corr)
+    assert np.array_equal(g.obf, r.obf) and np.array_equal(g.lse, r.lse)
+    eg, lg = orc.attn_ex(Qb, Kg, Vg, causal=True)
+    er, lr = orc.attn_ex(Qb, Kr, Vr, causal=True)
+    assert np.array_equal(eg, er) and np.array_equal(lg, lr)
