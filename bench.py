@@ -77,7 +77,9 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     oracle.build(force=False)
     heads = max(1, min(w.B * w.H, math.ceil(work_target / (w.Nq * w.Nk))))
     per_head = max(1, min(w.Nq, int(work_target / (heads * w.Nk))))
-    inp = make_inputs(1, heads, w.Nq, w.Nk, w.d, w.sigma, seed=0, mask=w.mask)
+    g = w.H // (w.Hkv or w.H)  # query heads per key/value head
+    inp = make_inputs(1, heads, w.Nq, w.Nk, w.d, w.sigma, seed=0, mask=w.mask,
+                      Hkv=max(1, heads // g) if g > 1 and heads % g == 0 else 0)
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     local = np.linspace(0, w.Nq - 1, per_head).astype(np.int64)
     rows = np.concatenate([h * w.Nq + local for h in range(heads)])
@@ -143,10 +145,11 @@ def main():
     del inp
 
     # every buffer allocated once, outside the timed region
-    qk = api.alloc_quantized(w.B, w.H, w.Nq, w.Nk, w.d, dev)
-    qws = api.quantize_workspace(w.B, w.H, w.Nk, w.d, dev)
-    vt, vs = api.alloc_prepared_v(w.B, w.H, w.Nk, w.d, w.pv, dev)
-    vws = api.prepare_v_workspace(w.B, w.H, w.Nk, w.d, w.pv, dev)
+    Hkv = w.Hkv or w.H
+    qk = api.alloc_quantized(w.B, w.H, w.Nq, w.Nk, w.d, dev, Hkv=Hkv)
+    qws = api.quantize_workspace(w.B, Hkv, w.Nk, w.d, dev)
+    vt, vs = api.alloc_prepared_v(w.B, Hkv, w.Nk, w.d, w.pv, dev)
+    vws = api.prepare_v_workspace(w.B, Hkv, w.Nk, w.d, w.pv, dev)
     mws = api.mask_workspace(w.B, w.Nq, w.Nk, 1 if mask is not None else 0, dev)
     out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
@@ -199,7 +202,7 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+f8" if w.pv == "fp8" else "i8+f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+        "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
                    "gpu_ms_per_step": round(gpu_ms_step, 4)},

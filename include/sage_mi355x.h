@@ -59,13 +59,17 @@ typedef struct {
   int64_t stride_b, stride_h, stride_n;
 } sage_qkv_desc;
 
-/* Quantized Q/K produced by sage_quantize_qk (all device buffers, caller-owned, contiguous):
- *   q8       int8  [B][H][Nq_pad][d]   rows >= Nq are zero
- *   k8       int8  [B][H][Nk_pad][d]   smoothed K codes; rows >= Nk are zero
- *   q_scale  fp32  [B][H][ceil(Nq/64)] per-64-token-block scale  (amax/127; 0 for an all-zero block)
- *   k_scale  fp32  [B][H][ceil(Nk/64)]
- *   k_mean   fp32  [B][H][d]           per-channel token mean of K (fp64 sum, rounded once)
- *   lse_corr fp32  [B][H][Nq]          sum_c Q[i,c]*k_mean[c]: adds the smoothing shift back to the LSE
+/* Quantized Q/K produced by sage_quantize_qk (all device buffers, caller-owned, contiguous).
+ * Q has H heads; K and V have Hkv heads, Hkv dividing H (group-query attention: query head h
+ * reads key/value head h / (H / Hkv); Hkv = H is ordinary attention).  (Group-query attention,
+ * 16 query heads over 4 key/value heads: sageattn section of the SageAttention docs digest.)
+ *   q8       int8  [B][H][Nq_pad][d]     rows >= Nq are zero
+ *   k8       int8  [B][Hkv][Nk_pad][d]   smoothed K codes; rows >= Nk are zero
+ *   q_scale  fp32  [B][H][ceil(Nq/64)]   per-64-token-block scale  (amax/127; 0 for an all-zero block)
+ *   k_scale  fp32  [B][Hkv][ceil(Nk/64)]
+ *   k_mean   fp32  [B][Hkv][d]           per-channel token mean of K (fp64 sum, rounded once)
+ *   lse_corr fp32  [B][H][Nq]            sum_c Q[i,c]*k_mean[c] with the query head's key head mean:
+ *                                        adds the smoothing shift back to the LSE
  * Nq_pad and Nk_pad must equal sage_pad_tokens(Nq) and sage_pad_tokens(Nk). */
 typedef struct {
   int8_t* q8;
@@ -74,7 +78,7 @@ typedef struct {
   float* k_scale;
   float* k_mean;
   float* lse_corr;
-  int64_t B, H, Nq, Nk, d, Nq_pad, Nk_pad;
+  int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;
 } sage_qk_quant;
 
 /* Padded token extent of q8 / k8 / prepared V: n rounded up to a multiple of 128. Host only. */
@@ -95,11 +99,13 @@ double sage_softmax_tau(sage_pv_dtype pv);
  * over the same keys; the choice moves l by at most the relative rounding error of P.  Host only. */
 int sage_rowsum_rounded(sage_pv_dtype pv);
 
-/* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean).  Host only. */
-size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d);
+/* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean); Hkv = heads of K.
+ * Host only. */
+size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t d);
 
-/* Step 1 (quantize).  Reads q and k (bf16, same B, H, d), writes every buffer of *out.
- * Per (b,h): k_mean = fp32(sum_t fp64(K[t,:]) / Nk); Ks = fp32(K - k_mean); for every 64-token
+/* Step 1 (quantize).  Reads q [B,H,Nq,d] and k [B,Hkv,Nk,d] (bf16, same B and d, Hkv dividing H;
+ * out->H = H, out->Hkv = Hkv), writes every buffer of *out.
+ * Per key head (b,h): k_mean = fp32(sum_t fp64(K[t,:]) / Nk); Ks = fp32(K - k_mean); for every 64-token
  * block of Q and of Ks: scale = amax/127, code = clamp(rne(x * (127/amax)), -127, 127)
  * (IEEE fp32 divisions, round-to-nearest-even); lse_corr[i] = fp32(sum_c fp64(Q[i,c])*fp64(k_mean[c])).
  * Sources: per-block INT8 Q/K and smooth_k on the Triton INT8/FP16 kernel section; smoothing by
@@ -133,12 +139,12 @@ sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, 
 size_t sage_mask_workspace_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h);
 
 /* Bytes of workspace sage_attn_fwd needs: prepared V, the fp8 V scales, sage_prepare_v's scratch
- * and the mask tile classification.  Host only. */
-size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
+ * and the mask tile classification.  Hkv = heads of V.  Host only. */
+size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
                                 int64_t mask_h);
 
 /* Step 2 (attention, all in one): sage_prepare_v into the workspace, then sage_attn_fwd_prepared.
- *   qk: from sage_quantize_qk; v: bf16 [B,H,Nk,d].
+ *   qk: from sage_quantize_qk; v: bf16 [B,Hkv,Nk,d].
  *   mask: NULL, or uint8 with nonzero = attend, shape [B][mask_h][Nq][Nk] addressed as
  *         mask + b*mask_stride_b + h*mask_stride_h + i*mask_stride_q + j (mask_h in {1, H};
  *         mask_stride_h is ignored when mask_h == 1; mask_stride_b may be 0 to broadcast over
@@ -165,7 +171,7 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
                           size_t workspace_bytes, void* stream);
 
 /* Step 2b (attention on prepared V): mask tile classification (if a mask is given) and the
- * attention kernel.  v_t / v_scale as written by sage_prepare_v for the same B, H, Nk, d and pv.
+ * attention kernel.  v_t / v_scale as written by sage_prepare_v for the same B, Hkv, Nk, d and pv.
  * workspace: at least sage_mask_workspace_bytes(B, Nq, Nk, mask_h) bytes (may be NULL without a
  * mask).  Other arguments and errors as for sage_attn_fwd. */
 sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
@@ -175,7 +181,8 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
                                    int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Debug: the raw int32 scores acc[i,j] = sum_c q8[i,c]*k8[j,c] of head (b,h) for rows
+/* Debug: the raw int32 scores acc[i,j] = sum_c q8[i,c]*k8[j,c] of query head (b,h) (and its key
+ * head h / (H / Hkv)) for rows
  * [row0, row0+nrows) and keys [col0, col0+ncols), computed by the same tile code as
  * sage_attn_fwd.  out: int32 [nrows][ncols] device buffer.  The window must lie inside
  * [0,Nq_pad) x [0,Nk_pad). */

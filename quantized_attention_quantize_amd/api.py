@@ -47,8 +47,8 @@ class QKVDesc(ctypes.Structure):
 class QKQuant(ctypes.Structure):
     _fields_ = [("q8", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("lse_corr", ctypes.c_void_p),
-                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64),
-                ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64), ("Nk_pad", ctypes.c_int64)]
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("Nq", ctypes.c_int64),
+                ("Nk", ctypes.c_int64), ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64), ("Nk_pad", ctypes.c_int64)]
 
 
 _lib = None
@@ -158,7 +158,8 @@ def _desc(t: torch.Tensor, layout: str) -> QKVDesc:
 
 @dataclass
 class QuantizedQK:
-    """Device buffers produced by quantize_qk (see sage_qk_quant in the header)."""
+    """Device buffers produced by quantize_qk (see sage_qk_quant in the header).  Q has H heads,
+    K has Hkv heads (group-query attention when Hkv < H)."""
     q8: torch.Tensor
     k8: torch.Tensor
     q_scale: torch.Tensor
@@ -170,35 +171,38 @@ class QuantizedQK:
     Nq: int
     Nk: int
     d: int
+    Hkv: int
 
     def cstruct(self) -> QKQuant:
         return QKQuant(self.q8.data_ptr(), self.k8.data_ptr(), self.q_scale.data_ptr(), self.k_scale.data_ptr(),
-                       self.k_mean.data_ptr(), self.lse_corr.data_ptr(), self.B, self.H, self.Nq, self.Nk, self.d,
-                       self.q8.shape[2], self.k8.shape[2])
+                       self.k_mean.data_ptr(), self.lse_corr.data_ptr(), self.B, self.H, self.Hkv, self.Nq, self.Nk,
+                       self.d, self.q8.shape[2], self.k8.shape[2])
 
 
-def alloc_quantized(B, H, Nq, Nk, d, device) -> QuantizedQK:
+def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None) -> QuantizedQK:
+    Hkv = H if Hkv is None else Hkv
     nq, nk = pad_tokens(Nq), pad_tokens(Nk)
     return QuantizedQK(torch.empty(B, H, nq, d, dtype=torch.int8, device=device),
-                       torch.empty(B, H, nk, d, dtype=torch.int8, device=device),
+                       torch.empty(B, Hkv, nk, d, dtype=torch.int8, device=device),
                        torch.empty(B, H, (Nq + 63) // 64, dtype=torch.float32, device=device),
-                       torch.empty(B, H, (Nk + 63) // 64, dtype=torch.float32, device=device),
-                       torch.empty(B, H, d, dtype=torch.float32, device=device),
-                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d)
+                       torch.empty(B, Hkv, (Nk + 63) // 64, dtype=torch.float32, device=device),
+                       torch.empty(B, Hkv, d, dtype=torch.float32, device=device),
+                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d, Hkv)
 
 
-def quantize_workspace(B, H, Nk, d, device) -> torch.Tensor:
-    n = int(load_library().sage_quantize_workspace_bytes(B, H, Nk, d))
+def quantize_workspace(B, Hkv, Nk, d, device) -> torch.Tensor:
+    n = int(load_library().sage_quantize_workspace_bytes(B, Hkv, Nk, d))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def quantize_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", out: QuantizedQK | None = None,
                 workspace: torch.Tensor | None = None) -> QuantizedQK:
-    """K mean, per-64-token-block INT8 Q and smoothed K, scales and the LSE shift."""
+    """K mean, per-64-token-block INT8 Q and smoothed K, scales and the LSE shift.  k may have fewer
+    heads than q (group-query attention: query head h reads key head h // (H // Hkv))."""
     L = load_library()
     dq, dk = _desc(q, tensor_layout), _desc(k, tensor_layout)
     if out is None:
-        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device)
+        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device, Hkv=dk.H)
     if workspace is None:
         workspace = quantize_workspace(dk.B, dk.H, dk.N, dk.d, q.device)
     qs = out.cstruct()
@@ -207,8 +211,8 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", ou
     return out
 
 
-def fwd_workspace(B, H, Nq, Nk, d, pv_dtype, mask_h, device) -> torch.Tensor:
-    n = int(load_library().sage_fwd_workspace_bytes(B, H, Nq, Nk, d, PV_CODES[pv_dtype], mask_h))
+def fwd_workspace(B, Hkv, Nq, Nk, d, pv_dtype, mask_h, device) -> torch.Tensor:
+    n = int(load_library().sage_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, PV_CODES[pv_dtype], mask_h))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -249,7 +253,7 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
         lse = torch.empty(B, H, Nq, dtype=torch.float32, device=v.device)
     m, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
     if workspace is None:
-        workspace = fwd_workspace(B, H, Nq, Nk, d, pv_dtype, mh, v.device)
+        workspace = fwd_workspace(B, qk.Hkv, Nq, Nk, d, pv_dtype, mh, v.device)
     qs = qk.cstruct()
     odt = SAGE_BF16 if out.dtype == torch.bfloat16 else SAGE_FP16
     _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mh, msb, msh, msq,
@@ -264,7 +268,8 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
              pv_dtype: str = "fp16"):
     """Quantized attention forward: INT8 Q/K with K smoothing, FP16 (or FP8 e4m3) PV.
 
-    q, k, v: bf16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}.
+    q: bf16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}; k, v: the same with Hkv
+    heads, Hkv dividing H (group-query attention: query head h reads key/value head h // (H // Hkv)).
     attn_mask: optional bool, broadcastable to [B, H, Nq, Nk], True = attend.
     sm_scale: defaults to 1/sqrt(d).  Returns out (same layout and dtype as q) or (out, lse) with
     lse fp32 [B, H, Nq] (natural log, of the unsmoothed scaled scores).
@@ -275,8 +280,8 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
         raise ValueError("k and v must have the same shape")
     hk = k.shape[1] if tensor_layout == "HND" else k.shape[2]
     hq = q.shape[1] if tensor_layout == "HND" else q.shape[2]
-    if hk != hq:
-        raise NotImplementedError("grouped-query attention (fewer K/V heads) is not supported yet")
+    if hq % hk != 0:
+        raise ValueError(f"the {hk} key/value heads do not divide the {hq} query heads")
     qk = quantize_qk(q, k, tensor_layout)
     return attn_fwd(qk, v, tensor_layout=tensor_layout, is_causal=is_causal, attn_mask=attn_mask, sm_scale=sm_scale,
                     pv_dtype=pv_dtype, return_lse=return_lse)

@@ -60,7 +60,8 @@ sage_status check_desc(const sage_qkv_desc* t) {
 sage_status check_qk(const sage_qk_quant* qk) {
   if (!qk || !qk->q8 || !qk->k8 || !qk->q_scale || !qk->k_scale || !qk->k_mean || !qk->lse_corr)
     return SAGE_ERR_INVALID_ARGUMENT;
-  if (qk->B <= 0 || qk->H <= 0 || qk->Nq <= 0 || qk->Nk <= 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (qk->B <= 0 || qk->H <= 0 || qk->Hkv <= 0 || qk->Nq <= 0 || qk->Nk <= 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (qk->H % qk->Hkv != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (qk->Nq > kMaxTokens || qk->Nk > kMaxTokens || qk->B * qk->H > 65535) return SAGE_ERR_INVALID_ARGUMENT;
   if (qk->d != 64 && qk->d != 128) return SAGE_ERR_UNSUPPORTED;
   if (qk->Nq_pad != sage_pad_tokens(qk->Nq) || qk->Nk_pad != sage_pad_tokens(qk->Nk))
@@ -86,15 +87,15 @@ struct FwdLayout {
   size_t vt, vscale, prep, mtiles, total;
 };
 
-FwdLayout fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv, int64_t mask_h) {
+FwdLayout fwd_layout(int64_t B, int64_t Hv, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv, int64_t mask_h) {
   FwdLayout L;
   size_t off = 0;
   L.vt = off;
-  off += align256(vt_bytes(B, H, Nk, d, pv));
+  off += align256(vt_bytes(B, Hv, Nk, d, pv));
   L.vscale = off;
-  if (pv == SAGE_PV_FP8_E4M3) off += align256((size_t)(B * H * d) * 4);
+  if (pv == SAGE_PV_FP8_E4M3) off += align256((size_t)(B * Hv * d) * 4);
   L.prep = off;
-  off += prep_ws_bytes(B, H, Nk, d, pv);
+  off += prep_ws_bytes(B, Hv, Nk, d, pv);
   L.mtiles = off;
   off += mask_ws_bytes(B, Nq, Nk, mask_h);
   L.total = off;
@@ -134,9 +135,9 @@ double sage_softmax_tau(sage_pv_dtype pv) { return kSoftmaxTau[pv == SAGE_PV_FP8
 
 int sage_rowsum_rounded(sage_pv_dtype pv) { return kRowsumRounded[pv == SAGE_PV_FP8_E4M3 ? 1 : 0]; }
 
-size_t sage_quantize_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d) {
-  if (B <= 0 || H <= 0 || Nk <= 0 || d <= 0) return 0;
-  return align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * sizeof(double));
+size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t d) {
+  if (B <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0) return 0;
+  return align256((size_t)(B * Hkv * cdiv(Nk, kChunkTokens) * d) * sizeof(double));
 }
 
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
@@ -144,9 +145,10 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   sage_status s;
   if ((s = check_desc(q)) != SAGE_OK) return s;
   if ((s = check_desc(k)) != SAGE_OK) return s;
-  if (q->B != k->B || q->H != k->H || q->d != k->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (q->B != k->B || q->d != k->d || q->H % k->H != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if ((s = check_qk(out)) != SAGE_OK) return s;
-  if (out->B != q->B || out->H != q->H || out->d != q->d || out->Nq != q->N || out->Nk != k->N)
+  if (out->B != q->B || out->H != q->H || out->Hkv != k->H || out->d != q->d || out->Nq != q->N ||
+      out->Nk != k->N)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!workspace) return SAGE_ERR_WORKSPACE;
   if (workspace_bytes < sage_quantize_workspace_bytes(k->B, k->H, k->N, k->d)) return SAGE_ERR_WORKSPACE;
@@ -169,6 +171,7 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   a.corr = out->lse_corr;
   a.B = q->B;
   a.H = q->H;
+  a.Hkv = k->H;
   a.Nq = q->N;
   a.Nk = k->N;
   a.d = q->d;
@@ -193,11 +196,11 @@ size_t sage_mask_workspace_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask
   return mask_ws_bytes(B, Nq, Nk, mask_h);
 }
 
-size_t sage_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
+size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
                                 int64_t mask_h) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || mask_h < 0) return 0;
+  if (B <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || mask_h < 0) return 0;
   if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return 0;
-  return fwd_layout(B, H, Nq, Nk, d, pv, mask_h).total;
+  return fwd_layout(B, Hkv, Nq, Nk, d, pv, mask_h).total;
 }
 
 }  // extern "C"
@@ -299,6 +302,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   a.lse = lse;
   a.B = qk->B;
   a.H = qk->H;
+  a.Hkv = qk->Hkv;
   a.Nq = qk->Nq;
   a.Nk = qk->Nk;
   a.Nq_pad = qk->Nq_pad;
@@ -333,9 +337,9 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
                                out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
   if ((s = check_desc(v)) != SAGE_OK) return s;
-  if (v->B != qk->B || v->H != qk->H || v->N != qk->Nk || v->d != qk->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (v->B != qk->B || v->H != qk->Hkv || v->N != qk->Nk || v->d != qk->d) return SAGE_ERR_INVALID_ARGUMENT;
   if (!workspace) return SAGE_ERR_WORKSPACE;
-  const FwdLayout L = fwd_layout(qk->B, qk->H, qk->Nq, qk->Nk, qk->d, pv, c.mh);
+  const FwdLayout L = fwd_layout(qk->B, qk->Hkv, qk->Nq, qk->Nk, qk->d, pv, c.mh);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
   if ((s = check_device()) != SAGE_OK) return s;
   char* ws = static_cast<char*>(workspace);
@@ -378,9 +382,9 @@ sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, i
   if (col0 < 0 || ncols <= 0 || col0 + ncols > qk->Nk_pad) return SAGE_ERR_INVALID_ARGUMENT;
   if ((s = check_device()) != SAGE_OK) return s;
   DebugQKArgs a;
-  const int64_t bh = b * qk->H + h;
+  const int64_t bh = b * qk->H + h, bhk = b * qk->Hkv + h / (qk->H / qk->Hkv);
   a.q8h = qk->q8 + bh * qk->Nq_pad * qk->d;
-  a.k8h = qk->k8 + bh * qk->Nk_pad * qk->d;
+  a.k8h = qk->k8 + bhk * qk->Nk_pad * qk->d;
   a.Nk_pad = qk->Nk_pad;
   a.row0 = row0;
   a.nrows = nrows;

@@ -431,8 +431,12 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
 #pragma unroll
       for (int e = 0; e < GS; ++e) {
         const int idx = gi * GS + e, kb = idx >> 4, r = idx & 15;
-        float t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[kb][r], c_cur, -rs.pm));
-        if constexpr (SLOW) t = sc[kb][r] == INT_MIN ? 0.f : t;
+        // The empty asm pins the score to this slot: without it the compiler converts all 32 scores
+        // at the top of the step, where no MFMA overlaps them.
+        int si = sc[kb][r];
+        asm volatile("" : "+v"(si));
+        float t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, -rs.pm));
+        if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
         x[e] = t;
       }
       if constexpr (PV == 0) {
@@ -508,8 +512,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
   __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
-  char* const kring = smem;
-  char* const vring = smem + kNS * G::K_BYTES;
+  // V ring first: with at most 64 KiB of V slots every V fragment read is a lane base plus an
+  // immediate ds_read offset
+  char* const vring = smem;
+  char* const kring = smem + kNS * G::V_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
 
@@ -535,13 +541,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const uint8_t* mrow =
       (a.mask && row < nq) ? a.mask + b * a.m_sb + (a.Hm == 1 ? 0 : h) * a.m_sh + (int64_t)row * a.m_sq : nullptr;
 
+  const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);  // key/value head (group-query attention)
   const int8_t* q8h = a.q8 + bh * a.Nq_pad * D;
-  const int8_t* k8h = a.k8 + bh * a.Nk_pad * D;
-  const uint8_t* vth = static_cast<const uint8_t*>(a.vt) + bh * D * a.Nk_pad * G::V_ESZ;
+  const int8_t* k8h = a.k8 + bhk * a.Nk_pad * D;
+  const uint8_t* vth = static_cast<const uint8_t*>(a.vt) + bhk * D * a.Nk_pad * G::V_ESZ;
   const int r0u = __builtin_amdgcn_readfirstlane(r0w);  // the same value, held in an SGPR
   const int qblk = r0u / kQuantBlock;                   // a wave's rows lie in one quantization block
   const float cq = qblk < a.nbq ? scalar_ld(a.qs + bh * a.nbq, qblk) : 0.f;
-  const float* ksh = a.ks + bh * a.nbk;
+  const float* ksh = a.ks + bhk * a.nbk;
 
   v16f o[D / 32];
 #pragma unroll
@@ -690,7 +697,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   // epilogue: normalize, store bf16 O and the LSE
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
   if (row < nq) {
-    const float* vsh = PV == 1 ? a.vscale + bh * D : nullptr;
+    const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     unsigned short* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;
 #pragma unroll

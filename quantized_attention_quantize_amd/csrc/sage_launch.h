@@ -24,7 +24,7 @@ struct QuantArgs {
   float* ks;
   float* kmean;
   float* corr;
-  int64_t B, H, Nq, Nk, d, Nq_pad, Nk_pad;
+  int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;  // Q has H heads, K has Hkv (Hkv divides H)
   int nbq, nbk;
 };
 
@@ -62,7 +62,7 @@ struct AttnArgs {
   unsigned short* out;    // bf16
   int64_t o_sb, o_sh, o_sn;
   float* lse;  // nullptr = not requested
-  int64_t B, H, Nq, Nk, Nq_pad, Nk_pad;
+  int64_t B, H, Hkv, Nq, Nk, Nq_pad, Nk_pad;  // query head h reads key/value head h / (H / Hkv)
   int nbq, nbk, nQT, nKT;
   int causal;
   int mask_vec4;  // mask rows 4-byte aligned: read 4 mask bytes at a time

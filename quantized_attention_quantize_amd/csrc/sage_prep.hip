@@ -106,8 +106,10 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
 
 // ---------------------------------------------------------------------------------------------
 // Per-block INT8 quantization.  grid = (Nq_pad/64 + Nk_pad/64, B*H), block = 256.
-// Block x < Nq_pad/64 handles Q rows [64x, 64x+64); the others handle K.  Blocks past the last
-// valid block only write zero pad rows.  Each thread holds 8 channels of RPB rows.
+// Block x < Nq_pad/64 handles Q rows [64x, 64x+64) of query head y; the others handle K rows of
+// key head y (only y < B*Hkv: the key heads of group-query attention).  Blocks past the last valid
+// block only write zero pad rows.  Each thread holds 8 channels of RPB rows.  A query head's LSE
+// shift uses the K mean of its key head h / (H / Hkv).
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
@@ -117,9 +119,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
   __shared__ float red[4];
   __shared__ float km_s[D];
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
-  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int nqb_pad = (int)(a.Nq_pad / kQuantBlock);
   const bool isq = (int)blockIdx.x < nqb_pad;
+  // query blocks: bh indexes B*H query heads; key blocks: bh indexes B*Hkv key heads
+  const int64_t nh = isq ? a.H : a.Hkv;
+  const int64_t bh = blockIdx.y;
+  if (bh >= a.B * nh) return;  // key blocks of the grid rows past the key heads
+  const int64_t b = bh / nh, h = bh % nh;
+  const int64_t bhk = isq ? b * a.Hkv + h / (a.H / a.Hkv) : bh;  // head of the K mean
   const int u = isq ? (int)blockIdx.x : (int)blockIdx.x - nqb_pad;
   const int64_t N = isq ? a.Nq : a.Nk;
   const int64_t Npad = isq ? a.Nq_pad : a.Nk_pad;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
     return;
   }
 
-  if (t < D) km_s[t] = a.kmean[bh * D + t];
+  if (t < D) km_s[t] = a.kmean[bhk * D + t];
   __syncthreads();
 
   const unsigned short* src =
@@ -340,13 +347,13 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
 // host-side launchers
 // ---------------------------------------------------------------------------------------------
 hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
-  dim3 g(nchunk, (unsigned)(a.B * a.H));
+  dim3 g(nchunk, (unsigned)(a.B * a.Hkv));
   if (a.d == 128) {
-    k_colred_partial<128, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.H, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
-    k_kmean_final<128><<<(unsigned)(a.B * a.H), 128, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+    k_colred_partial<128, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
+    k_kmean_final<128><<<(unsigned)(a.B * a.Hkv), 128, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
   } else {
-    k_colred_partial<64, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.H, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
-    k_kmean_final<64><<<(unsigned)(a.B * a.H), 64, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+    k_colred_partial<64, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
+    k_kmean_final<64><<<(unsigned)(a.B * a.Hkv), 64, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
   }
   return hipGetLastError();
 }

@@ -9,11 +9,12 @@ plain ``torch.randn`` bf16 tensors in HND layout, and a boolean mask that keeps 
 the keys.  Keys additionally carry a per-(batch, head, channel) bias of standard deviation sigma, the
 channel-wise offset that key smoothing exists to remove.
 
-Draw order (fp32, one CPU generator seeded with ``seed``):
+Draw order (fp32, one CPU generator seeded with ``seed``; Hk = H, or the key/value head count of a
+group-query workload):
     Q  = randn(B, H, Nq, d)
-    Kn = randn(B, H, Nk, d)
-    Kb = sigma * randn(B, H, 1, d)
-    V  = randn(B, H, Nk, d)
+    Kn = randn(B, Hk, Nk, d)
+    Kb = sigma * randn(B, Hk, 1, d)
+    V  = randn(B, Hk, Nk, d)
 then K = bf16(Kn + Kb), Q = bf16(Q), V = bf16(V).
 """
 
@@ -39,6 +40,7 @@ class Workload:
     pv: str = "fp16"  # "fp16" or "fp8"
     lse: bool = True
     note: str = field(default="", compare=False)
+    Hkv: int = 0  # key/value heads (group-query attention); 0 = H
 
     @property
     def ops(self) -> float:
@@ -58,6 +60,8 @@ WORKLOADS = {
                          note="B=2 H=32 N=8192 d=128 bf16, bool mask [B,1,N,N] keeping keys < N/2, LSE"),
     "n17776_fp8": Workload("n17776_fp8", 1, 24, 17776, 17776, 128, 8.0, pv="fp8",
                            note="B=1 H=24 N=17776 d=128 bf16, non-causal, INT8 QK + FP8 e4m3 PV"),
+    "n8k_gqa": Workload("n8k_gqa", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", Hkv=8,
+                        note="B=2 H=32 over 8 K/V heads, N=8192 d=128 bf16, non-causal, INT8 QK + FP16 PV, LSE"),
 }
 
 
@@ -77,12 +81,14 @@ class Inputs:
         return None if self.mask is None else self.mask.numpy().astype(np.uint8)
 
 
-def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None) -> Inputs:
+def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0) -> Inputs:
+    """Hkv > 0 draws K and V with Hkv heads (group-query attention), in the same order."""
+    Hk = Hkv if Hkv > 0 else H
     g = torch.Generator("cpu").manual_seed(seed)
     q = torch.randn(B, H, Nq, d, generator=g, dtype=torch.float32)
-    kn = torch.randn(B, H, Nk, d, generator=g, dtype=torch.float32)
-    kb = sigma * torch.randn(B, H, 1, d, generator=g, dtype=torch.float32)
-    v = torch.randn(B, H, Nk, d, generator=g, dtype=torch.float32)
+    kn = torch.randn(B, Hk, Nk, d, generator=g, dtype=torch.float32)
+    kb = sigma * torch.randn(B, Hk, 1, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, Hk, Nk, d, generator=g, dtype=torch.float32)
     k = (kn + kb).to(torch.bfloat16)
     del kn
     m = None
@@ -95,7 +101,7 @@ def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None) -> Inputs:
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
-    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.sigma, seed, w.mask)
+    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.sigma, seed, w.mask, w.Hkv)
 
 
 def random_mask(B, Hm, Nq, Nk, p_keep=0.7, seed=1) -> torch.Tensor:

@@ -98,17 +98,19 @@ def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None)
     |s_ij - s~_ij| <= sm * (sum_c |q_ic| * ks_j/2 + sum_c |k~_jc| * qs_i/2 + d * qs_i*ks_j/4),
     where k~ is the smoothed key (the smoothing shift itself cancels between the two LSEs)."""
     B, H, _, d = Qb.shape
+    grp = H // Kb.shape[1]  # query heads per key head (group-query attention)
     Q = f32_of_bf16_bits(Qb).astype(np.float64)
     Ks = (f32_of_bf16_bits(Kb) - qk.kmean[:, :, None, :]).astype(np.float32).astype(np.float64)
-    sk = np.abs(Ks).sum(-1)  # [B,H,Nk]
+    sk = np.abs(Ks).sum(-1)  # [B,Hkv,Nk]
     out = np.empty(rows.size)
     for n, rid in enumerate(rows):
         bh, i = divmod(int(rid), Nq)
         b, h = divmod(bh, H)
+        hk = h // grp
         qs = float(qk.qs[b, h, i // 64])
-        ks = np.repeat(qk.ks[b, h].astype(np.float64), 64)[:Nk]
+        ks = np.repeat(qk.ks[b, hk].astype(np.float64), 64)[:Nk]
         sq = np.abs(Q[b, h, i]).sum()
-        bnd = sm_scale * (sq * ks / 2 + sk[b, h] * qs / 2 + d * qs * ks / 4)
+        bnd = sm_scale * (sq * ks / 2 + sk[b, hk] * qs / 2 + d * qs * ks / 4)
         valid = np.ones(Nk, bool)
         if causal:
             valid[i + 1:] = False

@@ -68,12 +68,12 @@ def desc(B=1, H=2, N=256, d=64, dtype=0, data=FAKE, sb=None, sh=None, sn=None):
     return api.QKVDesc(data, dtype, B, H, N, d, sb, sh, sn)
 
 
-def quant(B=1, H=2, Nq=256, Nk=256, d=64, pad=None, null=None):
+def quant(B=1, H=2, Nq=256, Nk=256, d=64, pad=None, null=None, Hkv=None):
     ptrs = [FAKE] * 6
     if null is not None:
         ptrs[null] = 0
     npq = L_pad(Nq) if pad is None else pad
-    return api.QKQuant(*ptrs, B, H, Nq, Nk, d, npq, L_pad(Nk))
+    return api.QKQuant(*ptrs, B, H, H if Hkv is None else Hkv, Nq, Nk, d, npq, L_pad(Nk))
 
 
 def L_pad(n):
@@ -90,6 +90,7 @@ def call_quant(L, q, k, out, ws=FAKE, wsb=1 << 20):
     ("fp16", UNSUPPORTED), ("bad_dtype", INVALID), ("misaligned", INVALID), ("odd_stride", INVALID),
     ("small_stride_n", INVALID), ("qk_mismatch_H", INVALID), ("out_null_ptr", INVALID), ("out_bad_pad", INVALID),
     ("out_wrong_N", INVALID), ("no_workspace", WORKSPACE), ("small_workspace", WORKSPACE),
+    ("gqa_out_hkv", INVALID), ("gqa_not_divisor", INVALID),
 ])
 def test_quantize_validation(L, case, status):
     q, k, out = desc(), desc(), quant()
@@ -126,6 +127,10 @@ def test_quantize_validation(L, case, status):
         ws = 0
     elif case == "small_workspace":
         wsb = 16
+    elif case == "gqa_out_hkv":  # K has 1 head, the output struct says 2
+        k = desc(H=1)
+    elif case == "gqa_not_divisor":  # 3 key heads cannot serve 4 query heads
+        q, k, out = desc(H=4), desc(H=3), quant(H=4, Hkv=3)
     assert call_quant(L, q, k, out, ws, wsb) == status
 
 
@@ -137,7 +142,8 @@ def call_fwd(L, qk, v, mask=None, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=
 @pytest.mark.parametrize("case,status", [
     ("null_qk", INVALID), ("v_shape", INVALID), ("pv_bad", UNSUPPORTED), ("out_null", INVALID),
     ("out_fp16", UNSUPPORTED), ("out_misaligned", INVALID), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
-    ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED),
+    ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED), ("gqa_v_heads", INVALID),
+    ("gqa_hkv_zero", INVALID),
 ])
 def test_attn_validation(L, case, status):
     qk, v = quant(), desc()
@@ -164,6 +170,10 @@ def test_attn_validation(L, case, status):
         kw["ws"] = 0
     elif case == "qk_d":
         qk = quant(d=80)
+    elif case == "gqa_v_heads":  # V must have the Hkv heads of K
+        qk = quant(H=2, Hkv=1)
+    elif case == "gqa_hkv_zero":
+        qk = quant(Hkv=0)
     assert call_fwd(L, qk, v, **kw) == status
 
 

@@ -6,6 +6,8 @@ oracle's quantized emulation (both rounded to bf16) and LSE within 1e-3; against
 attention, cosine >= 0.999 and relative L1 <= 3e-2 for FP16 PV.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -49,6 +51,34 @@ def test_quantize_bitexact(orc, B, H, Nq, Nk, d):
     assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32))
     assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32))
     np.testing.assert_allclose(g.lse_corr.cpu().numpy(), c.corr, rtol=2e-6, atol=2e-6)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", [(1, 4, 2, 300, 417, 128), (2, 6, 1, 129, 65, 64)])
+def test_quantize_bitexact_gqa(orc, B, H, Hkv, Nq, Nk, d):
+    """Group-query attention: K has Hkv heads; each query head's LSE shift uses its key head's mean."""
+    say(f"quantize gqa B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d}")
+    inp = gqa_inputs(make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=5), Hkv)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qk(q, k)
+    torch.cuda.synchronize()
+    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k))
+    assert g.k8.shape[1] == Hkv and g.Hkv == Hkv
+    assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32))
+    assert np.array_equal(g.q8.cpu().numpy(), c.q8) and np.array_equal(g.k8.cpu().numpy(), c.k8)
+    assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32))
+    assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32))
+    np.testing.assert_allclose(g.lse_corr.cpu().numpy(), c.corr, rtol=2e-6, atol=2e-6)
+    # the debug scores of the last query head come from its own key head
+    got = sage.debug_qk_int32(g, B - 1, H - 1, 0, min(Nq, 64), 0, min(Nk, 64)).cpu().numpy()
+    hk = (H - 1) // (H // Hkv)
+    want = orc.scores(c.q8[:, H - 1:H], c.k8[:, hk:hk + 1], B - 1, 0, 0, min(Nq, 64), 0, min(Nk, 64))
+    assert np.array_equal(got, want)
+
+
+def gqa_inputs(inp, Hkv):
+    """The same inputs with K and V cut to Hkv heads (every (H/Hkv)-th head)."""
+    g = inp.q.shape[1] // Hkv
+    return dataclasses.replace(inp, k=inp.k[:, ::g].contiguous(), v=inp.v[:, ::g].contiguous())
 
 
 def test_quantize_nhd_layout_and_zero_blocks(orc):
@@ -180,6 +210,9 @@ CASES = [
     dict(name="fp8_mask", B=1, H=2, Nq=256, Nk=320, d=128, pv="fp8", mask="half"),
     dict(name="sm_scale", B=1, H=2, Nq=256, Nk=256, d=128, sm_scale=0.05),
     dict(name="nhd", B=2, H=3, Nq=200, Nk=260, d=64, layout="NHD"),
+    dict(name="gqa", B=1, H=4, Hkv=2, Nq=300, Nk=417, d=128),
+    dict(name="gqa_fp8_causal", B=2, H=6, Hkv=2, Nq=257, Nk=257, d=64, pv="fp8", causal=True),
+    dict(name="mqa_nhd_mask_per_head", B=1, H=4, Hkv=1, Nq=200, Nk=333, d=128, layout="NHD", mask="rand_h"),
 ]
 
 
@@ -189,6 +222,8 @@ def test_attention_parity(orc, case):
     say(f"attention case {c}")
     B, H, Nq, Nk, d = c["B"], c["H"], c["Nq"], c["Nk"], c["d"]
     inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=11)
+    if "Hkv" in c:
+        inp = gqa_inputs(inp, c["Hkv"])
     mask = None
     if c.get("mask") == "half":
         mask = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)

@@ -18,7 +18,7 @@ from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_qu
 
 pytestmark = pytest.mark.gpu
 
-N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024}
+N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -57,10 +57,13 @@ def test_workload_parity(orc, name):
 
     # int32 scores: 256 rows x all keys, first and last rows of two heads
     nqp, nkp = c.q8.shape[2], c.k8.shape[2]
+    grp = w.H // (w.Hkv or w.H)  # query heads per key/value head
     for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        hk = h // grp
         for r0 in (0, nqp - 256):
             got = sage.debug_qk_int32(g, b, h, r0, 256, 0, nkp).cpu().numpy()
-            assert np.array_equal(got, orc.scores(c.q8, c.k8, b, h, r0, 256, 0, nkp)), ("scores", b, h, r0)
+            want = orc.scores(c.q8[:, h:h + 1], c.k8[:, hk:hk + 1], b, 0, r0, 256, 0, nkp)
+            assert np.array_equal(got, want), ("scores", b, h, r0)
     say("  int32 scores bit-exact")
 
     # attention
