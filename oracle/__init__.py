@@ -6,7 +6,9 @@ no code with it.  Arithmetic lives in ``sage_oracle.c`` (plain C loops, fp64 whe
 definition calls for it); this module only compiles that file with gcc and marshals numpy arrays
 through ctypes.
 
-Entry points (all inputs are host numpy arrays; bf16 tensors travel as their uint16 bit patterns):
+Entry points (all inputs are host numpy arrays; bf16 and fp16 tensors travel as their uint16 bit
+patterns, with ``dtype="bf16"`` or ``"fp16"`` saying which; masks are uint8/bool, nonzero = attend,
+or float32, added to the scaled scores):
 
 * codecs: ``f32_to_f16``, ``f16_to_f32``, ``f32_to_bf16``, ``f32_to_e4m3``, ``e4m3_to_f32``
 * ``kmean(K)``                      -- per-(b,h,channel) token mean of K, fp64 sum -> fp32
@@ -14,7 +16,7 @@ Entry points (all inputs are host numpy arrays; bf16 tensors travel as their uin
 * ``prep_v(V, pv)``                 -- fp16 V or per-channel e4m3 V with its scales
 * ``scores(q8, k8, ...)``           -- exact int32 Q8 . K8^T window of one head
 * ``attn_qe(...)``                  -- the quantized emulation (online softmax over BN-key tiles)
-* ``attn_ex(...)``                  -- fp64 exact attention on the unquantized bf16 inputs
+* ``attn_ex(...)``                  -- fp64 exact attention on the unquantized inputs
 * ``run_qe(...)``                   -- convenience: all the steps above for given rows
 """
 
@@ -63,14 +65,14 @@ def lib():
                      "orc_e4m3_to_f32_n"):
             getattr(L, name).argtypes = [P, P, I]
             getattr(L, name).restype = None
-        L.orc_kmean.argtypes = [P, I, I, I, I, P]
-        L.orc_quant_qk.argtypes = [P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P]
-        L.orc_prep_v_fp16.argtypes = [P, I, I, I, I, P]
-        L.orc_prep_v_fp8.argtypes = [P, I, I, I, I, P, P]
+        L.orc_kmean.argtypes = [P, i32, I, I, I, I, P]
+        L.orc_quant_qk.argtypes = [P, P, i32, P, I, I, I, I, I, I, I, I, P, P, P, P, P]
+        L.orc_prep_v_fp16.argtypes = [P, i32, I, I, I, I, P]
+        L.orc_prep_v_fp8.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
-        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32, P, I, P, P,
-                                  P]
-        L.orc_attn_ex.argtypes = [P, P, P, P, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32, P,
+                                  I, P, i32, P, P]
+        L.orc_attn_ex.argtypes = [P, P, P, i32, P, i32, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
         for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
                      "orc_attn_qe", "orc_attn_ex"):
             getattr(L, name).restype = None
@@ -142,12 +144,18 @@ def pad_n(n: int) -> int:
     return (n + 127) // 128 * 128
 
 
-def kmean(K):
-    """K: uint16 bf16 bits [B,H,Nk,d] -> fp32 [B,H,d]."""
+def _in_fp16(dtype: str) -> int:
+    if dtype not in ("bf16", "fp16"):
+        raise ValueError(dtype)
+    return 1 if dtype == "fp16" else 0
+
+
+def kmean(K, dtype="bf16"):
+    """K: uint16 bf16 or fp16 bits [B,H,Nk,d] -> fp32 [B,H,d]."""
     K = _c(K, np.uint16)
     B, H, Nk, d = K.shape
     out = np.empty((B, H, d), np.float32)
-    lib().orc_kmean(_p(K), B, H, Nk, d, _p(out))
+    lib().orc_kmean(_p(K), _in_fp16(dtype), B, H, Nk, d, _p(out))
     return out
 
 
@@ -161,15 +169,16 @@ class QuantQK:
     corr: np.ndarray  # fp32 [B,H,Nq]
 
 
-def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None) -> QuantQK:
-    """Q [B,H,Nq,d], K [B,Hkv,Nk,d] (Hkv divides H; query head h reads key head h // (H // Hkv))."""
+def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None, dtype="bf16") -> QuantQK:
+    """Q [B,H,Nq,d], K [B,Hkv,Nk,d] (Hkv divides H; query head h reads key head h // (H // Hkv)),
+    both of ``dtype``."""
     Q = _c(Q, np.uint16)
     K = _c(K, np.uint16)
     B, H, Nq, d = Q.shape
     Hkv, Nk = K.shape[1], K.shape[2]
     assert K.shape[0] == B and K.shape[3] == d and H % Hkv == 0
     if km is None:
-        km = kmean(K)
+        km = kmean(K, dtype)
     km = _c(km, np.float32)
     Nq_pad = pad_n(Nq) if Nq_pad is None else Nq_pad
     Nk_pad = pad_n(Nk) if Nk_pad is None else Nk_pad
@@ -178,23 +187,24 @@ def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None) -> QuantQK:
     qs = np.empty((B, H, (Nq + QBLK - 1) // QBLK), np.float32)
     ks = np.empty((B, Hkv, (Nk + QBLK - 1) // QBLK), np.float32)
     corr = np.empty((B, H, Nq), np.float32)
-    lib().orc_quant_qk(_p(Q), _p(K), _p(km), B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
+    lib().orc_quant_qk(_p(Q), _p(K), _in_fp16(dtype), _p(km), B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
                        _p(corr))
     return QuantQK(q8, k8, qs, ks, km, corr)
 
 
-def prep_v(V, pv: str = "fp16"):
-    """Returns (vhat, vs): fp16 bits uint16 [B,H,Nk,d] and None, or e4m3 uint8 [B,H,Nk,d] and fp32 [B,H,d]."""
+def prep_v(V, pv: str = "fp16", dtype="bf16"):
+    """V of ``dtype``.  Returns (vhat, vs): fp16 bits uint16 [B,H,Nk,d] and None, or e4m3 uint8
+    [B,H,Nk,d] and fp32 [B,H,d]."""
     V = _c(V, np.uint16)
     B, H, Nk, d = V.shape
     if pv == "fp16":
         out = np.empty(V.shape, np.uint16)
-        lib().orc_prep_v_fp16(_p(V), B, H, Nk, d, _p(out))
+        lib().orc_prep_v_fp16(_p(V), _in_fp16(dtype), B, H, Nk, d, _p(out))
         return out, None
     if pv == "fp8":
         out = np.empty(V.shape, np.uint8)
         vs = np.empty((B, H, d), np.float32)
-        lib().orc_prep_v_fp8(_p(V), B, H, Nk, d, _p(out), _p(vs))
+        lib().orc_prep_v_fp8(_p(V), _in_fp16(dtype), B, H, Nk, d, _p(out), _p(vs))
         return out, vs
     raise ValueError(pv)
 
@@ -216,16 +226,18 @@ def default_sm_scale(d: int) -> float:
 
 
 def _mask_arg(mask, B, H, Nq, Nk):
+    """(array, mask_h, is_f32): a floating mask is additive (float32), anything else boolean (uint8)."""
     if mask is None:
-        return None, 0
-    m = np.ascontiguousarray(mask, dtype=np.uint8)
+        return None, 0, 0
+    f32 = np.issubdtype(np.asarray(mask).dtype, np.floating)
+    m = np.ascontiguousarray(mask, dtype=np.float32 if f32 else np.uint8)
     assert m.ndim == 4 and m.shape[0] == B and m.shape[2] == Nq and m.shape[3] == Nk and m.shape[1] in (1, H)
-    return m, m.shape[1]
+    return m, m.shape[1], int(f32)
 
 
 def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_scale=None, BN=64, tau=0.0,
-            lsum_rounded=False, rows=None):
-    """Quantized emulation.  Returns (o32 [R,d] fp32, obf [R,d] bf16 bits, lse [R] fp32).
+            lsum_rounded=False, rows=None, out_dtype="bf16"):
+    """Quantized emulation.  Returns (o32 [R,d] fp32, o16 [R,d] bits of out_dtype, lse [R] fp32).
 
     BN: keys per online-softmax tile; tau: the reference maximum is raised only when a tile's
     maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.
@@ -233,7 +245,7 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     B, H, Nq_pad, d = qk.q8.shape
     Hkv, Nk_pad = qk.k8.shape[1], qk.k8.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
-    m, mh = _mask_arg(mask, B, H, Nq, Nk)
+    m, mh, mf = _mask_arg(mask, B, H, Nq, Nk)
     if rows is None:
         R = B * H * Nq
         rp = None
@@ -242,16 +254,17 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
         R = rows.size
         rp = rows
     o32 = np.empty((R, d), np.float32)
-    obf = np.empty((R, d), np.uint16)
+    o16 = np.empty((R, d), np.uint16)
     lse = np.empty((R,), np.float32)
     lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
-                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d, Nq_pad,
-                      Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32), _p(obf), _p(lse))
-    return o32, obf, lse
+                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mf, mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d,
+                      Nq_pad, Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32),
+                      _in_fp16(out_dtype), _p(o16), _p(lse))
+    return o32, o16, lse
 
 
-def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
-    """fp64 exact attention on the bf16 inputs.  Returns (out [R,d] fp64, lse [R] fp64)."""
+def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None, dtype="bf16"):
+    """fp64 exact attention on the inputs (bits of ``dtype``).  Returns (out [R,d] fp64, lse [R] fp64)."""
     Q = _c(Q, np.uint16)
     K = _c(K, np.uint16)
     V = _c(V, np.uint16)
@@ -259,7 +272,7 @@ def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
     Hkv, Nk = K.shape[1], K.shape[2]
     assert H % Hkv == 0 and V.shape[1] == Hkv
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
-    m, mh = _mask_arg(mask, B, H, Nq, Nk)
+    m, mh, mf = _mask_arg(mask, B, H, Nq, Nk)
     if rows is None:
         R = B * H * Nq
         rp = None
@@ -268,7 +281,7 @@ def attn_ex(Q, K, V, *, causal=False, mask=None, sm_scale=None, rows=None):
         R = rp.size
     out = np.empty((R, d), np.float64)
     lse = np.empty((R,), np.float64)
-    lib().orc_attn_ex(_p(Q), _p(K), _p(V), _p(m), mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d, _p(rp), R,
+    lib().orc_attn_ex(_p(Q), _p(K), _p(V), _in_fp16(dtype), _p(m), mf, mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d, _p(rp), R,
                       _p(out), _p(lse))
     return out, lse
 
@@ -279,16 +292,17 @@ class QEResult:
     vhat: np.ndarray
     vs: np.ndarray | None
     o32: np.ndarray
-    obf: np.ndarray
+    o16: np.ndarray  # output bits (bf16 or fp16)
     lse: np.ndarray
 
 
 def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, tau=0.0, lsum_rounded=False,
-           rows=None) -> QEResult:
-    """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe."""
-    qk = quant_qk(Q, K)
-    vhat, vs = prep_v(V, pv)
+           rows=None, dtype="bf16", out_dtype=None) -> QEResult:
+    """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe.  The output dtype
+    defaults to the input dtype."""
+    qk = quant_qk(Q, K, dtype=dtype)
+    vhat, vs = prep_v(V, pv, dtype=dtype)
     Nq, Nk = Q.shape[2], K.shape[2]
-    o32, obf, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, tau=tau,
-                            lsum_rounded=lsum_rounded, rows=rows)
-    return QEResult(qk, vhat, vs, o32, obf, lse)
+    o32, o16, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, tau=tau,
+                            lsum_rounded=lsum_rounded, rows=rows, out_dtype=out_dtype or dtype)
+    return QEResult(qk, vhat, vs, o32, o16, lse)

@@ -22,7 +22,12 @@
  * Readings where the pages are silent (each one is listed in the design notes):
  *  - quantization block = 64 tokens for Q and K; symmetric scale = absmax/127, codes in [-127,127];
  *    an all-zero block has scale 0 and codes 0;
- *  - every rounding is round-to-nearest-even (int8 codes, fp16, e4m3, bf16 output);
+ *  - every rounding is round-to-nearest-even (int8 codes, fp16, e4m3, bf16 or fp16 output);
+ *  - Q, K and V are all bf16 or all fp16 ("in_fp16"); each value is decoded exactly to fp32 and
+ *    the method then runs unchanged; the output has its own dtype (bf16 or fp16);
+ *  - a float32 attention mask is additive: M_ij is added to the scaled score sm_scale * q_i.k_j
+ *    (natural-log units) before the softmax, and -inf entries drop the key; a boolean (uint8)
+ *    mask drops the keys whose entry is zero;
  *  - the K mean is summed in fp64 over all Nk tokens (mask and causality ignored), divided by Nk
  *    in fp64 and rounded once to fp32;
  *  - P for FP8 PV is quantized as e4m3(448 * p) with saturation, V per channel as
@@ -75,6 +80,9 @@ float orc_f16_to_f32(uint16_t h) {
     v = ldexp((double)(1024 + m), e - 25);
   return (float)(s ? -v : v);
 }
+
+/* An input element: bf16 (in_fp16 = 0) or IEEE binary16 (in_fp16 = 1) bits. */
+static float orc_in_to_f32(uint16_t h, int in_fp16) { return in_fp16 ? orc_f16_to_f32(h) : orc_bf16_to_f32(h); }
 
 /* fp32 -> binary16, round to nearest, ties to even; overflow to infinity. */
 uint16_t orc_f32_to_f16(float x) {
@@ -184,14 +192,14 @@ int orc_num_threads(void) {
 
 /* ------------------------------------------------------------------------------------------ */
 /* Step 1: K mean over tokens (smooth_k).                                                     */
-/* K is bf16 [B][H][Nk][d]; kmean is fp32 [B][H][d].                                          */
+/* K is bf16 or fp16 (in_fp16) [B][H][Nk][d]; kmean is fp32 [B][H][d].                       */
 /* ------------------------------------------------------------------------------------------ */
-void orc_kmean(const uint16_t* K, int64_t B, int64_t H, int64_t Nk, int64_t d, float* kmean) {
+void orc_kmean(const uint16_t* K, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, float* kmean) {
 #pragma omp parallel for schedule(static)
   for (int64_t bh = 0; bh < B * H; ++bh) {
     for (int64_t c = 0; c < d; ++c) {
       double s = 0.0;
-      for (int64_t t = 0; t < Nk; ++t) s += (double)orc_bf16_to_f32(K[(bh * Nk + t) * d + c]);
+      for (int64_t t = 0; t < Nk; ++t) s += (double)orc_in_to_f32(K[(bh * Nk + t) * d + c], in_fp16);
       kmean[bh * d + c] = (float)(s / (double)Nk);
     }
   }
@@ -230,13 +238,14 @@ static void quantize_blocks(const float* X, int64_t N, int64_t N_pad, int64_t d,
   memset(x8 + N * d, 0, (size_t)((N_pad - N) * d));
 }
 
-/* Q bf16 [B][H][Nq][d]; K bf16 [B][Hkv][Nk][d]; kmean fp32 [B][Hkv][d] (from orc_kmean).
+/* Q [B][H][Nq][d], K [B][Hkv][Nk][d], both bf16 or both fp16 (in_fp16); kmean fp32 [B][Hkv][d]
+ * (from orc_kmean).
  * Hkv divides H; query head h reads key/value head h / (H / Hkv) (group-query attention).
  * Outputs: q8 [B][H][Nq_pad][d], k8 [B][Hkv][Nk_pad][d], qs [B][H][ceil(Nq/64)],
  *          ks [B][Hkv][ceil(Nk/64)], corr [B][H][Nq] = fp32(sum_c fp64(Q_ic) * fp64(kmean_c)) with
  *          the K mean of the query head's key/value head.
  * K is smoothed as fp32(K - kmean) (one rounding) before quantizing. */
-void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int64_t B, int64_t H, int64_t Hkv,
+void orc_quant_qk(const uint16_t* Q, const uint16_t* K, int in_fp16, const float* kmean, int64_t B, int64_t H, int64_t Hkv,
                   int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8, int8_t* k8,
                   float* qs, float* ks, float* corr) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
@@ -245,7 +254,7 @@ void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int6
     float* xk = (float*)malloc((size_t)(Nk * d) * sizeof(float));
     const float* km = kmean + bh * d;
     for (int64_t t = 0; t < Nk; ++t)
-      for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_bf16_to_f32(K[(bh * Nk + t) * d + c]) - km[c];
+      for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_in_to_f32(K[(bh * Nk + t) * d + c], in_fp16) - km[c];
     quantize_blocks(xk, Nk, Nk_pad, d, k8 + bh * Nk_pad * d, ks + bh * nbk);
     free(xk);
   }
@@ -253,7 +262,7 @@ void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int6
   for (int64_t bh = 0; bh < B * H; ++bh) {
     float* xq = (float*)malloc((size_t)(Nq * d) * sizeof(float));
     const float* km = kmean + ((bh / H) * Hkv + (bh % H) / (H / Hkv)) * d;
-    for (int64_t i = 0; i < Nq * d; ++i) xq[i] = orc_bf16_to_f32(Q[bh * Nq * d + i]);
+    for (int64_t i = 0; i < Nq * d; ++i) xq[i] = orc_in_to_f32(Q[bh * Nq * d + i], in_fp16);
     quantize_blocks(xq, Nq, Nq_pad, d, q8 + bh * Nq_pad * d, qs + bh * nbq);
     for (int64_t i = 0; i < Nq; ++i) {
       double s = 0.0;
@@ -266,23 +275,24 @@ void orc_quant_qk(const uint16_t* Q, const uint16_t* K, const float* kmean, int6
 
 /* ------------------------------------------------------------------------------------------ */
 /* Step 3: V preparation.  Output keeps V's own layout [B][H][Nk][d].                         */
-/* fp16: vhat = fp16_rne(V).                                                                  */
+/* V is bf16 or fp16 (in_fp16).                                                               */
+/* fp16: vhat = fp16_rne(V) (the identity for fp16 V).                                        */
 /* fp8:  vmax_c = max_t |V_tc|; vs_c = fp32(vmax_c / 448); vinv_c = fp32(448 / vmax_c)        */
 /*       (0 when vmax_c = 0); vhat = e4m3_rne_sat(fp32(V * vinv_c)).                          */
 /* ------------------------------------------------------------------------------------------ */
-void orc_prep_v_fp16(const uint16_t* V, int64_t B, int64_t H, int64_t Nk, int64_t d, uint16_t* vhat) {
+void orc_prep_v_fp16(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, uint16_t* vhat) {
   int64_t n = B * H * Nk * d;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) vhat[i] = orc_f32_to_f16(orc_bf16_to_f32(V[i]));
+  for (int64_t i = 0; i < n; ++i) vhat[i] = orc_f32_to_f16(orc_in_to_f32(V[i], in_fp16));
 }
 
-void orc_prep_v_fp8(const uint16_t* V, int64_t B, int64_t H, int64_t Nk, int64_t d, uint8_t* vhat, float* vs) {
+void orc_prep_v_fp8(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, uint8_t* vhat, float* vs) {
 #pragma omp parallel for schedule(static)
   for (int64_t bh = 0; bh < B * H; ++bh) {
     for (int64_t c = 0; c < d; ++c) {
       float vmax = 0.0f;
       for (int64_t t = 0; t < Nk; ++t) {
-        float a = fabsf(orc_bf16_to_f32(V[(bh * Nk + t) * d + c]));
+        float a = fabsf(orc_in_to_f32(V[(bh * Nk + t) * d + c], in_fp16));
         if (a > vmax) vmax = a;
       }
       float sc = 0.0f, inv = 0.0f;
@@ -293,7 +303,7 @@ void orc_prep_v_fp8(const uint16_t* V, int64_t B, int64_t H, int64_t Nk, int64_t
       vs[bh * d + c] = sc;
       for (int64_t t = 0; t < Nk; ++t) {
         int64_t idx = (bh * Nk + t) * d + c;
-        vhat[idx] = orc_f32_to_e4m3(orc_bf16_to_f32(V[idx]) * inv);
+        vhat[idx] = orc_f32_to_e4m3(orc_in_to_f32(V[idx], in_fp16) * inv);
       }
     }
   }
@@ -321,21 +331,22 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /* Step 5: quantized attention forward (the emulation the GPU path must reproduce).           */
 /*                                                                                            */
 /* rows: flattened row ids (b*H + h)*Nq + i to evaluate; NULL = all B*H*Nq rows in order.     */
-/* mask: uint8 [B][mask_h][Nq][Nk], nonzero = attend; mask_h is 1 (broadcast over heads) or H; */
-/*       mask == NULL means no mask.                                                          */
+/* mask: [B][mask_h][Nq][Nk]; mask_h is 1 (broadcast over heads) or H; NULL means no mask.     */
+/*       mask_f32 = 0: uint8, nonzero = attend; mask_f32 = 1: fp32 added to the scaled score  */
+/*       (natural-log units), -inf = drop.                                                     */
 /* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
 /* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
 /* BN: keys per online-softmax tile; tau: lazy-maximum threshold in log2 units (0 = exact).    */
 /* lsum_rounded: 0 = l sums the fp32 p, 1 = l sums P as rounded for PV.                       */
-/* Outputs per requested row: o32 [nrows][d] (fp32 O before the bf16 rounding, may be NULL),  */
-/* obf [nrows][d] (bf16 bits), lse [nrows] (natural log, fp32).                               */
+/* Outputs per requested row: o32 [nrows][d] (fp32 O before the output rounding, may be NULL),*/
+/* o16 [nrows][d] (bf16 bits, or fp16 bits if out_fp16), lse [nrows] (natural log, fp32).     */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
-                 const void* vhat, const float* vs, int pv_fp8, const uint8_t* mask, int64_t mask_h, int causal,
+                 const void* vhat, const float* vs, int pv_fp8, const void* mask, int mask_f32, int64_t mask_h,
+                 int causal,
                  float sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
                  int64_t Nk_pad, int64_t BN, double tau, int lsum_rounded, const int64_t* rows, int64_t nrows,
-                 float* o32,
-                 uint16_t* obf, float* lse) {
+                 float* o32, int out_fp16, uint16_t* o16, float* lse) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
   if (rows == NULL) nrows = B * H * Nq;
 #pragma omp parallel
@@ -350,7 +361,9 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
       int64_t bhk = b * Hkv + h / (H / Hkv); /* key/value head of this query head */
       const int8_t* q = q8 + (bh * Nq_pad + i) * d;
       const int8_t* kh = k8 + bhk * Nk_pad * d;
-      const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
+      const int64_t moff = ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk;
+      const uint8_t* mrow = (mask && !mask_f32) ? (const uint8_t*)mask + moff : NULL;
+      const float* madd = (mask && mask_f32) ? (const float*)mask + moff : NULL;
       float qscale = qs[bh * nbq + i / ORC_QBLK];
       float m = -INFINITY, l = 0.0f;
       for (int64_t c = 0; c < d; ++c) o[c] = 0.0f;
@@ -362,6 +375,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           int valid = 1;
           if (causal && j > i) valid = 0;
           if (mrow && mrow[j] == 0) valid = 0;
+          if (madd && madd[j] == -INFINITY) valid = 0;
           if (!valid) {
             s[j - j0] = -INFINITY;
             continue;
@@ -371,6 +385,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           for (int64_t c = 0; c < d; ++c) acc += (int32_t)q[c] * (int32_t)k[c];
           float cst = (qscale * ks[bhk * nbk + j / ORC_QBLK]) * sm_scale;
           s[j - j0] = (float)acc * cst;
+          if (madd) s[j - j0] += madd[j]; /* additive mask, natural-log units */
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
         float mnew = m;
@@ -411,7 +426,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         else
           out = o[c] / l;
         if (o32) o32[r * d + c] = out;
-        if (obf) obf[r * d + c] = orc_f32_to_bf16(out);
+        if (o16) o16[r * d + c] = out_fp16 ? orc_f32_to_f16(out) : orc_f32_to_bf16(out);
       }
       if (lse) {
         if (l == 0.0f)
@@ -427,12 +442,13 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* Exact attention in fp64 on the original bf16 inputs: no smoothing, no quantization.        */
-/* s_ij = sm_scale * sum_c Q_ic K_jc; invalid entries -inf; two-pass softmax; O = P V;        */
+/* Exact attention in fp64 on the original bf16 or fp16 inputs: no smoothing, no quantization. */
+/* s_ij = sm_scale * sum_c Q_ic K_jc (+ M_ij for an fp32 mask); invalid entries -inf;         */
+/* two-pass softmax; O = P V;                                                                 */
 /* LSE_i = log sum_j exp(s_ij).  A row with no valid key gives O = 0, LSE = -inf.             */
 /* ------------------------------------------------------------------------------------------ */
-void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint8_t* mask, int64_t mask_h,
-                 int causal, double sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in_fp16, const void* mask, int mask_f32,
+                 int64_t mask_h, int causal, double sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                  const int64_t* rows, int64_t nrows, double* out, double* lse) {
   if (rows == NULL) nrows = B * H * Nq;
 #pragma omp parallel
@@ -444,17 +460,20 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
       int64_t rid = rows ? rows[r] : r;
       int64_t bh = rid / Nq, i = rid % Nq, b = bh / H, h = bh % H;
       int64_t bhk = b * Hkv + h / (H / Hkv); /* key/value head of this query head */
-      const uint8_t* mrow = mask ? mask + ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk : NULL;
-      for (int64_t c = 0; c < d; ++c) q[c] = (double)orc_bf16_to_f32(Q[(bh * Nq + i) * d + c]);
+      const int64_t moff = ((b * mask_h + (mask_h == 1 ? 0 : h)) * Nq + i) * Nk;
+      const uint8_t* mrow = (mask && !mask_f32) ? (const uint8_t*)mask + moff : NULL;
+      const float* madd = (mask && mask_f32) ? (const float*)mask + moff : NULL;
+      for (int64_t c = 0; c < d; ++c) q[c] = (double)orc_in_to_f32(Q[(bh * Nq + i) * d + c], in_fp16);
       double mx = -INFINITY;
       for (int64_t j = 0; j < Nk; ++j) {
-        if ((causal && j > i) || (mrow && mrow[j] == 0)) {
+        if ((causal && j > i) || (mrow && mrow[j] == 0) || (madd && madd[j] == -INFINITY)) {
           s[j] = -INFINITY;
           continue;
         }
         double acc = 0.0;
-        for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_bf16_to_f32(K[(bhk * Nk + j) * d + c]);
+        for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_in_to_f32(K[(bhk * Nk + j) * d + c], in_fp16);
         s[j] = sm_scale * acc;
+        if (madd) s[j] += (double)madd[j];
         if (s[j] > mx) mx = s[j];
       }
       double* o = out + r * d;
@@ -468,7 +487,7 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
         if (s[j] == -INFINITY) continue;
         double p = exp(s[j] - mx);
         den += p;
-        for (int64_t c = 0; c < d; ++c) o[c] += p * (double)orc_bf16_to_f32(V[(bhk * Nk + j) * d + c]);
+        for (int64_t c = 0; c < d; ++c) o[c] += p * (double)orc_in_to_f32(V[(bhk * Nk + j) * d + c], in_fp16);
       }
       for (int64_t c = 0; c < d; ++c) o[c] /= den;
       if (lse) lse[r] = mx + log(den);

@@ -15,7 +15,10 @@ group-query workload):
     Kn = randn(B, Hk, Nk, d)
     Kb = sigma * randn(B, Hk, 1, d)
     V  = randn(B, Hk, Nk, d)
-then K = bf16(Kn + Kb), Q = bf16(Q), V = bf16(V).
+then K = bf16(Kn + Kb), Q = bf16(Q), V = bf16(V) (or fp16 of the same draws for fp16 inputs).
+
+``additive_mask`` turns a boolean mask into the equivalent float32 additive mask (0 to attend, -inf
+to drop) and ``random_additive_mask`` draws a float32 mask with finite biases and -inf holes.
 """
 
 from __future__ import annotations
@@ -67,29 +70,36 @@ WORKLOADS = {
 
 @dataclass
 class Inputs:
-    q: torch.Tensor  # bf16 [B,H,Nq,d] (CPU)
+    q: torch.Tensor  # bf16 or fp16 [B,H,Nq,d] (CPU)
     k: torch.Tensor
     v: torch.Tensor
     mask: torch.Tensor | None  # bool [B,1,Nq,Nk] (CPU) or None
 
     def bits(self, t: torch.Tensor) -> np.ndarray:
-        """bf16 tensor -> numpy uint16 bit patterns (what the oracle consumes)."""
+        """bf16 / fp16 tensor -> numpy uint16 bit patterns (what the oracle consumes)."""
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    @property
+    def dtype(self) -> str:
+        """"bf16" or "fp16": the element type of q, k and v."""
+        return "fp16" if self.q.dtype == torch.float16 else "bf16"
 
     @property
     def mask_u8(self):
         return None if self.mask is None else self.mask.numpy().astype(np.uint8)
 
 
-def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0) -> Inputs:
-    """Hkv > 0 draws K and V with Hkv heads (group-query attention), in the same order."""
+def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0, dtype=torch.bfloat16) -> Inputs:
+    """Hkv > 0 draws K and V with Hkv heads (group-query attention), in the same order.  dtype is
+    torch.bfloat16 or torch.float16."""
+    assert dtype in (torch.bfloat16, torch.float16)
     Hk = Hkv if Hkv > 0 else H
     g = torch.Generator("cpu").manual_seed(seed)
     q = torch.randn(B, H, Nq, d, generator=g, dtype=torch.float32)
     kn = torch.randn(B, Hk, Nk, d, generator=g, dtype=torch.float32)
     kb = sigma * torch.randn(B, Hk, 1, d, generator=g, dtype=torch.float32)
     v = torch.randn(B, Hk, Nk, d, generator=g, dtype=torch.float32)
-    k = (kn + kb).to(torch.bfloat16)
+    k = (kn + kb).to(dtype)
     del kn
     m = None
     if mask == "half_keys":
@@ -97,7 +107,7 @@ def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0) -> Inputs:
         m[:, :, :, Nk // 2:] = False
     elif mask is not None:
         raise ValueError(mask)
-    return Inputs(q.to(torch.bfloat16), k, v.to(torch.bfloat16), m)
+    return Inputs(q.to(dtype), k, v.to(dtype), m)
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
@@ -108,3 +118,16 @@ def random_mask(B, Hm, Nq, Nk, p_keep=0.7, seed=1) -> torch.Tensor:
     """Element-wise random boolean mask (True = attend) for edge-case tests."""
     g = torch.Generator("cpu").manual_seed(seed)
     return torch.rand(B, Hm, Nq, Nk, generator=g) < p_keep
+
+
+def additive_mask(mask: torch.Tensor) -> torch.Tensor:
+    """Boolean mask (True = attend) -> float32 additive mask: 0 where True, -inf where False."""
+    return torch.zeros(mask.shape, dtype=torch.float32).masked_fill(~mask, float("-inf"))
+
+
+def random_additive_mask(B, Hm, Nq, Nk, p_drop=0.2, scale=2.0, seed=3) -> torch.Tensor:
+    """float32 additive mask: biases scale * randn, with a fraction p_drop of entries at -inf."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    m = scale * torch.randn(B, Hm, Nq, Nk, generator=g, dtype=torch.float32)
+    drop = torch.rand(B, Hm, Nq, Nk, generator=g) < p_drop
+    return m.masked_fill(drop, float("-inf"))

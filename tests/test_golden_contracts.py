@@ -29,7 +29,7 @@ def test_oracle_shapes_follow_page_contracts(orc):
         inp = make_inputs(B, H, N, N, d, seed=0)
         rows = np.arange(0, B * H * N, 97, dtype=np.int64)
         r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), rows=rows)
-        assert r.obf.shape == (rows.size, d) and r.lse.shape == (rows.size,)
+        assert r.o16.shape == (rows.size, d) and r.lse.shape == (rows.size,)
         if "lse" in case:
             assert case["lse"] == case["q"][:3]
         assert case["out"] == case["q"]

@@ -181,7 +181,7 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
 
 
 def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16"):
-    qe_o = f32_of_bf16_bits(r.obf)
+    qe_o = f32_of_bf16_bits(r.o16)
     e1 = rel_l1(got_o, qe_o)
     assert e1 <= QE_REL_L1, f"rel-L1 vs quantized emulation {e1}"
     assert_lse_close(got_l, r.lse, QE_LSE)

@@ -154,7 +154,7 @@ def test_qe_all_true_mask_is_no_mask(orc):
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     a = orc.run_qe(Qb, Kb, Vb)
     b = orc.run_qe(Qb, Kb, Vb, mask=np.ones((1, 1, 100, 130), np.uint8))
-    assert np.array_equal(a.obf, b.obf) and np.array_equal(a.lse, b.lse)
+    assert np.array_equal(a.o16, b.o16) and np.array_equal(a.lse, b.lse)
 
 
 def test_qe_rows_subset_matches_full(orc):
@@ -163,7 +163,7 @@ def test_qe_rows_subset_matches_full(orc):
     full = orc.run_qe(Qb, Kb, Vb, causal=True)
     rows = np.array([0, 69, 70, 139, 200, 279], np.int64)
     sub = orc.run_qe(Qb, Kb, Vb, causal=True, rows=rows)
-    assert np.array_equal(sub.obf, full.obf[rows]) and np.array_equal(sub.lse, full.lse[rows])
+    assert np.array_equal(sub.o16, full.o16[rows]) and np.array_equal(sub.lse, full.lse[rows])
 
 
 # ----------------------------------------------------------------------------------------------
@@ -241,7 +241,7 @@ def test_qe_lazy_maximum_only_moves_rounding(orc, sm):
     assert abs(_rel_l1(b.o32, eo) - _rel_l1(a.o32, eo)) < 1e-3
     # with tau = 0 the emulation is the exact running maximum: identical to tau = 1e-30
     c = orc.run_qe(Qb, Kb, Vb, BN=64, tau=1e-30, sm_scale=sm)
-    assert np.array_equal(c.obf, a.obf)
+    assert np.array_equal(c.o16, a.o16)
 
 
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
@@ -280,7 +280,7 @@ def test_gqa_equals_repeated_kv_heads(orc, pv):
     assert np.array_equal(np.repeat(g.qk.k8, 2, axis=1), r.qk.k8)
     assert np.array_equal(np.repeat(g.qk.ks, 2, axis=1), r.qk.ks)
     assert np.array_equal(g.qk.q8, r.qk.q8) and np.array_equal(g.qk.corr, r.qk.corr)
-    assert np.array_equal(g.obf, r.obf) and np.array_equal(g.lse, r.lse)
+    assert np.array_equal(g.o16, r.o16) and np.array_equal(g.lse, r.lse)
     eg, lg = orc.attn_ex(Qb, Kg, Vg, causal=True)
     er, lr = orc.attn_ex(Qb, Kr, Vr, causal=True)
     assert np.array_equal(eg, er) and np.array_equal(lg, lr)
