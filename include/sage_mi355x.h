@@ -24,8 +24,10 @@
  *    and the call returns without waiting; asynchronous faults surface at the caller's next sync.
  *  - Host-side argument validation runs before any HIP call and before any launch; a non-OK status
  *    means nothing was enqueued.  Launch failures report SAGE_ERR_HIP.
- *  - Inputs are bf16 with a contiguous channel (head_dim) axis; batch, head and token strides are
- *    free (HND or NHD), given in elements, and must keep every row 16-byte aligned.
+ *  - Inputs are bf16 or fp16, q, k and v alike (the input types the SageAttention usage section
+ *    names), with a contiguous channel (head_dim) axis; batch, head and token
+ *    strides are free (HND or NHD), given in elements, and must keep every row 16-byte aligned.
+ *    An fp16 input is decoded exactly; the method then runs as for bf16.
  *  - head_dim d must be 64 or 128.  Index arithmetic is 64-bit.
  */
 #ifndef SAGE_MI355X_H
@@ -41,12 +43,19 @@ extern "C" {
 typedef enum {
   SAGE_OK = 0,
   SAGE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride, alignment or dtype mismatch */
-  SAGE_ERR_UNSUPPORTED = 2,      /* head_dim not 64/128, fp16 input, or a device other than gfx950 */
+  SAGE_ERR_UNSUPPORTED = 2,      /* head_dim not 64/128, or a device other than gfx950 */
   SAGE_ERR_WORKSPACE = 3,        /* workspace smaller than the matching *_workspace_bytes() value */
   SAGE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } sage_status;
 
-typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1 /* reserved: not supported yet */ } sage_dtype;
+/* Element type of Q, K, V and of the output O. */
+typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1 } sage_dtype;
+
+/* Attention mask element type (optional boolean or float32 mask: Triton INT8/FP16 kernel section).
+ *   SAGE_MASK_BOOL: uint8, nonzero = attend, 0 = masked out.
+ *   SAGE_MASK_F32:  fp32 added to the scaled score sm_scale * q.k (natural-log units) before the
+ *                   softmax; -inf masks the key.  Entries must be finite or -inf. */
+typedef enum { SAGE_MASK_BOOL = 0, SAGE_MASK_F32 = 1 } sage_mask_dtype;
 
 typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_dtype;
 
@@ -103,15 +112,15 @@ int sage_rowsum_rounded(sage_pv_dtype pv);
  * Host only. */
 size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t d);
 
-/* Step 1 (quantize).  Reads q [B,H,Nq,d] and k [B,Hkv,Nk,d] (bf16, same B and d, Hkv dividing H;
+/* Step 1 (quantize).  Reads q [B,H,Nq,d] and k [B,Hkv,Nk,d] (both bf16 or both fp16, same B and d, Hkv dividing H;
  * out->H = H, out->Hkv = Hkv), writes every buffer of *out.
  * Per key head (b,h): k_mean = fp32(sum_t fp64(K[t,:]) / Nk); Ks = fp32(K - k_mean); for every 64-token
  * block of Q and of Ks: scale = amax/127, code = clamp(rne(x * (127/amax)), -127, 127)
  * (IEEE fp32 divisions, round-to-nearest-even); lse_corr[i] = fp32(sum_c fp64(Q[i,c])*fp64(k_mean[c])).
  * Sources: per-block INT8 Q/K and smooth_k on the Triton INT8/FP16 kernel section; smoothing by
  * the global token mean on the sageattn3_blackwell usage section (per_block_mean=False).
- * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, mismatched B/H/d, wrong pads or
- * misaligned rows; UNSUPPORTED for d not in {64,128} or non-bf16 input; WORKSPACE if
+ * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, mismatched B/H/d/dtype, wrong
+ * pads or misaligned rows; UNSUPPORTED for d not in {64,128}; WORKSPACE if
  * workspace_bytes < sage_quantize_workspace_bytes(). */
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
                              void* workspace, size_t workspace_bytes, void* stream);
@@ -119,7 +128,7 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
 /* Bytes of workspace sage_prepare_v needs (fp8: per-chunk partial maxima of |V|; fp16: 0). Host only. */
 size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv);
 
-/* Step 2a (V preparation).  v bf16 [B,H,Nk,d].
+/* Step 2a (V preparation).  v bf16 or fp16 [B,H,Nk,d].
  *   SAGE_PV_FP16:     v_t = fp16 (round to nearest even) of V, 2-byte elements [B][H][d][Nk_pad];
  *                     v_scale is not used (may be NULL).
  *   SAGE_PV_FP8_E4M3: v_scale fp32 [B][H][d] = max_t |V[t,c]| / 448 (0 for an all-zero channel),
@@ -144,15 +153,16 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
                                 int64_t mask_h);
 
 /* Step 2 (attention, all in one): sage_prepare_v into the workspace, then sage_attn_fwd_prepared.
- *   qk: from sage_quantize_qk; v: bf16 [B,Hkv,Nk,d].
- *   mask: NULL, or uint8 with nonzero = attend, shape [B][mask_h][Nq][Nk] addressed as
- *         mask + b*mask_stride_b + h*mask_stride_h + i*mask_stride_q + j (mask_h in {1, H};
- *         mask_stride_h is ignored when mask_h == 1; mask_stride_b may be 0 to broadcast over
- *         the batch).  (Boolean mask semantics: Triton INT8/FP16 kernel examples section, where
- *         False entries are masked out.)
+ *   qk: from sage_quantize_qk; v: bf16 or fp16 [B,Hkv,Nk,d].
+ *   mask: NULL, or a mask of mask_dtype (see sage_mask_dtype), shape [B][mask_h][Nq][Nk],
+ *         addressed as mask + b*mask_stride_b + h*mask_stride_h + i*mask_stride_q + j (element
+ *         offsets; mask_h in {1, H}; mask_stride_h is ignored when mask_h == 1; mask_stride_b may
+ *         be 0 to broadcast over the batch; an fp32 mask must be 4-byte aligned).  (Boolean mask
+ *         semantics: Triton INT8/FP16 kernel examples section, where False entries are masked out.)
  *   causal: key j is visible to query i only if j <= i (top-left aligned).
  *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
- *   out: [B,H,Nq,d] of out_dtype (must be SAGE_BF16) addressed with out_stride_{b,h,n}.
+ *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 or SAGE_FP16, rounded to nearest even) addressed with
+ *        out_stride_{b,h,n}.
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled, unsmoothed
  *        scores (lse_corr added back), for merging partial results ("return_lse" on the
  *        sageattn section and on "Utilize SageAttention for Distributed Inference").
@@ -162,9 +172,11 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  * sums P as rounded or unrounded per sage_rowsum_rounded(); O and l accumulate in fp32.  Keys j >= Nk are masked
  * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
  * gets O = 0 and LSE = -inf.
- * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, mask_h not
- * in {1,H}), UNSUPPORTED (d, dtype, pv, non-gfx950 device), WORKSPACE (too small), HIP. */
-sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const uint8_t* mask, int64_t mask_h,
+ * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, unknown
+ * dtype or mask_dtype, mask_h not in {1,H}), UNSUPPORTED (d, pv, non-gfx950 device), WORKSPACE (too
+ * small), HIP. */
+sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const void* mask,
+                          sage_mask_dtype mask_dtype, int64_t mask_h,
                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
                           float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
                           int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
@@ -175,7 +187,7 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
  * workspace: at least sage_mask_workspace_bytes(B, Nq, Nk, mask_h) bytes (may be NULL without a
  * mask).  Other arguments and errors as for sage_attn_fwd. */
 sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
-                                   const uint8_t* mask, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
+                                   const void* mask, sage_mask_dtype mask_dtype, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
                                    int64_t mask_stride_q, int causal, float sm_scale, void* out,
                                    sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
                                    int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,

@@ -5,8 +5,9 @@ HIP stream; every step of the computation runs in the library's gfx950 kernels. 
 is missing, every call raises -- there is no fallback path.
 
 User-level entry point, shaped like the pages' ``sageattn`` (SageAttention docs digest, context7
-llms.txt, section "sageattn -- Auto-selecting attention kernel") plus the boolean ``attn_mask`` of
-the Triton INT8/FP16 kernel examples and the FP8 PV option of ``sageattn_qk_int8_pv_fp8_cuda``::
+llms.txt, section "sageattn -- Auto-selecting attention kernel") plus the boolean or float32
+``attn_mask`` of the Triton INT8/FP16 kernel section and the FP8 PV option of
+``sageattn_qk_int8_pv_fp8_cuda``; q, k and v are bf16 or fp16 and the output takes their dtype::
 
     out = sageattn(q, k, v, tensor_layout="HND", is_causal=False, attn_mask=None,
                    sm_scale=None, return_lse=False, pv_dtype="fp16")
@@ -28,6 +29,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsage_mi355x.so")
 
 SAGE_BF16, SAGE_FP16 = 0, 1
+SAGE_MASK_BOOL, SAGE_MASK_F32 = 0, 1
 PV_CODES = {"fp16": 0, "fp8": 1, "fp8_e4m3": 1}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
@@ -92,10 +94,10 @@ def load_library():
     L.sage_mask_workspace_bytes.restype = SZ
     L.sage_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I, I64]
     L.sage_fwd_workspace_bytes.restype = SZ
-    L.sage_attn_fwd.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, I64, I64, I64, I64, I, F, I, P, I,
+    L.sage_attn_fwd.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, I, I64, I64, I64, I64, I, F, I, P, I,
                                 I64, I64, I64, P, P, SZ, P]
     L.sage_attn_fwd.restype = I
-    L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I64, I64, I64, I64, I, F, P, I, I64, I64,
+    L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I, I64, I64, I64, I64, I, F, P, I, I64, I64,
                                          I64, P, P, SZ, P]
     L.sage_attn_fwd_prepared.restype = I
     L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
@@ -134,15 +136,18 @@ def rowsum_rounded(pv_dtype: str = "fp16") -> bool:
     return bool(load_library().sage_rowsum_rounded(PV_CODES[pv_dtype]))
 
 
+def _dtype_code(dt: torch.dtype, what: str) -> int:
+    if dt == torch.bfloat16:
+        return SAGE_BF16
+    if dt == torch.float16:
+        return SAGE_FP16
+    raise ValueError(f"{what} must be bfloat16 or float16, got {dt}")
+
+
 def _desc(t: torch.Tensor, layout: str) -> QKVDesc:
     if t.dim() != 4:
         raise ValueError("q/k/v must be 4-D")
-    if t.dtype == torch.bfloat16:
-        dt = SAGE_BF16
-    elif t.dtype == torch.float16:
-        dt = SAGE_FP16
-    else:
-        raise ValueError(f"unsupported dtype {t.dtype}")
+    dt = _dtype_code(t.dtype, "q/k/v")
     if t.stride(3) != 1:
         raise ValueError("the head_dim axis must be contiguous")
     if layout == "HND":
@@ -159,7 +164,7 @@ def _desc(t: torch.Tensor, layout: str) -> QKVDesc:
 @dataclass
 class QuantizedQK:
     """Device buffers produced by quantize_qk (see sage_qk_quant in the header).  Q has H heads,
-    K has Hkv heads (group-query attention when Hkv < H)."""
+    K has Hkv heads (group-query attention when Hkv < H); dtype is the input dtype of Q and K."""
     q8: torch.Tensor
     k8: torch.Tensor
     q_scale: torch.Tensor
@@ -172,6 +177,7 @@ class QuantizedQK:
     Nk: int
     d: int
     Hkv: int
+    dtype: torch.dtype = torch.bfloat16
 
     def cstruct(self) -> QKQuant:
         return QKQuant(self.q8.data_ptr(), self.k8.data_ptr(), self.q_scale.data_ptr(), self.k_scale.data_ptr(),
@@ -179,7 +185,7 @@ class QuantizedQK:
                        self.d, self.q8.shape[2], self.k8.shape[2])
 
 
-def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None) -> QuantizedQK:
+def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None, dtype=torch.bfloat16) -> QuantizedQK:
     Hkv = H if Hkv is None else Hkv
     nq, nk = pad_tokens(Nq), pad_tokens(Nk)
     return QuantizedQK(torch.empty(B, H, nq, d, dtype=torch.int8, device=device),
@@ -187,7 +193,7 @@ def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None) -> QuantizedQK:
                        torch.empty(B, H, (Nq + 63) // 64, dtype=torch.float32, device=device),
                        torch.empty(B, Hkv, (Nk + 63) // 64, dtype=torch.float32, device=device),
                        torch.empty(B, Hkv, d, dtype=torch.float32, device=device),
-                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d, Hkv)
+                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d, Hkv, dtype)
 
 
 def quantize_workspace(B, Hkv, Nk, d, device) -> torch.Tensor:
@@ -202,7 +208,8 @@ def quantize_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", ou
     L = load_library()
     dq, dk = _desc(q, tensor_layout), _desc(k, tensor_layout)
     if out is None:
-        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device, Hkv=dk.H)
+        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
+    out.dtype = q.dtype
     if workspace is None:
         workspace = quantize_workspace(dk.B, dk.H, dk.N, dk.d, q.device)
     qs = out.cstruct()
@@ -217,10 +224,15 @@ def fwd_workspace(B, Hkv, Nq, Nk, d, pv_dtype, mask_h, device) -> torch.Tensor:
 
 
 def _mask_args(attn_mask, B, H, Nq, Nk):
+    """(mask, mask dtype code, mask_h, stride_b, stride_h, stride_q) for the C call."""
     if attn_mask is None:
-        return None, 0, 0, 0, 0
-    if attn_mask.dtype != torch.bool:
-        raise NotImplementedError("only boolean masks (True = attend) are supported")
+        return None, SAGE_MASK_BOOL, 0, 0, 0, 0
+    if attn_mask.dtype == torch.bool:
+        code = SAGE_MASK_BOOL
+    elif attn_mask.dtype == torch.float32:
+        code = SAGE_MASK_F32
+    else:
+        raise ValueError(f"attn_mask must be bool (True = attend) or float32 (additive), got {attn_mask.dtype}")
     m = attn_mask
     while m.dim() < 4:
         m = m.unsqueeze(0)
@@ -231,14 +243,15 @@ def _mask_args(attn_mask, B, H, Nq, Nk):
     mh = m.shape[1]
     sb = m.stride(0) if m.shape[0] == B else 0
     sh = m.stride(1) if mh == H and H > 1 else 0
-    return m, (mh if mh == H else 1), sb, sh, m.stride(2)
+    return m, code, (mh if mh == H else 1), sb, sh, m.stride(2)
 
 
 def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is_causal: bool = False,
              attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, pv_dtype: str = "fp16",
              return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
              workspace: torch.Tensor | None = None):
-    """Attention on pre-quantized Q/K (from quantize_qk) with bf16 V.  Returns out or (out, lse)."""
+    """Attention on pre-quantized Q/K (from quantize_qk) with bf16 or fp16 V.  Returns out or (out, lse);
+    out defaults to V's dtype."""
     L = load_library()
     dv = _desc(v, tensor_layout)
     B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
@@ -251,12 +264,13 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
         osb, osh, osn = out.stride(0), out.stride(2), out.stride(1)
     if return_lse and lse is None:
         lse = torch.empty(B, H, Nq, dtype=torch.float32, device=v.device)
-    m, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
+    m, mcode, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
     if workspace is None:
         workspace = fwd_workspace(B, qk.Hkv, Nq, Nk, d, pv_dtype, mh, v.device)
     qs = qk.cstruct()
-    odt = SAGE_BF16 if out.dtype == torch.bfloat16 else SAGE_FP16
-    _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mh, msb, msh, msq,
+    odt = _dtype_code(out.dtype, "out")
+    _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mcode, mh, msb,
+                           msh, msq,
                            1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale), PV_CODES[pv_dtype],
                            out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                            workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_attn_fwd")
@@ -268,9 +282,11 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
              pv_dtype: str = "fp16"):
     """Quantized attention forward: INT8 Q/K with K smoothing, FP16 (or FP8 e4m3) PV.
 
-    q: bf16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}; k, v: the same with Hkv
-    heads, Hkv dividing H (group-query attention: query head h reads key/value head h // (H // Hkv)).
-    attn_mask: optional bool, broadcastable to [B, H, Nq, Nk], True = attend.
+    q: bf16 or fp16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}; k, v: the same
+    dtype with Hkv heads, Hkv dividing H (group-query attention: query head h reads key/value head
+    h // (H // Hkv)).
+    attn_mask: optional, broadcastable to [B, H, Nq, Nk]: bool (True = attend) or float32 (added to
+    the scaled scores; -inf masks).
     sm_scale: defaults to 1/sqrt(d).  Returns out (same layout and dtype as q) or (out, lse) with
     lse fp32 [B, H, Nq] (natural log, of the unsmoothed scaled scores).
     """
@@ -278,6 +294,8 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
         raise ValueError("head_dim must be 64 or 128")
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must have the same dtype")
     hk = k.shape[1] if tensor_layout == "HND" else k.shape[2]
     hq = q.shape[1] if tensor_layout == "HND" else q.shape[2]
     if hq % hk != 0:
@@ -333,26 +351,27 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
                       tensor_layout: str = "HND", is_causal: bool = False, attn_mask: torch.Tensor | None = None,
                       sm_scale: float | None = None, return_lse: bool = False, out: torch.Tensor | None = None,
                       lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Attention on pre-quantized Q/K and prepared V (from prepare_v).  Returns out or (out, lse)."""
+    """Attention on pre-quantized Q/K and prepared V (from prepare_v).  Returns out or (out, lse);
+    out defaults to the dtype Q and K had."""
     L = load_library()
     B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
     dev = qk.q8.device
     if out is None:
         shape = (B, H, Nq, d) if tensor_layout == "HND" else (B, Nq, H, d)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(shape, dtype=qk.dtype, device=dev)
     if tensor_layout == "HND":
         osb, osh, osn = out.stride(0), out.stride(1), out.stride(2)
     else:
         osb, osh, osn = out.stride(0), out.stride(2), out.stride(1)
     if return_lse and lse is None:
         lse = torch.empty(B, H, Nq, dtype=torch.float32, device=dev)
-    m, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
+    m, mcode, mh, msb, msh, msq = _mask_args(attn_mask, B, H, Nq, Nk)
     if workspace is None and mh > 0:
         workspace = mask_workspace(B, Nq, Nk, mh, dev)
     qs = qk.cstruct()
-    odt = SAGE_BF16 if out.dtype == torch.bfloat16 else SAGE_FP16
+    odt = _dtype_code(out.dtype, "out")
     _check(L.sage_attn_fwd_prepared(ctypes.byref(qs), v_t.data_ptr(), None if v_scale is None else v_scale.data_ptr(),
-                                    PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mh, msb, msh, msq,
+                                    PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mcode, mh, msb, msh, msq,
                                     1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
                                     out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                                     None if workspace is None else workspace.data_ptr(),

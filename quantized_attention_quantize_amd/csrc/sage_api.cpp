@@ -48,8 +48,7 @@ sage_status check_desc(const sage_qkv_desc* t) {
   if (!t || !t->data) return SAGE_ERR_INVALID_ARGUMENT;
   if (t->B <= 0 || t->H <= 0 || t->N <= 0 || t->d <= 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (t->N > kMaxTokens || t->B * t->H > 65535) return SAGE_ERR_INVALID_ARGUMENT;
-  if (t->dtype == SAGE_FP16) return SAGE_ERR_UNSUPPORTED;
-  if (t->dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (t->dtype != SAGE_BF16 && t->dtype != SAGE_FP16) return SAGE_ERR_INVALID_ARGUMENT;
   if (t->d != 64 && t->d != 128) return SAGE_ERR_UNSUPPORTED;
   if (t->stride_b < 0 || t->stride_h < 0 || t->stride_n < t->d) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(t->data) || (t->stride_b % 8) || (t->stride_h % 8) || (t->stride_n % 8))
@@ -117,6 +116,7 @@ PrepVArgs prep_v_args(const sage_qkv_desc* v, void* vt, float* vscale, float* vm
   a.d = v->d;
   a.Nk_pad = sage_pad_tokens(v->N);
   a.nchunk = (int)cdiv(v->N, kChunkTokens);
+  a.in_fp16 = v->dtype == SAGE_FP16;
   return a;
 }
 
@@ -145,7 +145,7 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   sage_status s;
   if ((s = check_desc(q)) != SAGE_OK) return s;
   if ((s = check_desc(k)) != SAGE_OK) return s;
-  if (q->B != k->B || q->d != k->d || q->H % k->H != 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (q->B != k->B || q->d != k->d || q->H % k->H != 0 || q->dtype != k->dtype) return SAGE_ERR_INVALID_ARGUMENT;
   if ((s = check_qk(out)) != SAGE_OK) return s;
   if (out->B != q->B || out->H != q->H || out->Hkv != k->H || out->d != q->d || out->Nq != q->N ||
       out->Nk != k->N)
@@ -179,6 +179,7 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   a.Nk_pad = out->Nk_pad;
   a.nbq = (int)cdiv(a.Nq, 64);
   a.nbk = (int)cdiv(a.Nk, 64);
+  a.in_fp16 = q->dtype == SAGE_FP16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = hip_status(launch_kmean(a, static_cast<double*>(workspace), (int)cdiv(a.Nk, kChunkTokens), st))) != SAGE_OK)
     return s;
@@ -230,7 +231,8 @@ struct FwdCommon {
   int64_t mh;
 };
 
-sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const uint8_t* mask, int64_t mask_h,
+sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const void* mask,
+                                sage_mask_dtype mask_dtype, int64_t mask_h,
                                 int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, void* out,
                                 sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
                                 int64_t out_stride_n, FwdCommon* c) {
@@ -238,13 +240,14 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
   if ((s = check_qk(qk)) != SAGE_OK) return s;
   if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
   if (!out) return SAGE_ERR_INVALID_ARGUMENT;
-  if (out_dtype == SAGE_FP16) return SAGE_ERR_UNSUPPORTED;
-  if (out_dtype != SAGE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SAGE_BF16 && out_dtype != SAGE_FP16) return SAGE_ERR_INVALID_ARGUMENT;
   if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < qk->d) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(out) || (out_stride_b % 8) || (out_stride_h % 8) || (out_stride_n % 8))
     return SAGE_ERR_INVALID_ARGUMENT;
   c->mh = 0;
   if (mask) {
+    if (mask_dtype != SAGE_MASK_BOOL && mask_dtype != SAGE_MASK_F32) return SAGE_ERR_INVALID_ARGUMENT;
+    if (mask_dtype == SAGE_MASK_F32 && (uintptr_t)mask % 4 != 0) return SAGE_ERR_INVALID_ARGUMENT;
     if (mask_h != 1 && mask_h != qk->H) return SAGE_ERR_INVALID_ARGUMENT;
     if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_q < qk->Nk) return SAGE_ERR_INVALID_ARGUMENT;
     c->mh = mask_h;
@@ -254,18 +257,27 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
 
 // Mask classification (if any) and the attention kernel, on already prepared V.
 sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
-                              const uint8_t* mask, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
-                              int64_t mask_stride_q, int causal, float sm_scale, void* out, int64_t out_stride_b,
-                              int64_t out_stride_h, int64_t out_stride_n, float* lse, int* mtiles,
-                              hipStream_t st) {
+                              const void* mask, sage_mask_dtype mask_dtype, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
+                              int64_t mask_stride_q, int causal, float sm_scale, void* out, sage_dtype out_dtype,
+                              int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
+                              int* mtiles, hipStream_t st) {
   sage_status s;
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.nQT = (int)cdiv(qk->Nq, kTileRows);
   a.nKT = (int)cdiv(qk->Nk, kTileKeys);
   if (mask) {
+    const int f32 = mask_dtype == SAGE_MASK_F32;
+    const int64_t esz = f32 ? 4 : 1;  // bytes per mask element
+    // every row start (and the base) aligned to `bytes`
+    auto rows_aligned = [&](int64_t bytes) {
+      const int64_t el = bytes / esz;
+      return (uintptr_t)mask % bytes == 0 && mask_stride_b % el == 0 && (mh == 1 || mask_stride_h % el == 0) &&
+             mask_stride_q % el == 0;
+    };
     MaskTileArgs m;
     m.mask = mask;
+    m.f32 = f32;
     m.sb = mask_stride_b;
     m.sh = mask_stride_h;
     m.sq = mask_stride_q;
@@ -275,8 +287,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
     m.Nk = qk->Nk;
     m.nQT = a.nQT;
     m.nKT = a.nKT;
-    m.vec16 = aligned16(mask) && (mask_stride_b % 16 == 0) && (mh == 1 || mask_stride_h % 16 == 0) &&
-              (mask_stride_q % 16 == 0);
+    m.vec16 = rows_aligned(16);
     m.state = mtiles;
     if ((s = hip_status(launch_mask_tiles(m, st))) != SAGE_OK) return s;
     a.mask = mask;
@@ -285,8 +296,8 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
     a.m_sq = mask_stride_q;
     a.mtiles = mtiles;
     a.Hm = mh;
-    a.mask_vec4 = ((uintptr_t)mask % 4 == 0) && (mask_stride_b % 4 == 0) && (mask_stride_h % 4 == 0) &&
-                  (mask_stride_q % 4 == 0);
+    a.mask_f32 = f32;
+    a.mask_vec4 = rows_aligned(4 * esz);  // 4 elements at a time
   }
   a.q8 = qk->q8;
   a.k8 = qk->k8;
@@ -296,6 +307,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   a.vt = v_t;
   a.vscale = pv == SAGE_PV_FP8_E4M3 ? v_scale : nullptr;
   a.out = static_cast<unsigned short*>(out);
+  a.out_fp16 = out_dtype == SAGE_FP16;
   a.o_sb = out_stride_b;
   a.o_sh = out_stride_h;
   a.o_sn = out_stride_n;
@@ -326,15 +338,16 @@ sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, 
   return enqueue_prepare(v, pv, v_t, v_scale, workspace, static_cast<hipStream_t>(stream));
 }
 
-sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const uint8_t* mask, int64_t mask_h,
+sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const void* mask,
+                          sage_mask_dtype mask_dtype, int64_t mask_h,
                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
                           float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
                           int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   sage_status s;
   FwdCommon c;
-  if ((s = validate_fwd_common(qk, pv, mask, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out, out_dtype,
-                               out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
+  if ((s = validate_fwd_common(qk, pv, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
+                               out_dtype, out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
   if ((s = check_desc(v)) != SAGE_OK) return s;
   if (v->B != qk->B || v->H != qk->Hkv || v->N != qk->Nk || v->d != qk->d) return SAGE_ERR_INVALID_ARGUMENT;
@@ -346,29 +359,29 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* vscale = pv == SAGE_PV_FP8_E4M3 ? reinterpret_cast<float*>(ws + L.vscale) : nullptr;
   if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st)) != SAGE_OK) return s;
-  return enqueue_attention(qk, ws + L.vt, vscale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
-                           sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
+  return enqueue_attention(qk, ws + L.vt, vscale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h,
+                           mask_stride_q, causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            reinterpret_cast<int*>(ws + L.mtiles), st);
 }
 
 sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
-                                   const uint8_t* mask, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
+                                   const void* mask, sage_mask_dtype mask_dtype, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
                                    int64_t mask_stride_q, int causal, float sm_scale, void* out,
                                    sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
                                    int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   sage_status s;
   FwdCommon c;
-  if ((s = validate_fwd_common(qk, pv, mask, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out, out_dtype,
-                               out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
+  if ((s = validate_fwd_common(qk, pv, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
+                               out_dtype, out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
   const size_t need = mask_ws_bytes(qk->B, qk->Nq, qk->Nk, c.mh);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_ERR_WORKSPACE;
   if ((s = check_device()) != SAGE_OK) return s;
-  return enqueue_attention(qk, v_t, v_scale, pv, mask, c.mh, mask_stride_b, mask_stride_h, mask_stride_q, causal,
-                           sm_scale, out, out_stride_b, out_stride_h, out_stride_n, lse,
+  return enqueue_attention(qk, v_t, v_scale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h, mask_stride_q,
+                           causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            static_cast<int*>(workspace), static_cast<hipStream_t>(stream));
 }
 

@@ -274,29 +274,74 @@ __device__ __forceinline__ void mask_scores(v16i (&acc)[2], int g, int lim, cons
     }
 }
 
+// Float-mask form: every score of a tile becomes the fp32 bit pattern of its log2-unit value
+// acc * c + log2(e) * M[j] (M = 0 where mtile is null), and -inf outside the visible keys
+// (j > lim) or where M is -inf.  mtile is the row's mask at the tile's first key, read only if
+// has_m (the same for the whole wave); full4: the tile's 64 keys all exist and the row is 16-byte
+// aligned, so it is read 16 bytes at a time; otherwise one element at a time at indices clamped
+// to the visible range (j <= max(lim, 0) < Nk - j0: always inside the row).  No per-lane branches.
+__device__ __forceinline__ void mask_scores_f32(v16i (&acc)[2], int g, int lim, const float* mtile, bool has_m,
+                                                bool full4, float c) {
+  const int jmax = lim > 0 ? lim : 0;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int j4 = kb * 32 + rq * 8 + g * 4;
+      float mv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (has_m) {
+        if (full4) {
+          const float4 m4 = *reinterpret_cast<const float4*>(mtile + j4);
+          mv[0] = m4.x;
+          mv[1] = m4.y;
+          mv[2] = m4.z;
+          mv[3] = m4.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[e] = mtile[j4 + e < jmax ? j4 + e : jmax];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = __builtin_fmaf((float)acc[kb][rq * 4 + e], c, mv[e] * kLog2e);
+        acc[kb][rq * 4 + e] = __float_as_int(j4 + e <= lim ? t : -INFINITY);
+      }
+    }
+}
+
 // Row maximum of a tile's scores in four independent chains of eight: piece p (0..7) advances
-// chain p/2 by two max3/max steps.
+// chain p/2 by two max3/max steps.  The scores are int32 (MF = false) or fp32 bit patterns (MF).
+template <bool MF>
+__device__ __forceinline__ int smax(int x, int y) {
+  if constexpr (MF)
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  else
+    return max(x, y);
+}
 __device__ __forceinline__ int score_at(const v16i (&acc)[2], int i) { return acc[i >> 4][i & 15]; }
+template <bool MF = false>
 __device__ __forceinline__ void max_piece(const v16i (&acc)[2], int (&ch)[4], int p) {
   const int c = p >> 1, e = 8 * c;
   if ((p & 1) == 0) {
-    ch[c] = max(max(score_at(acc, e), score_at(acc, e + 1)), score_at(acc, e + 2));
-    ch[c] = max(max(ch[c], score_at(acc, e + 3)), score_at(acc, e + 4));
+    ch[c] = smax<MF>(smax<MF>(score_at(acc, e), score_at(acc, e + 1)), score_at(acc, e + 2));
+    ch[c] = smax<MF>(smax<MF>(ch[c], score_at(acc, e + 3)), score_at(acc, e + 4));
   } else {
-    ch[c] = max(max(ch[c], score_at(acc, e + 5)), score_at(acc, e + 6));
-    ch[c] = max(ch[c], score_at(acc, e + 7));
+    ch[c] = smax<MF>(smax<MF>(ch[c], score_at(acc, e + 5)), score_at(acc, e + 6));
+    ch[c] = smax<MF>(ch[c], score_at(acc, e + 7));
   }
 }
 // Combines the chains across the wave's halves and moves the reference maximum (lazy by
 // kSoftmaxTau[PV] log2 units).  Returns 2^(m_old - m_new); the new exponent offset goes to pm_new.
-template <int PV, bool MASKED>
+template <int PV, bool MASKED, bool MF = false>
 __device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowState& rs, float& pm_new) {
   constexpr float kTau = kSoftmaxTau[PV];
-  int im = max(max(ch[0], ch[1]), max(ch[2], ch[3]));
+  int im = smax<MF>(smax<MF>(ch[0], ch[1]), smax<MF>(ch[2], ch[3]));
   const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);  // lanes l and l ^ 32
-  im = max((int)sw[0], (int)sw[1]);
+  im = smax<MF>((int)sw[0], (int)sw[1]);
   float mt;
-  if constexpr (MASKED)
+  if constexpr (MF)
+    mt = __int_as_float(im);  // already log2-unit fp32, -inf if nothing is visible
+  else if constexpr (MASKED)
     mt = im == INT_MIN ? -INFINITY : (float)im * c;
   else
     mt = (float)im * c;
@@ -344,14 +389,18 @@ __device__ __forceinline__ typename StepGeom<D, PV>::VFrag vfrag(const char* sV,
 // just-issued MFMA.  Every MFMA is issued with a slice of VALU work and the LDS reads LA operands
 // ahead; sched_barrier fences keep that order.  At the end vpre receives the first operands of the
 // next step's PV (V tile sVn).  With SLOW, T[n]'s scores may be masked (INT_MIN) and T[n+1] is
-// masked by lim / mtile (mask_scores).  Returns 2^(m_{n-1} - m_n), the factor O takes after the
-// PV of T[n-1].
-template <int D, int PV, bool SLOW>
+// masked by lim / mtile (mask_scores).  With MF (float mask; implies SLOW) T[n]'s raw scores are
+// converted at the start of the step to log2-unit fp32 with the mask added (mask_scores_f32, with
+// lim / mtile / has_m / mvec4 describing T[n] and scale c_cur), all its row maxima follow, and the
+// exponentials take the converted scores as they are.  Returns 2^(m_{n-1} - m_n), the factor O
+// takes after the PV of T[n-1].
+template <int D, int PV, bool SLOW, bool MF = false>
 __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<PV>& P,
                                            typename StepGeom<D, PV>::VFrag (&vpre)[StepGeom<D, PV>::LA],
                                            const char* sKn, const char* sVp, const char* sVn, const v4i (&qf)[D / 32],
                                            v16f (&o)[D / 32], float c_cur, RowState& rs, const LaneBases& lb, int g,
-                                           int lim, const uint8_t* mtile, bool mvec4) {
+                                           int lim, const void* mtile, bool mvec4, bool has_m = false) {
+  static_assert(SLOW || !MF, "the float-mask step is a masked step");
   using SG = StepGeom<D, PV>;
   constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = SG::NM, LA = SG::LA;
   constexpr int NG = PV == 0 ? 16 : 8;  // exponential groups of 2 (fp16) or 4 (e4m3) scores
@@ -379,7 +428,14 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   // slot of row-max piece p < 4 of T[n+1] (key block 0): two MFMAs after that block's last QK
   auto max_slot = [](int p) { return NPV + NB + 1 + p / 2 < NM - 1 ? NPV + NB + 1 + p / 2 : NM - 1; };
 
-  const v16i sc[2] = {acc[0], acc[1]};  // scores of T[n]
+  v16i sc[2] = {acc[0], acc[1]};  // scores of T[n]
+  if constexpr (MF) {
+    // T[n]'s scores to log2-unit fp32 with its mask (lim / mtile / has_m / mvec4 describe T[n]),
+    // and all eight row-maximum pieces, before the MFMA stream
+    mask_scores_f32(sc, g, lim, static_cast<const float*>(mtile), has_m, mvec4, c_cur);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) max_piece<true>(sc, ch, p);
+  }
   const PFrag<PV> pin = P;              // probabilities of T[n-1]
   VFrag vf[NPV];
   v4i kf[NQ];
@@ -413,13 +469,13 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
       }
     }
     // T[n]'s row maxima over its second key block, then its reference maximum
-    if (k == 0) {
+    if (!MF && k == 0) {
 #pragma unroll
       for (int p = 4; p < 8; ++p) max_piece(sc, ch, p);
     }
     if (k == FIN) {
       float pm_new;
-      alpha = finish_max<PV, SLOW>(ch, c_cur, rs, pm_new);
+      alpha = finish_max<PV, SLOW, MF>(ch, c_cur, rs, pm_new);
       rs.pm = pm_new;
     }
     // exponentials of T[n] assigned to slot k
@@ -435,8 +491,13 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
         // at the top of the step, where no MFMA overlaps them.
         int si = sc[kb][r];
         asm volatile("" : "+v"(si));
-        float t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, -rs.pm));
-        if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
+        float t;
+        if constexpr (MF) {
+          t = __builtin_amdgcn_exp2f(__int_as_float(si) - rs.pm);  // -inf gives 0
+        } else {
+          t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, -rs.pm));
+          if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
+        }
         x[e] = t;
       }
       if constexpr (PV == 0) {
@@ -460,8 +521,8 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (SLOW) {
-    mask_scores(acc, g, lim, mtile, mvec4);
+  if constexpr (!MF && SLOW) {
+    mask_scores(acc, g, lim, static_cast<const uint8_t*>(mtile), mvec4);
 #pragma unroll
     for (int p = 0; p < 4; ++p) max_piece(acc, ch, p);
   }
@@ -506,8 +567,8 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
 // vslot i%4.  Step n consumes K of T[n+1] and V of T[n-1], issues the loads of V of T[n+2] and K
 // of T[n+3] into slots freed two steps earlier, and waits at its end only for the loads of the
 // previous step.  The loop is unrolled four times so every slot is a compile-time offset.  One
-// barrier per tile.
-template <int D, int PV>
+// barrier per tile.  MF: the mask is fp32 and additive, and every tile takes the masked step.
+template <int D, int PV, int MF>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
@@ -538,8 +599,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     if (lim < kt_end) kt_end = lim;
   }
   const int* mt = a.mtiles ? a.mtiles + ((b * a.Hm + (a.Hm == 1 ? 0 : h)) * a.nQT + qt) * a.nKT : nullptr;
-  const uint8_t* mrow =
-      (a.mask && row < nq) ? a.mask + b * a.m_sb + (a.Hm == 1 ? 0 : h) * a.m_sh + (int64_t)row * a.m_sq : nullptr;
+  constexpr int kMaskBytes = MF ? 4 : 1;  // bytes per mask element
+  // the float-mask step reads rows past Nq at row Nq - 1 (never stored), so a tile's mask pointer
+  // is null or not for the whole wave
+  const int mrow_i = MF && row >= nq ? nq - 1 : row;
+  const char* mrow = (a.mask && mrow_i < nq) ? static_cast<const char*>(a.mask) +
+                                                   (b * a.m_sb + (a.Hm == 1 ? 0 : h) * a.m_sh +
+                                                    (int64_t)mrow_i * a.m_sq) * kMaskBytes
+                                             : nullptr;
 
   const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);  // key/value head (group-query attention)
   const int8_t* q8h = a.q8 + bh * a.Nq_pad * D;
@@ -598,7 +665,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     const int j0 = __builtin_amdgcn_mbcnt_lo(0u, t) * kBlockN;
     return j0 + kBlockN > nk || (a.causal && j0 + kBlockN - 1 > r0u) || (mt != nullptr && scalar_ld(mt, t) == 2);
   };
-  auto visible = [&](int t, int& lim, const uint8_t*& mtile) {
+  auto visible = [&](int t, int& lim, const void*& mtile) {
     if (t >= kt_end) {
       lim = -1;
       mtile = nullptr;
@@ -610,7 +677,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const int dr = row - j0;
       lim = dr < lim ? (dr < -1 ? -1 : dr) : lim;
     }
-    mtile = (mt != nullptr && scalar_ld(mt, t) == 2 && mrow) ? mrow + j0 : nullptr;
+    mtile = (mt != nullptr && scalar_ld(mt, t) == 2 && mrow) ? mrow + (int64_t)j0 * kMaskBytes : nullptr;
+  };
+  // float-mask step: whether tile t reads its mask (uniform), and whether it may read it 16 bytes
+  // at a time; the mask pointer is then formed for every lane
+  auto fmask_of = [&](int t, bool& has_m, bool& full4) -> const void* {
+    has_m = t < kt_end && mt != nullptr && scalar_ld(mt, t) == 2;
+    full4 = a.mask_vec4 && (t + 1) * kBlockN <= nk;
+    return mrow ? mrow + (int64_t)(t < kt_end ? t : 0) * kBlockN * kMaskBytes : nullptr;
   };
 
   LaneBases lb;
@@ -629,11 +703,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   {  // scores of T[0] and the row maxima of its first key block; the first PV operands
     qk_tile<D>(kring, qf, lr, g, acc);
     int lim;
-    const uint8_t* mtile;
+    const void* mtile;
     visible(t0, lim, mtile);
-    if (part_cur) mask_scores(acc, g, lim, mtile, a.mask_vec4);
+    if constexpr (!MF) {  // (the float-mask step takes T[n]'s masking and maxima itself)
+      if (part_cur) mask_scores(acc, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) max_piece(acc, ch, p);
+      for (int p = 0; p < 4; ++p) max_piece(acc, ch, p);
+    }
 #pragma unroll
     for (int r = 0; r < StepGeom<D, PV>::LA; ++r) vpre[r] = vfrag<D, PV>(vring + (kNS - 1) * G::V_BYTES, lb, g, r);
   }
@@ -653,9 +729,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     const char* sKn = kring + ((Q + 1) % kNS) * G::K_BYTES;        // K of T[n+1]
     const bool part_nxt = partial(tn);
     float alpha;
-    if (part_cur || part_nxt) {
+    if constexpr (MF) {
       int lim;
-      const uint8_t* mtile;
+      const void* mtile;
+      visible(tc, lim, mtile);
+      bool has_m, full4;
+      const void* mf = fmask_of(tc, has_m, full4);
+      // a per-lane test of a wave-uniform condition (as in partial()): two specialised steps
+      if (__builtin_amdgcn_mbcnt_lo(0u, has_m ? 1u : 0u) != 0u)
+        alpha = tile_step<D, PV, true, true>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mf, full4,
+                                             true);
+      else
+        alpha = tile_step<D, PV, true, true>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mf, full4,
+                                             false);
+    } else if (part_cur || part_nxt) {
+      int lim;
+      const void* mtile;
       visible(tn, lim, mtile);
       alpha = tile_step<D, PV, true>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mtile,
                                      a.mask_vec4);
@@ -694,7 +783,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   __syncthreads();
   if (n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
 
-  // epilogue: normalize, store bf16 O and the LSE
+  // epilogue: normalize, store O (bf16 or fp16) and the LSE
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
   if (row < nq) {
     const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
@@ -713,11 +802,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
           else
             f[e] = o[db][rq * 4 + e] * inv;
         }
-        const v2bf lo = __builtin_convertvector((v2f{f[0], f[1]}), v2bf);  // round to nearest even
-        const v2bf hi = __builtin_convertvector((v2f{f[2], f[3]}), v2bf);
         uint2 pk;
-        pk.x = __builtin_bit_cast(unsigned, lo);
-        pk.y = __builtin_bit_cast(unsigned, hi);
+        if (a.out_fp16) {
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
+        } else {
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
+        }
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
     if (g == 0 && a.lse) {
@@ -759,24 +851,36 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
     }
 }
 
-template <int D, int PV>
+// Every variant instantiated explicitly: the launches below alone do not make hipcc's host pass
+// emit the launch stubs of the MF = 0 kernels.
+template __global__ void k_attn_fwd<128, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 1>(AttnArgs);
+
+template <int D, int PV, int MF>
 static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
-  k_attn_fwd<D, PV><<<grid, kAttnThreads, 0, s>>>(a);
+  k_attn_fwd<D, PV, MF><<<grid, kAttnThreads, 0, s>>>(a);
+}
+
+template <int D>
+static void launch_attn_d(const AttnArgs& a, int pv_fp8, unsigned grid, hipStream_t s) {
+  if (pv_fp8)
+    a.mask_f32 ? launch_attn_t<D, 1, 1>(a, grid, s) : launch_attn_t<D, 1, 0>(a, grid, s);
+  else
+    a.mask_f32 ? launch_attn_t<D, 0, 1>(a, grid, s) : launch_attn_t<D, 0, 0>(a, grid, s);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nQT * a.B * a.H);
-  if (d == 128) {
-    if (pv_fp8)
-      launch_attn_t<128, 1>(a, grid, s);
-    else
-      launch_attn_t<128, 0>(a, grid, s);
-  } else {
-    if (pv_fp8)
-      launch_attn_t<64, 1>(a, grid, s);
-    else
-      launch_attn_t<64, 0>(a, grid, s);
-  }
+  if (d == 128)
+    launch_attn_d<128>(a, pv_fp8, grid, s);
+  else
+    launch_attn_d<64>(a, pv_fp8, grid, s);
   return hipGetLastError();
 }
 

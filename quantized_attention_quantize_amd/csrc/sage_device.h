@@ -34,6 +34,15 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
   return __uint_as_float(static_cast<unsigned>(h) << 16);
 }
 
+// An input element (Q, K or V) as fp32: bf16 (IN = 0) or IEEE binary16 (IN = 1) bits.  Exact.
+template <int IN>
+__device__ __forceinline__ float in_to_f32(unsigned short h) {
+  if constexpr (IN == 0)
+    return bf16_to_f32(h);
+  else
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
 // fp32 -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   unsigned u = __float_as_uint(f);

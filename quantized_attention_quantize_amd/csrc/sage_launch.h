@@ -15,8 +15,8 @@ constexpr float kSoftmaxTau[2] = {8.f, 0.f};
 constexpr int kRowsumRounded[2] = {1, 0};
 
 struct QuantArgs {
-  const unsigned short* q;  // bf16
-  const unsigned short* k;  // bf16
+  const unsigned short* q;  // bf16 or fp16 (in_fp16), as K
+  const unsigned short* k;
   int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn;
   int8_t* q8;
   int8_t* k8;
@@ -26,25 +26,28 @@ struct QuantArgs {
   float* corr;
   int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;  // Q has H heads, K has Hkv (Hkv divides H)
   int nbq, nbk;
+  int in_fp16;
 };
 
 struct PrepVArgs {
-  const unsigned short* v;  // bf16
+  const unsigned short* v;  // bf16 or fp16 (in_fp16)
   int64_t v_sb, v_sh, v_sn;
   void* vt;             // fp16 or e4m3 [B][H][d][Nk_pad]
   float* vscale;        // fp8 only: [B][H][d]
   float* vmax_partial;  // fp8 only: [B][H][nchunk][d]
   int64_t B, H, Nk, d, Nk_pad;
   int nchunk;
+  int in_fp16;
 };
 
 struct MaskTileArgs {
-  const uint8_t* mask;
+  const void* mask;  // uint8 (nonzero = attend) or, with f32, fp32 additive (-inf = drop)
+  int f32;
   int64_t sb, sh, sq;
   int64_t B, Hm, Nq, Nk;
   int nQT, nKT;
   int vec16;  // rows and base are 16-byte aligned: read 16 bytes at a time
-  int* state;  // [B*Hm][nQT][nKT]: 0 all masked, 1 all visible, 2 mixed
+  int* state;  // [B*Hm][nQT][nKT]: 0 all masked, 1 all visible (fp32: all exactly 0), 2 mixed
 };
 
 struct AttnArgs {
@@ -55,17 +58,19 @@ struct AttnArgs {
   const float* corr;
   const void* vt;  // prepared V
   const float* vscale;
-  const uint8_t* mask;  // element mask (only read for mixed tiles)
+  const void* mask;  // element mask (only read for mixed tiles); strides in elements
   int64_t m_sb, m_sh, m_sq;
+  int mask_f32;       // 0: uint8, nonzero = attend; 1: fp32 added to the scaled score, -inf = drop
   const int* mtiles;  // tile states or nullptr
   int64_t Hm;             // 0 = no mask
-  unsigned short* out;    // bf16
+  unsigned short* out;    // bf16, or fp16 if out_fp16
+  int out_fp16;
   int64_t o_sb, o_sh, o_sn;
   float* lse;  // nullptr = not requested
   int64_t B, H, Hkv, Nq, Nk, Nq_pad, Nk_pad;  // query head h reads key/value head h / (H / Hkv)
   int nbq, nbk, nQT, nKT;
   int causal;
-  int mask_vec4;  // mask rows 4-byte aligned: read 4 mask bytes at a time
+  int mask_vec4;  // mask rows aligned to 4 elements: read 4 mask elements at a time
   float sm_scale;
 };
 

@@ -8,8 +8,9 @@
 //   k_prep_v16        V -> fp16 (round to nearest even), transposed to [d][Nk_pad] in the key
 //                     order the PV MFMA consumes
 //   k_prep_v8         V -> e4m3 with per-channel scale 448/max|V|, transposed likewise
-//   k_mask_tiles      classifies each (256-row x 64-key) tile of a boolean mask as all-masked,
-//                     all-visible or mixed, so the attention kernel skips or simplifies it
+//   k_mask_tiles      classifies each (256-row x 64-key) tile of a boolean or fp32 additive mask
+//                     as all-masked, all-visible (fp32: all exactly 0) or mixed, so the attention
+//                     kernel skips a tile or reads no mask for it
 //
 // Method sources (page title, section): SageAttention docs digest (context7 llms.txt) --
 // "sageattn_qk_int8_pv_fp16_triton" (per-block INT8 Q/K, smooth_k), "sageattn3_blackwell" usage
@@ -24,10 +25,11 @@ constexpr int kPrepThreads = 256;
 
 // ---------------------------------------------------------------------------------------------
 // Column reductions over token chunks.  MODE 0: fp64 sums of x; MODE 1: fp32 maxima of |x|.
+// x is bf16 (IN = 0) or fp16 (IN = 1).
 // grid = (nchunk, B*H), block = 256.  Thread t covers channels [8*(t % (D/8)), +8) of the rows
 // t / (D/8) + i * (256 / (D/8)) of the chunk.
 // ---------------------------------------------------------------------------------------------
-template <int D, int MODE>
+template <int D, int MODE, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned short* __restrict__ x, int64_t H,
                                                                  int64_t N, int64_t sb, int64_t sh, int64_t sn,
                                                                  void* __restrict__ partial, int nchunk) {
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
       u16x8 v = *reinterpret_cast<const u16x8*>(base + tok * sn);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float f = bf16_to_f32(v[j]);
+        float f = in_to_f32<IN>(v[j]);
         if constexpr (MODE == 0)
           sum[j] += (double)f;
         else
@@ -111,7 +113,7 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
 // block only write zero pad rows.  Each thread holds 8 channels of RPB rows.  A query head's LSE
 // shift uses the K mean of its key head h / (H / Hkv).
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPI = kPrepThreads / CG;  // 16 (D=128) or 32 (D=64)
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
       u16x8 v = *reinterpret_cast<const u16x8*>(src + tok * sn);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float f = bf16_to_f32(v[j]);
+        float f = in_to_f32<IN>(v[j]);
         if (!isq) f = f - km_s[cg * 8 + j];  // one fp32 rounding
         x[i][j] = f;
         amax = fmaxf(amax, fabsf(f));
@@ -218,7 +220,7 @@ __device__ __forceinline__ int fp8_pos_to_key(int p) {
   return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
 }
 
-template <int D>
+template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPI = kPrepThreads / CG;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
     if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = (_Float16)bf16_to_f32(v[j]);  // RNE
+    for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = (_Float16)in_to_f32<IN>(v[j]);  // RNE (exact for fp16)
   }
   __syncthreads();
   // D rows x 8 chunks of 8 halves; chunk q holds positions [8q, 8q+8)
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
 }
 
 // V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1>.
-template <int D>
+template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPI = kPrepThreads / CG;
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
     if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float f = bf16_to_f32(v[j]) * inv_s[cg * 8 + j];
+      float f = in_to_f32<IN>(v[j]) * inv_s[cg * 8 + j];
       if (fabsf(f) > 448.f) f = copysignf(448.f, f);  // saturate (NaN passes through)
       tile[r][cg * 8 + j] = f;
     }
@@ -304,94 +306,124 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Mask tile classification.  grid = (nKT, nQT, B*Hm), block = 256 (one thread per tile row).
-// state: 0 = every (valid) entry masked, 1 = every valid entry visible, 2 = mixed.
-// Entries beyond Nq / Nk do not count.
+// state: 0 = every (valid) entry masked, 1 = every valid entry visible with nothing added (boolean:
+// nonzero; fp32: exactly +-0), 2 = anything else.  Entries beyond Nq / Nk do not count.  F32: the
+// mask is fp32 and additive, -inf masks.
 // ---------------------------------------------------------------------------------------------
+template <bool F32>
 __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t bm = blockIdx.z, b = bm / a.Hm, hm = bm % a.Hm;
   const int64_t i = (int64_t)qt * kMaskTileRows + threadIdx.x;
   const int64_t j0 = (int64_t)kt * kBlockN;
-  int any0 = 0, any1 = 0;
+  int any0 = 0, any1 = 0, anyx = 0;  // a masked entry / a plainly visible one / anything else
   if (i < a.Nq) {
-    const uint8_t* row = a.mask + b * a.sb + hm * a.sh + i * a.sq;
+    const int64_t off = b * a.sb + hm * a.sh + i * a.sq;
     int64_t jn = a.Nk - j0 < kBlockN ? a.Nk - j0 : kBlockN;
-    if (a.vec16 && jn == kBlockN) {
+    if constexpr (F32) {
+      const float* row = static_cast<const float*>(a.mask) + off + j0;
+      auto classify = [&](float v) {
+        any0 |= v == -INFINITY;
+        any1 |= v == 0.f;
+        anyx |= v != -INFINITY && v != 0.f;
+      };
+      if (a.vec16 && jn == kBlockN) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 w = *reinterpret_cast<const uint4*>(row + j0 + 16 * c);
-        unsigned ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          unsigned v = ws[e];
-          // per byte: zero -> any0, nonzero -> any1
-          unsigned nz = ((v & 0x7f7f7f7fu) + 0x7f7f7f7fu | v) & 0x80808080u;
-          any1 |= nz != 0u;
-          any0 |= nz != 0x80808080u;
+        for (int c = 0; c < kBlockN / 4; ++c) {
+          const float4 w = *reinterpret_cast<const float4*>(row + 4 * c);
+          classify(w.x);
+          classify(w.y);
+          classify(w.z);
+          classify(w.w);
         }
+      } else {
+        for (int64_t j = 0; j < jn; ++j) classify(row[j]);
       }
     } else {
-      for (int64_t j = 0; j < jn; ++j) {
-        uint8_t v = row[j0 + j];
-        any1 |= v != 0;
-        any0 |= v == 0;
+      const uint8_t* row = static_cast<const uint8_t*>(a.mask) + off;
+      if (a.vec16 && jn == kBlockN) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint4 w = *reinterpret_cast<const uint4*>(row + j0 + 16 * c);
+          unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            unsigned v = ws[e];
+            // per byte: zero -> any0, nonzero -> any1
+            unsigned nz = ((v & 0x7f7f7f7fu) + 0x7f7f7f7fu | v) & 0x80808080u;
+            any1 |= nz != 0u;
+            any0 |= nz != 0x80808080u;
+          }
+        }
+      } else {
+        for (int64_t j = 0; j < jn; ++j) {
+          uint8_t v = row[j0 + j];
+          any1 |= v != 0;
+          any0 |= v == 0;
+        }
       }
     }
   }
-  int z = __syncthreads_or(any0);
-  int o = __syncthreads_or(any1);
-  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = z && o ? 2 : (o ? 1 : 0);
+  const int z = __syncthreads_or(any0);
+  const int o = __syncthreads_or(any1);
+  const int x = __syncthreads_or(anyx);
+  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = x || (z && o) ? 2 : (o ? 1 : 0);
 }
 
 // ---------------------------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------------------------
-hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
+template <int D, int IN>
+static void launch_kmean_t(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
   dim3 g(nchunk, (unsigned)(a.B * a.Hkv));
-  if (a.d == 128) {
-    k_colred_partial<128, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
-    k_kmean_final<128><<<(unsigned)(a.B * a.Hkv), 128, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
-  } else {
-    k_colred_partial<64, 0><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
-    k_kmean_final<64><<<(unsigned)(a.B * a.Hkv), 64, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
-  }
+  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
+  k_kmean_final<D><<<(unsigned)(a.B * a.Hkv), D, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+}
+
+hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
+  if (a.d == 128)
+    a.in_fp16 ? launch_kmean_t<128, 1>(a, partial, nchunk, s) : launch_kmean_t<128, 0>(a, partial, nchunk, s);
+  else
+    a.in_fp16 ? launch_kmean_t<64, 1>(a, partial, nchunk, s) : launch_kmean_t<64, 0>(a, partial, nchunk, s);
   return hipGetLastError();
 }
 
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
   dim3 g((unsigned)(a.Nq_pad / kQuantBlock + a.Nk_pad / kQuantBlock), (unsigned)(a.B * a.H));
   if (a.d == 128)
-    k_quant_qk<128><<<g, kPrepThreads, 0, s>>>(a);
+    a.in_fp16 ? k_quant_qk<128, 1><<<g, kPrepThreads, 0, s>>>(a) : k_quant_qk<128, 0><<<g, kPrepThreads, 0, s>>>(a);
   else
-    k_quant_qk<64><<<g, kPrepThreads, 0, s>>>(a);
+    a.in_fp16 ? k_quant_qk<64, 1><<<g, kPrepThreads, 0, s>>>(a) : k_quant_qk<64, 0><<<g, kPrepThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
+template <int D, int IN>
+static void launch_prep_v_t(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
   dim3 g((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.H));
   if (!pv_fp8) {
-    if (a.d == 128)
-      k_prep_v16<128><<<g, kPrepThreads, 0, s>>>(a);
-    else
-      k_prep_v16<64><<<g, kPrepThreads, 0, s>>>(a);
+    k_prep_v16<D, IN><<<g, kPrepThreads, 0, s>>>(a);
   } else {
     dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
-    if (a.d == 128) {
-      k_colred_partial<128, 1><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
+    k_colred_partial<D, 1, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
                                                           a.nchunk);
-      k_prep_v8<128><<<g, kPrepThreads, 0, s>>>(a);
-    } else {
-      k_colred_partial<64, 1><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
-                                                         a.nchunk);
-      k_prep_v8<64><<<g, kPrepThreads, 0, s>>>(a);
-    }
+    k_prep_v8<D, IN><<<g, kPrepThreads, 0, s>>>(a);
   }
+}
+
+hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
+  if (a.d == 128)
+    a.in_fp16 ? launch_prep_v_t<128, 1>(a, pv_fp8, s) : launch_prep_v_t<128, 0>(a, pv_fp8, s);
+  else
+    a.in_fp16 ? launch_prep_v_t<64, 1>(a, pv_fp8, s) : launch_prep_v_t<64, 0>(a, pv_fp8, s);
   return hipGetLastError();
 }
 
 hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s) {
   dim3 g((unsigned)a.nKT, (unsigned)a.nQT, (unsigned)(a.B * a.Hm));
-  k_mask_tiles<<<g, kPrepThreads, 0, s>>>(a);
+  if (a.f32)
+    k_mask_tiles<true><<<g, kPrepThreads, 0, s>>>(a);
+  else
+    k_mask_tiles<false><<<g, kPrepThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

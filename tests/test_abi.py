@@ -87,7 +87,7 @@ def call_quant(L, q, k, out, ws=FAKE, wsb=1 << 20):
 
 @pytest.mark.parametrize("case,status", [
     ("null_q", INVALID), ("null_data", INVALID), ("zero_B", INVALID), ("neg_N", INVALID), ("d96", UNSUPPORTED),
-    ("fp16", UNSUPPORTED), ("bad_dtype", INVALID), ("misaligned", INVALID), ("odd_stride", INVALID),
+    ("qk_dtype_mismatch", INVALID), ("bad_dtype", INVALID), ("misaligned", INVALID), ("odd_stride", INVALID),
     ("small_stride_n", INVALID), ("qk_mismatch_H", INVALID), ("out_null_ptr", INVALID), ("out_bad_pad", INVALID),
     ("out_wrong_N", INVALID), ("no_workspace", WORKSPACE), ("small_workspace", WORKSPACE),
     ("gqa_out_hkv", INVALID), ("gqa_not_divisor", INVALID),
@@ -105,7 +105,7 @@ def test_quantize_validation(L, case, status):
         k = desc(N=-5)
     elif case == "d96":
         q, k = desc(d=96), desc(d=96)
-    elif case == "fp16":
+    elif case == "qk_dtype_mismatch":  # fp16 Q with bf16 K
         q = desc(dtype=1)
     elif case == "bad_dtype":
         q = desc(dtype=9)
@@ -134,14 +134,15 @@ def test_quantize_validation(L, case, status):
     assert call_quant(L, q, k, out, ws, wsb) == status
 
 
-def call_fwd(L, qk, v, mask=None, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30):
-    return L.sage_attn_fwd(ctypes.byref(qk) if qk else None, ctypes.byref(v) if v else None, mask, mask_h, 0, 0, msq,
-                           0, 0.0, pv, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
+def call_fwd(L, qk, v, mask=None, mdt=0, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30):
+    return L.sage_attn_fwd(ctypes.byref(qk) if qk else None, ctypes.byref(v) if v else None, mask, mdt, mask_h, 0, 0,
+                           msq, 0, 0.0, pv, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
 
 
 @pytest.mark.parametrize("case,status", [
     ("null_qk", INVALID), ("v_shape", INVALID), ("pv_bad", UNSUPPORTED), ("out_null", INVALID),
-    ("out_fp16", UNSUPPORTED), ("out_misaligned", INVALID), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
+    ("out_bad_dtype", INVALID), ("out_misaligned", INVALID), ("mask_dtype_bad", INVALID),
+    ("mask_f32_misaligned", INVALID), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
     ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED), ("gqa_v_heads", INVALID),
     ("gqa_hkv_zero", INVALID),
 ])
@@ -156,8 +157,12 @@ def test_attn_validation(L, case, status):
         kw["pv"] = 5
     elif case == "out_null":
         kw["out"] = 0
-    elif case == "out_fp16":
-        kw["odt"] = 1
+    elif case == "out_bad_dtype":
+        kw["odt"] = 7
+    elif case == "mask_dtype_bad":
+        kw.update(mask=FAKE, mdt=5, mask_h=1)
+    elif case == "mask_f32_misaligned":  # an fp32 mask must be 4-byte aligned
+        kw.update(mask=FAKE + 2, mdt=1, mask_h=1)
     elif case == "out_misaligned":
         kw["out"] = FAKE + 8
     elif case == "mask_h_bad":
@@ -194,11 +199,11 @@ def test_debug_validation(L):
 
 def test_prepared_attn_validation(L):
     qk = quant()
-    args = [0, None, 0, 0, 0, 0, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
+    args = [0, None, 0, 0, 0, 0, 0, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
     f = L.sage_attn_fwd_prepared
     assert f(ctypes.byref(qk), 0, None, *args, None, 0, None) == INVALID  # no v_t
     assert f(ctypes.byref(qk), FAKE, None, 1, *args[1:], None, 0, None) == INVALID  # fp8 without v_scale
-    masked = [0, FAKE, 1, 0, 0, 256, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
+    masked = [0, FAKE, 0, 1, 0, 0, 256, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
     assert f(ctypes.byref(qk), FAKE, None, *masked, None, 0, None) == WORKSPACE  # mask needs tile workspace
     assert L.sage_mask_workspace_bytes(2, 8192, 8192, 1) == 2 * 32 * 128 * 4  # one int32 state per tile
     assert L.sage_mask_workspace_bytes(2, 8192, 8192, 0) == 0

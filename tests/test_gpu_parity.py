@@ -1,9 +1,10 @@
 """GPU parity on small and ragged shapes: the HIP path through the C ABI against the CPU oracle.
 
 Bit-exact: K mean, int8 Q/K codes, their scales, the prepared V (fp16 / e4m3 bytes and the e4m3
-per-channel scale) and the int32 Q8.K8^T scores.  Tolerance: O within relative L1 1e-3 of the
-oracle's quantized emulation (both rounded to bf16) and LSE within 1e-3; against fp64 exact
-attention, cosine >= 0.999 and relative L1 <= 3e-2 for FP16 PV.
+per-channel scale) and the int32 Q8.K8^T scores, from bf16 and from fp16 inputs.  Tolerance: O
+within relative L1 1e-3 of the oracle's quantized emulation (both rounded to the output dtype) and
+LSE within 1e-3; against fp64 exact attention, cosine >= 0.999 and relative L1 <= 3e-2 for FP16
+PV.  Masks: boolean and float32 additive.
 """
 
 import dataclasses
@@ -14,7 +15,8 @@ import torch
 
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd import api
-from quantized_attention_quantize_amd.synthetic import make_inputs, random_mask
+from quantized_attention_quantize_amd.synthetic import (additive_mask, make_inputs, random_additive_mask,
+                                                        random_mask)
 
 from gpu_helpers import (DEV, assert_lse_close, bits, cosine, f32_of_bf16_bits, lse_rows, rel_l1, rows_of, say,
                          to_dev, unpermute_vt)
@@ -37,14 +39,15 @@ SHAPES = [(1, 2, 256, 256, 64), (1, 1, 1, 1, 64), (1, 2, 63, 63, 128), (2, 1, 65
           (1, 3, 300, 129, 128), (2, 2, 64, 64, 64), (1, 1, 700, 1000, 128)]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("B,H,Nq,Nk,d", SHAPES)
-def test_quantize_bitexact(orc, B, H, Nq, Nk, d):
-    say(f"quantize B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
-    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=3)
+def test_quantize_bitexact(orc, B, H, Nq, Nk, d, dtype):
+    say(f"quantize B={B} H={H} Nq={Nq} Nk={Nk} d={d} {dtype}")
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=3, dtype=dtype)
     q, k, v = to_dev(inp)
     g = sage.quantize_qk(q, k)
     torch.cuda.synchronize()
-    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k))
+    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k), dtype=inp.dtype)
     assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32))
     assert np.array_equal(g.q8.cpu().numpy(), c.q8)
     assert np.array_equal(g.k8.cpu().numpy(), c.k8)
@@ -128,14 +131,15 @@ def test_debug_scores_extremes(orc):
     assert (got[:, :64] == -127 * 127 * d).all() and (got[:, 64:] == 127 * 127 * d).all()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
 @pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 64), (2, 1, 65, 128), (1, 3, 300, 128), (1, 1, 1, 64)])
-def test_prep_v_bitexact(orc, pv, B, H, N, d):
-    say(f"prep_v {pv} B={B} H={H} N={N} d={d}")
-    inp = make_inputs(B, H, N, N, d, seed=6)
+def test_prep_v_bitexact(orc, pv, B, H, N, d, dtype):
+    say(f"prep_v {pv} B={B} H={H} N={N} d={d} {dtype}")
+    inp = make_inputs(B, H, N, N, d, seed=6, dtype=dtype)
     vt, vs = sage.prepare_v(inp.v.to(DEV), pv)
     torch.cuda.synchronize()
-    want, want_s = orc.prep_v(inp.bits(inp.v), pv)
+    want, want_s = orc.prep_v(inp.bits(inp.v), pv, dtype=inp.dtype)
     got = vt.cpu().numpy()
     got = got.view(np.uint16) if pv == "fp16" else got
     nat = unpermute_vt(got, pv)
@@ -158,6 +162,13 @@ def test_prep_v_fp8_extremes(orc):
     assert np.array_equal(nat[:, :, :N], want) and np.array_equal(vs.cpu().numpy(), want_s)
 
 
+def oracle_mask(mask):
+    """A bool mask as uint8, a float32 mask as it is."""
+    if mask is None:
+        return None
+    return mask.numpy() if mask.dtype == torch.float32 else mask.numpy().astype(np.uint8)
+
+
 def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None):
     q, k, v = to_dev(inp)
     if layout == "NHD":
@@ -166,22 +177,23 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     out, lse = sage.sageattn(q, k, v, tensor_layout=layout, is_causal=causal, attn_mask=mask_dev, sm_scale=sm_scale,
                              return_lse=True, pv_dtype=pv)
     torch.cuda.synchronize()
+    assert out.dtype == inp.q.dtype  # the output takes the input dtype
     B, H, Nq, d = inp.q.shape
     if rows is None:
         rows = np.arange(B * H * Nq, dtype=np.int64)
-    m_u8 = None if mask is None else mask.numpy().astype(np.uint8)
-    r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m_u8,
+    m = oracle_mask(mask)
+    r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m,
                    sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv),
-                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows)
-    ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m_u8,
-                             sm_scale=sm_scale, rows=rows)
+                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype)
+    ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m,
+                             sm_scale=sm_scale, rows=rows, dtype=inp.dtype)
     got_o = rows_of(out, rows, layout)
     got_l = lse_rows(lse, rows)
     return got_o, got_l, r, ex_o, ex_l
 
 
-def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16"):
-    qe_o = f32_of_bf16_bits(r.o16)
+def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16"):
+    qe_o = f32_of_bf16_bits(r.o16) if out_dtype == "bf16" else r.o16.view(np.float16).astype(np.float32)
     e1 = rel_l1(got_o, qe_o)
     assert e1 <= QE_REL_L1, f"rel-L1 vs quantized emulation {e1}"
     assert_lse_close(got_l, r.lse, QE_LSE)
@@ -213,7 +225,48 @@ CASES = [
     dict(name="gqa", B=1, H=4, Hkv=2, Nq=300, Nk=417, d=128),
     dict(name="gqa_fp8_causal", B=2, H=6, Hkv=2, Nq=257, Nk=257, d=64, pv="fp8", causal=True),
     dict(name="mqa_nhd_mask_per_head", B=1, H=4, Hkv=1, Nq=200, Nk=333, d=128, layout="NHD", mask="rand_h"),
+    # fp16 inputs (and outputs)
+    dict(name="fp16_in", B=1, H=2, Nq=300, Nk=417, d=128, dtype="fp16"),
+    dict(name="fp16_in_d64_causal", B=2, H=2, Nq=257, Nk=257, d=64, dtype="fp16", causal=True),
+    dict(name="fp16_in_fp8_pv", B=1, H=2, Nq=400, Nk=333, d=128, dtype="fp16", pv="fp8", sigma=8.0),
+    dict(name="fp16_in_gqa_nhd_mask", B=1, H=4, Hkv=2, Nq=200, Nk=260, d=128, dtype="fp16", layout="NHD",
+         mask="rand_h"),
+    # float32 additive masks
+    dict(name="fmask_bcast", B=2, H=2, Nq=300, Nk=417, d=128, mask="f_rand_1"),
+    dict(name="fmask_per_head_d64", B=1, H=3, Nq=257, Nk=200, d=64, mask="f_rand_h"),
+    dict(name="fmask_causal", B=1, H=2, Nq=600, Nk=600, d=128, mask="f_rand_1", causal=True),
+    dict(name="fmask_fp8", B=1, H=2, Nq=300, Nk=450, d=128, pv="fp8", sigma=8.0, mask="f_rand_h"),
+    dict(name="fmask_fp8_d64_causal", B=1, H=2, Nq=200, Nk=333, d=64, pv="fp8", causal=True, mask="f_rand_1"),
+    dict(name="fmask_zero_inf_tiles", B=1, H=2, Nq=520, Nk=700, d=128, mask="f_tiles"),
+    dict(name="fmask_gqa_fp16_in_nhd", B=1, H=4, Hkv=1, Nq=130, Nk=260, d=128, dtype="fp16", layout="NHD",
+         mask="f_rand_h"),
 ]
+
+
+def case_mask(c, B, H, Nq, Nk):
+    kind = c.get("mask")
+    if kind == "half":
+        mask = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+        mask[..., Nk // 2:] = False
+        return mask
+    if kind == "rand_h":
+        return random_mask(B, H, Nq, Nk, 0.6, seed=3)
+    if kind == "rand_1":
+        return random_mask(B, 1, Nq, Nk, 0.5, seed=4)
+    if kind == "f_rand_1":
+        return random_additive_mask(B, 1, Nq, Nk, p_drop=0.25, scale=2.0, seed=5)
+    if kind == "f_rand_h":
+        return random_additive_mask(B, H, Nq, Nk, p_drop=0.3, scale=3.0, seed=6)
+    if kind == "f_tiles":
+        # whole 256 x 64 tiles that are all 0 (read no mask), all -inf (skipped) or mixed
+        m = torch.zeros(B, 1, Nq, Nk, dtype=torch.float32)
+        m[..., 64:128] = float("-inf")  # a dropped key tile
+        m[..., 256:512, 192:256] = float("-inf")
+        m[..., 300:, 320:384] = 0.5 * torch.randn(B, 1, Nq - 300, 64, generator=torch.Generator().manual_seed(7))
+        m[..., 9, :] = float("-inf")  # a row that sees nothing
+        return m
+    assert kind is None, kind
+    return None
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
@@ -221,20 +274,14 @@ def test_attention_parity(orc, case):
     c = dict(case)
     say(f"attention case {c}")
     B, H, Nq, Nk, d = c["B"], c["H"], c["Nq"], c["Nk"], c["d"]
-    inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=11)
+    dtype = torch.float16 if c.get("dtype") == "fp16" else torch.bfloat16
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=11, dtype=dtype)
     if "Hkv" in c:
         inp = gqa_inputs(inp, c["Hkv"])
-    mask = None
-    if c.get("mask") == "half":
-        mask = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
-        mask[..., Nk // 2:] = False
-    elif c.get("mask") == "rand_h":
-        mask = random_mask(B, H, Nq, Nk, 0.6, seed=3)
-    elif c.get("mask") == "rand_1":
-        mask = random_mask(B, 1, Nq, Nk, 0.5, seed=4)
+    mask = case_mask(c, B, H, Nq, Nk)
     got_o, got_l, r, ex_o, ex_l = run_both(orc, inp, pv=c.get("pv", "fp16"), causal=c.get("causal", False), mask=mask,
                                            sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"))
-    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"))
+    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype)
     say(f"  rel-L1 vs QE {e1:.3e}")
 
 
@@ -294,6 +341,44 @@ def test_errors_raise():
     q, k, v = to_dev(inp)
     with pytest.raises(ValueError):
         sage.sageattn(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
-    with pytest.raises(api.SageError) as ei:
-        sage.sageattn(q.half(), k.half(), v.half())
-    assert ei.value.status == 2
+    with pytest.raises(ValueError):  # mixed input dtypes
+        sage.sageattn(q.half(), k, v)
+    with pytest.raises(ValueError):  # a float mask must be float32
+        sage.sageattn(q, k, v, attn_mask=torch.zeros(1, 1, 64, 64, dtype=torch.float16, device=DEV))
+    with pytest.raises(api.SageError) as ei:  # fp16 Q with bf16 K, past the Python checks
+        sage.quantize_qk(q.half(), k)
+    assert ei.value.status == 1
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_zero_inf_float_mask_equals_boolean_mask(pv):
+    """A float32 mask of 0 / -inf gives what the boolean mask gives, up to the float path's
+    rounding (the float-mask kernel converts every score to fp32 before its maximum)."""
+    B, H, Nq, Nk, d = 1, 2, 300, 400, 128
+    inp = make_inputs(B, H, Nq, Nk, d, seed=17, sigma=4.0 if pv == "fp16" else 8.0)
+    q, k, v = to_dev(inp)
+    bm = random_mask(B, 1, Nq, Nk, 0.5, seed=8)
+    ob, lb = sage.sageattn(q, k, v, attn_mask=bm.to(DEV), return_lse=True, pv_dtype=pv)
+    of, lf = sage.sageattn(q, k, v, attn_mask=additive_mask(bm).to(DEV), return_lse=True, pv_dtype=pv)
+    torch.cuda.synchronize()
+    assert rel_l1(of.float().cpu().numpy(), ob.float().cpu().numpy()) < 2e-3
+    assert_lse_close(lf.cpu().numpy(), lb.cpu().numpy(), 1e-4)
+
+
+def test_output_dtype_is_a_choice(orc):
+    """bf16 inputs with an fp16 output buffer (and the reverse) through the C ABI."""
+    B, H, N, d = 1, 2, 200, 128
+    for dt_in, dt_out in ((torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16)):
+        say(f"output dtype {dt_in} -> {dt_out}")
+        inp = make_inputs(B, H, N, N, d, seed=18, dtype=dt_in)
+        q, k, v = to_dev(inp)
+        qk = sage.quantize_qk(q, k)
+        out = torch.empty(B, H, N, d, dtype=dt_out, device=DEV)
+        sage.attn_fwd(qk, v, out=out)
+        torch.cuda.synchronize()
+        name = "fp16" if dt_out == torch.float16 else "bf16"
+        r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), BN=sage.block_n("fp16"),
+                       tau=sage.softmax_tau("fp16"), lsum_rounded=sage.rowsum_rounded("fp16"), dtype=inp.dtype,
+                       out_dtype=name)
+        want = f32_of_bf16_bits(r.o16) if name == "bf16" else r.o16.view(np.float16).astype(np.float32)
+        assert rel_l1(out.float().cpu().numpy().reshape(-1, d), want) <= QE_REL_L1
