@@ -70,6 +70,7 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     import math
 
     import numpy as np
+    import torch
 
     import oracle
     from quantized_attention_quantize_amd.synthetic import make_inputs
@@ -79,15 +80,16 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     per_head = max(1, min(w.Nq, int(work_target / (heads * w.Nk))))
     g = w.H // (w.Hkv or w.H)  # query heads per key/value head
     inp = make_inputs(1, heads, w.Nq, w.Nk, w.d, w.sigma, seed=0, mask=w.mask,
-                      Hkv=max(1, heads // g) if g > 1 and heads % g == 0 else 0)
+                      Hkv=max(1, heads // g) if g > 1 and heads % g == 0 else 0,
+                      dtype=torch.float16 if w.dtype == "fp16" else torch.bfloat16)
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     local = np.linspace(0, w.Nq - 1, per_head).astype(np.int64)
     rows = np.concatenate([h * w.Nq + local for h in range(heads)])
     t0 = time.perf_counter()
-    qk = oracle.quant_qk(Qb, Kb)
-    vh, vs = oracle.prep_v(Vb, w.pv)
+    qk = oracle.quant_qk(Qb, Kb, dtype=w.dtype)
+    vh, vs = oracle.prep_v(Vb, w.pv, dtype=w.dtype)
     oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, tau=tau,
-                   lsum_rounded=lsum_rounded, rows=rows)
+                   lsum_rounded=lsum_rounded, rows=rows, out_dtype=w.dtype)
     dt = time.perf_counter() - t0
     if w.causal:
         ops = heads * float(sum(4.0 * (int(i) + 1) * w.d for i in local))
@@ -146,12 +148,12 @@ def main():
 
     # every buffer allocated once, outside the timed region
     Hkv = w.Hkv or w.H
-    qk = api.alloc_quantized(w.B, w.H, w.Nq, w.Nk, w.d, dev, Hkv=Hkv)
+    qk = api.alloc_quantized(w.B, w.H, w.Nq, w.Nk, w.d, dev, Hkv=Hkv, dtype=q.dtype)
     qws = api.quantize_workspace(w.B, Hkv, w.Nk, w.d, dev)
     vt, vs = api.alloc_prepared_v(w.B, Hkv, w.Nk, w.d, w.pv, dev)
     vws = api.prepare_v_workspace(w.B, Hkv, w.Nk, w.d, w.pv, dev)
     mws = api.mask_workspace(w.B, w.Nq, w.Nk, 1 if mask is not None else 0, dev)
-    out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=q.dtype, device=dev)
     lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -203,7 +205,7 @@ def main():
         "dtype": "i8+f8" if w.pv == "fp8" else "i8+f16",
         "data": "synthetic",
         "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse,
+                   "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
                    "gpu_ms_per_step": round(gpu_ms_step, 4)},
         "roofline": {"kernel": "k_attn_fwd", "bound": "mfma", "achieved": round(achieved, 2),

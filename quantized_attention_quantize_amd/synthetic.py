@@ -39,11 +39,14 @@ class Workload:
     d: int
     sigma: float
     causal: bool = False
-    mask: str | None = None  # None or "half_keys" ([B,1,Nq,Nk] bool, True for keys < Nk/2)
+    # None, "half_keys" ([B,1,Nq,Nk] bool, True for keys < Nk/2) or "half_keys_f32" (the same as a
+    # float32 additive mask: 0 for keys < Nk/2, -inf beyond)
+    mask: str | None = None
     pv: str = "fp16"  # "fp16" or "fp8"
     lse: bool = True
     note: str = field(default="", compare=False)
     Hkv: int = 0  # key/value heads (group-query attention); 0 = H
+    dtype: str = "bf16"  # element type of q, k, v and the output: "bf16" or "fp16"
 
     @property
     def ops(self) -> float:
@@ -65,6 +68,11 @@ WORKLOADS = {
                            note="B=1 H=24 N=17776 d=128 bf16, non-causal, INT8 QK + FP8 e4m3 PV"),
     "n8k_gqa": Workload("n8k_gqa", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", Hkv=8,
                         note="B=2 H=32 over 8 K/V heads, N=8192 d=128 bf16, non-causal, INT8 QK + FP16 PV, LSE"),
+    "n8k_fp16": Workload("n8k_fp16", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", dtype="fp16",
+                         note="B=2 H=32 N=8192 d=128 fp16 in and out, non-causal, INT8 QK + FP16 PV, LSE"),
+    "n8k_fmask": Workload("n8k_fmask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys_f32", pv="fp16",
+                          note="B=2 H=32 N=8192 d=128 bf16, float32 additive mask [B,1,N,N]: 0 for keys < N/2, "
+                               "-inf beyond, LSE"),
 }
 
 
@@ -73,7 +81,7 @@ class Inputs:
     q: torch.Tensor  # bf16 or fp16 [B,H,Nq,d] (CPU)
     k: torch.Tensor
     v: torch.Tensor
-    mask: torch.Tensor | None  # bool [B,1,Nq,Nk] (CPU) or None
+    mask: torch.Tensor | None  # bool or float32 [B,1,Nq,Nk] (CPU) or None
 
     def bits(self, t: torch.Tensor) -> np.ndarray:
         """bf16 / fp16 tensor -> numpy uint16 bit patterns (what the oracle consumes)."""
@@ -86,7 +94,10 @@ class Inputs:
 
     @property
     def mask_u8(self):
-        return None if self.mask is None else self.mask.numpy().astype(np.uint8)
+        """The mask as the oracle takes it: uint8 for a boolean mask, float32 as it is."""
+        if self.mask is None:
+            return None
+        return self.mask.numpy() if self.mask.dtype == torch.float32 else self.mask.numpy().astype(np.uint8)
 
 
 def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0, dtype=torch.bfloat16) -> Inputs:
@@ -102,16 +113,19 @@ def make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=0, mask=None, Hkv=0, dtype=torc
     k = (kn + kb).to(dtype)
     del kn
     m = None
-    if mask == "half_keys":
+    if mask in ("half_keys", "half_keys_f32"):
         m = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
         m[:, :, :, Nk // 2:] = False
+        if mask == "half_keys_f32":
+            m = additive_mask(m)
     elif mask is not None:
         raise ValueError(mask)
     return Inputs(q.to(dtype), k, v.to(dtype), m)
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
-    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.sigma, seed, w.mask, w.Hkv)
+    return make_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.sigma, seed, w.mask, w.Hkv,
+                       torch.float16 if w.dtype == "fp16" else torch.bfloat16)
 
 
 def random_mask(B, Hm, Nq, Nk, p_keep=0.7, seed=1) -> torch.Tensor:

@@ -90,17 +90,20 @@ def assert_lse_close(got, want, atol):
         assert err <= atol, f"LSE max abs diff {err} > {atol}"
 
 
-def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None):
+def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None, dtype="bf16"):
     """Per-row bound on |LSE(quantized scores) - LSE(exact scores)|.
 
     logsumexp is 1-Lipschitz in the max norm, so the LSE moves by at most the largest score error
     over the row's visible keys.  With |q - qs*q8| <= qs/2 and |ks - ks*k8| <= ks/2 per element,
     |s_ij - s~_ij| <= sm * (sum_c |q_ic| * ks_j/2 + sum_c |k~_jc| * qs_i/2 + d * qs_i*ks_j/4),
-    where k~ is the smoothed key (the smoothing shift itself cancels between the two LSEs)."""
+    where k~ is the smoothed key (the smoothing shift itself cancels between the two LSEs, and so
+    does an additive mask).  mask: uint8 (0 = masked) or float32 (-inf = masked); Qb, Kb are bits
+    of ``dtype``."""
     B, H, _, d = Qb.shape
     grp = H // Kb.shape[1]  # query heads per key head (group-query attention)
-    Q = f32_of_bf16_bits(Qb).astype(np.float64)
-    Ks = (f32_of_bf16_bits(Kb) - qk.kmean[:, :, None, :]).astype(np.float32).astype(np.float64)
+    dec = f32_of_bf16_bits if dtype == "bf16" else (lambda b: b.view(np.float16).astype(np.float32))
+    Q = dec(Qb).astype(np.float64)
+    Ks = (dec(Kb) - qk.kmean[:, :, None, :]).astype(np.float32).astype(np.float64)
     sk = np.abs(Ks).sum(-1)  # [B,Hkv,Nk]
     out = np.empty(rows.size)
     for n, rid in enumerate(rows):
@@ -115,6 +118,7 @@ def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None)
         if causal:
             valid[i + 1:] = False
         if mask is not None:
-            valid &= mask[b, 0 if mask.shape[1] == 1 else h, i] != 0
+            mrow = mask[b, 0 if mask.shape[1] == 1 else h, i]
+            valid &= (mrow != -np.inf) if mask.dtype == np.float32 else (mrow != 0)
         out[n] = bnd[valid].max() if valid.any() else 0.0
     return out

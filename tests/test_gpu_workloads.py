@@ -18,7 +18,8 @@ from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_qu
 
 pytestmark = pytest.mark.gpu
 
-N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048}
+N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048,
+                 "n8k_fp16": 2048, "n8k_fmask": 2048}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -33,7 +34,7 @@ def test_workload_parity(orc, name):
     # quantization: whole tensors, bit for bit
     g = sage.quantize_qk(q, k)
     torch.cuda.synchronize()
-    c = orc.quant_qk(Qb, Kb)
+    c = orc.quant_qk(Qb, Kb, dtype=inp.dtype)
     assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32)), "k_mean"
     assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32)), "q_scale"
     assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32)), "k_scale"
@@ -45,7 +46,7 @@ def test_workload_parity(orc, name):
     # prepared V: whole tensor, bit for bit
     vt, vs = sage.prepare_v(v, w.pv)
     torch.cuda.synchronize()
-    vh, vsc = orc.prep_v(Vb, w.pv)
+    vh, vsc = orc.prep_v(Vb, w.pv, dtype=inp.dtype)
     got = vt.cpu().numpy()
     nat = unpermute_vt(got.view(np.uint16) if w.pv == "fp16" else got, w.pv)
     assert np.array_equal(nat[:, :, :w.Nk], vh), "prepared V"
@@ -81,15 +82,17 @@ def test_workload_parity(orc, name):
     vh_o, vs_o = (vh, vsc)
     o32, obf, qlse = orc.attn_qe(c, vh_o, vs_o, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8,
                                  BN=sage.block_n(w.pv), tau=sage.softmax_tau(w.pv),
-                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows)
+                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows, out_dtype=inp.dtype)
     got_o = rows_of(out, rows)
     got_l = lse_rows(lse, rows)
-    e_qe = rel_l1(got_o, f32_of_bf16_bits(obf))
+    assert out.dtype == inp.q.dtype
+    want_o = f32_of_bf16_bits(obf) if inp.dtype == "bf16" else obf.view(np.float16).astype(np.float32)
+    e_qe = rel_l1(got_o, want_o)
     say(f"  rows={rows.size} rel-L1 vs quantized emulation {e_qe:.3e}")
     assert e_qe <= 1e-3
     assert_lse_close(got_l, qlse, 1e-3)
     ex_rows = rows[:: max(1, rows.size // 512)]
-    ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, mask=m_u8, rows=ex_rows)
+    ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, mask=m_u8, rows=ex_rows, dtype=inp.dtype)
     sel = np.searchsorted(rows, ex_rows)
     cos = cosine(got_o[sel], ex_o)
     e_ex = rel_l1(got_o[sel], ex_o)
@@ -102,7 +105,7 @@ def test_workload_parity(orc, name):
         # cannot be met by a faithful implementation; the measured value is reported above.
         assert e_ex <= 5e-2
     # LSE against the exact LSE: within the per-row score-quantization bound (plus fp32 slack)
-    bound = lse_quant_bound(c, Qb, Kb, ex_rows, w.Nq, w.Nk, orc.default_sm_scale(w.d), w.causal, m_u8)
+    bound = lse_quant_bound(c, Qb, Kb, ex_rows, w.Nq, w.Nk, orc.default_sm_scale(w.d), w.causal, m_u8, inp.dtype)
     excess = np.abs(got_l[sel] - ex_l) - bound
     say(f"  LSE vs exact: worst excess over the quantization bound {excess.max():.3e} (bound max {bound.max():.3e})")
     assert excess.max() <= 1e-4
