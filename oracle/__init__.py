@@ -18,6 +18,7 @@ or float32, added to the scaled scores):
 * ``attn_qe(...)``                  -- the quantized emulation (online softmax over BN-key tiles)
 * ``attn_ex(...)``                  -- fp64 exact attention on the unquantized inputs
 * ``run_qe(...)``                   -- convenience: all the steps above for given rows
+* ``merge_lse(o_parts, lse_parts)`` -- partial results over disjoint key sets -> the result over their union
 """
 
 from __future__ import annotations
@@ -73,8 +74,9 @@ def lib():
         L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32, P,
                                   I, P, i32, P, P]
         L.orc_attn_ex.argtypes = [P, P, P, i32, P, i32, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
+        L.orc_merge_lse.argtypes = [P, P, I, I, I, P, P]
         for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
-                     "orc_attn_qe", "orc_attn_ex"):
+                     "orc_attn_qe", "orc_attn_ex", "orc_merge_lse"):
             getattr(L, name).restype = None
         _lib = L
     return _lib
@@ -306,3 +308,18 @@ def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64,
     o32, o16, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, tau=tau,
                             lsum_rounded=lsum_rounded, rows=rows, out_dtype=out_dtype or dtype)
     return QEResult(qk, vhat, vs, o32, o16, lse)
+
+
+def merge_lse(o_parts, lse_parts):
+    """Merge S partial attention results over disjoint key sets.
+
+    o_parts: [S, R, d] (any float dtype; taken as fp32), lse_parts: [S, R] natural-log LSEs.
+    Returns (out [R, d] fp64, lse [R] fp64)."""
+    o = _c(o_parts, np.float32)
+    lp = _c(lse_parts, np.float32)
+    S, R, d = o.shape
+    assert lp.shape == (S, R)
+    out = np.empty((R, d), np.float64)
+    lse = np.empty((R,), np.float64)
+    lib().orc_merge_lse(_p(o), _p(lp), S, R, d, _p(out), _p(lse))
+    return out, lse

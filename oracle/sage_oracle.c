@@ -496,3 +496,36 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in
     free(q);
   }
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Merging partial attention results over disjoint key sets (the use of the LSE output on    */
+/* the docs digest, "Utilize SageAttention for Distributed Inference": sequence parallelism,  */
+/* Ring Attention).  Written from the softmax's definition: if part s covers keys K_s with    */
+/* O_s = sum_{j in K_s} e^{s_j} v_j / sum_{j in K_s} e^{s_j} and LSE_s = log sum_{j in K_s}    */
+/* e^{s_j}, then over the union LSE = log sum_s e^{LSE_s} and O = sum_s e^{LSE_s - LSE} O_s.  */
+/* A part with LSE_s = -inf (no visible key) contributes nothing; if every part has -inf,     */
+/* O = 0 and LSE = -inf.                                                                      */
+/* o_parts [S][R][d] (fp32), lse_parts [S][R]; out [R][d] and lse [R] in fp64.                */
+/* ------------------------------------------------------------------------------------------ */
+void orc_merge_lse(const float* o_parts, const float* lse_parts, int64_t S, int64_t R, int64_t d, double* out,
+                   double* lse) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < R; ++r) {
+    double m = -INFINITY;
+    for (int64_t s = 0; s < S; ++s)
+      if ((double)lse_parts[s * R + r] > m) m = (double)lse_parts[s * R + r];
+    for (int64_t c = 0; c < d; ++c) out[r * d + c] = 0.0;
+    if (m == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double tot = 0.0;
+    for (int64_t s = 0; s < S; ++s) tot += exp((double)lse_parts[s * R + r] - m);
+    double L = m + log(tot);
+    for (int64_t s = 0; s < S; ++s) {
+      double w = exp((double)lse_parts[s * R + r] - L);
+      for (int64_t c = 0; c < d; ++c) out[r * d + c] += w * (double)o_parts[(s * R + r) * d + c];
+    }
+    lse[r] = L;
+  }
+}
