@@ -48,8 +48,9 @@ typedef enum {
   SAGE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } sage_status;
 
-/* Element type of Q, K, V and of the output O. */
-typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1 } sage_dtype;
+/* Element type of Q, K, V (bf16 or fp16) and of the output O (any of the three; fp32 for partial
+ * results that sage_merge_lse combines later). */
+typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1, SAGE_F32 = 2 } sage_dtype;
 
 /* Attention mask element type (optional boolean or float32 mask: Triton INT8/FP16 kernel section).
  *   SAGE_MASK_BOOL: uint8, nonzero = attend, 0 = masked out.
@@ -161,8 +162,8 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  *         semantics: Triton INT8/FP16 kernel examples section, where False entries are masked out.)
  *   causal: key j is visible to query i only if j <= i (top-left aligned).
  *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
- *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 or SAGE_FP16, rounded to nearest even) addressed with
- *        out_stride_{b,h,n}.
+ *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 or SAGE_FP16, rounded to nearest even, or SAGE_F32)
+ *        addressed with out_stride_{b,h,n} (every row 16-byte aligned).
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled, unsmoothed
  *        scores (lse_corr added back), for merging partial results ("return_lse" on the
  *        sageattn section and on "Utilize SageAttention for Distributed Inference").
@@ -192,6 +193,23 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
                                    sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
                                    int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/* Merge S partial attention results over disjoint key sets into the result over their union
+ * (what the LSE output is for: "Utilize SageAttention for Distributed Inference" on the
+ * SageAttention docs digest -- sequence parallelism, Ring Attention).  With part s covering the
+ * keys K_s: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the softmax identity; a
+ * part with LSE_s = -inf adds nothing; all -inf gives O = 0, LSE = -inf).  Computed in fp32.
+ *   o_parts:   S contiguous [B][H][Nq][d] outputs of part_dtype (fp32 keeps the parts unrounded),
+ *              16-byte aligned; e.g. sage_attn_fwd outputs over key slices.
+ *   lse_parts: fp32 [S][B][H][Nq], natural log, as sage_attn_fwd writes them.
+ *   out:       [B,H,Nq,d] of out_dtype with out_stride_{b,h,n} (elements; rows 16-byte aligned).
+ *   lse:       NULL, or fp32 [B][H][Nq] contiguous.
+ * d must be a positive multiple of 8 (at most 1024).  No workspace.
+ * Errors: INVALID_ARGUMENT (sizes, null or misaligned pointers, dtypes), UNSUPPORTED (device), HIP. */
+sage_status sage_merge_lse(int64_t S, int64_t B, int64_t H, int64_t Nq, int64_t d, const void* o_parts,
+                           sage_dtype part_dtype, const float* lse_parts, void* out, sage_dtype out_dtype,
+                           int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
+                           void* stream);
 
 /* Debug: the raw int32 scores acc[i,j] = sum_c q8[i,c]*k8[j,c] of query head (b,h) (and its key
  * head h / (H / Hkv)) for rows

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     debug_qk_int32,
     lib_path,
     load_library,
+    merge_lse,
     pad_tokens,
     prepare_v,
     quantize_qk,

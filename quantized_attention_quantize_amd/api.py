@@ -28,7 +28,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsage_mi355x.so")
 
-SAGE_BF16, SAGE_FP16 = 0, 1
+SAGE_BF16, SAGE_FP16, SAGE_F32 = 0, 1, 2
 SAGE_MASK_BOOL, SAGE_MASK_F32 = 0, 1
 PV_CODES = {"fp16": 0, "fp8": 1, "fp8_e4m3": 1}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
@@ -57,8 +57,8 @@ _lib = None
 
 EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_rounded", "sage_quantize_workspace_bytes", "sage_quantize_qk",
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
-           "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_debug_qk_int32",
-           "sage_status_string")
+           "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_merge_lse",
+           "sage_debug_qk_int32", "sage_status_string")
 
 
 def lib_path() -> str:
@@ -100,6 +100,8 @@ def load_library():
     L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I, I64, I64, I64, I64, I, F, P, I, I64, I64,
                                          I64, P, P, SZ, P]
     L.sage_attn_fwd_prepared.restype = I
+    L.sage_merge_lse.argtypes = [I64, I64, I64, I64, I64, P, I, P, P, I, I64, I64, I64, P, P]
+    L.sage_merge_lse.restype = I
     L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
     L.sage_debug_qk_int32.restype = I
     L.sage_status_string.argtypes = [I]
@@ -136,12 +138,14 @@ def rowsum_rounded(pv_dtype: str = "fp16") -> bool:
     return bool(load_library().sage_rowsum_rounded(PV_CODES[pv_dtype]))
 
 
-def _dtype_code(dt: torch.dtype, what: str) -> int:
+def _dtype_code(dt: torch.dtype, what: str, allow_f32: bool = False) -> int:
     if dt == torch.bfloat16:
         return SAGE_BF16
     if dt == torch.float16:
         return SAGE_FP16
-    raise ValueError(f"{what} must be bfloat16 or float16, got {dt}")
+    if allow_f32 and dt == torch.float32:
+        return SAGE_F32
+    raise ValueError(f"{what} must be bfloat16 or float16{' or float32' if allow_f32 else ''}, got {dt}")
 
 
 def _desc(t: torch.Tensor, layout: str) -> QKVDesc:
@@ -268,7 +272,7 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
     if workspace is None:
         workspace = fwd_workspace(B, qk.Hkv, Nq, Nk, d, pv_dtype, mh, v.device)
     qs = qk.cstruct()
-    odt = _dtype_code(out.dtype, "out")
+    odt = _dtype_code(out.dtype, "out", allow_f32=True)
     _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mcode, mh, msb,
                            msh, msq,
                            1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale), PV_CODES[pv_dtype],
@@ -369,7 +373,7 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
     if workspace is None and mh > 0:
         workspace = mask_workspace(B, Nq, Nk, mh, dev)
     qs = qk.cstruct()
-    odt = _dtype_code(out.dtype, "out")
+    odt = _dtype_code(out.dtype, "out", allow_f32=True)
     _check(L.sage_attn_fwd_prepared(ctypes.byref(qs), v_t.data_ptr(), None if v_scale is None else v_scale.data_ptr(),
                                     PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mcode, mh, msb, msh, msq,
                                     1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
@@ -382,3 +386,29 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
 
 def default_sm_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out: torch.Tensor | None = None,
+              lse: torch.Tensor | None = None, out_dtype: torch.dtype | None = None, return_lse: bool = True):
+    """Merge S partial attention results over disjoint key sets (e.g. key slices of one sequence).
+
+    o_parts: [S, B, H, Nq, d] (bf16, fp16 or fp32; contiguous), lse_parts: fp32 [S, B, H, Nq] as
+    returned with return_lse=True.  Returns out [B, H, Nq, d] (out_dtype, default that of the
+    parts) or (out, lse)."""
+    L = load_library()
+    if o_parts.dim() != 5 or lse_parts.shape != o_parts.shape[:4]:
+        raise ValueError("o_parts must be [S,B,H,Nq,d] and lse_parts [S,B,H,Nq]")
+    if lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32")
+    o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+    S, B, H, Nq, d = o_parts.shape
+    pdt = _dtype_code(o_parts.dtype, "o_parts", allow_f32=True)
+    if out is None:
+        out = torch.empty(B, H, Nq, d, dtype=out_dtype or o_parts.dtype, device=o_parts.device)
+    odt = _dtype_code(out.dtype, "out", allow_f32=True)
+    if return_lse and lse is None:
+        lse = torch.empty(B, H, Nq, dtype=torch.float32, device=o_parts.device)
+    _check(L.sage_merge_lse(S, B, H, Nq, d, o_parts.data_ptr(), pdt, lse_parts.data_ptr(), out.data_ptr(), odt,
+                            out.stride(0), out.stride(1), out.stride(2), None if lse is None else lse.data_ptr(),
+                            _stream(o_parts)), "sage_merge_lse")
+    return (out, lse) if return_lse else out

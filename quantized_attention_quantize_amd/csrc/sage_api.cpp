@@ -240,9 +240,10 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
   if ((s = check_qk(qk)) != SAGE_OK) return s;
   if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
   if (!out) return SAGE_ERR_INVALID_ARGUMENT;
-  if (out_dtype != SAGE_BF16 && out_dtype != SAGE_FP16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SAGE_BF16 && out_dtype != SAGE_FP16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARGUMENT;
   if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < qk->d) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(out) || (out_stride_b % 8) || (out_stride_h % 8) || (out_stride_n % 8))
+  const int64_t oel = out_dtype == SAGE_F32 ? 4 : 8;  // elements per 16 bytes
+  if (!aligned16(out) || (out_stride_b % oel) || (out_stride_h % oel) || (out_stride_n % oel))
     return SAGE_ERR_INVALID_ARGUMENT;
   c->mh = 0;
   if (mask) {
@@ -306,8 +307,8 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   a.corr = qk->lse_corr;
   a.vt = v_t;
   a.vscale = pv == SAGE_PV_FP8_E4M3 ? v_scale : nullptr;
-  a.out = static_cast<unsigned short*>(out);
-  a.out_fp16 = out_dtype == SAGE_FP16;
+  a.out = out;
+  a.out_kind = out_dtype == SAGE_F32 ? 2 : (out_dtype == SAGE_FP16 ? 1 : 0);
   a.o_sb = out_stride_b;
   a.o_sh = out_stride_h;
   a.o_sn = out_stride_n;
@@ -383,6 +384,38 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
   return enqueue_attention(qk, v_t, v_scale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h, mask_stride_q,
                            causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            static_cast<int*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_merge_lse(int64_t S, int64_t B, int64_t H, int64_t Nq, int64_t d, const void* o_parts,
+                           sage_dtype part_dtype, const float* lse_parts, void* out, sage_dtype out_dtype,
+                           int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
+                           void* stream) {
+  if (S <= 0 || B <= 0 || H <= 0 || Nq <= 0 || d <= 0 || d % 8 != 0 || d > 1024) return SAGE_ERR_INVALID_ARGUMENT;
+  if (B * H > 65535 || Nq > kMaxTokens || S > 4096) return SAGE_ERR_INVALID_ARGUMENT;
+  auto dtype_ok = [](sage_dtype t) { return t == SAGE_BF16 || t == SAGE_FP16 || t == SAGE_F32; };
+  if (!dtype_ok(part_dtype) || !dtype_ok(out_dtype)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!o_parts || !lse_parts || !out || !aligned16(o_parts) || !aligned16(out)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < d) return SAGE_ERR_INVALID_ARGUMENT;
+  const int64_t oel = out_dtype == SAGE_F32 ? 4 : 8;  // elements per 16 bytes
+  if ((out_stride_b % oel) || (out_stride_h % oel) || (out_stride_n % oel)) return SAGE_ERR_INVALID_ARGUMENT;
+  sage_status s;
+  if ((s = check_device()) != SAGE_OK) return s;
+  MergeArgs a;
+  a.parts = o_parts;
+  a.lse_parts = lse_parts;
+  a.S = S;
+  a.R = B * H * Nq;
+  a.d = d;
+  a.H = H;
+  a.Nq = Nq;
+  a.out = out;
+  a.o_sb = out_stride_b;
+  a.o_sh = out_stride_h;
+  a.o_sn = out_stride_n;
+  a.out_kind = out_dtype == SAGE_F32 ? 2 : (out_dtype == SAGE_FP16 ? 1 : 0);
+  a.part_kind = part_dtype == SAGE_F32 ? 2 : (part_dtype == SAGE_FP16 ? 1 : 0);
+  a.lse = lse;
+  return hip_status(launch_merge(a, static_cast<hipStream_t>(stream)));
 }
 
 sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, int64_t row0, int64_t nrows,

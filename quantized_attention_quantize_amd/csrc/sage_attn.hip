@@ -38,8 +38,6 @@ namespace sage {
 
 constexpr int kWaves = kBlockM / 32;  // waves per attention workgroup, 32 query rows each
 constexpr int kAttnThreads = kWaves * 64;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_448 = 8.807354922057604f;
 
 template <int D, int PV>
@@ -783,12 +781,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   __syncthreads();
   if (n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
 
-  // epilogue: normalize, store O (bf16 or fp16) and the LSE
+  // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
   if (row < nq) {
     const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    unsigned short* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;
+    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;  // elements
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -802,15 +800,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
           else
             f[e] = o[db][rq * 4 + e] * inv;
         }
-        uint2 pk;
-        if (a.out_fp16) {
-          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
-          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
+        if (a.out_kind == 2) {  // fp32, e.g. partial results that are merged later
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
         } else {
-          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
-          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
+          uint2 pk;
+          if (a.out_kind == 1) {
+            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
+            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
+          } else {
+            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
+            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
+          }
+          *reinterpret_cast<uint2*>(static_cast<unsigned short*>(a.out) + obase + d0) = pk;
         }
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
     if (g == 0 && a.lse) {
       float v = -INFINITY;

@@ -28,6 +28,8 @@ constexpr int kMaskTileRows = kBlockM;       // mask classification granularity 
 // 0x4B400000 + acc is the binary32 pattern of the float 1.5*2^23 + acc, so an MFMA started from
 // this value yields the scores already as floats (offset by 1.5*2^23).
 constexpr int kMagicBits = 0x4B400000;
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e), rounded to fp32
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2), rounded to fp32
 constexpr float kMagic = 12582912.0f;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short h) {

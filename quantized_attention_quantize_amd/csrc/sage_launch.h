@@ -63,8 +63,8 @@ struct AttnArgs {
   int mask_f32;       // 0: uint8, nonzero = attend; 1: fp32 added to the scaled score, -inf = drop
   const int* mtiles;  // tile states or nullptr
   int64_t Hm;             // 0 = no mask
-  unsigned short* out;    // bf16, or fp16 if out_fp16
-  int out_fp16;
+  void* out;    // out_kind 0: bf16, 1: fp16, 2: fp32
+  int out_kind;
   int64_t o_sb, o_sh, o_sn;
   float* lse;  // nullptr = not requested
   int64_t B, H, Hkv, Nq, Nk, Nq_pad, Nk_pad;  // query head h reads key/value head h / (H / Hkv)
@@ -72,6 +72,17 @@ struct AttnArgs {
   int causal;
   int mask_vec4;  // mask rows aligned to 4 elements: read 4 mask elements at a time
   float sm_scale;
+};
+
+struct MergeArgs {
+  const void* parts;      // [S][R][d] partial outputs, part_kind 0: bf16, 1: fp16, 2: fp32
+  const float* lse_parts;  // [S][R] natural-log LSEs (-inf: the part saw no key of the row)
+  int64_t S, R, d;        // R = B*H*Nq rows, row r = (b*H + h)*Nq + i
+  int64_t H, Nq;
+  void* out;              // out_kind 0: bf16, 1: fp16, 2: fp32; element strides below
+  int64_t o_sb, o_sh, o_sn;
+  int out_kind, part_kind;
+  float* lse;             // [R] or nullptr
 };
 
 struct DebugQKArgs {
@@ -88,5 +99,6 @@ hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s);
 hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s);
 hipError_t launch_debug_qk(const DebugQKArgs& a, int d, int64_t Nq_pad, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace sage

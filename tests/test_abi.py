@@ -218,3 +218,34 @@ def test_no_oracle_on_product_path():
         if path.endswith((".py", ".cpp", ".hip", ".h")):
             text = open(path).read()
             assert not re.search(r"^\s*(import|from)\s+oracle\b|libsage_oracle|sage_oracle\.c", text, flags=re.M), path
+
+
+@pytest.mark.parametrize("case", ["S0", "d_odd", "d_big", "bad_part_dtype", "bad_out_dtype", "null_parts", "null_lse",
+                                  "null_out", "parts_misaligned", "out_stride_small", "out_stride_odd"])
+def test_merge_validation(L, case):
+    a = dict(S=2, B=1, H=2, Nq=64, d=64, parts=FAKE, pdt=0, lse=FAKE, out=FAKE, odt=0, sb=2 * 64 * 64, sh=64 * 64, sn=64)
+    if case == "S0":
+        a["S"] = 0
+    elif case == "d_odd":
+        a["d"] = 60
+    elif case == "d_big":
+        a["d"] = 2048
+    elif case == "bad_part_dtype":
+        a["pdt"] = 3
+    elif case == "bad_out_dtype":
+        a["odt"] = -1
+    elif case == "null_parts":
+        a["parts"] = 0
+    elif case == "null_lse":
+        a["lse"] = 0
+    elif case == "null_out":
+        a["out"] = 0
+    elif case == "parts_misaligned":
+        a["parts"] = FAKE + 4
+    elif case == "out_stride_small":
+        a["sn"] = 32
+    elif case == "out_stride_odd":
+        a["sn"] = 68
+    st = L.sage_merge_lse(a["S"], a["B"], a["H"], a["Nq"], a["d"], a["parts"], a["pdt"], a["lse"], a["out"], a["odt"],
+                          a["sb"], a["sh"], a["sn"], None, None)
+    assert st == INVALID
