@@ -86,17 +86,25 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     local = np.linspace(0, w.Nq - 1, per_head).astype(np.int64)
     rows = np.concatenate([h * w.Nq + local for h in range(heads)])
     t0 = time.perf_counter()
-    qk = oracle.quant_qk(Qb, Kb, dtype=w.dtype)
-    vh, vs = oracle.prep_v(Vb, w.pv, dtype=w.dtype)
-    oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, w.Nk, causal=w.causal, mask=inp.mask_u8, BN=64, tau=tau,
-                   lsum_rounded=lsum_rounded, rows=rows, out_dtype=w.dtype)
+    S = w.kv_splits
+    bounds = [w.Nk * s // S for s in range(S + 1)]
+    parts = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):  # one slice, or all keys
+        Ks, Vs = np.ascontiguousarray(Kb[:, :, lo:hi]), np.ascontiguousarray(Vb[:, :, lo:hi])
+        qk = oracle.quant_qk(Qb, Ks, dtype=w.dtype)
+        vh, vs = oracle.prep_v(Vs, w.pv, dtype=w.dtype)
+        parts.append(oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, hi - lo, causal=w.causal, mask=inp.mask_u8, BN=64,
+                                    tau=tau, lsum_rounded=lsum_rounded, rows=rows, out_dtype=w.dtype))
+    if S > 1:
+        oracle.merge_lse(np.stack([p[0] for p in parts]), np.stack([p[2] for p in parts]))
     dt = time.perf_counter() - t0
     if w.causal:
         ops = heads * float(sum(4.0 * (int(i) + 1) * w.d for i in local))
     else:  # the mask workload counts formula ops too, as the GPU metric does
         ops = 4.0 * rows.size * w.Nk * w.d
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{heads} head(s) (B=1) of {w.name}: K mean + INT8 quantization + V prep of the heads, "
+            "sample": f"{heads} head(s) (B=1) of {w.name}: K mean + INT8 quantization + V prep of the heads"
+                      f"{f' per key slice ({S}), merged' if S > 1 else ''}, "
                       f"quantized emulation of {per_head} evenly spaced query rows per head x {w.Nk} keys; "
                       f"{dt:.2f} s"}
 
@@ -148,47 +156,74 @@ def main():
 
     # every buffer allocated once, outside the timed region
     Hkv = w.Hkv or w.H
-    qk = api.alloc_quantized(w.B, w.H, w.Nq, w.Nk, w.d, dev, Hkv=Hkv, dtype=q.dtype)
-    qws = api.quantize_workspace(w.B, Hkv, w.Nk, w.d, dev)
-    vt, vs = api.alloc_prepared_v(w.B, Hkv, w.Nk, w.d, w.pv, dev)
-    vws = api.prepare_v_workspace(w.B, Hkv, w.Nk, w.d, w.pv, dev)
+    S = w.kv_splits
+    bounds = [w.Nk * s // S for s in range(S + 1)]
+    if S > 1:  # key slices, resident before timing
+        kv = [(k[:, :, lo:hi].contiguous(), v[:, :, lo:hi].contiguous()) for lo, hi in zip(bounds[:-1], bounds[1:])]
+    else:
+        kv = [(k, v)]
+    del k, v
+    qks, qwss, vts, vwss = [], [], [], []
+    for ks, _ in kv:
+        nk = ks.shape[2]
+        qks.append(api.alloc_quantized(w.B, w.H, w.Nq, nk, w.d, dev, Hkv=Hkv, dtype=q.dtype))
+        qwss.append(api.quantize_workspace(w.B, Hkv, nk, w.d, dev))
+        vts.append(api.alloc_prepared_v(w.B, Hkv, nk, w.d, w.pv, dev))
+        vwss.append(api.prepare_v_workspace(w.B, Hkv, nk, w.d, w.pv, dev))
     mws = api.mask_workspace(w.B, w.Nq, w.Nk, 1 if mask is not None else 0, dev)
     out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=q.dtype, device=dev)
     lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
+    if S > 1:
+        if mask is not None or w.causal:
+            raise SystemExit("key-sliced workloads take neither a mask nor causality")
+        o_parts = torch.empty(S, w.B, w.H, w.Nq, w.d, dtype=torch.float32, device=dev)
+        l_parts = torch.empty(S, w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        api.quantize_qk(q, k, out=qk, workspace=qws)
-        api.prepare_v(v, w.pv, out=(vt, vs), workspace=vws)
-        if ev is not None:
-            ev[0].record(stream)
-        api.attn_fwd_prepared(qk, vt, vs, pv_dtype=w.pv, is_causal=w.causal, attn_mask=mask, return_lse=w.lse,
-                              out=out, lse=lse, workspace=mws)
-        if ev is not None:
-            ev[1].record(stream)
+    def step(ev=None, mev=None):
+        for s, (ks, vs_) in enumerate(kv):
+            api.quantize_qk(q, ks, out=qks[s], workspace=qwss[s])
+            api.prepare_v(vs_, w.pv, out=vts[s], workspace=vwss[s])
+            if ev is not None:
+                ev[s][0].record(stream)
+            api.attn_fwd_prepared(qks[s], vts[s][0], vts[s][1], pv_dtype=w.pv, is_causal=w.causal, attn_mask=mask,
+                                  return_lse=w.lse or S > 1, out=out if S == 1 else o_parts[s],
+                                  lse=lse if S == 1 else l_parts[s], workspace=mws)
+            if ev is not None:
+                ev[s][1].record(stream)
+        if S > 1:
+            if mev is not None:
+                mev[0].record(stream)
+            api.merge_lse(o_parts, l_parts, out=out, lse=lse if w.lse else None, return_lse=w.lse)
+            if mev is not None:
+                mev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    evs = [[pair() for _ in range(S)] for _ in range(args.steps)]
+    mevs = [pair() for _ in range(args.steps)] if S > 1 else [None] * args.steps
+    g0, g1 = pair()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], mevs[i])
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_step = wall * 1e3 / args.steps
     gpu_ms_step = g0.elapsed_time(g1) / args.steps
-    attn_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    attn_ms = sorted(a.elapsed_time(b) for e in evs for a, b in e)  # one entry per attention launch
     attn_avg = sum(attn_ms) / len(attn_ms)
     ops = w.ops
     value = ops / (ms_step * 1e-3) / 1e12
-    achieved = ops / (attn_avg * 1e-3) / 1e12
+    achieved = ops / S / (attn_avg * 1e-3) / 1e12  # one launch covers 1/S of the keys
     traffic = traffic_from_profile(w.name)
 
     line = {
@@ -216,6 +251,15 @@ def main():
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
                      "min_ms": round(attn_ms[0], 4)},
     }
+    if S > 1:
+        merge_ms = sorted(a.elapsed_time(b) for a, b in mevs)
+        merge_avg = sum(merge_ms) / len(merge_ms)
+        R = w.B * w.H * w.Nq
+        mbytes = S * R * w.d * 4 + S * R * 4 + R * w.d * out.element_size() + (R * 4 if w.lse else 0)
+        line["merge_roofline"] = {"kernel": "k_merge_lse", "bound": "hbm", "achieved": round(mbytes / (merge_avg * 1e-3) / 1e9, 1),
+                                  "peak": 8000.0, "unit": "GB/s",
+                                  "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
+                                  "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
     print(json.dumps(line), flush=True)

@@ -47,6 +47,7 @@ class Workload:
     note: str = field(default="", compare=False)
     Hkv: int = 0  # key/value heads (group-query attention); 0 = H
     dtype: str = "bf16"  # element type of q, k, v and the output: "bf16" or "fp16"
+    kv_splits: int = 1  # > 1: the keys run as this many slices with fp32 partial results, then merged
 
     @property
     def ops(self) -> float:
@@ -70,6 +71,9 @@ WORKLOADS = {
                         note="B=2 H=32 over 8 K/V heads, N=8192 d=128 bf16, non-causal, INT8 QK + FP16 PV, LSE"),
     "n8k_fp16": Workload("n8k_fp16", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", dtype="fp16",
                          note="B=2 H=32 N=8192 d=128 fp16 in and out, non-causal, INT8 QK + FP16 PV, LSE"),
+    "n8k_split2": Workload("n8k_split2", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", kv_splits=2,
+                           note="B=2 H=32 N=8192 d=128 bf16, keys in 2 slices of 4096 (each quantized with its own K "
+                                "mean), fp32 partial O + LSE, merged to bf16 O + LSE"),
     "n8k_fmask": Workload("n8k_fmask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys_f32", pv="fp16",
                           note="B=2 H=32 N=8192 d=128 bf16, float32 additive mask [B,1,N,N]: 0 for keys < N/2, "
                                "-inf beyond, LSE"),

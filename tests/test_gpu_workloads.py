@@ -19,10 +19,10 @@ from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_qu
 pytestmark = pytest.mark.gpu
 
 N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048,
-                 "n8k_fp16": 2048, "n8k_fmask": 2048}
+                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024}
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits == 1])
 def test_workload_parity(orc, name):
     w = WORKLOADS[name]
     say(f"workload {name}: {w.note}")
@@ -109,3 +109,54 @@ def test_workload_parity(orc, name):
     excess = np.abs(got_l[sel] - ex_l) - bound
     say(f"  LSE vs exact: worst excess over the quantization bound {excess.max():.3e} (bound max {bound.max():.3e})")
     assert excess.max() <= 1e-4
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits > 1])
+def test_split_workload_parity(orc, name):
+    """Key-sliced workloads as the benchmark runs them: per slice the whole quantized method with
+    fp32 partial results (quantization bit-exact per slice), then the LSE merge; sampled rows
+    against the oracle's merge of its per-slice emulations and against exact attention."""
+    w = WORKLOADS[name]
+    say(f"workload {name}: {w.note}")
+    inp = workload_inputs(w, seed=0)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    q, k, v = to_dev(inp)
+    S = w.kv_splits
+    bounds = [w.Nk * s // S for s in range(S + 1)]
+    o_parts = torch.empty(S, w.B, w.H, w.Nq, w.d, dtype=torch.float32, device=DEV)
+    l_parts = torch.empty(S, w.B, w.H, w.Nq, dtype=torch.float32, device=DEV)
+    rng = np.random.default_rng(0)
+    R = w.B * w.H * w.Nq
+    ends = [bh * w.Nq + i for bh in (0, w.B * w.H - 1) for i in list(range(64)) + list(range(w.Nq - 64, w.Nq))]
+    rows = np.unique(np.concatenate([rng.choice(R, N_RANDOM_ROWS[name], replace=False), np.array(ends)]))
+    rows = rows.astype(np.int64)
+    qe_parts = []
+    for s, (lo, hi) in enumerate(zip(bounds[:-1], bounds[1:])):
+        Ks, Vs = np.ascontiguousarray(Kb[:, :, lo:hi]), np.ascontiguousarray(Vb[:, :, lo:hi])
+        g = sage.quantize_qk(q, k[:, :, lo:hi].contiguous())
+        sage.attn_fwd(g, v[:, :, lo:hi].contiguous(), pv_dtype=w.pv, return_lse=True, out=o_parts[s], lse=l_parts[s])
+        torch.cuda.synchronize()
+        c = orc.quant_qk(Qb, Ks, dtype=inp.dtype)
+        assert np.array_equal(g.k8.cpu().numpy(), c.k8) and np.array_equal(g.q8.cpu().numpy(), c.q8), ("codes", s)
+        assert np.array_equal(g.k_scale.cpu().numpy(), c.ks) and np.array_equal(g.k_mean.cpu().numpy(), c.kmean)
+        vh, vsc = orc.prep_v(Vs, w.pv, dtype=inp.dtype)
+        qe_parts.append(orc.attn_qe(c, vh, vsc, w.pv, w.Nq, hi - lo, BN=sage.block_n(w.pv),
+                                    tau=sage.softmax_tau(w.pv), lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows))
+        say(f"  slice {s}: quantization bit-exact")
+    out, lse = sage.merge_lse(o_parts, l_parts, out_dtype=inp.q.dtype)
+    torch.cuda.synchronize()
+    wo, wl = orc.merge_lse(np.stack([p[0] for p in qe_parts]), np.stack([p[2] for p in qe_parts]))
+    got_o = rows_of(out, rows)
+    got_l = lse_rows(lse, rows)
+    e_qe = rel_l1(got_o, f32_of_bf16_bits(orc.f32_to_bf16(wo.astype(np.float32))))
+    say(f"  rows={rows.size} rel-L1 vs merged emulation {e_qe:.3e}")
+    assert e_qe <= 1e-3
+    assert_lse_close(got_l, wl, 1e-3)
+    ex_rows = rows[:: max(1, rows.size // 256)]
+    ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, rows=ex_rows, dtype=inp.dtype)
+    sel = np.searchsorted(rows, ex_rows)
+    cos = cosine(got_o[sel], ex_o)
+    e_ex = rel_l1(got_o[sel], ex_o)
+    say(f"  vs fp64 exact over all keys: cosine {cos:.6f} rel-L1 {e_ex:.3e}")
+    assert cos >= 0.999 and e_ex <= 3e-2
+    assert np.abs(got_l[sel] - ex_l).max() < 2e-2
