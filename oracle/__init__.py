@@ -19,6 +19,7 @@ or float32, added to the scaled scores):
 * ``attn_ex(...)``                  -- fp64 exact attention on the unquantized inputs
 * ``run_qe(...)``                   -- convenience: all the steps above for given rows
 * ``merge_lse(o_parts, lse_parts)`` -- partial results over disjoint key sets -> the result over their union
+* ``run_qe_varlen`` / ``attn_ex_varlen`` -- packed variable-length batches, one sequence at a time
 """
 
 from __future__ import annotations
@@ -322,4 +323,62 @@ def merge_lse(o_parts, lse_parts):
     out = np.empty((R, d), np.float64)
     lse = np.empty((R,), np.float64)
     lib().orc_merge_lse(_p(o), _p(lp), S, R, d, _p(out), _p(lse))
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# variable-length batches (packed sequences with cumulative lengths)
+# ---------------------------------------------------------------------------------------------
+def _seq_heads(X, lo, hi):
+    """Rows [lo, hi) of a packed [total, H, d] array as one-sequence HND [1, H, n, d]."""
+    return np.ascontiguousarray(np.transpose(X[lo:hi], (1, 0, 2))[None])
+
+
+def run_qe_varlen(Q, K, V, cu_q, cu_k, *, pv="fp16", causal=False, sm_scale=None, BN=64, tau=0.0,
+                  lsum_rounded=False, dtype="bf16", out_dtype=None):
+    """Quantized emulation of packed variable-length batches (the docs digest's ``sageattn_varlen``).
+
+    Q: [total_q, H, d], K and V: [total_k, Hkv, d] (bits of ``dtype``); sequence b holds query rows
+    [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]).  Reading: each sequence is its own
+    attention problem, so the whole method (K mean, 64-token blocks, online softmax, causal mask
+    aligned at the sequence's first query and key) runs on each sequence alone.
+    Returns (o32 [total_q, H, d] fp32, o16 [total_q, H, d] bits, lse [H, total_q] fp32)."""
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    Tq, H, d = Q.shape
+    o32 = np.zeros((Tq, H, d), np.float32)
+    o16 = np.zeros((Tq, H, d), np.uint16)
+    lse = np.full((H, Tq), -np.inf, np.float32)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0:
+            continue
+        if k1 == k0:  # no keys: every row sees nothing
+            continue
+        r = run_qe(_seq_heads(Q, q0, q1), _seq_heads(K, k0, k1), _seq_heads(V, k0, k1), pv=pv, causal=causal,
+                   sm_scale=sm_scale, BN=BN, tau=tau, lsum_rounded=lsum_rounded, dtype=dtype, out_dtype=out_dtype)
+        n = q1 - q0
+        o32[q0:q1] = r.o32.reshape(H, n, d).transpose(1, 0, 2)
+        o16[q0:q1] = r.o16.reshape(H, n, d).transpose(1, 0, 2)
+        lse[:, q0:q1] = r.lse.reshape(H, n)
+    return o32, o16, lse
+
+
+def attn_ex_varlen(Q, K, V, cu_q, cu_k, *, causal=False, sm_scale=None, dtype="bf16"):
+    """fp64 exact attention of packed variable-length batches, one sequence at a time.
+    Returns (out [total_q, H, d] fp64, lse [H, total_q] fp64)."""
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    Tq, H, d = Q.shape
+    out = np.zeros((Tq, H, d), np.float64)
+    lse = np.full((H, Tq), -np.inf, np.float64)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        o, l = attn_ex(_seq_heads(Q, q0, q1), _seq_heads(K, k0, k1), _seq_heads(V, k0, k1), causal=causal,
+                       sm_scale=sm_scale, dtype=dtype)
+        n = q1 - q0
+        out[q0:q1] = o.reshape(H, n, d).transpose(1, 0, 2)
+        lse[:, q0:q1] = l.reshape(H, n)
     return out, lse

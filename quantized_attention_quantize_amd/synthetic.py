@@ -149,3 +149,38 @@ def random_additive_mask(B, Hm, Nq, Nk, p_drop=0.2, scale=2.0, seed=3) -> torch.
     m = scale * torch.randn(B, Hm, Nq, Nk, generator=g, dtype=torch.float32)
     drop = torch.rand(B, Hm, Nq, Nk, generator=g) < p_drop
     return m.masked_fill(drop, float("-inf"))
+
+
+@dataclass
+class VarlenInputs:
+    q: torch.Tensor  # [total_q, H, d] (CPU), packed
+    k: torch.Tensor  # [total_k, Hkv, d]
+    v: torch.Tensor
+    cu_q: torch.Tensor  # int32 [nseq + 1], starts at 0
+    cu_k: torch.Tensor
+
+    def bits(self, t: torch.Tensor) -> np.ndarray:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    @property
+    def dtype(self) -> str:
+        return "fp16" if self.q.dtype == torch.float16 else "bf16"
+
+
+def make_varlen_inputs(seqlens_q, seqlens_k, H, d, sigma=4.0, seed=0, Hkv=0, dtype=torch.bfloat16) -> VarlenInputs:
+    """Packed variable-length batch, as in the docs digest's ``sageattn_varlen`` example: sequence b
+    has seqlens_q[b] query and seqlens_k[b] key rows.  Draws (fp32, one generator): Q = randn(Tq,H,d),
+    Kn = randn(Tk,Hk,d), Kb = sigma * randn(nseq,Hk,d) (each sequence's key-channel offset, added to
+    its rows), V = randn(Tk,Hk,d)."""
+    Hk = Hkv if Hkv > 0 else H
+    Tq, Tk = int(sum(seqlens_q)), int(sum(seqlens_k))
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(Tq, H, d, generator=g, dtype=torch.float32)
+    k = torch.randn(Tk, Hk, d, generator=g, dtype=torch.float32)
+    kb = sigma * torch.randn(len(seqlens_k), Hk, d, generator=g, dtype=torch.float32)
+    v = torch.randn(Tk, Hk, d, generator=g, dtype=torch.float32)
+    cu_q = torch.tensor([0] + list(np.cumsum(seqlens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(seqlens_k)), dtype=torch.int32)
+    for b in range(len(seqlens_k)):
+        k[cu_k[b]:cu_k[b + 1]] += kb[b]
+    return VarlenInputs(q.to(dtype), k.to(dtype), v.to(dtype), cu_q, cu_k)
