@@ -194,6 +194,42 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
                                    int64_t out_stride_n, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Packed variable-length batches (sageattn_varlen section of the SageAttention docs digest:
+ * packed tensors with cumulative sequence lengths, as flash_attn_varlen_func takes them).
+ * Sequence b holds query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of a packed q of total_q rows
+ * and key/value rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of packed k / v of total_k rows;
+ * cu_seqlens_* are device int32 arrays of B+1 nondecreasing entries starting at 0 (the library
+ * reads them only on the device: lengths are clamped to [0, max] and rows to the packed buffers,
+ * so malformed arrays give wrong results but no out-of-bounds access).  Each sequence is its own
+ * attention problem: its own K mean, 64-token blocks from its first token, and causality aligned
+ * at its first query and key.
+ *   q, k, v: descriptors with B = number of sequences, N = the longest sequence (max_seqlen_q for
+ *            q, max_seqlen_k for k and v), H heads, and the strides of one packed row
+ *            (stride_n) and head (stride_h); stride_b is ignored.  Packed [total, H, d] has
+ *            stride_n = H*d, stride_h = d.
+ *   out (quantize): a sage_qk_quant for B sequences of Nq = max_seqlen_q, Nk = max_seqlen_k (the
+ *            dense padded layout; rows past a sequence's end are zero).
+ * Workspace and errors as for sage_quantize_qk; also INVALID_ARGUMENT for null cu_seqlens or a
+ * negative / too large total. */
+sage_status sage_quantize_qk_varlen(const sage_qkv_desc* q, const sage_qkv_desc* k, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
+                                    const sage_qk_quant* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Attention of a packed variable-length batch (V preparation into the workspace included).
+ *   qk: from sage_quantize_qk_varlen with the same cu_seqlens; v as k there.
+ *   out: packed [total_q, H, d] of out_dtype, row stride out_stride_n and head stride
+ *        out_stride_h (elements).
+ *   lse: NULL, or fp32 [H][total_q] (the layout flash_attn_varlen_func uses for its LSE).
+ * No mask.  A sequence without keys gives O = 0 and LSE = -inf for its rows.  Workspace: at least
+ * sage_fwd_workspace_bytes(B, Hkv, max_seqlen_q, max_seqlen_k, d, pv, 0).  Errors as for
+ * sage_attn_fwd. */
+sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k, int causal,
+                                 float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype,
+                                 int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Merge S partial attention results over disjoint key sets into the result over their union
  * (what the LSE output is for: "Utilize SageAttention for Distributed Inference" on the
  * SageAttention docs digest -- sequence parallelism, Ring Attention).  With part s covering the

@@ -18,7 +18,9 @@ from .api import (  # noqa: F401
     pad_tokens,
     prepare_v,
     quantize_qk,
+    quantize_qk_varlen,
     rowsum_rounded,
     sageattn,
+    sageattn_varlen,
     softmax_tau,
 )

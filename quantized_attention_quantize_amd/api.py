@@ -57,7 +57,8 @@ _lib = None
 
 EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_rounded", "sage_quantize_workspace_bytes", "sage_quantize_qk",
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
-           "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_merge_lse",
+           "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_quantize_qk_varlen",
+           "sage_attn_fwd_varlen", "sage_merge_lse",
            "sage_debug_qk_int32", "sage_status_string")
 
 
@@ -100,6 +101,12 @@ def load_library():
     L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I, I64, I64, I64, I64, I, F, P, I, I64, I64,
                                          I64, P, P, SZ, P]
     L.sage_attn_fwd_prepared.restype = I
+    L.sage_quantize_qk_varlen.argtypes = [ctypes.POINTER(QKVDesc), ctypes.POINTER(QKVDesc), P, P, I64, I64,
+                                          ctypes.POINTER(QKQuant), P, SZ, P]
+    L.sage_quantize_qk_varlen.restype = I
+    L.sage_attn_fwd_varlen.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, P, I64, I64, I, F, I, P, I,
+                                       I64, I64, P, P, SZ, P]
+    L.sage_attn_fwd_varlen.restype = I
     L.sage_merge_lse.argtypes = [I64, I64, I64, I64, I64, P, I, P, P, I, I64, I64, I64, P, P]
     L.sage_merge_lse.restype = I
     L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
@@ -411,4 +418,75 @@ def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out: torch.Tens
     _check(L.sage_merge_lse(S, B, H, Nq, d, o_parts.data_ptr(), pdt, lse_parts.data_ptr(), out.data_ptr(), odt,
                             out.stride(0), out.stride(1), out.stride(2), None if lse is None else lse.data_ptr(),
                             _stream(o_parts)), "sage_merge_lse")
+    return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------------------------------------
+# packed variable-length batches
+# ---------------------------------------------------------------------------------------------
+def _packed_desc(t: torch.Tensor, nseq: int, max_seqlen: int) -> QKVDesc:
+    """A packed [total, H, d] tensor as the descriptor of nseq sequences of at most max_seqlen rows."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("packed q/k/v must be [total, H, d] with a contiguous head_dim")
+    return QKVDesc(t.data_ptr(), _dtype_code(t.dtype, "q/k/v"), nseq, t.shape[1], max_seqlen, t.shape[2], 0,
+                   t.stride(1), t.stride(0))
+
+
+def _cu(t: torch.Tensor, what: str) -> torch.Tensor:
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_cuda:
+        raise ValueError(f"{what} must be a 1-D int32 device tensor")
+    return t.contiguous()
+
+
+def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                       max_seqlen_q: int, max_seqlen_k: int) -> QuantizedQK:
+    """Per-sequence K mean and INT8 quantization of packed q [total_q, H, d] and k [total_k, Hkv, d]
+    into the dense padded layout of len(cu_seqlens) - 1 sequences of max_seqlen tokens."""
+    L = load_library()
+    cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    nseq = cq.numel() - 1
+    if ck.numel() != nseq + 1 or nseq < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold nseq + 1 >= 2 entries")
+    dq, dk = _packed_desc(q, nseq, max_seqlen_q), _packed_desc(k, nseq, max_seqlen_k)
+    out = alloc_quantized(nseq, dq.H, max_seqlen_q, max_seqlen_k, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
+    ws = quantize_workspace(nseq, dk.H, max_seqlen_k, dk.d, q.device)
+    qs = out.cstruct()
+    _check(L.sage_quantize_qk_varlen(ctypes.byref(dq), ctypes.byref(dk), cq.data_ptr(), ck.data_ptr(), q.shape[0],
+                                     k.shape[0], ctypes.byref(qs), ws.data_ptr(), ws.numel(), _stream(q)),
+           "sage_quantize_qk_varlen")
+    return out
+
+
+def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
+                    sm_scale: float | None = None, smooth_k: bool = True, return_lse: bool = False,
+                    pv_dtype: str = "fp16"):
+    """Quantized attention of packed variable-length sequences (the docs digest's ``sageattn_varlen``).
+
+    q: [total_q, H, d], k and v: [total_k, Hkv, d] (bf16 or fp16, one dtype); cu_seqlens_*: int32
+    device tensors of nseq + 1 cumulative lengths starting at 0; max_seqlen_*: the longest
+    sequence.  Each sequence is its own attention problem (own K mean; causal aligned at its first
+    query and key).  Returns out [total_q, H, d] (q's dtype) or (out, lse) with lse fp32
+    [H, total_q]."""
+    if not smooth_k:
+        raise ValueError("this library always smooths K (smooth_k=True)")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must have the same dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"the {k.shape[1]} key/value heads do not divide the {q.shape[1]} query heads")
+    L = load_library()
+    qk = quantize_qk_varlen(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    dv = _packed_desc(v, qk.B, max_seqlen_k)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=q.device) if return_lse else None
+    ws = fwd_workspace(qk.B, qk.Hkv, max_seqlen_q, max_seqlen_k, qk.d, pv_dtype, 0, q.device)
+    qs = qk.cstruct()
+    _check(L.sage_attn_fwd_varlen(ctypes.byref(qs), ctypes.byref(dv), cq.data_ptr(), ck.data_ptr(), q.shape[0],
+                                  k.shape[0], 1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+                                  PV_CODES[pv_dtype], out.data_ptr(), _dtype_code(out.dtype, "out"), out.stride(1),
+                                  out.stride(0), None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream(q)), "sage_attn_fwd_varlen")
     return (out, lse) if return_lse else out

@@ -117,6 +117,8 @@ PrepVArgs prep_v_args(const sage_qkv_desc* v, void* vt, float* vscale, float* vm
   a.Nk_pad = sage_pad_tokens(v->N);
   a.nchunk = (int)cdiv(v->N, kChunkTokens);
   a.in_fp16 = v->dtype == SAGE_FP16;
+  a.cu_k = nullptr;
+  a.total_k = 0;
   return a;
 }
 
@@ -140,8 +142,12 @@ size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t
   return align256((size_t)(B * Hkv * cdiv(Nk, kChunkTokens) * d) * sizeof(double));
 }
 
-sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sage_status validate_quantize(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                              const void* workspace, size_t workspace_bytes) {
   sage_status s;
   if ((s = check_desc(q)) != SAGE_OK) return s;
   if ((s = check_desc(k)) != SAGE_OK) return s;
@@ -152,9 +158,12 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!workspace) return SAGE_ERR_WORKSPACE;
   if (workspace_bytes < sage_quantize_workspace_bytes(k->B, k->H, k->N, k->d)) return SAGE_ERR_WORKSPACE;
-  if ((s = check_device()) != SAGE_OK) return s;
+  return check_device();
+}
 
+QuantArgs quant_args(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out) {
   QuantArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = static_cast<const unsigned short*>(q->data);
   a.k = static_cast<const unsigned short*>(k->data);
   a.q_sb = q->stride_b;
@@ -180,10 +189,50 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   a.nbq = (int)cdiv(a.Nq, 64);
   a.nbk = (int)cdiv(a.Nk, 64);
   a.in_fp16 = q->dtype == SAGE_FP16;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+sage_status enqueue_quantize(const QuantArgs& a, void* workspace, hipStream_t st) {
+  sage_status s;
   if ((s = hip_status(launch_kmean(a, static_cast<double*>(workspace), (int)cdiv(a.Nk, kChunkTokens), st))) != SAGE_OK)
     return s;
   return hip_status(launch_quant(a, st));
+}
+
+// Packed variable-length batches: the token counts of the descriptors are the longest sequence,
+// the cumulative lengths live on the device, and totals bound the packed buffers.
+sage_status check_varlen(const int32_t* cu_q, const int32_t* cu_k, int64_t total_q, int64_t total_k) {
+  if (!cu_q || !cu_k) return SAGE_ERR_INVALID_ARGUMENT;
+  if (total_q < 0 || total_k < 0 || total_q > (int64_t(1) << 31) || total_k > (int64_t(1) << 31))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  sage_status s;
+  if ((s = validate_quantize(q, k, out, workspace, workspace_bytes)) != SAGE_OK) return s;
+  return enqueue_quantize(quant_args(q, k, out), workspace, static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_quantize_qk_varlen(const sage_qkv_desc* q, const sage_qkv_desc* k, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
+                                    const sage_qk_quant* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  sage_status s;
+  if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
+  if ((s = validate_quantize(q, k, out, workspace, workspace_bytes)) != SAGE_OK) return s;
+  QuantArgs a = quant_args(q, k, out);
+  a.q_sb = a.k_sb = 0;  // rows are addressed from the cumulative lengths
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return enqueue_quantize(a, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
@@ -221,9 +270,14 @@ sage_status validate_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, const voi
 }
 
 sage_status enqueue_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
-                            hipStream_t st) {
+                            hipStream_t st, const int32_t* cu_k = nullptr, int64_t total_k = 0) {
   const int pv8 = pv == SAGE_PV_FP8_E4M3;
   PrepVArgs pa = prep_v_args(v, v_t, pv8 ? v_scale : nullptr, pv8 ? static_cast<float*>(workspace) : nullptr);
+  if (cu_k) {  // packed variable-length V
+    pa.v_sb = 0;
+    pa.cu_k = cu_k;
+    pa.total_k = total_k;
+  }
   return hip_status(launch_prep_v(pa, pv8, st));
 }
 
@@ -261,10 +315,22 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
                               const void* mask, sage_mask_dtype mask_dtype, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
                               int64_t mask_stride_q, int causal, float sm_scale, void* out, sage_dtype out_dtype,
                               int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
-                              int* mtiles, hipStream_t st) {
+                              int* mtiles, hipStream_t st, const int32_t* cu_q = nullptr,
+                              const int32_t* cu_k = nullptr, int64_t total_q = 0, int64_t total_k = 0) {
   sage_status s;
   AttnArgs a;
   memset(&a, 0, sizeof(a));
+  if (cu_q) {  // packed variable-length batch: output rows and the LSE [H][total_q] follow cu_q
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    a.l_sb = 0;
+    a.l_sh = total_q;
+  } else {  // LSE [B][H][Nq]
+    a.l_sb = qk->H * qk->Nq;
+    a.l_sh = qk->Nq;
+  }
   a.nQT = (int)cdiv(qk->Nq, kTileRows);
   a.nKT = (int)cdiv(qk->Nk, kTileKeys);
   if (mask) {
@@ -384,6 +450,32 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
   return enqueue_attention(qk, v_t, v_scale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h, mask_stride_q,
                            causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            static_cast<int*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k, int causal,
+                                 float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype,
+                                 int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  sage_status s;
+  FwdCommon c;
+  if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
+  if ((s = validate_fwd_common(qk, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
+                               out_stride_n, &c)) != SAGE_OK)
+    return s;
+  if ((s = check_desc(v)) != SAGE_OK) return s;
+  if (v->B != qk->B || v->H != qk->Hkv || v->N != qk->Nk || v->d != qk->d) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!workspace) return SAGE_ERR_WORKSPACE;
+  const FwdLayout L = fwd_layout(qk->B, qk->Hkv, qk->Nq, qk->Nk, qk->d, pv, 0);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGE_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* vscale = pv == SAGE_PV_FP8_E4M3 ? reinterpret_cast<float*>(ws + L.vscale) : nullptr;
+  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st, cu_seqlens_k, total_k)) != SAGE_OK) return s;
+  return enqueue_attention(qk, ws + L.vt, vscale, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
+                           out_dtype, 0, out_stride_h, out_stride_n, lse, nullptr, st, cu_seqlens_q, cu_seqlens_k,
+                           total_q, total_k);
 }
 
 sage_status sage_merge_lse(int64_t S, int64_t B, int64_t H, int64_t Nq, int64_t d, const void* o_parts,

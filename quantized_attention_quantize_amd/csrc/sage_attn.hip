@@ -589,9 +589,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const int q0 = qt * kBlockM;
   const int r0w = q0 + w * 32;  // first row of this wave (token counts are < 2^30)
   const int row = r0w + lr;
-  const int nk = (int)a.Nk, nq = (int)a.Nq;
+  // this batch entry's query and key counts (a packed variable-length batch: its sequence's)
+  const SeqSpan sq = seq_span(a.cu_q, b, a.Nq, a.total_q), sk = seq_span(a.cu_k, b, a.Nk, a.total_k);
+  const int nk = (int)sk.len, nq = (int)sq.len;
+  if (q0 >= nq) return;  // a query tile past the end of a shorter sequence: the whole workgroup leaves
 
-  int kt_end = a.nKT;
+  int kt_end = (nk + kBlockN - 1) / kBlockN;
   if (a.causal) {
     const int lim = (q0 + kBlockM + kBlockN - 1) / kBlockN;
     if (lim < kt_end) kt_end = lim;
@@ -786,7 +789,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   if (row < nq) {
     const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;  // elements
+    const int64_t obase = b * a.o_sb + h * a.o_sh + (sq.off + row) * a.o_sn;  // elements
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -820,7 +823,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
         // l_tot sums 2^(s - pm) over the row (e4m3 P carries the 448 inside pm)
         v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.corr[bh * a.Nq + row];
       }
-      a.lse[bh * a.Nq + row] = v;
+      a.lse[b * a.l_sb + h * a.l_sh + sq.off + row] = v;
     }
   }
 }

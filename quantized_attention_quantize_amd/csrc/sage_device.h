@@ -53,6 +53,21 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   return static_cast<unsigned short>(u >> 16);
 }
 
+// Sequence b of a batch: the row of its first token and its length.  Dense batches (cu null)
+// have n rows per batch entry, addressed through the batch stride.  A packed variable-length batch
+// holds sequence b in rows [cu[b], cu[b+1]) of a buffer of `total` rows; offsets and lengths are
+// clamped to that buffer and to n, so any cu contents keep every access inside it.
+struct SeqSpan {
+  int64_t off, len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int* cu, int64_t b, int64_t n, int64_t total) {
+  if (cu == nullptr) return {0, n};
+  int64_t lo = cu[b], hi = cu[b + 1];
+  lo = lo < 0 ? 0 : (lo > total ? total : lo);
+  hi = hi < lo ? lo : (hi > total ? total : hi);
+  return {lo, hi - lo < n ? hi - lo : n};
+}
+
 // LDS swizzle of 16-byte chunks inside a row.  A fragment read (ds_read_b128) fetches one logical
 // chunk from each of 32 consecutive rows, and LDS serves it 16 lanes (16 rows) at a time.  With
 // 128-byte rows the 16 rows of such a group hit distinct banks iff the even rows land on 8

@@ -27,6 +27,11 @@ struct QuantArgs {
   int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;  // Q has H heads, K has Hkv (Hkv divides H)
   int nbq, nbk;
   int in_fp16;
+  // packed variable-length batch (null: dense): sequence b = rows [cu[b], cu[b+1]) of total rows,
+  // at most Nq (Nk) long; the batch stride is then unused
+  const int* cu_q;
+  const int* cu_k;
+  int64_t total_q, total_k;
 };
 
 struct PrepVArgs {
@@ -38,6 +43,8 @@ struct PrepVArgs {
   int64_t B, H, Nk, d, Nk_pad;
   int nchunk;
   int in_fp16;
+  const int* cu_k;  // packed variable-length batch (null: dense), as in QuantArgs
+  int64_t total_k;
 };
 
 struct MaskTileArgs {
@@ -72,6 +79,12 @@ struct AttnArgs {
   int causal;
   int mask_vec4;  // mask rows aligned to 4 elements: read 4 mask elements at a time
   float sm_scale;
+  // packed variable-length batch (null: dense; Nq / Nk are then the longest sequence): query row
+  // i of sequence b is output row cu_q[b] + i, and its LSE sits at b*l_sb + h*l_sh + cu_q[b] + i
+  const int* cu_q;
+  const int* cu_k;
+  int64_t total_q, total_k;
+  int64_t l_sb, l_sh;
 };
 
 struct MergeArgs {

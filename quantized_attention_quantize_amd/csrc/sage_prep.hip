@@ -31,14 +31,17 @@ constexpr int kPrepThreads = 256;
 // ---------------------------------------------------------------------------------------------
 template <int D, int MODE, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned short* __restrict__ x, int64_t H,
-                                                                 int64_t N, int64_t sb, int64_t sh, int64_t sn,
-                                                                 void* __restrict__ partial, int nchunk) {
+                                                                 int64_t Nmax, int64_t sb, int64_t sh, int64_t sn,
+                                                                 void* __restrict__ partial, int nchunk,
+                                                                 const int* __restrict__ cu, int64_t total) {
   constexpr int CG = D / 8;               // threads per row
   constexpr int RPI = kPrepThreads / CG;  // rows per iteration
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / H, h = bh % H;
+  const SeqSpan sp = seq_span(cu, b, Nmax, total);
+  const int64_t N = sp.len;
   const int64_t t0 = (int64_t)blockIdx.x * kChunk;
-  const unsigned short* base = x + b * sb + h * sh + cg * 8;
+  const unsigned short* base = x + b * sb + h * sh + sp.off * sn + cg * 8;
   double sum[8];
   float mx[8];
 #pragma unroll
@@ -84,15 +87,17 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
   }
 }
 
-// k_mean = fp32(sum_chunks partial / Nk); grid = B*H, block = D.
+// k_mean = fp32(sum_chunks partial / Nk); grid = B*H, block = D.  A sequence without keys gets 0.
 template <int D>
-__global__ __launch_bounds__(D) void k_kmean_final(const double* __restrict__ partial, int nchunk, int64_t N,
+__global__ __launch_bounds__(D) void k_kmean_final(const double* __restrict__ partial, int nchunk, int64_t H,
+                                                   int64_t Nmax, const int* __restrict__ cu, int64_t total,
                                                    float* __restrict__ kmean) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
+  const int64_t N = seq_span(cu, bh / H, Nmax, total).len;
   double s = 0.0;
   for (int i = 0; i < nchunk; ++i) s += partial[(bh * nchunk + i) * D + c];
-  kmean[bh * D + c] = (float)(s / (double)N);
+  kmean[bh * D + c] = N > 0 ? (float)(s / (double)N) : 0.f;
 }
 
 // block-wide max of a non-negative float (256 threads)
@@ -130,26 +135,28 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
   const int64_t b = bh / nh, h = bh % nh;
   const int64_t bhk = isq ? b * a.Hkv + h / (a.H / a.Hkv) : bh;  // head of the K mean
   const int u = isq ? (int)blockIdx.x : (int)blockIdx.x - nqb_pad;
-  const int64_t N = isq ? a.Nq : a.Nk;
+  const SeqSpan sp = isq ? seq_span(a.cu_q, b, a.Nq, a.total_q) : seq_span(a.cu_k, b, a.Nk, a.total_k);
+  const int64_t N = sp.len;  // this sequence's tokens (dense: Nq or Nk)
   const int64_t Npad = isq ? a.Nq_pad : a.Nk_pad;
   int8_t* x8 = (isq ? a.q8 : a.k8) + (bh * Npad + (int64_t)u * kQuantBlock) * D;
   const int64_t r0 = (int64_t)u * kQuantBlock;
 
-  if (r0 >= N) {  // pure pad block
+  if (r0 >= N) {  // pure pad block: zero codes, and a zero scale where the scale array has a slot
 #pragma unroll
     for (int i = 0; i < RPB; ++i) {
       int r = rs + i * RPI;
       *reinterpret_cast<uint2*>(x8 + (int64_t)r * D + cg * 8) = make_uint2(0u, 0u);
     }
+    if (t == 0 && u < (isq ? a.nbq : a.nbk)) (isq ? a.qs : a.ks)[bh * (isq ? a.nbq : a.nbk) + u] = 0.f;
     return;
   }
 
   if (t < D) km_s[t] = a.kmean[bhk * D + t];
   __syncthreads();
 
-  const unsigned short* src =
-      isq ? a.q + b * a.q_sb + h * a.q_sh + cg * 8 : a.k + b * a.k_sb + h * a.k_sh + cg * 8;
   const int64_t sn = isq ? a.q_sn : a.k_sn;
+  const unsigned short* src =
+      (isq ? a.q + b * a.q_sb + h * a.q_sh : a.k + b * a.k_sb + h * a.k_sh) + sp.off * sn + cg * 8;
   float x[RPB][8];
   float amax = 0.f;
 #pragma unroll
@@ -228,11 +235,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t k0 = (int64_t)blockIdx.x * 64;
-  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + cg * 8;
+  const SeqSpan sp = seq_span(a.cu_k, b, a.Nk, a.total_k);
+  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + sp.off * a.v_sn + cg * 8;
   for (int r = rs; r < 64; r += RPI) {
     int64_t tok = k0 + r;
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
+    if (tok < sp.len) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = (_Float16)in_to_f32<IN>(v[j]);  // RNE (exact for fp16)
   }
@@ -275,11 +283,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
     if (blockIdx.x == 0) a.vscale[bh * D + t] = sc;
   }
   __syncthreads();
-  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + cg * 8;
+  const SeqSpan sp = seq_span(a.cu_k, b, a.Nk, a.total_k);
+  const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + sp.off * a.v_sn + cg * 8;
   for (int r = rs; r < 64; r += RPI) {
     int64_t tok = k0 + r;
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (tok < a.Nk) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
+    if (tok < sp.len) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float f = in_to_f32<IN>(v[j]) * inv_s[cg * 8 + j];
@@ -376,8 +385,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
 template <int D, int IN>
 static void launch_kmean_t(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
   dim3 g(nchunk, (unsigned)(a.B * a.Hkv));
-  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk);
-  k_kmean_final<D><<<(unsigned)(a.B * a.Hkv), D, 0, s>>>(partial, nchunk, a.Nk, a.kmean);
+  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk,
+                                                        a.cu_k, a.total_k);
+  k_kmean_final<D><<<(unsigned)(a.B * a.Hkv), D, 0, s>>>(partial, nchunk, a.Hkv, a.Nk, a.cu_k, a.total_k, a.kmean);
 }
 
 hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
@@ -405,7 +415,7 @@ static void launch_prep_v_t(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
   } else {
     dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
     k_colred_partial<D, 1, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
-                                                          a.nchunk);
+                                                          a.nchunk, a.cu_k, a.total_k);
     k_prep_v8<D, IN><<<g, kPrepThreads, 0, s>>>(a);
   }
 }
