@@ -76,6 +76,9 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     from quantized_attention_quantize_amd.synthetic import make_inputs
 
     oracle.build(force=False)
+    if w.seqlens:  # a packed batch: sample whole heads of its first sequence
+        import dataclasses
+        w = dataclasses.replace(w, B=1, Nq=w.seqlens[0], Nk=w.seqlens[0], seqlens=())
     heads = max(1, min(w.B * w.H, math.ceil(work_target / (w.Nq * w.Nk))))
     per_head = max(1, min(w.Nq, int(work_target / (heads * w.Nk))))
     g = w.H // (w.Hkv or w.H)  # query heads per key/value head
@@ -107,6 +110,119 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
                       f"{f' per key slice ({S}), merged' if S > 1 else ''}, "
                       f"quantized emulation of {per_head} evenly spaced query rows per head x {w.Nk} keys; "
                       f"{dt:.2f} s"}
+
+
+def varlen_setup(w, dev):
+    """Packed variable-length workload: buffers allocated once; step = per-sequence K mean and INT8
+    quantization, V preparation, attention (one launch over all sequences)."""
+    import torch
+
+    from quantized_attention_quantize_amd import api
+    from quantized_attention_quantize_amd.synthetic import make_varlen_inputs
+
+    vin = make_varlen_inputs(list(w.seqlens), list(w.seqlens), w.H, w.d, w.sigma, seed=0, Hkv=w.Hkv,
+                             dtype=torch.float16 if w.dtype == "fp16" else torch.bfloat16)
+    q, k, v = vin.q.to(dev), vin.k.to(dev), vin.v.to(dev)
+    cq, ck = vin.cu_q.to(dev), vin.cu_k.to(dev)
+    nseq, mx, Hkv = len(w.seqlens), max(w.seqlens), w.Hkv or w.H
+    qk = api.alloc_quantized(nseq, w.H, mx, mx, w.d, dev, Hkv=Hkv, dtype=q.dtype)
+    qws = api.quantize_workspace(nseq, Hkv, mx, w.d, dev)
+    vt_vs = api.alloc_prepared_v(nseq, Hkv, mx, w.d, w.pv, dev)
+    vws = api.prepare_v_workspace(nseq, Hkv, mx, w.d, w.pv, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.H, q.shape[0], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None, mev=None):
+        api.quantize_qk_varlen(q, k, cq, ck, mx, mx, out=qk, workspace=qws)
+        api.prepare_v_varlen(v, ck, mx, w.pv, out=vt_vs, workspace=vws)
+        if ev is not None:
+            ev[0][0].record(stream)
+        api.attn_fwd_prepared_varlen(qk, vt_vs[0], vt_vs[1], cq, ck, q.shape[0], k.shape[0], pv_dtype=w.pv,
+                                     is_causal=w.causal, return_lse=w.lse, out=out, lse=lse if w.lse else None)
+        if ev is not None:
+            ev[0][1].record(stream)
+
+    return step, 1, out.element_size()
+
+
+def run_timed(args, w, step, S, out_esize, dev):
+    """Warm-up, then exactly args.steps timed steps; prints the JSON line.  step(ev, mev) records
+    HIP events around each of its S attention launches (ev[s]) and around the merge (mev)."""
+    import torch
+
+    import quantized_attention_quantize_amd as sage
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    evs = [[pair() for _ in range(S)] for _ in range(args.steps)]
+    mevs = [pair() for _ in range(args.steps)] if S > 1 else [None] * args.steps
+    g0, g1 = pair()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for i in range(args.steps):
+        step(evs[i], mevs[i])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    gpu_ms_step = g0.elapsed_time(g1) / args.steps
+    attn_ms = sorted(a.elapsed_time(b) for e in evs for a, b in e)  # one entry per attention launch
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    ops = w.ops
+    value = ops / (ms_step * 1e-3) / 1e12
+    achieved = ops / S / (attn_avg * 1e-3) / 1e12  # one launch covers 1/S of the keys
+    traffic = traffic_from_profile(w.name)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+f8" if w.pv == "fp8" else "i8+f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": w.Hkv or w.H, "Nq": w.Nq, "Nk": w.Nk,
+                   "d": w.d,
+                   "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
+                   "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
+                   "gpu_ms_per_step": round(gpu_ms_step, 4),
+                   **({"seqlens": list(w.seqlens)} if w.seqlens else {})},
+        "roofline": {"kernel": "k_attn_fwd", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(mfma_peak(w.pv), 1), "unit": "TOPS", "frac": round(achieved / mfma_peak(w.pv), 4),
+                     "peak_basis": "dense MFMA: INT8 5000 TOPS for QK^T, " +
+                                   ("FP16 2500 TFLOP/s" if w.pv == "fp16" else "FP8 5000 TFLOP/s") +
+                                   " for PV, each half of the counted ops",
+                     "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
+                     "min_ms": round(attn_ms[0], 4)},
+    }
+    if S > 1:
+        merge_ms = sorted(a.elapsed_time(b) for a, b in mevs)
+        merge_avg = sum(merge_ms) / len(merge_ms)
+        R = w.B * w.H * w.Nq
+        mbytes = S * R * w.d * 4 + S * R * 4 + R * w.d * out_esize + (R * 4 if w.lse else 0)
+        line["merge_roofline"] = {"kernel": "k_merge_lse", "bound": "hbm", "achieved": round(mbytes / (merge_avg * 1e-3) / 1e9, 1),
+                                  "peak": 8000.0, "unit": "GB/s",
+                                  "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
+                                  "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
+    print(json.dumps(line), flush=True)
+
+
 
 
 def main():
@@ -149,6 +265,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sage.load_library()
+    if w.seqlens:
+        return run_timed(args, w, *varlen_setup(w, dev), dev)
     inp = workload_inputs(w, seed=0)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     mask = None if inp.mask is None else inp.mask.to(dev)
@@ -198,71 +316,7 @@ def main():
             if mev is not None:
                 mev[1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    def pair():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    evs = [[pair() for _ in range(S)] for _ in range(args.steps)]
-    mevs = [pair() for _ in range(args.steps)] if S > 1 else [None] * args.steps
-    g0, g1 = pair()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g0.record(stream)
-    for i in range(args.steps):
-        step(evs[i], mevs[i])
-    g1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    ms_step = wall * 1e3 / args.steps
-    gpu_ms_step = g0.elapsed_time(g1) / args.steps
-    attn_ms = sorted(a.elapsed_time(b) for e in evs for a, b in e)  # one entry per attention launch
-    attn_avg = sum(attn_ms) / len(attn_ms)
-    ops = w.ops
-    value = ops / (ms_step * 1e-3) / 1e12
-    achieved = ops / S / (attn_avg * 1e-3) / 1e12  # one launch covers 1/S of the keys
-    traffic = traffic_from_profile(w.name)
-
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TOPS",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8+f8" if w.pv == "fp8" else "i8+f16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
-                   "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
-                   "gpu_ms_per_step": round(gpu_ms_step, 4)},
-        "roofline": {"kernel": "k_attn_fwd", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": round(mfma_peak(w.pv), 1), "unit": "TOPS", "frac": round(achieved / mfma_peak(w.pv), 4),
-                     "peak_basis": "dense MFMA: INT8 5000 TOPS for QK^T, " +
-                                   ("FP16 2500 TFLOP/s" if w.pv == "fp16" else "FP8 5000 TFLOP/s") +
-                                   " for PV, each half of the counted ops",
-                     "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
-                     "min_ms": round(attn_ms[0], 4)},
-    }
-    if S > 1:
-        merge_ms = sorted(a.elapsed_time(b) for a, b in mevs)
-        merge_avg = sum(merge_ms) / len(merge_ms)
-        R = w.B * w.H * w.Nq
-        mbytes = S * R * w.d * 4 + S * R * 4 + R * w.d * out.element_size() + (R * 4 if w.lse else 0)
-        line["merge_roofline"] = {"kernel": "k_merge_lse", "bound": "hbm", "achieved": round(mbytes / (merge_avg * 1e-3) / 1e9, 1),
-                                  "peak": 8000.0, "unit": "GB/s",
-                                  "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
-                                  "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
-    print(json.dumps(line), flush=True)
+    return run_timed(args, w, step, S, out.element_size(), dev)
 
 
 if __name__ == "__main__":

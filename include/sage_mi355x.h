@@ -230,6 +230,20 @@ sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v
                                  int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* The two steps of sage_attn_fwd_varlen, for callers that reuse a prepared V: sage_prepare_v of a
+ * packed V (v as for sage_attn_fwd_varlen; v_t / v_scale in the dense padded layout of B
+ * sequences of max_seqlen_k keys, as sage_prepare_v writes for B, Hkv, max_seqlen_k), then the
+ * attention on it.  Workspace of the first: sage_prepare_v_workspace_bytes(B, Hkv, max_seqlen_k, d,
+ * pv); the second needs none.  Errors as for sage_attn_fwd_varlen. */
+sage_status sage_prepare_v_varlen(const sage_qkv_desc* v, const int32_t* cu_seqlens_k, int64_t total_k,
+                                  sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
+                                          sage_pv_dtype pv, const int32_t* cu_seqlens_q,
+                                          const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
+                                          int causal, float sm_scale, void* out, sage_dtype out_dtype,
+                                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* stream);
+
 /* Merge S partial attention results over disjoint key sets into the result over their union
  * (what the LSE output is for: "Utilize SageAttention for Distributed Inference" on the
  * SageAttention docs digest -- sequence parallelism, Ring Attention).  With part s covering the

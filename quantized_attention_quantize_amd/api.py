@@ -58,7 +58,7 @@ _lib = None
 EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_rounded", "sage_quantize_workspace_bytes", "sage_quantize_qk",
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
            "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_quantize_qk_varlen",
-           "sage_attn_fwd_varlen", "sage_merge_lse",
+           "sage_attn_fwd_varlen", "sage_prepare_v_varlen", "sage_attn_fwd_prepared_varlen", "sage_merge_lse",
            "sage_debug_qk_int32", "sage_status_string")
 
 
@@ -107,6 +107,11 @@ def load_library():
     L.sage_attn_fwd_varlen.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, P, I64, I64, I, F, I, P, I,
                                        I64, I64, P, P, SZ, P]
     L.sage_attn_fwd_varlen.restype = I
+    L.sage_prepare_v_varlen.argtypes = [ctypes.POINTER(QKVDesc), P, I64, I, P, P, P, SZ, P]
+    L.sage_prepare_v_varlen.restype = I
+    L.sage_attn_fwd_prepared_varlen.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, P, I64, I64, I, F, P, I, I64, I64,
+                                                P, P]
+    L.sage_attn_fwd_prepared_varlen.restype = I
     L.sage_merge_lse.argtypes = [I64, I64, I64, I64, I64, P, I, P, P, I, I64, I64, I64, P, P]
     L.sage_merge_lse.restype = I
     L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
@@ -439,7 +444,8 @@ def _cu(t: torch.Tensor, what: str) -> torch.Tensor:
 
 
 def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
-                       max_seqlen_q: int, max_seqlen_k: int) -> QuantizedQK:
+                       max_seqlen_q: int, max_seqlen_k: int, out: QuantizedQK | None = None,
+                       workspace: torch.Tensor | None = None) -> QuantizedQK:
     """Per-sequence K mean and INT8 quantization of packed q [total_q, H, d] and k [total_k, Hkv, d]
     into the dense padded layout of len(cu_seqlens) - 1 sequences of max_seqlen tokens."""
     L = load_library()
@@ -448,8 +454,10 @@ def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Ten
     if ck.numel() != nseq + 1 or nseq < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold nseq + 1 >= 2 entries")
     dq, dk = _packed_desc(q, nseq, max_seqlen_q), _packed_desc(k, nseq, max_seqlen_k)
-    out = alloc_quantized(nseq, dq.H, max_seqlen_q, max_seqlen_k, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
-    ws = quantize_workspace(nseq, dk.H, max_seqlen_k, dk.d, q.device)
+    if out is None:
+        out = alloc_quantized(nseq, dq.H, max_seqlen_q, max_seqlen_k, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
+    out.dtype = q.dtype
+    ws = quantize_workspace(nseq, dk.H, max_seqlen_k, dk.d, q.device) if workspace is None else workspace
     qs = out.cstruct()
     _check(L.sage_quantize_qk_varlen(ctypes.byref(dq), ctypes.byref(dk), cq.data_ptr(), ck.data_ptr(), q.shape[0],
                                      k.shape[0], ctypes.byref(qs), ws.data_ptr(), ws.numel(), _stream(q)),
@@ -489,4 +497,45 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
                                   PV_CODES[pv_dtype], out.data_ptr(), _dtype_code(out.dtype, "out"), out.stride(1),
                                   out.stride(0), None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(),
                                   _stream(q)), "sage_attn_fwd_varlen")
+    return (out, lse) if return_lse else out
+
+
+def prepare_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, pv_dtype: str = "fp16",
+                     out=None, workspace: torch.Tensor | None = None):
+    """V preparation of a packed [total_k, Hkv, d] V into the dense padded layout: (v_t, v_scale)."""
+    L = load_library()
+    ck = _cu(cu_seqlens_k, "cu_seqlens_k")
+    nseq = ck.numel() - 1
+    dv = _packed_desc(v, nseq, max_seqlen_k)
+    vt, vs = alloc_prepared_v(nseq, dv.H, max_seqlen_k, dv.d, pv_dtype, v.device) if out is None else out
+    if workspace is None:
+        workspace = prepare_v_workspace(nseq, dv.H, max_seqlen_k, dv.d, pv_dtype, v.device)
+    _check(L.sage_prepare_v_varlen(ctypes.byref(dv), ck.data_ptr(), v.shape[0], PV_CODES[pv_dtype], vt.data_ptr(),
+                                   None if vs is None else vs.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream(v)), "sage_prepare_v_varlen")
+    return vt, vs
+
+
+def attn_fwd_prepared_varlen(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor | None,
+                             cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int, *,
+                             pv_dtype: str = "fp16", is_causal: bool = False, sm_scale: float | None = None,
+                             return_lse: bool = False, out: torch.Tensor | None = None,
+                             lse: torch.Tensor | None = None):
+    """Attention of a packed variable-length batch on pre-quantized Q/K and prepared V.  Returns out
+    [total_q, H, d] or (out, lse [H, total_q])."""
+    L = load_library()
+    cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
+    dev = qk.q8.device
+    if out is None:
+        out = torch.empty(total_q, qk.H, qk.d, dtype=qk.dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty(qk.H, total_q, dtype=torch.float32, device=dev)
+    qs = qk.cstruct()
+    _check(L.sage_attn_fwd_prepared_varlen(ctypes.byref(qs), v_t.data_ptr(),
+                                           None if v_scale is None else v_scale.data_ptr(), PV_CODES[pv_dtype],
+                                           cq.data_ptr(), ck.data_ptr(), total_q, total_k, 1 if is_causal else 0,
+                                           0.0 if sm_scale is None else float(sm_scale), out.data_ptr(),
+                                           _dtype_code(out.dtype, "out", allow_f32=True), out.stride(1),
+                                           out.stride(0), None if lse is None else lse.data_ptr(), _stream(out)),
+           "sage_attn_fwd_prepared_varlen")
     return (out, lse) if return_lse else out

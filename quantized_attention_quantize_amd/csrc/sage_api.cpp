@@ -478,6 +478,35 @@ sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v
                            total_q, total_k);
 }
 
+sage_status sage_prepare_v_varlen(const sage_qkv_desc* v, const int32_t* cu_seqlens_k, int64_t total_k,
+                                  sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  sage_status s;
+  if ((s = check_varlen(cu_seqlens_k, cu_seqlens_k, 0, total_k)) != SAGE_OK) return s;
+  if ((s = validate_prepare(v, pv, v_t, v_scale, workspace, workspace_bytes)) != SAGE_OK) return s;
+  if ((s = check_device()) != SAGE_OK) return s;
+  return enqueue_prepare(v, pv, v_t, v_scale, workspace, static_cast<hipStream_t>(stream), cu_seqlens_k, total_k);
+}
+
+sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
+                                          sage_pv_dtype pv, const int32_t* cu_seqlens_q,
+                                          const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
+                                          int causal, float sm_scale, void* out, sage_dtype out_dtype,
+                                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* stream) {
+  sage_status s;
+  FwdCommon c;
+  if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
+  if ((s = validate_fwd_common(qk, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
+                               out_stride_n, &c)) != SAGE_OK)
+    return s;
+  if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_device()) != SAGE_OK) return s;
+  return enqueue_attention(qk, v_t, v_scale, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
+                           out_dtype, 0, out_stride_h, out_stride_n, lse, nullptr, static_cast<hipStream_t>(stream),
+                           cu_seqlens_q, cu_seqlens_k, total_q, total_k);
+}
+
 sage_status sage_merge_lse(int64_t S, int64_t B, int64_t H, int64_t Nq, int64_t d, const void* o_parts,
                            sage_dtype part_dtype, const float* lse_parts, void* out, sage_dtype out_dtype,
                            int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,

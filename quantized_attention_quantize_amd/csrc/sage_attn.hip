@@ -578,12 +578,29 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
 
-  // workgroup -> (head, q-tile); consecutive logical ids land on the same XCD
+  // workgroup -> (head, q-tile).  Workgroup ids go round-robin over the 8 XCDs (each with its own
+  // L2).  When the key/value heads split evenly, XCD x works through key/value heads x, x+8, ...,
+  // each with all its query heads and q-tiles in a row, so K and V stay in one L2 and heads of
+  // unequal cost (sequences of a packed batch) spread evenly.  Otherwise consecutive logical ids
+  // land on the same XCD.
   const int total = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, jx = bid >> 3, per = total >> 3, rem = total & 7;
-  const int L = xcd < rem ? xcd * (per + 1) + jx : rem * (per + 1) + (xcd - rem) * per + jx;
-  const int64_t bh = L / a.nQT;
-  int qt = L % a.nQT;
+  const int xcd = bid & 7, jx = bid >> 3;
+  const int grp = (int)(a.H / a.Hkv);  // query heads per key/value head
+  const int64_t units = a.B * a.Hkv;
+  int64_t bh;
+  int qt;
+  if (units % 8 == 0 && (int64_t)total == units * grp * a.nQT) {
+    const int per_unit = grp * a.nQT;
+    const int64_t u = xcd + 8 * (int64_t)(jx / per_unit);  // b * Hkv + key/value head
+    const int r = jx % per_unit;
+    bh = (u / a.Hkv) * a.H + (u % a.Hkv) * grp + r / a.nQT;
+    qt = r % a.nQT;
+  } else {
+    const int per = total >> 3, rem = total & 7;
+    const int L = xcd < rem ? xcd * (per + 1) + jx : rem * (per + 1) + (xcd - rem) * per + jx;
+    bh = L / a.nQT;
+    qt = L % a.nQT;
+  }
   if (a.causal) qt = a.nQT - 1 - qt;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int q0 = qt * kBlockM;

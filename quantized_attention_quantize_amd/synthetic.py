@@ -48,11 +48,16 @@ class Workload:
     Hkv: int = 0  # key/value heads (group-query attention); 0 = H
     dtype: str = "bf16"  # element type of q, k, v and the output: "bf16" or "fp16"
     kv_splits: int = 1  # > 1: the keys run as this many slices with fp32 partial results, then merged
+    seqlens: tuple = ()  # a packed variable-length batch of these sequence lengths (B, Nq, Nk: count, longest)
 
     @property
     def ops(self) -> float:
-        """Throughput numerator 4*B*H*Nq*Nk*d, halved for causal."""
-        o = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        """Throughput numerator 4*B*H*Nq*Nk*d (summed over the sequences of a packed batch), halved
+        for causal."""
+        if self.seqlens:
+            o = 4.0 * self.H * self.d * float(sum(n * n for n in self.seqlens))
+        else:
+            o = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
         return o / 2 if self.causal else o
 
 
@@ -74,6 +79,10 @@ WORKLOADS = {
     "n8k_split2": Workload("n8k_split2", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", kv_splits=2,
                            note="B=2 H=32 N=8192 d=128 bf16, keys in 2 slices of 4096 (each quantized with its own K "
                                 "mean), fp32 partial O + LSE, merged to bf16 O + LSE"),
+    "varlen_mix": Workload("varlen_mix", 8, 32, 8192, 8192, 128, 4.0, pv="fp16", dtype="fp16",
+                           seqlens=(8192, 4096, 2048, 6144, 1024, 3072, 512, 7680),
+                           note="packed batch of 8 sequences (8192, 4096, 2048, 6144, 1024, 3072, 512, 7680 tokens; "
+                                "32768 in all), H=32 d=128 fp16, non-causal, INT8 QK + FP16 PV, LSE"),
     "n8k_fmask": Workload("n8k_fmask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys_f32", pv="fp16",
                           note="B=2 H=32 N=8192 d=128 bf16, float32 additive mask [B,1,N,N]: 0 for keys < N/2, "
                                "-inf beyond, LSE"),

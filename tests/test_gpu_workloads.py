@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import quantized_attention_quantize_amd as sage
-from quantized_attention_quantize_amd.synthetic import WORKLOADS, workload_inputs
+from quantized_attention_quantize_amd.synthetic import WORKLOADS, make_varlen_inputs, workload_inputs
 
 from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_quant_bound, lse_rows, rel_l1, rows_of,
                          say, to_dev, unpermute_vt)
@@ -22,7 +22,7 @@ N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048
                  "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024}
 
 
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits == 1])
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits == 1 and not w.seqlens])
 def test_workload_parity(orc, name):
     w = WORKLOADS[name]
     say(f"workload {name}: {w.note}")
@@ -160,3 +160,58 @@ def test_split_workload_parity(orc, name):
     say(f"  vs fp64 exact over all keys: cosine {cos:.6f} rel-L1 {e_ex:.3e}")
     assert cos >= 0.999 and e_ex <= 3e-2
     assert np.abs(got_l[sel] - ex_l).max() < 2e-2
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.seqlens])
+def test_varlen_workload_parity(orc, name):
+    """Packed variable-length workloads as the benchmark runs them: every sequence's quantization
+    bit-exact against the dense oracle on that sequence; O and LSE on sampled rows of every
+    sequence against the oracle's emulation of that sequence, and against exact attention."""
+    w = WORKLOADS[name]
+    say(f"workload {name}: {w.note}")
+    vin = make_varlen_inputs(list(w.seqlens), list(w.seqlens), w.H, w.d, w.sigma, seed=0, Hkv=w.Hkv,
+                             dtype=torch.float16 if w.dtype == "fp16" else torch.bfloat16)
+    q, k, v = vin.q.to(DEV), vin.k.to(DEV), vin.v.to(DEV)
+    cq, ck = vin.cu_q.to(DEV), vin.cu_k.to(DEV)
+    mx = max(w.seqlens)
+    g = sage.quantize_qk_varlen(q, k, cq, ck, mx, mx)
+    out, lse = sage.sageattn_varlen(q, k, v, cq, ck, mx, mx, is_causal=w.causal, return_lse=True, pv_dtype=w.pv)
+    torch.cuda.synchronize()
+    Q, K, V = vin.bits(vin.q), vin.bits(vin.k), vin.bits(vin.v)
+    cu = vin.cu_q.tolist()
+    H, d = w.H, w.d
+    got_all = []
+    want_all = []
+    rng = np.random.default_rng(0)
+    for b, n in enumerate(w.seqlens):
+        lo = cu[b]
+        Qs = np.ascontiguousarray(Q[lo:lo + n].transpose(1, 0, 2)[None])
+        Ks = np.ascontiguousarray(K[lo:lo + n].transpose(1, 0, 2)[None])
+        Vs = np.ascontiguousarray(V[lo:lo + n].transpose(1, 0, 2)[None])
+        c = orc.quant_qk(Qs, Ks, dtype=vin.dtype)
+        npad = c.q8.shape[2]
+        assert np.array_equal(g.q8[b, :, :npad].cpu().numpy(), c.q8[0]), ("q8", b)
+        assert np.array_equal(g.k8[b, :, :npad].cpu().numpy(), c.k8[0]), ("k8", b)
+        assert np.array_equal(g.k_mean[b].cpu().numpy(), c.kmean[0]), ("k_mean", b)
+        assert np.array_equal(g.q_scale[b, :, :c.qs.shape[2]].cpu().numpy(), c.qs[0])
+        vh, vsc = orc.prep_v(Vs, w.pv, dtype=vin.dtype)
+        rows = np.unique(np.concatenate([rng.choice(H * n, 96, replace=False), [0, n - 1, H * n - 1]]))
+        rows = rows.astype(np.int64)
+        o32, o16, ql = orc.attn_qe(c, vh, vsc, w.pv, n, n, causal=w.causal, BN=sage.block_n(w.pv),
+                                   tau=sage.softmax_tau(w.pv), lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows,
+                                   out_dtype=vin.dtype)
+        hh, ii = rows // n, rows % n
+        got = out[torch.from_numpy(lo + ii).to(DEV), torch.from_numpy(hh).to(DEV)].float().cpu().numpy()
+        gl = lse[torch.from_numpy(hh).to(DEV), torch.from_numpy(lo + ii).to(DEV)].cpu().numpy()
+        want = o16.view(np.float16).astype(np.float32) if vin.dtype == "fp16" else \
+            (o16.astype(np.uint32) << 16).view(np.float32)
+        assert_lse_close(gl, ql, 1e-3)
+        got_all.append(got)
+        want_all.append(want)
+        if b < 2:  # exact attention on a few rows of the first sequences
+            eo, el = orc.attn_ex(Qs, Ks, Vs, causal=w.causal, rows=rows[:16], dtype=vin.dtype)
+            assert cosine(got[:16], eo) >= 0.999 and rel_l1(got[:16], eo) <= 3e-2
+    say(f"  every sequence's quantization bit-exact")
+    e_qe = rel_l1(np.concatenate(got_all), np.concatenate(want_all))
+    say(f"  rel-L1 vs per-sequence emulation {e_qe:.3e}")
+    assert e_qe <= 1e-3
