@@ -69,11 +69,11 @@ def lib():
             getattr(L, name).restype = None
         L.orc_kmean.argtypes = [P, i32, I, I, I, I, P]
         L.orc_quant_qk.argtypes = [P, P, i32, P, I, I, I, I, I, I, I, I, P, P, P, P, P]
-        L.orc_prep_v_fp16.argtypes = [P, i32, I, I, I, I, P]
+        L.orc_prep_v_fp16.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_prep_v_fp8.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
-        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32, P,
-                                  I, P, i32, P, P]
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32,
+                                  P, I, P, i32, P, P]
         L.orc_attn_ex.argtypes = [P, P, P, i32, P, i32, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
         L.orc_merge_lse.argtypes = [P, P, I, I, I, P, P]
         for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
@@ -195,15 +195,19 @@ def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None, dtype="bf16") -> QuantQK:
     return QuantQK(q8, k8, qs, ks, km, corr)
 
 
-def prep_v(V, pv: str = "fp16", dtype="bf16"):
+def prep_v(V, pv: str = "fp16", dtype="bf16", vmean=None):
     """V of ``dtype``.  Returns (vhat, vs): fp16 bits uint16 [B,H,Nk,d] and None, or e4m3 uint8
-    [B,H,Nk,d] and fp32 [B,H,d]."""
+    [B,H,Nk,d] and fp32 [B,H,d].  vmean (fp32 [B,H,d], FP16 PV only): smooth_v, V - vmean is
+    prepared instead of V."""
     V = _c(V, np.uint16)
     B, H, Nk, d = V.shape
     if pv == "fp16":
         out = np.empty(V.shape, np.uint16)
-        lib().orc_prep_v_fp16(_p(V), _in_fp16(dtype), B, H, Nk, d, _p(out))
+        vm = None if vmean is None else _c(vmean, np.float32)
+        lib().orc_prep_v_fp16(_p(V), _in_fp16(dtype), B, H, Nk, d, _p(vm), _p(out))
         return out, None
+    if vmean is not None:
+        raise ValueError("smooth_v is defined for FP16 PV only")
     if pv == "fp8":
         out = np.empty(V.shape, np.uint8)
         vs = np.empty((B, H, d), np.float32)
@@ -239,12 +243,13 @@ def _mask_arg(mask, B, H, Nq, Nk):
 
 
 def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_scale=None, BN=64, tau=0.0,
-            lsum_rounded=False, rows=None, out_dtype="bf16"):
+            lsum_rounded=False, rows=None, out_dtype="bf16", vmean=None):
     """Quantized emulation.  Returns (o32 [R,d] fp32, o16 [R,d] bits of out_dtype, lse [R] fp32).
 
     BN: keys per online-softmax tile; tau: the reference maximum is raised only when a tile's
     maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.
-    lsum_rounded: the denominator sums P as rounded for the PV product instead of the fp32 p."""
+    lsum_rounded: the denominator sums P as rounded for the PV product instead of the fp32 p.
+    vmean: smooth_v's V mean [B,Hkv,d] (vhat then holds V - vmean), added back to the output."""
     B, H, Nq_pad, d = qk.q8.shape
     Hkv, Nk_pad = qk.k8.shape[1], qk.k8.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
@@ -259,8 +264,9 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     o32 = np.empty((R, d), np.float32)
     o16 = np.empty((R, d), np.uint16)
     lse = np.empty((R,), np.float32)
+    vm = None if vmean is None else _c(vmean, np.float32)
     lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
-                      _p(vs), 1 if pv == "fp8" else 0, _p(m), mf, mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d,
+                      _p(vs), _p(vm), 1 if pv == "fp8" else 0, _p(m), mf, mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d,
                       Nq_pad, Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32),
                       _in_fp16(out_dtype), _p(o16), _p(lse))
     return o32, o16, lse
@@ -300,14 +306,16 @@ class QEResult:
 
 
 def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, tau=0.0, lsum_rounded=False,
-           rows=None, dtype="bf16", out_dtype=None) -> QEResult:
+           rows=None, dtype="bf16", out_dtype=None, smooth_v=False) -> QEResult:
     """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe.  The output dtype
-    defaults to the input dtype."""
+    defaults to the input dtype.  smooth_v: V's token mean (taken as K's) is subtracted before the
+    FP16 rounding of V and added back to the output."""
     qk = quant_qk(Q, K, dtype=dtype)
-    vhat, vs = prep_v(V, pv, dtype=dtype)
+    vmean = kmean(V, dtype) if smooth_v else None
+    vhat, vs = prep_v(V, pv, dtype=dtype, vmean=vmean)
     Nq, Nk = Q.shape[2], K.shape[2]
     o32, o16, lse = attn_qe(qk, vhat, vs, pv, Nq, Nk, causal=causal, mask=mask, sm_scale=sm_scale, BN=BN, tau=tau,
-                            lsum_rounded=lsum_rounded, rows=rows, out_dtype=out_dtype or dtype)
+                            lsum_rounded=lsum_rounded, rows=rows, out_dtype=out_dtype or dtype, vmean=vmean)
     return QEResult(qk, vhat, vs, o32, o16, lse)
 
 

@@ -40,6 +40,10 @@
  *    is then at most 2^tau.  The normalized result does not depend on tau; only where P is
  *    rounded does;
  *  - a row with no valid key gives O = 0 and LSE = -inf;
+ *  - smooth_v (FP16 PV only, as the pages tie it to the FP16 kernel): V's per-channel token mean is
+ *    taken exactly like K's (fp64 sum over all Nk tokens, one rounding to fp32), V - mean is
+ *    rounded once to fp32 and then to fp16, and the mean is added back to the normalized output
+ *    of every row that has a visible key (exact, since the probabilities sum to one);
  *  - LSE is natural-log and adds back the smoothing shift sm_scale * (q_i . kmean), so it is the
  *    LSE of the unsmoothed scores.
  *
@@ -276,14 +280,20 @@ void orc_quant_qk(const uint16_t* Q, const uint16_t* K, int in_fp16, const float
 /* ------------------------------------------------------------------------------------------ */
 /* Step 3: V preparation.  Output keeps V's own layout [B][H][Nk][d].                         */
 /* V is bf16 or fp16 (in_fp16).                                                               */
-/* fp16: vhat = fp16_rne(V) (the identity for fp16 V).                                        */
+/* fp16: vhat = fp16_rne(V) (the identity for fp16 V); with smooth_v (vmean != NULL, from      */
+/*       orc_kmean of V) vhat = fp16_rne(fp32(V - vmean)).                                    */
 /* fp8:  vmax_c = max_t |V_tc|; vs_c = fp32(vmax_c / 448); vinv_c = fp32(448 / vmax_c)        */
 /*       (0 when vmax_c = 0); vhat = e4m3_rne_sat(fp32(V * vinv_c)).                          */
 /* ------------------------------------------------------------------------------------------ */
-void orc_prep_v_fp16(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, uint16_t* vhat) {
+void orc_prep_v_fp16(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d,
+                     const float* vmean, uint16_t* vhat) {
   int64_t n = B * H * Nk * d;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) vhat[i] = orc_f32_to_f16(orc_in_to_f32(V[i], in_fp16));
+  for (int64_t i = 0; i < n; ++i) {
+    float x = orc_in_to_f32(V[i], in_fp16);
+    if (vmean) x = x - vmean[(i / (Nk * d)) * d + i % d]; /* one fp32 rounding */
+    vhat[i] = orc_f32_to_f16(x);
+  }
 }
 
 void orc_prep_v_fp8(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, uint8_t* vhat, float* vs) {
@@ -336,13 +346,15 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /*       (natural-log units), -inf = drop.                                                     */
 /* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
 /* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
+/* vmean: smooth_v's per-channel V mean [B][Hkv][d], added back to the output, or NULL.        */
 /* BN: keys per online-softmax tile; tau: lazy-maximum threshold in log2 units (0 = exact).    */
 /* lsum_rounded: 0 = l sums the fp32 p, 1 = l sums P as rounded for PV.                       */
 /* Outputs per requested row: o32 [nrows][d] (fp32 O before the output rounding, may be NULL),*/
 /* o16 [nrows][d] (bf16 bits, or fp16 bits if out_fp16), lse [nrows] (natural log, fp32).     */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
-                 const void* vhat, const float* vs, int pv_fp8, const void* mask, int mask_f32, int64_t mask_h,
+                 const void* vhat, const float* vs, const float* vmean, int pv_fp8, const void* mask, int mask_f32,
+                 int64_t mask_h,
                  int causal,
                  float sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad,
                  int64_t Nk_pad, int64_t BN, double tau, int lsum_rounded, const int64_t* rows, int64_t nrows,
@@ -425,6 +437,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           out = (float)((double)o[c] * (double)vs[bhk * d + c] / (448.0 * (double)l));
         else
           out = o[c] / l;
+        if (vmean && l != 0.0f) out = out + vmean[bhk * d + c]; /* smooth_v: add the mean back */
         if (o32) o32[r * d + c] = out;
         if (o16) o16[r * d + c] = out_fp16 ? orc_f32_to_f16(out) : orc_f32_to_bf16(out);
       }
