@@ -126,12 +126,17 @@ size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace sage_prepare_v needs (fp8: per-chunk partial maxima of |V|; fp16: 0). Host only. */
+/* Bytes of workspace sage_prepare_v needs: per-chunk partial maxima of |V| (fp8) or fp64 partial
+ * sums of V (FP16 with smooth_v); an FP16 call without smooth_v needs none.  Host only. */
 size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv);
 
 /* Step 2a (V preparation).  v bf16 or fp16 [B,H,Nk,d].
  *   SAGE_PV_FP16:     v_t = fp16 (round to nearest even) of V, 2-byte elements [B][H][d][Nk_pad];
- *                     v_scale is not used (may be NULL).
+ *                     v_scale is not used (may be NULL).  With v_mean non-NULL (smooth_v: the
+ *                     sm80 INT8/FP16 kernel section's option for biased value tensors), v_mean fp32
+ *                     [B][H][d] receives V's per-channel token mean (fp64 sum over the Nk tokens,
+ *                     one rounding, as the K mean) and v_t holds fp16(fp32(V - v_mean)); the
+ *                     attention adds v_mean back (pass it to sage_attn_fwd_prepared).
  *   SAGE_PV_FP8_E4M3: v_scale fp32 [B][H][d] = max_t |V[t,c]| / 448 (0 for an all-zero channel),
  *                     v_t = e4m3 (round to nearest even, saturating at +-448) of
  *                     V * (448 / max_t |V[t,c]|), bytes [B][H][d][Nk_pad].
@@ -139,17 +144,18 @@ size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t 
  * FlashInfer API doc.)  Key order inside v_t is the order the PV MFMA consumes: fp16 stores each
  * group of 16 keys as [0-3, 8-11, 4-7, 12-15]; e4m3 stores key kb*32 + w of each group of 64 at
  * position ((w/4)%2)*32 + kb*16 + (w/8)*4 + w%4.  Pad keys (>= Nk) are zero.
- * Errors: INVALID_ARGUMENT (descriptor, null/misaligned v_t, fp8 without v_scale), UNSUPPORTED,
- * WORKSPACE (fp8 and workspace below sage_prepare_v_workspace_bytes), HIP. */
-sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
-                           size_t workspace_bytes, void* stream);
+ * Errors: INVALID_ARGUMENT (descriptor, null/misaligned v_t, fp8 without v_scale), UNSUPPORTED (also
+ * v_mean with SAGE_PV_FP8_E4M3), WORKSPACE (fp8 or smooth_v with a workspace below
+ * sage_prepare_v_workspace_bytes), HIP. */
+sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, float* v_mean,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace the mask tile classification needs (0 when mask_h == 0).  Host only.
  * mask_h: 0 = no mask, 1 = mask broadcast over heads, H = one mask per head. */
 size_t sage_mask_workspace_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h);
 
-/* Bytes of workspace sage_attn_fwd needs: prepared V, the fp8 V scales, sage_prepare_v's scratch
- * and the mask tile classification.  Hkv = heads of V.  Host only. */
+/* Bytes of workspace sage_attn_fwd needs: prepared V, the fp8 V scales or the smooth_v V mean,
+ * sage_prepare_v's scratch and the mask tile classification.  Hkv = heads of V.  Host only. */
 size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv,
                                 int64_t mask_h);
 
@@ -162,6 +168,8 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  *         semantics: Triton INT8/FP16 kernel examples section, where False entries are masked out.)
  *   causal: key j is visible to query i only if j <= i (top-left aligned).
  *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
+ *   smooth_v: nonzero subtracts V's per-channel token mean before the FP16 rounding of V and adds
+ *        it back to O (see sage_prepare_v); SAGE_PV_FP16 only, else UNSUPPORTED.
  *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 or SAGE_FP16, rounded to nearest even, or SAGE_F32)
  *        addressed with out_stride_{b,h,n} (every row 16-byte aligned).
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled, unsmoothed
@@ -179,15 +187,17 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
 sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const void* mask,
                           sage_mask_dtype mask_dtype, int64_t mask_h,
                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
-                          float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
-                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                          float sm_scale, sage_pv_dtype pv, int smooth_v, void* out, sage_dtype out_dtype,
+                          int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /* Step 2b (attention on prepared V): mask tile classification (if a mask is given) and the
- * attention kernel.  v_t / v_scale as written by sage_prepare_v for the same B, Hkv, Nk, d and pv.
+ * attention kernel.  v_t / v_scale / v_mean as written by sage_prepare_v for the same B, Hkv, Nk, d
+ * and pv (v_mean NULL unless V was prepared with it).
  * workspace: at least sage_mask_workspace_bytes(B, Nq, Nk, mask_h) bytes (may be NULL without a
  * mask).  Other arguments and errors as for sage_attn_fwd. */
-sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
+                                   const float* v_mean, sage_pv_dtype pv,
                                    const void* mask, sage_mask_dtype mask_dtype, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
                                    int64_t mask_stride_q, int causal, float sm_scale, void* out,
                                    sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
@@ -226,7 +236,7 @@ sage_status sage_quantize_qk_varlen(const sage_qkv_desc* q, const sage_qkv_desc*
  * sage_attn_fwd. */
 sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k, int causal,
-                                 float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype,
+                                 float sm_scale, sage_pv_dtype pv, int smooth_v, void* out, sage_dtype out_dtype,
                                  int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
@@ -236,10 +246,10 @@ sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v
  * attention on it.  Workspace of the first: sage_prepare_v_workspace_bytes(B, Hkv, max_seqlen_k, d,
  * pv); the second needs none.  Errors as for sage_attn_fwd_varlen. */
 sage_status sage_prepare_v_varlen(const sage_qkv_desc* v, const int32_t* cu_seqlens_k, int64_t total_k,
-                                  sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                                  sage_pv_dtype pv, void* v_t, float* v_scale, float* v_mean, void* workspace,
                                   size_t workspace_bytes, void* stream);
 sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
-                                          sage_pv_dtype pv, const int32_t* cu_seqlens_q,
+                                          const float* v_mean, sage_pv_dtype pv, const int32_t* cu_seqlens_q,
                                           const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
                                           int causal, float sm_scale, void* out, sage_dtype out_dtype,
                                           int64_t out_stride_h, int64_t out_stride_n, float* lse, void* stream);

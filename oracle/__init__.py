@@ -343,7 +343,7 @@ def _seq_heads(X, lo, hi):
 
 
 def run_qe_varlen(Q, K, V, cu_q, cu_k, *, pv="fp16", causal=False, sm_scale=None, BN=64, tau=0.0,
-                  lsum_rounded=False, dtype="bf16", out_dtype=None):
+                  lsum_rounded=False, dtype="bf16", out_dtype=None, smooth_v=False):
     """Quantized emulation of packed variable-length batches (the docs digest's ``sageattn_varlen``).
 
     Q: [total_q, H, d], K and V: [total_k, Hkv, d] (bits of ``dtype``); sequence b holds query rows
@@ -364,7 +364,8 @@ def run_qe_varlen(Q, K, V, cu_q, cu_k, *, pv="fp16", causal=False, sm_scale=None
         if k1 == k0:  # no keys: every row sees nothing
             continue
         r = run_qe(_seq_heads(Q, q0, q1), _seq_heads(K, k0, k1), _seq_heads(V, k0, k1), pv=pv, causal=causal,
-                   sm_scale=sm_scale, BN=BN, tau=tau, lsum_rounded=lsum_rounded, dtype=dtype, out_dtype=out_dtype)
+                   sm_scale=sm_scale, BN=BN, tau=tau, lsum_rounded=lsum_rounded, dtype=dtype, out_dtype=out_dtype,
+                   smooth_v=smooth_v)
         n = q1 - q0
         o32[q0:q1] = r.o32.reshape(H, n, d).transpose(1, 0, 2)
         o16[q0:q1] = r.o16.reshape(H, n, d).transpose(1, 0, 2)

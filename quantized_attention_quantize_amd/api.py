@@ -89,28 +89,30 @@ def load_library():
     L.sage_quantize_qk.restype = I
     L.sage_prepare_v_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     L.sage_prepare_v_workspace_bytes.restype = SZ
-    L.sage_prepare_v.argtypes = [ctypes.POINTER(QKVDesc), I, P, P, P, SZ, P]
+    L.sage_prepare_v.argtypes = [ctypes.POINTER(QKVDesc), I, P, P, P, P, SZ, P]
     L.sage_prepare_v.restype = I
     L.sage_mask_workspace_bytes.argtypes = [I64, I64, I64, I64]
     L.sage_mask_workspace_bytes.restype = SZ
     L.sage_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I, I64]
     L.sage_fwd_workspace_bytes.restype = SZ
-    L.sage_attn_fwd.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, I, I64, I64, I64, I64, I, F, I, P, I,
+    L.sage_attn_fwd.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, I, I64, I64, I64, I64, I, F, I, I,
+                                P, I,
                                 I64, I64, I64, P, P, SZ, P]
     L.sage_attn_fwd.restype = I
-    L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, I, I64, I64, I64, I64, I, F, P, I, I64, I64,
+    L.sage_attn_fwd_prepared.argtypes = [ctypes.POINTER(QKQuant), P, P, P, I, P, I, I64, I64, I64, I64, I, F, P, I, I64,
+                                         I64,
                                          I64, P, P, SZ, P]
     L.sage_attn_fwd_prepared.restype = I
     L.sage_quantize_qk_varlen.argtypes = [ctypes.POINTER(QKVDesc), ctypes.POINTER(QKVDesc), P, P, I64, I64,
                                           ctypes.POINTER(QKQuant), P, SZ, P]
     L.sage_quantize_qk_varlen.restype = I
-    L.sage_attn_fwd_varlen.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, P, I64, I64, I, F, I, P, I,
-                                       I64, I64, P, P, SZ, P]
+    L.sage_attn_fwd_varlen.argtypes = [ctypes.POINTER(QKQuant), ctypes.POINTER(QKVDesc), P, P, I64, I64, I, F, I, I, P,
+                                       I, I64, I64, P, P, SZ, P]
     L.sage_attn_fwd_varlen.restype = I
-    L.sage_prepare_v_varlen.argtypes = [ctypes.POINTER(QKVDesc), P, I64, I, P, P, P, SZ, P]
+    L.sage_prepare_v_varlen.argtypes = [ctypes.POINTER(QKVDesc), P, I64, I, P, P, P, P, SZ, P]
     L.sage_prepare_v_varlen.restype = I
-    L.sage_attn_fwd_prepared_varlen.argtypes = [ctypes.POINTER(QKQuant), P, P, I, P, P, I64, I64, I, F, P, I, I64, I64,
-                                                P, P]
+    L.sage_attn_fwd_prepared_varlen.argtypes = [ctypes.POINTER(QKQuant), P, P, P, I, P, P, I64, I64, I, F, P, I, I64,
+                                                I64, P, P]
     L.sage_attn_fwd_prepared_varlen.restype = I
     L.sage_merge_lse.argtypes = [I64, I64, I64, I64, I64, P, I, P, P, I, I64, I64, I64, P, P]
     L.sage_merge_lse.restype = I
@@ -265,9 +267,10 @@ def _mask_args(attn_mask, B, H, Nq, Nk):
 def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is_causal: bool = False,
              attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, pv_dtype: str = "fp16",
              return_lse: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-             workspace: torch.Tensor | None = None):
+             workspace: torch.Tensor | None = None, smooth_v: bool = False):
     """Attention on pre-quantized Q/K (from quantize_qk) with bf16 or fp16 V.  Returns out or (out, lse);
-    out defaults to V's dtype."""
+    out defaults to V's dtype.  smooth_v: V's channel means are subtracted before its FP16 rounding
+    and added back to O (FP16 PV only)."""
     L = load_library()
     dv = _desc(v, tensor_layout)
     B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
@@ -288,14 +291,14 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
     _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mcode, mh, msb,
                            msh, msq,
                            1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale), PV_CODES[pv_dtype],
-                           out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
+                           1 if smooth_v else 0, out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                            workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_attn_fwd")
     return (out, lse) if return_lse else out
 
 
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
              attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, return_lse: bool = False,
-             pv_dtype: str = "fp16"):
+             pv_dtype: str = "fp16", smooth_v: bool = False):
     """Quantized attention forward: INT8 Q/K with K smoothing, FP16 (or FP8 e4m3) PV.
 
     q: bf16 or fp16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}; k, v: the same
@@ -318,7 +321,7 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
         raise ValueError(f"the {hk} key/value heads do not divide the {hq} query heads")
     qk = quantize_qk(q, k, tensor_layout)
     return attn_fwd(qk, v, tensor_layout=tensor_layout, is_causal=is_causal, attn_mask=attn_mask, sm_scale=sm_scale,
-                    pv_dtype=pv_dtype, return_lse=return_lse)
+                    pv_dtype=pv_dtype, return_lse=return_lse, smooth_v=smooth_v)
 
 
 def debug_qk_int32(qk: QuantizedQK, b: int, h: int, row0: int, nrows: int, col0: int, ncols: int) -> torch.Tensor:
@@ -346,15 +349,18 @@ def prepare_v_workspace(B, H, Nk, d, pv_dtype, device) -> torch.Tensor:
 
 
 def prepare_v(v: torch.Tensor, pv_dtype: str = "fp16", tensor_layout: str = "HND", out=None,
-              workspace: torch.Tensor | None = None):
-    """V preparation: returns (v_t, v_scale); see sage_prepare_v for the storage order."""
+              workspace: torch.Tensor | None = None, v_mean: torch.Tensor | None = None):
+    """V preparation: returns (v_t, v_scale); see sage_prepare_v for the storage order.  v_mean
+    (fp32 [B, H, d], FP16 PV only): smooth_v -- the channel means are written there and
+    subtracted; pass the same tensor to attn_fwd_prepared."""
     L = load_library()
     dv = _desc(v, tensor_layout)
     vt, vs = alloc_prepared_v(dv.B, dv.H, dv.N, dv.d, pv_dtype, v.device) if out is None else out
     if workspace is None:
         workspace = prepare_v_workspace(dv.B, dv.H, dv.N, dv.d, pv_dtype, v.device)
     _check(L.sage_prepare_v(ctypes.byref(dv), PV_CODES[pv_dtype], vt.data_ptr(), None if vs is None else vs.data_ptr(),
-                            workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_prepare_v")
+                            None if v_mean is None else v_mean.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                            _stream(v)), "sage_prepare_v")
     return vt, vs
 
 
@@ -366,9 +372,10 @@ def mask_workspace(B, Nq, Nk, mask_h, device) -> torch.Tensor:
 def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor | None, *, pv_dtype: str = "fp16",
                       tensor_layout: str = "HND", is_causal: bool = False, attn_mask: torch.Tensor | None = None,
                       sm_scale: float | None = None, return_lse: bool = False, out: torch.Tensor | None = None,
-                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Attention on pre-quantized Q/K and prepared V (from prepare_v).  Returns out or (out, lse);
-    out defaults to the dtype Q and K had."""
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      v_mean: torch.Tensor | None = None):
+    """Attention on pre-quantized Q/K and prepared V (from prepare_v; v_mean as given to it for
+    smooth_v).  Returns out or (out, lse); out defaults to the dtype Q and K had."""
     L = load_library()
     B, H, Nq, Nk, d = qk.B, qk.H, qk.Nq, qk.Nk, qk.d
     dev = qk.q8.device
@@ -387,7 +394,7 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
     qs = qk.cstruct()
     odt = _dtype_code(out.dtype, "out", allow_f32=True)
     _check(L.sage_attn_fwd_prepared(ctypes.byref(qs), v_t.data_ptr(), None if v_scale is None else v_scale.data_ptr(),
-                                    PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mcode, mh, msb, msh, msq,
+                                    None if v_mean is None else v_mean.data_ptr(), PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mcode, mh, msb, msh, msq,
                                     1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
                                     out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                                     None if workspace is None else workspace.data_ptr(),
@@ -468,7 +475,7 @@ def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Ten
 def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
                     sm_scale: float | None = None, smooth_k: bool = True, return_lse: bool = False,
-                    pv_dtype: str = "fp16"):
+                    pv_dtype: str = "fp16", smooth_v: bool = False):
     """Quantized attention of packed variable-length sequences (the docs digest's ``sageattn_varlen``).
 
     q: [total_q, H, d], k and v: [total_k, Hkv, d] (bf16 or fp16, one dtype); cu_seqlens_*: int32
@@ -494,14 +501,14 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     qs = qk.cstruct()
     _check(L.sage_attn_fwd_varlen(ctypes.byref(qs), ctypes.byref(dv), cq.data_ptr(), ck.data_ptr(), q.shape[0],
                                   k.shape[0], 1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
-                                  PV_CODES[pv_dtype], out.data_ptr(), _dtype_code(out.dtype, "out"), out.stride(1),
+                                  PV_CODES[pv_dtype], 1 if smooth_v else 0, out.data_ptr(), _dtype_code(out.dtype, "out"), out.stride(1),
                                   out.stride(0), None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(),
                                   _stream(q)), "sage_attn_fwd_varlen")
     return (out, lse) if return_lse else out
 
 
 def prepare_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, pv_dtype: str = "fp16",
-                     out=None, workspace: torch.Tensor | None = None):
+                     out=None, workspace: torch.Tensor | None = None, v_mean: torch.Tensor | None = None):
     """V preparation of a packed [total_k, Hkv, d] V into the dense padded layout: (v_t, v_scale)."""
     L = load_library()
     ck = _cu(cu_seqlens_k, "cu_seqlens_k")
@@ -511,7 +518,8 @@ def prepare_v_varlen(v: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: 
     if workspace is None:
         workspace = prepare_v_workspace(nseq, dv.H, max_seqlen_k, dv.d, pv_dtype, v.device)
     _check(L.sage_prepare_v_varlen(ctypes.byref(dv), ck.data_ptr(), v.shape[0], PV_CODES[pv_dtype], vt.data_ptr(),
-                                   None if vs is None else vs.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   None if vs is None else vs.data_ptr(),
+                                   None if v_mean is None else v_mean.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                    _stream(v)), "sage_prepare_v_varlen")
     return vt, vs
 
@@ -520,7 +528,7 @@ def attn_fwd_prepared_varlen(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.
                              cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int, *,
                              pv_dtype: str = "fp16", is_causal: bool = False, sm_scale: float | None = None,
                              return_lse: bool = False, out: torch.Tensor | None = None,
-                             lse: torch.Tensor | None = None):
+                             lse: torch.Tensor | None = None, v_mean: torch.Tensor | None = None):
     """Attention of a packed variable-length batch on pre-quantized Q/K and prepared V.  Returns out
     [total_q, H, d] or (out, lse [H, total_q])."""
     L = load_library()
@@ -532,7 +540,8 @@ def attn_fwd_prepared_varlen(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.
         lse = torch.empty(qk.H, total_q, dtype=torch.float32, device=dev)
     qs = qk.cstruct()
     _check(L.sage_attn_fwd_prepared_varlen(ctypes.byref(qs), v_t.data_ptr(),
-                                           None if v_scale is None else v_scale.data_ptr(), PV_CODES[pv_dtype],
+                                           None if v_scale is None else v_scale.data_ptr(),
+                                           None if v_mean is None else v_mean.data_ptr(), PV_CODES[pv_dtype],
                                            cq.data_ptr(), ck.data_ptr(), total_q, total_k, 1 if is_causal else 0,
                                            0.0 if sm_scale is None else float(sm_scale), out.data_ptr(),
                                            _dtype_code(out.dtype, "out", allow_f32=True), out.stride(1),

@@ -74,16 +74,17 @@ sage_status hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_E
 size_t vt_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
   return (size_t)(B * H * d * sage_pad_tokens(Nk)) * (pv == SAGE_PV_FP16 ? 2 : 1);
 }
-size_t prep_ws_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv) {
-  return pv == SAGE_PV_FP8_E4M3 ? align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * 4) : 0;
+// sage_prepare_v scratch: per-chunk partial maxima of |V| (fp8) or fp64 partial sums (smooth_v)
+size_t prep_ws_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype) {
+  return align256((size_t)(B * H * cdiv(Nk, kChunkTokens) * d) * sizeof(double));
 }
 size_t mask_ws_bytes(int64_t B, int64_t Nq, int64_t Nk, int64_t mask_h) {
   return mask_h > 0 ? align256((size_t)(B * mask_h * cdiv(Nq, kTileRows) * cdiv(Nk, kTileKeys)) * sizeof(int)) : 0;
 }
 
-// sage_attn_fwd workspace: [prepared V | fp8 V scale | prepare-V scratch | mask tile states]
+// sage_attn_fwd workspace: [prepared V | fp8 V scale | smooth_v V mean | prepare-V scratch | mask tile states]
 struct FwdLayout {
-  size_t vt, vscale, prep, mtiles, total;
+  size_t vt, vscale, vmean, prep, mtiles, total;
 };
 
 FwdLayout fwd_layout(int64_t B, int64_t Hv, int64_t Nq, int64_t Nk, int64_t d, sage_pv_dtype pv, int64_t mask_h) {
@@ -93,6 +94,8 @@ FwdLayout fwd_layout(int64_t B, int64_t Hv, int64_t Nq, int64_t Nk, int64_t d, s
   off += align256(vt_bytes(B, Hv, Nk, d, pv));
   L.vscale = off;
   if (pv == SAGE_PV_FP8_E4M3) off += align256((size_t)(B * Hv * d) * 4);
+  L.vmean = off;
+  off += align256((size_t)(B * Hv * d) * 4);
   L.prep = off;
   off += prep_ws_bytes(B, Hv, Nk, d, pv);
   L.mtiles = off;
@@ -258,21 +261,25 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
 namespace {
 
 sage_status validate_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, const void* v_t, const float* v_scale,
-                             const void* workspace, size_t workspace_bytes) {
+                             const float* v_mean, const void* workspace, size_t workspace_bytes) {
   sage_status s;
   if ((s = check_desc(v)) != SAGE_OK) return s;
   if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
+  if (v_mean && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;  // smooth_v belongs to the FP16 PV path
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
-  const size_t need = prep_ws_bytes(v->B, v->H, v->N, v->d, pv);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_ERR_WORKSPACE;
+  if (pv == SAGE_PV_FP8_E4M3 || v_mean) {
+    if (!workspace || workspace_bytes < prep_ws_bytes(v->B, v->H, v->N, v->d, pv)) return SAGE_ERR_WORKSPACE;
+  }
   return SAGE_OK;
 }
 
-sage_status enqueue_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
-                            hipStream_t st, const int32_t* cu_k = nullptr, int64_t total_k = 0) {
+sage_status enqueue_prepare(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, float* v_mean,
+                            void* workspace, hipStream_t st, const int32_t* cu_k = nullptr, int64_t total_k = 0) {
   const int pv8 = pv == SAGE_PV_FP8_E4M3;
   PrepVArgs pa = prep_v_args(v, v_t, pv8 ? v_scale : nullptr, pv8 ? static_cast<float*>(workspace) : nullptr);
+  pa.vmean = pv8 ? nullptr : v_mean;
+  pa.vsum_partial = pa.vmean ? static_cast<double*>(workspace) : nullptr;
   if (cu_k) {  // packed variable-length V
     pa.v_sb = 0;
     pa.cu_k = cu_k;
@@ -311,7 +318,8 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
 }
 
 // Mask classification (if any) and the attention kernel, on already prepared V.
-sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const float* v_scale, const float* v_mean,
+                              sage_pv_dtype pv,
                               const void* mask, sage_mask_dtype mask_dtype, int64_t mh, int64_t mask_stride_b, int64_t mask_stride_h,
                               int64_t mask_stride_q, int causal, float sm_scale, void* out, sage_dtype out_dtype,
                               int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
@@ -373,6 +381,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   a.corr = qk->lse_corr;
   a.vt = v_t;
   a.vscale = pv == SAGE_PV_FP8_E4M3 ? v_scale : nullptr;
+  a.vmean = pv == SAGE_PV_FP8_E4M3 ? nullptr : v_mean;
   a.out = out;
   a.out_kind = out_dtype == SAGE_F32 ? 2 : (out_dtype == SAGE_FP16 ? 1 : 0);
   a.o_sb = out_stride_b;
@@ -397,22 +406,23 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
 
 extern "C" {
 
-sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+sage_status sage_prepare_v(const sage_qkv_desc* v, sage_pv_dtype pv, void* v_t, float* v_scale, float* v_mean,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   sage_status s;
-  if ((s = validate_prepare(v, pv, v_t, v_scale, workspace, workspace_bytes)) != SAGE_OK) return s;
+  if ((s = validate_prepare(v, pv, v_t, v_scale, v_mean, workspace, workspace_bytes)) != SAGE_OK) return s;
   if ((s = check_device()) != SAGE_OK) return s;
-  return enqueue_prepare(v, pv, v_t, v_scale, workspace, static_cast<hipStream_t>(stream));
+  return enqueue_prepare(v, pv, v_t, v_scale, v_mean, workspace, static_cast<hipStream_t>(stream));
 }
 
 sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const void* mask,
                           sage_mask_dtype mask_dtype, int64_t mask_h,
                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, int causal,
-                          float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype, int64_t out_stride_b,
-                          int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
+                          float sm_scale, sage_pv_dtype pv, int smooth_v, void* out, sage_dtype out_dtype,
+                          int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   sage_status s;
   FwdCommon c;
+  if (smooth_v && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
   if ((s = validate_fwd_common(qk, pv, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
                                out_dtype, out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
@@ -425,13 +435,15 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* vscale = pv == SAGE_PV_FP8_E4M3 ? reinterpret_cast<float*>(ws + L.vscale) : nullptr;
-  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st)) != SAGE_OK) return s;
-  return enqueue_attention(qk, ws + L.vt, vscale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h,
+  float* vmean = smooth_v ? reinterpret_cast<float*>(ws + L.vmean) : nullptr;
+  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, vmean, ws + L.prep, st)) != SAGE_OK) return s;
+  return enqueue_attention(qk, ws + L.vt, vscale, vmean, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h,
                            mask_stride_q, causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            reinterpret_cast<int*>(ws + L.mtiles), st);
 }
 
-sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale, sage_pv_dtype pv,
+sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
+                                   const float* v_mean, sage_pv_dtype pv,
                                    const void* mask, sage_mask_dtype mask_dtype, int64_t mask_h, int64_t mask_stride_b, int64_t mask_stride_h,
                                    int64_t mask_stride_q, int causal, float sm_scale, void* out,
                                    sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
@@ -444,21 +456,23 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
     return s;
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  if (v_mean && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
   const size_t need = mask_ws_bytes(qk->B, qk->Nq, qk->Nk, c.mh);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_ERR_WORKSPACE;
   if ((s = check_device()) != SAGE_OK) return s;
-  return enqueue_attention(qk, v_t, v_scale, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h, mask_stride_q,
+  return enqueue_attention(qk, v_t, v_scale, v_mean, pv, mask, mask_dtype, c.mh, mask_stride_b, mask_stride_h, mask_stride_q,
                            causal, sm_scale, out, out_dtype, out_stride_b, out_stride_h, out_stride_n, lse,
                            static_cast<int*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k, int causal,
-                                 float sm_scale, sage_pv_dtype pv, void* out, sage_dtype out_dtype,
+                                 float sm_scale, sage_pv_dtype pv, int smooth_v, void* out, sage_dtype out_dtype,
                                  int64_t out_stride_h, int64_t out_stride_n, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   sage_status s;
   FwdCommon c;
+  if (smooth_v && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
   if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
   if ((s = validate_fwd_common(qk, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
                                out_stride_n, &c)) != SAGE_OK)
@@ -472,24 +486,27 @@ sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* vscale = pv == SAGE_PV_FP8_E4M3 ? reinterpret_cast<float*>(ws + L.vscale) : nullptr;
-  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, ws + L.prep, st, cu_seqlens_k, total_k)) != SAGE_OK) return s;
-  return enqueue_attention(qk, ws + L.vt, vscale, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
+  float* vmean = smooth_v ? reinterpret_cast<float*>(ws + L.vmean) : nullptr;
+  if ((s = enqueue_prepare(v, pv, ws + L.vt, vscale, vmean, ws + L.prep, st, cu_seqlens_k, total_k)) != SAGE_OK)
+    return s;
+  return enqueue_attention(qk, ws + L.vt, vscale, vmean, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
                            out_dtype, 0, out_stride_h, out_stride_n, lse, nullptr, st, cu_seqlens_q, cu_seqlens_k,
                            total_q, total_k);
 }
 
 sage_status sage_prepare_v_varlen(const sage_qkv_desc* v, const int32_t* cu_seqlens_k, int64_t total_k,
-                                  sage_pv_dtype pv, void* v_t, float* v_scale, void* workspace,
+                                  sage_pv_dtype pv, void* v_t, float* v_scale, float* v_mean, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   sage_status s;
   if ((s = check_varlen(cu_seqlens_k, cu_seqlens_k, 0, total_k)) != SAGE_OK) return s;
-  if ((s = validate_prepare(v, pv, v_t, v_scale, workspace, workspace_bytes)) != SAGE_OK) return s;
+  if ((s = validate_prepare(v, pv, v_t, v_scale, v_mean, workspace, workspace_bytes)) != SAGE_OK) return s;
   if ((s = check_device()) != SAGE_OK) return s;
-  return enqueue_prepare(v, pv, v_t, v_scale, workspace, static_cast<hipStream_t>(stream), cu_seqlens_k, total_k);
+  return enqueue_prepare(v, pv, v_t, v_scale, v_mean, workspace, static_cast<hipStream_t>(stream), cu_seqlens_k,
+                         total_k);
 }
 
 sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v_t, const float* v_scale,
-                                          sage_pv_dtype pv, const int32_t* cu_seqlens_q,
+                                          const float* v_mean, sage_pv_dtype pv, const int32_t* cu_seqlens_q,
                                           const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
                                           int causal, float sm_scale, void* out, sage_dtype out_dtype,
                                           int64_t out_stride_h, int64_t out_stride_n, float* lse, void* stream) {
@@ -501,8 +518,9 @@ sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v
     return s;
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv == SAGE_PV_FP8_E4M3 && !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  if (v_mean && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
   if ((s = check_device()) != SAGE_OK) return s;
-  return enqueue_attention(qk, v_t, v_scale, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
+  return enqueue_attention(qk, v_t, v_scale, v_mean, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, causal, sm_scale, out,
                            out_dtype, 0, out_stride_h, out_stride_n, lse, nullptr, static_cast<hipStream_t>(stream),
                            cu_seqlens_q, cu_seqlens_k, total_q, total_k);
 }

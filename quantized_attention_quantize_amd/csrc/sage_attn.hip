@@ -806,6 +806,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   if (row < nq) {
     const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float* vmh = (a.vmean && l_tot > 0.f) ? a.vmean + bhk * D : nullptr;  // smooth_v
     const int64_t obase = b * a.o_sb + h * a.o_sh + (sq.off + row) * a.o_sn;  // elements
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -819,6 +820,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
             f[e] = o[db][rq * 4 + e] * (vsh[d0 + e] * inv);
           else
             f[e] = o[db][rq * 4 + e] * inv;
+          if (vmh) f[e] = f[e] + vmh[d0 + e];
         }
         if (a.out_kind == 2) {  // fp32, e.g. partial results that are merged later
           *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);

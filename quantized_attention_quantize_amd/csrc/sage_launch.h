@@ -40,6 +40,8 @@ struct PrepVArgs {
   void* vt;             // fp16 or e4m3 [B][H][d][Nk_pad]
   float* vscale;        // fp8 only: [B][H][d]
   float* vmax_partial;  // fp8 only: [B][H][nchunk][d]
+  float* vmean;         // fp16 only, smooth_v: [B][H][d] written here and subtracted (null: off)
+  double* vsum_partial;  // smooth_v: [B][H][nchunk][d] fp64 partial sums
   int64_t B, H, Nk, d, Nk_pad;
   int nchunk;
   int in_fp16;
@@ -65,6 +67,7 @@ struct AttnArgs {
   const float* corr;
   const void* vt;  // prepared V
   const float* vscale;
+  const float* vmean;  // smooth_v: [B][Hkv][d] added back to O (null: off)
   const void* mask;  // element mask (only read for mixed tiles); strides in elements
   int64_t m_sb, m_sh, m_sq;
   int mask_f32;       // 0: uint8, nonzero = attend; 1: fp32 added to the scaled score, -inf = drop

@@ -5,8 +5,8 @@
 //   k_kmean_final     k_mean[b,h,c] = fp32(sum over chunks / Nk)
 //   k_quant_qk        per-64-token-block INT8 quantization of Q and of the smoothed K, their
 //                     scales, and the LSE shift sum_c Q[i,c]*k_mean[c]
-//   k_prep_v16        V -> fp16 (round to nearest even), transposed to [d][Nk_pad] in the key
-//                     order the PV MFMA consumes
+//   k_prep_v16        V (or, with smooth_v, fp32(V - mean)) -> fp16 (round to nearest even),
+//                     transposed to [d][Nk_pad] in the key order the PV MFMA consumes
 //   k_prep_v8         V -> e4m3 with per-channel scale 448/max|V|, transposed likewise
 //   k_mask_tiles      classifies each (256-row x 64-key) tile of a boolean or fp32 additive mask
 //                     as all-masked, all-visible (fp32: all exactly 0) or mixed, so the attention
@@ -232,17 +232,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPI = kPrepThreads / CG;
   __shared__ _Float16 tile[64][D + 8];  // +8 halves of padding against bank conflicts
+  __shared__ float vm[D];
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t k0 = (int64_t)blockIdx.x * 64;
   const SeqSpan sp = seq_span(a.cu_k, b, a.Nk, a.total_k);
+  if (t < D) vm[t] = a.vmean ? a.vmean[bh * D + t] : 0.f;  // smooth_v: the channel means
+  __syncthreads();
   const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + sp.off * a.v_sn + cg * 8;
   for (int r = rs; r < 64; r += RPI) {
     int64_t tok = k0 + r;
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
     if (tok < sp.len) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = (_Float16)in_to_f32<IN>(v[j]);  // RNE (exact for fp16)
+    for (int j = 0; j < 8; ++j) {
+      float x = in_to_f32<IN>(v[j]);
+      if (a.vmean) x = x - vm[cg * 8 + j];  // one fp32 rounding
+      tile[r][cg * 8 + j] = tok < sp.len ? (_Float16)x : (_Float16)0.f;  // RNE (exact for fp16 V); pad keys 0
+    }
   }
   __syncthreads();
   // D rows x 8 chunks of 8 halves; chunk q holds positions [8q, 8q+8)
@@ -411,6 +418,13 @@ template <int D, int IN>
 static void launch_prep_v_t(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
   dim3 g((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.H));
   if (!pv_fp8) {
+    if (a.vmean) {  // smooth_v: V's channel means first, exactly as K's
+      dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
+      k_colred_partial<D, 0, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vsum_partial,
+                                                            a.nchunk, a.cu_k, a.total_k);
+      k_kmean_final<D><<<(unsigned)(a.B * a.H), D, 0, s>>>(a.vsum_partial, a.nchunk, a.H, a.Nk, a.cu_k, a.total_k,
+                                                          a.vmean);
+    }
     k_prep_v16<D, IN><<<g, kPrepThreads, 0, s>>>(a);
   } else {
     dim3 gr(a.nchunk, (unsigned)(a.B * a.H));

@@ -48,7 +48,8 @@ def test_host_queries(L):
     assert L.sage_quantize_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_quantize_workspace_bytes(0, 1, 1, 64) == 0
     # prepared fp16 V of the 8192-token, 64-head workload
-    assert L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 0) == 2 * 32 * 128 * 8192 * 2
+    # prepared V, the smooth_v V mean and the fp64 partial sums (one per 256-token chunk)
+    assert L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 0) == 2 * 32 * 128 * (8192 * 2 + 4 + 32 * 8)
     base8 = L.sage_fwd_workspace_bytes(1, 24, 17776, 17776, 128, 1, 0)
     assert base8 >= 24 * 128 * 17792 + 24 * 128 * 4
     with_mask = L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 1)
@@ -134,15 +135,16 @@ def test_quantize_validation(L, case, status):
     assert call_quant(L, q, k, out, ws, wsb) == status
 
 
-def call_fwd(L, qk, v, mask=None, mdt=0, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30):
+def call_fwd(L, qk, v, mask=None, mdt=0, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30,
+             smooth_v=0):
     return L.sage_attn_fwd(ctypes.byref(qk) if qk else None, ctypes.byref(v) if v else None, mask, mdt, mask_h, 0, 0,
-                           msq, 0, 0.0, pv, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
+                           msq, 0, 0.0, pv, smooth_v, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
 
 
 @pytest.mark.parametrize("case,status", [
     ("null_qk", INVALID), ("v_shape", INVALID), ("pv_bad", UNSUPPORTED), ("out_null", INVALID),
     ("out_bad_dtype", INVALID), ("out_misaligned", INVALID), ("mask_dtype_bad", INVALID),
-    ("mask_f32_misaligned", INVALID), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
+    ("mask_f32_misaligned", INVALID), ("smooth_v_fp8", UNSUPPORTED), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
     ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED), ("gqa_v_heads", INVALID),
     ("gqa_hkv_zero", INVALID),
 ])
@@ -163,6 +165,8 @@ def test_attn_validation(L, case, status):
         kw.update(mask=FAKE, mdt=5, mask_h=1)
     elif case == "mask_f32_misaligned":  # an fp32 mask must be 4-byte aligned
         kw.update(mask=FAKE + 2, mdt=1, mask_h=1)
+    elif case == "smooth_v_fp8":  # smooth_v belongs to the FP16 PV path
+        kw.update(pv=1, smooth_v=1)
     elif case == "out_misaligned":
         kw["out"] = FAKE + 8
     elif case == "mask_h_bad":
@@ -190,24 +194,26 @@ def test_debug_validation(L):
     assert L.sage_debug_qk_int32(ctypes.byref(qk), 0, 0, 200, 100, 0, 10, out, None) == INVALID  # past Nq_pad
     assert L.sage_debug_qk_int32(ctypes.byref(qk), 0, 0, 0, 10, -1, 10, out, None) == INVALID
     v = desc()
-    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, None, FAKE, 1 << 20, None) == INVALID  # fp8 needs v_scale
-    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, FAKE, 10, None) == WORKSPACE
-    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, 0, 1 << 20, None) == WORKSPACE
-    assert L.sage_prepare_v(ctypes.byref(v), 3, FAKE, None, FAKE, 1 << 20, None) == UNSUPPORTED
-    assert L.sage_prepare_v(ctypes.byref(v), 0, FAKE + 4, None, None, 0, None) == INVALID  # misaligned v_t
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, None, None, FAKE, 1 << 20, None) == INVALID  # fp8 needs v_scale
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, None, FAKE, 10, None) == WORKSPACE
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, None, 0, 1 << 20, None) == WORKSPACE
+    assert L.sage_prepare_v(ctypes.byref(v), 3, FAKE, None, None, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert L.sage_prepare_v(ctypes.byref(v), 0, FAKE + 4, None, None, None, 0, None) == INVALID  # misaligned v_t
+    assert L.sage_prepare_v(ctypes.byref(v), 1, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == UNSUPPORTED  # fp8 + smooth_v
+    assert L.sage_prepare_v(ctypes.byref(v), 0, FAKE, None, FAKE, None, 0, None) == WORKSPACE  # smooth_v needs scratch
 
 
 def test_prepared_attn_validation(L):
     qk = quant()
     args = [0, None, 0, 0, 0, 0, 0, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
     f = L.sage_attn_fwd_prepared
-    assert f(ctypes.byref(qk), 0, None, *args, None, 0, None) == INVALID  # no v_t
-    assert f(ctypes.byref(qk), FAKE, None, 1, *args[1:], None, 0, None) == INVALID  # fp8 without v_scale
+    assert f(ctypes.byref(qk), 0, None, None, *args, None, 0, None) == INVALID  # no v_t
+    assert f(ctypes.byref(qk), FAKE, None, None, 1, *args[1:], None, 0, None) == INVALID  # fp8 without v_scale
     masked = [0, FAKE, 0, 1, 0, 0, 256, 0, 0.0, FAKE, 0, 2 * 256 * 64, 256 * 64, 64, None]
-    assert f(ctypes.byref(qk), FAKE, None, *masked, None, 0, None) == WORKSPACE  # mask needs tile workspace
+    assert f(ctypes.byref(qk), FAKE, None, None, *masked, None, 0, None) == WORKSPACE  # mask needs tile workspace
     assert L.sage_mask_workspace_bytes(2, 8192, 8192, 1) == 2 * 32 * 128 * 4  # one int32 state per tile
     assert L.sage_mask_workspace_bytes(2, 8192, 8192, 0) == 0
-    assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 0) == 0
+    assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 0) >= 24 * 70 * 128 * 8  # smooth_v's fp64 sums
     assert L.sage_prepare_v_workspace_bytes(1, 24, 17776, 128, 1) >= 24 * 70 * 128 * 4
 
 

@@ -132,6 +132,25 @@ def test_debug_scores_extremes(orc):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 64), (2, 1, 65, 128), (1, 3, 300, 128), (1, 1, 1, 64)])
+def test_prep_v_smooth_v_bitexact(orc, B, H, N, d, dtype):
+    """smooth_v: V's channel means and the fp16 codes of V - mean, bit for bit."""
+    say(f"prep_v smooth_v B={B} H={H} N={N} d={d} {dtype}")
+    inp = make_inputs(B, H, N, N, d, seed=6, dtype=dtype)
+    v = (inp.v.float() + 37.0).to(dtype)
+    vm = torch.empty(B, H, d, dtype=torch.float32, device=DEV)
+    vt, vs = sage.prepare_v(v.to(DEV), "fp16", v_mean=vm)
+    torch.cuda.synchronize()
+    vb = bits(v)
+    want_m = orc.kmean(vb, inp.dtype)
+    want, _ = orc.prep_v(vb, "fp16", dtype=inp.dtype, vmean=want_m)
+    assert np.array_equal(vm.cpu().numpy().view(np.uint32), want_m.view(np.uint32))
+    nat = unpermute_vt(vt.cpu().numpy().view(np.uint16), "fp16")
+    assert np.array_equal(nat[:, :, :N, :], want)
+    assert not nat[:, :, N:, :].any()  # pad keys stay zero
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
 @pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 64), (2, 1, 65, 128), (1, 3, 300, 128), (1, 1, 1, 64)])
 def test_prep_v_bitexact(orc, pv, B, H, N, d, dtype):
@@ -169,13 +188,13 @@ def oracle_mask(mask):
     return mask.numpy() if mask.dtype == torch.float32 else mask.numpy().astype(np.uint8)
 
 
-def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None):
+def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None, smooth_v=False):
     q, k, v = to_dev(inp)
     if layout == "NHD":
         q, k, v = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v))
     mask_dev = None if mask is None else mask.to(DEV)
     out, lse = sage.sageattn(q, k, v, tensor_layout=layout, is_causal=causal, attn_mask=mask_dev, sm_scale=sm_scale,
-                             return_lse=True, pv_dtype=pv)
+                             return_lse=True, pv_dtype=pv, smooth_v=smooth_v)
     torch.cuda.synchronize()
     assert out.dtype == inp.q.dtype  # the output takes the input dtype
     B, H, Nq, d = inp.q.shape
@@ -184,7 +203,7 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     m = oracle_mask(mask)
     r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m,
                    sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv),
-                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype)
+                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype, smooth_v=smooth_v)
     ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m,
                              sm_scale=sm_scale, rows=rows, dtype=inp.dtype)
     got_o = rows_of(out, rows, layout)
@@ -240,6 +259,12 @@ CASES = [
     dict(name="fmask_zero_inf_tiles", B=1, H=2, Nq=520, Nk=700, d=128, mask="f_tiles"),
     dict(name="fmask_gqa_fp16_in_nhd", B=1, H=4, Hkv=1, Nq=130, Nk=260, d=128, dtype="fp16", layout="NHD",
          mask="f_rand_h"),
+    # smooth_v on values with a large channel bias
+    dict(name="smooth_v", B=1, H=2, Nq=300, Nk=417, d=128, smooth_v=True, v_bias=60.0),
+    dict(name="smooth_v_causal_gqa_mask_d64", B=2, H=4, Hkv=2, Nq=257, Nk=257, d=64, smooth_v=True, v_bias=20.0,
+         causal=True, mask="rand_1"),
+    dict(name="smooth_v_fp16_in_nhd", B=1, H=3, Nq=200, Nk=129, d=128, dtype="fp16", layout="NHD", smooth_v=True,
+         v_bias=100.0),
 ]
 
 
@@ -278,9 +303,13 @@ def test_attention_parity(orc, case):
     inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=11, dtype=dtype)
     if "Hkv" in c:
         inp = gqa_inputs(inp, c["Hkv"])
+    if "v_bias" in c:  # a per-channel offset of +-v_bias on V (what smooth_v is for)
+        sign = torch.where(torch.arange(d) % 3 == 0, -1.0, 1.0)
+        inp = dataclasses.replace(inp, v=(inp.v.float() + c["v_bias"] * sign).to(dtype))
     mask = case_mask(c, B, H, Nq, Nk)
     got_o, got_l, r, ex_o, ex_l = run_both(orc, inp, pv=c.get("pv", "fp16"), causal=c.get("causal", False), mask=mask,
-                                           sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"))
+                                           sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"),
+                                           smooth_v=c.get("smooth_v", False))
     e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype)
     say(f"  rel-L1 vs QE {e1:.3e}")
 
@@ -348,6 +377,9 @@ def test_errors_raise():
     with pytest.raises(api.SageError) as ei:  # fp16 Q with bf16 K, past the Python checks
         sage.quantize_qk(q.half(), k)
     assert ei.value.status == 1
+    with pytest.raises(api.SageError) as ei:  # smooth_v belongs to the FP16 PV path
+        sage.sageattn(q, k, v, pv_dtype="fp8", smooth_v=True)
+    assert ei.value.status == 2
 
 
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])

@@ -41,6 +41,7 @@ CASES = [
     dict(name="gqa_fp8", sq=[333, 129], sk=[333, 500], H=4, Hkv=2, d=128, pv="fp8", sigma=8.0),
     dict(name="gqa_fp8_causal_d64", sq=[200, 65, 256], sk=[200, 65, 256], H=4, Hkv=1, d=64, pv="fp8", sigma=8.0,
          causal=True),
+    dict(name="smooth_v_ragged", sq=[70, 1, 130, 300], sk=[90, 5, 130, 0], H=2, d=128, smooth_v=True, v_bias=40.0),
 ]
 
 
@@ -51,10 +52,14 @@ def test_varlen_parity(orc, case):
     pv, causal = c.get("pv", "fp16"), c.get("causal", False)
     inp = make_varlen_inputs(c["sq"], c["sk"], c["H"], c["d"], sigma=c.get("sigma", 4.0), seed=60,
                              Hkv=c.get("Hkv", 0), dtype=c.get("dtype", torch.bfloat16))
+    if "v_bias" in c:
+        inp.v = (inp.v.float() + c["v_bias"]).to(inp.v.dtype)
+    sv = c.get("smooth_v", False)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
     cq, ck = inp.cu_q.to(DEV), inp.cu_k.to(DEV)
     mq, mk = max(c["sq"]), max(c["sk"])
-    out, lse = sage.sageattn_varlen(q, k, v, cq, ck, mq, mk, is_causal=causal, return_lse=True, pv_dtype=pv)
+    out, lse = sage.sageattn_varlen(q, k, v, cq, ck, mq, mk, is_causal=causal, return_lse=True, pv_dtype=pv,
+                                    smooth_v=sv)
     g = sage.quantize_qk_varlen(q, k, cq, ck, mq, mk)
     torch.cuda.synchronize()
     assert out.shape == q.shape and out.dtype == q.dtype and lse.shape == (c["H"], q.shape[0])
@@ -79,7 +84,7 @@ def test_varlen_parity(orc, case):
 
     o32, o16, qlse = orc.run_qe_varlen(Q, K, V, cuq, cuk, pv=pv, causal=causal, BN=sage.block_n(pv),
                                        tau=sage.softmax_tau(pv), lsum_rounded=sage.rowsum_rounded(pv),
-                                       dtype=inp.dtype)
+                                       dtype=inp.dtype, smooth_v=sv)
     got = out.float().cpu().numpy()
     e1 = rel_l1(got, _dec(o16, inp.dtype))
     say(f"  rel-L1 vs per-sequence emulation {e1:.3e}")
