@@ -68,15 +68,16 @@ def lib():
             getattr(L, name).argtypes = [P, P, I]
             getattr(L, name).restype = None
         L.orc_kmean.argtypes = [P, i32, I, I, I, I, P]
-        L.orc_quant_qk.argtypes = [P, P, i32, P, I, I, I, I, I, I, I, I, P, P, P, P, P]
+        L.orc_block_mean.argtypes = [P, i32, I, I, I, I, P]
+        L.orc_quant_qk.argtypes = [P, P, i32, P, i32, I, I, I, I, I, I, I, I, P, P, P, P, P, P]
         L.orc_prep_v_fp16.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_prep_v_fp8.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_scores.argtypes = [P, P, I, I, I, I, I, P]
-        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32,
+        L.orc_attn_qe.argtypes = [P, P, P, P, P, P, P, P, P, i32, P, i32, I, i32, f32, I, I, I, I, I, I, I, I, I, f64, i32,
                                   P, I, P, i32, P, P]
         L.orc_attn_ex.argtypes = [P, P, P, i32, P, i32, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
         L.orc_merge_lse.argtypes = [P, P, I, I, I, P, P]
-        for name in ("orc_kmean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
+        for name in ("orc_kmean", "orc_block_mean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
                      "orc_attn_qe", "orc_attn_ex", "orc_merge_lse"):
             getattr(L, name).restype = None
         _lib = L
@@ -162,26 +163,37 @@ def kmean(K, dtype="bf16"):
     return out
 
 
+def block_mean(K, dtype="bf16"):
+    """K: [B,H,Nk,d] bits -> per-64-token-block means fp32 [B,H,ceil(Nk/64),d] (per_block_mean)."""
+    K = _c(K, np.uint16)
+    B, H, Nk, d = K.shape
+    out = np.empty((B, H, (Nk + QBLK - 1) // QBLK, d), np.float32)
+    lib().orc_block_mean(_p(K), _in_fp16(dtype), B, H, Nk, d, _p(out))
+    return out
+
+
 @dataclass
 class QuantQK:
     q8: np.ndarray  # int8 [B,H,Nq_pad,d]
     k8: np.ndarray  # int8 [B,Hkv,Nk_pad,d]
     qs: np.ndarray  # fp32 [B,H,ceil(Nq/64)]
     ks: np.ndarray  # fp32 [B,Hkv,ceil(Nk/64)]
-    kmean: np.ndarray  # fp32 [B,Hkv,d]
-    corr: np.ndarray  # fp32 [B,H,Nq]
+    kmean: np.ndarray  # fp32 [B,Hkv,d], or the block means [B,Hkv,ceil(Nk/64),d] with per_block_mean
+    corr: np.ndarray  # fp32 [B,H,Nq] (0 with per_block_mean)
+    corr_blk: np.ndarray | None = None  # per_block_mean: fp32 [B,H,ceil(Nk/64),Nq]
 
 
-def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None, dtype="bf16") -> QuantQK:
+def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None, dtype="bf16", per_block_mean=False) -> QuantQK:
     """Q [B,H,Nq,d], K [B,Hkv,Nk,d] (Hkv divides H; query head h reads key head h // (H // Hkv)),
-    both of ``dtype``."""
+    both of ``dtype``.  per_block_mean: K is smoothed by its 64-token block's mean and the
+    per-block score terms come out in corr_blk."""
     Q = _c(Q, np.uint16)
     K = _c(K, np.uint16)
     B, H, Nq, d = Q.shape
     Hkv, Nk = K.shape[1], K.shape[2]
     assert K.shape[0] == B and K.shape[3] == d and H % Hkv == 0
     if km is None:
-        km = kmean(K, dtype)
+        km = block_mean(K, dtype) if per_block_mean else kmean(K, dtype)
     km = _c(km, np.float32)
     Nq_pad = pad_n(Nq) if Nq_pad is None else Nq_pad
     Nk_pad = pad_n(Nk) if Nk_pad is None else Nk_pad
@@ -190,9 +202,10 @@ def quant_qk(Q, K, km=None, Nq_pad=None, Nk_pad=None, dtype="bf16") -> QuantQK:
     qs = np.empty((B, H, (Nq + QBLK - 1) // QBLK), np.float32)
     ks = np.empty((B, Hkv, (Nk + QBLK - 1) // QBLK), np.float32)
     corr = np.empty((B, H, Nq), np.float32)
-    lib().orc_quant_qk(_p(Q), _p(K), _in_fp16(dtype), _p(km), B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks),
-                       _p(corr))
-    return QuantQK(q8, k8, qs, ks, km, corr)
+    cb = np.empty((B, H, (Nk + QBLK - 1) // QBLK, Nq), np.float32) if per_block_mean else None
+    lib().orc_quant_qk(_p(Q), _p(K), _in_fp16(dtype), _p(km), 1 if per_block_mean else 0, B, H, Hkv, Nq, Nk, d, Nq_pad,
+                       Nk_pad, _p(q8), _p(k8), _p(qs), _p(ks), _p(corr), _p(cb))
+    return QuantQK(q8, k8, qs, ks, km, corr, cb)
 
 
 def prep_v(V, pv: str = "fp16", dtype="bf16", vmean=None):
@@ -265,7 +278,8 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     o16 = np.empty((R, d), np.uint16)
     lse = np.empty((R,), np.float32)
     vm = None if vmean is None else _c(vmean, np.float32)
-    lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(np.ascontiguousarray(vhat)),
+    lib().orc_attn_qe(_p(qk.q8), _p(qk.k8), _p(qk.qs), _p(qk.ks), _p(qk.corr), _p(qk.corr_blk),
+                      _p(np.ascontiguousarray(vhat)),
                       _p(vs), _p(vm), 1 if pv == "fp8" else 0, _p(m), mf, mh, 1 if causal else 0, sm, B, H, Hkv, Nq, Nk, d,
                       Nq_pad, Nk_pad, BN, float(tau), 1 if lsum_rounded else 0, _p(rp), R, _p(o32),
                       _in_fp16(out_dtype), _p(o16), _p(lse))
@@ -306,11 +320,11 @@ class QEResult:
 
 
 def run_qe(Q, K, V, *, pv="fp16", causal=False, mask=None, sm_scale=None, BN=64, tau=0.0, lsum_rounded=False,
-           rows=None, dtype="bf16", out_dtype=None, smooth_v=False) -> QEResult:
+           rows=None, dtype="bf16", out_dtype=None, smooth_v=False, per_block_mean=False) -> QEResult:
     """All quantized-emulation steps: kmean -> quant_qk -> prep_v -> attn_qe.  The output dtype
     defaults to the input dtype.  smooth_v: V's token mean (taken as K's) is subtracted before the
     FP16 rounding of V and added back to the output."""
-    qk = quant_qk(Q, K, dtype=dtype)
+    qk = quant_qk(Q, K, dtype=dtype, per_block_mean=per_block_mean)
     vmean = kmean(V, dtype) if smooth_v else None
     vhat, vs = prep_v(V, pv, dtype=dtype, vmean=vmean)
     Nq, Nk = Q.shape[2], K.shape[2]
@@ -343,7 +357,7 @@ def _seq_heads(X, lo, hi):
 
 
 def run_qe_varlen(Q, K, V, cu_q, cu_k, *, pv="fp16", causal=False, sm_scale=None, BN=64, tau=0.0,
-                  lsum_rounded=False, dtype="bf16", out_dtype=None, smooth_v=False):
+                  lsum_rounded=False, dtype="bf16", out_dtype=None, smooth_v=False, per_block_mean=False):
     """Quantized emulation of packed variable-length batches (the docs digest's ``sageattn_varlen``).
 
     Q: [total_q, H, d], K and V: [total_k, Hkv, d] (bits of ``dtype``); sequence b holds query rows
@@ -365,7 +379,7 @@ def run_qe_varlen(Q, K, V, cu_q, cu_k, *, pv="fp16", causal=False, sm_scale=None
             continue
         r = run_qe(_seq_heads(Q, q0, q1), _seq_heads(K, k0, k1), _seq_heads(V, k0, k1), pv=pv, causal=causal,
                    sm_scale=sm_scale, BN=BN, tau=tau, lsum_rounded=lsum_rounded, dtype=dtype, out_dtype=out_dtype,
-                   smooth_v=smooth_v)
+                   smooth_v=smooth_v, per_block_mean=per_block_mean)
         n = q1 - q0
         o32[q0:q1] = r.o32.reshape(H, n, d).transpose(1, 0, 2)
         o16[q0:q1] = r.o16.reshape(H, n, d).transpose(1, 0, 2)

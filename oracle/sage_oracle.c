@@ -40,6 +40,11 @@
  *    is then at most 2^tau.  The normalized result does not depend on tau; only where P is
  *    rounded does;
  *  - a row with no valid key gives O = 0 and LSE = -inf;
+ *  - per_block_mean (the sageattn3_blackwell usage section's option): K is smoothed by the mean of
+ *    its own 64-token quantization block (fp64 sum over the block's tokens, one rounding) instead
+ *    of the global mean.  That shift differs between blocks, so it does not cancel in the softmax:
+ *    the term sm_scale * (q_i . m_u) of key block u is added to each score (computed as
+ *    fp32(sum_c fp64(Q_ic) * fp64(m_uc))), and the LSE needs no further correction;
  *  - smooth_v (FP16 PV only, as the pages tie it to the FP16 kernel): V's per-channel token mean is
  *    taken exactly like K's (fp64 sum over all Nk tokens, one rounding to fp32), V - mean is
  *    rounded once to fp32 and then to fp16, and the mean is added back to the normalized output
@@ -242,36 +247,67 @@ static void quantize_blocks(const float* X, int64_t N, int64_t N_pad, int64_t d,
   memset(x8 + N * d, 0, (size_t)((N_pad - N) * d));
 }
 
+/* Per-block K means for per_block_mean: bmean [B][H][ceil(Nk/64)][d], block u's mean over its
+ * tokens [64u, min(64u+64, Nk)), fp64 sum rounded once to fp32. */
+void orc_block_mean(const uint16_t* K, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d, float* bmean) {
+  int64_t nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t u = 0; u < nbk; ++u) {
+      int64_t t0 = u * ORC_QBLK, t1 = t0 + ORC_QBLK < Nk ? t0 + ORC_QBLK : Nk;
+      for (int64_t c = 0; c < d; ++c) {
+        double s = 0.0;
+        for (int64_t t = t0; t < t1; ++t) s += (double)orc_in_to_f32(K[(bh * Nk + t) * d + c], in_fp16);
+        bmean[(bh * nbk + u) * d + c] = (float)(s / (double)(t1 - t0));
+      }
+    }
+}
+
 /* Q [B][H][Nq][d], K [B][Hkv][Nk][d], both bf16 or both fp16 (in_fp16); kmean fp32 [B][Hkv][d]
  * (from orc_kmean).
  * Hkv divides H; query head h reads key/value head h / (H / Hkv) (group-query attention).
  * Outputs: q8 [B][H][Nq_pad][d], k8 [B][Hkv][Nk_pad][d], qs [B][H][ceil(Nq/64)],
  *          ks [B][Hkv][ceil(Nk/64)], corr [B][H][Nq] = fp32(sum_c fp64(Q_ic) * fp64(kmean_c)) with
  *          the K mean of the query head's key/value head.
- * K is smoothed as fp32(K - kmean) (one rounding) before quantizing. */
-void orc_quant_qk(const uint16_t* Q, const uint16_t* K, int in_fp16, const float* kmean, int64_t B, int64_t H, int64_t Hkv,
-                  int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8, int8_t* k8,
-                  float* qs, float* ks, float* corr) {
+ * K is smoothed as fp32(K - kmean) (one rounding) before quantizing.
+ * per_block != 0: kmean holds the per-block means [B][Hkv][ceil(Nk/64)][d] (orc_block_mean); K is
+ * smoothed by its block's mean, corr is 0, and corr_blk [B][H][ceil(Nk/64)][Nq] receives the
+ * score terms fp32(sum_c fp64(Q_ic) * fp64(m_uc)) of the query head's key/value head. */
+void orc_quant_qk(const uint16_t* Q, const uint16_t* K, int in_fp16, const float* kmean, int per_block, int64_t B,
+                  int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int64_t Nq_pad, int64_t Nk_pad, int8_t* q8,
+                  int8_t* k8, float* qs, float* ks, float* corr, float* corr_blk) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bh = 0; bh < B * Hkv; ++bh) {
     float* xk = (float*)malloc((size_t)(Nk * d) * sizeof(float));
-    const float* km = kmean + bh * d;
-    for (int64_t t = 0; t < Nk; ++t)
+    for (int64_t t = 0; t < Nk; ++t) {
+      const float* km = per_block ? kmean + (bh * nbk + t / ORC_QBLK) * d : kmean + bh * d;
       for (int64_t c = 0; c < d; ++c) xk[t * d + c] = orc_in_to_f32(K[(bh * Nk + t) * d + c], in_fp16) - km[c];
+    }
     quantize_blocks(xk, Nk, Nk_pad, d, k8 + bh * Nk_pad * d, ks + bh * nbk);
     free(xk);
   }
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bh = 0; bh < B * H; ++bh) {
     float* xq = (float*)malloc((size_t)(Nq * d) * sizeof(float));
-    const float* km = kmean + ((bh / H) * Hkv + (bh % H) / (H / Hkv)) * d;
+    const int64_t bhk = (bh / H) * Hkv + (bh % H) / (H / Hkv);
     for (int64_t i = 0; i < Nq * d; ++i) xq[i] = orc_in_to_f32(Q[bh * Nq * d + i], in_fp16);
     quantize_blocks(xq, Nq, Nq_pad, d, q8 + bh * Nq_pad * d, qs + bh * nbq);
     for (int64_t i = 0; i < Nq; ++i) {
-      double s = 0.0;
-      for (int64_t c = 0; c < d; ++c) s += (double)xq[i * d + c] * (double)km[c];
-      corr[bh * Nq + i] = (float)s;
+      if (per_block) {
+        corr[bh * Nq + i] = 0.0f;
+        for (int64_t u = 0; u < nbk; ++u) {
+          const float* km = kmean + (bhk * nbk + u) * d;
+          double s = 0.0;
+          for (int64_t c = 0; c < d; ++c) s += (double)xq[i * d + c] * (double)km[c];
+          corr_blk[(bh * nbk + u) * Nq + i] = (float)s;
+        }
+      } else {
+        const float* km = kmean + bhk * d;
+        double s = 0.0;
+        for (int64_t c = 0; c < d; ++c) s += (double)xq[i * d + c] * (double)km[c];
+        corr[bh * Nq + i] = (float)s;
+      }
     }
     free(xq);
   }
@@ -347,12 +383,14 @@ void orc_scores(const int8_t* q8h, const int8_t* k8h, int64_t d, int64_t row0, i
 /* vhat: fp16 bits (pv_fp8 = 0) or e4m3 bytes (pv_fp8 = 1), layout [B][H][Nk][d].             */
 /* vs:   per-channel V scale [B][H][d] (fp8 only).                                            */
 /* vmean: smooth_v's per-channel V mean [B][Hkv][d], added back to the output, or NULL.        */
+/* corr_blk: per_block_mean's score terms [B][H][ceil(Nk/64)][Nq] (orc_quant_qk), or NULL.      */
 /* BN: keys per online-softmax tile; tau: lazy-maximum threshold in log2 units (0 = exact).    */
 /* lsum_rounded: 0 = l sums the fp32 p, 1 = l sums P as rounded for PV.                       */
 /* Outputs per requested row: o32 [nrows][d] (fp32 O before the output rounding, may be NULL),*/
 /* o16 [nrows][d] (bf16 bits, or fp16 bits if out_fp16), lse [nrows] (natural log, fp32).     */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const float* ks, const float* corr,
+                 const float* corr_blk,
                  const void* vhat, const float* vs, const float* vmean, int pv_fp8, const void* mask, int mask_f32,
                  int64_t mask_h,
                  int causal,
@@ -397,6 +435,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           for (int64_t c = 0; c < d; ++c) acc += (int32_t)q[c] * (int32_t)k[c];
           float cst = (qscale * ks[bhk * nbk + j / ORC_QBLK]) * sm_scale;
           s[j - j0] = (float)acc * cst;
+          if (corr_blk) s[j - j0] += sm_scale * corr_blk[(bh * nbk + j / ORC_QBLK) * Nq + i]; /* per-block mean */
           if (madd) s[j - j0] += madd[j]; /* additive mask, natural-log units */
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
