@@ -80,7 +80,14 @@ typedef struct {
  *   k_mean   fp32  [B][Hkv][d]           per-channel token mean of K (fp64 sum, rounded once)
  *   lse_corr fp32  [B][H][Nq]            sum_c Q[i,c]*k_mean[c] with the query head's key head mean:
  *                                        adds the smoothing shift back to the LSE
- * Nq_pad and Nk_pad must equal sage_pad_tokens(Nq) and sage_pad_tokens(Nk). */
+ * Nq_pad and Nk_pad must equal sage_pad_tokens(Nq) and sage_pad_tokens(Nk).
+ * per_block_mean (the sageattn3_blackwell usage section's option; both pointers set, else both
+ * NULL): K is smoothed by the mean of its own 64-token block instead of the global mean.  That
+ * shift differs between blocks, so its score terms are kept and added back to the scores:
+ *   k_block_mean fp32 [B][Hkv][ceil(Nk/64)][d]  block means (fp64 sum over the block's tokens,
+ *                                               one rounding)
+ *   blk_corr     fp32 [B][H][ceil(Nk/64)][Nq]   sum_c Q[i,c] * k_block_mean[u,c] (fp32 sums)
+ * and k_mean, lse_corr hold zeros (the LSE then needs no shift).  Not combined with an fp32 mask. */
 typedef struct {
   int8_t* q8;
   int8_t* k8;
@@ -89,6 +96,8 @@ typedef struct {
   float* k_mean;
   float* lse_corr;
   int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;
+  float* k_block_mean;
+  float* blk_corr;
 } sage_qk_quant;
 
 /* Padded token extent of q8 / k8 / prepared V: n rounded up to a multiple of 128. Host only. */

@@ -50,7 +50,8 @@ class QKQuant(ctypes.Structure):
     _fields_ = [("q8", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("lse_corr", ctypes.c_void_p),
                 ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("Nq", ctypes.c_int64),
-                ("Nk", ctypes.c_int64), ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64), ("Nk_pad", ctypes.c_int64)]
+                ("Nk", ctypes.c_int64), ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64), ("Nk_pad", ctypes.c_int64),
+                ("k_block_mean", ctypes.c_void_p), ("blk_corr", ctypes.c_void_p)]
 
 
 _lib = None
@@ -196,22 +197,29 @@ class QuantizedQK:
     d: int
     Hkv: int
     dtype: torch.dtype = torch.bfloat16
+    k_block_mean: torch.Tensor | None = None  # per_block_mean: [B, Hkv, ceil(Nk/64), d]
+    blk_corr: torch.Tensor | None = None  # per_block_mean: [B, H, ceil(Nk/64), Nq]
 
     def cstruct(self) -> QKQuant:
         return QKQuant(self.q8.data_ptr(), self.k8.data_ptr(), self.q_scale.data_ptr(), self.k_scale.data_ptr(),
                        self.k_mean.data_ptr(), self.lse_corr.data_ptr(), self.B, self.H, self.Hkv, self.Nq, self.Nk,
-                       self.d, self.q8.shape[2], self.k8.shape[2])
+                       self.d, self.q8.shape[2], self.k8.shape[2],
+                       None if self.k_block_mean is None else self.k_block_mean.data_ptr(),
+                       None if self.blk_corr is None else self.blk_corr.data_ptr())
 
 
-def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None, dtype=torch.bfloat16) -> QuantizedQK:
+def alloc_quantized(B, H, Nq, Nk, d, device, Hkv=None, dtype=torch.bfloat16, per_block_mean=False) -> QuantizedQK:
     Hkv = H if Hkv is None else Hkv
     nq, nk = pad_tokens(Nq), pad_tokens(Nk)
+    nbk = (Nk + 63) // 64
+    pbm = dict(k_block_mean=torch.empty(B, Hkv, nbk, d, dtype=torch.float32, device=device),
+               blk_corr=torch.empty(B, H, nbk, Nq, dtype=torch.float32, device=device)) if per_block_mean else {}
     return QuantizedQK(torch.empty(B, H, nq, d, dtype=torch.int8, device=device),
                        torch.empty(B, Hkv, nk, d, dtype=torch.int8, device=device),
                        torch.empty(B, H, (Nq + 63) // 64, dtype=torch.float32, device=device),
                        torch.empty(B, Hkv, (Nk + 63) // 64, dtype=torch.float32, device=device),
                        torch.empty(B, Hkv, d, dtype=torch.float32, device=device),
-                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d, Hkv, dtype)
+                       torch.empty(B, H, Nq, dtype=torch.float32, device=device), B, H, Nq, Nk, d, Hkv, dtype, **pbm)
 
 
 def quantize_workspace(B, Hkv, Nk, d, device) -> torch.Tensor:
@@ -220,13 +228,15 @@ def quantize_workspace(B, Hkv, Nk, d, device) -> torch.Tensor:
 
 
 def quantize_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", out: QuantizedQK | None = None,
-                workspace: torch.Tensor | None = None) -> QuantizedQK:
+                workspace: torch.Tensor | None = None, per_block_mean: bool = False) -> QuantizedQK:
     """K mean, per-64-token-block INT8 Q and smoothed K, scales and the LSE shift.  k may have fewer
-    heads than q (group-query attention: query head h reads key head h // (H // Hkv))."""
+    heads than q (group-query attention: query head h reads key head h // (H // Hkv)).
+    per_block_mean: each 64-token K block is smoothed by its own mean (score terms in blk_corr)."""
     L = load_library()
     dq, dk = _desc(q, tensor_layout), _desc(k, tensor_layout)
     if out is None:
-        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
+        out = alloc_quantized(dq.B, dq.H, dq.N, dk.N, dq.d, q.device, Hkv=dk.H, dtype=q.dtype,
+                              per_block_mean=per_block_mean)
     out.dtype = q.dtype
     if workspace is None:
         workspace = quantize_workspace(dk.B, dk.H, dk.N, dk.d, q.device)
@@ -298,7 +308,7 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
 
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND", is_causal: bool = False,
              attn_mask: torch.Tensor | None = None, sm_scale: float | None = None, return_lse: bool = False,
-             pv_dtype: str = "fp16", smooth_v: bool = False):
+             pv_dtype: str = "fp16", smooth_v: bool = False, per_block_mean: bool = False):
     """Quantized attention forward: INT8 Q/K with K smoothing, FP16 (or FP8 e4m3) PV.
 
     q: bf16 or fp16 [B, H, N, d] ("HND") or [B, N, H, d] ("NHD"), d in {64, 128}; k, v: the same
@@ -319,7 +329,7 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
     hq = q.shape[1] if tensor_layout == "HND" else q.shape[2]
     if hq % hk != 0:
         raise ValueError(f"the {hk} key/value heads do not divide the {hq} query heads")
-    qk = quantize_qk(q, k, tensor_layout)
+    qk = quantize_qk(q, k, tensor_layout, per_block_mean=per_block_mean)
     return attn_fwd(qk, v, tensor_layout=tensor_layout, is_causal=is_causal, attn_mask=attn_mask, sm_scale=sm_scale,
                     pv_dtype=pv_dtype, return_lse=return_lse, smooth_v=smooth_v)
 
@@ -452,7 +462,7 @@ def _cu(t: torch.Tensor, what: str) -> torch.Tensor:
 
 def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                        max_seqlen_q: int, max_seqlen_k: int, out: QuantizedQK | None = None,
-                       workspace: torch.Tensor | None = None) -> QuantizedQK:
+                       workspace: torch.Tensor | None = None, per_block_mean: bool = False) -> QuantizedQK:
     """Per-sequence K mean and INT8 quantization of packed q [total_q, H, d] and k [total_k, Hkv, d]
     into the dense padded layout of len(cu_seqlens) - 1 sequences of max_seqlen tokens."""
     L = load_library()
@@ -462,7 +472,8 @@ def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Ten
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold nseq + 1 >= 2 entries")
     dq, dk = _packed_desc(q, nseq, max_seqlen_q), _packed_desc(k, nseq, max_seqlen_k)
     if out is None:
-        out = alloc_quantized(nseq, dq.H, max_seqlen_q, max_seqlen_k, dq.d, q.device, Hkv=dk.H, dtype=q.dtype)
+        out = alloc_quantized(nseq, dq.H, max_seqlen_q, max_seqlen_k, dq.d, q.device, Hkv=dk.H, dtype=q.dtype,
+                              per_block_mean=per_block_mean)
     out.dtype = q.dtype
     ws = quantize_workspace(nseq, dk.H, max_seqlen_k, dk.d, q.device) if workspace is None else workspace
     qs = out.cstruct()
@@ -475,7 +486,7 @@ def quantize_qk_varlen(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Ten
 def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
                     sm_scale: float | None = None, smooth_k: bool = True, return_lse: bool = False,
-                    pv_dtype: str = "fp16", smooth_v: bool = False):
+                    pv_dtype: str = "fp16", smooth_v: bool = False, per_block_mean: bool = False):
     """Quantized attention of packed variable-length sequences (the docs digest's ``sageattn_varlen``).
 
     q: [total_q, H, d], k and v: [total_k, Hkv, d] (bf16 or fp16, one dtype); cu_seqlens_*: int32
@@ -492,7 +503,8 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if q.shape[1] % k.shape[1] != 0:
         raise ValueError(f"the {k.shape[1]} key/value heads do not divide the {q.shape[1]} query heads")
     L = load_library()
-    qk = quantize_qk_varlen(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    qk = quantize_qk_varlen(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                            per_block_mean=per_block_mean)
     cq, ck = _cu(cu_seqlens_q, "cu_seqlens_q"), _cu(cu_seqlens_k, "cu_seqlens_k")
     dv = _packed_desc(v, qk.B, max_seqlen_k)
     out = torch.empty_like(q)

@@ -66,6 +66,7 @@ sage_status check_qk(const sage_qk_quant* qk) {
   if (qk->Nq_pad != sage_pad_tokens(qk->Nq) || qk->Nk_pad != sage_pad_tokens(qk->Nk))
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(qk->q8) || !aligned16(qk->k8)) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((qk->k_block_mean == nullptr) != (qk->blk_corr == nullptr)) return SAGE_ERR_INVALID_ARGUMENT;
   return SAGE_OK;
 }
 
@@ -192,6 +193,8 @@ QuantArgs quant_args(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_
   a.nbq = (int)cdiv(a.Nq, 64);
   a.nbk = (int)cdiv(a.Nk, 64);
   a.in_fp16 = q->dtype == SAGE_FP16;
+  a.kbmean = out->k_block_mean;
+  a.blk_corr = out->blk_corr;
   return a;
 }
 
@@ -199,7 +202,8 @@ sage_status enqueue_quantize(const QuantArgs& a, void* workspace, hipStream_t st
   sage_status s;
   if ((s = hip_status(launch_kmean(a, static_cast<double*>(workspace), (int)cdiv(a.Nk, kChunkTokens), st))) != SAGE_OK)
     return s;
-  return hip_status(launch_quant(a, st));
+  if ((s = hip_status(launch_quant(a, st))) != SAGE_OK) return s;
+  return a.kbmean ? hip_status(launch_block_corr(a, st)) : SAGE_OK;
 }
 
 // Packed variable-length batches: the token counts of the descriptors are the longest sequence,
@@ -309,6 +313,7 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
   c->mh = 0;
   if (mask) {
     if (mask_dtype != SAGE_MASK_BOOL && mask_dtype != SAGE_MASK_F32) return SAGE_ERR_INVALID_ARGUMENT;
+    if (mask_dtype == SAGE_MASK_F32 && qk->blk_corr) return SAGE_ERR_UNSUPPORTED;  // not combined
     if (mask_dtype == SAGE_MASK_F32 && (uintptr_t)mask % 4 != 0) return SAGE_ERR_INVALID_ARGUMENT;
     if (mask_h != 1 && mask_h != qk->H) return SAGE_ERR_INVALID_ARGUMENT;
     if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_q < qk->Nk) return SAGE_ERR_INVALID_ARGUMENT;
@@ -376,6 +381,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   }
   a.q8 = qk->q8;
   a.k8 = qk->k8;
+  a.blk_corr = qk->blk_corr;
   a.qs = qk->q_scale;
   a.ks = qk->k_scale;
   a.corr = qk->lse_corr;

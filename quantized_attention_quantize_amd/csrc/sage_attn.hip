@@ -330,8 +330,8 @@ __device__ __forceinline__ void max_piece(const v16i (&acc)[2], int (&ch)[4], in
 }
 // Combines the chains across the wave's halves and moves the reference maximum (lazy by
 // kSoftmaxTau[PV] log2 units).  Returns 2^(m_old - m_new); the new exponent offset goes to pm_new.
-template <int PV, bool MASKED, bool MF = false>
-__device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowState& rs, float& pm_new) {
+template <int PV, bool MASKED, bool MF = false, bool BM = false>
+__device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowState& rs, float& pm_new, float cb = 0.f) {
   constexpr float kTau = kSoftmaxTau[PV];
   int im = smax<MF>(smax<MF>(ch[0], ch[1]), smax<MF>(ch[2], ch[3]));
   const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);  // lanes l and l ^ 32
@@ -339,6 +339,10 @@ __device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowStat
   float mt;
   if constexpr (MF)
     mt = __int_as_float(im);  // already log2-unit fp32, -inf if nothing is visible
+  else if constexpr (BM && MASKED)  // with the row's per-block score term cb (per_block_mean)
+    mt = im == INT_MIN ? -INFINITY : __builtin_fmaf((float)im, c, cb);
+  else if constexpr (BM)
+    mt = __builtin_fmaf((float)im, c, cb);
   else if constexpr (MASKED)
     mt = im == INT_MIN ? -INFINITY : (float)im * c;
   else
@@ -392,13 +396,15 @@ __device__ __forceinline__ typename StepGeom<D, PV>::VFrag vfrag(const char* sV,
 // lim / mtile / has_m / mvec4 describing T[n] and scale c_cur), all its row maxima follow, and the
 // exponentials take the converted scores as they are.  Returns 2^(m_{n-1} - m_n), the factor O
 // takes after the PV of T[n-1].
-template <int D, int PV, bool SLOW, bool MF = false>
+template <int D, int PV, bool SLOW, bool MF = false, bool BM = false>
 __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<PV>& P,
                                            typename StepGeom<D, PV>::VFrag (&vpre)[StepGeom<D, PV>::LA],
                                            const char* sKn, const char* sVp, const char* sVn, const v4i (&qf)[D / 32],
                                            v16f (&o)[D / 32], float c_cur, RowState& rs, const LaneBases& lb, int g,
-                                           int lim, const void* mtile, bool mvec4, bool has_m = false) {
+                                           int lim, const void* mtile, bool mvec4, bool has_m = false,
+                                           float cb_cur = 0.f) {
   static_assert(SLOW || !MF, "the float-mask step is a masked step");
+  static_assert(!(MF && BM), "per_block_mean is not combined with a float mask");
   using SG = StepGeom<D, PV>;
   constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = SG::NM, LA = SG::LA;
   constexpr int NG = PV == 0 ? 16 : 8;  // exponential groups of 2 (fp16) or 4 (e4m3) scores
@@ -446,6 +452,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
       kf[r - NPV] = kfrag(r - NPV);
   };
   float psum = 0.f, alpha = 1.f;
+  float nb = 0.f;  // per_block_mean: T[n]'s row term minus the exponent offset
   const v2h ones = {(_Float16)1.f, (_Float16)1.f};
 
 #pragma unroll
@@ -473,8 +480,9 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
     }
     if (k == FIN) {
       float pm_new;
-      alpha = finish_max<PV, SLOW, MF>(ch, c_cur, rs, pm_new);
+      alpha = finish_max<PV, SLOW, MF, BM>(ch, c_cur, rs, pm_new, cb_cur);
       rs.pm = pm_new;
+      if constexpr (BM) nb = cb_cur - pm_new;
     }
     // exponentials of T[n] assigned to slot k
 #pragma unroll
@@ -493,7 +501,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
         if constexpr (MF) {
           t = __builtin_amdgcn_exp2f(__int_as_float(si) - rs.pm);  // -inf gives 0
         } else {
-          t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, -rs.pm));
+          t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, BM ? nb : -rs.pm));
           if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
         }
         x[e] = t;
@@ -566,7 +574,9 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
 // of T[n+3] into slots freed two steps earlier, and waits at its end only for the loads of the
 // previous step.  The loop is unrolled four times so every slot is a compile-time offset.  One
 // barrier per tile.  MF: the mask is fp32 and additive, and every tile takes the masked step.
-template <int D, int PV, int MF>
+// BM: per_block_mean -- every score of key tile t gets the row's term blk_corr[t][row] (loaded a
+// step ahead, before the step's staging loads, so the vmcnt waits below cover it).
+template <int D, int PV, int MF, int BM>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
@@ -718,6 +728,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   typename StepGeom<D, PV>::VFrag vpre[StepGeom<D, PV>::LA];
   float c_cur = scale_of(t0);
   bool part_cur = partial(t0);
+  // per_block_mean: the row's score term of a key tile, in log2 units (rows past Nq read row Nq-1)
+  const float* cbh = BM ? a.blk_corr + (bh * a.nbk) * a.Nq + (row < a.Nq ? row : a.Nq - 1) : nullptr;
+  const float cbs = a.sm_scale * kLog2e;
+  auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
+  float cb_cur = cb_of(t0);
   {  // scores of T[0] and the row maxima of its first key block; the first PV operands
     qk_tile<D>(kring, qf, lr, g, acc);
     int lim;
@@ -739,6 +754,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   auto step = [&](auto slot) -> bool {
     constexpr int Q = decltype(slot)::value;  // n % kNS
     if (tc >= kt_end) return false;
+    const float cb_nxt = cb_of(tn);  // before the staging loads (see above)
     __syncthreads();
     st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
     st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
@@ -764,15 +780,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       int lim;
       const void* mtile;
       visible(tn, lim, mtile);
-      alpha = tile_step<D, PV, true>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mtile,
-                                     a.mask_vec4);
+      alpha = tile_step<D, PV, true, false, BM>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mtile,
+                                                a.mask_vec4, false, cb_cur);
     } else {
-      alpha = tile_step<D, PV, false>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, kBlockN - 1, nullptr,
-                                      false);
+      alpha = tile_step<D, PV, false, false, BM>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g,
+                                                 kBlockN - 1, nullptr, false, false, cb_cur);
     }
     // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare for the lazy FP16 maximum)
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
     c_cur = scale_of(tn);
+    cb_cur = cb_nxt;
     part_cur = part_nxt;
     // the loads of the previous steps must have landed before the next barrier
     switch (nload) {
@@ -877,26 +894,41 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
 
 // Every variant instantiated explicitly: the launches below alone do not make hipcc's host pass
 // emit the launch stubs of the MF = 0 kernels.
-template __global__ void k_attn_fwd<128, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 0, 1>(AttnArgs);
-template __global__ void k_attn_fwd<128, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 1, 1>(AttnArgs);
-template __global__ void k_attn_fwd<64, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 0, 1>(AttnArgs);
-template __global__ void k_attn_fwd<64, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 1>(AttnArgs);
 
-template <int D, int PV, int MF>
+template <int D, int PV, int MF, int BM>
 static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
-  k_attn_fwd<D, PV, MF><<<grid, kAttnThreads, 0, s>>>(a);
+  k_attn_fwd<D, PV, MF, BM><<<grid, kAttnThreads, 0, s>>>(a);
+}
+
+// the float-mask and per_block_mean variants are not combined (the host rejects both at once)
+template <int D, int PV>
+static void launch_attn_p(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (a.mask_f32)
+    launch_attn_t<D, PV, 1, 0>(a, grid, s);
+  else if (a.blk_corr)
+    launch_attn_t<D, PV, 0, 1>(a, grid, s);
+  else
+    launch_attn_t<D, PV, 0, 0>(a, grid, s);
 }
 
 template <int D>
 static void launch_attn_d(const AttnArgs& a, int pv_fp8, unsigned grid, hipStream_t s) {
   if (pv_fp8)
-    a.mask_f32 ? launch_attn_t<D, 1, 1>(a, grid, s) : launch_attn_t<D, 1, 0>(a, grid, s);
+    launch_attn_p<D, 1>(a, grid, s);
   else
-    a.mask_f32 ? launch_attn_t<D, 0, 1>(a, grid, s) : launch_attn_t<D, 0, 0>(a, grid, s);
+    launch_attn_p<D, 0>(a, grid, s);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s) {

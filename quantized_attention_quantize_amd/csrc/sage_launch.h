@@ -32,6 +32,10 @@ struct QuantArgs {
   const int* cu_q;
   const int* cu_k;
   int64_t total_q, total_k;
+  // per_block_mean (null: global-mean smoothing): K block means [B][Hkv][nbk][d] and the score
+  // terms [B][H][nbk][Nq]; kmean and corr then hold zeros
+  float* kbmean;
+  float* blk_corr;
 };
 
 struct PrepVArgs {
@@ -68,6 +72,7 @@ struct AttnArgs {
   const void* vt;  // prepared V
   const float* vscale;
   const float* vmean;  // smooth_v: [B][Hkv][d] added back to O (null: off)
+  const float* blk_corr;  // per_block_mean: [B][H][nbk][Nq] score terms (null: global-mean smoothing)
   const void* mask;  // element mask (only read for mixed tiles); strides in elements
   int64_t m_sb, m_sh, m_sq;
   int mask_f32;       // 0: uint8, nonzero = attend; 1: fp32 added to the scaled score, -inf = drop
@@ -111,6 +116,7 @@ struct DebugQKArgs {
 
 hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
+hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s);
 hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s);
 hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s);

@@ -116,7 +116,9 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
 // Block x < Nq_pad/64 handles Q rows [64x, 64x+64) of query head y; the others handle K rows of
 // key head y (only y < B*Hkv: the key heads of group-query attention).  Blocks past the last valid
 // block only write zero pad rows.  Each thread holds 8 channels of RPB rows.  A query head's LSE
-// shift uses the K mean of its key head h / (H / Hkv).
+// shift uses the K mean of its key head h / (H / Hkv).  per_block_mean (kbmean set): a key block
+// is smoothed by its own column means (fp64 sums of its valid rows, combined in a fixed order, one
+// rounding), which it also writes out; the global K mean is then zero.
 // ---------------------------------------------------------------------------------------------
 template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
@@ -148,6 +150,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
       *reinterpret_cast<uint2*>(x8 + (int64_t)r * D + cg * 8) = make_uint2(0u, 0u);
     }
     if (t == 0 && u < (isq ? a.nbq : a.nbk)) (isq ? a.qs : a.ks)[bh * (isq ? a.nbq : a.nbk) + u] = 0.f;
+    if (!isq && a.kbmean != nullptr && u < a.nbk && t < D) a.kbmean[(bh * a.nbk + u) * D + t] = 0.f;
     return;
   }
 
@@ -157,6 +160,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
   const int64_t sn = isq ? a.q_sn : a.k_sn;
   const unsigned short* src =
       (isq ? a.q + b * a.q_sb + h * a.q_sh : a.k + b * a.k_sb + h * a.k_sh) + sp.off * sn + cg * 8;
+  const bool pbm = !isq && a.kbmean != nullptr;  // uniform
   float x[RPB][8];
   float amax = 0.f;
 #pragma unroll
@@ -167,13 +171,44 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float f = in_to_f32<IN>(v[j]);
-        if (!isq) f = f - km_s[cg * 8 + j];  // one fp32 rounding
+        if (!isq && !pbm) f = f - km_s[cg * 8 + j];  // one fp32 rounding
         x[i][j] = f;
         amax = fmaxf(amax, fabsf(f));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
+    }
+  }
+  if (pbm) {  // the block's own column means, then the smoothed values and their amax
+    __shared__ double colsum[RPI][D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double s = 0.0;
+#pragma unroll
+      for (int i = 0; i < RPB; ++i) s += (double)x[i][j];  // rows past N hold 0
+      colsum[rs][cg * 8 + j] = s;
+    }
+    __syncthreads();
+    if (t < D) {
+      double s = 0.0;
+      for (int r = 0; r < RPI; ++r) s += colsum[r][t];
+      const int64_t nv = N - r0 < kQuantBlock ? N - r0 : kQuantBlock;
+      const float m = (float)(s / (double)nv);
+      km_s[t] = m;
+      a.kbmean[(bh * a.nbk + u) * D + t] = m;
+    }
+    __syncthreads();
+    amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPB; ++i) {
+      const bool valid = r0 + rs + i * RPI < N;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = valid ? x[i][j] - km_s[cg * 8 + j] : 0.f;  // one fp32 rounding
+        x[i][j] = f;
+        amax = fmaxf(amax, fabsf(f));
+      }
     }
   }
   amax = block_max256(amax, red);
@@ -210,6 +245,50 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
       for (int o = 1; o < CG; o <<= 1) s += __shfl_xor(s, o);
       int64_t tok = r0 + rs + i * RPI;
       if (cg == 0 && tok < N) a.corr[bh * a.Nq + tok] = (float)s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// per_block_mean score terms: blk_corr[b,h,u,i] = sum_c Q[i,c] * kbmean[b,hk,u,c] in fp32, for the
+// valid key blocks u of the sequence.  grid = (ceil(Nq/64), B*H), block = 256: 64 query rows of one
+// head in LDS as fp32, the block means in chunks of 64; thread (row t%64, block group t/64).
+// ---------------------------------------------------------------------------------------------
+template <int D, int IN>
+__global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a) {
+  __shared__ float sq[64][D + 1];  // +1: rows of the query tile land in distinct banks
+  __shared__ float sm[64][D + 1];
+  const int t = threadIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);
+  const SeqSpan sp = seq_span(a.cu_q, b, a.Nq, a.total_q);
+  const SeqSpan sk = seq_span(a.cu_k, b, a.Nk, a.total_k);
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  if (i0 >= sp.len) return;
+  const int nbk_b = (int)((sk.len + kQuantBlock - 1) / kQuantBlock);
+  const unsigned short* src = a.q + b * a.q_sb + h * a.q_sh + sp.off * a.q_sn;
+  for (int e = t; e < 64 * (D / 8); e += kPrepThreads) {
+    const int r = e / (D / 8), cg = e % (D / 8);
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (i0 + r < sp.len) v = *reinterpret_cast<const u16x8*>(src + (i0 + r) * a.q_sn + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sq[r][cg * 8 + j] = in_to_f32<IN>(v[j]);
+  }
+  const int r = t & 63, ug = t >> 6;
+  for (int u0 = 0; u0 < nbk_b; u0 += 64) {
+    __syncthreads();  // the query tile is in place; the previous chunk's means are consumed
+    for (int e = t; e < 64 * D; e += kPrepThreads) {
+      const int uu = e / D, c = e % D;
+      sm[uu][c] = u0 + uu < nbk_b ? a.kbmean[(bhk * a.nbk + u0 + uu) * D + c] : 0.f;
+    }
+    __syncthreads();
+    for (int k = 0; k < 16; ++k) {
+      const int uu = ug + 4 * k;
+      if (u0 + uu >= nbk_b) break;  // the same for the whole wave
+      float s = 0.f;
+#pragma unroll 16
+      for (int c = 0; c < D; ++c) s = __builtin_fmaf(sq[r][c], sm[uu][c], s);
+      if (i0 + r < sp.len) a.blk_corr[(bh * a.nbk + u0 + uu) * a.Nq + i0 + r] = s;
     }
   }
 }
@@ -391,6 +470,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <int D, int IN>
 static void launch_kmean_t(const QuantArgs& a, double* partial, int nchunk, hipStream_t s) {
+  if (a.kbmean) {  // per_block_mean: the global mean is zero (no chunks summed)
+    k_kmean_final<D><<<(unsigned)(a.B * a.Hkv), D, 0, s>>>(partial, 0, a.Hkv, a.Nk, a.cu_k, a.total_k, a.kmean);
+    return;
+  }
   dim3 g(nchunk, (unsigned)(a.B * a.Hkv));
   k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk,
                                                         a.cu_k, a.total_k);
@@ -402,6 +485,15 @@ hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStre
     a.in_fp16 ? launch_kmean_t<128, 1>(a, partial, nchunk, s) : launch_kmean_t<128, 0>(a, partial, nchunk, s);
   else
     a.in_fp16 ? launch_kmean_t<64, 1>(a, partial, nchunk, s) : launch_kmean_t<64, 0>(a, partial, nchunk, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s) {
+  dim3 g((unsigned)((a.Nq + 63) / 64), (unsigned)(a.B * a.H));
+  if (a.d == 128)
+    a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a) : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a);
+  else
+    a.in_fp16 ? k_block_corr<64, 1><<<g, kPrepThreads, 0, s>>>(a) : k_block_corr<64, 0><<<g, kPrepThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

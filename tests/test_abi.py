@@ -74,7 +74,7 @@ def quant(B=1, H=2, Nq=256, Nk=256, d=64, pad=None, null=None, Hkv=None):
     if null is not None:
         ptrs[null] = 0
     npq = L_pad(Nq) if pad is None else pad
-    return api.QKQuant(*ptrs, B, H, H if Hkv is None else Hkv, Nq, Nk, d, npq, L_pad(Nk))
+    return api.QKQuant(*ptrs, B, H, H if Hkv is None else Hkv, Nq, Nk, d, npq, L_pad(Nk), None, None)
 
 
 def L_pad(n):
@@ -184,6 +184,14 @@ def test_attn_validation(L, case, status):
     elif case == "gqa_hkv_zero":
         qk = quant(Hkv=0)
     assert call_fwd(L, qk, v, **kw) == status
+
+
+def test_per_block_mean_validation(L):
+    qk = quant()
+    qk.k_block_mean = FAKE  # without blk_corr
+    assert call_fwd(L, qk, desc()) == INVALID
+    qk.blk_corr = FAKE  # per_block_mean with an fp32 mask is not offered
+    assert call_fwd(L, qk, desc(), mask=FAKE, mdt=1, mask_h=1) == UNSUPPORTED
 
 
 def test_debug_validation(L):

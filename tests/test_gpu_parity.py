@@ -78,6 +78,46 @@ def test_quantize_bitexact_gqa(orc, B, H, Hkv, Nq, Nk, d):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", [(1, 2, 2, 300, 417, 128), (2, 4, 2, 129, 65, 64), (1, 1, 1, 700, 1000, 128)])
+def test_quantize_per_block_mean(orc, B, H, Hkv, Nq, Nk, d, dtype):
+    """per_block_mean: block means, codes and scales bit-exact; the score terms within fp32
+    accumulation of the oracle's fp64 dot products; the global mean and the LSE shift zero."""
+    say(f"quantize per_block_mean B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype}")
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=9, dtype=dtype)
+    if Hkv != H:
+        inp = gqa_inputs(inp, Hkv)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qk(q, k, per_block_mean=True)
+    torch.cuda.synchronize()
+    c = orc.quant_qk(inp.bits(inp.q), inp.bits(inp.k), dtype=inp.dtype, per_block_mean=True)
+    assert np.array_equal(g.k_block_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32))
+    assert np.array_equal(g.q8.cpu().numpy(), c.q8) and np.array_equal(g.k8.cpu().numpy(), c.k8)
+    assert np.array_equal(g.q_scale.cpu().numpy(), c.qs) and np.array_equal(g.k_scale.cpu().numpy(), c.ks)
+    assert not g.k_mean.any() and not g.lse_corr.any()
+    gc = g.blk_corr.cpu().numpy()
+    scale = np.abs(c.corr_blk).max() + 1e-30
+    assert np.abs(gc - c.corr_blk).max() <= 2e-6 * scale * d ** 0.5
+
+
+def test_per_block_mean_beats_global_mean_on_drifting_keys(orc):
+    """Keys whose channel offsets change every 64 tokens: per-block smoothing is closer to exact
+    attention than smoothing by the global mean (the GPU path against the oracle's exact path)."""
+    B, H, N, d = 1, 2, 512, 128
+    inp = make_inputs(B, H, N, N, d, sigma=2.0, seed=19)
+    g = torch.Generator().manual_seed(4)
+    drift = 6.0 * torch.randn(B, H, N // 64, 1, d, generator=g)
+    k = (inp.k.float().reshape(B, H, N // 64, 64, d) + drift).reshape(B, H, N, d).to(torch.bfloat16)
+    inp = dataclasses.replace(inp, k=k)
+    q, kk, v = to_dev(inp)
+    eo, _ = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v))
+    og = sage.sageattn(q, kk, v).float().cpu().numpy().reshape(-1, d)
+    ob = sage.sageattn(q, kk, v, per_block_mean=True).float().cpu().numpy().reshape(-1, d)
+    eg, eb = rel_l1(og, eo), rel_l1(ob, eo)
+    say(f"  rel-L1 vs exact: global mean {eg:.3e}, per-block mean {eb:.3e}")
+    assert eb < eg and eb < 3e-2
+
+
 def gqa_inputs(inp, Hkv):
     """The same inputs with K and V cut to Hkv heads (every (H/Hkv)-th head)."""
     g = inp.q.shape[1] // Hkv
@@ -188,13 +228,14 @@ def oracle_mask(mask):
     return mask.numpy() if mask.dtype == torch.float32 else mask.numpy().astype(np.uint8)
 
 
-def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None, smooth_v=False):
+def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, layout="HND", rows=None, smooth_v=False,
+             per_block_mean=False):
     q, k, v = to_dev(inp)
     if layout == "NHD":
         q, k, v = (t.permute(0, 2, 1, 3).contiguous() for t in (q, k, v))
     mask_dev = None if mask is None else mask.to(DEV)
     out, lse = sage.sageattn(q, k, v, tensor_layout=layout, is_causal=causal, attn_mask=mask_dev, sm_scale=sm_scale,
-                             return_lse=True, pv_dtype=pv, smooth_v=smooth_v)
+                             return_lse=True, pv_dtype=pv, smooth_v=smooth_v, per_block_mean=per_block_mean)
     torch.cuda.synchronize()
     assert out.dtype == inp.q.dtype  # the output takes the input dtype
     B, H, Nq, d = inp.q.shape
@@ -203,7 +244,8 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     m = oracle_mask(mask)
     r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m,
                    sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv),
-                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype, smooth_v=smooth_v)
+                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype, smooth_v=smooth_v,
+                   per_block_mean=per_block_mean)
     ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m,
                              sm_scale=sm_scale, rows=rows, dtype=inp.dtype)
     got_o = rows_of(out, rows, layout)
@@ -265,6 +307,14 @@ CASES = [
          causal=True, mask="rand_1"),
     dict(name="smooth_v_fp16_in_nhd", B=1, H=3, Nq=200, Nk=129, d=128, dtype="fp16", layout="NHD", smooth_v=True,
          v_bias=100.0),
+    # per_block_mean: K smoothed by each 64-token block's own mean, block score terms added back
+    dict(name="pbm", B=1, H=2, Nq=300, Nk=417, d=128, per_block_mean=True),
+    dict(name="pbm_causal_mask_gqa_d64", B=2, H=4, Hkv=2, Nq=257, Nk=257, d=64, per_block_mean=True, causal=True,
+         mask="rand_1"),
+    dict(name="pbm_fp8_fp16_in", B=1, H=2, Nq=333, Nk=700, d=128, pv="fp8", sigma=8.0, dtype="fp16",
+         per_block_mean=True),
+    dict(name="pbm_smooth_v_nhd", B=1, H=3, Nq=200, Nk=129, d=128, layout="NHD", per_block_mean=True, smooth_v=True,
+         v_bias=30.0),
 ]
 
 
@@ -309,7 +359,8 @@ def test_attention_parity(orc, case):
     mask = case_mask(c, B, H, Nq, Nk)
     got_o, got_l, r, ex_o, ex_l = run_both(orc, inp, pv=c.get("pv", "fp16"), causal=c.get("causal", False), mask=mask,
                                            sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"),
-                                           smooth_v=c.get("smooth_v", False))
+                                           smooth_v=c.get("smooth_v", False),
+                                           per_block_mean=c.get("per_block_mean", False))
     e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype)
     say(f"  rel-L1 vs QE {e1:.3e}")
 
@@ -379,6 +430,9 @@ def test_errors_raise():
     assert ei.value.status == 1
     with pytest.raises(api.SageError) as ei:  # smooth_v belongs to the FP16 PV path
         sage.sageattn(q, k, v, pv_dtype="fp8", smooth_v=True)
+    assert ei.value.status == 2
+    with pytest.raises(api.SageError) as ei:  # per_block_mean is not combined with a float mask
+        sage.sageattn(q, k, v, per_block_mean=True, attn_mask=torch.zeros(1, 1, 64, 64, device=DEV))
     assert ei.value.status == 2
 
 

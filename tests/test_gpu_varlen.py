@@ -42,6 +42,8 @@ CASES = [
     dict(name="gqa_fp8_causal_d64", sq=[200, 65, 256], sk=[200, 65, 256], H=4, Hkv=1, d=64, pv="fp8", sigma=8.0,
          causal=True),
     dict(name="smooth_v_ragged", sq=[70, 1, 130, 300], sk=[90, 5, 130, 0], H=2, d=128, smooth_v=True, v_bias=40.0),
+    dict(name="per_block_mean_ragged_causal", sq=[70, 1, 130, 300], sk=[90, 5, 200, 0], H=4, Hkv=2, d=128,
+         per_block_mean=True, causal=True),
 ]
 
 
@@ -55,12 +57,13 @@ def test_varlen_parity(orc, case):
     if "v_bias" in c:
         inp.v = (inp.v.float() + c["v_bias"]).to(inp.v.dtype)
     sv = c.get("smooth_v", False)
+    pbm = c.get("per_block_mean", False)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
     cq, ck = inp.cu_q.to(DEV), inp.cu_k.to(DEV)
     mq, mk = max(c["sq"]), max(c["sk"])
     out, lse = sage.sageattn_varlen(q, k, v, cq, ck, mq, mk, is_causal=causal, return_lse=True, pv_dtype=pv,
-                                    smooth_v=sv)
-    g = sage.quantize_qk_varlen(q, k, cq, ck, mq, mk)
+                                    smooth_v=sv, per_block_mean=pbm)
+    g = sage.quantize_qk_varlen(q, k, cq, ck, mq, mk, per_block_mean=pbm)
     torch.cuda.synchronize()
     assert out.shape == q.shape and out.dtype == q.dtype and lse.shape == (c["H"], q.shape[0])
     Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
@@ -72,19 +75,25 @@ def test_varlen_parity(orc, case):
         if q1 == q0 or k1 == k0:
             continue
         cq_ = orc.quant_qk(np.ascontiguousarray(Q[q0:q1].transpose(1, 0, 2)[None]),
-                           np.ascontiguousarray(K[k0:k1].transpose(1, 0, 2)[None]), dtype=inp.dtype)
+                           np.ascontiguousarray(K[k0:k1].transpose(1, 0, 2)[None]), dtype=inp.dtype,
+                           per_block_mean=pbm)
         nqp, nkp = cq_.q8.shape[2], cq_.k8.shape[2]
         assert np.array_equal(g.q8[b, :, :nqp].cpu().numpy(), cq_.q8[0]), ("q8", b)
         assert np.array_equal(g.k8[b, :, :nkp].cpu().numpy(), cq_.k8[0]), ("k8", b)
         assert not g.q8[b, :, nqp:].any() and not g.k8[b, :, nkp:].any()
         assert np.array_equal(g.q_scale[b, :, :cq_.qs.shape[2]].cpu().numpy(), cq_.qs[0])
         assert np.array_equal(g.k_scale[b, :, :cq_.ks.shape[2]].cpu().numpy(), cq_.ks[0])
-        assert np.array_equal(g.k_mean[b].cpu().numpy(), cq_.kmean[0])
+        if pbm:
+            nb = cq_.kmean.shape[2]
+            assert np.array_equal(g.k_block_mean[b, :, :nb].cpu().numpy(), cq_.kmean[0])
+            assert np.allclose(g.blk_corr[b, :, :nb, :q1 - q0].cpu().numpy(), cq_.corr_blk[0], rtol=1e-5, atol=1e-4)
+        else:
+            assert np.array_equal(g.k_mean[b].cpu().numpy(), cq_.kmean[0])
     say("  per-sequence quantization bit-exact")
 
     o32, o16, qlse = orc.run_qe_varlen(Q, K, V, cuq, cuk, pv=pv, causal=causal, BN=sage.block_n(pv),
                                        tau=sage.softmax_tau(pv), lsum_rounded=sage.rowsum_rounded(pv),
-                                       dtype=inp.dtype, smooth_v=sv)
+                                       dtype=inp.dtype, smooth_v=sv, per_block_mean=pbm)
     got = out.float().cpu().numpy()
     e1 = rel_l1(got, _dec(o16, inp.dtype))
     say(f"  rel-L1 vs per-sequence emulation {e1:.3e}")
