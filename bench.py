@@ -94,10 +94,11 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     parts = []
     for lo, hi in zip(bounds[:-1], bounds[1:]):  # one slice, or all keys
         Ks, Vs = np.ascontiguousarray(Kb[:, :, lo:hi]), np.ascontiguousarray(Vb[:, :, lo:hi])
-        qk = oracle.quant_qk(Qb, Ks, dtype=w.dtype)
-        vh, vs = oracle.prep_v(Vs, w.pv, dtype=w.dtype)
+        qk = oracle.quant_qk(Qb, Ks, dtype=w.dtype, per_block_mean=w.per_block_mean)
+        vm = oracle.kmean(Vs, w.dtype) if w.smooth_v else None
+        vh, vs = oracle.prep_v(Vs, w.pv, dtype=w.dtype, vmean=vm)
         parts.append(oracle.attn_qe(qk, vh, vs, w.pv, w.Nq, hi - lo, causal=w.causal, mask=inp.mask_u8, BN=64,
-                                    tau=tau, lsum_rounded=lsum_rounded, rows=rows, out_dtype=w.dtype))
+                                    tau=tau, lsum_rounded=lsum_rounded, rows=rows, out_dtype=w.dtype, vmean=vm))
     if S > 1:
         oracle.merge_lse(np.stack([p[0] for p in parts]), np.stack([p[2] for p in parts]))
     dt = time.perf_counter() - t0
@@ -198,6 +199,7 @@ def run_timed(args, w, step, S, out_esize, dev):
         "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": w.Hkv or w.H, "Nq": w.Nq, "Nk": w.Nk,
                    "d": w.d,
                    "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
+                   "smooth_v": w.smooth_v, "per_block_mean": w.per_block_mean,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
                    "gpu_ms_per_step": round(gpu_ms_step, 4),
                    **({"seqlens": list(w.seqlens)} if w.seqlens else {})},
@@ -281,13 +283,15 @@ def main():
     else:
         kv = [(k, v)]
     del k, v
-    qks, qwss, vts, vwss = [], [], [], []
+    qks, qwss, vts, vwss, vms = [], [], [], [], []
     for ks, _ in kv:
         nk = ks.shape[2]
-        qks.append(api.alloc_quantized(w.B, w.H, w.Nq, nk, w.d, dev, Hkv=Hkv, dtype=q.dtype))
+        qks.append(api.alloc_quantized(w.B, w.H, w.Nq, nk, w.d, dev, Hkv=Hkv, dtype=q.dtype,
+                                       per_block_mean=w.per_block_mean))
         qwss.append(api.quantize_workspace(w.B, Hkv, nk, w.d, dev))
         vts.append(api.alloc_prepared_v(w.B, Hkv, nk, w.d, w.pv, dev))
         vwss.append(api.prepare_v_workspace(w.B, Hkv, nk, w.d, w.pv, dev))
+        vms.append(torch.empty(w.B, Hkv, w.d, dtype=torch.float32, device=dev) if w.smooth_v else None)
     mws = api.mask_workspace(w.B, w.Nq, w.Nk, 1 if mask is not None else 0, dev)
     out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=q.dtype, device=dev)
     lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
@@ -300,13 +304,13 @@ def main():
 
     def step(ev=None, mev=None):
         for s, (ks, vs_) in enumerate(kv):
-            api.quantize_qk(q, ks, out=qks[s], workspace=qwss[s])
-            api.prepare_v(vs_, w.pv, out=vts[s], workspace=vwss[s])
+            api.quantize_qk(q, ks, out=qks[s], workspace=qwss[s], per_block_mean=w.per_block_mean)
+            api.prepare_v(vs_, w.pv, out=vts[s], workspace=vwss[s], v_mean=vms[s])
             if ev is not None:
                 ev[s][0].record(stream)
             api.attn_fwd_prepared(qks[s], vts[s][0], vts[s][1], pv_dtype=w.pv, is_causal=w.causal, attn_mask=mask,
                                   return_lse=w.lse or S > 1, out=out if S == 1 else o_parts[s],
-                                  lse=lse if S == 1 else l_parts[s], workspace=mws)
+                                  lse=lse if S == 1 else l_parts[s], workspace=mws, v_mean=vms[s])
             if ev is not None:
                 ev[s][1].record(stream)
         if S > 1:

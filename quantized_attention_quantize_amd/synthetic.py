@@ -49,6 +49,8 @@ class Workload:
     dtype: str = "bf16"  # element type of q, k, v and the output: "bf16" or "fp16"
     kv_splits: int = 1  # > 1: the keys run as this many slices with fp32 partial results, then merged
     seqlens: tuple = ()  # a packed variable-length batch of these sequence lengths (B, Nq, Nk: count, longest)
+    smooth_v: bool = False  # V's channel means subtracted before its FP16 rounding, added back to O
+    per_block_mean: bool = False  # K smoothed by each 64-token block's own mean
 
     @property
     def ops(self) -> float:
@@ -83,6 +85,10 @@ WORKLOADS = {
                            seqlens=(8192, 4096, 2048, 6144, 1024, 3072, 512, 7680),
                            note="packed batch of 8 sequences (8192, 4096, 2048, 6144, 1024, 3072, 512, 7680 tokens; "
                                 "32768 in all), H=32 d=128 fp16, non-causal, INT8 QK + FP16 PV, LSE"),
+    "n8k_smoothv_pbm": Workload("n8k_smoothv_pbm", 2, 32, 8192, 8192, 128, 4.0, pv="fp16", smooth_v=True,
+                                per_block_mean=True,
+                                note="B=2 H=32 N=8192 d=128 bf16, non-causal, INT8 QK with per-block K means + FP16 PV "
+                                     "with smooth_v, LSE"),
     "n8k_fmask": Workload("n8k_fmask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys_f32", pv="fp16",
                           note="B=2 H=32 N=8192 d=128 bf16, float32 additive mask [B,1,N,N]: 0 for keys < N/2, "
                                "-inf beyond, LSE"),

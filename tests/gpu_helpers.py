@@ -103,7 +103,11 @@ def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None,
     grp = H // Kb.shape[1]  # query heads per key head (group-query attention)
     dec = f32_of_bf16_bits if dtype == "bf16" else (lambda b: b.view(np.float16).astype(np.float32))
     Q = dec(Qb).astype(np.float64)
-    Ks = (dec(Kb) - qk.kmean[:, :, None, :]).astype(np.float32).astype(np.float64)
+    if qk.kmean.ndim == 4:  # per_block_mean: each key block smoothed by its own mean
+        m = np.repeat(qk.kmean, 64, axis=2)[:, :, :Kb.shape[2]]
+    else:
+        m = qk.kmean[:, :, None, :]
+    Ks = (dec(Kb) - m).astype(np.float32).astype(np.float64)
     sk = np.abs(Ks).sum(-1)  # [B,Hkv,Nk]
     out = np.empty(rows.size)
     for n, rid in enumerate(rows):

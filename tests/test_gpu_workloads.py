@@ -19,7 +19,7 @@ from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_qu
 pytestmark = pytest.mark.gpu
 
 N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048,
-                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024}
+                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024, "n8k_smoothv_pbm": 2048}
 
 
 @pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits == 1 and not w.seqlens])
@@ -32,10 +32,16 @@ def test_workload_parity(orc, name):
     mask_dev = None if inp.mask is None else inp.mask.to(DEV)
 
     # quantization: whole tensors, bit for bit
-    g = sage.quantize_qk(q, k)
+    g = sage.quantize_qk(q, k, per_block_mean=w.per_block_mean)
     torch.cuda.synchronize()
-    c = orc.quant_qk(Qb, Kb, dtype=inp.dtype)
-    assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32)), "k_mean"
+    c = orc.quant_qk(Qb, Kb, dtype=inp.dtype, per_block_mean=w.per_block_mean)
+    if w.per_block_mean:
+        assert np.array_equal(g.k_block_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32)), "block means"
+        gc = g.blk_corr.cpu().numpy()
+        assert np.abs(gc - c.corr_blk).max() <= 1e-5 * (np.abs(c.corr_blk).max() + 1e-30), "block terms"
+        del gc
+    else:
+        assert np.array_equal(g.k_mean.cpu().numpy().view(np.uint32), c.kmean.view(np.uint32)), "k_mean"
     assert np.array_equal(g.q_scale.cpu().numpy().view(np.uint32), c.qs.view(np.uint32)), "q_scale"
     assert np.array_equal(g.k_scale.cpu().numpy().view(np.uint32), c.ks.view(np.uint32)), "k_scale"
     assert np.array_equal(g.q8.cpu().numpy(), c.q8), "q8"
@@ -44,9 +50,13 @@ def test_workload_parity(orc, name):
     say("  quantization bit-exact")
 
     # prepared V: whole tensor, bit for bit
-    vt, vs = sage.prepare_v(v, w.pv)
+    vmean = torch.empty(w.B, w.Hkv or w.H, w.d, dtype=torch.float32, device=DEV) if w.smooth_v else None
+    vt, vs = sage.prepare_v(v, w.pv, v_mean=vmean)
     torch.cuda.synchronize()
-    vh, vsc = orc.prep_v(Vb, w.pv, dtype=inp.dtype)
+    vm = orc.kmean(Vb, inp.dtype) if w.smooth_v else None
+    vh, vsc = orc.prep_v(Vb, w.pv, dtype=inp.dtype, vmean=vm)
+    if w.smooth_v:
+        assert np.array_equal(vmean.cpu().numpy().view(np.uint32), vm.view(np.uint32)), "V mean"
     got = vt.cpu().numpy()
     nat = unpermute_vt(got.view(np.uint16) if w.pv == "fp16" else got, w.pv)
     assert np.array_equal(nat[:, :, :w.Nk], vh), "prepared V"
@@ -68,7 +78,8 @@ def test_workload_parity(orc, name):
     say("  int32 scores bit-exact")
 
     # attention
-    out, lse = sage.sageattn(q, k, v, is_causal=w.causal, attn_mask=mask_dev, return_lse=True, pv_dtype=w.pv)
+    out, lse = sage.sageattn(q, k, v, is_causal=w.causal, attn_mask=mask_dev, return_lse=True, pv_dtype=w.pv,
+                             smooth_v=w.smooth_v, per_block_mean=w.per_block_mean)
     torch.cuda.synchronize()
     R = w.B * w.H * w.Nq
     n_rand = N_RANDOM_ROWS[name]
@@ -82,7 +93,7 @@ def test_workload_parity(orc, name):
     vh_o, vs_o = (vh, vsc)
     o32, obf, qlse = orc.attn_qe(c, vh_o, vs_o, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8,
                                  BN=sage.block_n(w.pv), tau=sage.softmax_tau(w.pv),
-                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows, out_dtype=inp.dtype)
+                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows, out_dtype=inp.dtype, vmean=vm)
     got_o = rows_of(out, rows)
     got_l = lse_rows(lse, rows)
     assert out.dtype == inp.q.dtype
