@@ -15,6 +15,8 @@
 // Method sources (page title, section): SageAttention docs digest (context7 llms.txt) --
 // "sageattn_qk_int8_pv_fp16_triton" (per-block INT8 Q/K, smooth_k), "sageattn3_blackwell" usage
 // (smoothing by the global token mean), "sageattn_qk_int8_pv_fp8_cuda" (per-channel FP8 V).
+#include <type_traits>
+
 #include "sage_device.h"
 #include "sage_launch.h"
 
@@ -250,45 +252,73 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// per_block_mean score terms: blk_corr[b,h,u,i] = sum_c Q[i,c] * kbmean[b,hk,u,c] in fp32, for the
-// valid key blocks u of the sequence.  grid = (ceil(Nq/64), B*H), block = 256: 64 query rows of one
-// head in LDS as fp32, the block means in chunks of 64; thread (row t%64, block group t/64).
+// per_block_mean score terms: blk_corr[b,h,u,i] = sum_c Q[i,c] * kbmean[b,hk,u,c] for the valid key
+// blocks u of the sequence, on the matrix cores: D (32 blocks x 32 query rows) += M (32 x 16) Q^T
+// (16 x 32) per 16 channels.  Q enters exactly (it is bf16 / fp16 already); each fp32 block mean
+// is split into a sum of input-format parts (bf16: three parts, 24 significant bits; fp16: two
+// parts, 22 bits) -- the rounding residue of a part is exact in fp32 -- so the products are exact
+// and only the fp32 accumulation rounds.  grid = (ceil(Nq/32), B*H), block = 256: four waves,
+// each over every fourth group of 32 key blocks for the same 32 query rows.
 // ---------------------------------------------------------------------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v8f __attribute__((ext_vector_type(8)));
+
 template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a) {
-  __shared__ float sq[64][D + 1];  // +1: rows of the query tile land in distinct banks
-  __shared__ float sm[64][D + 1];
-  const int t = threadIdx.x;
+  using V8 = typename std::conditional<IN == 0, v8bf, v8h>::type;
+  constexpr int NP = IN == 0 ? 3 : 2;  // parts of a mean
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, g = lane >> 5;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);
   const SeqSpan sp = seq_span(a.cu_q, b, a.Nq, a.total_q);
   const SeqSpan sk = seq_span(a.cu_k, b, a.Nk, a.total_k);
-  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int64_t i0 = (int64_t)blockIdx.x * 32;
   if (i0 >= sp.len) return;
   const int nbk_b = (int)((sk.len + kQuantBlock - 1) / kQuantBlock);
-  const unsigned short* src = a.q + b * a.q_sb + h * a.q_sh + sp.off * a.q_sn;
-  for (int e = t; e < 64 * (D / 8); e += kPrepThreads) {
-    const int r = e / (D / 8), cg = e % (D / 8);
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (i0 + r < sp.len) v = *reinterpret_cast<const u16x8*>(src + (i0 + r) * a.q_sn + cg * 8);
+  // B operands: query row i0 + lr, channels 16 kk + 8 g .. + 8
+  const int64_t row = i0 + lr;
+  const bool rv = row < sp.len;
+  const unsigned short* src = a.q + b * a.q_sb + h * a.q_sh + (sp.off + (rv ? row : 0)) * a.q_sn + 8 * g;
+  V8 qb[D / 16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sq[r][cg * 8 + j] = in_to_f32<IN>(v[j]);
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (rv) v = *reinterpret_cast<const u16x8*>(src + 16 * kk);
+    qb[kk] = __builtin_bit_cast(V8, v);
   }
-  const int r = t & 63, ug = t >> 6;
-  for (int u0 = 0; u0 < nbk_b; u0 += 64) {
-    __syncthreads();  // the query tile is in place; the previous chunk's means are consumed
-    for (int e = t; e < 64 * D; e += kPrepThreads) {
-      const int uu = e / D, c = e % D;
-      sm[uu][c] = u0 + uu < nbk_b ? a.kbmean[(bhk * a.nbk + u0 + uu) * D + c] : 0.f;
+  for (int bt = w; bt * 32 < nbk_b; bt += 4) {
+    const int u = bt * 32 + lr;  // A operand: key block u
+    const bool uv = u < nbk_b;
+    const float* mp = a.kbmean + (bhk * a.nbk + (uv ? u : 0)) * D + 8 * g;
+    v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      v8f m = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (uv) {
+        const float4 lo = *reinterpret_cast<const float4*>(mp + 16 * kk);
+        const float4 hi = *reinterpret_cast<const float4*>(mp + 16 * kk + 4);
+        m = v8f{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+      V8 part[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {  // m = part[0] + part[1] (+ part[2]), residues exact in fp32
+        part[p] = __builtin_convertvector(m, V8);  // round to nearest even
+        m = m - __builtin_convertvector(part[p], v8f);
+      }
+#pragma unroll
+      for (int p = NP - 1; p >= 0; --p) {  // smallest part first
+        if constexpr (IN == 0)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(part[p], qb[kk], acc, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(part[p], qb[kk], acc, 0, 0, 0);
+      }
     }
-    __syncthreads();
-    for (int k = 0; k < 16; ++k) {
-      const int uu = ug + 4 * k;
-      if (u0 + uu >= nbk_b) break;  // the same for the whole wave
-      float s = 0.f;
-#pragma unroll 16
-      for (int c = 0; c < D; ++c) s = __builtin_fmaf(sq[r][c], sm[uu][c], s);
-      if (i0 + r < sp.len) a.blk_corr[(bh * a.nbk + u0 + uu) * a.Nq + i0 + r] = s;
+    if (rv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {  // D row (r/4)*8 + 4g + r%4 is key block bt*32 + that
+        const int ub = bt * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (ub < nbk_b) a.blk_corr[(bh * a.nbk + ub) * a.Nq + row] = acc[r];
+      }
     }
   }
 }
@@ -489,7 +519,7 @@ hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStre
 }
 
 hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s) {
-  dim3 g((unsigned)((a.Nq + 63) / 64), (unsigned)(a.B * a.H));
+  dim3 g((unsigned)((a.Nq + 31) / 32), (unsigned)(a.B * a.H));
   if (a.d == 128)
     a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a) : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a);
   else
