@@ -20,6 +20,8 @@ or float32, added to the scaled scores):
 * ``run_qe(...)``                   -- convenience: all the steps above for given rows
 * ``merge_lse(o_parts, lse_parts)`` -- partial results over disjoint key sets -> the result over their union
 * ``run_qe_varlen`` / ``attn_ex_varlen`` -- packed variable-length batches, one sequence at a time
+* FP4 microscaling method (``sage_fp4_oracle.c``): ``f32_to_e2m1``, ``e2m1_to_f32``, ``mx_exp``,
+  ``fp4_quant_qk``, ``fp4_prep_v``, ``fp4_scores``, ``fp4_attn_qe``, ``run_fp4``
 """
 
 from __future__ import annotations
@@ -34,6 +36,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sage_oracle.c")
+_SRC_FP4 = os.path.join(_HERE, "sage_fp4_oracle.c")
 _LIB = os.path.join(_HERE, "libsage_oracle.so")
 QBLK = 64
 
@@ -42,11 +45,12 @@ _lib = None
 
 def build(force: bool = True) -> str:
     """Compile sage_oracle.c into libsage_oracle.so with gcc (OpenMP, no fast-math, no FP contraction)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if (not force and os.path.exists(_LIB)
+            and os.path.getmtime(_LIB) >= max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_FP4))):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
-           "-Wall", "-o", tmp, _SRC, "-lm"]
+           "-Wall", "-o", tmp, _SRC, _SRC_FP4, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -77,8 +81,16 @@ def lib():
                                   P, I, P, i32, P, P]
         L.orc_attn_ex.argtypes = [P, P, P, i32, P, i32, I, i32, f64, I, I, I, I, I, I, P, I, P, P]
         L.orc_merge_lse.argtypes = [P, P, I, I, I, P, P]
+        # FP4 microscaling method (sage_fp4_oracle.c)
+        for name in ("orc_f32_to_e2m1_n", "orc_e2m1_to_f32_n", "orc_mx_exp_n"):
+            getattr(L, name).argtypes = [P, P, I]
+        L.orc_fp4_quant_qk.argtypes = [P, P, i32, i32, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.orc_fp4_prep_v.argtypes = [P, i32, I, I, I, I, P, P]
+        L.orc_fp4_scores.argtypes = [P, P, P, P, P, i32, I, I, I, I, I, I, I, I, I, I, I, P]
+        L.orc_fp4_attn_qe.argtypes = [P, P, P, P, P, i32, P, P, P, i32, f32, I, I, I, I, I, I, I, P, I, P, i32, P, P]
         for name in ("orc_kmean", "orc_block_mean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
-                     "orc_attn_qe", "orc_attn_ex", "orc_merge_lse"):
+                     "orc_attn_qe", "orc_attn_ex", "orc_merge_lse", "orc_f32_to_e2m1_n", "orc_e2m1_to_f32_n",
+                     "orc_mx_exp_n", "orc_fp4_quant_qk", "orc_fp4_prep_v", "orc_fp4_scores", "orc_fp4_attn_qe"):
             getattr(L, name).restype = None
         _lib = L
     return _lib
@@ -405,3 +417,138 @@ def attn_ex_varlen(Q, K, V, cu_q, cu_k, *, causal=False, sm_scale=None, dtype="b
         out[q0:q1] = o.reshape(H, n, d).transpose(1, 0, 2)
         lse[:, q0:q1] = l.reshape(H, n)
     return out, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# FP4 microscaling method (sage_fp4_oracle.c): MX FP4 Q, K (per 32 channels) and V (per 32 tokens),
+# Q smoothed by its 128-token block means (or global mean) with the FP32 correction rows, e4m3 P
+# ---------------------------------------------------------------------------------------------
+MX = 32
+QMBLK = 128
+
+
+def f32_to_e2m1(x):
+    """fp32 -> e2m1 codes (sign in bit 3), nearest with ties to the even code, saturating at 6."""
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint8)
+    lib().orc_f32_to_e2m1_n(_p(x), _p(y), x.size)
+    return y
+
+
+def e2m1_to_f32(x):
+    x = _c(x, np.uint8)
+    y = np.empty(x.shape, np.float32)
+    lib().orc_e2m1_to_f32_n(_p(x), _p(y), x.size)
+    return y
+
+
+def mx_exp(amax):
+    """Shared exponent X of MX blocks with the given largest magnitudes (E8M0 byte = X + 127)."""
+    a = _c(amax, np.float32)
+    y = np.empty(a.shape, np.int32)
+    lib().orc_mx_exp_n(_p(a), _p(y), a.size)
+    return y
+
+
+def mx_dequant(codes, e8, axis):
+    """Dequantized values of MX codes whose E8M0 bytes cover 32 consecutive elements along axis."""
+    v = e2m1_to_f32(codes).astype(np.float64)
+    sc = np.ldexp(1.0, e8.astype(np.int64) - 127)
+    sc = np.repeat(sc, MX, axis=axis)
+    sl = [slice(None)] * v.ndim
+    sl[axis] = slice(0, v.shape[axis])
+    return v * sc[tuple(sl)]
+
+
+@dataclass
+class FP4QK:
+    kmean: np.ndarray     # [B,Hkv,d]
+    qmean: np.ndarray     # [B,H,nqm,d]
+    q4: np.ndarray        # [B,H,Nq,d] e2m1 codes
+    qe: np.ndarray        # [B,H,Nq,d/32] E8M0
+    k4: np.ndarray        # [B,Hkv,Nk,d]
+    ke: np.ndarray        # [B,Hkv,Nk,d/32]
+    qk_corr: np.ndarray   # [B,H,nqm,Nk]
+    lse_corr: np.ndarray  # [B,H,Nq]
+    per_block: bool
+
+
+def fp4_quant_qk(Q, K, dtype="bf16", per_block_mean=True) -> FP4QK:
+    Q = _c(Q, np.uint16)
+    K = _c(K, np.uint16)
+    B, H, Nq, d = Q.shape
+    Hkv, Nk = K.shape[1], K.shape[2]
+    if d % MX or H % Hkv:
+        raise ValueError("d must be a multiple of 32 and Hkv must divide H")
+    nqm = (Nq + QMBLK - 1) // QMBLK if per_block_mean else 1
+    km = kmean(K, dtype)
+    qm = np.empty((B, H, nqm, d), np.float32)
+    q4 = np.empty((B, H, Nq, d), np.uint8)
+    qe = np.empty((B, H, Nq, d // MX), np.uint8)
+    k4 = np.empty((B, Hkv, Nk, d), np.uint8)
+    ke = np.empty((B, Hkv, Nk, d // MX), np.uint8)
+    corr = np.empty((B, H, nqm, Nk), np.float32)
+    lc = np.empty((B, H, Nq), np.float32)
+    lib().orc_fp4_quant_qk(_p(Q), _p(K), _in_fp16(dtype), 1 if per_block_mean else 0, B, H, Hkv, Nq, Nk, d, _p(km),
+                           _p(qm), _p(q4), _p(qe), _p(k4), _p(ke), _p(corr), _p(lc))
+    return FP4QK(km, qm, q4, qe, k4, ke, corr, lc, bool(per_block_mean))
+
+
+def fp4_prep_v(V, dtype="bf16"):
+    """V [B,Hkv,Nk,d] bits -> (v4 [B,Hkv,Nk,d] codes, ve [B,Hkv,ceil(Nk/32),d] E8M0)."""
+    V = _c(V, np.uint16)
+    B, Hkv, Nk, d = V.shape
+    v4 = np.empty((B, Hkv, Nk, d), np.uint8)
+    ve = np.empty((B, Hkv, (Nk + MX - 1) // MX, d), np.uint8)
+    lib().orc_fp4_prep_v(_p(V), _in_fp16(dtype), B, Hkv, Nk, d, _p(v4), _p(ve))
+    return v4, ve
+
+
+def fp4_scores(qk: FP4QK, b, h, row0, nrows, col0, ncols):
+    """Raw scores (before sm_scale) of a window of head (b, h): fp32 [nrows, ncols]."""
+    B, H, Nq, d = qk.q4.shape
+    Hkv, Nk = qk.k4.shape[1], qk.k4.shape[2]
+    out = np.empty((nrows, ncols), np.float32)
+    lib().orc_fp4_scores(_p(qk.q4), _p(qk.qe), _p(qk.k4), _p(qk.ke), _p(qk.qk_corr), 1 if qk.per_block else 0, H, Hkv,
+                         Nq, Nk, d, b, h, row0, nrows, col0, ncols, _p(out))
+    return out
+
+
+def fp4_attn_qe(qk: FP4QK, v4, ve, *, causal=False, sm_scale=None, BN=64, rows=None, out_dtype="bf16"):
+    """Returns (o32 [R,d] fp32, o16 [R,d] output bits, lse [R] fp32) for the requested flattened rows."""
+    B, H, Nq, d = qk.q4.shape
+    Hkv, Nk = qk.k4.shape[1], qk.k4.shape[2]
+    sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
+    if rows is None:
+        R = B * H * Nq
+        rp = None
+    else:
+        rp = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rp.size
+    o32 = np.empty((R, d), np.float32)
+    o16 = np.empty((R, d), np.uint16)
+    lse = np.empty((R,), np.float32)
+    lib().orc_fp4_attn_qe(_p(qk.q4), _p(qk.qe), _p(qk.k4), _p(qk.ke), _p(qk.qk_corr), 1 if qk.per_block else 0,
+                          _p(qk.lse_corr), _p(_c(v4, np.uint8)), _p(_c(ve, np.uint8)), 1 if causal else 0, sm, B, H,
+                          Hkv, Nq, Nk, d, BN, _p(rp), R, _p(o32), 1 if out_dtype == "fp16" else 0, _p(o16), _p(lse))
+    return o32, o16, lse
+
+
+@dataclass
+class FP4Result:
+    qk: FP4QK
+    v4: np.ndarray
+    ve: np.ndarray
+    o32: np.ndarray
+    o16: np.ndarray
+    lse: np.ndarray
+
+
+def run_fp4(Q, K, V, *, causal=False, per_block_mean=True, sm_scale=None, BN=64, rows=None, dtype="bf16",
+            out_dtype=None) -> FP4Result:
+    """All FP4 emulation steps: Q/K smoothing and quantization, V quantization, attention."""
+    qk = fp4_quant_qk(Q, K, dtype=dtype, per_block_mean=per_block_mean)
+    v4, ve = fp4_prep_v(V, dtype)
+    o32, o16, lse = fp4_attn_qe(qk, v4, ve, causal=causal, sm_scale=sm_scale, BN=BN, rows=rows,
+                                out_dtype=out_dtype or dtype)
+    return FP4Result(qk, v4, ve, o32, o16, lse)

@@ -1,0 +1,277 @@
+"""Pins for the oracle's FP4 microscaling method (sage_fp4_oracle.c).
+
+Pages: SageAttention docs digest, "FP4 Attention for Blackwell GPUs" / "sageattn3_blackwell"
+(microscaling FP4 Q, K and V; per_block_mean or global mean); FlashInfer API doc,
+"flashinfer.nvfp4_attention_sm120_fwd" (per-vector 8-bit scales, an FP32 correction row per
+128-token Q block, sm_scale default, optional LSE).  Formats: tests/golden/mx_fp4_format.json
+(the OCP MX specification's FP4 E2M1 / E8M0 parameters).
+
+Each part is pinned against something other than the oracle's own code:
+* e2m1 decoding against the generic minifloat formula evaluated from the published format
+  parameters; encoding against a brute-force nearest search in numpy with the ties-to-even-code
+  rule, saturation and the sign of zero;
+* the shared exponent against the spec's defining property (the block maximum scaled by 2^-X lies
+  in [4, 8)), powers of two and the clamps;
+* smoothing: the Q block means against math.fsum; a constant added to one Q block leaves that
+  block's codes alone and moves only its correction row, by the constant times the smoothed keys;
+* scores: on dyadic inputs whose smoothed parts are exactly representable, the emulated scores
+  equal fp64 Q . (K - kmean) exactly, so the LSE equals exact attention's and O differs only by
+  the e4m3 rounding of P;
+* closed forms: Q = 0 gives the mean of the dequantized V and LSE = ln Nk; one key or causal row 0
+  gives that key's dequantized V;
+* V: its scales run along the tokens (a channel scaled by 2^k moves only that channel's E8M0
+  bytes, by k);
+* GQA equals repeated key/value heads; per_block_mean beats the global mean on Q whose offsets
+  drift between blocks; the error against exact attention stays within the measured FP4 budget.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_attention_quantize_amd.synthetic import make_inputs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mx_fp4_format.json")))
+
+
+def _bits(x, dtype=torch.bfloat16):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _spec_values():
+    """All 16 e2m1 code values from the format parameters (sign, exponent field, mantissa)."""
+    f = GOLD["e2m1"]
+    mb, bias = f["mantissa_bits"], f["exponent_bias"]
+    vals = []
+    for code in range(16):
+        s = (code >> 3) & 1
+        e = (code >> mb) & ((1 << f["exponent_bits"]) - 1)
+        m = code & ((1 << mb) - 1)
+        mag = (m / 2 ** mb) * 2.0 ** (1 - bias) if e == 0 else (1 + m / 2 ** mb) * 2.0 ** (e - bias)
+        vals.append(-mag if s else mag)
+    return np.array(vals)
+
+
+def test_e2m1_decode_matches_the_format_definition(orc):
+    spec = _spec_values()
+    got = orc.e2m1_to_f32(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    assert np.array_equal(got, spec)
+    f = GOLD["e2m1"]
+    mags = np.abs(spec)
+    assert mags.max() == f["max_normal"] and mags[mags > 0].min() == f["min_subnormal"]
+    assert 2.0 ** f["emax"] * 1.5 == f["max_normal"]
+
+
+def _nearest_even(y, table):
+    """numpy brute force: nearest magnitude code, ties to the even code, saturating."""
+    a = np.abs(y.astype(np.float64))[:, None]
+    d = np.abs(a - table[None, :8])
+    best = d.min(1, keepdims=True)
+    cand = (d == best)
+    cand &= (np.arange(8)[None, :] % 2 == 0) | (cand.sum(1, keepdims=True) == 1)
+    idx = cand.argmax(1)
+    return (idx | np.where(np.signbit(y), 8, 0)).astype(np.uint8)
+
+
+def test_e2m1_encode_is_nearest_with_ties_to_even(orc):
+    table = np.abs(_spec_values())
+    rng = np.random.default_rng(0)
+    mids = (table[:7] + table[1:8]) / 2  # every tie point
+    ys = np.concatenate([mids, -mids, table, -table, rng.uniform(-8, 8, 20000), rng.uniform(-0.3, 0.3, 2000),
+                         [6.5, 7.99, 100.0, -1e6, 1e-30, -1e-30, 0.0, -0.0]]).astype(np.float32)
+    got = orc.f32_to_e2m1(ys)
+    assert np.array_equal(got, _nearest_even(ys, table))
+    # ties land on codes with a zero mantissa bit; beyond 6 saturates; tiny negatives keep the sign
+    assert (orc.f32_to_e2m1(mids.astype(np.float32)) % 2 == 0).all()
+    assert orc.f32_to_e2m1(np.float32([7.99, -100.0])).tolist() == [7, 15]
+    assert orc.f32_to_e2m1(np.float32([-0.1, 0.1])).tolist() == [8, 0]
+
+
+def test_mx_shared_exponent_property(orc):
+    rng = np.random.default_rng(1)
+    amax = np.exp2(rng.uniform(-60, 60, 50000)).astype(np.float32)
+    amax = np.concatenate([amax, np.exp2(np.arange(-100, 100)).astype(np.float32)])
+    X = orc.mx_exp(amax).astype(np.float64)
+    scaled = amax.astype(np.float64) * np.exp2(-X)
+    assert ((scaled >= 2.0 ** GOLD["e2m1"]["emax"]) & (scaled < 2.0 ** (GOLD["e2m1"]["emax"] + 1))).all()
+    e = GOLD["e8m0"]
+    assert orc.mx_exp(np.float32([0.0])).tolist() == [e["min_exponent"]]
+    assert orc.mx_exp(np.float32([1e-38, 3e38])).tolist() == [e["min_exponent"], 125]  # clamped; 2^125 * [4, 8)
+
+
+def _mx_roundtrip_ok(x, codes, e8, axis):
+    """|x - deq| <= half the e2m1 spacing at x's binade, or 2^(X+1) where the block saturates."""
+    import oracle
+    deq = oracle.mx_dequant(codes, e8, axis)
+    sc = np.repeat(np.ldexp(1.0, e8.astype(np.int64) - 127), 32, axis=axis)
+    sl = [slice(None)] * x.ndim
+    sl[axis] = slice(0, x.shape[axis])
+    sc = sc[tuple(sl)]
+    y = np.abs(x) / sc
+    half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    bound = np.where(y > 6, y - 6, half) * sc
+    return (np.abs(x - deq) <= bound * (1 + 1e-12)).all()
+
+
+@pytest.mark.parametrize("per_block", [True, False])
+def test_quant_means_codes_and_roundtrip(orc, per_block):
+    B, H, Hkv, Nq, Nk, d = 1, 2, 1, 300, 200, 128
+    inp = make_inputs(B, H, Nq, Nk, d, seed=80, Hkv=Hkv)
+    Q, K = inp.bits(inp.q), inp.bits(inp.k)
+    r = orc.fp4_quant_qk(Q, K, per_block_mean=per_block)
+    Qf, Kf = _f32(Q).astype(np.float64), _f32(K).astype(np.float64)
+    # Q means against math.fsum
+    if per_block:
+        for u, (t0, t1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+            for c in (0, 77, 127):
+                assert r.qmean[0, 1, u, c] == np.float32(math.fsum(Qf[0, 1, t0:t1, c]) / (t1 - t0))
+    else:
+        assert r.qmean.shape == (B, H, 1, d)
+        assert r.qmean[0, 0, 0, 5] == np.float32(math.fsum(Qf[0, 0, :, 5]) / Nq)
+    # smoothed values reconstructed within the MX rounding bound
+    qm = np.repeat(r.qmean, 128, axis=2)[:, :, :Nq] if per_block else r.qmean
+    Qt = (_f32(Q) - qm).astype(np.float64)
+    Kt = (_f32(K) - r.kmean[:, :, None, :]).astype(np.float64)
+    assert _mx_roundtrip_ok(Qt, r.q4, r.qe, 3) and _mx_roundtrip_ok(Kt, r.k4, r.ke, 3)
+    # every block's largest code magnitude is 4 or 6 (the scaled maximum lies in [4, 8))
+    mags = orc.e2m1_to_f32(r.k4).reshape(B, Hkv, Nk, d // 32, 32)
+    assert set(np.unique(np.abs(mags).max(-1))) <= {4.0, 6.0}
+
+
+def test_block_shift_moves_only_its_correction_row(orc):
+    """A dyadic constant added to every token of Q block 1 leaves all codes alone and adds
+    c . Ktilde_j to that block's correction row only."""
+    B, H, N, d = 1, 1, 384, 64
+    rng = np.random.default_rng(2)
+    Qv = np.round(rng.standard_normal((B, H, N, d)) * 8) / 8
+    Kv = np.round(rng.standard_normal((B, H, N, d)) * 8) / 8
+    cvec = np.round(rng.standard_normal(d) * 4) / 4
+    Q2 = Qv.copy()
+    Q2[:, :, 128:256] += cvec
+    Qb, Q2b, Kb = _bits(Qv), _bits(Q2), _bits(Kv)
+    assert np.array_equal(_f32(Q2b), Q2.astype(np.float32))  # the shifted values are still exact in bf16
+    a = orc.fp4_quant_qk(Qb, Kb)
+    b = orc.fp4_quant_qk(Q2b, Kb)
+    assert np.array_equal(a.q4, b.q4) and np.array_equal(a.qe, b.qe)
+    assert np.array_equal(a.qk_corr[:, :, [0, 2]], b.qk_corr[:, :, [0, 2]])
+    Kt = (_f32(Kb) - a.kmean[:, :, None, :]).astype(np.float64)
+    want = a.qk_corr[0, 0, 1].astype(np.float64) + Kt[0, 0] @ cvec
+    np.testing.assert_allclose(b.qk_corr[0, 0, 1], want, rtol=1e-6, atol=1e-5)
+
+
+def _dyadic_case(H=2, Hkv=2, Nq=256, Nk=192, d=64, seed=3):
+    """Q, K, V in bf16 whose smoothed parts are exactly MX-representable: tokens come in +-pairs
+    around per-block (Q) or global (K) constants, each 32-element block holds a 4 or 6 times its
+    power of two, and every sum stays within bf16's 8 significant bits."""
+    rng = np.random.default_rng(seed)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+
+    def tilde(n_pairs, nb, axis_len):
+        e = rng.integers(-3, -1, size=(n_pairs, nb))  # one power of two per block
+        v = rng.choice(mags, size=(n_pairs, nb, 32)) * rng.choice([-1, 1], size=(n_pairs, nb, 32))
+        v[:, :, 0] = rng.choice([4.0, 6.0], size=(n_pairs, nb))
+        half = (v * np.ldexp(1.0, e)[..., None]).reshape(n_pairs, axis_len)
+        return np.stack([half, -half], 1).reshape(2 * n_pairs, axis_len)
+
+    Kt = np.stack([tilde(Nk // 2, d // 32, d) for _ in range(Hkv)])[None]
+    kc = np.round(rng.uniform(-8, 8, (1, Hkv, 1, d)) * 4) / 4
+    Qt = np.stack([tilde(Nq // 2, d // 32, d) for _ in range(H)])[None]
+    qc = np.round(rng.uniform(-4, 4, (1, H, Nq // 128, 1, d)) * 4) / 4
+    Qv = (Qt.reshape(1, H, Nq // 128, 128, d) + qc).reshape(1, H, Nq, d)
+    Kv = Kt + kc
+    # V: per channel, per 32-token block, a power of two times e2m1 magnitudes with a 4 or 6
+    vt = tilde(Nk // 32 * d // 2, 1, 32).reshape(Nk // 32, d, 32)  # [block][channel][token]
+    Vv = np.transpose(vt, (0, 2, 1)).reshape(Nk, d)[None, None].repeat(Hkv, 1)
+    for x in (Qv, Kv, Vv):
+        assert np.array_equal(_f32(_bits(x)), x.astype(np.float32))
+    return _bits(Qv), _bits(Kv), _bits(Vv), Qv, Kv, Vv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_scores_on_representable_inputs(orc, causal):
+    H, Nq, Nk, d = 2, 256, 192, 64
+    Qb, Kb, Vb, Qv, Kv, Vv = _dyadic_case(H=H, Nq=Nq, Nk=Nk, d=d)
+    qk = orc.fp4_quant_qk(Qb, Kb)
+    # the smoothed values are reproduced exactly, so the scores are Q . (K - kmean) exactly
+    assert np.array_equal(qk.kmean[0, :, None, :].astype(np.float64), Kv.mean(2)[0][:, None, :])
+    S = orc.fp4_scores(qk, 0, 1, 0, Nq, 0, Nk)
+    want = (Qv[0, 1] @ (Kv[0, 1] - Kv[0, 1].mean(0)).T).astype(np.float32)
+    assert np.array_equal(S, want)
+    v4, ve = orc.fp4_prep_v(Vb)
+    assert np.array_equal(orc.mx_dequant(v4, ve, 2), Vv)  # V exactly representable as well
+    o32, _, lse = orc.fp4_attn_qe(qk, v4, ve, causal=causal)
+    eo, el = orc.attn_ex(Qb, Kb, Vb, causal=causal)
+    np.testing.assert_allclose(lse, el, rtol=0, atol=2e-5)  # l takes the unquantized p
+    rel = np.abs(o32 - eo).sum() / np.abs(eo).sum()
+    assert rel < 2.5e-2, rel  # only P's e4m3 rounding remains (3 mantissa bits: up to 2^-4 per element)
+
+
+def test_closed_forms(orc):
+    Hkv, N, d = 1, 100, 64
+    inp = make_inputs(1, 1, N, N, d, seed=81)
+    K, V = inp.bits(inp.k), inp.bits(inp.v)
+    v4, ve = orc.fp4_prep_v(V)
+    vdeq = orc.mx_dequant(v4, ve, 2)[0, 0]
+    Q0 = np.zeros((1, 1, N, d), np.uint16)
+    r = orc.run_fp4(Q0, K, V)
+    np.testing.assert_allclose(r.o32, np.broadcast_to(vdeq.mean(0), (N, d)), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(r.lse, np.log(N), rtol=0, atol=1e-6)
+    # causal row 0 sees key 0 only; one key sees itself
+    rc = orc.run_fp4(inp.bits(inp.q), K, V, causal=True)
+    assert np.array_equal(rc.o32[0], vdeq[0].astype(np.float32))
+    r1 = orc.run_fp4(inp.bits(inp.q), np.ascontiguousarray(K[:, :, :1]), np.ascontiguousarray(V[:, :, :1]))
+    v4_1, ve_1 = orc.fp4_prep_v(np.ascontiguousarray(V[:, :, :1]))
+    assert np.array_equal(r1.o32, np.broadcast_to(orc.mx_dequant(v4_1, ve_1, 2)[0, 0, 0], (N, d)).astype(np.float32))
+
+
+def test_v_scales_run_along_tokens(orc):
+    inp = make_inputs(1, 1, 64, 96, 64, seed=82)
+    V = inp.v.float().numpy()
+    v4, ve = orc.fp4_prep_v(_bits(V))
+    V2 = V.copy()
+    V2[..., 5] *= 8.0  # one channel scaled by 2^3
+    v42, ve2 = orc.fp4_prep_v(_bits(V2))
+    assert ve.shape == (1, 1, 3, 64)
+    assert np.array_equal(v4, v42)
+    diff = ve2.astype(int) - ve.astype(int)
+    assert (diff[..., 5] == 3).all() and (np.delete(diff, 5, axis=-1) == 0).all()
+
+
+def test_gqa_equals_repeated_heads(orc):
+    inp = make_inputs(1, 4, 150, 130, 64, seed=83, Hkv=2)
+    Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    r = orc.run_fp4(Q, K, V, causal=True)
+    rr = orc.run_fp4(Q, np.repeat(K, 2, axis=1), np.repeat(V, 2, axis=1), causal=True)
+    assert np.array_equal(r.o32, rr.o32) and np.array_equal(r.lse, rr.lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_error_budget_and_per_block_mean(orc, causal):
+    """Against exact attention: within the measured MX-FP4 budget; on Q whose token offsets
+    change from one 128-token block to the next, per-block means beat the global mean."""
+    B, H, N, d = 1, 2, 512, 128
+    inp = make_inputs(B, H, N, N, d, sigma=4.0, seed=84)
+    Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    r = orc.run_fp4(Q, K, V, causal=causal)
+    eo, el = orc.attn_ex(Q, K, V, causal=causal)
+    rel = np.abs(r.o32 - eo).sum() / np.abs(eo).sum()
+    cos = (r.o32 * eo).sum() / math.sqrt((r.o32.astype(np.float64) ** 2).sum() * (eo ** 2).sum())
+    assert rel < 0.25 and cos > 0.97, (rel, cos)
+    rng = np.random.default_rng(5)
+    drift = np.repeat(rng.standard_normal((1, H, N // 128, 1, d)) * 3, 128, axis=3).reshape(1, H, N, d)
+    Qd = _bits(inp.q.float().numpy() + drift)
+    eo, _ = orc.attn_ex(Qd, K, V, causal=causal)
+    errs = {}
+    for pb in (True, False):
+        o = orc.run_fp4(Qd, K, V, causal=causal, per_block_mean=pb).o32
+        errs[pb] = np.abs(o - eo).sum() / np.abs(eo).sum()
+    assert errs[True] < errs[False], errs
