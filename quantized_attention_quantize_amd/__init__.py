@@ -1,4 +1,4 @@
-"""MI355X-native SageAttention-style quantized attention forward (INT8 QK, FP16/FP8 PV).
+"""MI355X-native SageAttention-style quantized attention forward (INT8 QK, FP16/FP8 PV; MX FP4).
 
 The compute path is a C-ABI shared library of hand-written gfx950 HIP kernels
 (``libsage_mi355x.so``, built from ``csrc/``); this package is a thin ctypes binding over it.
@@ -23,4 +23,11 @@ from .api import (  # noqa: F401
     sageattn,
     sageattn_varlen,
     softmax_tau,
+)
+from .fp4 import (  # noqa: F401
+    QuantizedFP4,
+    attn_fwd_fp4,
+    debug_scores_fp4,
+    quantize_qkv_fp4,
+    sageattn_fp4,
 )

@@ -54,13 +54,24 @@ class QKQuant(ctypes.Structure):
                 ("k_block_mean", ctypes.c_void_p), ("blk_corr", ctypes.c_void_p)]
 
 
+class FP4QKV(ctypes.Structure):
+    """sage_fp4_qkv (include/sage_fp4.h)."""
+    _fields_ = [("q4", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k4", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v4t", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_mean", ctypes.c_void_p), ("q_mean", ctypes.c_void_p), ("qk_corr", ctypes.c_void_p),
+                ("lse_corr", ctypes.c_void_p), ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+                ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("d", ctypes.c_int64), ("Nq_pad", ctypes.c_int64),
+                ("Nk_pad", ctypes.c_int64), ("per_block_mean", ctypes.c_int)]
+
+
 _lib = None
 
 EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_rounded", "sage_quantize_workspace_bytes", "sage_quantize_qk",
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
            "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_quantize_qk_varlen",
            "sage_attn_fwd_varlen", "sage_prepare_v_varlen", "sage_attn_fwd_prepared_varlen", "sage_merge_lse",
-           "sage_debug_qk_int32", "sage_status_string")
+           "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_workspace_bytes",
+           "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores")
 
 
 def lib_path() -> str:
@@ -121,6 +132,17 @@ def load_library():
     L.sage_debug_qk_int32.restype = I
     L.sage_status_string.argtypes = [I]
     L.sage_status_string.restype = ctypes.c_char_p
+    L.sage_fp4_q_blocks.argtypes = [I64, I]
+    L.sage_fp4_q_blocks.restype = I64
+    L.sage_fp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
+    L.sage_fp4_workspace_bytes.restype = SZ
+    D = ctypes.POINTER(QKVDesc)
+    L.sage_fp4_quantize_qkv.argtypes = [D, D, D, ctypes.POINTER(FP4QKV), P, SZ, P]
+    L.sage_fp4_quantize_qkv.restype = I
+    L.sage_fp4_attn_fwd.argtypes = [ctypes.POINTER(FP4QKV), I, F, P, I, I64, I64, I64, P, P]
+    L.sage_fp4_attn_fwd.restype = I
+    L.sage_fp4_debug_scores.argtypes = [ctypes.POINTER(FP4QKV), I64, I64, I64, I64, I64, I64, P, P]
+    L.sage_fp4_debug_scores.restype = I
     _lib = L
     return L
 

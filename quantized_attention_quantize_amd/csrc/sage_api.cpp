@@ -10,6 +10,7 @@
 
 #include <atomic>
 
+#include "sage_fp4.h"
 #include "sage_launch.h"
 #include "sage_mi355x.h"
 
@@ -599,6 +600,169 @@ const char* sage_status_string(sage_status s) {
       return "HIP runtime error";
   }
   return "unknown status";
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// FP4 microscaling method (include/sage_fp4.h)
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kMaxFp4Tokens = (int64_t)1 << 24;
+
+int64_t fp4_q_blocks(int64_t Nq, int per_block) { return per_block ? cdiv(Nq, 128) : 1; }
+
+sage_status check_fp4_qkv(const sage_fp4_qkv* x) {
+  if (!x || !x->q4 || !x->q_scale || !x->k4 || !x->k_scale || !x->v4t || !x->v_scale || !x->k_mean || !x->q_mean ||
+      !x->qk_corr || !x->lse_corr)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x->q4, x->q_scale, x->k4, x->k_scale, x->v4t, x->v_scale, x->k_mean, x->q_mean, x->qk_corr,
+                        x->lse_corr};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (x->B <= 0 || x->H <= 0 || x->Hkv <= 0 || x->Nq <= 0 || x->Nk <= 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (x->H % x->Hkv != 0 || x->B * x->H > 65535) return SAGE_ERR_INVALID_ARGUMENT;
+  if (x->per_block_mean != 0 && x->per_block_mean != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (x->d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (x->Nq > kMaxFp4Tokens || x->Nk > kMaxFp4Tokens) return SAGE_ERR_UNSUPPORTED;
+  if (x->Nq_pad != sage_pad_tokens(x->Nq) || x->Nk_pad != sage_pad_tokens(x->Nk)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (fp4_q_blocks(x->Nq, x->per_block_mean) * x->Nk_pad * 4 >= ((int64_t)1 << 31)) return SAGE_ERR_UNSUPPORTED;
+  return SAGE_OK;
+}
+
+Fp4AttnArgs fp4_attn_args(const sage_fp4_qkv* x) {
+  Fp4AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q4 = x->q4;
+  a.q_sc = x->q_scale;
+  a.k4 = x->k4;
+  a.k_sc = x->k_scale;
+  a.v4t = x->v4t;
+  a.v_sc = x->v_scale;
+  a.qk_corr = x->qk_corr;
+  a.lse_corr = x->lse_corr;
+  a.B = x->B;
+  a.H = x->H;
+  a.Hkv = x->Hkv;
+  a.Nq = x->Nq;
+  a.Nk = x->Nk;
+  a.Nq_pad = x->Nq_pad;
+  a.Nk_pad = x->Nk_pad;
+  a.nqm = (int)fp4_q_blocks(x->Nq, x->per_block_mean);
+  a.per_block = x->per_block_mean;
+  a.nQT = (int)cdiv(x->Nq, kTileRows);
+  a.sm_scale = (float)(1.0 / sqrt((double)x->d));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sage_fp4_q_blocks(int64_t Nq, int per_block_mean) { return Nq <= 0 ? 0 : fp4_q_blocks(Nq, per_block_mean); }
+
+size_t sage_fp4_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  return align256((size_t)fp4_mean_partial_doubles(B, H, Hkv, Nq, Nk, d) * sizeof(double));
+}
+
+sage_status sage_fp4_quantize_qkv(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qkv_desc* v,
+                                  const sage_fp4_qkv* out, void* workspace, size_t workspace_bytes, void* stream) {
+  sage_status s;
+  if ((s = check_desc(q)) != SAGE_OK) return s;
+  if ((s = check_desc(k)) != SAGE_OK) return s;
+  if ((s = check_desc(v)) != SAGE_OK) return s;
+  if (q->B != k->B || k->B != v->B || q->d != k->d || k->d != v->d || k->H != v->H || k->N != v->N ||
+      q->H % k->H != 0 || q->dtype != k->dtype || k->dtype != v->dtype)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_fp4_qkv(out)) != SAGE_OK) return s;
+  if (out->B != q->B || out->H != q->H || out->Hkv != k->H || out->d != q->d || out->Nq != q->N || out->Nk != k->N)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < sage_fp4_workspace_bytes(q->B, q->H, k->H, q->N, k->N, q->d))
+    return SAGE_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGE_OK) return s;
+  Fp4QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const unsigned short*>(q->data);
+  a.k = static_cast<const unsigned short*>(k->data);
+  a.v = static_cast<const unsigned short*>(v->data);
+  a.q_sb = q->stride_b;
+  a.q_sh = q->stride_h;
+  a.q_sn = q->stride_n;
+  a.k_sb = k->stride_b;
+  a.k_sh = k->stride_h;
+  a.k_sn = k->stride_n;
+  a.v_sb = v->stride_b;
+  a.v_sh = v->stride_h;
+  a.v_sn = v->stride_n;
+  a.q4 = out->q4;
+  a.q_sc = out->q_scale;
+  a.k4 = out->k4;
+  a.k_sc = out->k_scale;
+  a.v4t = out->v4t;
+  a.v_sc = out->v_scale;
+  a.k_mean = out->k_mean;
+  a.q_mean = out->q_mean;
+  a.qk_corr = out->qk_corr;
+  a.lse_corr = out->lse_corr;
+  a.B = q->B;
+  a.H = q->H;
+  a.Hkv = k->H;
+  a.Nq = q->N;
+  a.Nk = k->N;
+  a.d = q->d;
+  a.Nq_pad = out->Nq_pad;
+  a.Nk_pad = out->Nk_pad;
+  a.nqm = (int)fp4_q_blocks(q->N, out->per_block_mean);
+  a.per_block = out->per_block_mean;
+  a.in_fp16 = q->dtype == SAGE_FP16;
+  return hip_status(launch_fp4_quant(a, static_cast<double*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_fp4_attn_fwd(const sage_fp4_qkv* qkv, int causal, float sm_scale, void* out, sage_dtype out_dtype,
+                              int64_t out_stride_b, int64_t out_stride_h, int64_t out_stride_n, float* lse,
+                              void* stream) {
+  sage_status s;
+  if ((s = check_fp4_qkv(qkv)) != SAGE_OK) return s;
+  if (!out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SAGE_BF16 && out_dtype != SAGE_FP16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARGUMENT;
+  if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < qkv->d) return SAGE_ERR_INVALID_ARGUMENT;
+  const int64_t oel = out_dtype == SAGE_F32 ? 4 : 8;  // elements per 16 bytes
+  if (!aligned16(out) || (out_stride_b % oel) || (out_stride_h % oel) || (out_stride_n % oel))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_device()) != SAGE_OK) return s;
+  Fp4AttnArgs a = fp4_attn_args(qkv);
+  a.out = out;
+  a.out_kind = out_dtype == SAGE_F32 ? 2 : (out_dtype == SAGE_FP16 ? 1 : 0);
+  a.o_sb = out_stride_b;
+  a.o_sh = out_stride_h;
+  a.o_sn = out_stride_n;
+  a.lse = lse;
+  a.causal = causal ? 1 : 0;
+  if (sm_scale > 0.f && isfinite(sm_scale)) a.sm_scale = sm_scale;
+  return hip_status(launch_fp4_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_fp4_debug_scores(const sage_fp4_qkv* qkv, int64_t b, int64_t h, int64_t row0, int64_t nrows,
+                                  int64_t col0, int64_t ncols, float* out, void* stream) {
+  sage_status s;
+  if ((s = check_fp4_qkv(qkv)) != SAGE_OK) return s;
+  if (!out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (b < 0 || b >= qkv->B || h < 0 || h >= qkv->H) return SAGE_ERR_INVALID_ARGUMENT;
+  if (row0 < 0 || nrows <= 0 || row0 + nrows > qkv->Nq_pad) return SAGE_ERR_INVALID_ARGUMENT;
+  if (col0 < 0 || ncols <= 0 || col0 + ncols > qkv->Nk_pad) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((s = check_device()) != SAGE_OK) return s;
+  Fp4DebugArgs d;
+  d.a = fp4_attn_args(qkv);
+  d.b = b;
+  d.h = h;
+  d.row0 = row0;
+  d.nrows = nrows;
+  d.col0 = col0;
+  d.ncols = ncols;
+  d.out = out;
+  return hip_status(launch_fp4_debug(d, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

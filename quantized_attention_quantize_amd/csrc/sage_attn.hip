@@ -62,8 +62,6 @@ struct TileGeom {
 // modulo 16 only, so a lane's offset inside a segment depends on the segment's parity alone: one
 // per-lane offset register serves every segment of a wave, and the segment and tile offsets are
 // wave-uniform (SGPR soffset).
-typedef __attribute__((address_space(3))) void lds_void_t;
-constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer resource word 3: 32-bit data format
 
 // Offset (relative to its segment's first row) of the global chunk that lane `lane` stores, for a
 // segment of parity `par` of a buffer with ROW_BYTES-byte LDS rows and global row stride gstride.
@@ -126,13 +124,6 @@ struct Stager {
   }
 };
 
-// s_waitcnt with vmcnt = N (other counters untouched): all but this wave's N most recent vector
-// memory operations -- here the direct-to-LDS loads -- have completed
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
-}
 // loads one wave issues for a tile buffer of SEGS 1 KiB segments shared by NW waves
 template <int SEGS, int NW>
 __device__ __forceinline__ int segs_of_wave(int w) {
@@ -172,13 +163,6 @@ __device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32],
 
 __device__ __forceinline__ int key_of(int kb, int r, int g) { return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3); }
 
-// Wave-uniform read-only scalars (k-scales, mask-tile states) are read through the constant
-// address space so they become scalar loads: a vector load here would be counted by vmcnt, whose
-// in-order wait would also drain the in-flight direct-to-LDS prefetches.
-typedef __attribute__((address_space(4))) const float cfloat_t;
-typedef __attribute__((address_space(4))) const int cint_t;
-__device__ __forceinline__ float scalar_ld(const float* p, int i) { return ((cfloat_t*)p)[i]; }
-__device__ __forceinline__ int scalar_ld(const int* p, int i) { return ((cint_t*)p)[i]; }
 
 // P^T fragments of one tile in the PV MFMA's B-operand layout (one 32-row block).
 template <int PV>
@@ -588,30 +572,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
 
-  // workgroup -> (head, q-tile).  Workgroup ids go round-robin over the 8 XCDs (each with its own
-  // L2).  When the key/value heads split evenly, XCD x works through key/value heads x, x+8, ...,
-  // each with all its query heads and q-tiles in a row, so K and V stay in one L2 and heads of
-  // unequal cost (sequences of a packed batch) spread evenly.  Otherwise consecutive logical ids
-  // land on the same XCD.
-  const int total = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, jx = bid >> 3;
-  const int grp = (int)(a.H / a.Hkv);  // query heads per key/value head
-  const int64_t units = a.B * a.Hkv;
   int64_t bh;
   int qt;
-  if (units % 8 == 0 && (int64_t)total == units * grp * a.nQT) {
-    const int per_unit = grp * a.nQT;
-    const int64_t u = xcd + 8 * (int64_t)(jx / per_unit);  // b * Hkv + key/value head
-    const int r = jx % per_unit;
-    bh = (u / a.Hkv) * a.H + (u % a.Hkv) * grp + r / a.nQT;
-    qt = r % a.nQT;
-  } else {
-    const int per = total >> 3, rem = total & 7;
-    const int L = xcd < rem ? xcd * (per + 1) + jx : rem * (per + 1) + (xcd - rem) * per + jx;
-    bh = L / a.nQT;
-    qt = L % a.nQT;
-  }
-  if (a.causal) qt = a.nQT - 1 - qt;
+  map_workgroup(a.B, a.H, a.Hkv, a.nQT, a.causal, bh, qt);
   const int64_t b = bh / a.H, h = bh % a.H;
   const int q0 = qt * kBlockM;
   const int r0w = q0 + w * 32;  // first row of this wave (token counts are < 2^30)

@@ -84,4 +84,51 @@ __device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
     return row * 64 + ((chunk ^ swz64(row)) << 4);
 }
 
+// Direct global -> LDS loads (buffer_load ... lds) take their LDS destination as an address-space-3
+// pointer; buffer resources carry this word 3 (gfx9: 32-bit data format).
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kBufferWord3 = 0x00020000;
+
+// s_waitcnt with vmcnt = N (other counters untouched): all but this wave's N most recent vector
+// memory operations -- here the direct-to-LDS loads -- have completed
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+}
+
+// Wave-uniform read-only scalars (k-scales, mask-tile states) are read through the constant
+// address space so they become scalar loads: a vector load here would be counted by vmcnt, whose
+// in-order wait would also drain the in-flight direct-to-LDS prefetches.
+typedef __attribute__((address_space(4))) const float cfloat_t;
+typedef __attribute__((address_space(4))) const int cint_t;
+__device__ __forceinline__ float scalar_ld(const float* p, int i) { return ((cfloat_t*)p)[i]; }
+__device__ __forceinline__ int scalar_ld(const int* p, int i) { return ((cint_t*)p)[i]; }
+
+// Attention workgroup -> (query head bh = b*H + h, q-tile qt).  Workgroup ids go round-robin over
+// the 8 XCDs (each with its own L2).  When the key/value heads split evenly, XCD x works through
+// key/value heads x, x+8, ..., each with all its query heads and q-tiles in a row, so K and V stay
+// in one L2 and heads of unequal cost (sequences of a packed batch) spread evenly.  Otherwise
+// consecutive logical ids land on the same XCD.  Causal q-tiles run longest first.
+__device__ __forceinline__ void map_workgroup(int64_t B, int64_t H, int64_t Hkv, int nQT, int causal, int64_t& bh,
+                                              int& qt) {
+  const int total = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, jx = bid >> 3;
+  const int grp = (int)(H / Hkv);  // query heads per key/value head
+  const int64_t units = B * Hkv;
+  if (units % 8 == 0 && (int64_t)total == units * grp * nQT) {
+    const int per_unit = grp * nQT;
+    const int64_t u = xcd + 8 * (int64_t)(jx / per_unit);  // b * Hkv + key/value head
+    const int r = jx % per_unit;
+    bh = (u / Hkv) * H + (u % Hkv) * grp + r / nQT;
+    qt = r % nQT;
+  } else {
+    const int per = total >> 3, rem = total & 7;
+    const int L = xcd < rem ? xcd * (per + 1) + jx : rem * (per + 1) + (xcd - rem) * per + jx;
+    bh = L / nQT;
+    qt = L % nQT;
+  }
+  if (causal) qt = nQT - 1 - qt;
+}
+
 }  // namespace sage

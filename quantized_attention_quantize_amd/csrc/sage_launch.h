@@ -114,6 +114,59 @@ struct DebugQKArgs {
   int32_t* out;
 };
 
+// FP4 microscaling method (MX FP4 Q, K, V; e4m3 P).  Layouts (bytes unless noted):
+//   q4  [B][H][Nq_pad][d/2], k4 [B][Hkv][Nk_pad][d/2]: e2m1 pairs, low nibble = even channel
+//   q_sc [B][H][Nq_pad][d/32], k_sc [B][Hkv][Nk_pad][d/32]: E8M0 bytes in lane order -- block
+//        2*cs + g (channels [64 cs + 32 g, +32)) at byte g*(d/64) + cs
+//   v4t [B][Hkv][d][Nk_pad/2]: V transposed, e2m1 pairs along tokens, low nibble = even token
+//   v_sc [B][Hkv][Nk_pad/32][d]: E8M0 of (32-token block, channel 32 db + l) at byte l*(d/32) + db
+//   k_mean fp32 [B][Hkv][d]; q_mean fp32 [B][H][nqm][d]; qk_corr fp32 [B][H][nqm][Nk_pad]
+//   (zero past Nk); lse_corr fp32 [B][H][Nq]
+struct Fp4QuantArgs {
+  const unsigned short* q;
+  const unsigned short* k;
+  const unsigned short* v;
+  int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn;
+  uint8_t* q4;
+  uint8_t* q_sc;
+  uint8_t* k4;
+  uint8_t* k_sc;
+  uint8_t* v4t;
+  uint8_t* v_sc;
+  float* k_mean;
+  float* q_mean;
+  float* qk_corr;
+  float* lse_corr;
+  int64_t B, H, Hkv, Nq, Nk, d, Nq_pad, Nk_pad;
+  int nqm;        // Q smoothing rows: ceil(Nq/128) (per_block) or 1 (global mean)
+  int per_block;  // Q smoothed by its 128-token block means (else by its global mean, in q_mean)
+  int in_fp16;
+};
+
+struct Fp4AttnArgs {
+  const uint8_t* q4;
+  const uint8_t* q_sc;
+  const uint8_t* k4;
+  const uint8_t* k_sc;
+  const uint8_t* v4t;
+  const uint8_t* v_sc;
+  const float* qk_corr;
+  const float* lse_corr;
+  void* out;  // out_kind 0: bf16, 1: fp16, 2: fp32
+  int out_kind;
+  int64_t o_sb, o_sh, o_sn;
+  float* lse;  // nullptr = not requested
+  int64_t B, H, Hkv, Nq, Nk, Nq_pad, Nk_pad;
+  int nqm, per_block, nQT, causal;
+  float sm_scale;
+};
+
+struct Fp4DebugArgs {
+  Fp4AttnArgs a;
+  int64_t b, h, row0, nrows, col0, ncols;
+  float* out;  // [nrows][ncols] raw scores S (before sm_scale)
+};
+
 hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s);
@@ -122,5 +175,14 @@ hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s);
 hipError_t launch_debug_qk(const DebugQKArgs& a, int d, int64_t Nq_pad, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+int64_t token_mean_partial_doubles(int64_t B, int64_t H, int64_t N, int64_t d);
+hipError_t launch_token_mean(const unsigned short* x, int in_fp16, int d, int64_t B, int64_t H, int64_t N, int64_t sb,
+                             int64_t sh, int64_t sn, double* partial, float* mean, hipStream_t s);
+// FP4 method: global means (K; Q when not per-block) need `partial` fp64 workspace of
+// fp4_mean_partial_doubles() doubles
+int64_t fp4_mean_partial_doubles(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d);
+hipError_t launch_fp4_quant(const Fp4QuantArgs& a, double* partial, hipStream_t s);
+hipError_t launch_fp4_attn(const Fp4AttnArgs& a, hipStream_t s);
+hipError_t launch_fp4_debug(const Fp4DebugArgs& a, hipStream_t s);
 
 }  // namespace sage

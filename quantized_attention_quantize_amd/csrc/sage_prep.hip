@@ -518,6 +518,32 @@ hipError_t launch_kmean(const QuantArgs& a, double* partial, int nchunk, hipStre
   return hipGetLastError();
 }
 
+// Per-(b,h,channel) token mean of x [B][H][N][d] (fp64 chunk sums, one rounding to fp32), the same
+// reduction as the K mean; partial holds token_mean_partial_doubles() doubles.
+int64_t token_mean_partial_doubles(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return B * H * ((N + kChunk - 1) / kChunk) * d;
+}
+
+template <int D, int IN>
+static void launch_token_mean_t(const unsigned short* x, int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh,
+                                int64_t sn, double* partial, float* mean, hipStream_t s) {
+  const int nchunk = (int)((N + kChunk - 1) / kChunk);
+  dim3 g(nchunk, (unsigned)(B * H));
+  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(x, H, N, sb, sh, sn, partial, nchunk, nullptr, 0);
+  k_kmean_final<D><<<(unsigned)(B * H), D, 0, s>>>(partial, nchunk, H, N, nullptr, 0, mean);
+}
+
+hipError_t launch_token_mean(const unsigned short* x, int in_fp16, int d, int64_t B, int64_t H, int64_t N, int64_t sb,
+                             int64_t sh, int64_t sn, double* partial, float* mean, hipStream_t s) {
+  if (d == 128)
+    in_fp16 ? launch_token_mean_t<128, 1>(x, B, H, N, sb, sh, sn, partial, mean, s)
+            : launch_token_mean_t<128, 0>(x, B, H, N, sb, sh, sn, partial, mean, s);
+  else
+    in_fp16 ? launch_token_mean_t<64, 1>(x, B, H, N, sb, sh, sn, partial, mean, s)
+            : launch_token_mean_t<64, 0>(x, B, H, N, sb, sh, sn, partial, mean, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s) {
   dim3 g((unsigned)((a.Nq + 31) / 32), (unsigned)(a.B * a.H));
   if (a.d == 128)

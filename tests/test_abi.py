@@ -263,3 +263,51 @@ def test_merge_validation(L, case):
     st = L.sage_merge_lse(a["S"], a["B"], a["H"], a["Nq"], a["d"], a["parts"], a["pdt"], a["lse"], a["out"], a["odt"],
                           a["sb"], a["sh"], a["sn"], None, None)
     assert st == INVALID
+
+
+def _fp4_struct(B=1, H=2, Hkv=2, Nq=300, Nk=200, d=128, pbm=1, ptr=None):
+    p = FAKE if ptr is None else ptr
+    return api.FP4QKV(p, p, p, p, p, p, p, p, p, p, B, H, Hkv, Nq, Nk, d, L_pad(Nq), L_pad(Nk), pbm)
+
+
+def L_pad(n):
+    return (n + 127) // 128 * 128
+
+
+def test_fp4_host_queries(L):
+    assert L.sage_fp4_q_blocks(300, 1) == 3 and L.sage_fp4_q_blocks(300, 0) == 1 and L.sage_fp4_q_blocks(0, 1) == 0
+    # fp64 partial sums of the larger of the Q and K token-mean reductions (256-token chunks)
+    assert L.sage_fp4_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * 32 * 32 * 128 * 8
+    assert L.sage_fp4_workspace_bytes(0, 1, 1, 1, 1, 128) == 0
+
+
+def test_fp4_validation(L):
+    q = desc(B=1, H=2, N=300, d=128)
+    k = desc(B=1, H=2, N=200, d=128)
+    x = _fp4_struct()
+    f = L.sage_fp4_quantize_qkv
+    ws = 1 << 20
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(x), FAKE, 10, None) == WORKSPACE
+    assert f(ctypes.byref(q), ctypes.byref(k), None, ctypes.byref(x), FAKE, ws, None) == INVALID
+    k64 = desc(B=1, H=2, N=200, d=64)
+    assert f(ctypes.byref(q), ctypes.byref(k64), ctypes.byref(k64), ctypes.byref(x), FAKE, ws, None) == INVALID
+    q64 = desc(B=1, H=2, N=300, d=64)
+    x64 = _fp4_struct(d=64)
+    assert f(ctypes.byref(q64), ctypes.byref(k64), ctypes.byref(k64), ctypes.byref(x64), FAKE, ws, None) == UNSUPPORTED
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(_fp4_struct(pbm=2)), FAKE, ws,
+             None) == INVALID
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(_fp4_struct(ptr=FAKE + 8)), FAKE, ws,
+             None) == INVALID  # misaligned buffers
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(_fp4_struct(Nk=201)), FAKE, ws,
+             None) == INVALID  # shape mismatch with k
+    big = _fp4_struct(Nq=1 << 24, Nk=1 << 24)  # correction rows of one head past 2 GiB
+    a = L.sage_fp4_attn_fwd
+    assert a(ctypes.byref(big), 0, 0.0, FAKE, 0, 128, 128, 128, None, None) == UNSUPPORTED
+    assert a(ctypes.byref(x), 0, 0.0, None, 0, 128, 128, 128, None, None) == INVALID
+    assert a(ctypes.byref(x), 0, 0.0, FAKE, 7, 128, 128, 128, None, None) == INVALID  # unknown out dtype
+    assert a(ctypes.byref(x), 0, 0.0, FAKE, 0, 128, 128, 100, None, None) == INVALID  # stride_n < d
+    assert a(ctypes.byref(x), 0, 0.0, FAKE + 2, 0, 128, 128, 128, None, None) == INVALID
+    g = L.sage_fp4_debug_scores
+    assert g(ctypes.byref(x), 0, 2, 0, 10, 0, 10, FAKE, None) == INVALID  # h >= H
+    assert g(ctypes.byref(x), 0, 0, 300, 100, 0, 10, FAKE, None) == INVALID  # past Nq_pad
+    assert g(ctypes.byref(x), 0, 0, 0, 10, 0, 10, None, None) == INVALID
