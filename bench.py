@@ -12,6 +12,10 @@ causal, over the whole step.  ``roofline`` reports the attention kernel alone: i
 ops per launch over its average duration, measured with HIP events recorded on the stream the
 kernel runs on, against the MFMA peak of its own dtypes (INT8 for QK^T, FP16 or FP8 for PV).  ``cpu_baseline`` times the CPU oracle (the
 plain reference implementation used by the tests) on a bounded sample of the same workload.
+
+The FP4 workloads (``fp4_b1h24n4096``, ``n8k_fp4``) time the FP4 microscaling method instead:
+sage_fp4_quantize_qkv (smoothing, MX FP4 Q/K/V, correction rows) -> sage_fp4_attn_fwd, with the
+roofline of k_fp4_attn against the FP4 (QK^T) and FP8 (PV) MFMA peaks.
 """
 
 from __future__ import annotations
@@ -32,12 +36,20 @@ INT8_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA (datasheet, no sparsity); FP8 
 FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 MFMA
 
 
-def mfma_peak(pv: str) -> float:
-    """MFMA ceiling of the attention kernel for its own dtypes: half its counted ops are INT8 QK^T,
-    half are PV in FP16 (or FP8), so the ceiling is the harmonic combination of the two peaks."""
+FP4_PEAK_TOPS = 10100.0  # MI355X dense FP4 MFMA
+FP8_PEAK_TOPS = 5000.0
+
+
+def mfma_peak(pv: str, method: str = "int8") -> float:
+    """MFMA ceiling of the attention kernel for its own dtypes: half its counted ops are QK^T (INT8,
+    or e2m1 for the FP4 method), half are PV (FP16, FP8, or e2m1 x e4m3 at the FP8 rate), so the
+    ceiling is the harmonic combination of the two peaks."""
+    if method == "fp4":
+        return 1.0 / (0.5 / FP4_PEAK_TOPS + 0.5 / FP8_PEAK_TOPS)
     pv_peak = FP16_PEAK_TOPS if pv == "fp16" else INT8_PEAK_TOPS
     return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
 KERNEL_SOURCES = ["quantized_attention_quantize_amd/csrc/sage_attn.hip",
+                  "quantized_attention_quantize_amd/csrc/sage_fp4.hip",
                   "quantized_attention_quantize_amd/csrc/sage_device.h"]
 
 
@@ -76,6 +88,8 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     from quantized_attention_quantize_amd.synthetic import make_inputs
 
     oracle.build(force=False)
+    if w.method == "fp4":  # its emulation dequantizes every product in fp64: about 3x the INT8 cost per pair
+        work_target /= 3.0
     if w.seqlens:  # a packed batch: sample whole heads of its first sequence
         import dataclasses
         w = dataclasses.replace(w, B=1, Nq=w.seqlens[0], Nk=w.seqlens[0], seqlens=())
@@ -88,6 +102,15 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     local = np.linspace(0, w.Nq - 1, per_head).astype(np.int64)
     rows = np.concatenate([h * w.Nq + local for h in range(heads)])
+    if w.method == "fp4":
+        t0 = time.perf_counter()
+        oracle.run_fp4(Qb, Kb, Vb, causal=w.causal, per_block_mean=w.per_block_mean, rows=rows, dtype=w.dtype)
+        dt = time.perf_counter() - t0
+        ops = 4.0 * rows.size * w.Nk * w.d / (2 if w.causal else 1)
+        return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"{heads} head(s) (B=1) of {w.name}: smoothing and MX FP4 quantization of the heads' Q, K "
+                          f"and V, FP4 emulation of {per_head} evenly spaced query rows per head x {w.Nk} keys; "
+                          f"{dt:.2f} s"}
     t0 = time.perf_counter()
     S = w.kv_splits
     bounds = [w.Nk * s // S for s in range(S + 1)]
@@ -147,6 +170,35 @@ def varlen_setup(w, dev):
     return step, 1, out.element_size()
 
 
+def fp4_setup(w, dev):
+    """FP4 microscaling workload: buffers allocated once; step = smoothing and MX FP4 quantization of
+    Q, K, V with the correction rows, then attention."""
+    import torch
+
+    from quantized_attention_quantize_amd import fp4
+    from quantized_attention_quantize_amd.synthetic import workload_inputs
+
+    inp = workload_inputs(w, seed=0)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    del inp
+    Hkv = w.Hkv or w.H
+    qkv = fp4.alloc_fp4(w.B, w.H, Hkv, w.Nq, w.Nk, w.d, dev, per_block_mean=w.per_block_mean, dtype=q.dtype)
+    ws = fp4.fp4_workspace(w.B, w.H, Hkv, w.Nq, w.Nk, w.d, dev)
+    out = torch.empty(w.B, w.H, w.Nq, w.d, dtype=q.dtype, device=dev)
+    lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None, mev=None):
+        fp4.quantize_qkv_fp4(q, k, v, per_block_mean=w.per_block_mean, out=qkv, workspace=ws)
+        if ev is not None:
+            ev[0][0].record(stream)
+        fp4.attn_fwd_fp4(qkv, is_causal=w.causal, return_lse=w.lse, out=out, lse=lse if w.lse else None)
+        if ev is not None:
+            ev[0][1].record(stream)
+
+    return step, 1, out.element_size()
+
+
 def run_timed(args, w, step, S, out_esize, dev):
     """Warm-up, then exactly args.steps timed steps; prints the JSON line.  step(ev, mev) records
     HIP events around each of its S attention launches (ev[s]) and around the merge (mev)."""
@@ -194,20 +246,26 @@ def run_timed(args, w, step, S, out_esize, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8+f8" if w.pv == "fp8" else "i8+f16",
+        "dtype": "fp4+f8" if w.method == "fp4" else ("i8+f8" if w.pv == "fp8" else "i8+f16"),
         "data": "synthetic",
         "config": {"workload": w.name, "desc": w.note, "B": w.B, "H": w.H, "Hkv": w.Hkv or w.H, "Nq": w.Nq, "Nk": w.Nk,
                    "d": w.d,
-                   "causal": w.causal, "mask": w.mask, "pv": w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
+                   "causal": w.causal, "mask": w.mask, "method": w.method,
+                   "pv": "e2m1 V x e4m3 P" if w.method == "fp4" else w.pv, "return_lse": w.lse, "io_dtype": w.dtype,
                    "smooth_v": w.smooth_v, "per_block_mean": w.per_block_mean,
                    "ops_per_step": ops, "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
                    "gpu_ms_per_step": round(gpu_ms_step, 4),
                    **({"seqlens": list(w.seqlens)} if w.seqlens else {})},
-        "roofline": {"kernel": "k_attn_fwd", "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": round(mfma_peak(w.pv), 1), "unit": "TOPS", "frac": round(achieved / mfma_peak(w.pv), 4),
-                     "peak_basis": "dense MFMA: INT8 5000 TOPS for QK^T, " +
-                                   ("FP16 2500 TFLOP/s" if w.pv == "fp16" else "FP8 5000 TFLOP/s") +
-                                   " for PV, each half of the counted ops",
+        "roofline": {"kernel": "k_fp4_attn" if w.method == "fp4" else "k_attn_fwd", "bound": "mfma",
+                     "achieved": round(achieved, 2),
+                     "peak": round(mfma_peak(w.pv, w.method), 1), "unit": "TOPS",
+                     "frac": round(achieved / mfma_peak(w.pv, w.method), 4),
+                     "peak_basis": ("dense MFMA: FP4 10100 TOPS for QK^T (e2m1 x e2m1), FP8 5000 TFLOP/s for PV "
+                                    "(e2m1 V x e4m3 P runs at the FP8 rate), each half of the counted ops"
+                                    if w.method == "fp4" else
+                                    "dense MFMA: INT8 5000 TOPS for QK^T, " +
+                                    ("FP16 2500 TFLOP/s" if w.pv == "fp16" else "FP8 5000 TFLOP/s") +
+                                    " for PV, each half of the counted ops"),
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
                      "min_ms": round(attn_ms[0], 4)},
     }
@@ -221,7 +279,8 @@ def run_timed(args, w, step, S, out_esize, dev):
                                   "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
                                   "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
+        pv = "fp8" if w.method == "fp4" else w.pv
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(pv), sage.rowsum_rounded(pv))
     print(json.dumps(line), flush=True)
 
 
@@ -269,6 +328,8 @@ def main():
     sage.load_library()
     if w.seqlens:
         return run_timed(args, w, *varlen_setup(w, dev), dev)
+    if w.method == "fp4":
+        return run_timed(args, w, *fp4_setup(w, dev), dev)
     inp = workload_inputs(w, seed=0)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     mask = None if inp.mask is None else inp.mask.to(dev)

@@ -50,7 +50,8 @@ class Workload:
     kv_splits: int = 1  # > 1: the keys run as this many slices with fp32 partial results, then merged
     seqlens: tuple = ()  # a packed variable-length batch of these sequence lengths (B, Nq, Nk: count, longest)
     smooth_v: bool = False  # V's channel means subtracted before its FP16 rounding, added back to O
-    per_block_mean: bool = False  # K smoothed by each 64-token block's own mean
+    per_block_mean: bool = False  # INT8: K smoothed by each 64-token block's own mean; FP4: Q by its 128-token blocks'
+    method: str = "int8"  # "int8" (INT8 QK, FP16/FP8 PV) or "fp4" (MX FP4 Q/K/V, e4m3 P)
 
     @property
     def ops(self) -> float:
@@ -89,6 +90,13 @@ WORKLOADS = {
                                 per_block_mean=True,
                                 note="B=2 H=32 N=8192 d=128 bf16, non-causal, INT8 QK with per-block K means + FP16 PV "
                                      "with smooth_v, LSE"),
+    "fp4_b1h24n4096": Workload("fp4_b1h24n4096", 1, 24, 4096, 4096, 128, 4.0, lse=False, per_block_mean=True,
+                               method="fp4",
+                               note="B=1 H=24 N=4096 d=128 bf16, non-causal, MX FP4 Q/K/V (Q smoothed by 128-token "
+                                    "block means) + e4m3 P, bf16 out"),
+    "n8k_fp4": Workload("n8k_fp4", 2, 32, 8192, 8192, 128, 4.0, per_block_mean=True, method="fp4",
+                        note="B=2 H=32 N=8192 d=128 bf16, non-causal, MX FP4 Q/K/V (Q smoothed by 128-token block "
+                             "means) + e4m3 P, bf16 out + fp32 LSE"),
     "n8k_fmask": Workload("n8k_fmask", 2, 32, 8192, 8192, 128, 4.0, mask="half_keys_f32", pv="fp16",
                           note="B=2 H=32 N=8192 d=128 bf16, float32 additive mask [B,1,N,N]: 0 for keys < N/2, "
                                "-inf beyond, LSE"),

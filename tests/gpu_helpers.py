@@ -126,3 +126,52 @@ def lse_quant_bound(qk, Qb, Kb, rows, Nq, Nk, sm_scale, causal=False, mask=None,
             valid &= (mrow != -np.inf) if mask.dtype == np.float32 else (mrow != 0)
         out[n] = bnd[valid].max() if valid.any() else 0.0
     return out
+
+
+# ---- FP4 microscaling method: undoing the documented packing and lane order of sage_fp4_qkv ----
+def fp4_nibbles(b: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] pairs -> codes [..., 2n] (low nibble first)."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def fp4_qk_scales(sc: np.ndarray) -> np.ndarray:
+    """lane-order scale bytes [..., d/32] -> logical blocks: block k sits at (k & 1) * (d/64) + k // 2."""
+    nb = sc.shape[-1]
+    pos = [(k & 1) * (nb // 2) + k // 2 for k in range(nb)]
+    return sc[..., pos]
+
+
+def fp4_v_scales(sc: np.ndarray, d: int) -> np.ndarray:
+    """[..., nkb, d] lane order -> logical channel order: channel c at (c % 32) * (d/32) + c // 32."""
+    pos = [(c % 32) * (d // 32) + c // 32 for c in range(d)]
+    return sc[..., pos]
+
+
+def fp4_check_quant(g, r, Nq, Nk, vq=None, kt_max=1.0):
+    """GPU packed buffers against the oracle's FP4QK (r) and V codes (vq = (v4, ve)); kt_max bounds
+    |K - kmean| (for the correction rows' fp32 accumulation bound)."""
+    q4 = fp4_nibbles(g.q4.cpu().numpy())
+    k4 = fp4_nibbles(g.k4.cpu().numpy())
+    assert np.array_equal(g.k_mean.cpu().numpy(), r.kmean), "k_mean"
+    assert np.array_equal(g.q_mean.cpu().numpy(), r.qmean), "q_mean"
+    assert np.array_equal(q4[:, :, :Nq], r.q4), "q codes"
+    assert np.array_equal(k4[:, :, :Nk], r.k4), "k codes"
+    assert not q4[:, :, Nq:].any() and not k4[:, :, Nk:].any(), "pad rows"
+    assert np.array_equal(fp4_qk_scales(g.q_scale.cpu().numpy())[:, :, :Nq], r.qe), "q scales"
+    assert np.array_equal(fp4_qk_scales(g.k_scale.cpu().numpy())[:, :, :Nk], r.ke), "k scales"
+    np.testing.assert_allclose(g.lse_corr.cpu().numpy(), r.lse_corr, rtol=2e-6, atol=2e-6)
+    corr = g.qk_corr.cpu().numpy()
+    # fp32 sums of exact products: error well inside 1e-5 of sum_c |qmean_c| |Ktilde_jc|
+    bound = np.abs(r.qmean).max() * kt_max * r.qmean.shape[-1]
+    np.testing.assert_allclose(corr[..., :Nk], r.qk_corr, rtol=0, atol=1e-5 * bound + 1e-30)
+    assert not corr[..., Nk:].any()
+    if vq is not None:
+        v4, ve = vq
+        vt = fp4_nibbles(g.v4t.cpu().numpy())  # [B, Hkv, d, Nk_pad]
+        assert np.array_equal(np.swapaxes(vt, -1, -2)[:, :, :Nk], v4), "v codes"
+        assert not vt[..., Nk:].any()
+        nkb = ve.shape[2]
+        assert np.array_equal(fp4_v_scales(g.v_scale.cpu().numpy(), v4.shape[-1])[:, :, :nkb], ve), "v scales"

@@ -17,7 +17,8 @@ import torch
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd.synthetic import make_inputs
 
-from gpu_helpers import DEV, assert_lse_close, cosine, f32_of_bf16_bits, rel_l1, say, to_dev
+from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, fp4_check_quant, rel_l1, say,
+                         to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,60 +29,12 @@ def _lib():
     sage.load_library()
 
 
-def _nibbles(b: np.ndarray) -> np.ndarray:
-    """uint8 [..., n] pairs -> codes [..., 2n] (low nibble first)."""
-    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
-    out[..., 0::2] = b & 15
-    out[..., 1::2] = b >> 4
-    return out
-
-
-def _qk_scales(sc: np.ndarray) -> np.ndarray:
-    """lane-order scale bytes [..., d/32] -> logical blocks: block k sits at (k & 1) * (d/64) + k // 2."""
-    nb = sc.shape[-1]
-    pos = [(k & 1) * (nb // 2) + k // 2 for k in range(nb)]
-    return sc[..., pos]
-
-
-def _v_scales(sc: np.ndarray, d: int) -> np.ndarray:
-    """[..., nkb, d] lane order -> logical channel order: channel c at (c % 32) * (d/32) + c // 32."""
-    pos = [(c % 32) * (d // 32) + c // 32 for c in range(d)]
-    return sc[..., pos]
-
-
 def _dec(bits, dtype):
     return f32_of_bf16_bits(bits) if dtype == "bf16" else bits.view(np.float16).astype(np.float32)
 
 
 def _out_f32(out: torch.Tensor) -> np.ndarray:
     return out.float().cpu().numpy()
-
-
-def _check_quant(orc, g, r, Nq, Nk, vq=None, kt_max=1.0):
-    """GPU packed buffers against the oracle's FP4QK (r) and V codes (vq = (v4, ve)); kt_max bounds
-    |K - kmean| (for the correction rows' fp32 accumulation bound)."""
-    q4 = _nibbles(g.q4.cpu().numpy())
-    k4 = _nibbles(g.k4.cpu().numpy())
-    assert np.array_equal(g.k_mean.cpu().numpy(), r.kmean), "k_mean"
-    assert np.array_equal(g.q_mean.cpu().numpy(), r.qmean), "q_mean"
-    assert np.array_equal(q4[:, :, :Nq], r.q4), "q codes"
-    assert np.array_equal(k4[:, :, :Nk], r.k4), "k codes"
-    assert not q4[:, :, Nq:].any() and not k4[:, :, Nk:].any(), "pad rows"
-    assert np.array_equal(_qk_scales(g.q_scale.cpu().numpy())[:, :, :Nq], r.qe), "q scales"
-    assert np.array_equal(_qk_scales(g.k_scale.cpu().numpy())[:, :, :Nk], r.ke), "k scales"
-    np.testing.assert_allclose(g.lse_corr.cpu().numpy(), r.lse_corr, rtol=2e-6, atol=2e-6)
-    corr = g.qk_corr.cpu().numpy()
-    # fp32 sums of exact products: error well inside 1e-5 of sum_c |qmean_c| |Ktilde_jc|
-    bound = np.abs(r.qmean).max() * kt_max * r.qmean.shape[-1]
-    np.testing.assert_allclose(corr[..., :Nk], r.qk_corr, rtol=0, atol=1e-5 * bound + 1e-30)
-    assert not corr[..., Nk:].any()
-    if vq is not None:
-        v4, ve = vq
-        vt = _nibbles(g.v4t.cpu().numpy())  # [B, Hkv, d, Nk_pad]
-        assert np.array_equal(np.swapaxes(vt, -1, -2)[:, :, :Nk], v4), "v codes"
-        assert not vt[..., Nk:].any()
-        nkb = ve.shape[2]
-        assert np.array_equal(_v_scales(g.v_scale.cpu().numpy(), v4.shape[-1])[:, :, :nkb], ve), "v scales"
 
 
 CASES = [
@@ -116,7 +69,7 @@ def test_fp4_parity(orc, case):
     v4, ve = orc.fp4_prep_v(V, dts)
     Kf = _dec(K, dts)
     kt_max = float(np.abs(Kf - r.kmean[:, :, None, :]).max())
-    _check_quant(orc, g, r, Nq, Nk, (v4, ve), kt_max)
+    fp4_check_quant(g, r, Nq, Nk, (v4, ve), kt_max)
     say("  quantization bit-exact")
     out_dt = c.get("out") or tdt
     ods = {torch.float32: "bf16", torch.bfloat16: "bf16", torch.float16: "fp16"}[out_dt]

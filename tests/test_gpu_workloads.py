@@ -13,16 +13,18 @@ import torch
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd.synthetic import WORKLOADS, make_varlen_inputs, workload_inputs
 
-from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, lse_quant_bound, lse_rows, rel_l1, rows_of,
-                         say, to_dev, unpermute_vt)
+from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, fp4_check_quant, lse_quant_bound, lse_rows,
+                         rel_l1, rows_of, say, to_dev, unpermute_vt)
 
 pytestmark = pytest.mark.gpu
 
 N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048,
-                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024, "n8k_smoothv_pbm": 2048}
+                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024, "n8k_smoothv_pbm": 2048,
+                 "fp4_b1h24n4096": 2048, "n8k_fp4": 2048}
 
 
-@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.kv_splits == 1 and not w.seqlens])
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items()
+                                  if w.kv_splits == 1 and not w.seqlens and w.method == "int8"])
 def test_workload_parity(orc, name):
     w = WORKLOADS[name]
     say(f"workload {name}: {w.note}")
@@ -226,3 +228,41 @@ def test_varlen_workload_parity(orc, name):
     e_qe = rel_l1(np.concatenate(got_all), np.concatenate(want_all))
     say(f"  rel-L1 vs per-sequence emulation {e_qe:.3e}")
     assert e_qe <= 1e-3
+
+
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.method == "fp4"])
+def test_fp4_workload_parity(orc, name):
+    """FP4 microscaling workloads at full size: means, codes and scales of Q, K and V bit for bit over
+    the whole tensors, the correction rows and LSE shift within fp32 accumulation error; O and LSE on
+    sampled rows against the FP4 emulation (rel-L1 1e-3, LSE 1e-3) and exact attention (the MX-FP4
+    budget: cosine >= 0.97, rel-L1 <= 0.25)."""
+    w = WORKLOADS[name]
+    say(f"workload {name}: {w.note}")
+    inp = workload_inputs(w, seed=0)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qkv_fp4(q, k, v, per_block_mean=w.per_block_mean)
+    out, lse = sage.attn_fwd_fp4(g, is_causal=w.causal, return_lse=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    r = orc.fp4_quant_qk(Qb, Kb, dtype=w.dtype, per_block_mean=w.per_block_mean)
+    v4, ve = orc.fp4_prep_v(Vb, w.dtype)
+    kt_max = float(np.abs(f32_of_bf16_bits(Kb) - r.kmean[:, :, None, :]).max())
+    fp4_check_quant(g, r, w.Nq, w.Nk, (v4, ve), kt_max)
+    say("  quantization bit-exact over the whole tensors")
+    del g
+    rng = np.random.default_rng(7)
+    R = w.B * w.H * w.Nq
+    edge = np.concatenate([np.arange(64), np.arange(w.Nq - 64, w.Nq), (w.B * w.H - 1) * w.Nq + np.arange(64),
+                           R - 64 + np.arange(64)])
+    rows = np.unique(np.concatenate([rng.choice(R, N_RANDOM_ROWS[name], replace=False), edge]))
+    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=w.causal, rows=rows, out_dtype=w.dtype)
+    got = rows_of(out, rows)
+    e1 = rel_l1(got, f32_of_bf16_bits(o16))
+    say(f"  {rows.size} rows: rel-L1 vs emulation {e1:.3e}")
+    assert e1 <= 1e-3
+    assert_lse_close(lse_rows(lse, rows), qlse, 1e-3)
+    eo, _ = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, rows=rows, dtype=w.dtype)
+    cs, rl = cosine(got, eo), rel_l1(got, eo)
+    say(f"  vs exact: cosine {cs:.5f} rel-L1 {rl:.3e}")
+    assert cs >= 0.97 and rl <= 0.25
