@@ -87,7 +87,8 @@ def lib():
         L.orc_fp4_quant_qk.argtypes = [P, P, i32, i32, I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         L.orc_fp4_prep_v.argtypes = [P, i32, I, I, I, I, P, P]
         L.orc_fp4_scores.argtypes = [P, P, P, P, P, i32, I, I, I, I, I, I, I, I, I, I, I, P]
-        L.orc_fp4_attn_qe.argtypes = [P, P, P, P, P, i32, P, P, P, i32, f32, I, I, I, I, I, I, I, P, I, P, i32, P, P]
+        L.orc_fp4_attn_qe.argtypes = [P, P, P, P, P, i32, P, P, P, i32, f32, I, I, I, I, I, I, I, f64, P, I, P, i32, P,
+                                      P]
         for name in ("orc_kmean", "orc_block_mean", "orc_quant_qk", "orc_prep_v_fp16", "orc_prep_v_fp8", "orc_scores",
                      "orc_attn_qe", "orc_attn_ex", "orc_merge_lse", "orc_f32_to_e2m1_n", "orc_e2m1_to_f32_n",
                      "orc_mx_exp_n", "orc_fp4_quant_qk", "orc_fp4_prep_v", "orc_fp4_scores", "orc_fp4_attn_qe"):
@@ -514,8 +515,12 @@ def fp4_scores(qk: FP4QK, b, h, row0, nrows, col0, ncols):
     return out
 
 
-def fp4_attn_qe(qk: FP4QK, v4, ve, *, causal=False, sm_scale=None, BN=64, rows=None, out_dtype="bf16"):
-    """Returns (o32 [R,d] fp32, o16 [R,d] output bits, lse [R] fp32) for the requested flattened rows."""
+def fp4_attn_qe(qk: FP4QK, v4, ve, *, causal=False, sm_scale=None, BN=64, tau=0, rows=None, out_dtype="bf16"):
+    """Returns (o32 [R,d] fp32, o16 [R,d] output bits, lse [R] fp32) for the requested flattened rows.
+    tau: whole log2 units by which a tile's maximum must exceed the reference maximum to move it
+    (0: the exact running maximum); P is e4m3(448 * 2^-tau * p)."""
+    if int(tau) != tau or tau < 0:
+        raise ValueError("tau must be a non-negative whole number")
     B, H, Nq, d = qk.q4.shape
     Hkv, Nk = qk.k4.shape[1], qk.k4.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))
@@ -530,7 +535,8 @@ def fp4_attn_qe(qk: FP4QK, v4, ve, *, causal=False, sm_scale=None, BN=64, rows=N
     lse = np.empty((R,), np.float32)
     lib().orc_fp4_attn_qe(_p(qk.q4), _p(qk.qe), _p(qk.k4), _p(qk.ke), _p(qk.qk_corr), 1 if qk.per_block else 0,
                           _p(qk.lse_corr), _p(_c(v4, np.uint8)), _p(_c(ve, np.uint8)), 1 if causal else 0, sm, B, H,
-                          Hkv, Nq, Nk, d, BN, _p(rp), R, _p(o32), 1 if out_dtype == "fp16" else 0, _p(o16), _p(lse))
+                          Hkv, Nq, Nk, d, BN, float(tau), _p(rp), R, _p(o32), 1 if out_dtype == "fp16" else 0,
+                          _p(o16), _p(lse))
     return o32, o16, lse
 
 
@@ -544,11 +550,11 @@ class FP4Result:
     lse: np.ndarray
 
 
-def run_fp4(Q, K, V, *, causal=False, per_block_mean=True, sm_scale=None, BN=64, rows=None, dtype="bf16",
+def run_fp4(Q, K, V, *, causal=False, per_block_mean=True, sm_scale=None, BN=64, tau=0, rows=None, dtype="bf16",
             out_dtype=None) -> FP4Result:
     """All FP4 emulation steps: Q/K smoothing and quantization, V quantization, attention."""
     qk = fp4_quant_qk(Q, K, dtype=dtype, per_block_mean=per_block_mean)
     v4, ve = fp4_prep_v(V, dtype)
-    o32, o16, lse = fp4_attn_qe(qk, v4, ve, causal=causal, sm_scale=sm_scale, BN=BN, rows=rows,
+    o32, o16, lse = fp4_attn_qe(qk, v4, ve, causal=causal, sm_scale=sm_scale, BN=BN, tau=tau, rows=rows,
                                 out_dtype=out_dtype or dtype)
     return FP4Result(qk, v4, ve, o32, o16, lse)

@@ -31,8 +31,11 @@
  *    mean (fp64 sums over the valid tokens, one rounding to fp32); the subtracted part's scores,
  *    qk_corr[u][j] = qmean_u . Ktilde_j with Ktilde = fp32(K - kmean), are computed in fp64 from
  *    the unquantized values, rounded to fp32 and added to every score of block u's rows;
- *  - P is not named among the FP4 tensors: it is quantized as in the FP8 PV method, e4m3(448 p)
- *    under the exact running maximum (tau = 0), with l summing the unquantized fp32 p;
+ *  - P is not named among the FP4 tensors: it is quantized to e4m3 as in the FP8 PV method, with
+ *    the online schedule a parameter: over key tiles of BN keys the reference maximum m moves only
+ *    when a tile's maximum exceeds it by more than tau log2 units (tau = 0: the exact running
+ *    maximum), p = exp(s - m) <= 2^tau, and P = e4m3(448 * 2^-tau * p) keeps P <= 448; l sums the
+ *    unquantized fp32 p.  The normalized result does not depend on tau, only where P is rounded;
  *  - scores are S_ij = fp32(sum_c deq(q)_ic deq(k)_jc + qk_corr) with the sum in fp64 (every
  *    product of two dequantized values is exact), then s = S * sm_scale in fp32.
  *
@@ -240,16 +243,19 @@ void orc_fp4_scores(const uint8_t* q4, const uint8_t* qe, const uint8_t* k4, con
 
 /* ------------------------------------------------------------------------------------------ */
 /* FP4 quantized attention forward (the emulation the GPU path must reproduce).              */
-/* Key tiles of BN keys in increasing order; exact running maximum m; per tile                */
-/* p = exp(s - m) in fp32, Phat = e4m3(448 p), l = alpha l + sum p, o = alpha o + Phat . Vdeq. */
-/* O = o / (448 l); LSE = m + ln l + sm_scale * lse_corr.  A row with no visible key: 0, -inf. */
+/* Key tiles of BN keys in increasing order; reference maximum m, moved to the running maximum */
+/* when a tile's maximum exceeds it by more than tau log2 units; per tile p = exp(s - m) in     */
+/* fp32, Phat = e4m3(ps * p) with ps = 448 * 2^-tau, l = alpha l + sum p,                      */
+/* o = alpha o + Phat . Vdeq.  O = o / (ps l); LSE = m + ln l + sm_scale * lse_corr.           */
+/* A row with no visible key: 0, -inf.                                                         */
 /* rows: flattened (b*H + h)*Nq + i, or NULL for all.  Outputs as orc_attn_qe.               */
 /* ------------------------------------------------------------------------------------------ */
 void orc_fp4_attn_qe(const uint8_t* q4, const uint8_t* qe, const uint8_t* k4, const uint8_t* ke,
                      const float* qk_corr, int per_block, const float* lse_corr, const uint8_t* v4, const uint8_t* ve,
                      int causal, float sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
-                     int64_t BN, const int64_t* rows, int64_t nrows, float* o32, int out_fp16, uint16_t* o16,
-                     float* lse) {
+                     int64_t BN, double tau, const int64_t* rows, int64_t nrows, float* o32, int out_fp16,
+                     uint16_t* o16, float* lse) {
+  const float ps = (float)ldexp(448.0, -(int)tau); /* tau is a whole number of log2 units */
   const int64_t nqm = per_block ? (Nq + ORC_QMBLK - 1) / ORC_QMBLK : 1, nb = d / ORC_MX;
   const int64_t nkb = (Nk + ORC_MX - 1) / ORC_MX;
   if (rows == NULL) nrows = B * H * Nq;
@@ -277,12 +283,13 @@ void orc_fp4_attn_qe(const uint8_t* q4, const uint8_t* qe, const uint8_t* k4, co
           s[j - j0] = s[j - j0] * sm_scale;
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
-        float mnew = m > tmax ? m : tmax;
+        float mnew = m;
+        if (m == -INFINITY || (double)tmax > (double)m + tau * M_LN2) mnew = m > tmax ? m : tmax;
         float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mnew));
         float psum = 0.0f;
         for (int64_t j = j0; j < j1; ++j) {
           float p = (float)exp((double)(s[j - j0] - mnew));
-          pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(448.0f * p));
+          pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(ps * p));
           psum += p;
         }
         l = alpha * l + psum;
@@ -295,7 +302,7 @@ void orc_fp4_attn_qe(const uint8_t* q4, const uint8_t* qe, const uint8_t* k4, co
         m = mnew;
       }
       for (int64_t c = 0; c < d; ++c) {
-        float out = l == 0.0f ? 0.0f : (float)((double)o[c] / (448.0 * (double)l));
+        float out = l == 0.0f ? 0.0f : (float)((double)o[c] / ((double)ps * (double)l));
         if (o32) o32[r * d + c] = out;
         if (o16) o16[r * d + c] = out_fp16 ? orc_f32_to_f16(out) : orc_f32_to_bf16(out);
       }

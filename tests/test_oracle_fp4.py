@@ -275,3 +275,27 @@ def test_error_budget_and_per_block_mean(orc, causal):
         o = orc.run_fp4(Qd, K, V, causal=causal, per_block_mean=pb).o32
         errs[pb] = np.abs(o - eo).sum() / np.abs(eo).sum()
     assert errs[True] < errs[False], errs
+
+
+def test_lazy_maximum_only_moves_rounding(orc):
+    """The reference maximum moving only by more than tau log2 units changes where P is rounded,
+    not what is normalized: tau = 0 and tau = 2 agree within e4m3's rounding of P, the LSE agrees
+    to fp32 rounding (l sums the unquantized p), and tau = 0 is the exact running maximum."""
+    inp = make_inputs(1, 2, 300, 520, 128, seed=85)
+    Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    a = orc.run_fp4(Q, K, V, causal=True, tau=0)
+    b = orc.run_fp4(Q, K, V, causal=True, tau=2)
+    np.testing.assert_allclose(b.lse, a.lse, rtol=0, atol=2e-5)
+    rel = np.abs(b.o32 - a.o32).sum() / np.abs(a.o32).sum()
+    assert 0 < rel < 2e-2, rel  # the two schedules round P at different points
+    eo, _ = orc.attn_ex(Q, K, V, causal=True)
+    ea = np.abs(a.o32 - eo).sum() / np.abs(eo).sum()
+    eb = np.abs(b.o32 - eo).sum() / np.abs(eo).sum()
+    assert abs(ea - eb) < 0.1 * ea  # the same accuracy against exact attention
+    # P stays within e4m3's range: with tau = 2 a peaked row (one dominant key) keeps p <= 4
+    Qp = Q.copy()
+    Qp[0, 0, 5] = _bits(inp.k.float().numpy()[0, 0, 3] * 4.0)  # row 5 aligned with key 3
+    c = orc.run_fp4(Qp, K, V, tau=2)
+    assert np.isfinite(c.o32).all() and np.isfinite(c.lse).all()
+    with pytest.raises(ValueError):
+        orc.fp4_attn_qe(a.qk, a.v4, a.ve, tau=1.5)
