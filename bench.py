@@ -48,28 +48,29 @@ def mfma_peak(pv: str, method: str = "int8") -> float:
         return 1.0 / (0.5 / FP4_PEAK_TOPS + 0.5 / FP8_PEAK_TOPS)
     pv_peak = FP16_PEAK_TOPS if pv == "fp16" else INT8_PEAK_TOPS
     return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
-KERNEL_SOURCES = ["quantized_attention_quantize_amd/csrc/sage_attn.hip",
-                  "quantized_attention_quantize_amd/csrc/sage_fp4.hip",
-                  "quantized_attention_quantize_amd/csrc/sage_device.h"]
+KERNEL_SOURCES = {"k_attn_fwd": ["quantized_attention_quantize_amd/csrc/sage_attn.hip",
+                                  "quantized_attention_quantize_amd/csrc/sage_device.h"],
+                  "k_fp4_attn": ["quantized_attention_quantize_amd/csrc/sage_fp4.hip",
+                                 "quantized_attention_quantize_amd/csrc/sage_device.h"]}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "k_attn_fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kernel: str = "k_attn_fwd"):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"k_attn_fwd_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return t.get("bytes_per_launch")
 
@@ -104,7 +105,8 @@ def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
     rows = np.concatenate([h * w.Nq + local for h in range(heads)])
     if w.method == "fp4":
         t0 = time.perf_counter()
-        oracle.run_fp4(Qb, Kb, Vb, causal=w.causal, per_block_mean=w.per_block_mean, rows=rows, dtype=w.dtype)
+        oracle.run_fp4(Qb, Kb, Vb, causal=w.causal, per_block_mean=w.per_block_mean, tau=tau, rows=rows,
+                       dtype=w.dtype)
         dt = time.perf_counter() - t0
         ops = 4.0 * rows.size * w.Nk * w.d / (2 if w.causal else 1)
         return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
@@ -233,7 +235,7 @@ def run_timed(args, w, step, S, out_esize, dev):
     ops = w.ops
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / S / (attn_avg * 1e-3) / 1e12  # one launch covers 1/S of the keys
-    traffic = traffic_from_profile(w.name)
+    traffic = traffic_from_profile(w.name, "k_fp4_attn" if w.method == "fp4" else "k_attn_fwd")
 
     line = {
         "metric": METRIC,
@@ -279,8 +281,10 @@ def run_timed(args, w, step, S, out_esize, dev):
                                   "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
                                   "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
     if not args.no_cpu_baseline:
-        pv = "fp8" if w.method == "fp4" else w.pv
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(pv), sage.rowsum_rounded(pv))
+        if w.method == "fp4":
+            line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau_fp4(), False)
+        else:
+            line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
     print(json.dumps(line), flush=True)
 
 

@@ -19,8 +19,10 @@
  *     (clamped to [-127, 127]; -127 for an all-zero block), elements round to the nearest e2m1
  *     value with ties to the even code and saturate at 6.  This is the block-scale format that
  *     gfx950's scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) applies in hardware.
- *   - P is quantized as in the FP8 PV path (e4m3 of 448 p under the exact running maximum); the
- *     softmax denominator sums the unquantized p; O accumulates in fp32.
+ *   - P is quantized to e4m3 as in the FP8 PV path, scaled to leave room for a lazy reference
+ *     maximum: over 64-key tiles the maximum moves only when a tile exceeds it by more than
+ *     sage_fp4_softmax_tau() log2 units, p = exp(s - m) <= 2^tau and P = e4m3(448 * 2^-tau * p);
+ *     the softmax denominator sums the unquantized p; O accumulates in fp32.
  *
  * Conventions as in sage_mi355x.h: device pointers, caller-owned buffers, no allocation or
  * synchronization, host validation before anything is enqueued, stream as void*.  head_dim must
@@ -70,6 +72,12 @@ typedef struct {
 /* Rows of q_mean / qk_corr per head: ceil(Nq/128) with per_block_mean, else 1.  Host only. */
 int64_t sage_fp4_q_blocks(int64_t Nq, int per_block_mean);
 
+/* Lazy-maximum threshold of sage_fp4_attn_fwd's online softmax in log2 units (a whole number):
+ * the reference maximum moves only when a 64-key tile's maximum exceeds it by more than this, and
+ * P = e4m3(448 * 2^-tau * p).  The normalized result does not depend on it; only the point at
+ * which P is rounded does.  Host only. */
+double sage_fp4_softmax_tau(void);
+
 /* Workspace bytes sage_fp4_quantize_qkv needs (fp64 partial sums of the token means).  Host only. */
 size_t sage_fp4_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d);
 
@@ -97,8 +105,8 @@ sage_status sage_fp4_quantize_qkv(const sage_qkv_desc* q, const sage_qkv_desc* k
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled scores of the
  *        unsmoothed K (lse_corr added back).
  * Scores S_ij = sum_c deq(q)_ic deq(k)_jc + qk_corr[u(i)][j] accumulate in fp32 on the MFMA; the
- * online softmax runs over 64-key tiles in increasing key order with the exact running maximum;
- * P = e4m3(448 p); keys j >= Nk are masked before the softmax (FlashInfer API doc, parameter
+ * online softmax runs over 64-key tiles in increasing key order with the lazy reference maximum of
+ * sage_fp4_softmax_tau(); keys j >= Nk are masked before the softmax (FlashInfer API doc, parameter
  * unpadded_k_len).  A row with no visible key gets O = 0 and LSE = -inf.
  * Errors: INVALID_ARGUMENT (null or misaligned pointers, bad strides or out_dtype), UNSUPPORTED,
  * HIP. */

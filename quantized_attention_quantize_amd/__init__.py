@@ -30,4 +30,5 @@ from .fp4 import (  # noqa: F401
     debug_scores_fp4,
     quantize_qkv_fp4,
     sageattn_fp4,
+    softmax_tau_fp4,
 )

@@ -70,7 +70,8 @@ EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_r
            "sage_prepare_v_workspace_bytes", "sage_prepare_v", "sage_mask_workspace_bytes",
            "sage_fwd_workspace_bytes", "sage_attn_fwd", "sage_attn_fwd_prepared", "sage_quantize_qk_varlen",
            "sage_attn_fwd_varlen", "sage_prepare_v_varlen", "sage_attn_fwd_prepared_varlen", "sage_merge_lse",
-           "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_workspace_bytes",
+           "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_softmax_tau",
+           "sage_fp4_workspace_bytes",
            "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores")
 
 
@@ -134,6 +135,8 @@ def load_library():
     L.sage_status_string.restype = ctypes.c_char_p
     L.sage_fp4_q_blocks.argtypes = [I64, I]
     L.sage_fp4_q_blocks.restype = I64
+    L.sage_fp4_softmax_tau.argtypes = []
+    L.sage_fp4_softmax_tau.restype = ctypes.c_double
     L.sage_fp4_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I64]
     L.sage_fp4_workspace_bytes.restype = SZ
     D = ctypes.POINTER(QKVDesc)

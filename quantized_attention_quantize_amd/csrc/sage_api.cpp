@@ -662,6 +662,8 @@ extern "C" {
 
 int64_t sage_fp4_q_blocks(int64_t Nq, int per_block_mean) { return Nq <= 0 ? 0 : fp4_q_blocks(Nq, per_block_mean); }
 
+double sage_fp4_softmax_tau(void) { return (double)fp4_softmax_tau(); }
+
 size_t sage_fp4_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
   if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
   return align256((size_t)fp4_mean_partial_doubles(B, H, Hkv, Nq, Nk, d) * sizeof(double));

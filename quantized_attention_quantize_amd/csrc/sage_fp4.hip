@@ -32,7 +32,9 @@
 //      on the k-elements that the e2m1 V operand of lane group g pairs with keys [32g, 32g+32), and
 //      V^T needs no key permutation -- its MX blocks are 32 consecutive tokens;
 //    - O^T += V^T P^T on the same MFMA with A = e2m1 V (scale per channel and 32-token block) and
-//      B = e4m3 P with unit scale, under the exact running maximum (P = 448 p <= 448).
+//      B = e4m3 P with unit scale; P = 448 * 2^-2 * p under a reference maximum that moves only
+//      when a tile exceeds it by more than 2 log2 units (p <= 4, P <= 448), so the whole-wave
+//      rescaling of O is rare.
 //    The tile's correction values and K / V scale bytes travel through the LDS ring with the K and
 //    V codes.  Head dimension 128.
 #include "sage_device.h"
@@ -43,7 +45,11 @@ namespace sage {
 constexpr int kMX = 32;     // elements per MX block
 constexpr int kQMB = 128;   // tokens per Q smoothing block
 constexpr int kF4Threads = 256;
-constexpr float kF4Log2_448 = 8.807354922057604f;  // log2(448): P is carried as 448 * p
+constexpr float kF4Log2_448 = 8.807354922057604f;  // log2(448)
+// Lazy reference maximum of the online softmax (log2 units): it moves only when a tile's maximum
+// exceeds it by more than kF4Tau, so p = 2^(t - m) <= 2^kF4Tau and P = e4m3(448 * 2^-kF4Tau * p)
+// stays within e4m3's range while O is rarely rescaled.
+constexpr int kF4Tau = 2;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));
@@ -404,23 +410,24 @@ __device__ __forceinline__ void f4_max_piece(const v16f (&s)[2], float (&ch)[4],
 }
 
 struct F4Row {
-  float m;   // running maximum (log2 units)
-  float pm;  // exponent offset: m - log2(448)
-  float l;   // partial denominator (sum of 448 p over this lane group's keys)
+  float m;   // reference maximum (log2 units)
+  float pm;  // exponent offset: m - log2(448) + kF4Tau
+  float l;   // partial denominator (sum of P's unrounded values over this lane group's keys)
 };
 
-// Combines the chains over the row (lanes l and l ^ 32) and moves the running maximum; returns
-// 2^(m_old - m_new).  c = sm_scale * log2(e) > 0.
+// Combines the chains over the row (lanes l and l ^ 32) and moves the reference maximum when the
+// tile's maximum exceeds it by more than kF4Tau; returns 2^(m_old - m_new).
+// c = sm_scale * log2(e) > 0.
 __device__ __forceinline__ float f4_finish_max(const float (&ch)[4], float c, F4Row& rs) {
   float im = fmaxf(fmaxf(ch[0], ch[1]), fmaxf(ch[2], ch[3]));
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(im), __float_as_int(im), false, false);
   im = fmaxf(__int_as_float((int)sw[0]), __int_as_float((int)sw[1]));
   const float mt = im * c;  // -inf if nothing of the tile is visible
-  const float m_new = mt > rs.m ? mt : rs.m;
+  const float m_new = mt > rs.m + (float)kF4Tau ? mt : rs.m;
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(rs.m - m_use);
   rs.m = m_new;
-  rs.pm = m_use - kF4Log2_448;
+  rs.pm = m_use - kF4Log2_448 + (float)kF4Tau;
   return alpha;
 }
 
@@ -853,4 +860,8 @@ hipError_t launch_fp4_debug(const Fp4DebugArgs& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+}  // namespace sage
+
+namespace sage {
+int fp4_softmax_tau() { return kF4Tau; }
 }  // namespace sage

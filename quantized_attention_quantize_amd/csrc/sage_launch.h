@@ -184,5 +184,6 @@ int64_t fp4_mean_partial_doubles(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, 
 hipError_t launch_fp4_quant(const Fp4QuantArgs& a, double* partial, hipStream_t s);
 hipError_t launch_fp4_attn(const Fp4AttnArgs& a, hipStream_t s);
 hipError_t launch_fp4_debug(const Fp4DebugArgs& a, hipStream_t s);
+int fp4_softmax_tau();  // lazy-maximum threshold of k_fp4_attn (log2 units)
 
 }  // namespace sage

@@ -50,6 +50,11 @@ class QuantizedFP4:
                       self.d, self.q4.shape[2], self.k4.shape[2], 1 if self.per_block_mean else 0)
 
 
+def softmax_tau_fp4() -> int:
+    """Lazy-maximum threshold (whole log2 units) of the FP4 attention kernel's online softmax."""
+    return int(load_library().sage_fp4_softmax_tau())
+
+
 def q_blocks(Nq: int, per_block_mean: bool) -> int:
     return int(load_library().sage_fp4_q_blocks(Nq, 1 if per_block_mean else 0))
 

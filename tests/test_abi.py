@@ -276,6 +276,7 @@ def L_pad(n):
 
 def test_fp4_host_queries(L):
     assert L.sage_fp4_q_blocks(300, 1) == 3 and L.sage_fp4_q_blocks(300, 0) == 1 and L.sage_fp4_q_blocks(0, 1) == 0
+    assert L.sage_fp4_softmax_tau() == 2.0  # P = e4m3(448 / 4 * p), p <= 4
     # fp64 partial sums of the larger of the Q and K token-mean reductions (256-token chunks)
     assert L.sage_fp4_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_fp4_workspace_bytes(0, 1, 1, 1, 1, 128) == 0

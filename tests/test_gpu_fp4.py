@@ -73,7 +73,7 @@ def test_fp4_parity(orc, case):
     say("  quantization bit-exact")
     out_dt = c.get("out") or tdt
     ods = {torch.float32: "bf16", torch.bfloat16: "bf16", torch.float16: "fp16"}[out_dt]
-    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=causal, out_dtype=ods)
+    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=causal, tau=sage.softmax_tau_fp4(), out_dtype=ods)
     got = _out_f32(out).reshape(-1, d)
     want = o32 if out_dt == torch.float32 else _dec(o16, ods)
     e1 = rel_l1(got, want)

@@ -256,7 +256,8 @@ def test_fp4_workload_parity(orc, name):
     edge = np.concatenate([np.arange(64), np.arange(w.Nq - 64, w.Nq), (w.B * w.H - 1) * w.Nq + np.arange(64),
                            R - 64 + np.arange(64)])
     rows = np.unique(np.concatenate([rng.choice(R, N_RANDOM_ROWS[name], replace=False), edge]))
-    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=w.causal, rows=rows, out_dtype=w.dtype)
+    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=w.causal, tau=sage.softmax_tau_fp4(), rows=rows,
+                                      out_dtype=w.dtype)
     got = rows_of(out, rows)
     e1 = rel_l1(got, f32_of_bf16_bits(o16))
     say(f"  {rows.size} rows: rel-L1 vs emulation {e1:.3e}")
