@@ -54,13 +54,14 @@ constexpr int kF4Tau = 2;
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));
 
-// e2m1 code of y: the nearest of the magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6, a tie going to the even
-// code, saturating at 6; bit 3 is the sign bit of y (so a negative value rounding to 0 gives -0).
-__device__ __forceinline__ unsigned e2m1_code(float y) {
-  const float a = fabsf(y);
-  const unsigned c = (unsigned)(a > 0.25f) + (unsigned)(a >= 0.75f) + (unsigned)(a > 1.25f) +
-                     (unsigned)(a >= 1.75f) + (unsigned)(a > 2.5f) + (unsigned)(a >= 3.5f) + (unsigned)(a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+// e2m1 codes of y0 (low nibble) and y1 (high nibble) into byte `sel` of w: the nearest of the
+// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, saturating at 6, bit 3 = the
+// sign bit (a negative value rounding to 0 gives -0).  gfx950's v_cvt_scalef32_pk_fp4_f32 with
+// unit scale computes exactly this: checked on the GPU against the rule written out as threshold
+// comparisons over every non-NaN fp32 bit pattern.
+template <int SEL>
+__device__ __forceinline__ unsigned e2m1_pair(unsigned w, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, SEL);
 }
 
 // E8M0 byte X + 127 of an MX block with largest magnitude amax >= 0, X = floor(log2 amax) - 2
@@ -88,8 +89,10 @@ __device__ __forceinline__ void mx_store8(const float (&x)[8], int cg, uint8_t* 
   float inv;
   const unsigned e8 = mx_scale_byte(amax, inv);
   unsigned w = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w |= e2m1_code(x[j] * inv) << (4 * j);
+  w = e2m1_pair<0>(w, x[0] * inv, x[1] * inv);
+  w = e2m1_pair<1>(w, x[2] * inv, x[3] * inv);
+  w = e2m1_pair<2>(w, x[4] * inv, x[5] * inv);
+  w = e2m1_pair<3>(w, x[6] * inv, x[7] * inv);
   *reinterpret_cast<unsigned*>(codes_row + cg * 4) = w;
   if ((cg & 3) == 0) {
     const int lb = cg >> 2;
@@ -230,8 +233,15 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_prep_v(Fp4QuantArgs a) {
     float inv;
     const unsigned e8 = mx_scale_byte(amax, inv);
     unsigned w[4] = {0u, 0u, 0u, 0u};
+    const float* col = &sv[kMX * blk][c];
 #pragma unroll
-    for (int k = 0; k < kMX; ++k) w[k >> 3] |= e2m1_code(sv[kMX * blk + k][c] * inv) << (4 * (k & 7));
+    for (int q = 0; q < 4; ++q) {  // tokens 8 q .. 8 q + 7 into word q
+      const float* t8 = col + 8 * q * (D + 1);
+      w[q] = e2m1_pair<0>(w[q], t8[0] * inv, t8[D + 1] * inv);
+      w[q] = e2m1_pair<1>(w[q], t8[2 * (D + 1)] * inv, t8[3 * (D + 1)] * inv);
+      w[q] = e2m1_pair<2>(w[q], t8[4 * (D + 1)] * inv, t8[5 * (D + 1)] * inv);
+      w[q] = e2m1_pair<3>(w[q], t8[6 * (D + 1)] * inv, t8[7 * (D + 1)] * inv);
+    }
     uint8_t* dst = a.v4t + (bhk * D + c) * (a.Nk_pad / 2) + blockIdx.x * 32 + blk * 16;
     *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     a.v_sc[(bhk * (a.Nk_pad / kMX) + blockIdx.x * 2 + blk) * D + (c % 32) * (D / 32) + c / 32] = (uint8_t)e8;
@@ -250,8 +260,10 @@ __device__ __forceinline__ void split3(v8f x, v8bf (&p)[3]) {
 
 // qk_corr[b,h,u,j] = sum_c qmean[b,h,u,c] * Ktilde[b,hk,j,c] with Ktilde = fp32(K - kmean), for
 // keys j < Nk_pad (zero past Nk): D (32 keys x 32 Q blocks) += Ktilde (32 x 16) qmean^T (16 x 32)
-// per 16 channels on the bf16 MFMA, each operand in three exact bf16 parts (nine products,
-// smallest first): every product is exact and only the fp32 accumulation rounds.
+// per 16 channels on the bf16 MFMA, each operand in three exact bf16 parts.  The six products of
+// parts p + q <= 2 (smallest first) are kept -- each is exact, and the three dropped ones are each
+// below 2^-24 of |qmean_c Ktilde_jc|, fp32's own rounding of the sum -- and alternate 16-channel
+// steps accumulate in two independent chains.
 // grid = (Nk_pad / 128, B*H), block = 256: wave w takes keys [128 x + 32 w, +32) for every Q block.
 template <int D, int IN>
 __global__ __launch_bounds__(kF4Threads) void k_fp4_corr(Fp4QuantArgs a) {
@@ -278,7 +290,11 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_corr(Fp4QuantArgs a) {
     const int u = u0 + lr;  // B operand column: Q block u
     const bool uv = u < a.nqm;
     const float* qm = a.q_mean + (bh * a.nqm + (uv ? u : 0)) * D + 8 * g;
-    v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    v16f acc2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc2[h][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       v8f y = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -289,11 +305,13 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_corr(Fp4QuantArgs a) {
       }
       v8bf bp[3];
       split3(y, bp);
+      v16f& acc = acc2[kk & 1];
 #pragma unroll
       for (int p = 2; p >= 0; --p)
 #pragma unroll
-        for (int q = 2; q >= 0; --q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][p], bp[q], acc, 0, 0, 0);
+        for (int q = 2 - p; q >= 0; --q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][p], bp[q], acc, 0, 0, 0);
     }
+    const v16f acc = acc2[0] + acc2[1];
     if (uv) {
       float* dst = a.qk_corr + (bh * a.nqm + u) * a.Nk_pad + j0 + g * 4;
 #pragma unroll
