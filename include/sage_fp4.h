@@ -86,8 +86,10 @@ size_t sage_fp4_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, i
  *   k_mean = fp32(sum_t fp64(K_t) / Nk);  Ktilde = fp32(K - k_mean);
  *   q_mean_u = fp32(sum_{t in block u} fp64(Q_t) / count) (or over all Nq tokens);
  *   Qtilde = fp32(Q - q_mean_u);  MX FP4 codes and scales of Qtilde, Ktilde (per 32 channels) and
- *   of V (per 32 tokens); qk_corr and lse_corr as above (the GPU sums qk_corr with exact bf16
- *   splits of both operands and fp32 accumulation).
+ *   of V (per 32 tokens); qk_corr and lse_corr as above.  The GPU forms qk_corr as
+ *   q_mean_u . K_j - q_mean_u . k_mean: exact products of bf16 parts of both (three for q_mean,
+ *   one for a bf16 K, two for an fp16 K) accumulated in fp32 from -(q_mean_u . k_mean), which is
+ *   summed in fp64; its error scales with |q_mean| |K|.
  * Sources: docs digest "FP4 Attention for Blackwell GPUs" / "sageattn3_blackwell"; FlashInfer API
  * doc, parameters q_fp4 / k_fp4 / v_fp4_t, q_scale / k_scale / v_scale_t, qk_correction,
  * per_block_mean.

@@ -9,8 +9,8 @@
 // "flashinfer.nvfp4_attention_sm120_fwd", parameter unpadded_k_len).
 //
 // Design (MI355X / CDNA4):
-//  * One workgroup = 4 waves = 256 query rows of one (b,h), one wave per SIMD; each wave owns 64
-//    rows as two 32-row MFMA blocks that share every K and V fragment read from LDS.  Inside a
+//  * One workgroup = 8 waves = 256 query rows of one (b,h), two waves per SIMD; each wave owns one
+//    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  Inside a
 //    wave the key loop is software-pipelined (QK of the next tile, softmax of this tile and PV of
 //    the previous tile are interleaved), so MFMA and VALU work of one wave overlap.
 //  * S^T = K8 . Q8^T on v_mfma_i32_32x32x32_i8: the K tile (A operand) comes from LDS, the

@@ -110,34 +110,57 @@ template <int D, int IN>
 __global__ __launch_bounds__(kF4Threads) void k_fp4_quant_q(Fp4QuantArgs a) {
   constexpr int CG = D / 8, RPI = kF4Threads / CG, TPT = kQMB / RPI;
   __shared__ double csum[RPI][D];
-  __shared__ float qm_s[D], km_s[D];
+  __shared__ float qm_s[D];
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);
   const int u = blockIdx.x;
   const int64_t t0 = (int64_t)u * kQMB;
   const unsigned short* src = a.q + b * a.q_sb + h * a.q_sh + cg * 8;
-  float x[TPT][8];
+  float km[8];
+  {
+    const float4 k0 = *reinterpret_cast<const float4*>(a.k_mean + bhk * D + cg * 8);
+    const float4 k1 = *reinterpret_cast<const float4*>(a.k_mean + bhk * D + cg * 8 + 4);
+    km[0] = k0.x, km[1] = k0.y, km[2] = k0.z, km[3] = k0.w, km[4] = k1.x, km[5] = k1.y, km[6] = k1.z, km[7] = k1.w;
+  }
+  // all loads first (kept as raw 16-bit values); then one pass over them: this thread's column
+  // sums (fp64, exact for any realistic spread of magnitudes) and each token's partial lse_corr
+  // over its 8 channels (exact fp64 products), a token at a time
+  u16x8 raw[TPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int64_t tok = t0 + rs + i * RPI;
-    if (tok < a.Nq) {
-      const u16x8 v = *reinterpret_cast<const u16x8*>(src + tok * a.q_sn);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[i][j] = in_to_f32<IN>(v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
-    }
+    raw[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok < a.Nq) raw[i] = *reinterpret_cast<const u16x8*>(src + tok * a.q_sn);
   }
-  if (a.per_block) {  // fp64 column sums of the block's valid tokens, combined in a fixed order
+  double cs[8], ls[TPT];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cs[j] = 0.0;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    ls[i] = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      double s = 0.0;
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) s += (double)x[i][j];
-      csum[rs][cg * 8 + j] = s;
+      const double xd = (double)in_to_f32<IN>(raw[i][j]);
+      cs[j] += xd;
+      ls[i] += xd * (double)km[j];
     }
+    asm volatile("" : "+v"(cs[0]), "+v"(cs[1]), "+v"(cs[2]), "+v"(cs[3]), "+v"(cs[4]), "+v"(cs[5]), "+v"(cs[6]),
+                 "+v"(cs[7]), "+v"(ls[i]));
+  }
+  // The empty asm statements (no code) pin the sums token by token and hide the raw values from
+  // the compiler: otherwise it sinks the sums past this loop and converts the raw values once for
+  // both loops, keeping 64 fp64 values live across the barrier; the loop below converts again.
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    unsigned w4[4];
+    __builtin_memcpy(w4, &raw[i], 16);
+    asm volatile("" : "+v"(w4[0]), "+v"(w4[1]), "+v"(w4[2]), "+v"(w4[3]));
+    __builtin_memcpy(&raw[i], w4, 16);
+  }
+  if (a.per_block) {  // the block's column sums combined in a fixed order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) csum[rs][cg * 8 + j] = cs[j];
     __syncthreads();
     if (t < D) {
       double s = 0.0;
@@ -150,22 +173,21 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_quant_q(Fp4QuantArgs a) {
   } else if (t < D) {
     qm_s[t] = a.q_mean[bh * D + t];
   }
-  if (t < D) km_s[t] = a.k_mean[bhk * D + t];
   __syncthreads();
+  float qm[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qm[j] = qm_s[cg * 8 + j];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int64_t tok = t0 + rs + i * RPI;
     const bool valid = tok < a.Nq;
-    double s = 0.0;
-    float xs[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s += (double)x[i][j] * (double)km_s[cg * 8 + j];
-      xs[j] = valid ? x[i][j] - qm_s[cg * 8 + j] : 0.f;  // one fp32 rounding
-    }
+    double s = ls[i];
 #pragma unroll
     for (int o = 1; o < CG; o <<= 1) s += __shfl_xor(s, o);
     if (cg == 0 && valid) a.lse_corr[bh * a.Nq + tok] = (float)s;
+    float xs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xs[j] = valid ? in_to_f32<IN>(raw[i][j]) - qm[j] : 0.f;  // one fp32 rounding
     const int64_t row = bh * a.Nq_pad + tok;
     mx_store8<D>(xs, cg, a.q4 + row * (D / 2), a.q_sc + row * (D / kMX));
   }
@@ -258,67 +280,135 @@ __device__ __forceinline__ void split3(v8f x, v8bf (&p)[3]) {
   }
 }
 
-// qk_corr[b,h,u,j] = sum_c qmean[b,h,u,c] * Ktilde[b,hk,j,c] with Ktilde = fp32(K - kmean), for
-// keys j < Nk_pad (zero past Nk): D (32 keys x 32 Q blocks) += Ktilde (32 x 16) qmean^T (16 x 32)
-// per 16 channels on the bf16 MFMA, each operand in three exact bf16 parts.  The six products of
-// parts p + q <= 2 (smallest first) are kept -- each is exact, and the three dropped ones are each
-// below 2^-24 of |qmean_c Ktilde_jc|, fp32's own rounding of the sum -- and alternate 16-channel
-// steps accumulate in two independent chains.
-// grid = (Nk_pad / 128, B*H), block = 256: wave w takes keys [128 x + 32 w, +32) for every Q block.
+// qk_corr[b,h,u,j] = qmean[b,h,u,:] . (K[b,hk,j,:] - kmean) for keys j < Nk (zero for j < Nk_pad
+// past Nk), as qmean . K_j - qmean . kmean: D (32 Q blocks x 32 keys) += qmean (32 x 16) K^T
+// (16 x 32) per 16 channels on the bf16 MFMA, starting from D = -(qmean . kmean) (summed in fp64,
+// rounded once).  qmean enters in three exact bf16 parts; a bf16 K is its own single part, an fp16
+// K splits into two exact bf16 parts (its 11 significant bits) and the product of the two smallest
+// parts, below 2^-24 of |qmean_c K_jc|, is dropped.  Every product is exact, so the only error is
+// the fp32 accumulation; it scales with |qmean| |K| -- far below K's own input rounding relative
+// to K - kmean, however large K's mean.
+// A wave splits the means of one group of 32 Q blocks once, keeps the parts in registers and
+// streams up to kpw blocks of 32 keys past them.  Work item c = (b*H + h) * nchunk + chunk covers
+// 4 * kpw key blocks (wave w takes blocks 4 i + w of the chunk).  The ngroups workgroups of one
+// item sit 8 apart in launch order: workgroups are dealt to the 8 XCDs in turn, so all groups of
+// an item run on one XCD and read its K through one L2.
+__host__ __device__ constexpr int64_t f4corr_chunks(int64_t Nk_pad, int kpw) {
+  return (Nk_pad / 32 + 4 * kpw - 1) / (4 * kpw);
+}
+
 template <int D, int IN>
-__global__ __launch_bounds__(kF4Threads) void k_fp4_corr(Fp4QuantArgs a) {
+__global__ __launch_bounds__(kF4Threads) __attribute__((amdgpu_waves_per_eu(2))) void k_fp4_corr(Fp4QuantArgs a,
+                                                                                                  int ngroups,
+                                                                                                  int kpw) {
+  __shared__ float km_s[D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, g = lane >> 5;
-  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t nchunk = f4corr_chunks(a.Nk_pad, kpw), nkb = a.Nk_pad / 32;
+  const int64_t wg = blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
+  if (c >= a.B * a.H * nchunk) return;  // the whole workgroup, before the barrier
+  const int64_t bh = c / nchunk, b = bh / a.H, h = bh % a.H;
   const int64_t hk = h / (a.H / a.Hkv), bhk = b * a.Hkv + hk;
-  const int64_t j0 = (int64_t)blockIdx.x * 128 + 32 * w;
-  const int64_t key = j0 + lr;  // A operand row: this lane's key, channels 16 kk + 8 g .. + 8
-  const bool kv = key < a.Nk;
-  const unsigned short* src = a.k + b * a.k_sb + hk * a.k_sh + (kv ? key : 0) * a.k_sn + 8 * g;
-  const float* km = a.k_mean + bhk * D + 8 * g;
-  v8bf ap[D / 16][3];
+  const int64_t kb0 = (c % nchunk) * 4 * kpw + w;
+  int64_t nb = (nkb - kb0 + 3) / 4;
+  nb = nb < kpw ? nb : kpw;  // blocks kb0, kb0 + 4, ... of this wave (none in a ragged last chunk)
+  const unsigned short* kh = a.k + b * a.k_sb + hk * a.k_sh + 8 * g;
+  // B operand column: key 32 kb + lr, channels 16 kk + 8 g .. + 8.  The loads carry no branch (a
+  // key past Nk reads row Nk - 1; its D column is independent of the others and stored as zero).
+  auto load_k = [&](int64_t kb, u16x8(&r)[D / 16]) {
+    const int64_t key = 32 * kb + lr;
+    const unsigned short* src = kh + (key < a.Nk ? key : a.Nk - 1) * a.k_sn;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) r[kk] = *reinterpret_cast<const u16x8*>(src + 16 * kk);
+  };
+  auto kb_of = [&](int64_t i) { return kb0 + 4 * (i < nb ? i : (nb > 0 ? nb - 1 : 0)); };
+  // the first two key blocks, the means and K's mean are all requested before anything waits
+  u16x8 ka[D / 16], kz[D / 16];
+  if (nb > 0) {
+    load_k(kb_of(0), ka);
+    load_k(kb_of(1), kz);
+  }
+  const int u = 32 * (int)grp + lr;  // A operand row: Q block u, channels 16 kk + 8 g .. + 8
+  const bool uv = u < a.nqm;
+  const float* qm = a.q_mean + (bh * a.nqm + (uv ? u : 0)) * D + 8 * g;
+  v8f y[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    v8f x = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (kv) {
-      const u16x8 v = *reinterpret_cast<const u16x8*>(src + 16 * kk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = in_to_f32<IN>(v[e]) - km[16 * kk + e];  // as k_fp4_quant_k
+    y[kk] = v8f{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (uv) {
+      const float4 lo = *reinterpret_cast<const float4*>(qm + 16 * kk);
+      const float4 hi = *reinterpret_cast<const float4*>(qm + 16 * kk + 4);
+      y[kk] = v8f{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
-    split3(x, ap[kk]);
   }
-  for (int u0 = 0; u0 < a.nqm; u0 += 32) {
-    const int u = u0 + lr;  // B operand column: Q block u
-    const bool uv = u < a.nqm;
-    const float* qm = a.q_mean + (bh * a.nqm + (uv ? u : 0)) * D + 8 * g;
-    v16f acc2[2];
+  if (threadIdx.x < D) km_s[threadIdx.x] = a.k_mean[bhk * D + threadIdx.x];
+  __syncthreads();
+  if (nb <= 0) return;
+  v8bf ap[D / 16][3];
+  double qk = 0.0;  // qmean_u . kmean over this lane's channels
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int kk = 0; kk < D / 16; ++kk) {
+    split3(y[kk], ap[kk]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc2[h][r] = 0.f;
+    for (int e = 0; e < 8; ++e) qk += (double)y[kk][e] * (double)km_s[16 * kk + 8 * g + e];
+  }
+  qk += __shfl_xor(qk, 32);
+  const float qkf = (float)qk;
+  v16f c0;  // D row 8 rq + 4 g + e is Q block 32 grp + 8 rq + 4 g + e, whose qmean . kmean lane 8 rq + 4 g + e holds
+#pragma unroll
+  for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c0[4 * rq + e] = -__shfl(qkf, 8 * rq + 4 * g + e);
+  // this head's correction rows (nqm * Nk_pad * 4 < 2^31 bytes, host-checked); the stores of rows
+  // past nqm (in the last group) go to an offset past the range, which the hardware drops, so they
+  // need no branch
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.qk_corr + bh * a.nqm * a.Nk_pad), (short)0, (int)(a.nqm * a.Nk_pad * 4), kBufferWord3);
+  constexpr int kOutOfRange = 0x7ffffffc;
+  auto block = [&](int64_t kb, const u16x8(&kr)[D / 16]) {
+    v16f acc = c0;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      v8f y = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (uv) {
-        const float4 lo = *reinterpret_cast<const float4*>(qm + 16 * kk);
-        const float4 hi = *reinterpret_cast<const float4*>(qm + 16 * kk + 4);
-        y = v8f{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if constexpr (IN == 0) {
+        const v8bf kp = __builtin_bit_cast(v8bf, kr[kk]);
+#pragma unroll
+        for (int p = 2; p >= 0; --p) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][p], kp, acc, 0, 0, 0);
+      } else {
+        v8f x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = in_to_f32<IN>(kr[kk][e]);
+        const v8bf k0 = __builtin_convertvector(x, v8bf);  // round to nearest even
+        const v8bf k1 = __builtin_convertvector(x - __builtin_convertvector(k0, v8f), v8bf);  // exact residue
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][2], k0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][1], k1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][1], k0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][0], k1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][0], k0, acc, 0, 0, 0);
       }
-      v8bf bp[3];
-      split3(y, bp);
-      v16f& acc = acc2[kk & 1];
-#pragma unroll
-      for (int p = 2; p >= 0; --p)
-#pragma unroll
-        for (int q = 2 - p; q >= 0; --q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][p], bp[q], acc, 0, 0, 0);
     }
-    const v16f acc = acc2[0] + acc2[1];
-    if (uv) {
-      float* dst = a.qk_corr + (bh * a.nqm + u) * a.Nk_pad + j0 + g * 4;
+    const bool kv = 32 * kb + lr < a.Nk;  // D column lr is key 32 kb + lr
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq)  // D rows 8 rq + 4 g + e are keys j0 + 8 rq + 4 g + e
-        *reinterpret_cast<float4*>(dst + rq * 8) =
-            make_float4(acc[4 * rq], acc[4 * rq + 1], acc[4 * rq + 2], acc[4 * rq + 3]);
-    }
+    for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int uu = 32 * (int)grp + 8 * rq + 4 * g + e;
+        const int off = uu < a.nqm ? (int)(((int64_t)uu * a.Nk_pad + 32 * kb + lr) * 4) : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, kv ? acc[4 * rq + e] : 0.f), crs, off, 0, 0);
+      }
+  };
+  // Two register buffers: the next block's loads are issued before the current block's products
+  // (past the end, a block reloads itself).  The first block is peeled off so that the loop is
+  // entered, as it repeats, with one block's stores in flight between the two buffers' loads: the
+  // compiler's wait for a buffer then lets those stores retire in the background.
+  __builtin_amdgcn_sched_barrier(0);
+  block(kb_of(0), ka);
+  for (int64_t i = 1; i < nb; i += 2) {
+    load_k(kb_of(i + 1), ka);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kb_of(i), kz);
+    if (i + 1 >= nb) break;
+    load_k(kb_of(i + 2), kz);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kb_of(i + 1), ka);
   }
 }
 
@@ -845,12 +935,25 @@ int64_t fp4_mean_partial_doubles(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, 
   return kq > kk ? kq : kk;
 }
 
+// Key blocks per wave of k_fp4_corr for a total of wave_blocks (Q-block group, key block) pairs:
+// about 768 waves (three per CU), at least 1 and at most 16 blocks each.  A wave's set-up (loading
+// and splitting the means, its first loads) costs as much as several key blocks, so fewer, longer
+// waves measure faster even below one wave per SIMD (on 24 heads x 4096 keys: 4 blocks per wave
+// 14 us, 1 block 20 us; on 64 heads x 8192 keys x 2 groups: 16 blocks 63 us, 4 blocks 80 us).
+static int fp4_corr_blocks_per_wave(int64_t wave_blocks) {
+  const int64_t k = wave_blocks / 768;
+  return (int)(k < 1 ? 1 : (k > 16 ? 16 : k));
+}
+
 template <int D, int IN>
 static void launch_fp4_quant_t(const Fp4QuantArgs& a, hipStream_t s) {
   k_fp4_quant_q<D, IN><<<dim3((unsigned)(a.Nq_pad / kQMB), (unsigned)(a.B * a.H)), kF4Threads, 0, s>>>(a);
   k_fp4_quant_k<D, IN><<<dim3((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.Hkv)), kF4Threads, 0, s>>>(a);
   k_fp4_prep_v<D, IN><<<dim3((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.Hkv)), kF4Threads, 0, s>>>(a);
-  k_fp4_corr<D, IN><<<dim3((unsigned)(a.Nk_pad / 128), (unsigned)(a.B * a.H)), kF4Threads, 0, s>>>(a);
+  const int64_t ngroups = (a.nqm + 31) / 32;
+  const int kpw = fp4_corr_blocks_per_wave(a.B * a.H * ngroups * (a.Nk_pad / 32));
+  const int64_t items = a.B * a.H * f4corr_chunks(a.Nk_pad, kpw);
+  k_fp4_corr<D, IN><<<(unsigned)((items + 7) / 8 * 8 * ngroups), kF4Threads, 0, s>>>(a, (int)ngroups, kpw);
 }
 
 // K mean; the global Q mean (not per_block) into q_mean; then Q, K, V and the correction rows.

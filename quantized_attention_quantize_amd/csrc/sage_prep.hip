@@ -51,20 +51,25 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
     sum[j] = 0.0;
     mx[j] = 0.f;
   }
-  for (int r = rs; r < kChunk; r += RPI) {
-    int64_t tok = t0 + r;
-    if (tok < N) {
-      u16x8 v = *reinterpret_cast<const u16x8*>(base + tok * sn);
+  // all of the chunk's loads are issued before the first is used (zero rows past N add nothing)
+  constexpr int TPT = kChunk / RPI;
+  u16x8 v[TPT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float f = in_to_f32<IN>(v[j]);
-        if constexpr (MODE == 0)
-          sum[j] += (double)f;
-        else
-          mx[j] = fmaxf(mx[j], fabsf(f));
-      }
-    }
+  for (int i = 0; i < TPT; ++i) {
+    const int64_t tok = t0 + rs + i * RPI;
+    v[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok < N) v[i] = *reinterpret_cast<const u16x8*>(base + tok * sn);
   }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = in_to_f32<IN>(v[i][j]);
+      if constexpr (MODE == 0)
+        sum[j] += (double)f;
+      else
+        mx[j] = fmaxf(mx[j], fabsf(f));
+    }
   // combine the RPI row-slices in a fixed order
   if constexpr (MODE == 0) {
     __shared__ double red[RPI][D];
@@ -98,7 +103,15 @@ __global__ __launch_bounds__(D) void k_kmean_final(const double* __restrict__ pa
   const int c = threadIdx.x;
   const int64_t N = seq_span(cu, bh / H, Nmax, total).len;
   double s = 0.0;
-  for (int i = 0; i < nchunk; ++i) s += partial[(bh * nchunk + i) * D + c];
+  int i = 0;
+  for (; i + 8 <= nchunk; i += 8) {  // eight loads in flight, added in chunk order
+    double p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = partial[(bh * nchunk + i + k) * D + c];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += p[k];
+  }
+  for (; i < nchunk; ++i) s += partial[(bh * nchunk + i) * D + c];
   kmean[bh * D + c] = N > 0 ? (float)(s / (double)N) : 0.f;
 }
 

@@ -7,7 +7,8 @@ accumulation error; raw scores of a window (debug entry) within fp32 accumulatio
 oracle's exact sums; O within rel-L1 1e-3 of the oracle's emulation (both rounded to the output
 dtype), LSE within 1e-3; against exact attention the measured MX-FP4 budget (cosine >= 0.97,
 rel-L1 <= 0.25).  Cases: ragged tails (Nq, Nk not multiples of 128 or 64), causal with Nq != Nk,
-GQA, per-block and global Q means, fp16 inputs, fp32 output, one key, one query, Q = 0.
+GQA, per-block and global Q means, fp16 inputs, fp32 output, one key, one query, Q = 0, a K whose
+channel means are large against its spread.
 """
 
 import numpy as np
@@ -48,6 +49,8 @@ CASES = [
     dict(name="fp32_out_global", B=1, H=2, Nq=128, Nk=700, pbm=False, out=torch.float32),
     dict(name="one_key", B=1, H=2, Nq=70, Nk=1),
     dict(name="one_query", B=1, H=2, Nq=1, Nk=300, causal=True),
+    dict(name="large_k_mean", B=1, H=2, Nq=400, Nk=450, sigma=96.0),
+    dict(name="large_k_mean_fp16", B=1, H=2, Nq=200, Nk=333, sigma=96.0, dtype=torch.float16),
 ]
 
 
@@ -59,7 +62,7 @@ def test_fp4_parity(orc, case):
     causal, pbm = c.get("causal", False), c.get("pbm", True)
     tdt = c.get("dtype", torch.bfloat16)
     dts = "fp16" if tdt == torch.float16 else "bf16"
-    inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=90, Hkv=Hkv, dtype=tdt)
+    inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=90, Hkv=Hkv, dtype=tdt)
     q, k, v = to_dev(inp)
     g = sage.quantize_qkv_fp4(q, k, v, per_block_mean=pbm)
     out, lse = sage.attn_fwd_fp4(g, is_causal=causal, return_lse=True, out_dtype=c.get("out"))
@@ -68,8 +71,8 @@ def test_fp4_parity(orc, case):
     r = orc.fp4_quant_qk(Q, K, dtype=dts, per_block_mean=pbm)
     v4, ve = orc.fp4_prep_v(V, dts)
     Kf = _dec(K, dts)
-    kt_max = float(np.abs(Kf - r.kmean[:, :, None, :]).max())
-    fp4_check_quant(g, r, Nq, Nk, (v4, ve), kt_max)
+    k_max = max(float(np.abs(Kf).max()), float(np.abs(Kf - r.kmean[:, :, None, :]).max()))
+    fp4_check_quant(g, r, Nq, Nk, (v4, ve), k_max)
     say("  quantization bit-exact")
     out_dt = c.get("out") or tdt
     ods = {torch.float32: "bf16", torch.bfloat16: "bf16", torch.float16: "fp16"}[out_dt]

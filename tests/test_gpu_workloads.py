@@ -247,8 +247,9 @@ def test_fp4_workload_parity(orc, name):
     del q, k, v
     r = orc.fp4_quant_qk(Qb, Kb, dtype=w.dtype, per_block_mean=w.per_block_mean)
     v4, ve = orc.fp4_prep_v(Vb, w.dtype)
-    kt_max = float(np.abs(f32_of_bf16_bits(Kb) - r.kmean[:, :, None, :]).max())
-    fp4_check_quant(g, r, w.Nq, w.Nk, (v4, ve), kt_max)
+    Kf = f32_of_bf16_bits(Kb)
+    k_max = max(float(np.abs(Kf).max()), float(np.abs(Kf - r.kmean[:, :, None, :]).max()))
+    fp4_check_quant(g, r, w.Nq, w.Nk, (v4, ve), k_max)
     say("  quantization bit-exact over the whole tensors")
     del g
     rng = np.random.default_rng(7)
