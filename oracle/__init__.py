@@ -273,9 +273,12 @@ def attn_qe(qk: QuantQK, vhat, vs, pv, Nq, Nk, *, causal=False, mask=None, sm_sc
     """Quantized emulation.  Returns (o32 [R,d] fp32, o16 [R,d] bits of out_dtype, lse [R] fp32).
 
     BN: keys per online-softmax tile; tau: the reference maximum is raised only when a tile's
-    maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.
+    maximum exceeds it by more than tau (log2 units); 0 = exact running maximum.  For pv = "fp8"
+    tau is a whole number and P = e4m3(448 * 2^-tau * p).
     lsum_rounded: the denominator sums P as rounded for the PV product instead of the fp32 p.
     vmean: smooth_v's V mean [B,Hkv,d] (vhat then holds V - vmean), added back to the output."""
+    if pv == "fp8" and (int(tau) != tau or tau < 0):
+        raise ValueError("with e4m3 P, tau must be a non-negative whole number")
     B, H, Nq_pad, d = qk.q8.shape
     Hkv, Nk_pad = qk.k8.shape[1], qk.k8.shape[2]
     sm = default_sm_scale(d) if sm_scale is None else float(np.float32(sm_scale))

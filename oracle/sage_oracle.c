@@ -30,10 +30,11 @@
  *    mask drops the keys whose entry is zero;
  *  - the K mean is summed in fp64 over all Nk tokens (mask and causality ignored), divided by Nk
  *    in fp64 and rounded once to fp32;
- *  - P for FP8 PV is quantized as e4m3(448 * p) with saturation, V per channel as
+ *  - P for FP8 PV is quantized as e4m3(ps * p) with ps = 448 * 2^-tau (tau a whole number, see
+ *    below: p <= 2^tau, so ps * p <= 448) and saturation, V per channel as
  *    e4m3(V * 448 / max_t |V|);
  *  - the softmax denominator l sums, per the lsum_rounded argument, either the unquantized fp32 p
- *    (0) or P as rounded for the PV product (1: the fp16 value, or e4m3(448*p)/448);
+ *    (0) or P as rounded for the PV product (1: the fp16 value, or e4m3(ps*p)/ps);
  *  - the online softmax runs over key tiles of BN keys in increasing key order.  Its reference
  *    maximum m starts at -inf and, after each tile, is replaced by the running maximum whenever
  *    that exceeds m by more than tau*ln(2) (tau = 0: the exact running maximum); p = exp(s - m)
@@ -398,6 +399,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
                  int64_t Nk_pad, int64_t BN, double tau, int lsum_rounded, const int64_t* rows, int64_t nrows,
                  float* o32, int out_fp16, uint16_t* o16, float* lse) {
   int64_t nbq = (Nq + ORC_QBLK - 1) / ORC_QBLK, nbk = (Nk + ORC_QBLK - 1) / ORC_QBLK;
+  const float ps = (float)ldexp(448.0, -(int)tau); /* e4m3 P scale (fp8: tau is a whole number) */
   if (rows == NULL) nrows = B * H * Nq;
 #pragma omp parallel
   {
@@ -447,13 +449,13 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         for (int64_t j = j0; j < j1; ++j) {
           float p = (s[j - j0] == -INFINITY) ? 0.0f : (float)exp((double)(s[j - j0] - mnew));
           if (pv_fp8)
-            pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(448.0f * p));
+            pq[j - j0] = orc_e4m3_to_f32(orc_f32_to_e4m3(ps * p));
           else
             pq[j - j0] = orc_f16_to_f32(orc_f32_to_f16(p));
           if (!lsum_rounded)
             psum += p;
           else
-            psum += pv_fp8 ? pq[j - j0] / 448.0f : pq[j - j0];
+            psum += pv_fp8 ? pq[j - j0] / ps : pq[j - j0];
         }
         l = alpha * l + psum;
         for (int64_t c = 0; c < d; ++c) {
@@ -473,7 +475,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
         if (l == 0.0f)
           out = 0.0f;
         else if (pv_fp8)
-          out = (float)((double)o[c] * (double)vs[bhk * d + c] / (448.0 * (double)l));
+          out = (float)((double)o[c] * (double)vs[bhk * d + c] / ((double)ps * (double)l));
         else
           out = o[c] / l;
         if (vmean && l != 0.0f) out = out + vmean[bhk * d + c]; /* smooth_v: add the mean back */

@@ -244,6 +244,29 @@ def test_qe_lazy_maximum_only_moves_rounding(orc, sm):
     assert np.array_equal(c.o16, a.o16)
 
 
+@pytest.mark.parametrize("sm", [None, 0.6])
+def test_qe_lazy_maximum_e4m3_scales_p(orc, sm):
+    """With e4m3 P the lazy reference maximum lets p reach 2^tau, so P is e4m3(448 * 2^-tau * p):
+    the LSE (denominator over the fp32 p) is the same as with the exact running maximum to fp32
+    rounding, O moves only by e4m3 rounding noise (of the order of the emulation's own distance to
+    exact attention) and stays as close to exact attention.  Without
+    the 2^-tau the peaked rows (sm_scale = 0.6) would saturate at 448 and O would be far off.  tau
+    must be whole, so that the scale is exact."""
+    inp = make_inputs(1, 2, 300, 900, 128, seed=16)
+    Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    a = orc.run_qe(Qb, Kb, Vb, pv="fp8", BN=64, tau=0.0, sm_scale=sm)
+    eo, _ = orc.attn_ex(Qb, Kb, Vb, sm_scale=sm)
+    for tau in (2.0, 3.0):
+        b = orc.run_qe(Qb, Kb, Vb, pv="fp8", BN=64, tau=tau, sm_scale=sm)
+        np.testing.assert_allclose(b.lse, a.lse, atol=2e-5)
+        # rounding noise: each emulation is ~4% (rel-L1) from exact attention, so the two differ
+        # by that order, while their distances to exact attention agree much more closely
+        assert _rel_l1(b.o32, a.o32) < 1.5 * _rel_l1(a.o32, eo)
+        assert abs(_rel_l1(b.o32, eo) - _rel_l1(a.o32, eo)) < 5e-3
+    with pytest.raises(ValueError):
+        orc.run_qe(Qb, Kb, Vb, pv="fp8", tau=1.5)
+
+
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
 def test_qe_rounded_rowsum_is_a_per_row_rescale(orc, pv):
     """Summing the rounded P instead of the fp32 p changes only the denominator l: the accumulated
