@@ -110,11 +110,12 @@ int sage_block_n(sage_pv_dtype pv);
 /* Lazy-maximum threshold of the online softmax, in log2 units: sage_attn_fwd moves a row's
  * reference maximum only when a tile's maximum exceeds it by more than this (0 = the exact running
  * maximum).  The normalized result does not depend on it; only the point at which P is rounded
- * does.  8 for SAGE_PV_FP16 (P <= 256 fits fp16), 0 for SAGE_PV_FP8_E4M3.  Host only. */
+ * does.  8 for SAGE_PV_FP16 (P <= 256 fits fp16), 3 for SAGE_PV_FP8_E4M3 (P = e4m3(448 * 2^-tau * p)
+ * <= 448).  Host only. */
 double sage_softmax_tau(sage_pv_dtype pv);
 
 /* 1 if sage_attn_fwd's softmax denominator sums P as rounded for the PV product (fp16 P), 0 if it
- * sums the unrounded fp32 p (e4m3 P, where it sums 448*p).  Either way O = (sum P V) / l with l
+ * sums the unrounded fp32 p (e4m3 P, where it sums 448*2^-tau*p).  Either way O = (sum P V) / l with l
  * over the same keys; the choice moves l by at most the relative rounding error of P.  Host only. */
 int sage_rowsum_rounded(sage_pv_dtype pv);
 
@@ -186,7 +187,7 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  *        sageattn section and on "Utilize SageAttention for Distributed Inference").
  * The online softmax runs over sage_block_n() keys per tile in increasing key order; a row's
  * reference maximum moves when a tile's maximum exceeds it by more than sage_softmax_tau() (log2
- * units); P is rounded to fp16 (or e4m3 of 448*p) against the reference maximum; the denominator
+ * units); P is rounded to fp16 (or e4m3 of 448*2^-tau*p) against the reference maximum; the denominator
  * sums P as rounded or unrounded per sage_rowsum_rounded(); O and l accumulate in fp32.  Keys j >= Nk are masked
  * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
  * gets O = 0 and LSE = -inf.

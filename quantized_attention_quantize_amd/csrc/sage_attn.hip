@@ -223,7 +223,7 @@ __device__ __forceinline__ v4i frag64v(const char* base, const LaneBases& lb, in
 // same reference maximum, and each holds the partial denominator of its half of the keys.
 struct RowState {
   float m;      // reference maximum (log2 units) of the newest scored tile
-  float pm;     // exponent offset of the tile being exponentiated (m, or m - log2(448) for e4m3 P)
+  float pm;     // exponent offset of the tile being exponentiated (m, or m - log2(448) + tau for e4m3 P)
   float l;      // partial denominator
   float alpha;  // 2^(previous m - m) for the tile being exponentiated; O takes it after the
                 // previous tile's PV
@@ -335,7 +335,7 @@ __device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowStat
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(rs.m - m_use);
   rs.m = m_new;
-  pm_new = PV == 1 ? m_use - kLog2_448 : m_use;  // the e4m3 path carries P as 448 * p
+  pm_new = PV == 1 ? m_use - (kLog2_448 - kTau) : m_use;  // the e4m3 path carries P as 448 * 2^-tau * p
   return alpha;
 }
 
@@ -819,7 +819,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     if (g == 0 && a.lse) {
       float v = -INFINITY;
       if (l_tot > 0.f) {
-        // l_tot sums 2^(s - pm) over the row (e4m3 P carries the 448 inside pm)
+        // l_tot sums 2^(s - pm) over the row (e4m3 P carries its scale 448 * 2^-tau inside pm)
         v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.corr[bh * a.Nq + row];
       }
       a.lse[b * a.l_sb + h * a.l_sh + sq.off + row] = v;

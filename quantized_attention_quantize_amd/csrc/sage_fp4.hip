@@ -49,7 +49,7 @@ constexpr float kF4Log2_448 = 8.807354922057604f;  // log2(448)
 // Lazy reference maximum of the online softmax (log2 units): it moves only when a tile's maximum
 // exceeds it by more than kF4Tau, so p = 2^(t - m) <= 2^kF4Tau and P = e4m3(448 * 2^-kF4Tau * p)
 // stays within e4m3's range while O is rarely rescaled.
-constexpr int kF4Tau = 2;
+constexpr int kF4Tau = 3;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));

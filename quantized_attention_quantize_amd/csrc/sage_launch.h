@@ -7,9 +7,10 @@
 namespace sage {
 
 // Lazy online-softmax maximum (log2 units) by PV type: the reference maximum moves only when a
-// tile's maximum exceeds it by more than this, so FP16 P stays <= 2^8 (no overflow) while O is
-// rarely rescaled; e4m3 P (448 * p <= 448) needs the exact running maximum.
-constexpr float kSoftmaxTau[2] = {8.f, 0.f};
+// tile's maximum exceeds it by more than this, so O is rarely rescaled while p = exp(s - m) stays
+// <= 2^tau: FP16 P <= 2^8 (no overflow); e4m3 P is 448 * 2^-tau * p <= 448 (a whole tau keeps
+// that scale exact).
+constexpr float kSoftmaxTau[2] = {8.f, 3.f};
 // Whether the softmax denominator sums P as rounded for the PV product (FP16: one v_dot2 per two
 // probabilities) rather than the fp32 p (e4m3), by PV type.
 constexpr int kRowsumRounded[2] = {1, 0};

@@ -43,7 +43,7 @@ def test_host_queries(L):
     assert L.sage_pad_tokens(0) == 0
     assert L.sage_block_n(0) == 64 and L.sage_block_n(1) == 64
     L.sage_softmax_tau.restype = ctypes.c_double
-    assert L.sage_softmax_tau(0) == 8.0 and L.sage_softmax_tau(1) == 0.0  # FP16 P <= 2^8; e4m3 exact max
+    assert L.sage_softmax_tau(0) == 8.0 and L.sage_softmax_tau(1) == 3.0  # FP16 P <= 2^8; e4m3 448 / 8 * p
     assert L.sage_rowsum_rounded(0) == 1 and L.sage_rowsum_rounded(1) == 0
     assert L.sage_quantize_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_quantize_workspace_bytes(0, 1, 1, 64) == 0
@@ -276,7 +276,7 @@ def L_pad(n):
 
 def test_fp4_host_queries(L):
     assert L.sage_fp4_q_blocks(300, 1) == 3 and L.sage_fp4_q_blocks(300, 0) == 1 and L.sage_fp4_q_blocks(0, 1) == 0
-    assert L.sage_fp4_softmax_tau() == 2.0  # P = e4m3(448 / 4 * p), p <= 4
+    assert L.sage_fp4_softmax_tau() == 3.0  # P = e4m3(448 / 8 * p), p <= 8
     # fp64 partial sums of the larger of the Q and K token-mean reductions (256-token chunks)
     assert L.sage_fp4_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_fp4_workspace_bytes(0, 1, 1, 1, 1, 128) == 0
