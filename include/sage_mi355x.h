@@ -87,7 +87,8 @@ typedef struct {
  *   k_block_mean fp32 [B][Hkv][ceil(Nk/64)][d]  block means (fp64 sum over the block's tokens,
  *                                               one rounding)
  *   blk_corr     fp32 [B][H][ceil(Nk/64)][Nq]   sum_c Q[i,c] * k_block_mean[u,c] (fp32 sums)
- * and k_mean, lse_corr hold zeros (the LSE then needs no shift).  Not combined with an fp32 mask. */
+ * and k_mean, lse_corr hold zeros (the LSE then needs no shift).  Not combined with an fp32 mask.
+ * One head's terms must fit 2 GiB: ceil(Nk/64) * Nq * 4 < 2^31 bytes, else UNSUPPORTED. */
 typedef struct {
   int8_t* q8;
   int8_t* k8;
@@ -131,7 +132,7 @@ size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t
  * Sources: per-block INT8 Q/K and smooth_k on the Triton INT8/FP16 kernel section; smoothing by
  * the global token mean on the sageattn3_blackwell usage section (per_block_mean=False).
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, mismatched B/H/d/dtype, wrong
- * pads or misaligned rows; UNSUPPORTED for d not in {64,128}; WORKSPACE if
+ * pads or misaligned rows; UNSUPPORTED for d not in {64,128} or per_block_mean past its size limit; WORKSPACE if
  * workspace_bytes < sage_quantize_workspace_bytes(). */
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
                              void* workspace, size_t workspace_bytes, void* stream);

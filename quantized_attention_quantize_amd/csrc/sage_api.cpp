@@ -68,6 +68,8 @@ sage_status check_qk(const sage_qk_quant* qk) {
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(qk->q8) || !aligned16(qk->k8)) return SAGE_ERR_INVALID_ARGUMENT;
   if ((qk->k_block_mean == nullptr) != (qk->blk_corr == nullptr)) return SAGE_ERR_INVALID_ARGUMENT;
+  // per_block_mean: one head's score terms are addressed through a 32-bit buffer range
+  if (qk->blk_corr && cdiv(qk->Nk, 64) * qk->Nq * 4 >= ((int64_t)1 << 31)) return SAGE_ERR_UNSUPPORTED;
   return SAGE_OK;
 }
 

@@ -392,7 +392,9 @@ __global__ __launch_bounds__(kF4Threads) __attribute__((amdgpu_waves_per_eu(2)))
       for (int e = 0; e < 4; ++e) {
         const int uu = 32 * (int)grp + 8 * rq + 4 * g + e;
         const int off = uu < a.nqm ? (int)(((int64_t)uu * a.Nk_pad + 32 * kb + lr) * 4) : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, kv ? acc[4 * rq + e] : 0.f), crs, off, 0, 0);
+        // a scalar first: hipcc compiles __builtin_bit_cast of a vector element as element 0
+        const float x = kv ? acc[4 * rq + e] : 0.f;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), crs, off, 0, 0);
       }
   };
   // Two register buffers: the next block's loads are issued before the current block's products

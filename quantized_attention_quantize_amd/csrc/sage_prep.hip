@@ -266,73 +266,112 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // per_block_mean score terms: blk_corr[b,h,u,i] = sum_c Q[i,c] * kbmean[b,hk,u,c] for the valid key
-// blocks u of the sequence, on the matrix cores: D (32 blocks x 32 query rows) += M (32 x 16) Q^T
-// (16 x 32) per 16 channels.  Q enters exactly (it is bf16 / fp16 already); each fp32 block mean
-// is split into a sum of input-format parts (bf16: three parts, 24 significant bits; fp16: two
-// parts, 22 bits) -- the rounding residue of a part is exact in fp32 -- so the products are exact
-// and only the fp32 accumulation rounds.  grid = (ceil(Nq/32), B*H), block = 256: four waves,
-// each over every fourth group of 32 key blocks for the same 32 query rows.
+// blocks u and query rows i of the sequence, on the matrix cores: D (32 blocks x 32 query rows) +=
+// M (32 x 16) Q^T (16 x 32) per 16 channels.  Q enters exactly (it is bf16 / fp16 already); each
+// fp32 block mean is split into a sum of input-format parts (bf16: three parts, 24 significant
+// bits; fp16: two parts, 22 bits) -- the rounding residue of a part is exact in fp32 -- so the
+// products are exact and only the fp32 accumulation rounds.
+// A wave splits the means of one group of 32 key blocks once, keeps the parts in registers and
+// streams up to kpw blocks of 32 query rows past them.  Work item c = (b*H + h) * nchunk + chunk
+// covers 4 * kpw row blocks (wave w takes blocks 4 i + w of the chunk); the ngroups workgroups of
+// one item sit 8 apart in launch order, so they run on one XCD (workgroups are dealt to the 8 XCDs
+// in turn) and read its Q rows through one L2.  Stores outside the sequence's rows and key blocks
+// go to an offset past the head's buffer range, which the hardware drops.
 // ---------------------------------------------------------------------------------------------
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));
 
+__host__ __device__ constexpr int64_t block_corr_chunks(int64_t Nq, int kpw) {
+  return ((Nq + 31) / 32 + 4 * kpw - 1) / (4 * kpw);
+}
+
 template <int D, int IN>
-__global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a) {
+__global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a, int ngroups, int kpw) {
   using V8 = typename std::conditional<IN == 0, v8bf, v8h>::type;
   constexpr int NP = IN == 0 ? 3 : 2;  // parts of a mean
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, g = lane >> 5;
-  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t nchunk = block_corr_chunks(a.Nq, kpw);
+  const int64_t wg = blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
+  if (c >= a.B * a.H * nchunk) return;
+  const int64_t bh = c / nchunk, b = bh / a.H, h = bh % a.H;
   const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);
   const SeqSpan sp = seq_span(a.cu_q, b, a.Nq, a.total_q);
   const SeqSpan sk = seq_span(a.cu_k, b, a.Nk, a.total_k);
-  const int64_t i0 = (int64_t)blockIdx.x * 32;
-  if (i0 >= sp.len) return;
   const int nbk_b = (int)((sk.len + kQuantBlock - 1) / kQuantBlock);
-  // B operands: query row i0 + lr, channels 16 kk + 8 g .. + 8
-  const int64_t row = i0 + lr;
-  const bool rv = row < sp.len;
-  const unsigned short* src = a.q + b * a.q_sb + h * a.q_sh + (sp.off + (rv ? row : 0)) * a.q_sn + 8 * g;
-  V8 qb[D / 16];
+  if (32 * grp >= nbk_b || sp.len <= 0) return;
+  const int64_t nrb = (sp.len + 31) / 32;
+  const int64_t rb0 = (c % nchunk) * 4 * kpw + w;
+  int64_t nb = (nrb - rb0 + 3) / 4;
+  nb = nb < kpw ? nb : kpw;  // row blocks rb0, rb0 + 4, ... of this wave
+  if (nb <= 0) return;
+  // A operand: key block u = 32 grp + lr, channels 16 kk + 8 g .. + 8, as NP exact parts
+  const int u = 32 * (int)grp + lr;
+  const float* mp = a.kbmean + (bhk * a.nbk + (u < nbk_b ? u : 0)) * D + 8 * g;
+  V8 ap[D / 16][NP];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (rv) v = *reinterpret_cast<const u16x8*>(src + 16 * kk);
-    qb[kk] = __builtin_bit_cast(V8, v);
+    v8f m = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (u < nbk_b) {
+      const float4 lo = *reinterpret_cast<const float4*>(mp + 16 * kk);
+      const float4 hi = *reinterpret_cast<const float4*>(mp + 16 * kk + 4);
+      m = v8f{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {  // m = part[0] + part[1] (+ part[2]), residues exact in fp32
+      ap[kk][p] = __builtin_convertvector(m, V8);  // round to nearest even
+      m = m - __builtin_convertvector(ap[kk][p], v8f);
+    }
   }
-  for (int bt = w; bt * 32 < nbk_b; bt += 4) {
-    const int u = bt * 32 + lr;  // A operand: key block u
-    const bool uv = u < nbk_b;
-    const float* mp = a.kbmean + (bhk * a.nbk + (uv ? u : 0)) * D + 8 * g;
+  // B operand: query row 32 rb + lr, channels 16 kk + 8 g .. + 8 (a row past the sequence reads
+  // its last row; its column is not stored)
+  const unsigned short* qh = a.q + b * a.q_sb + h * a.q_sh + sp.off * a.q_sn + 8 * g;
+  auto load_q = [&](int64_t rb, u16x8(&r)[D / 16]) {
+    const int64_t row = 32 * rb + lr;
+    const unsigned short* src = qh + (row < sp.len ? row : sp.len - 1) * a.q_sn;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) r[kk] = *reinterpret_cast<const u16x8*>(src + 16 * kk);
+  };
+  // this head's terms, nbk * Nq * 4 < 2^31 bytes (host-checked)
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.blk_corr + bh * a.nbk * a.Nq), (short)0, (int)(a.nbk * a.Nq * 4), kBufferWord3);
+  constexpr int kOutOfRange = 0x7ffffffc;
+  auto block = [&](int64_t rb, const u16x8(&qr)[D / 16]) {
     v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      v8f m = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (uv) {
-        const float4 lo = *reinterpret_cast<const float4*>(mp + 16 * kk);
-        const float4 hi = *reinterpret_cast<const float4*>(mp + 16 * kk + 4);
-        m = v8f{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
-      V8 part[NP];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {  // m = part[0] + part[1] (+ part[2]), residues exact in fp32
-        part[p] = __builtin_convertvector(m, V8);  // round to nearest even
-        m = m - __builtin_convertvector(part[p], v8f);
-      }
+      const V8 qb = __builtin_bit_cast(V8, qr[kk]);
 #pragma unroll
       for (int p = NP - 1; p >= 0; --p) {  // smallest part first
         if constexpr (IN == 0)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(part[p], qb[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[kk][p], qb, acc, 0, 0, 0);
         else
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(part[p], qb[kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap[kk][p], qb, acc, 0, 0, 0);
       }
     }
-    if (rv) {
+    const int64_t row = 32 * rb + lr;  // D column lr
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {  // D row (r/4)*8 + 4g + r%4 is key block bt*32 + that
-        const int ub = bt * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (ub < nbk_b) a.blk_corr[(bh * a.nbk + ub) * a.Nq + row] = acc[r];
-      }
+    for (int r = 0; r < 16; ++r) {  // D row (r/4)*8 + 4g + r%4 is key block 32 grp + that
+      const int ub = 32 * (int)grp + (r >> 2) * 8 + g * 4 + (r & 3);
+      const int off = (ub < nbk_b && row < sp.len) ? (int)(((int64_t)ub * a.Nq + row) * 4) : kOutOfRange;
+      // copied to a scalar first: hipcc compiles __builtin_bit_cast of a vector element (acc[r])
+      // as element 0 for every r
+      const float x = acc[r];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), crs, off, 0, 0);
     }
+  };
+  // Two register buffers: the next block's loads are issued before the current block's products
+  // (past the end, a block reloads itself).
+  auto rb_of = [&](int64_t i) { return rb0 + 4 * (i < nb ? i : nb - 1); };
+  u16x8 qa[D / 16], qz[D / 16];
+  load_q(rb_of(0), qa);
+  for (int64_t i = 0; i < nb; i += 2) {
+    load_q(rb_of(i + 1), qz);
+    __builtin_amdgcn_sched_barrier(0);
+    block(rb_of(i), qa);
+    if (i + 1 >= nb) break;
+    load_q(rb_of(i + 2), qa);
+    __builtin_amdgcn_sched_barrier(0);
+    block(rb_of(i + 1), qz);
   }
 }
 
@@ -557,12 +596,26 @@ hipError_t launch_token_mean(const unsigned short* x, int in_fp16, int d, int64_
   return hipGetLastError();
 }
 
+// Row blocks per wave of k_block_corr for wave_blocks (key-block group, row block) pairs in all:
+// about 768 waves (three per CU), 1 to 16 blocks each -- a wave's set-up (loading and splitting its
+// means) costs several blocks, so fewer, longer waves are faster.
+static int block_corr_rows_per_wave(int64_t wave_blocks) {
+  const int64_t k = wave_blocks / 768;
+  return (int)(k < 1 ? 1 : (k > 16 ? 16 : k));
+}
+
 hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s) {
-  dim3 g((unsigned)((a.Nq + 31) / 32), (unsigned)(a.B * a.H));
+  const int64_t ngroups = (a.nbk + 31) / 32;
+  const int kpw = block_corr_rows_per_wave(a.B * a.H * ngroups * ((a.Nq + 31) / 32));
+  const int64_t items = a.B * a.H * block_corr_chunks(a.Nq, kpw);
+  const unsigned g = (unsigned)((items + 7) / 8 * 8 * ngroups);
+  const int ng = (int)ngroups;
   if (a.d == 128)
-    a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a) : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a);
+    a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw)
+              : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw);
   else
-    a.in_fp16 ? k_block_corr<64, 1><<<g, kPrepThreads, 0, s>>>(a) : k_block_corr<64, 0><<<g, kPrepThreads, 0, s>>>(a);
+    a.in_fp16 ? k_block_corr<64, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw)
+              : k_block_corr<64, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw);
   return hipGetLastError();
 }
 

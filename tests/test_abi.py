@@ -194,6 +194,24 @@ def test_per_block_mean_validation(L):
     assert call_fwd(L, qk, desc(), mask=FAKE, mdt=1, mask_h=1) == UNSUPPORTED
 
 
+def test_per_block_mean_size_limit(L):
+    """One head's per_block_mean score terms are addressed through a 32-bit buffer range, so
+    ceil(Nk/64) * Nq * 4 bytes past 2^31 is UNSUPPORTED.  A null workspace (checked later) shows
+    that the limit is what rejects the call, and only with per_block_mean."""
+    n = 1 << 20  # 16384 key blocks x 2^20 rows x 4 B = 64 GiB per head
+    q, k = desc(N=n), desc(N=n)
+    out = quant(Nq=n, Nk=n)
+    assert call_quant(L, q, k, out, ws=0) == WORKSPACE
+    out.k_block_mean = FAKE
+    out.blk_corr = FAKE
+    assert call_quant(L, q, k, out, ws=0) == UNSUPPORTED
+    m = 1 << 14  # 256 x 16384 x 4 B = 16 MiB
+    small = quant(Nq=m, Nk=m)
+    small.k_block_mean = FAKE
+    small.blk_corr = FAKE
+    assert call_quant(L, desc(N=m), desc(N=m), small, ws=0) == WORKSPACE
+
+
 def test_debug_validation(L):
     qk = quant()
     out = FAKE
