@@ -49,7 +49,8 @@ def mfma_peak(pv: str, method: str = "int8") -> float:
     pv_peak = FP16_PEAK_TOPS if pv == "fp16" else INT8_PEAK_TOPS
     return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
 KERNEL_SOURCES = {"k_attn_fwd": ["quantized_attention_quantize_amd/csrc/sage_attn.hip",
-                                  "quantized_attention_quantize_amd/csrc/sage_device.h"],
+                                  "quantized_attention_quantize_amd/csrc/sage_device.h",
+                                  "quantized_attention_quantize_amd/csrc/sage_launch.h"],
                   "k_fp4_attn": ["quantized_attention_quantize_amd/csrc/sage_fp4.hip",
                                  "quantized_attention_quantize_amd/csrc/sage_device.h"]}
 

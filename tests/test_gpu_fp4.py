@@ -90,6 +90,25 @@ def test_fp4_parity(orc, case):
         assert cs >= 0.97 and rl <= 0.25
 
 
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,pbm", [(1, 2, 2, 4500, 1100, True), (1, 8, 4, 4500, 4000, True),
+                                              (2, 4, 4, 3000, 2600, False)])
+def test_fp4_quantize_groups_of_q_blocks(orc, B, H, Hkv, Nq, Nk, pbm):
+    """Quantization bit-exact and correction rows within fp32 accumulation error where the
+    correction kernel takes more than one group of 32 Q blocks (36 blocks: a partial second group)
+    and, for 8 heads x 4000 keys, two key blocks per wave; and with the global Q mean."""
+    say(f"fp4 quantize B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} per_block_mean={pbm}")
+    inp = make_inputs(B, H, Nq, Nk, 128, sigma=4.0, seed=95, Hkv=Hkv)
+    q, k, v = to_dev(inp)
+    g = sage.quantize_qkv_fp4(q, k, v, per_block_mean=pbm)
+    torch.cuda.synchronize()
+    Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+    r = orc.fp4_quant_qk(Q, K, per_block_mean=pbm)
+    v4, ve = orc.fp4_prep_v(V)
+    Kf = f32_of_bf16_bits(K)
+    k_max = max(float(np.abs(Kf).max()), float(np.abs(Kf - r.kmean[:, :, None, :]).max()))
+    fp4_check_quant(g, r, Nq, Nk, (v4, ve), k_max)
+
+
 def test_fp4_debug_scores_window(orc):
     B, H, Nq, Nk, d = 1, 2, 300, 200, 128
     inp = make_inputs(B, H, Nq, Nk, d, seed=91)

@@ -79,10 +79,13 @@ def test_quantize_bitexact_gqa(orc, B, H, Hkv, Nq, Nk, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
-@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", [(1, 2, 2, 300, 417, 128), (2, 4, 2, 129, 65, 64), (1, 1, 1, 700, 1000, 128)])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d", [(1, 2, 2, 300, 417, 128), (2, 4, 2, 129, 65, 64), (1, 1, 1, 700, 1000, 128),
+                                             (1, 2, 2, 1100, 2500, 128), (1, 4, 2, 8192, 2500, 64)])
 def test_quantize_per_block_mean(orc, B, H, Hkv, Nq, Nk, d, dtype):
     """per_block_mean: block means, codes and scales bit-exact; the score terms within fp32
-    accumulation of the oracle's fp64 dot products; the global mean and the LSE shift zero."""
+    accumulation of the oracle's fp64 dot products; the global mean and the LSE shift zero.  The
+    last two shapes have 40 key blocks (a second, partial group of 32 for the score kernel), the
+    last one two 32-row blocks per wave."""
     say(f"quantize per_block_mean B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype}")
     inp = make_inputs(B, H, Nq, Nk, d, sigma=4.0, seed=9, dtype=dtype)
     if Hkv != H:
