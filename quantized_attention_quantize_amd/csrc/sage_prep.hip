@@ -429,7 +429,26 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
   }
 }
 
-// V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1>.
+// max over chunks of the column maxima of k_colred_partial<MODE 1>, written over the first chunk's
+// entry (grid = B*H, block = D; eight loads in flight per step)
+template <int D>
+__global__ __launch_bounds__(D) void k_vmax_final(float* __restrict__ partial, int nchunk) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  float m = 0.f;
+  int i = 0;
+  for (; i + 8 <= nchunk; i += 8) {
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = partial[(bh * nchunk + i + k) * D + c];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, p[k]);
+  }
+  for (; i < nchunk; ++i) m = fmaxf(m, partial[(bh * nchunk + i) * D + c]);
+  partial[(bh * nchunk) * D + c] = m;
+}
+
+// V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1> and k_vmax_final.
 template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
   constexpr int CG = D / 8;
@@ -440,8 +459,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t k0 = (int64_t)blockIdx.x * 64;
   if (t < D) {
-    float m = 0.f;
-    for (int i = 0; i < a.nchunk; ++i) m = fmaxf(m, a.vmax_partial[(bh * a.nchunk + i) * D + t]);
+    const float m = a.vmax_partial[(bh * a.nchunk) * D + t];  // max over chunks (k_vmax_final)
     float sc = 0.f, inv = 0.f;
     if (m > 0.f) {
       sc = m / 448.0f;
@@ -644,6 +662,7 @@ static void launch_prep_v_t(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
     dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
     k_colred_partial<D, 1, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
                                                           a.nchunk, a.cu_k, a.total_k);
+    k_vmax_final<D><<<(unsigned)(a.B * a.H), D, 0, s>>>(a.vmax_partial, a.nchunk);
     k_prep_v8<D, IN><<<g, kPrepThreads, 0, s>>>(a);
   }
 }
