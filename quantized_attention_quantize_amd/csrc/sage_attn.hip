@@ -749,7 +749,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       alpha = tile_step<D, PV, false, false, BM>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g,
                                                  kBlockN - 1, nullptr, false, false, cb_cur);
     }
-    // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare for the lazy FP16 maximum)
+    // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare under the lazy maximum)
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
     c_cur = scale_of(tn);
     cb_cur = cb_nxt;

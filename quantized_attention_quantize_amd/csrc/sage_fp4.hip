@@ -15,8 +15,8 @@
 //    microscaling format, so the block scales are applied inside the MFMA.
 //  * Quantization: Q (its 128-token block means or global mean, smoothing, codes, the LSE shift of
 //    K's smoothing), K (smoothed by its global mean, codes), V (codes along the tokens, written
-//    transposed) and the correction rows qk_corr[u][j] = qmean_u . (K_j - kmean) on the bf16 MFMA
-//    with exact three-part splits of both fp32 operands.
+//    transposed) and the correction rows qk_corr[u][j] = qmean_u . (K_j - kmean), formed as
+//    qmean_u . K_j - qmean_u . kmean on the bf16 MFMA from exact bf16 parts of qmean and K.
 //  * Attention: the INT8 kernel's organisation (8 waves x 32 query rows per workgroup, a
 //    four-stage LDS ring filled by direct buffer-to-LDS loads two tiles ahead, one barrier per
 //    64-key tile; in each wave the PV of tile n-1, the softmax of tile n and the QK of tile n+1
@@ -32,9 +32,9 @@
 //      on the k-elements that the e2m1 V operand of lane group g pairs with keys [32g, 32g+32), and
 //      V^T needs no key permutation -- its MX blocks are 32 consecutive tokens;
 //    - O^T += V^T P^T on the same MFMA with A = e2m1 V (scale per channel and 32-token block) and
-//      B = e4m3 P with unit scale; P = 448 * 2^-2 * p under a reference maximum that moves only
-//      when a tile exceeds it by more than 2 log2 units (p <= 4, P <= 448), so the whole-wave
-//      rescaling of O is rare.
+//      B = e4m3 P with unit scale; P = 448 * 2^-tau * p under a reference maximum that moves only
+//      when a tile exceeds it by more than tau = kF4Tau log2 units (p <= 2^tau, P <= 448), so the
+//      whole-wave rescaling of O is rare.
 //    The tile's correction values and K / V scale bytes travel through the LDS ring with the K and
 //    V codes.  Head dimension 128.
 #include "sage_device.h"
