@@ -293,18 +293,22 @@ __device__ __forceinline__ void split3(v8f x, v8bf (&p)[3]) {
 // 4 * kpw key blocks (wave w takes blocks 4 i + w of the chunk).  The ngroups workgroups of one
 // item sit 8 apart in launch order: workgroups are dealt to the 8 XCDs in turn, so all groups of
 // an item run on one XCD and read its K through one L2.
+// Workgroup ids per launch of k_fp4_corr, whose id count grows with Nq * Nk: larger problems take
+// several launches, each from an offset wg0 that is a multiple of 8 (the id's XCD is kept).
+constexpr int64_t kF4MaxCorrLaunch = (int64_t)1 << 20;
+
 __host__ __device__ constexpr int64_t f4corr_chunks(int64_t Nk_pad, int kpw) {
   return (Nk_pad / 32 + 4 * kpw - 1) / (4 * kpw);
 }
 
 template <int D, int IN>
 __global__ __launch_bounds__(kF4Threads) __attribute__((amdgpu_waves_per_eu(2))) void k_fp4_corr(Fp4QuantArgs a,
-                                                                                                  int ngroups,
-                                                                                                  int kpw) {
+                                                                                                  int ngroups, int kpw,
+                                                                                                  int64_t wg0) {
   __shared__ float km_s[D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, g = lane >> 5;
   const int64_t nchunk = f4corr_chunks(a.Nk_pad, kpw), nkb = a.Nk_pad / 32;
-  const int64_t wg = blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
+  const int64_t wg = wg0 + blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
   if (c >= a.B * a.H * nchunk) return;  // the whole workgroup, before the barrier
   const int64_t bh = c / nchunk, b = bh / a.H, h = bh % a.H;
   const int64_t hk = h / (a.H / a.Hkv), bhk = b * a.Hkv + hk;
@@ -955,7 +959,11 @@ static void launch_fp4_quant_t(const Fp4QuantArgs& a, hipStream_t s) {
   const int64_t ngroups = (a.nqm + 31) / 32;
   const int kpw = fp4_corr_blocks_per_wave(a.B * a.H * ngroups * (a.Nk_pad / 32));
   const int64_t items = a.B * a.H * f4corr_chunks(a.Nk_pad, kpw);
-  k_fp4_corr<D, IN><<<(unsigned)((items + 7) / 8 * 8 * ngroups), kF4Threads, 0, s>>>(a, (int)ngroups, kpw);
+  const int64_t nwg = (items + 7) / 8 * 8 * ngroups;
+  for (int64_t wg0 = 0; wg0 < nwg; wg0 += kF4MaxCorrLaunch) {
+    const unsigned g = (unsigned)(nwg - wg0 < kF4MaxCorrLaunch ? nwg - wg0 : kF4MaxCorrLaunch);
+    k_fp4_corr<D, IN><<<g, kF4Threads, 0, s>>>(a, (int)ngroups, kpw, wg0);
+  }
 }
 
 // K mean; the global Q mean (not per_block) into q_mean; then Q, K, V and the correction rows.

@@ -281,17 +281,21 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));
 
+// Workgroup ids per launch of k_block_corr, whose id count grows with Nq * Nk: larger problems
+// take several launches, each from an offset wg0 that is a multiple of 8 (the id's XCD is kept).
+constexpr int64_t kMaxCorrLaunch = (int64_t)1 << 20;
+
 __host__ __device__ constexpr int64_t block_corr_chunks(int64_t Nq, int kpw) {
   return ((Nq + 31) / 32 + 4 * kpw - 1) / (4 * kpw);
 }
 
 template <int D, int IN>
-__global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a, int ngroups, int kpw) {
+__global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a, int ngroups, int kpw, int64_t wg0) {
   using V8 = typename std::conditional<IN == 0, v8bf, v8h>::type;
   constexpr int NP = IN == 0 ? 3 : 2;  // parts of a mean
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, g = lane >> 5;
   const int64_t nchunk = block_corr_chunks(a.Nq, kpw);
-  const int64_t wg = blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
+  const int64_t wg = wg0 + blockIdx.x, grp = (wg >> 3) % ngroups, c = (wg & 7) + 8 * ((wg >> 3) / ngroups);
   if (c >= a.B * a.H * nchunk) return;
   const int64_t bh = c / nchunk, b = bh / a.H, h = bh % a.H;
   const int64_t bhk = b * a.Hkv + h / (a.H / a.Hkv);
@@ -626,14 +630,17 @@ hipError_t launch_block_corr(const QuantArgs& a, hipStream_t s) {
   const int64_t ngroups = (a.nbk + 31) / 32;
   const int kpw = block_corr_rows_per_wave(a.B * a.H * ngroups * ((a.Nq + 31) / 32));
   const int64_t items = a.B * a.H * block_corr_chunks(a.Nq, kpw);
-  const unsigned g = (unsigned)((items + 7) / 8 * 8 * ngroups);
+  const int64_t nwg = (items + 7) / 8 * 8 * ngroups;
   const int ng = (int)ngroups;
-  if (a.d == 128)
-    a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw)
-              : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw);
-  else
-    a.in_fp16 ? k_block_corr<64, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw)
-              : k_block_corr<64, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw);
+  for (int64_t wg0 = 0; wg0 < nwg; wg0 += kMaxCorrLaunch) {
+    const unsigned g = (unsigned)(nwg - wg0 < kMaxCorrLaunch ? nwg - wg0 : kMaxCorrLaunch);
+    if (a.d == 128)
+      a.in_fp16 ? k_block_corr<128, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw, wg0)
+                : k_block_corr<128, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw, wg0);
+    else
+      a.in_fp16 ? k_block_corr<64, 1><<<g, kPrepThreads, 0, s>>>(a, ng, kpw, wg0)
+                : k_block_corr<64, 0><<<g, kPrepThreads, 0, s>>>(a, ng, kpw, wg0);
+  }
   return hipGetLastError();
 }
 
