@@ -223,12 +223,13 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_quant_k(Fp4QuantArgs a) {
 }
 
 // V: per channel and 32-token block, MX codes along the tokens, written transposed.  grid =
-// (Nk_pad / 64, B*Hkv), block = 256: the 64 x D tile goes through LDS; thread t < 2D then
+// (Nk_pad / 64, B*Hkv), block = 256: the 64 x D tile goes through LDS as its raw 16-bit inputs
+// (half the bytes of fp32, so twice the workgroups per CU hide the loads); thread t < 2D then
 // quantizes channel t % D over the tile's 32-token block t / D.  Tokens past Nk count as zero.
 template <int D, int IN>
 __global__ __launch_bounds__(kF4Threads) void k_fp4_prep_v(Fp4QuantArgs a) {
   constexpr int CG = D / 8, RPI = kF4Threads / CG, TPT = 64 / RPI;
-  __shared__ float sv[64][D + 1];  // +1: a column read by consecutive channels is conflict free
+  __shared__ unsigned short sv[64][D + 2];  // raw inputs (17 KB: eight workgroups per CU)
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bhk = blockIdx.y, b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
@@ -240,10 +241,10 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_prep_v(Fp4QuantArgs a) {
     if (tok < a.Nk) {
       const u16x8 v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[r][cg * 8 + j] = in_to_f32<IN>(v[j]);
+      for (int j = 0; j < 8; ++j) sv[r][cg * 8 + j] = v[j];
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[r][cg * 8 + j] = 0.f;
+      for (int j = 0; j < 8; ++j) sv[r][cg * 8 + j] = 0;
     }
   }
   __syncthreads();
@@ -251,18 +252,17 @@ __global__ __launch_bounds__(kF4Threads) void k_fp4_prep_v(Fp4QuantArgs a) {
     const int c = t % D, blk = t / D;
     float amax = 0.f;
 #pragma unroll 8
-    for (int k = 0; k < kMX; ++k) amax = fmaxf(amax, fabsf(sv[kMX * blk + k][c]));
+    for (int k = 0; k < kMX; ++k) amax = fmaxf(amax, fabsf(in_to_f32<IN>(sv[kMX * blk + k][c])));
     float inv;
     const unsigned e8 = mx_scale_byte(amax, inv);
     unsigned w[4] = {0u, 0u, 0u, 0u};
-    const float* col = &sv[kMX * blk][c];
+    auto x = [&](int k) { return in_to_f32<IN>(sv[kMX * blk + k][c]) * inv; };
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // tokens 8 q .. 8 q + 7 into word q
-      const float* t8 = col + 8 * q * (D + 1);
-      w[q] = e2m1_pair<0>(w[q], t8[0] * inv, t8[D + 1] * inv);
-      w[q] = e2m1_pair<1>(w[q], t8[2 * (D + 1)] * inv, t8[3 * (D + 1)] * inv);
-      w[q] = e2m1_pair<2>(w[q], t8[4 * (D + 1)] * inv, t8[5 * (D + 1)] * inv);
-      w[q] = e2m1_pair<3>(w[q], t8[6 * (D + 1)] * inv, t8[7 * (D + 1)] * inv);
+      w[q] = e2m1_pair<0>(w[q], x(8 * q), x(8 * q + 1));
+      w[q] = e2m1_pair<1>(w[q], x(8 * q + 2), x(8 * q + 3));
+      w[q] = e2m1_pair<2>(w[q], x(8 * q + 4), x(8 * q + 5));
+      w[q] = e2m1_pair<3>(w[q], x(8 * q + 6), x(8 * q + 7));
     }
     uint8_t* dst = a.v4t + (bhk * D + c) * (a.Nk_pad / 2) + blockIdx.x * 32 + blk * 16;
     *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
