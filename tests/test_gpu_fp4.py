@@ -51,6 +51,9 @@ CASES = [
     dict(name="one_query", B=1, H=2, Nq=1, Nk=300, causal=True),
     dict(name="large_k_mean", B=1, H=2, Nq=400, Nk=450, sigma=96.0),
     dict(name="large_k_mean_fp16", B=1, H=2, Nq=200, Nk=333, sigma=96.0, dtype=torch.float16),
+    # peaked rows: p reaches 2^tau under the lazy maximum (P = 448 * 2^-tau * p nears 448); FP4's
+    # distance to exact attention grows with the peak, so only parity with the emulation is checked
+    dict(name="peaked_causal", B=1, H=2, Nq=300, Nk=500, causal=True, sm_scale=0.3, budget=False),
 ]
 
 
@@ -65,7 +68,8 @@ def test_fp4_parity(orc, case):
     inp = make_inputs(B, H, Nq, Nk, d, sigma=c.get("sigma", 4.0), seed=90, Hkv=Hkv, dtype=tdt)
     q, k, v = to_dev(inp)
     g = sage.quantize_qkv_fp4(q, k, v, per_block_mean=pbm)
-    out, lse = sage.attn_fwd_fp4(g, is_causal=causal, return_lse=True, out_dtype=c.get("out"))
+    sm = c.get("sm_scale")
+    out, lse = sage.attn_fwd_fp4(g, is_causal=causal, sm_scale=sm, return_lse=True, out_dtype=c.get("out"))
     torch.cuda.synchronize()
     Q, K, V = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     r = orc.fp4_quant_qk(Q, K, dtype=dts, per_block_mean=pbm)
@@ -76,17 +80,17 @@ def test_fp4_parity(orc, case):
     say("  quantization bit-exact")
     out_dt = c.get("out") or tdt
     ods = {torch.float32: "bf16", torch.bfloat16: "bf16", torch.float16: "fp16"}[out_dt]
-    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=causal, tau=sage.softmax_tau_fp4(), out_dtype=ods)
+    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=causal, sm_scale=sm, tau=sage.softmax_tau_fp4(), out_dtype=ods)
     got = _out_f32(out).reshape(-1, d)
     want = o32 if out_dt == torch.float32 else _dec(o16, ods)
     e1 = rel_l1(got, want)
     say(f"  rel-L1 vs emulation {e1:.3e}")
     assert e1 <= 1e-3
     assert_lse_close(lse.cpu().numpy().reshape(-1), qlse, 1e-3)
-    eo, el = orc.attn_ex(Q, K, V, causal=causal, dtype=dts)
+    eo, el = orc.attn_ex(Q, K, V, causal=causal, sm_scale=sm, dtype=dts)
     cs, rl = cosine(got, eo), rel_l1(got, eo)
     say(f"  vs exact: cosine {cs:.5f} rel-L1 {rl:.3e}")
-    if Nk > 1 and Nq > 1:
+    if Nk > 1 and Nq > 1 and c.get("budget", True):
         assert cs >= 0.97 and rl <= 0.25
 
 

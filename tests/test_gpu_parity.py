@@ -256,7 +256,7 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     return got_o, got_l, r, ex_o, ex_l
 
 
-def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16"):
+def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16", ex_cos=EX_COS):
     qe_o = f32_of_bf16_bits(r.o16) if out_dtype == "bf16" else r.o16.view(np.float16).astype(np.float32)
     e1 = rel_l1(got_o, qe_o)
     assert e1 <= QE_REL_L1, f"rel-L1 vs quantized emulation {e1}"
@@ -265,7 +265,7 @@ def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16"):
     if live.any():
         cos = cosine(got_o[live], ex_o[live])
         ex1 = rel_l1(got_o[live], ex_o[live])
-        assert cos >= EX_COS, f"cosine vs exact {cos}"
+        assert cos >= ex_cos, f"cosine vs exact {cos}"
         assert ex1 <= (EX_REL_L1 if pv == "fp16" else 5e-2), f"rel-L1 vs exact {ex1}"
     return e1
 
@@ -285,6 +285,11 @@ CASES = [
     dict(name="fp8_d64_causal", B=1, H=2, Nq=300, Nk=300, d=64, pv="fp8", causal=True),
     dict(name="fp8_mask", B=1, H=2, Nq=256, Nk=320, d=128, pv="fp8", mask="half"),
     dict(name="sm_scale", B=1, H=2, Nq=256, Nk=256, d=128, sm_scale=0.05),
+    # peaked rows: under the lazy maximum p reaches 2^tau, so e4m3 P = 448 * 2^-tau * p nears 448
+    # (e4m3 P and V on rows this peaked are at cosine 0.9989 from exact attention in the emulation
+    # itself, with the exact running maximum as with the lazy one)
+    dict(name="fp8_peaked", B=1, H=2, Nq=300, Nk=900, d=128, pv="fp8", sm_scale=0.6, ex_cos=0.998),
+    dict(name="fp16_peaked_causal", B=1, H=2, Nq=400, Nk=400, d=128, sm_scale=0.6, causal=True),
     dict(name="nhd", B=2, H=3, Nq=200, Nk=260, d=64, layout="NHD"),
     dict(name="gqa", B=1, H=4, Hkv=2, Nq=300, Nk=417, d=128),
     dict(name="gqa_fp8_causal", B=2, H=6, Hkv=2, Nq=257, Nk=257, d=64, pv="fp8", causal=True),
@@ -364,7 +369,7 @@ def test_attention_parity(orc, case):
                                            sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"),
                                            smooth_v=c.get("smooth_v", False),
                                            per_block_mean=c.get("per_block_mean", False))
-    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype)
+    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype, ex_cos=c.get("ex_cos", EX_COS))
     say(f"  rel-L1 vs QE {e1:.3e}")
 
 
