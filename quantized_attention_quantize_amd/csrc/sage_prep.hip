@@ -452,12 +452,14 @@ __global__ __launch_bounds__(D) void k_vmax_final(float* __restrict__ partial, i
   partial[(bh * nchunk) * D + c] = m;
 }
 
-// V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1> and k_vmax_final.
+// V -> e4m3.  The per-channel maxima come from k_colred_partial<MODE 1> and k_vmax_final.  The
+// tile goes through LDS as its raw 16-bit inputs (half the bytes of fp32: twice the workgroups per
+// CU to hide the loads); the scaling and saturation follow the LDS read.
 template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPI = kPrepThreads / CG;
-  __shared__ float tile[64][D + 1];
+  __shared__ unsigned short tile[64][D + 2];
   __shared__ float inv_s[D];
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -480,24 +482,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
     u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
     if (tok < sp.len) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float f = in_to_f32<IN>(v[j]) * inv_s[cg * 8 + j];
-      if (fabsf(f) > 448.f) f = copysignf(448.f, f);  // saturate (NaN passes through)
-      tile[r][cg * 8 + j] = f;
-    }
+    for (int j = 0; j < 8; ++j) tile[r][cg * 8 + j] = v[j];
   }
   __syncthreads();
   // D rows x 4 chunks of 16 bytes; chunk q holds positions [16q, 16q+16)
   uint8_t* dst = static_cast<uint8_t*>(a.vt) + (bh * D) * a.Nk_pad + k0;
   for (int i = t; i < D * 4; i += kPrepThreads) {
     int c = i / 4, q = i % 4;
+    const float inv = inv_s[c];
+    auto x = [&](int key) {
+      float f = in_to_f32<IN>(tile[key][c]) * inv;
+      return fabsf(f) > 448.f ? copysignf(448.f, f) : f;  // saturate (NaN passes through)
+    };
     v4i o;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       int p = q * 16 + w * 4;
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(tile[fp8_pos_to_key(p)][c], tile[fp8_pos_to_key(p + 1)][c], 0, false);
-      o[w] = __builtin_amdgcn_cvt_pk_fp8_f32(tile[fp8_pos_to_key(p + 2)][c], tile[fp8_pos_to_key(p + 3)][c], lo,
-                                             true);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x(fp8_pos_to_key(p)), x(fp8_pos_to_key(p + 1)), 0, false);
+      o[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x(fp8_pos_to_key(p + 2)), x(fp8_pos_to_key(p + 3)), lo, true);
     }
     *reinterpret_cast<v4i*>(dst + (int64_t)c * a.Nk_pad + q * 16) = o;
   }
