@@ -103,12 +103,13 @@ __device__ __forceinline__ void mx_store8(const float (&x)[8], int cg, uint8_t* 
 // ---------------------------------------------------------------------------------------------
 // Q: block means (per_block) or the global mean from q_mean, smoothing, MX codes per 32 channels,
 // and lse_corr[i] = sum_c fp64(Q[i,c]) * fp64(kmean[c]) of the query head's key head.
-// grid = (Nq_pad / 128, B*H), block = 256: thread t holds channels [8 (t % (D/8)), +8) of the
-// block's tokens t / (D/8) + i * (256 / (D/8)).  Rows past Nq get zero codes and scale bytes.
+// grid = (Nq_pad / 128, B*H), block = 512: thread t holds channels [8 (t % (D/8)), +8) of the
+// block's tokens t / (D/8) + i * (512 / (D/8)) -- four tokens a thread at d = 128, whose 72
+// registers leave room for seven waves per SIMD.  Rows past Nq get zero codes and scale bytes.
 // ---------------------------------------------------------------------------------------------
 template <int D, int IN>
-__global__ __launch_bounds__(kF4Threads) void k_fp4_quant_q(Fp4QuantArgs a) {
-  constexpr int CG = D / 8, RPI = kF4Threads / CG, TPT = kQMB / RPI;
+__global__ __launch_bounds__(2 * kF4Threads) void k_fp4_quant_q(Fp4QuantArgs a) {
+  constexpr int CG = D / 8, RPI = 2 * kF4Threads / CG, TPT = kQMB / RPI;
   __shared__ double csum[RPI][D];
   __shared__ float qm_s[D];
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
@@ -953,7 +954,7 @@ static int fp4_corr_blocks_per_wave(int64_t wave_blocks) {
 
 template <int D, int IN>
 static void launch_fp4_quant_t(const Fp4QuantArgs& a, hipStream_t s) {
-  k_fp4_quant_q<D, IN><<<dim3((unsigned)(a.Nq_pad / kQMB), (unsigned)(a.B * a.H)), kF4Threads, 0, s>>>(a);
+  k_fp4_quant_q<D, IN><<<dim3((unsigned)(a.Nq_pad / kQMB), (unsigned)(a.B * a.H)), 2 * kF4Threads, 0, s>>>(a);
   k_fp4_quant_k<D, IN><<<dim3((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.Hkv)), kF4Threads, 0, s>>>(a);
   k_fp4_prep_v<D, IN><<<dim3((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.Hkv)), kF4Threads, 0, s>>>(a);
   const int64_t ngroups = (a.nqm + 31) / 32;
