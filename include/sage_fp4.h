@@ -19,10 +19,9 @@
  *     (clamped to [-127, 127]; -127 for an all-zero block), elements round to the nearest e2m1
  *     value with ties to the even code and saturate at 6.  This is the block-scale format that
  *     gfx950's scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) applies in hardware.
- *   - P is quantized to e4m3 as in the FP8 PV path, scaled to leave room for a lazy reference
- *     maximum: over 64-key tiles the maximum moves only when a tile exceeds it by more than
- *     sage_fp4_softmax_tau() log2 units, p = exp(s - m) <= 2^tau and P = e4m3(448 * 2^-tau * p);
- *     the softmax denominator sums the unquantized p; O accumulates in fp32.
+ *   - P is quantized to e4m3 as in the FP8 PV path: over 64-key tiles against the exact running
+ *     maximum (sage_fp4_softmax_tau() = 0), p = exp(s - m) <= 1 and P = e4m3(448 * p); the
+ *     softmax denominator sums the unquantized p; O accumulates in fp32.
  *
  * Conventions as in sage_mi355x.h: device pointers, caller-owned buffers, no allocation or
  * synchronization, host validation before anything is enqueued, stream as void*.  head_dim must
@@ -72,10 +71,9 @@ typedef struct {
 /* Rows of q_mean / qk_corr per head: ceil(Nq/128) with per_block_mean, else 1.  Host only. */
 int64_t sage_fp4_q_blocks(int64_t Nq, int per_block_mean);
 
-/* Lazy-maximum threshold of sage_fp4_attn_fwd's online softmax in log2 units (a whole number):
- * the reference maximum moves only when a 64-key tile's maximum exceeds it by more than this, and
- * P = e4m3(448 * 2^-tau * p).  The normalized result does not depend on it; only the point at
- * which P is rounded does.  Host only. */
+/* Threshold of sage_fp4_attn_fwd's online softmax in log2 units: the reference maximum moves when
+ * a 64-key tile's maximum exceeds it by more than this.  It is 0, the exact running maximum, so
+ * P = e4m3(448 * p) with p <= 1.  Host only. */
 double sage_fp4_softmax_tau(void);
 
 /* Workspace bytes sage_fp4_quantize_qkv needs (fp64 partial sums of the token means).  Host only. */
@@ -101,7 +99,8 @@ sage_status sage_fp4_quantize_qkv(const sage_qkv_desc* q, const sage_qkv_desc* k
 
 /* Step 2 (attention) on the packed tensors of step 1.
  *   causal: key j is visible to query i only if j <= i (top-left aligned).
- *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
+ *   sm_scale: <= 0 selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale); NaN or +-inf is
+ *        INVALID_ARGUMENT.
  *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 / SAGE_FP16 rounded to nearest even, or SAGE_F32),
  *        addressed with out_stride_{b,h,n} in elements (rows 16-byte aligned).
  *   lse: NULL, or fp32 [B][H][Nq] contiguous: natural-log log-sum-exp of the scaled scores of the

@@ -101,6 +101,21 @@ typedef struct {
   float* blk_corr;
 } sage_qk_quant;
 
+/* Bytes of one device allocation holding every buffer of a sage_qk_quant for these sizes: q8, k8,
+ * q_scale, k_scale, k_mean, lse_corr and, with per_block_mean nonzero, k_block_mean and blk_corr,
+ * in that order, each starting on a 256-byte boundary.  0 if the sizes are invalid (non-positive,
+ * Hkv not dividing H, d not in {64,128}).  Host only.  (The separate quantize -> attention steps
+ * with caller-owned buffers: FlashInfer API doc, flashinfer.nvfp4_attention_sm120_fwd.) */
+size_t sage_qk_quant_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int per_block_mean);
+
+/* Lays a sage_qk_quant out in one caller allocation: fills every pointer of *out (offsets as in
+ * sage_qk_quant_bytes from base), the sizes and the pads.  base must be 256-byte aligned and hold
+ * at least sage_qk_quant_bytes(...) bytes.  Host only: touches neither HIP nor the memory; the
+ * caller still owns the allocation.  Errors: INVALID_ARGUMENT (null base or out, misaligned base,
+ * bytes too small, invalid sizes). */
+sage_status sage_qk_quant_init(void* base, size_t bytes, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                               int64_t d, int per_block_mean, sage_qk_quant* out);
+
 /* Padded token extent of q8 / k8 / prepared V: n rounded up to a multiple of 128. Host only. */
 int64_t sage_pad_tokens(int64_t n);
 
@@ -108,16 +123,16 @@ int64_t sage_pad_tokens(int64_t n);
  * tile, which fixes where P is rounded).  Host only. */
 int sage_block_n(sage_pv_dtype pv);
 
-/* Lazy-maximum threshold of the online softmax, in log2 units: sage_attn_fwd moves a row's
+/* Threshold of the online softmax's reference maximum, in log2 units: sage_attn_fwd moves a row's
  * reference maximum only when a tile's maximum exceeds it by more than this (0 = the exact running
  * maximum).  The normalized result does not depend on it; only the point at which P is rounded
- * does.  8 for SAGE_PV_FP16 (P <= 256 fits fp16), 3 for SAGE_PV_FP8_E4M3 (P = e4m3(448 * 2^-tau * p)
- * <= 448).  Host only. */
+ * does.  8 for SAGE_PV_FP16 (a lazy maximum: P <= 256 fits fp16), 0 for SAGE_PV_FP8_E4M3 (the
+ * exact running maximum: P = e4m3(448 * p) with p <= 1).  Host only. */
 double sage_softmax_tau(sage_pv_dtype pv);
 
-/* 1 if sage_attn_fwd's softmax denominator sums P as rounded for the PV product (fp16 P), 0 if it
- * sums the unrounded fp32 p (e4m3 P, where it sums 448*2^-tau*p).  Either way O = (sum P V) / l with l
- * over the same keys; the choice moves l by at most the relative rounding error of P.  Host only. */
+/* 1 if sage_attn_fwd's softmax denominator sums P as rounded for the PV product, 0 if it sums the
+ * unrounded fp32 p.  It is 0 for both PV types: the denominator is the plain softmax sum.  Host
+ * only. */
 int sage_rowsum_rounded(sage_pv_dtype pv);
 
 /* Bytes of workspace sage_quantize_qk needs (fp64 partial sums of the K mean); Hkv = heads of K.
@@ -132,7 +147,8 @@ size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t
  * Sources: per-block INT8 Q/K and smooth_k on the Triton INT8/FP16 kernel section; smoothing by
  * the global token mean on the sageattn3_blackwell usage section (per_block_mean=False).
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes, mismatched B/H/d/dtype, wrong
- * pads or misaligned rows; UNSUPPORTED for d not in {64,128} or per_block_mean past its size limit; WORKSPACE if
+ * pads or misaligned rows; UNSUPPORTED for d not in {64,128}, for one head's K8 rows past a 32-bit buffer
+ * range (Nk_pad * d >= 2^31) or per_block_mean past its size limit; WORKSPACE if
  * workspace_bytes < sage_quantize_workspace_bytes(). */
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
                              void* workspace, size_t workspace_bytes, void* stream);
@@ -175,10 +191,13 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  *   mask: NULL, or a mask of mask_dtype (see sage_mask_dtype), shape [B][mask_h][Nq][Nk],
  *         addressed as mask + b*mask_stride_b + h*mask_stride_h + i*mask_stride_q + j (element
  *         offsets; mask_h in {1, H}; mask_stride_h is ignored when mask_h == 1; mask_stride_b may
- *         be 0 to broadcast over the batch; an fp32 mask must be 4-byte aligned).  (Boolean mask
+ *         be 0 to broadcast over the batch and mask_stride_q 0 to broadcast one row of keys over
+ *         the queries, a key-padding mask [B,1|H,1,Nk]; otherwise mask_stride_q >= Nk; an fp32
+ *         mask must be 4-byte aligned).  (Boolean mask
  *         semantics: Triton INT8/FP16 kernel examples section, where False entries are masked out.)
  *   causal: key j is visible to query i only if j <= i (top-left aligned).
- *   sm_scale: <= 0 (or not finite) selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale).
+ *   sm_scale: <= 0 selects 1/sqrt(d) (FlashInfer API doc, parameter sm_scale); NaN or +-inf is
+ *        INVALID_ARGUMENT.
  *   smooth_v: nonzero subtracts V's per-channel token mean before the FP16 rounding of V and adds
  *        it back to O (see sage_prepare_v); SAGE_PV_FP16 only, else UNSUPPORTED.
  *   out: [B,H,Nq,d] of out_dtype (SAGE_BF16 or SAGE_FP16, rounded to nearest even, or SAGE_F32)
@@ -188,12 +207,14 @@ size_t sage_fwd_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nq, int64_t Nk, 
  *        sageattn section and on "Utilize SageAttention for Distributed Inference").
  * The online softmax runs over sage_block_n() keys per tile in increasing key order; a row's
  * reference maximum moves when a tile's maximum exceeds it by more than sage_softmax_tau() (log2
- * units); P is rounded to fp16 (or e4m3 of 448*2^-tau*p) against the reference maximum; the denominator
- * sums P as rounded or unrounded per sage_rowsum_rounded(); O and l accumulate in fp32.  Keys j >= Nk are masked
+ * units); P is rounded to fp16 (or to e4m3 of 448*p) against the reference maximum; the denominator
+ * sums the unrounded fp32 p (sage_rowsum_rounded() = 0); O and l accumulate in fp32.  Keys j >= Nk are masked
  * before the softmax (FlashInfer API doc, parameter unpadded_k_len).  A row with no visible key
  * gets O = 0 and LSE = -inf.
  * Errors: INVALID_ARGUMENT (null pointers, shape/stride mismatch with qk, misalignment, unknown
- * dtype or mask_dtype, mask_h not in {1,H}), UNSUPPORTED (d, pv, non-gfx950 device), WORKSPACE (too
+ * dtype or mask_dtype, mask_h not in {1,H}, sm_scale not finite), UNSUPPORTED (d, pv, non-gfx950
+ * device, or one head's prepared V past a 32-bit buffer range: Nk_pad * d * (2 for FP16 PV, 1 for
+ * e4m3) >= 2^31, i.e. more than 8,388,480 keys per head at d = 128 with FP16 PV), WORKSPACE (too
  * small), HIP. */
 sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const void* mask,
                           sage_mask_dtype mask_dtype, int64_t mask_h,

@@ -72,7 +72,8 @@ EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_r
            "sage_attn_fwd_varlen", "sage_prepare_v_varlen", "sage_attn_fwd_prepared_varlen", "sage_merge_lse",
            "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_softmax_tau",
            "sage_fp4_workspace_bytes",
-           "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores")
+           "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores", "sage_qk_quant_bytes",
+           "sage_qk_quant_init")
 
 
 def lib_path() -> str:
@@ -131,6 +132,10 @@ def load_library():
     L.sage_merge_lse.restype = I
     L.sage_debug_qk_int32.argtypes = [ctypes.POINTER(QKQuant), I64, I64, I64, I64, I64, I64, P, P]
     L.sage_debug_qk_int32.restype = I
+    L.sage_qk_quant_bytes.argtypes = [I64, I64, I64, I64, I64, I64, I]
+    L.sage_qk_quant_bytes.restype = SZ
+    L.sage_qk_quant_init.argtypes = [P, SZ, I64, I64, I64, I64, I64, I64, I, ctypes.POINTER(QKQuant)]
+    L.sage_qk_quant_init.restype = I
     L.sage_status_string.argtypes = [I]
     L.sage_status_string.restype = ctypes.c_char_p
     L.sage_fp4_q_blocks.argtypes = [I64, I]
@@ -276,6 +281,17 @@ def fwd_workspace(B, Hkv, Nq, Nk, d, pv_dtype, mask_h, device) -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def sm_scale_arg(sm_scale) -> float:
+    """The C ABI's sm_scale: 0 selects 1/sqrt(d) when none is given; an explicit value must be a
+    positive finite number."""
+    if sm_scale is None:
+        return 0.0
+    s = float(sm_scale)
+    if not math.isfinite(s) or s <= 0.0:
+        raise ValueError(f"sm_scale must be a positive finite number, got {sm_scale!r}")
+    return s
+
+
 def _mask_args(attn_mask, B, H, Nq, Nk):
     """(mask, mask dtype code, mask_h, stride_b, stride_h, stride_q) for the C call."""
     if attn_mask is None:
@@ -289,14 +305,15 @@ def _mask_args(attn_mask, B, H, Nq, Nk):
     m = attn_mask
     while m.dim() < 4:
         m = m.unsqueeze(0)
-    if m.shape[-2:] != (Nq, Nk) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
+    if m.shape[-1] != Nk or m.shape[-2] not in (1, Nq) or m.shape[0] not in (1, B) or m.shape[1] not in (1, H):
         raise ValueError(f"attn_mask of shape {tuple(attn_mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
     if m.stride(3) != 1:
         m = m.contiguous()
     mh = m.shape[1]
     sb = m.stride(0) if m.shape[0] == B else 0
     sh = m.stride(1) if mh == H and H > 1 else 0
-    return m, code, (mh if mh == H else 1), sb, sh, m.stride(2)
+    sq = m.stride(2) if m.shape[2] == Nq and Nq > 1 else 0  # one row of keys broadcast over the queries
+    return m, code, (mh if mh == H else 1), sb, sh, sq
 
 
 def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is_causal: bool = False,
@@ -325,7 +342,7 @@ def attn_fwd(qk: QuantizedQK, v: torch.Tensor, *, tensor_layout: str = "HND", is
     odt = _dtype_code(out.dtype, "out", allow_f32=True)
     _check(L.sage_attn_fwd(ctypes.byref(qs), ctypes.byref(dv), None if m is None else m.data_ptr(), mcode, mh, msb,
                            msh, msq,
-                           1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale), PV_CODES[pv_dtype],
+                           1 if is_causal else 0, sm_scale_arg(sm_scale), PV_CODES[pv_dtype],
                            1 if smooth_v else 0, out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                            workspace.data_ptr(), workspace.numel(), _stream(v)), "sage_attn_fwd")
     return (out, lse) if return_lse else out
@@ -430,7 +447,7 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
     odt = _dtype_code(out.dtype, "out", allow_f32=True)
     _check(L.sage_attn_fwd_prepared(ctypes.byref(qs), v_t.data_ptr(), None if v_scale is None else v_scale.data_ptr(),
                                     None if v_mean is None else v_mean.data_ptr(), PV_CODES[pv_dtype], None if m is None else m.data_ptr(), mcode, mh, msb, msh, msq,
-                                    1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+                                    1 if is_causal else 0, sm_scale_arg(sm_scale),
                                     out.data_ptr(), odt, osb, osh, osn, None if lse is None else lse.data_ptr(),
                                     None if workspace is None else workspace.data_ptr(),
                                     0 if workspace is None else workspace.numel(), _stream(out)),
@@ -537,7 +554,7 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     ws = fwd_workspace(qk.B, qk.Hkv, max_seqlen_q, max_seqlen_k, qk.d, pv_dtype, 0, q.device)
     qs = qk.cstruct()
     _check(L.sage_attn_fwd_varlen(ctypes.byref(qs), ctypes.byref(dv), cq.data_ptr(), ck.data_ptr(), q.shape[0],
-                                  k.shape[0], 1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+                                  k.shape[0], 1 if is_causal else 0, sm_scale_arg(sm_scale),
                                   PV_CODES[pv_dtype], 1 if smooth_v else 0, out.data_ptr(), _dtype_code(out.dtype, "out"), out.stride(1),
                                   out.stride(0), None if lse is None else lse.data_ptr(), ws.data_ptr(), ws.numel(),
                                   _stream(q)), "sage_attn_fwd_varlen")
@@ -580,7 +597,7 @@ def attn_fwd_prepared_varlen(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.
                                            None if v_scale is None else v_scale.data_ptr(),
                                            None if v_mean is None else v_mean.data_ptr(), PV_CODES[pv_dtype],
                                            cq.data_ptr(), ck.data_ptr(), total_q, total_k, 1 if is_causal else 0,
-                                           0.0 if sm_scale is None else float(sm_scale), out.data_ptr(),
+                                           sm_scale_arg(sm_scale), out.data_ptr(),
                                            _dtype_code(out.dtype, "out", allow_f32=True), out.stride(1),
                                            out.stride(0), None if lse is None else lse.data_ptr(), _stream(out)),
            "sage_attn_fwd_prepared_varlen")

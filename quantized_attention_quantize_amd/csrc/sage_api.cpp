@@ -23,6 +23,7 @@ constexpr int64_t kTileRows = 256;      // attention workgroup rows == mask tile
 constexpr int64_t kTileKeys = 64;       // attention key tile
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxRange = (int64_t)1 << 31;  // bytes a kernel addresses through one buffer range
 
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -68,8 +69,9 @@ sage_status check_qk(const sage_qk_quant* qk) {
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(qk->q8) || !aligned16(qk->k8)) return SAGE_ERR_INVALID_ARGUMENT;
   if ((qk->k_block_mean == nullptr) != (qk->blk_corr == nullptr)) return SAGE_ERR_INVALID_ARGUMENT;
-  // per_block_mean: one head's score terms are addressed through a 32-bit buffer range
-  if (qk->blk_corr && cdiv(qk->Nk, 64) * qk->Nq * 4 >= ((int64_t)1 << 31)) return SAGE_ERR_UNSUPPORTED;
+  // One head's K8 rows, and per_block_mean's score terms, are addressed through 32-bit buffer ranges
+  if (qk->Nk_pad * qk->d >= kMaxRange) return SAGE_ERR_UNSUPPORTED;
+  if (qk->blk_corr && cdiv(qk->Nk, 64) * qk->Nq * 4 >= kMaxRange) return SAGE_ERR_UNSUPPORTED;
   return SAGE_OK;
 }
 
@@ -134,6 +136,71 @@ PrepVArgs prep_v_args(const sage_qkv_desc* v, void* vt, float* vscale, float* vm
 extern "C" {
 
 int64_t sage_pad_tokens(int64_t n) { return n <= 0 ? 0 : (n + 127) / 128 * 128; }
+
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the buffers of a sage_qk_quant inside one allocation (each 256-byte aligned).
+struct QuantLayout {
+  size_t q8, k8, qs, ks, kmean, corr, kbmean, blk, total;
+};
+
+bool quant_layout(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int per_block_mean,
+                  QuantLayout* L) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || H % Hkv != 0 || (d != 64 && d != 128)) return false;
+  if (Nq > kMaxTokens || Nk > kMaxTokens || B * H > 65535) return false;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L->q8 = take((size_t)(B * H * sage_pad_tokens(Nq) * d));
+  L->k8 = take((size_t)(B * Hkv * sage_pad_tokens(Nk) * d));
+  L->qs = take((size_t)(B * H * cdiv(Nq, 64)) * 4);
+  L->ks = take((size_t)(B * Hkv * cdiv(Nk, 64)) * 4);
+  L->kmean = take((size_t)(B * Hkv * d) * 4);
+  L->corr = take((size_t)(B * H * Nq) * 4);
+  L->kbmean = per_block_mean ? take((size_t)(B * Hkv * cdiv(Nk, 64) * d) * 4) : 0;
+  L->blk = per_block_mean ? take((size_t)(B * H * cdiv(Nk, 64) * Nq) * 4) : 0;
+  L->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sage_qk_quant_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, int per_block_mean) {
+  QuantLayout L;
+  return quant_layout(B, H, Hkv, Nq, Nk, d, per_block_mean, &L) ? L.total : 0;
+}
+
+sage_status sage_qk_quant_init(void* base, size_t bytes, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk,
+                               int64_t d, int per_block_mean, sage_qk_quant* out) {
+  QuantLayout L;
+  if (!base || !out || ((uintptr_t)base & 255u) != 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!quant_layout(B, H, Hkv, Nq, Nk, d, per_block_mean, &L) || bytes < L.total) return SAGE_ERR_INVALID_ARGUMENT;
+  char* p = static_cast<char*>(base);
+  out->q8 = reinterpret_cast<int8_t*>(p + L.q8);
+  out->k8 = reinterpret_cast<int8_t*>(p + L.k8);
+  out->q_scale = reinterpret_cast<float*>(p + L.qs);
+  out->k_scale = reinterpret_cast<float*>(p + L.ks);
+  out->k_mean = reinterpret_cast<float*>(p + L.kmean);
+  out->lse_corr = reinterpret_cast<float*>(p + L.corr);
+  out->k_block_mean = per_block_mean ? reinterpret_cast<float*>(p + L.kbmean) : nullptr;
+  out->blk_corr = per_block_mean ? reinterpret_cast<float*>(p + L.blk) : nullptr;
+  out->B = B;
+  out->H = H;
+  out->Hkv = Hkv;
+  out->Nq = Nq;
+  out->Nk = Nk;
+  out->d = d;
+  out->Nq_pad = sage_pad_tokens(Nq);
+  out->Nk_pad = sage_pad_tokens(Nk);
+  return SAGE_OK;
+}
 
 int sage_block_n(sage_pv_dtype pv) {
   (void)pv;
@@ -299,7 +366,7 @@ struct FwdCommon {
   int64_t mh;
 };
 
-sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const void* mask,
+sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, float sm_scale, const void* mask,
                                 sage_mask_dtype mask_dtype, int64_t mask_h,
                                 int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q, void* out,
                                 sage_dtype out_dtype, int64_t out_stride_b, int64_t out_stride_h,
@@ -307,6 +374,9 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
   sage_status s;
   if ((s = check_qk(qk)) != SAGE_OK) return s;
   if (pv != SAGE_PV_FP16 && pv != SAGE_PV_FP8_E4M3) return SAGE_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return SAGE_ERR_INVALID_ARGUMENT;  // <= 0 selects 1/sqrt(d)
+  // one head's prepared V is addressed through a 32-bit buffer range
+  if (qk->Nk_pad * qk->d * (pv == SAGE_PV_FP16 ? 2 : 1) >= kMaxRange) return SAGE_ERR_UNSUPPORTED;
   if (!out) return SAGE_ERR_INVALID_ARGUMENT;
   if (out_dtype != SAGE_BF16 && out_dtype != SAGE_FP16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID_ARGUMENT;
   if (out_stride_b < 0 || out_stride_h < 0 || out_stride_n < qk->d) return SAGE_ERR_INVALID_ARGUMENT;
@@ -319,7 +389,9 @@ sage_status validate_fwd_common(const sage_qk_quant* qk, sage_pv_dtype pv, const
     if (mask_dtype == SAGE_MASK_F32 && qk->blk_corr) return SAGE_ERR_UNSUPPORTED;  // not combined
     if (mask_dtype == SAGE_MASK_F32 && (uintptr_t)mask % 4 != 0) return SAGE_ERR_INVALID_ARGUMENT;
     if (mask_h != 1 && mask_h != qk->H) return SAGE_ERR_INVALID_ARGUMENT;
-    if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_q < qk->Nk) return SAGE_ERR_INVALID_ARGUMENT;
+    // mask_stride_q = 0 broadcasts one row of keys over all queries (a key-padding mask)
+    if (mask_stride_b < 0 || mask_stride_h < 0 || (mask_stride_q != 0 && mask_stride_q < qk->Nk))
+      return SAGE_ERR_INVALID_ARGUMENT;
     c->mh = mask_h;
   }
   return SAGE_OK;
@@ -407,7 +479,7 @@ sage_status enqueue_attention(const sage_qk_quant* qk, const void* v_t, const fl
   a.nbq = (int)cdiv(qk->Nq, 64);
   a.nbk = (int)cdiv(qk->Nk, 64);
   a.causal = causal ? 1 : 0;
-  a.sm_scale = (sm_scale > 0.f && isfinite(sm_scale)) ? sm_scale : (float)(1.0 / sqrt((double)qk->d));
+  a.sm_scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)qk->d));
   return hip_status(launch_attn(a, (int)qk->d, pv == SAGE_PV_FP8_E4M3, st));
 }
 
@@ -432,7 +504,7 @@ sage_status sage_attn_fwd(const sage_qk_quant* qk, const sage_qkv_desc* v, const
   sage_status s;
   FwdCommon c;
   if (smooth_v && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
-  if ((s = validate_fwd_common(qk, pv, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
+  if ((s = validate_fwd_common(qk, pv, sm_scale, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
                                out_dtype, out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
   if ((s = check_desc(v)) != SAGE_OK) return s;
@@ -460,7 +532,7 @@ sage_status sage_attn_fwd_prepared(const sage_qk_quant* qk, const void* v_t, con
                                    void* stream) {
   sage_status s;
   FwdCommon c;
-  if ((s = validate_fwd_common(qk, pv, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
+  if ((s = validate_fwd_common(qk, pv, sm_scale, mask, mask_dtype, mask_h, mask_stride_b, mask_stride_h, mask_stride_q, out,
                                out_dtype, out_stride_b, out_stride_h, out_stride_n, &c)) != SAGE_OK)
     return s;
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -483,7 +555,7 @@ sage_status sage_attn_fwd_varlen(const sage_qk_quant* qk, const sage_qkv_desc* v
   FwdCommon c;
   if (smooth_v && pv != SAGE_PV_FP16) return SAGE_ERR_UNSUPPORTED;
   if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
-  if ((s = validate_fwd_common(qk, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
+  if ((s = validate_fwd_common(qk, pv, sm_scale, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
                                out_stride_n, &c)) != SAGE_OK)
     return s;
   if ((s = check_desc(v)) != SAGE_OK) return s;
@@ -522,7 +594,7 @@ sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v
   sage_status s;
   FwdCommon c;
   if ((s = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k)) != SAGE_OK) return s;
-  if ((s = validate_fwd_common(qk, pv, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
+  if ((s = validate_fwd_common(qk, pv, sm_scale, nullptr, SAGE_MASK_BOOL, 0, 0, 0, 0, out, out_dtype, 0, out_stride_h,
                                out_stride_n, &c)) != SAGE_OK)
     return s;
   if (!v_t || !aligned16(v_t)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -735,6 +807,7 @@ sage_status sage_fp4_attn_fwd(const sage_fp4_qkv* qkv, int causal, float sm_scal
   const int64_t oel = out_dtype == SAGE_F32 ? 4 : 8;  // elements per 16 bytes
   if (!aligned16(out) || (out_stride_b % oel) || (out_stride_h % oel) || (out_stride_n % oel))
     return SAGE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(sm_scale)) return SAGE_ERR_INVALID_ARGUMENT;  // <= 0 selects 1/sqrt(d)
   if ((s = check_device()) != SAGE_OK) return s;
   Fp4AttnArgs a = fp4_attn_args(qkv);
   a.out = out;
@@ -744,7 +817,7 @@ sage_status sage_fp4_attn_fwd(const sage_fp4_qkv* qkv, int causal, float sm_scal
   a.o_sn = out_stride_n;
   a.lse = lse;
   a.causal = causal ? 1 : 0;
-  if (sm_scale > 0.f && isfinite(sm_scale)) a.sm_scale = sm_scale;
+  if (sm_scale > 0.f) a.sm_scale = sm_scale;
   return hip_status(launch_fp4_attn(a, static_cast<hipStream_t>(stream)));
 }
 

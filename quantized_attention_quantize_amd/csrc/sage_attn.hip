@@ -143,24 +143,6 @@ __device__ __forceinline__ void load_q_frags(const int8_t* q8h, int64_t row, int
   }
 }
 
-// S^T for 64 keys x the wave's 32 queries.  acc[kb][r] = score of query lr and key
-// kb*32 + (r/4)*8 + g*4 + r%4 of the tile.
-template <int D>
-__device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32], int lr, int g, v16i (&acc)[2]) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[kb][r] = 0;
-#pragma unroll
-  for (int cs = 0; cs < D / 32; ++cs) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      v4i a = *reinterpret_cast<const v4i*>(sK + lds_chunk_offset<D>(kb * 32 + lr, 2 * cs + g));
-      acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[cs], acc[kb], 0, 0, 0);
-    }
-  }
-}
-
 __device__ __forceinline__ int key_of(int kb, int r, int g) { return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3); }
 
 
@@ -217,6 +199,41 @@ __device__ __forceinline__ v4i frag64k(const char* base, const LaneBases& lb, in
 }
 __device__ __forceinline__ v4i frag64v(const char* base, const LaneBases& lb, int k, int c) {
   return *reinterpret_cast<const v4i*>(base + lb.v64[c] + 2048 * k);
+}
+
+// A operand of QK MFMA q of a tile (key block q / (D/32), chunk step q % (D/32)): K rows
+// 32*kb + lr, chunk 2*cs + g of the K tile at sK.  Every K tile of the attention kernel, and the
+// debug scores, are read through this.
+template <int D>
+__device__ __forceinline__ v4i kfrag(const char* sK, const LaneBases& lb, int q) {
+  constexpr int NB = D / 32;
+  const int kb = q / NB, cs = q % NB;
+  if constexpr (D == 128)
+    return frag128(sK, lb, kb, cs);
+  else
+    return frag64k(sK, lb, kb, cs);
+}
+
+// QK MFMA q of S^T = K8 . Q8^T: starts key block q / (D/32)'s int32 accumulator at its first chunk
+// step, accumulates the later ones.  acc[kb][r] = score of query lr and key kb*32 + (r/4)*8 + g*4 + r%4.
+template <int D>
+__device__ __forceinline__ void qk_mfma(v4i kf, const v4i (&qf)[D / 32], int q, v16i (&acc)[2]) {
+  constexpr int NB = D / 32;
+  const int kb = q / NB, cs = q % NB;
+  if (cs == 0) {
+    const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[cs], z, 0, 0, 0);
+  } else {
+    acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[cs], acc[kb], 0, 0, 0);
+  }
+}
+
+// S^T for 64 keys x the wave's 32 queries, by the same operand reads and MFMA sequence as the
+// QK half of every tile step.
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32], const LaneBases& lb, v16i (&acc)[2]) {
+#pragma unroll
+  for (int q = 0; q < 2 * (D / 32); ++q) qk_mfma<D>(kfrag<D>(sK, lb, q), qf, q, acc);
 }
 
 // Softmax state of a wave's rows.  Lane (lr, g) holds row lr; both halves of the wave carry the
@@ -346,7 +363,7 @@ struct StepGeom {
   static constexpr int NQ = 2 * NB;                   // QK MFMAs: key block q / NB, chunk step q % NB
   static constexpr int NPV = PV == 0 ? 4 * NB : NB;  // PV MFMAs
   static constexpr int NM = NPV + NQ;                 // MFMA k < NPV is PV MFMA k, else QK MFMA k - NPV
-  static constexpr int LA = PV == 0 ? 2 : 1;          // operands read from LDS ahead of the MFMA stream
+  static constexpr int LA = PV == 0 ? 3 : 1;          // operands read from LDS ahead of the MFMA stream
   using VFrag = typename std::conditional<PV == 0, v4i, v8i>::type;
 };
 
@@ -391,25 +408,18 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   static_assert(!(MF && BM), "per_block_mean is not combined with a float mask");
   using SG = StepGeom<D, PV>;
   constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = SG::NM, LA = SG::LA;
-  constexpr int NG = PV == 0 ? 16 : 8;  // exponential groups of 2 (fp16) or 4 (e4m3) scores
+  constexpr int NG = 8;                 // exponential groups of 4 scores
   constexpr int FIN = 1;                // slot of the reference-maximum update (pieces 4-7 in slot 0)
   using VFrag = typename SG::VFrag;
 
-  // A operand of QK MFMA q: K rows 32*kb + lr, chunk 2*cs + g
-  auto kfrag = [&](int q) -> v4i {
-    const int kb = q / NB, cs = q % NB;
-    if constexpr (D == 128)
-      return frag128(sKn, lb, kb, cs);
-    else
-      return frag64k(sKn, lb, kb, cs);
-  };
   // Slot of exponential group gi, after the reference maximum.  FP16: after the PV MFMAs that
   // read the P registers it overwrites, spread so that each key block's scores are consumed
   // before the QK of T[n+1] overwrites them.  e4m3: every PV MFMA reads all of P, so P is written
   // into fresh registers, spread over the slots before the second key block's QK.
   auto exp_slot = [](int gi) {
     if (PV == 1) return FIN + 1 + gi * (NPV + NB - FIN - 1) / NG;
-    const int first = ((gi >> 2) + 1) * NB > FIN + 1 ? ((gi >> 2) + 1) * NB : FIN + 1;
+    // group gi writes P fragment gi / 2, which PV MFMAs (gi / 2) * NB .. (gi / 2) * NB + NB - 1 read
+    const int first = ((gi >> 1) + 1) * NB > FIN + 1 ? ((gi >> 1) + 1) * NB : FIN + 1;
     const int s = NB + gi * NPV / NG;
     return s > first ? s : first;
   };
@@ -433,11 +443,10 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
     if (r < NPV)
       vf[r] = vfrag<D, PV>(sVp, lb, g, r);
     else
-      kf[r - NPV] = kfrag(r - NPV);
+      kf[r - NPV] = kfrag<D>(sKn, lb, r - NPV);
   };
   float psum = 0.f, alpha = 1.f;
   float nb = 0.f;  // per_block_mean: T[n]'s row term minus the exponent offset
-  const v2h ones = {(_Float16)1.f, (_Float16)1.f};
 
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
@@ -449,13 +458,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
       else
         o[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[k], pin.b, o[k], 0, 0, 0, 127, 0, 127);
     } else {
-      const int q = k - NPV, kb = q / NB, cs = q % NB;
-      if (cs == 0) {
-        const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[q], qf[cs], z, 0, 0, 0);
-      } else {
-        acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[q], qf[cs], acc[kb], 0, 0, 0);
-      }
+      qk_mfma<D>(kf[k - NPV], qf, k - NPV, acc);
     }
     // T[n]'s row maxima over its second key block, then its reference maximum
     if (!MF && k == 0) {
@@ -490,15 +493,18 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
         }
         x[e] = t;
       }
+      // the row sum takes the fp32 probabilities (before P's rounding)
+      psum += (x[0] + x[1]) + (x[2] + x[3]);
       if constexpr (PV == 0) {
-        const int idx = gi * 2, kb = idx >> 4, r = idx & 15;
-        const int s2 = kb * 2 + (r >> 3), jj = (r & 7) >> 1;
-        const v2h hh = __builtin_convertvector((v2f{x[0], x[1]}), v2h);  // round to nearest even
-        P.s[s2][2 * jj] = hh[0];
-        P.s[s2][2 * jj + 1] = hh[1];
-        psum = __builtin_amdgcn_fdot2(hh, ones, psum, false);  // the row sum takes the rounded P
+        const int idx = gi * 4, kb = idx >> 4, r = idx & 15;
+        const int s2 = kb * 2 + (r >> 3), jj = (r & 7) >> 1;  // jj = 0 or 2
+        const v2h h0 = __builtin_convertvector((v2f{x[0], x[1]}), v2h);  // round to nearest even
+        const v2h h1 = __builtin_convertvector((v2f{x[2], x[3]}), v2h);
+        P.s[s2][2 * jj] = h0[0];
+        P.s[s2][2 * jj + 1] = h0[1];
+        P.s[s2][2 * jj + 2] = h1[0];
+        P.s[s2][2 * jj + 3] = h1[1];
       } else {
-        psum += (x[0] + x[1]) + (x[2] + x[3]);
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
         P.b[gi] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
       }
@@ -560,6 +566,15 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
 // barrier per tile.  MF: the mask is fp32 and additive, and every tile takes the masked step.
 // BM: per_block_mean -- every score of key tile t gets the row's term blk_corr[t][row] (loaded a
 // step ahead, before the step's staging loads, so the vmcnt waits below cover it).
+// The kernel's argument block, read through an opaque copy of its address: loads through it are
+// issued where they appear instead of being hoisted into SGPRs held across the loop.
+template <typename T>
+__device__ __forceinline__ const T* kernarg_reload() {
+  const T* p = (const T*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
 template <int D, int PV, int MF, int BM>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   using G = TileGeom<D, PV>;
@@ -642,6 +657,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   }
   v4i qf[D / 32];
   load_q_frags<D>(q8h, row, a.Nq_pad, g, qf);
+  LaneBases lb;
+  lb.init(lr, g);
   __builtin_amdgcn_s_waitcnt(0);  // Q fragments and the prologue tiles resident
   __syncthreads();
 
@@ -678,8 +695,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     return mrow ? mrow + (int64_t)(t < kt_end ? t : 0) * kBlockN * kMaskBytes : nullptr;
   };
 
-  LaneBases lb;
-  lb.init(lr, g);
   RowState rs;
   rs.m = -INFINITY;
   rs.pm = 0.f;
@@ -697,7 +712,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
   float cb_cur = cb_of(t0);
   {  // scores of T[0] and the row maxima of its first key block; the first PV operands
-    qk_tile<D>(kring, qf, lr, g, acc);
+    qk_tile<D>(kring, qf, lb, acc);
     int lim;
     const void* mtile;
     visible(t0, lim, mtile);
@@ -781,13 +796,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   __syncthreads();
   if (n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
 
-  // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE
+  // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE.  The arguments it needs are
+  // read again from the kernel-argument segment here, so they hold no SGPRs across the loop.
+  const AttnArgs& ea = *kernarg_reload<AttnArgs>();
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
   if (row < nq) {
-    const float* vsh = PV == 1 ? a.vscale + bhk * D : nullptr;
+    const float* vsh = PV == 1 ? ea.vscale + bhk * D : nullptr;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float* vmh = (a.vmean && l_tot > 0.f) ? a.vmean + bhk * D : nullptr;  // smooth_v
-    const int64_t obase = b * a.o_sb + h * a.o_sh + (sq.off + row) * a.o_sn;  // elements
+    const float* vmh = (ea.vmean && l_tot > 0.f) ? ea.vmean + bhk * D : nullptr;  // smooth_v
+    const int64_t obase = b * ea.o_sb + h * ea.o_sh + (sq.off + row) * ea.o_sn;  // elements
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -802,32 +819,33 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
             f[e] = o[db][rq * 4 + e] * inv;
           if (vmh) f[e] = f[e] + vmh[d0 + e];
         }
-        if (a.out_kind == 2) {  // fp32, e.g. partial results that are merged later
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
+        if (ea.out_kind == 2) {  // fp32, e.g. partial results that are merged later
+          *reinterpret_cast<float4*>(static_cast<float*>(ea.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
         } else {
           uint2 pk;
-          if (a.out_kind == 1) {
+          if (ea.out_kind == 1) {
             pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
             pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
           } else {
             pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
             pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
           }
-          *reinterpret_cast<uint2*>(static_cast<unsigned short*>(a.out) + obase + d0) = pk;
+          *reinterpret_cast<uint2*>(static_cast<unsigned short*>(ea.out) + obase + d0) = pk;
         }
       }
-    if (g == 0 && a.lse) {
+    if (g == 0 && ea.lse) {
       float v = -INFINITY;
       if (l_tot > 0.f) {
         // l_tot sums 2^(s - pm) over the row (e4m3 P carries its scale 448 * 2^-tau inside pm)
-        v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.corr[bh * a.Nq + row];
+        v = (rs.pm + log2f(l_tot)) * kLn2 + ea.sm_scale * ea.corr[bh * ea.Nq + row];
       }
-      a.lse[b * a.l_sb + h * a.l_sh + sq.off + row] = v;
+      ea.lse[b * ea.l_sb + h * ea.l_sh + sq.off + row] = v;
     }
   }
 }
 
-// Raw int32 scores of a window of one head, via the same staging and tile code as k_attn_fwd.
+// Raw int32 scores of a window of one head, via the same staging (Stager, swizzled LDS rows),
+// operand reads (LaneBases, kfrag) and MFMA sequence (qk_mfma) as every tile step of k_attn_fwd.
 // grid = (32-row blocks, 64-key tiles) covering the window; block = one wave.
 template <int D>
 __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) {
@@ -843,8 +861,10 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
   v4i qf[D / 32];
   const int64_t row = rb * 32 + lr;
   load_q_frags<D>(a.q8h, row, Nq_pad, g, qf);
+  LaneBases lb;
+  lb.init(lr, g);
   v16i acc[2];
-  qk_tile<D>(sK, qf, lr, g, acc);
+  qk_tile<D>(sK, qf, lb, acc);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll

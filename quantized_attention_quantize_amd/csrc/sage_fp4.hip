@@ -32,9 +32,8 @@
 //      on the k-elements that the e2m1 V operand of lane group g pairs with keys [32g, 32g+32), and
 //      V^T needs no key permutation -- its MX blocks are 32 consecutive tokens;
 //    - O^T += V^T P^T on the same MFMA with A = e2m1 V (scale per channel and 32-token block) and
-//      B = e4m3 P with unit scale; P = 448 * 2^-tau * p under a reference maximum that moves only
-//      when a tile exceeds it by more than tau = kF4Tau log2 units (p <= 2^tau, P <= 448), so the
-//      whole-wave rescaling of O is rare.
+//      B = e4m3 P with unit scale; P = e4m3(448 * p) against the exact running maximum (p <= 1,
+//      the row maximum maps to 448).
 //    The tile's correction values and K / V scale bytes travel through the LDS ring with the K and
 //    V codes.  Head dimension 128.
 #include "sage_device.h"
@@ -46,10 +45,10 @@ constexpr int kMX = 32;     // elements per MX block
 constexpr int kQMB = 128;   // tokens per Q smoothing block
 constexpr int kF4Threads = 256;
 constexpr float kF4Log2_448 = 8.807354922057604f;  // log2(448)
-// Lazy reference maximum of the online softmax (log2 units): it moves only when a tile's maximum
-// exceeds it by more than kF4Tau, so p = 2^(t - m) <= 2^kF4Tau and P = e4m3(448 * 2^-kF4Tau * p)
-// stays within e4m3's range while O is rarely rescaled.
-constexpr int kF4Tau = 3;
+// Reference maximum of the online softmax (log2 units): it moves when a tile's maximum exceeds it
+// by more than kF4Tau.  With kF4Tau = 0 it is the exact running maximum, so p = 2^(t - m) <= 1 and
+// P = e4m3(448 * p).
+constexpr int kF4Tau = 0;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v8f __attribute__((ext_vector_type(8)));

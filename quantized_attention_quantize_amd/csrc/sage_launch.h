@@ -6,14 +6,14 @@
 
 namespace sage {
 
-// Lazy online-softmax maximum (log2 units) by PV type: the reference maximum moves only when a
-// tile's maximum exceeds it by more than this, so O is rarely rescaled while p = exp(s - m) stays
-// <= 2^tau: FP16 P <= 2^8 (no overflow); e4m3 P is 448 * 2^-tau * p <= 448 (a whole tau keeps
-// that scale exact).
-constexpr float kSoftmaxTau[2] = {8.f, 3.f};
-// Whether the softmax denominator sums P as rounded for the PV product (FP16: one v_dot2 per two
-// probabilities) rather than the fp32 p (e4m3), by PV type.
-constexpr int kRowsumRounded[2] = {1, 0};
+// Online-softmax reference maximum (log2 units) by PV type: it moves only when a tile's maximum
+// exceeds it by more than this, so O is rarely rescaled.  FP16 P is lazy by 8 (p = exp(s - m)
+// stays <= 2^8, well inside fp16); e4m3 P is e4m3(448 * p) against the exact running maximum
+// (p <= 1), so the row maximum maps to 448.
+constexpr float kSoftmaxTau[2] = {8.f, 0.f};
+// Whether the softmax denominator sums P as rounded for the PV product rather than the fp32 p,
+// by PV type: both sum the fp32 p.
+constexpr int kRowsumRounded[2] = {0, 0};
 
 struct QuantArgs {
   const unsigned short* q;  // bf16 or fp16 (in_fp16), as K

@@ -18,7 +18,7 @@ from dataclasses import dataclass
 
 import torch
 
-from .api import FP4QKV, _check, _desc, _dtype_code, _stream, load_library, pad_tokens
+from .api import FP4QKV, _check, _desc, _dtype_code, _stream, load_library, pad_tokens, sm_scale_arg
 
 
 @dataclass
@@ -105,7 +105,7 @@ def attn_fwd_fp4(qkv: QuantizedFP4, *, is_causal: bool = False, sm_scale: float 
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != qkv.B * qkv.H * qkv.Nq):
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     cs = qkv.cstruct()
-    _check(L.sage_fp4_attn_fwd(ctypes.byref(cs), 1 if is_causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+    _check(L.sage_fp4_attn_fwd(ctypes.byref(cs), 1 if is_causal else 0, sm_scale_arg(sm_scale),
                                out.data_ptr(), _dtype_code(out.dtype, "out", allow_f32=True), out.stride(0),
                                out.stride(1), out.stride(2), None if lse is None else lse.data_ptr(), _stream(out)),
            "sage_fp4_attn_fwd")

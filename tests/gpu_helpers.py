@@ -10,6 +10,46 @@ import torch
 
 DEV = "cuda"
 
+from schedule import BLOCK_N, PLAIN_TOL, QE_TOL, ROW_TOL, ROWSUM_ROUNDED, TAU, TAU_FP4  # noqa: F401
+
+
+def qe_schedule(pv: str) -> dict:
+    """Keyword arguments of the oracle's emulation for the kernels' schedule."""
+    return dict(BN=BLOCK_N, tau=TAU[pv], lsum_rounded=ROWSUM_ROUNDED)
+
+
+def row_rel_l1(a, b) -> np.ndarray:
+    """Per-row relative L1 of [R, d] arrays: sum_c |a - b| / sum_c |b| (0 for rows where both are
+    all zero, inf where only b is)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    num = np.abs(a - b).sum(-1)
+    den = np.abs(b).sum(-1)
+    out = np.zeros(num.shape)
+    nz = den > 0
+    out[nz] = num[nz] / den[nz]
+    out[~nz & (num > 0)] = np.inf
+    return out
+
+
+def check_o(got, want, pv: str, tag: str, plain=None) -> float:
+    """O parity: aggregate relative L1 <= QE_TOL and every row within ROW_TOL[pv] of the emulation
+    (want), and, when given, aggregate relative L1 <= PLAIN_TOL against the plain reading (plain).
+    Returns the aggregate relative L1 against want."""
+    e = rel_l1(got, want)
+    rows = row_rel_l1(got, want)
+    worst = float(rows.max()) if rows.size else 0.0
+    msg = f"{tag}: rel-L1 vs emulation {e:.3e}, worst row {worst:.3e}"
+    if plain is not None:
+        ep = rel_l1(got, plain)
+        msg += f", rel-L1 vs plain reading {ep:.3e}"
+    say("  " + msg)
+    assert e <= QE_TOL, msg
+    assert worst <= ROW_TOL[pv], msg
+    if plain is not None:
+        assert ep <= PLAIN_TOL, msg
+    return e
+
 
 def say(*a):
     """Flushed progress line, so a failing GPU step names its case."""

@@ -10,6 +10,8 @@ import pytest
 
 from quantized_attention_quantize_amd import api
 
+from schedule import BLOCK_N, ROWSUM_ROUNDED, TAU, TAU_FP4
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
@@ -42,9 +44,11 @@ def test_host_queries(L):
     assert L.sage_pad_tokens(1) == 128 and L.sage_pad_tokens(128) == 128 and L.sage_pad_tokens(17776) == 17792
     assert L.sage_pad_tokens(0) == 0
     assert L.sage_block_n(0) == 64 and L.sage_block_n(1) == 64
+    # the library reports the online schedule the parity tests fix as constants (gpu_helpers)
     L.sage_softmax_tau.restype = ctypes.c_double
-    assert L.sage_softmax_tau(0) == 8.0 and L.sage_softmax_tau(1) == 3.0  # FP16 P <= 2^8; e4m3 448 / 8 * p
-    assert L.sage_rowsum_rounded(0) == 1 and L.sage_rowsum_rounded(1) == 0
+    assert L.sage_block_n(0) == BLOCK_N and L.sage_block_n(1) == BLOCK_N
+    assert L.sage_softmax_tau(0) == TAU["fp16"] and L.sage_softmax_tau(1) == TAU["fp8"]
+    assert L.sage_rowsum_rounded(0) == int(ROWSUM_ROUNDED) and L.sage_rowsum_rounded(1) == int(ROWSUM_ROUNDED)
     assert L.sage_quantize_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_quantize_workspace_bytes(0, 1, 1, 64) == 0
     # prepared fp16 V of the 8192-token, 64-head workload
@@ -136,9 +140,9 @@ def test_quantize_validation(L, case, status):
 
 
 def call_fwd(L, qk, v, mask=None, mdt=0, mask_h=0, msq=256, pv=0, out=FAKE, odt=0, osn=64, ws=FAKE, wsb=1 << 30,
-             smooth_v=0):
+             smooth_v=0, sm=0.0):
     return L.sage_attn_fwd(ctypes.byref(qk) if qk else None, ctypes.byref(v) if v else None, mask, mdt, mask_h, 0, 0,
-                           msq, 0, 0.0, pv, smooth_v, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
+                           msq, 0, sm, pv, smooth_v, out, odt, 2 * 256 * 64, 256 * 64, osn, None, ws, wsb, None)
 
 
 @pytest.mark.parametrize("case,status", [
@@ -146,7 +150,10 @@ def call_fwd(L, qk, v, mask=None, mdt=0, mask_h=0, msq=256, pv=0, out=FAKE, odt=
     ("out_bad_dtype", INVALID), ("out_misaligned", INVALID), ("mask_dtype_bad", INVALID),
     ("mask_f32_misaligned", INVALID), ("smooth_v_fp8", UNSUPPORTED), ("mask_h_bad", INVALID), ("mask_stride_small", INVALID),
     ("ws_small", WORKSPACE), ("ws_null", WORKSPACE), ("qk_d", UNSUPPORTED), ("gqa_v_heads", INVALID),
-    ("gqa_hkv_zero", INVALID),
+    ("gqa_hkv_zero", INVALID), ("sm_nan", INVALID), ("sm_inf", INVALID),
+    # a key-padding mask (one row of keys for every query, mask_stride_q = 0) passes validation:
+    # the call then stops at the workspace check, before anything is enqueued
+    ("mask_stride_q_zero", WORKSPACE),
 ])
 def test_attn_validation(L, case, status):
     qk, v = quant(), desc()
@@ -183,7 +190,67 @@ def test_attn_validation(L, case, status):
         qk = quant(H=2, Hkv=1)
     elif case == "gqa_hkv_zero":
         qk = quant(Hkv=0)
+    elif case == "sm_nan":
+        kw["sm"] = float("nan")
+    elif case == "sm_inf":
+        kw["sm"] = float("inf")
+    elif case == "mask_stride_q_zero":
+        kw.update(mask=FAKE, mask_h=1, msq=0, wsb=100)
     assert call_fwd(L, qk, v, **kw) == status
+
+
+@pytest.mark.parametrize("pv,Nk,status", [
+    # one head's prepared V is addressed through a 32-bit buffer range: Nk_pad * d * esz < 2^31
+    (0, (1 << 23) - 128, WORKSPACE), (0, 1 << 23, UNSUPPORTED),  # FP16 V, 2 bytes per element
+    (1, 1 << 23, WORKSPACE), (1, (1 << 24) - 128, WORKSPACE),    # e4m3 V, 1 byte per element
+])
+def test_attn_buffer_range_limit(L, pv, Nk, status):
+    """Past the 32-bit buffer ranges of the attention kernel's prepared-V addressing the call is
+    UNSUPPORTED (host validation, nothing enqueued); just below it the call passes validation and
+    stops at the (deliberately small) workspace."""
+    qk, v = quant(Nk=Nk, d=128), desc(N=Nk, d=128)
+    assert call_fwd(L, qk, v, pv=pv, osn=128, wsb=100) == status
+
+
+@pytest.mark.parametrize("Nk,status", [((1 << 24) - 128, WORKSPACE), (1 << 24, UNSUPPORTED)])
+def test_quantize_buffer_range_limit(L, Nk, status):
+    """One head's K8 rows (Nk_pad * d bytes) are addressed through a 32-bit buffer range."""
+    q, k, out = desc(d=128), desc(N=Nk, d=128), quant(Nk=Nk, d=128)
+    assert call_quant(L, q, k, out, wsb=16) == status
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,pbm", [(1, 2, 2, 256, 256, 64, 0), (2, 32, 8, 8192, 8192, 128, 0),
+                                                  (1, 3, 1, 300, 417, 128, 1), (2, 4, 4, 1, 17776, 64, 1)])
+def test_qk_quant_bytes_and_init(L, B, H, Hkv, Nq, Nk, d, pbm):
+    """sage_qk_quant_bytes sizes one allocation for every buffer of the quantized Q/K (each on a
+    256-byte boundary, in the documented order), and sage_qk_quant_init lays the struct out in it:
+    pointers at those offsets, the sizes and pads filled in.  The buffer sizes are the shapes the
+    Python binding allocates (alloc_quantized)."""
+    import torch
+    g = api.alloc_quantized(B, H, Nq, Nk, d, "cpu", Hkv=Hkv, per_block_mean=bool(pbm))
+    bufs = [g.q8, g.k8, g.q_scale, g.k_scale, g.k_mean, g.lse_corr]
+    if pbm:
+        bufs += [g.k_block_mean, g.blk_corr]
+    offs, off = [], 0
+    for t in bufs:
+        offs.append(off)
+        off += (t.numel() * t.element_size() + 255) // 256 * 256
+    assert L.sage_qk_quant_bytes(B, H, Hkv, Nq, Nk, d, pbm) == off
+    base = 0x40000000
+    st = api.QKQuant()
+    assert L.sage_qk_quant_init(base, off, B, H, Hkv, Nq, Nk, d, pbm, ctypes.byref(st)) == 0
+    ptrs = [st.q8, st.k8, st.q_scale, st.k_scale, st.k_mean, st.lse_corr] + \
+        ([st.k_block_mean, st.blk_corr] if pbm else [])
+    assert [p - base for p in ptrs] == offs
+    assert (st.B, st.H, st.Hkv, st.Nq, st.Nk, st.d) == (B, H, Hkv, Nq, Nk, d)
+    assert (st.Nq_pad, st.Nk_pad) == (L_pad(Nq), L_pad(Nk))
+    if not pbm:
+        assert not st.k_block_mean and not st.blk_corr
+    # too small, misaligned, or invalid sizes
+    assert L.sage_qk_quant_init(base, off - 1, B, H, Hkv, Nq, Nk, d, pbm, ctypes.byref(st)) == INVALID
+    assert L.sage_qk_quant_init(base + 16, off, B, H, Hkv, Nq, Nk, d, pbm, ctypes.byref(st)) == INVALID
+    assert L.sage_qk_quant_bytes(B, H, 5, Nq, Nk, d, pbm) == 0 and L.sage_qk_quant_bytes(B, H, Hkv, Nq, Nk, 96, pbm) == 0
+    del torch
 
 
 def test_per_block_mean_validation(L):
@@ -294,7 +361,7 @@ def L_pad(n):
 
 def test_fp4_host_queries(L):
     assert L.sage_fp4_q_blocks(300, 1) == 3 and L.sage_fp4_q_blocks(300, 0) == 1 and L.sage_fp4_q_blocks(0, 1) == 0
-    assert L.sage_fp4_softmax_tau() == 3.0  # P = e4m3(448 / 8 * p), p <= 8
+    assert L.sage_fp4_softmax_tau() == TAU_FP4  # the exact running maximum: P = e4m3(448 * p)
     # fp64 partial sums of the larger of the Q and K token-mean reductions (256-token chunks)
     assert L.sage_fp4_workspace_bytes(2, 32, 8, 8192, 8192, 128) == 2 * 32 * 32 * 128 * 8
     assert L.sage_fp4_workspace_bytes(0, 1, 1, 1, 1, 128) == 0
@@ -330,3 +397,13 @@ def test_fp4_validation(L):
     assert g(ctypes.byref(x), 0, 2, 0, 10, 0, 10, FAKE, None) == INVALID  # h >= H
     assert g(ctypes.byref(x), 0, 0, 300, 100, 0, 10, FAKE, None) == INVALID  # past Nq_pad
     assert g(ctypes.byref(x), 0, 0, 0, 10, 0, 10, None, None) == INVALID
+
+
+def test_python_sm_scale_argument():
+    """The binding passes 0 (the C default, 1/sqrt(d)) only when no sm_scale is given; an explicit
+    zero, negative or non-finite value is refused instead of silently replaced."""
+    assert api.sm_scale_arg(None) == 0.0
+    assert api.sm_scale_arg(0.125) == 0.125
+    for bad in (0.0, -0.5, float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            api.sm_scale_arg(bad)

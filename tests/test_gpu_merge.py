@@ -16,7 +16,7 @@ import torch
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd.synthetic import make_inputs
 
-from gpu_helpers import DEV, assert_lse_close, cosine, f32_of_bf16_bits, rel_l1, say, to_dev
+from gpu_helpers import DEV, assert_lse_close, check_o, cosine, f32_of_bf16_bits, qe_schedule, rel_l1, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -86,13 +86,11 @@ def test_split_kv_slices(orc, pv, cuts):
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     R = B * H * N
     qe = [orc.run_qe(Qb, np.ascontiguousarray(Kb[:, :, lo:hi]), np.ascontiguousarray(Vb[:, :, lo:hi]), pv=pv,
-                     BN=sage.block_n(pv), tau=sage.softmax_tau(pv), lsum_rounded=sage.rowsum_rounded(pv))
+                     **qe_schedule(pv))
           for lo, hi in zip(cuts[:-1], cuts[1:])]
     # each part against its own emulation first (fp32 outputs: the kernel's unrounded O)
     for s, r in enumerate(qe):
-        ep = rel_l1(o_parts[s].cpu().numpy().reshape(R, d), r.o32)
-        say(f"  part {s}: fp32 O rel-L1 vs emulation {ep:.3e}")
-        assert ep <= 1e-3
+        check_o(o_parts[s].cpu().numpy().reshape(R, d), r.o32, pv, f"part {s} (fp32 O)")
     wo, wl = orc.merge_lse(np.stack([r.o32 for r in qe]), np.stack([r.lse for r in qe]))
     got = _as_f32(out).reshape(R, d)
     e1 = rel_l1(got, f32_of_bf16_bits(orc.f32_to_bf16(wo.astype(np.float32))))  # both rounded to bf16
@@ -131,6 +129,5 @@ def test_split_by_masks_with_empty_parts(orc):
     assert rel_l1(_as_f32(out).reshape(R, d), _as_f32(full_o).reshape(R, d)) <= 2e-3
     assert_lse_close(lse.cpu().numpy().reshape(R), full_l.cpu().numpy().reshape(R), 1e-4)
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
-    r = orc.run_qe(Qb, Kb, Vb, causal=True, BN=sage.block_n("fp16"), tau=sage.softmax_tau("fp16"),
-                   lsum_rounded=sage.rowsum_rounded("fp16"))
+    r = orc.run_qe(Qb, Kb, Vb, causal=True, **qe_schedule("fp16"))
     assert rel_l1(_as_f32(out).reshape(R, d), f32_of_bf16_bits(r.o16)) <= 2e-3

@@ -18,8 +18,8 @@ from quantized_attention_quantize_amd import api
 from quantized_attention_quantize_amd.synthetic import (additive_mask, make_inputs, random_additive_mask,
                                                         random_mask)
 
-from gpu_helpers import (DEV, assert_lse_close, bits, cosine, f32_of_bf16_bits, lse_rows, rel_l1, rows_of, say,
-                         to_dev, unpermute_vt)
+from gpu_helpers import (DEV, TAU, assert_lse_close, bits, check_o, cosine, f32_of_bf16_bits, lse_rows, qe_schedule,
+                         rel_l1, rows_of, say, to_dev, unpermute_vt)
 
 pytestmark = pytest.mark.gpu
 
@@ -224,10 +224,13 @@ def test_prep_v_fp8_extremes(orc):
     assert np.array_equal(nat[:, :, :N], want) and np.array_equal(vs.cpu().numpy(), want_s)
 
 
-def oracle_mask(mask):
-    """A bool mask as uint8, a float32 mask as it is."""
+def oracle_mask(mask, Nq=None):
+    """A bool mask as uint8, a float32 mask as it is; a mask broadcast over the queries ([B,1,1,Nk])
+    is written out to Nq rows for the oracle."""
     if mask is None:
         return None
+    if Nq is not None and mask.shape[-2] == 1:
+        mask = mask.expand(*mask.shape[:-2], Nq, mask.shape[-1]).contiguous()
     return mask.numpy() if mask.dtype == torch.float32 else mask.numpy().astype(np.uint8)
 
 
@@ -244,11 +247,14 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     B, H, Nq, d = inp.q.shape
     if rows is None:
         rows = np.arange(B * H * Nq, dtype=np.int64)
-    m = oracle_mask(mask)
+    m = oracle_mask(mask, inp.q.shape[2])
     r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m,
-                   sm_scale=sm_scale, BN=sage.block_n(pv), tau=sage.softmax_tau(pv),
-                   lsum_rounded=sage.rowsum_rounded(pv), rows=rows, dtype=inp.dtype, smooth_v=smooth_v,
-                   per_block_mean=per_block_mean)
+                   sm_scale=sm_scale, rows=rows, dtype=inp.dtype, smooth_v=smooth_v, per_block_mean=per_block_mean,
+                   **qe_schedule(pv))
+    # the plain reading (exact running maximum); for e4m3 P that is the kernels' schedule itself
+    r.plain = r if TAU[pv] == 0 else orc.run_qe(
+        inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), pv=pv, causal=causal, mask=m, sm_scale=sm_scale,
+        rows=rows, dtype=inp.dtype, smooth_v=smooth_v, per_block_mean=per_block_mean, tau=0.0)
     ex_o, ex_l = orc.attn_ex(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), causal=causal, mask=m,
                              sm_scale=sm_scale, rows=rows, dtype=inp.dtype)
     got_o = rows_of(out, rows, layout)
@@ -256,11 +262,11 @@ def run_both(orc, inp, *, pv="fp16", causal=False, mask=None, sm_scale=None, lay
     return got_o, got_l, r, ex_o, ex_l
 
 
-def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16", ex_cos=EX_COS):
-    qe_o = f32_of_bf16_bits(r.o16) if out_dtype == "bf16" else r.o16.view(np.float16).astype(np.float32)
-    e1 = rel_l1(got_o, qe_o)
-    assert e1 <= QE_REL_L1, f"rel-L1 vs quantized emulation {e1}"
+def check(got_o, got_l, r, ex_o, ex_l, *, pv="fp16", out_dtype="bf16", ex_cos=EX_COS, tag=""):
+    dec = f32_of_bf16_bits if out_dtype == "bf16" else (lambda b: b.view(np.float16).astype(np.float32))
+    e1 = check_o(got_o, dec(r.o16), pv, tag, plain=dec(r.plain.o16))
     assert_lse_close(got_l, r.lse, QE_LSE)
+    assert_lse_close(got_l, r.plain.lse, QE_LSE)
     live = np.abs(ex_o).sum(axis=1) > 0
     if live.any():
         cos = cosine(got_o[live], ex_o[live])
@@ -284,10 +290,13 @@ CASES = [
     dict(name="fp8", B=1, H=2, Nq=400, Nk=777, d=128, pv="fp8", sigma=8.0),
     dict(name="fp8_d64_causal", B=1, H=2, Nq=300, Nk=300, d=64, pv="fp8", causal=True),
     dict(name="fp8_mask", B=1, H=2, Nq=256, Nk=320, d=128, pv="fp8", mask="half"),
+    # key-padding masks [B, 1, 1, Nk], broadcast over the queries (mask_stride_q = 0)
+    dict(name="mask_keypad", B=2, H=2, Nq=300, Nk=417, d=128, mask="keypad"),
+    dict(name="fmask_keypad_fp8_causal", B=2, H=2, Nq=260, Nk=260, d=64, pv="fp8", causal=True, mask="f_keypad"),
     dict(name="sm_scale", B=1, H=2, Nq=256, Nk=256, d=128, sm_scale=0.05),
-    # peaked rows: under the lazy maximum p reaches 2^tau, so e4m3 P = 448 * 2^-tau * p nears 448
-    # (e4m3 P and V on rows this peaked are at cosine 0.9989 from exact attention in the emulation
-    # itself, with the exact running maximum as with the lazy one)
+    # peaked rows: most of a row's weight sits on a few keys, where e4m3 P = 448 * p reaches 448 and
+    # FP16 P (under its lazy maximum) reaches 2^8 (e4m3 P and V on rows this peaked are at cosine
+    # 0.9989 from exact attention in the emulation itself)
     dict(name="fp8_peaked", B=1, H=2, Nq=300, Nk=900, d=128, pv="fp8", sm_scale=0.6, ex_cos=0.998),
     dict(name="fp16_peaked_causal", B=1, H=2, Nq=400, Nk=400, d=128, sm_scale=0.6, causal=True),
     dict(name="nhd", B=2, H=3, Nq=200, Nk=260, d=64, layout="NHD"),
@@ -340,6 +349,17 @@ def case_mask(c, B, H, Nq, Nk):
         return random_additive_mask(B, 1, Nq, Nk, p_drop=0.25, scale=2.0, seed=5)
     if kind == "f_rand_h":
         return random_additive_mask(B, H, Nq, Nk, p_drop=0.3, scale=3.0, seed=6)
+    if kind == "keypad":  # a key-padding mask [B, 1, 1, Nk]: each batch entry drops its own keys
+        m = torch.ones(B, 1, 1, Nk, dtype=torch.bool)
+        for b in range(B):
+            m[b, 0, 0, Nk - 37 * (b + 1):] = False
+        m[0, 0, 0, 5:70] = False  # and a run crossing a key tile
+        return m
+    if kind == "f_keypad":  # the same as an fp32 additive mask [B, 1, 1, Nk], broadcast over the queries
+        m = torch.zeros(B, 1, 1, Nk, dtype=torch.float32)
+        m[..., Nk // 3:] = float("-inf")
+        m[..., :40] = 0.7
+        return m
     if kind == "f_tiles":
         # whole 256 x 64 tiles that are all 0 (read no mask), all -inf (skipped) or mixed
         m = torch.zeros(B, 1, Nq, Nk, dtype=torch.float32)
@@ -369,8 +389,8 @@ def test_attention_parity(orc, case):
                                            sm_scale=c.get("sm_scale"), layout=c.get("layout", "HND"),
                                            smooth_v=c.get("smooth_v", False),
                                            per_block_mean=c.get("per_block_mean", False))
-    e1 = check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype, ex_cos=c.get("ex_cos", EX_COS))
-    say(f"  rel-L1 vs QE {e1:.3e}")
+    check(got_o, got_l, r, ex_o, ex_l, pv=c.get("pv", "fp16"), out_dtype=inp.dtype, ex_cos=c.get("ex_cos", EX_COS),
+          tag=c["name"])
 
 
 def test_fully_masked_rows_and_tiles(orc):
@@ -471,8 +491,7 @@ def test_output_dtype_is_a_choice(orc):
         sage.attn_fwd(qk, v, out=out)
         torch.cuda.synchronize()
         name = "fp16" if dt_out == torch.float16 else "bf16"
-        r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), BN=sage.block_n("fp16"),
-                       tau=sage.softmax_tau("fp16"), lsum_rounded=sage.rowsum_rounded("fp16"), dtype=inp.dtype,
-                       out_dtype=name)
+        r = orc.run_qe(inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v), dtype=inp.dtype, out_dtype=name,
+                       **qe_schedule("fp16"))
         want = f32_of_bf16_bits(r.o16) if name == "bf16" else r.o16.view(np.float16).astype(np.float32)
         assert rel_l1(out.float().cpu().numpy().reshape(-1, d), want) <= QE_REL_L1

@@ -16,7 +16,7 @@ import torch
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd.synthetic import make_varlen_inputs
 
-from gpu_helpers import DEV, assert_lse_close, cosine, f32_of_bf16_bits, rel_l1, say
+from gpu_helpers import DEV, TAU, assert_lse_close, check_o, cosine, f32_of_bf16_bits, qe_schedule, rel_l1, say
 
 pytestmark = pytest.mark.gpu
 
@@ -91,13 +91,12 @@ def test_varlen_parity(orc, case):
             assert np.array_equal(g.k_mean[b].cpu().numpy(), cq_.kmean[0])
     say("  per-sequence quantization bit-exact")
 
-    o32, o16, qlse = orc.run_qe_varlen(Q, K, V, cuq, cuk, pv=pv, causal=causal, BN=sage.block_n(pv),
-                                       tau=sage.softmax_tau(pv), lsum_rounded=sage.rowsum_rounded(pv),
-                                       dtype=inp.dtype, smooth_v=sv, per_block_mean=pbm)
+    o32, o16, qlse = orc.run_qe_varlen(Q, K, V, cuq, cuk, pv=pv, causal=causal, dtype=inp.dtype, smooth_v=sv,
+                                       per_block_mean=pbm, **qe_schedule(pv))
+    plain = o16 if TAU[pv] == 0 else orc.run_qe_varlen(Q, K, V, cuq, cuk, pv=pv, causal=causal, dtype=inp.dtype,
+                                                       smooth_v=sv, per_block_mean=pbm, tau=0.0)[1]
     got = out.float().cpu().numpy()
-    e1 = rel_l1(got, _dec(o16, inp.dtype))
-    say(f"  rel-L1 vs per-sequence emulation {e1:.3e}")
-    assert e1 <= 1e-3
+    check_o(got, _dec(o16, inp.dtype), pv, "varlen", plain=_dec(plain, inp.dtype))
     assert_lse_close(lse.cpu().numpy(), qlse, 1e-3)
     eo, el = orc.attn_ex_varlen(Q, K, V, cuq, cuk, causal=causal, dtype=inp.dtype)
     live = np.abs(eo).sum(-1) > 0

@@ -1,9 +1,11 @@
 """GPU parity at the full workload sizes (the launch configuration the benchmark times).
 
 For every workload: the K mean, int8 Q/K, their scales and the prepared V are compared bit for bit
-over the whole tensors; int32 scores on windows of 256 rows x all keys of two heads; O and LSE on a
-seeded sample of rows (random rows over all heads plus each head's first and last rows) against
-the oracle's quantized emulation, and against fp64 exact attention.
+over the whole tensors; int32 scores on windows of 256 rows x all keys (the first and last 256 rows)
+of four heads; O and LSE on four full heads plus 4096 random rows over all heads against the
+oracle's quantized emulation run with the kernels' schedule (aggregate and per-row bounds), on the
+random rows against the plain reading (the exact running maximum), and on a subsample against fp64
+exact attention.
 """
 
 import numpy as np
@@ -13,14 +15,53 @@ import torch
 import quantized_attention_quantize_amd as sage
 from quantized_attention_quantize_amd.synthetic import WORKLOADS, make_varlen_inputs, workload_inputs
 
-from gpu_helpers import (DEV, assert_lse_close, cosine, f32_of_bf16_bits, fp4_check_quant, lse_quant_bound, lse_rows,
-                         rel_l1, rows_of, say, to_dev, unpermute_vt)
+from gpu_helpers import (DEV, TAU, TAU_FP4, assert_lse_close, check_o, cosine, f32_of_bf16_bits, fp4_check_quant,
+                         lse_quant_bound, lse_rows, qe_schedule, rel_l1, rows_of, say, to_dev, unpermute_vt)
 
 pytestmark = pytest.mark.gpu
 
-N_RANDOM_ROWS = {"tiny": None, "n8k": 2048, "n8k_causal": 2048, "n8k_mask": 2048, "n17776_fp8": 1024, "n8k_gqa": 2048,
-                 "n8k_fp16": 2048, "n8k_fmask": 2048, "n8k_split2": 1024, "n8k_smoothv_pbm": 2048,
-                 "fp4_b1h24n4096": 2048, "n8k_fp4": 2048}
+N_RANDOM_ROWS = 4096
+N_FULL_HEADS = 4
+# the benchmark's four configurations (8192 tokens plain, causal and masked; 17776 tokens with
+# FP8 PV) are checked on whole heads plus random rows; the other workloads on random rows and the
+# first and last rows of the first and last heads
+FULL_HEAD_WORKLOADS = ("n8k", "n8k_causal", "n8k_mask", "n17776_fp8")
+
+
+def sample_rows(B, H, Nq, seed=0, full_heads=True):
+    """Rows (b*H + h)*Nq + i to check at full size: every row of N_FULL_HEADS heads (the first, the
+    last and two seeded others; with full_heads=False their first and last 64 rows only) plus
+    N_RANDOM_ROWS seeded random rows over all heads.  Returns (all rows sorted, the random rows
+    sorted).  A workload with fewer rows is checked whole."""
+    R = B * H * Nq
+    if R <= N_RANDOM_ROWS:
+        r = np.arange(R, dtype=np.int64)
+        return r, r
+    rng = np.random.default_rng(seed)
+    nh = B * H
+    heads = sorted({0, nh - 1, *rng.choice(nh, N_FULL_HEADS - 2, replace=False).tolist()})
+    span = np.arange(Nq) if full_heads else np.concatenate([np.arange(64), np.arange(Nq - 64, Nq)])
+    full = np.concatenate([bh * Nq + span for bh in heads])
+    rand = np.sort(rng.choice(R, N_RANDOM_ROWS, replace=False)).astype(np.int64)
+    return np.unique(np.concatenate([full, rand])).astype(np.int64), rand
+
+
+def chunked(fn, rows, chunk=6144):
+    """fn(rows) -> (o32, o16, lse) over row chunks, with a progress line per chunk (the oracle takes
+    tens of seconds on whole heads)."""
+    parts = []
+    for i in range(0, rows.size, chunk):
+        parts.append(fn(rows[i:i + chunk]))
+        say(f"    oracle rows {min(i + chunk, rows.size)}/{rows.size}")
+    return tuple(np.concatenate([p[j] for p in parts]) for j in range(3))
+
+
+def window_heads(B, H, seed=0):
+    """Up to four (b, h) query heads for the int32 score windows: the first, the last and two others."""
+    rng = np.random.default_rng(seed + 1)
+    picks = [(0, 0)] if B * H == 1 else [(0, 0), (B - 1, H - 1)]
+    others = [divmod(int(bh), H) for bh in rng.permutation(B * H) if divmod(int(bh), H) not in picks]
+    return picks + others[:4 - len(picks)]
 
 
 @pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items()
@@ -68,10 +109,10 @@ def test_workload_parity(orc, name):
     del nat, got, vt
     say("  prepared V bit-exact")
 
-    # int32 scores: 256 rows x all keys, first and last rows of two heads
+    # int32 scores: 256 rows x all keys, the first and last rows of four heads
     nqp, nkp = c.q8.shape[2], c.k8.shape[2]
     grp = w.H // (w.Hkv or w.H)  # query heads per key/value head
-    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+    for (b, h) in window_heads(w.B, w.H):
         hk = h // grp
         for r0 in (0, nqp - 256):
             got = sage.debug_qk_int32(g, b, h, r0, 256, 0, nkp).cpu().numpy()
@@ -83,27 +124,23 @@ def test_workload_parity(orc, name):
     out, lse = sage.sageattn(q, k, v, is_causal=w.causal, attn_mask=mask_dev, return_lse=True, pv_dtype=w.pv,
                              smooth_v=w.smooth_v, per_block_mean=w.per_block_mean)
     torch.cuda.synchronize()
-    R = w.B * w.H * w.Nq
-    n_rand = N_RANDOM_ROWS[name]
-    if n_rand is None:
-        rows = np.arange(R, dtype=np.int64)
-    else:
-        rng = np.random.default_rng(0)
-        ends = [bh * w.Nq + i for bh in (0, w.B * w.H - 1) for i in list(range(64)) + list(range(w.Nq - 64, w.Nq))]
-        rows = np.unique(np.concatenate([rng.choice(R, n_rand, replace=False), np.array(ends)])).astype(np.int64)
+    rows, rand = sample_rows(w.B, w.H, w.Nq, full_heads=name in FULL_HEAD_WORKLOADS)
     m_u8 = inp.mask_u8
-    vh_o, vs_o = (vh, vsc)
-    o32, obf, qlse = orc.attn_qe(c, vh_o, vs_o, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8,
-                                 BN=sage.block_n(w.pv), tau=sage.softmax_tau(w.pv),
-                                 lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows, out_dtype=inp.dtype, vmean=vm)
+    dec = f32_of_bf16_bits if inp.dtype == "bf16" else (lambda b: b.view(np.float16).astype(np.float32))
+    o32, obf, qlse = chunked(lambda rr: orc.attn_qe(c, vh, vsc, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8, rows=rr,
+                                                    out_dtype=inp.dtype, vmean=vm, **qe_schedule(w.pv)), rows)
     got_o = rows_of(out, rows)
     got_l = lse_rows(lse, rows)
     assert out.dtype == inp.q.dtype
-    want_o = f32_of_bf16_bits(obf) if inp.dtype == "bf16" else obf.view(np.float16).astype(np.float32)
-    e_qe = rel_l1(got_o, want_o)
-    say(f"  rows={rows.size} rel-L1 vs quantized emulation {e_qe:.3e}")
-    assert e_qe <= 1e-3
+    check_o(got_o, dec(obf), w.pv, f"{rows.size} rows")
     assert_lse_close(got_l, qlse, 1e-3)
+    # the plain reading (exact running maximum) on the random rows; for e4m3 P it is the schedule
+    if TAU[w.pv] != 0:
+        _, pbf, plse = orc.attn_qe(c, vh, vsc, w.pv, w.Nq, w.Nk, causal=w.causal, mask=m_u8, rows=rand,
+                                   out_dtype=inp.dtype, vmean=vm, tau=0.0)
+        sel_r = np.searchsorted(rows, rand)
+        check_o(got_o[sel_r], dec(pbf), w.pv, f"{rand.size} random rows", plain=dec(pbf))
+        assert_lse_close(got_l[sel_r], plse, 1e-3)
     ex_rows = rows[:: max(1, rows.size // 512)]
     ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, mask=m_u8, rows=ex_rows, dtype=inp.dtype)
     sel = np.searchsorted(rows, ex_rows)
@@ -138,11 +175,7 @@ def test_split_workload_parity(orc, name):
     bounds = [w.Nk * s // S for s in range(S + 1)]
     o_parts = torch.empty(S, w.B, w.H, w.Nq, w.d, dtype=torch.float32, device=DEV)
     l_parts = torch.empty(S, w.B, w.H, w.Nq, dtype=torch.float32, device=DEV)
-    rng = np.random.default_rng(0)
-    R = w.B * w.H * w.Nq
-    ends = [bh * w.Nq + i for bh in (0, w.B * w.H - 1) for i in list(range(64)) + list(range(w.Nq - 64, w.Nq))]
-    rows = np.unique(np.concatenate([rng.choice(R, N_RANDOM_ROWS[name], replace=False), np.array(ends)]))
-    rows = rows.astype(np.int64)
+    rows, _ = sample_rows(w.B, w.H, w.Nq, full_heads=False)
     qe_parts = []
     for s, (lo, hi) in enumerate(zip(bounds[:-1], bounds[1:])):
         Ks, Vs = np.ascontiguousarray(Kb[:, :, lo:hi]), np.ascontiguousarray(Vb[:, :, lo:hi])
@@ -153,17 +186,14 @@ def test_split_workload_parity(orc, name):
         assert np.array_equal(g.k8.cpu().numpy(), c.k8) and np.array_equal(g.q8.cpu().numpy(), c.q8), ("codes", s)
         assert np.array_equal(g.k_scale.cpu().numpy(), c.ks) and np.array_equal(g.k_mean.cpu().numpy(), c.kmean)
         vh, vsc = orc.prep_v(Vs, w.pv, dtype=inp.dtype)
-        qe_parts.append(orc.attn_qe(c, vh, vsc, w.pv, w.Nq, hi - lo, BN=sage.block_n(w.pv),
-                                    tau=sage.softmax_tau(w.pv), lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows))
+        qe_parts.append(orc.attn_qe(c, vh, vsc, w.pv, w.Nq, hi - lo, rows=rows, **qe_schedule(w.pv)))
         say(f"  slice {s}: quantization bit-exact")
     out, lse = sage.merge_lse(o_parts, l_parts, out_dtype=inp.q.dtype)
     torch.cuda.synchronize()
     wo, wl = orc.merge_lse(np.stack([p[0] for p in qe_parts]), np.stack([p[2] for p in qe_parts]))
     got_o = rows_of(out, rows)
     got_l = lse_rows(lse, rows)
-    e_qe = rel_l1(got_o, f32_of_bf16_bits(orc.f32_to_bf16(wo.astype(np.float32))))
-    say(f"  rows={rows.size} rel-L1 vs merged emulation {e_qe:.3e}")
-    assert e_qe <= 1e-3
+    check_o(got_o, f32_of_bf16_bits(orc.f32_to_bf16(wo.astype(np.float32))), w.pv, f"{rows.size} merged rows")
     assert_lse_close(got_l, wl, 1e-3)
     ex_rows = rows[:: max(1, rows.size // 256)]
     ex_o, ex_l = orc.attn_ex(Qb, Kb, Vb, rows=ex_rows, dtype=inp.dtype)
@@ -210,9 +240,8 @@ def test_varlen_workload_parity(orc, name):
         vh, vsc = orc.prep_v(Vs, w.pv, dtype=vin.dtype)
         rows = np.unique(np.concatenate([rng.choice(H * n, 96, replace=False), [0, n - 1, H * n - 1]]))
         rows = rows.astype(np.int64)
-        o32, o16, ql = orc.attn_qe(c, vh, vsc, w.pv, n, n, causal=w.causal, BN=sage.block_n(w.pv),
-                                   tau=sage.softmax_tau(w.pv), lsum_rounded=sage.rowsum_rounded(w.pv), rows=rows,
-                                   out_dtype=vin.dtype)
+        o32, o16, ql = orc.attn_qe(c, vh, vsc, w.pv, n, n, causal=w.causal, rows=rows, out_dtype=vin.dtype,
+                                   **qe_schedule(w.pv))
         hh, ii = rows // n, rows % n
         got = out[torch.from_numpy(lo + ii).to(DEV), torch.from_numpy(hh).to(DEV)].float().cpu().numpy()
         gl = lse[torch.from_numpy(hh).to(DEV), torch.from_numpy(lo + ii).to(DEV)].cpu().numpy()
@@ -225,9 +254,7 @@ def test_varlen_workload_parity(orc, name):
             eo, el = orc.attn_ex(Qs, Ks, Vs, causal=w.causal, rows=rows[:16], dtype=vin.dtype)
             assert cosine(got[:16], eo) >= 0.999 and rel_l1(got[:16], eo) <= 3e-2
     say(f"  every sequence's quantization bit-exact")
-    e_qe = rel_l1(np.concatenate(got_all), np.concatenate(want_all))
-    say(f"  rel-L1 vs per-sequence emulation {e_qe:.3e}")
-    assert e_qe <= 1e-3
+    check_o(np.concatenate(got_all), np.concatenate(want_all), w.pv, "every sequence's sampled rows")
 
 
 @pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if w.method == "fp4"])
@@ -252,19 +279,14 @@ def test_fp4_workload_parity(orc, name):
     fp4_check_quant(g, r, w.Nq, w.Nk, (v4, ve), k_max)
     say("  quantization bit-exact over the whole tensors")
     del g
-    rng = np.random.default_rng(7)
-    R = w.B * w.H * w.Nq
-    edge = np.concatenate([np.arange(64), np.arange(w.Nq - 64, w.Nq), (w.B * w.H - 1) * w.Nq + np.arange(64),
-                           R - 64 + np.arange(64)])
-    rows = np.unique(np.concatenate([rng.choice(R, N_RANDOM_ROWS[name], replace=False), edge]))
-    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=w.causal, tau=sage.softmax_tau_fp4(), rows=rows,
-                                      out_dtype=w.dtype)
+    rows, _ = sample_rows(w.B, w.H, w.Nq, seed=7, full_heads=False)
+    o32, o16, qlse = orc.fp4_attn_qe(r, v4, ve, causal=w.causal, tau=TAU_FP4, rows=rows, out_dtype=w.dtype)
     got = rows_of(out, rows)
-    e1 = rel_l1(got, f32_of_bf16_bits(o16))
-    say(f"  {rows.size} rows: rel-L1 vs emulation {e1:.3e}")
-    assert e1 <= 1e-3
+    check_o(got, f32_of_bf16_bits(o16), "fp8", f"{rows.size} rows")  # e4m3 P, exact running maximum
     assert_lse_close(lse_rows(lse, rows), qlse, 1e-3)
-    eo, _ = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, rows=rows, dtype=w.dtype)
+    ex_rows = rows[:: max(1, rows.size // 1024)]
+    eo, _ = orc.attn_ex(Qb, Kb, Vb, causal=w.causal, rows=ex_rows, dtype=w.dtype)
+    got = got[np.searchsorted(rows, ex_rows)]
     cs, rl = cosine(got, eo), rel_l1(got, eo)
     say(f"  vs exact: cosine {cs:.5f} rel-L1 {rl:.3e}")
     assert cs >= 0.97 and rl <= 0.25

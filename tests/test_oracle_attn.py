@@ -244,14 +244,35 @@ def test_qe_lazy_maximum_only_moves_rounding(orc, sm):
     assert np.array_equal(c.o16, a.o16)
 
 
+@pytest.mark.parametrize("case", ["c1", "n2k", "peaked"])
+def test_qe_fp16_lazy_maximum_within_parity_bar(orc, case):
+    """The FP16 kernels run the online softmax with a reference maximum lazy by 8 log2 units; the
+    plain reading is the exact running maximum.  Both normalize the same exponentials, so they differ
+    only where fp16 P is rounded: measured 0.9e-4 to 2.9e-4 relative L1 (worst row 3.6e-4 to
+    4.5e-4) on these shapes, the tiny configuration, a 2048-key head and peaked rows, with the seeds
+    0 and 1.  Pinned here at 4e-4 aggregate and 6e-4 per row, which keeps the GPU's comparison with
+    the plain reading inside the 1e-3 parity bar with room for the GPU's own fp32 rounding."""
+    shape, sm = {"c1": ((1, 2, 256, 256, 64), None), "n2k": ((1, 2, 512, 2048, 128), None),
+                 "peaked": ((1, 2, 300, 900, 128), 0.6)}[case]
+    for seed in (0, 1):
+        inp = make_inputs(*shape, sigma=4.0, seed=seed)
+        Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
+        lazy = orc.run_qe(Qb, Kb, Vb, pv="fp16", BN=64, tau=8.0, sm_scale=sm)
+        plain = orc.run_qe(Qb, Kb, Vb, pv="fp16", BN=64, tau=0.0, sm_scale=sm)
+        a, b = lazy.o32.astype(np.float64), plain.o32.astype(np.float64)
+        assert _rel_l1(a, b) <= 4e-4
+        assert (np.abs(a - b).sum(-1) / np.abs(b).sum(-1)).max() <= 6e-4
+        np.testing.assert_allclose(lazy.lse, plain.lse, atol=1e-5)
+
+
 @pytest.mark.parametrize("sm", [None, 0.6])
-def test_qe_lazy_maximum_e4m3_scales_p(orc, sm):
-    """With e4m3 P the lazy reference maximum lets p reach 2^tau, so P is e4m3(448 * 2^-tau * p):
-    the LSE (denominator over the fp32 p) is the same as with the exact running maximum to fp32
-    rounding, O moves only by e4m3 rounding noise (of the order of the emulation's own distance to
-    exact attention) and stays as close to exact attention.  Without
-    the 2^-tau the peaked rows (sm_scale = 0.6) would saturate at 448 and O would be far off.  tau
-    must be whole, so that the scale is exact."""
+def test_qe_lazy_maximum_e4m3_moves_every_rounding_point(orc, sm):
+    """Why e4m3 P runs against the exact running maximum.  Under a lazy maximum the scale between
+    448 * p and the lazily referenced 448 * 2^-tau * p is 2^(m_exact - m_lazy - tau), not a power of
+    two, so every element of P is rounded at a different point: the LSE (a sum of fp32 p) agrees to
+    fp32 rounding, but O moves by the order of e4m3's own rounding error -- far beyond the 1e-3
+    parity bar -- while each reading stays as far from exact attention as the other.  tau must be
+    whole, so that the scale stays exact."""
     inp = make_inputs(1, 2, 300, 900, 128, seed=16)
     Qb, Kb, Vb = inp.bits(inp.q), inp.bits(inp.k), inp.bits(inp.v)
     a = orc.run_qe(Qb, Kb, Vb, pv="fp8", BN=64, tau=0.0, sm_scale=sm)
@@ -259,9 +280,7 @@ def test_qe_lazy_maximum_e4m3_scales_p(orc, sm):
     for tau in (2.0, 3.0):
         b = orc.run_qe(Qb, Kb, Vb, pv="fp8", BN=64, tau=tau, sm_scale=sm)
         np.testing.assert_allclose(b.lse, a.lse, atol=2e-5)
-        # rounding noise: each emulation is ~4% (rel-L1) from exact attention, so the two differ
-        # by that order, while their distances to exact attention agree much more closely
-        assert _rel_l1(b.o32, a.o32) < 1.5 * _rel_l1(a.o32, eo)
+        assert _rel_l1(b.o32, a.o32) > 2e-3  # outside the 1e-3 parity bar
         assert abs(_rel_l1(b.o32, eo) - _rel_l1(a.o32, eo)) < 5e-3
     with pytest.raises(ValueError):
         orc.run_qe(Qb, Kb, Vb, pv="fp8", tau=1.5)
