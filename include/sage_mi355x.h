@@ -153,6 +153,19 @@ size_t sage_quantize_workspace_bytes(int64_t B, int64_t Hkv, int64_t Nk, int64_t
 sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free step 1, for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The same computation, arguments and results
+ * as sage_quantize_qk, without the workspace: the K-mean partial sums go to a library-owned device
+ * array of SAGE_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the device's first call until the
+ * process ends.  Sizes whose sage_quantize_workspace_bytes(B, Hkv, Nk, d) exceeds it are refused
+ * with WORKSPACE (8 MiB holds B * Hkv * ceil(Nk/256) * d <= 1,048,576, e.g. 64 key heads of
+ * 32768 tokens at d = 128).  Every call on a GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialized by the caller.  Allocates and
+ * frees nothing.  Errors: as sage_quantize_qk; HIP if the array's address cannot be obtained. */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+sage_status sage_quantize_qk_noalloc(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                                     void* stream);
+
 /* Bytes of workspace sage_prepare_v needs: per-chunk partial maxima of |V| (fp8) or fp64 partial
  * sums of V (FP16 with smooth_v); an FP16 call without smooth_v needs none.  Host only. */
 size_t sage_prepare_v_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, sage_pv_dtype pv);

@@ -73,7 +73,7 @@ EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_r
            "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_softmax_tau",
            "sage_fp4_workspace_bytes",
            "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores", "sage_qk_quant_bytes",
-           "sage_qk_quant_init")
+           "sage_qk_quant_init", "sage_quantize_qk_noalloc")
 
 
 def lib_path() -> str:
@@ -136,6 +136,9 @@ def load_library():
     L.sage_qk_quant_bytes.restype = SZ
     L.sage_qk_quant_init.argtypes = [P, SZ, I64, I64, I64, I64, I64, I64, I, ctypes.POINTER(QKQuant)]
     L.sage_qk_quant_init.restype = I
+    L.sage_quantize_qk_noalloc.argtypes = [ctypes.POINTER(QKVDesc), ctypes.POINTER(QKVDesc), ctypes.POINTER(QKQuant),
+                                           P]
+    L.sage_quantize_qk_noalloc.restype = I
     L.sage_status_string.argtypes = [I]
     L.sage_status_string.restype = ctypes.c_char_p
     L.sage_fp4_q_blocks.argtypes = [I64, I]

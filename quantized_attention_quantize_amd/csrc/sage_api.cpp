@@ -296,6 +296,49 @@ sage_status sage_quantize_qk(const sage_qkv_desc* q, const sage_qkv_desc* k, con
   return enqueue_quantize(quant_args(q, k, out), workspace, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free quantize entry point: the K-mean fp64 partial sums.  One array per
+// GPU, in the library's device code, kept until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the device symbol): it takes the
+// device address once per device with hipGetSymbolAddress and uses that.
+static __device__ __align__(256) double scratch[SAGE_NOALLOC_SCRATCH_BYTES / sizeof(double)];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the device's first call).
+sage_status noalloc_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SAGE_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // the same address if two threads race here
+  }
+  *ptr = p;
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sage_status sage_quantize_qk_noalloc(const sage_qkv_desc* q, const sage_qkv_desc* k, const sage_qk_quant* out,
+                                     void* stream) {
+  sage_status s;
+  // host validation first, with the scratch array standing in as the workspace size
+  if ((s = validate_quantize(q, k, out, reinterpret_cast<void*>(uintptr_t(256)), SAGE_NOALLOC_SCRATCH_BYTES)) !=
+      SAGE_OK)
+    return s;
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != SAGE_OK) return s;
+  // every chunk's partial sums are written before they are read, so nothing needs clearing
+  return enqueue_quantize(quant_args(q, k, out), ws, static_cast<hipStream_t>(stream));
+}
+
 sage_status sage_quantize_qk_varlen(const sage_qkv_desc* q, const sage_qkv_desc* k, const int32_t* cu_seqlens_q,
                                     const int32_t* cu_seqlens_k, int64_t total_q, int64_t total_k,
                                     const sage_qk_quant* out, void* workspace, size_t workspace_bytes,

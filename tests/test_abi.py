@@ -407,3 +407,17 @@ def test_python_sm_scale_argument():
     for bad in (0.0, -0.5, float("nan"), float("inf")):
         with pytest.raises(ValueError):
             api.sm_scale_arg(bad)
+
+
+def test_noalloc_quantize_validation(L):
+    """The allocation-free quantize entry point validates like sage_quantize_qk (host only, before
+    any HIP call) and refuses sizes whose K-mean partial sums would not fit its 8 MiB scratch array:
+    B * Hkv * ceil(Nk/256) * d doubles."""
+    def call(q, k, out):
+        return L.sage_quantize_qk_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(out), None)
+    assert call(desc(data=0), desc(), quant()) == INVALID
+    assert call(desc(d=96), desc(d=96), quant(d=96)) == UNSUPPORTED
+    assert L.sage_quantize_workspace_bytes(1, 64, 40000, 128) > (8 << 20)
+    big_q, big_k, big_out = desc(H=64, N=40000, d=128), desc(H=64, N=40000, d=128), quant(H=64, Nq=40000, Nk=40000,
+                                                                                           d=128)
+    assert call(big_q, big_k, big_out) == WORKSPACE
