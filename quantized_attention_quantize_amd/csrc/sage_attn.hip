@@ -216,13 +216,14 @@ __device__ __forceinline__ v4i kfrag(const char* sK, const LaneBases& lb, int q)
 
 // QK MFMA q of S^T = K8 . Q8^T: starts key block q / (D/32)'s int32 accumulator at its first chunk
 // step, accumulates the later ones.  acc[kb][r] = score of query lr and key kb*32 + (r/4)*8 + g*4 + r%4.
-template <int D>
-__device__ __forceinline__ void qk_mfma(v4i kf, const v4i (&qf)[D / 32], int q, v16i (&acc)[2]) {
+template <int D, bool MG = false>
+__device__ __forceinline__ void qk_mfma(v4i kf, const v4i (&qf)[D / 32], int q, v16i (&acc)[2],
+                                        const v16i& magic = v16i{}) {
   constexpr int NB = D / 32;
   const int kb = q / NB, cs = q % NB;
   if (cs == 0) {
     const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[cs], z, 0, 0, 0);
+    acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[cs], MG ? magic : z, 0, 0, 0);
   } else {
     acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[cs], acc[kb], 0, 0, 0);
   }
@@ -230,10 +231,11 @@ __device__ __forceinline__ void qk_mfma(v4i kf, const v4i (&qf)[D / 32], int q, 
 
 // S^T for 64 keys x the wave's 32 queries, by the same operand reads and MFMA sequence as the
 // QK half of every tile step.
-template <int D>
-__device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32], const LaneBases& lb, v16i (&acc)[2]) {
+template <int D, bool MG = false>
+__device__ __forceinline__ void qk_tile(const char* sK, const v4i (&qf)[D / 32], const LaneBases& lb, v16i (&acc)[2],
+                                        const v16i& magic = v16i{}) {
 #pragma unroll
-  for (int q = 0; q < 2 * (D / 32); ++q) qk_mfma<D>(kfrag<D>(sK, lb, q), qf, q, acc);
+  for (int q = 0; q < 2 * (D / 32); ++q) qk_mfma<D, MG>(kfrag<D>(sK, lb, q), qf, q, acc, magic);
 }
 
 // Softmax state of a wave's rows.  Lane (lr, g) holds row lr; both halves of the wave carry the
@@ -331,12 +333,13 @@ __device__ __forceinline__ void max_piece(const v16i (&acc)[2], int (&ch)[4], in
 }
 // Combines the chains across the wave's halves and moves the reference maximum (lazy by
 // kSoftmaxTau[PV] log2 units).  Returns 2^(m_old - m_new); the new exponent offset goes to pm_new.
-template <int PV, bool MASKED, bool MF = false, bool BM = false>
+template <int PV, bool MASKED, bool MF = false, bool BM = false, bool MG = false>
 __device__ __forceinline__ float finish_max(const int (&ch)[4], float c, RowState& rs, float& pm_new, float cb = 0.f) {
   constexpr float kTau = kSoftmaxTau[PV];
   int im = smax<MF>(smax<MF>(ch[0], ch[1]), smax<MF>(ch[2], ch[3]));
   const auto sw = __builtin_amdgcn_permlane32_swap(im, im, false, false);  // lanes l and l ^ 32
   im = smax<MF>((int)sw[0], (int)sw[1]);
+  if constexpr (MG) im = (MASKED && im == INT_MIN) ? INT_MIN : im - kMagicBits;  // the biased accumulator
   float mt;
   if constexpr (MF)
     mt = __int_as_float(im);  // already log2-unit fp32, -inf if nothing is visible
@@ -408,6 +411,11 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   static_assert(!(MF && BM), "per_block_mean is not combined with a float mask");
   using SG = StepGeom<D, PV>;
   constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = SG::NM, LA = SG::LA;
+  // FP16 P without a float mask: the QK accumulators start at the bit pattern of 1.5 * 2^23, so each
+  // score arrives as the float 1.5 * 2^23 + s and enters the exponent with one FMA
+  constexpr bool MG = PV == 0 && !MF;
+  const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
+                      kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   constexpr int NG = 8;                 // exponential groups of 4 scores
   constexpr int FIN = 1;                // slot of the reference-maximum update (pieces 4-7 in slot 0)
   using VFrag = typename SG::VFrag;
@@ -447,6 +455,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   };
   float psum = 0.f, alpha = 1.f;
   float nb = 0.f;  // per_block_mean: T[n]'s row term minus the exponent offset
+  float kk = 0.f;  // MG: the exponent's constant term, -(1.5 * 2^23) * c - pm (+ the row term)
 
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
@@ -458,7 +467,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
       else
         o[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[k], pin.b, o[k], 0, 0, 0, 127, 0, 127);
     } else {
-      qk_mfma<D>(kf[k - NPV], qf, k - NPV, acc);
+      qk_mfma<D, MG>(kf[k - NPV], qf, k - NPV, acc, magic);
     }
     // T[n]'s row maxima over its second key block, then its reference maximum
     if (!MF && k == 0) {
@@ -467,9 +476,10 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
     }
     if (k == FIN) {
       float pm_new;
-      alpha = finish_max<PV, SLOW, MF, BM>(ch, c_cur, rs, pm_new, cb_cur);
+      alpha = finish_max<PV, SLOW, MF, BM, MG>(ch, c_cur, rs, pm_new, cb_cur);
       rs.pm = pm_new;
       if constexpr (BM) nb = cb_cur - pm_new;
+      if constexpr (MG) kk = __builtin_fmaf(-kMagic, c_cur, BM ? nb : -pm_new);
     }
     // exponentials of T[n] assigned to slot k
 #pragma unroll
@@ -487,6 +497,9 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
         float t;
         if constexpr (MF) {
           t = __builtin_amdgcn_exp2f(__int_as_float(si) - rs.pm);  // -inf gives 0
+        } else if constexpr (MG) {
+          t = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(si), c_cur, kk));
+          if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
         } else {
           t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c_cur, BM ? nb : -rs.pm));
           if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
@@ -665,13 +678,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   // per-tile scale, and whether a tile needs per-element visibility (past the end, ragged tail,
   // causal diagonal, mixed mask tile); lim / mtile describe the visible keys of such a tile
   auto scale_of = [&](int t) { return t < kt_end ? ((cq * scalar_ld(ksh, t)) * a.sm_scale) * kLog2e : 0.f; };
+  // In the loop the k-scales arrive by vector loads a step ahead, counted by vmcnt with the staging
+  // loads: a scalar load there would need lgkmcnt(0), which also drains the in-flight LDS reads.
+  const __amdgpu_buffer_rsrc_t ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)ksh, (short)0, a.nbk * 4, kBufferWord3);
+  const int vzero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);  // 0 in a vector register: a vector load
+  auto ks_load = [&](int t) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, vzero, (t < kt_end ? t : 0) * 4, 0));
+  };
+  auto scale_from = [&](int t, float ks) { return t < kt_end ? ((cq * ks) * a.sm_scale) * kLog2e : 0.f; };
+  // Tiles [0, first_part) are whole for every row of this wave: no ragged tail, and (causal) every
+  // key at or before the wave's first row.  Tiles at or past it, and past kt_end, take the
+  // per-element step.
+  const int first_part = a.causal && (r0u + 1) / kBlockN < nk / kBlockN ? (r0u + 1) / kBlockN : nk / kBlockN;
   auto partial = [&](int t) {
-    if (t >= kt_end) return true;
     // The test runs on a vector-register copy of the tile index (v_mbcnt_lo with an empty mask
     // adds 0): the compiler then keeps the masked/unmasked step choice as a per-lane branch, which
     // it compiles without spills, and holds no row index in a vector register across the loop.
-    const int j0 = __builtin_amdgcn_mbcnt_lo(0u, t) * kBlockN;
-    return j0 + kBlockN > nk || (a.causal && j0 + kBlockN - 1 > r0u) || (mt != nullptr && scalar_ld(mt, t) == 2);
+    return (int)__builtin_amdgcn_mbcnt_lo(0u, t) >= first_part || (mt != nullptr && scalar_ld(mt, t) == 2);
   };
   auto visible = [&](int t, int& lim, const void*& mtile) {
     if (t >= kt_end) {
@@ -712,7 +735,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
   float cb_cur = cb_of(t0);
   {  // scores of T[0] and the row maxima of its first key block; the first PV operands
-    qk_tile<D>(kring, qf, lb, acc);
+    constexpr bool MG = PV == 0 && !MF;  // as in tile_step: biased QK accumulators
+    const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
+                        kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits};
+    qk_tile<D, MG>(kring, qf, lb, acc, magic);
     int lim;
     const void* mtile;
     visible(t0, lim, mtile);
@@ -729,13 +755,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
 
   int n = 0;
   int tc = t0, tn = t1, tnn = t2, tnnn = t3;  // T[n] .. T[n+3]
+  float ks_n1 = scalar_ld(ksh, t1 < kt_end ? t1 : 0);  // k-scale of T[n+1]
   auto step = [&](auto slot) -> bool {
     constexpr int Q = decltype(slot)::value;  // n % kNS
     if (tc >= kt_end) return false;
     const float cb_nxt = cb_of(tn);  // before the staging loads (see above)
-    __syncthreads();
+    // The barrier orders this step's staging writes after every wave's reads of the slots they
+    // reuse (read and consumed in earlier steps), and makes the loads waited for at the end of the
+    // previous step visible to all waves.  LDS reads still in flight (the next PV operands, of a
+    // slot not rewritten here) may cross it.
+    asm volatile("s_barrier" ::: "memory");
     st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
     st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
+    const float ks_n2 = ks_load(tnn);  // k-scale of T[n+2], after the staging loads
     const char* sVp = vring + ((Q + kNS - 1) % kNS) * G::V_BYTES;  // V of T[n-1]
     const char* sVn = vring + Q * G::V_BYTES;                      // V of T[n]
     const char* sKn = kring + ((Q + 1) % kNS) * G::K_BYTES;        // K of T[n+1]
@@ -766,19 +798,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     }
     // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare under the lazy maximum)
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
-    c_cur = scale_of(tn);
     cb_cur = cb_nxt;
     part_cur = part_nxt;
-    // the loads of the previous steps must have landed before the next barrier
+    // the loads of the previous steps (and the k-scale of T[n+1]) must have landed before the next
+    // barrier; this step's staging loads and k-scale load stay in flight
     switch (nload) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1>(); break;
-      case 2: wait_vmcnt<2>(); break;
-      case 3: wait_vmcnt<3>(); break;
-      case 4: wait_vmcnt<4>(); break;
-      case 5: wait_vmcnt<5>(); break;
-      default: wait_vmcnt<6>(); break;
+      case 0: wait_vmcnt<1>(); break;
+      case 1: wait_vmcnt<2>(); break;
+      case 2: wait_vmcnt<3>(); break;
+      case 3: wait_vmcnt<4>(); break;
+      case 4: wait_vmcnt<5>(); break;
+      case 5: wait_vmcnt<6>(); break;
+      default: wait_vmcnt<7>(); break;
     }
+    c_cur = scale_from(tn, ks_n1);
+    ks_n1 = ks_n2;
     tc = tn;
     tn = tnn;
     tnn = tnnn;
