@@ -406,7 +406,7 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
                                            const char* sKn, const char* sVp, const char* sVn, const v4i (&qf)[D / 32],
                                            v16f (&o)[D / 32], float c_cur, RowState& rs, const LaneBases& lb, int g,
                                            int lim, const void* mtile, bool mvec4, bool has_m = false,
-                                           float cb_cur = 0.f) {
+                                           float cb_cur = 0.f, const v16i& magic = v16i{}) {
   static_assert(SLOW || !MF, "the float-mask step is a masked step");
   static_assert(!(MF && BM), "per_block_mean is not combined with a float mask");
   using SG = StepGeom<D, PV>;
@@ -414,8 +414,6 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   // FP16 P without a float mask: the QK accumulators start at the bit pattern of 1.5 * 2^23, so each
   // score arrives as the float 1.5 * 2^23 + s and enters the exponent with one FMA
   constexpr bool MG = PV == 0 && !MF;
-  const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
-                      kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   constexpr int NG = 8;                 // exponential groups of 4 scores
   constexpr int FIN = 1;                // slot of the reference-maximum update (pieces 4-7 in slot 0)
   using VFrag = typename SG::VFrag;
@@ -718,6 +716,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     return mrow ? mrow + (int64_t)(t < kt_end ? t : 0) * kBlockN * kMaskBytes : nullptr;
   };
 
+  // FP16 P: the QK accumulators' starting value (see tile_step), held in registers for the whole
+  // loop -- the empty asm keeps the compiler from rebuilding the constant in every step
+  v16i magic;
+  if constexpr (PV == 0 && !MF) {
+    int mb = kMagicBits;
+    asm volatile("" : "+v"(mb));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) magic[r] = mb;
+  }
   RowState rs;
   rs.m = -INFINITY;
   rs.pm = 0.f;
@@ -735,10 +742,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
   float cb_cur = cb_of(t0);
   {  // scores of T[0] and the row maxima of its first key block; the first PV operands
-    constexpr bool MG = PV == 0 && !MF;  // as in tile_step: biased QK accumulators
-    const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
-                        kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits};
-    qk_tile<D, MG>(kring, qf, lb, acc, magic);
+    qk_tile<D, (PV == 0 && !MF)>(kring, qf, lb, acc, magic);
     int lim;
     const void* mtile;
     visible(t0, lim, mtile);
@@ -791,10 +795,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const void* mtile;
       visible(tn, lim, mtile);
       alpha = tile_step<D, PV, true, false, BM>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g, lim, mtile,
-                                                a.mask_vec4, false, cb_cur);
+                                                a.mask_vec4, false, cb_cur, magic);
     } else {
       alpha = tile_step<D, PV, false, false, BM>(acc, ch, P, vpre, sKn, sVp, sVn, qf, o, c_cur, rs, lb, g,
-                                                 kBlockN - 1, nullptr, false, false, cb_cur);
+                                                 kBlockN - 1, nullptr, false, false, cb_cur, magic);
     }
     // O moves to T[n]'s reference maximum after the PV of T[n-1] (rare under the lazy maximum)
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
