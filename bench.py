@@ -63,17 +63,103 @@ def kernel_source_hash(kernel: str = "k_attn_fwd") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, kernel: str = "k_attn_fwd"):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+def _profile(name: str, kernel: str):
+    """A committed profile summary (profiles/<name>.json) if it was taken on the current kernel
+    source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash(kernel):
+    return t if t.get("kernel_source_hash") == kernel_source_hash(kernel) else None
+
+
+def traffic_from_profile(workload: str, kernel: str = "k_attn_fwd"):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    t = _profile(f"{kernel}_{workload}_hbm_traffic", kernel)
+    return None if t is None else t.get("bytes_per_launch")
+
+
+def valu_ceiling(workload: str, ops_per_launch: float, kernel: str = "k_attn_fwd"):
+    """The VALU ceiling of the attention kernel: its own vector-ALU instructions per launch (the
+    committed rocprofv3 counts SQ_INSTS_VALU minus SQ_INSTS_MFMA, split into transcendental
+    (SQ_INSTS_VALU_TRANS_F32), conversion (SQ_INSTS_VALU_CVT) and the rest) times the measured time
+    each takes on one SIMD at full occupancy (profiles/isa_rates_gfx950.json: v_exp_f32,
+    v_cvt_f32_i32, v_fma_f32), spread over every SIMD.  The rate at which these instructions could
+    complete if nothing else limited the kernel, as ops/s; None without a profile of the current
+    kernel source."""
+    c = _profile(f"{kernel}_{workload}_counters", kernel)
+    rates_path = os.path.join(ROOT, "profiles", "isa_rates_gfx950.json")
+    if c is None or not os.path.exists(rates_path):
         return None
-    return t.get("bytes_per_launch")
+    with open(rates_path) as f:
+        r = json.load(f)["ns_per_wave_instr_per_simd_8wps"]
+    per = c["per_dispatch"]
+    trans, cvt = per["SQ_INSTS_VALU_TRANS_F32"], per["SQ_INSTS_VALU_CVT"]
+    other = per["SQ_INSTS_VALU"] - per["SQ_INSTS_MFMA"] - trans - cvt
+    simds = 4 * c["cus"]
+    ns = (trans * r["v_exp_f32"] + cvt * r["v_cvt_f32_i32"] + other * r["v_fma_f32"]) / simds
+    return {"peak": round(ops_per_launch / (ns * 1e-9) / 1e12, 1), "unit": "TOPS", "ms": round(ns * 1e-6, 4),
+            "valu_instr_per_launch": {"transcendental": trans, "conversion": cvt, "other": other},
+            "basis": "the kernel's VALU instructions per launch (rocprofv3 counts) x measured ns per "
+                     "instruction per SIMD at 8 waves/SIMD (bench_isa_rates.hip), over 1024 SIMDs"}
+
+
+def sample_clocks(out_path: str, stop_path: str):
+    """--sample-clocks: write one line of GFX clock readings (amd-smi, MHz) with a timestamp about
+    every 0.2 s until stop_path exists.  Started by the benchmark before it touches the GPU."""
+    import re
+    import subprocess
+
+    parent, t_end = os.getppid(), time.time() + 1800
+    with open(out_path, "w") as out:
+        # until told to stop, or the benchmark process is gone, or half an hour has passed
+        while not os.path.exists(stop_path) and os.getppid() == parent and time.time() < t_end:
+            t = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True, timeout=5)
+                mhz = [int(x) for x in re.findall(r"^\s+CLK:\s+(\d+) MHz", r.stdout, flags=re.M)]
+            except Exception:
+                mhz = []
+            out.write(json.dumps({"t": t, "mhz": mhz}) + "\n")
+            out.flush()
+            time.sleep(0.2)
+
+
+def start_clock_sampler():
+    """Starts the clock sampler in a child process before any GPU use; returns a function that stops
+    it and gives the GFX clock readings (MHz) taken between two wall-clock times."""
+    import subprocess
+    import tempfile
+
+    d = tempfile.mkdtemp(prefix="sage_clk_")
+    out, stop = os.path.join(d, "clk.jsonl"), os.path.join(d, "stop")
+    try:
+        p = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--sample-clocks", out, stop],
+                             stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    except Exception:
+        return lambda t0, t1: None
+
+    def finish(t0, t1):
+        open(stop, "w").close()
+        try:
+            p.wait(timeout=10)
+        except Exception:
+            p.kill()
+        mhz = []
+        if os.path.exists(out):
+            for line in open(out):
+                rec = json.loads(line)
+                if t0 <= rec["t"] <= t1:
+                    mhz += [m for m in rec["mhz"] if m > 0]
+        if not mhz:
+            return None
+        mhz.sort()
+        return {"median_mhz": mhz[len(mhz) // 2], "min_mhz": mhz[0], "max_mhz": mhz[-1], "readings": len(mhz),
+                "source": "amd-smi metric -c (GFX clock of every XCD), sampled during the timed steps"}
+
+    return finish
 
 
 def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
@@ -202,7 +288,7 @@ def fp4_setup(w, dev):
     return step, 1, out.element_size()
 
 
-def run_timed(args, w, step, S, out_esize, dev):
+def run_timed(args, w, step, S, out_esize, dev, clocks=None):
     """Warm-up, then exactly args.steps timed steps; prints the JSON line.  step(ev, mev) records
     HIP events around each of its S attention launches (ev[s]) and around the merge (mev)."""
     import torch
@@ -222,12 +308,14 @@ def run_timed(args, w, step, S, out_esize, dev):
     g0, g1 = pair()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    tw0 = time.time()
     g0.record(stream)
     for i in range(args.steps):
         step(evs[i], mevs[i])
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clocks(tw0, time.time()) if clocks is not None else None
 
     ms_step = wall * 1e3 / args.steps
     gpu_ms_step = g0.elapsed_time(g1) / args.steps
@@ -271,7 +359,13 @@ def run_timed(args, w, step, S, out_esize, dev):
                                     " for PV, each half of the counted ops"),
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
                      "min_ms": round(attn_ms[0], 4)},
+        "sclk": sclk,
     }
+    vc = valu_ceiling(w.name, ops / S, "k_fp4_attn" if w.method == "fp4" else "k_attn_fwd")
+    if vc is not None:
+        vc["achieved"] = line["roofline"]["achieved"]
+        vc["frac"] = round(vc["achieved"] / vc["peak"], 4)
+    line["roofline"]["valu"] = vc
     if S > 1:
         merge_ms = sorted(a.elapsed_time(b) for a, b in mevs)
         merge_avg = sum(merge_ms) / len(merge_ms)
@@ -282,10 +376,10 @@ def run_timed(args, w, step, S, out_esize, dev):
                                   "frac": round(mbytes / (merge_avg * 1e-3) / 1e9 / 8000.0, 4),
                                   "bytes_per_launch": mbytes, "avg_ms": round(merge_avg, 4)}
     if not args.no_cpu_baseline:
-        if w.method == "fp4":
-            line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau_fp4(), False)
-        else:
-            line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, sage.softmax_tau(w.pv), sage.rowsum_rounded(w.pv))
+        # the oracle run with the kernels' online schedule: 64-key tiles, a reference maximum lazy by
+        # 8 log2 units for FP16 P and exact for e4m3 P, the denominator over the fp32 probabilities
+        tau = 0.0 if (w.method == "fp4" or w.pv == "fp8") else 8.0
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_work, tau, False)
     print(json.dumps(line), flush=True)
 
 
@@ -303,7 +397,10 @@ def main():
     ap.add_argument("--cpu-work", type=float, default=2.7e8,
                     help="query-row x key pairs in the CPU-baseline sample (oracle on the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample-clocks", nargs=2, metavar=("OUT", "STOP"), help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.sample_clocks:
+        return sample_clocks(*args.sample_clocks)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -311,6 +408,8 @@ def main():
               f"WORLD_SIZE={world}).  Heads are independent, so N GPUs would each run B*H/N heads of the same "
               f"kernel with no communication.", file=sys.stderr)
         sys.exit(2)
+
+    clocks = start_clock_sampler()  # a child process, started before anything touches the GPU
 
     import torch
 
@@ -320,6 +419,7 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
+        clocks(0.0, 0.0)  # stops the sampler
         print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 5}), flush=True)
         return
 
@@ -332,9 +432,9 @@ def main():
     torch.cuda.set_device(dev)
     sage.load_library()
     if w.seqlens:
-        return run_timed(args, w, *varlen_setup(w, dev), dev)
+        return run_timed(args, w, *varlen_setup(w, dev), dev, clocks)
     if w.method == "fp4":
-        return run_timed(args, w, *fp4_setup(w, dev), dev)
+        return run_timed(args, w, *fp4_setup(w, dev), dev, clocks)
     inp = workload_inputs(w, seed=0)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     mask = None if inp.mask is None else inp.mask.to(dev)
@@ -386,7 +486,7 @@ def main():
             if mev is not None:
                 mev[1].record(stream)
 
-    return run_timed(args, w, step, S, out.element_size(), dev)
+    return run_timed(args, w, step, S, out.element_size(), dev, clocks)
 
 
 if __name__ == "__main__":
