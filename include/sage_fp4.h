@@ -27,6 +27,8 @@
  * synchronization, host validation before anything is enqueued, stream as void*.  head_dim must
  * be 128.  Every buffer below must be 16-byte aligned.  Limits: Nq, Nk <= 2^24 and
  * nqm * Nk_pad * 4 < 2^31 (the correction rows of one head fit a 32-bit buffer range).
+ * The rule for non-finite inputs stated in sage_mi355x.h covers the INT8 method only: here the
+ * inputs must be finite (a NaN or infinity gives unspecified values).
  */
 #ifndef SAGE_FP4_H
 #define SAGE_FP4_H

@@ -29,6 +29,19 @@
  *    strides are free (HND or NHD), given in elements, and must keep every row 16-byte aligned.
  *    An fp16 input is decoded exactly; the method then runs as for bf16.
  *  - head_dim d must be 64 or 128.  Index arithmetic is 64-bit.
+ *  - Non-finite inputs (no page covers them; this library's rule) are never dropped and never
+ *    turn into finite values.  A NaN in a quantization group (a 64-token block of Q or of the
+ *    smoothed K, an FP8 V channel) makes the group's scale NaN, and every code of a group whose
+ *    scale is NaN or +inf is 0; means are plain sums.  A row's O and LSE are NaN when one of its
+ *    visible keys has a NaN score (its Q block's scale, its key block's scale or mean, or K's
+ *    mean is NaN).  A NaN in fp16 V at (key j, channel c) makes O[i,c] NaN for every row i with a
+ *    visible key whose key loop covers j's 64-key tile: the rows that see key j and, because a
+ *    zero probability times NaN is NaN, the other rows of that loop (the loop of a 256-row query
+ *    block: under causal masking the tiles up to the block's last row; tiles that the mask hides
+ *    from the whole block are skipped).  A NaN FP8 V channel scale or smooth_v channel mean
+ *    reaches that channel of every row with a visible key; V never reaches the LSE.  A row
+ *    without a visible key gives O = 0 and LSE = -inf whatever the inputs hold.  Infinities in Q
+ *    or K give NaN scores the same way.
  */
 #ifndef SAGE_MI355X_H
 #define SAGE_MI355X_H
@@ -303,7 +316,8 @@ sage_status sage_attn_fwd_prepared_varlen(const sage_qk_quant* qk, const void* v
  * (what the LSE output is for: "Utilize SageAttention for Distributed Inference" on the
  * SageAttention docs digest -- sequence parallelism, Ring Attention).  With part s covering the
  * keys K_s: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the softmax identity; a
- * part with LSE_s = -inf adds nothing; all -inf gives O = 0, LSE = -inf).  Computed in fp32.
+ * part with LSE_s = -inf adds nothing and its O_s is not read; all -inf gives O = 0, LSE = -inf;
+ * a NaN LSE_s makes the row's O and LSE NaN).  Computed in fp32.
  *   o_parts:   S contiguous [B][H][Nq][d] outputs of part_dtype (fp32 keeps the parts unrounded),
  *              16-byte aligned; e.g. sage_attn_fwd outputs over key slices.
  *   lse_parts: fp32 [S][B][H][Nq], natural log, as sage_attn_fwd writes them.

@@ -51,7 +51,14 @@
  *    rounded once to fp32 and then to fp16, and the mean is added back to the normalized output
  *    of every row that has a visible key (exact, since the probabilities sum to one);
  *  - LSE is natural-log and adds back the smoothing shift sm_scale * (q_i . kmean), so it is the
- *    LSE of the unsmoothed scores.
+ *    LSE of the unsmoothed scores;
+ *  - non-finite inputs poison what depends on them and never vanish: the absolute maximum that
+ *    sets a scale (a Q or K block, an FP8 V channel) is NaN when its group holds a NaN (IEEE
+ *    754-2019 "maximum"), the scale is then NaN, and a code is 0 wherever x * (1/scale) is NaN
+ *    (every code of a NaN or +inf scale).  Means are plain sums.  NaN scores leave the running
+ *    maximum alone and give NaN probabilities; a tile is never skipped because nothing in the row
+ *    was visible so far, and under causal masking a row's key loop ends at the last tile holding
+ *    one of its keys.  A row with no visible key still gives O = 0 and LSE = -inf.
  *
  * Index arithmetic is 64-bit throughout.  Compile without -ffast-math and with -ffp-contract=off.
  */
@@ -220,30 +227,38 @@ void orc_kmean(const uint16_t* K, int in_fp16, int64_t B, int64_t H, int64_t Nk,
 /* Block u covers rows [64u, min(64u+64, N)) and all d channels.                              */
 /* x8 gets N_pad rows (rows >= N are zero); scale gets ceil(N/64) entries.                    */
 /* ------------------------------------------------------------------------------------------ */
+/* Running absolute maximum with IEEE 754-2019 "maximum" semantics: once a NaN is seen the
+ * maximum is NaN. */
+static float absmax_fold(float m, float x) {
+  float a = fabsf(x);
+  if (isnan(m) || isnan(a)) return NAN;
+  return a > m ? a : m;
+}
+
+/* INT8 code of a scaled value y: round to nearest even, clamp to [-127, 127]; NaN gives 0. */
+static int8_t int8_code(float y) {
+  if (isnan(y)) return 0;
+  float q = nearbyintf(y); /* ties to even */
+  if (q > 127.0f) q = 127.0f;
+  if (q < -127.0f) q = -127.0f;
+  return (int8_t)q;
+}
+
 static void quantize_blocks(const float* X, int64_t N, int64_t N_pad, int64_t d, int8_t* x8, float* scale) {
   int64_t nblk = (N + ORC_QBLK - 1) / ORC_QBLK;
   for (int64_t u = 0; u < nblk; ++u) {
     int64_t r0 = u * ORC_QBLK, r1 = r0 + ORC_QBLK < N ? r0 + ORC_QBLK : N;
     float amax = 0.0f;
     for (int64_t r = r0; r < r1; ++r)
-      for (int64_t c = 0; c < d; ++c) {
-        float a = fabsf(X[r * d + c]);
-        if (a > amax) amax = a;
-      }
+      for (int64_t c = 0; c < d; ++c) amax = absmax_fold(amax, X[r * d + c]);
     float sc = 0.0f, inv = 0.0f;
-    if (amax > 0.0f) {
+    if (amax != 0.0f) { /* NaN and +inf included: scale NaN / +inf, inverse NaN / 0 */
       sc = amax / 127.0f; /* IEEE binary32 division */
       inv = 127.0f / amax;
     }
     scale[u] = sc;
     for (int64_t r = r0; r < r1; ++r)
-      for (int64_t c = 0; c < d; ++c) {
-        float y = X[r * d + c] * inv; /* one binary32 rounding */
-        float q = nearbyintf(y);      /* ties to even */
-        if (q > 127.0f) q = 127.0f;
-        if (q < -127.0f) q = -127.0f;
-        x8[r * d + c] = (int8_t)q;
-      }
+      for (int64_t c = 0; c < d; ++c) x8[r * d + c] = int8_code(X[r * d + c] * inv); /* one rounding */
   }
   memset(x8 + N * d, 0, (size_t)((N_pad - N) * d));
 }
@@ -320,7 +335,8 @@ void orc_quant_qk(const uint16_t* Q, const uint16_t* K, int in_fp16, const float
 /* fp16: vhat = fp16_rne(V) (the identity for fp16 V); with smooth_v (vmean != NULL, from      */
 /*       orc_kmean of V) vhat = fp16_rne(fp32(V - vmean)).                                    */
 /* fp8:  vmax_c = max_t |V_tc|; vs_c = fp32(vmax_c / 448); vinv_c = fp32(448 / vmax_c)        */
-/*       (0 when vmax_c = 0); vhat = e4m3_rne_sat(fp32(V * vinv_c)).                          */
+/*       (0 when vmax_c = 0); vhat = e4m3_rne_sat(fp32(V * vinv_c)), 0 where that product is    */
+/*       NaN.  vmax_c is NaN when the channel holds a NaN (as for the INT8 blocks).             */
 /* ------------------------------------------------------------------------------------------ */
 void orc_prep_v_fp16(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_t Nk, int64_t d,
                      const float* vmean, uint16_t* vhat) {
@@ -338,19 +354,17 @@ void orc_prep_v_fp8(const uint16_t* V, int in_fp16, int64_t B, int64_t H, int64_
   for (int64_t bh = 0; bh < B * H; ++bh) {
     for (int64_t c = 0; c < d; ++c) {
       float vmax = 0.0f;
-      for (int64_t t = 0; t < Nk; ++t) {
-        float a = fabsf(orc_in_to_f32(V[(bh * Nk + t) * d + c], in_fp16));
-        if (a > vmax) vmax = a;
-      }
+      for (int64_t t = 0; t < Nk; ++t) vmax = absmax_fold(vmax, orc_in_to_f32(V[(bh * Nk + t) * d + c], in_fp16));
       float sc = 0.0f, inv = 0.0f;
-      if (vmax > 0.0f) {
+      if (vmax != 0.0f) {
         sc = vmax / 448.0f;
         inv = 448.0f / vmax;
       }
       vs[bh * d + c] = sc;
       for (int64_t t = 0; t < Nk; ++t) {
         int64_t idx = (bh * Nk + t) * d + c;
-        vhat[idx] = orc_f32_to_e4m3(orc_in_to_f32(V[idx], in_fp16) * inv);
+        float y = orc_in_to_f32(V[idx], in_fp16) * inv;
+        vhat[idx] = isnan(y) ? 0 : orc_f32_to_e4m3(y);
       }
     }
   }
@@ -419,7 +433,7 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
       float qscale = qs[bh * nbq + i / ORC_QBLK];
       float m = -INFINITY, l = 0.0f;
       for (int64_t c = 0; c < d; ++c) o[c] = 0.0f;
-      for (int64_t j0 = 0; j0 < Nk; j0 += BN) {
+      for (int64_t j0 = 0; j0 < Nk && !(causal && j0 > i); j0 += BN) {
         int64_t j1 = j0 + BN < Nk ? j0 + BN : Nk;
         /* scores of this key tile */
         float tmax = -INFINITY;
@@ -441,9 +455,10 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
           if (madd) s[j - j0] += madd[j]; /* additive mask, natural-log units */
           if (s[j - j0] > tmax) tmax = s[j - j0];
         }
+        /* NaN scores do not take part in the maximum (tmax skips them); with nothing finite seen so
+         * far mnew stays -inf, masked keys get p = 0 and NaN scores p = NaN */
         float mnew = m;
         if (m == -INFINITY || (double)tmax > (double)m + tau * M_LN2) mnew = m > tmax ? m : tmax;
-        if (mnew == -INFINITY) continue; /* nothing valid so far */
         float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)(m - mnew));
         float psum = 0.0f;
         for (int64_t j = j0; j < j1; ++j) {
@@ -499,7 +514,8 @@ void orc_attn_qe(const int8_t* q8, const int8_t* k8, const float* qs, const floa
 /* Exact attention in fp64 on the original bf16 or fp16 inputs: no smoothing, no quantization. */
 /* s_ij = sm_scale * sum_c Q_ic K_jc (+ M_ij for an fp32 mask); invalid entries -inf;         */
 /* two-pass softmax; O = P V;                                                                 */
-/* LSE_i = log sum_j exp(s_ij).  A row with no valid key gives O = 0, LSE = -inf.             */
+/* LSE_i = log sum_j exp(s_ij).  A row with no valid key gives O = 0, LSE = -inf; a row with  */
+/* a NaN score (a visible key) gives O = NaN and LSE = NaN.                                   */
 /* ------------------------------------------------------------------------------------------ */
 void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in_fp16, const void* mask, int mask_f32,
                  int64_t mask_h, int causal, double sm_scale, int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
@@ -519,6 +535,7 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in
       const float* madd = (mask && mask_f32) ? (const float*)mask + moff : NULL;
       for (int64_t c = 0; c < d; ++c) q[c] = (double)orc_in_to_f32(Q[(bh * Nq + i) * d + c], in_fp16);
       double mx = -INFINITY;
+      int has_nan = 0;
       for (int64_t j = 0; j < Nk; ++j) {
         if ((causal && j > i) || (mrow && mrow[j] == 0) || (madd && madd[j] == -INFINITY)) {
           s[j] = -INFINITY;
@@ -528,12 +545,13 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in
         for (int64_t c = 0; c < d; ++c) acc += q[c] * (double)orc_in_to_f32(K[(bhk * Nk + j) * d + c], in_fp16);
         s[j] = sm_scale * acc;
         if (madd) s[j] += (double)madd[j];
+        if (isnan(s[j])) has_nan = 1;
         if (s[j] > mx) mx = s[j];
       }
       double* o = out + r * d;
-      for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
-      if (mx == -INFINITY) {
-        if (lse) lse[r] = -INFINITY;
+      for (int64_t c = 0; c < d; ++c) o[c] = has_nan ? NAN : 0.0;
+      if (has_nan || mx == -INFINITY) {
+        if (lse) lse[r] = has_nan ? NAN : -INFINITY;
         continue;
       }
       double den = 0.0;
@@ -557,8 +575,8 @@ void orc_attn_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int in
 /* Ring Attention).  Written from the softmax's definition: if part s covers keys K_s with    */
 /* O_s = sum_{j in K_s} e^{s_j} v_j / sum_{j in K_s} e^{s_j} and LSE_s = log sum_{j in K_s}    */
 /* e^{s_j}, then over the union LSE = log sum_s e^{LSE_s} and O = sum_s e^{LSE_s - LSE} O_s.  */
-/* A part with LSE_s = -inf (no visible key) contributes nothing; if every part has -inf,     */
-/* O = 0 and LSE = -inf.                                                                      */
+/* A part with LSE_s = -inf (no visible key) contributes nothing (its O_s is not read); if    */
+/* every part has -inf, O = 0 and LSE = -inf.  A NaN LSE_s makes the row's O and LSE NaN.     */
 /* o_parts [S][R][d] (fp32), lse_parts [S][R]; out [R][d] and lse [R] in fp64.                */
 /* ------------------------------------------------------------------------------------------ */
 void orc_merge_lse(const float* o_parts, const float* lse_parts, int64_t S, int64_t R, int64_t d, double* out,
@@ -566,17 +584,21 @@ void orc_merge_lse(const float* o_parts, const float* lse_parts, int64_t S, int6
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < R; ++r) {
     double m = -INFINITY;
-    for (int64_t s = 0; s < S; ++s)
+    int has_nan = 0;
+    for (int64_t s = 0; s < S; ++s) {
+      if (isnan(lse_parts[s * R + r])) has_nan = 1;
       if ((double)lse_parts[s * R + r] > m) m = (double)lse_parts[s * R + r];
-    for (int64_t c = 0; c < d; ++c) out[r * d + c] = 0.0;
-    if (m == -INFINITY) {
-      lse[r] = -INFINITY;
+    }
+    for (int64_t c = 0; c < d; ++c) out[r * d + c] = has_nan ? NAN : 0.0;
+    if (has_nan || m == -INFINITY) {
+      lse[r] = has_nan ? NAN : -INFINITY;
       continue;
     }
     double tot = 0.0;
     for (int64_t s = 0; s < S; ++s) tot += exp((double)lse_parts[s * R + r] - m);
     double L = m + log(tot);
     for (int64_t s = 0; s < S; ++s) {
+      if (lse_parts[s * R + r] == -INFINITY) continue; /* a part without visible keys */
       double w = exp((double)lse_parts[s * R + r] - L);
       for (int64_t c = 0; c < d; ++c) out[r * d + c] += w * (double)o_parts[(s * R + r) * d + c];
     }

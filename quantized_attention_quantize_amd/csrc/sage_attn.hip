@@ -281,6 +281,9 @@ __device__ __forceinline__ void mask_scores(v16i (&acc)[2], int g, int lim, cons
 // has_m (the same for the whole wave); full4: the tile's 64 keys all exist and the row is 16-byte
 // aligned, so it is read 16 bytes at a time; otherwise one element at a time at indices clamped
 // to the visible range (j <= max(lim, 0) < Nk - j0: always inside the row).  No per-lane branches.
+// GUARD (a NaN or infinite scale c, where acc * c - inf is NaN): entries whose M is -inf are set
+// to -inf explicitly, so a masked key stays out of the row even then.
+template <bool GUARD>
 __device__ __forceinline__ void mask_scores_f32(v16i (&acc)[2], int g, int lim, const float* mtile, bool has_m,
                                                 bool full4, float c) {
   const int jmax = lim > 0 ? lim : 0;
@@ -305,7 +308,8 @@ __device__ __forceinline__ void mask_scores_f32(v16i (&acc)[2], int g, int lim, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float t = __builtin_fmaf((float)acc[kb][rq * 4 + e], c, mv[e] * kLog2e);
-        acc[kb][rq * 4 + e] = __float_as_int(j4 + e <= lim ? t : -INFINITY);
+        const bool vis = j4 + e <= lim && (!GUARD || mv[e] != -INFINITY);
+        acc[kb][rq * 4 + e] = __float_as_int(vis ? t : -INFINITY);
       }
     }
 }
@@ -436,7 +440,12 @@ __device__ __forceinline__ float tile_step(v16i (&acc)[2], int (&ch)[4], PFrag<P
   if constexpr (MF) {
     // T[n]'s scores to log2-unit fp32 with its mask (lim / mtile / has_m / mvec4 describe T[n]),
     // and all eight row-maximum pieces, before the MFMA stream
-    mask_scores_f32(sc, g, lim, static_cast<const float*>(mtile), has_m, mvec4, c_cur);
+    const float* mt4 = static_cast<const float*>(mtile);
+    const int cbits = __builtin_amdgcn_readfirstlane(__float_as_int(c_cur));  // the same in every lane
+    if ((cbits & 0x7f800000) != 0x7f800000)
+      mask_scores_f32<false>(sc, g, lim, mt4, has_m, mvec4, c_cur);
+    else
+      mask_scores_f32<true>(sc, g, lim, mt4, has_m, mvec4, c_cur);
 #pragma unroll
     for (int p = 0; p < 8; ++p) max_piece<true>(sc, ch, p);
   }
@@ -840,8 +849,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
   if (row < nq) {
     const float* vsh = PV == 1 ? ea.vscale + bhk * D : nullptr;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float* vmh = (ea.vmean && l_tot > 0.f) ? ea.vmean + bhk * D : nullptr;  // smooth_v
+    // A row without a visible key (l = 0) stores O = 0 and LSE = -inf, whatever a zero
+    // probability times a NaN in V left in o; a NaN l (a NaN score) makes both NaN.
+    const bool live = l_tot != 0.f;
+    const float inv = live ? 1.f / l_tot : 0.f;
+    const float* vmh = (ea.vmean && live) ? ea.vmean + bhk * D : nullptr;  // smooth_v
     const int64_t obase = b * ea.o_sb + h * ea.o_sh + (sq.off + row) * ea.o_sn;  // elements
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -856,6 +868,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
           else
             f[e] = o[db][rq * 4 + e] * inv;
           if (vmh) f[e] = f[e] + vmh[d0 + e];
+          f[e] = live ? f[e] : 0.f;
         }
         if (ea.out_kind == 2) {  // fp32, e.g. partial results that are merged later
           *reinterpret_cast<float4*>(static_cast<float*>(ea.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
@@ -873,7 +886,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       }
     if (g == 0 && ea.lse) {
       float v = -INFINITY;
-      if (l_tot > 0.f) {
+      if (l_tot != 0.f) {
         // l_tot sums 2^(s - pm) over the row (e4m3 P carries its scale 448 * 2^-tau inside pm)
         v = (rs.pm + log2f(l_tot)) * kLn2 + ea.sm_scale * ea.corr[bh * ea.Nq + row];
       }

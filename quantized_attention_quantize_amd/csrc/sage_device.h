@@ -53,6 +53,13 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   return static_cast<unsigned short>(u >> 16);
 }
 
+// Maximum of two magnitudes (values with a clear sign bit, NaN included) that keeps NaN: the
+// unsigned order of such bit patterns is finite < +inf < NaN, so a block holding a NaN gets a NaN
+// maximum and hence a NaN scale (fmaxf would drop it).
+__device__ __forceinline__ float mag_max(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+}
+
 // Sequence b of a batch: the row of its first token and its length.  Dense batches (cu null)
 // have n rows per batch entry, addressed through the batch stride.  A packed variable-length batch
 // holds sequence b in rows [cu[b], cu[b+1]) of a buffer of `total` rows; offsets and lengths are

@@ -42,13 +42,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_lse(MergeArgs a) {
   const int64_t r = t / cgs;
   if (r >= a.R) return;
   const int cg = (int)(t % cgs);
+  // the largest LSE, NaN if any part's is NaN (that NaN then reaches O and the LSE)
   float m = -INFINITY;
-  for (int64_t s = 0; s < a.S; ++s) m = fmaxf(m, a.lse_parts[s * a.R + r]);
+  for (int64_t s = 0; s < a.S; ++s) {
+    const float x = a.lse_parts[s * a.R + r];
+    m = (x != x || x > m) ? x : m;
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
     for (int64_t s = 0; s < a.S; ++s) {
-      const float w = __builtin_amdgcn_exp2f((a.lse_parts[s * a.R + r] - m) * kLog2e);  // 0 for a -inf part
+      const float ls = a.lse_parts[s * a.R + r];
+      if (ls == -INFINITY) continue;  // a part without visible keys: its O is not read
+      const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
       tot += w;
       float x[8];
       load8<PART>(a.parts, (s * a.R + r) * a.d + cg * 8, x);
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_lse(MergeArgs a) {
       for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(w, x[j], acc[j]);
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float inv = tot != 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] *= inv;
   const int64_t bh = r / a.Nq, i = r % a.Nq, b = bh / a.H, h = bh % a.H;

@@ -12,6 +12,11 @@
 //                     as all-masked, all-visible (fp32: all exactly 0) or mixed, so the attention
 //                     kernel skips a tile or reads no mask for it
 //
+// Non-finite inputs: every maximum that sets a scale keeps NaN (mag_max), so a Q or K block or an
+// FP8 V channel holding a NaN gets a NaN scale, and a NaN or +inf scale gives every code of its
+// group the value 0; the means are plain sums.  The NaN then reaches the outputs through the
+// scales and means instead of turning into finite codes.
+//
 // Method sources (page title, section): SageAttention docs digest (context7 llms.txt) --
 // "sageattn_qk_int8_pv_fp16_triton" (per-block INT8 Q/K, smooth_k), "sageattn3_blackwell" usage
 // (smoothing by the global token mean), "sageattn_qk_int8_pv_fp8_cuda" (per-channel FP8 V).
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
       if constexpr (MODE == 0)
         sum[j] += (double)f;
       else
-        mx[j] = fmaxf(mx[j], fabsf(f));
+        mx[j] = mag_max(mx[j], fabsf(f));
     }
   // combine the RPI row-slices in a fixed order
   if constexpr (MODE == 0) {
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
     __syncthreads();
     if (t < D) {
       float m = 0.f;
-      for (int r = 0; r < RPI; ++r) m = fmaxf(m, red[r][t]);
+      for (int r = 0; r < RPI; ++r) m = mag_max(m, red[r][t]);
       static_cast<float*>(partial)[(bh * nchunk + blockIdx.x) * D + t] = m;
     }
   }
@@ -115,14 +120,14 @@ __global__ __launch_bounds__(D) void k_kmean_final(const double* __restrict__ pa
   kmean[bh * D + c] = N > 0 ? (float)(s / (double)N) : 0.f;
 }
 
-// block-wide max of a non-negative float (256 threads)
+// block-wide maximum of a magnitude, NaN kept (256 threads)
 __device__ __forceinline__ float block_max256(float v, float* red) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 32; o >= 1; o >>= 1) v = mag_max(v, __shfl_xor(v, o));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = mag_max(mag_max(red[0], red[1]), mag_max(red[2], red[3]));
   return r;
 }
 
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
         float f = in_to_f32<IN>(v[j]);
         if (!isq && !pbm) f = f - km_s[cg * 8 + j];  // one fp32 rounding
         x[i][j] = f;
-        amax = fmaxf(amax, fabsf(f));
+        amax = mag_max(amax, fabsf(f));
       }
     } else {
 #pragma unroll
@@ -222,13 +227,13 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float f = valid ? x[i][j] - km_s[cg * 8 + j] : 0.f;  // one fp32 rounding
         x[i][j] = f;
-        amax = fmaxf(amax, fabsf(f));
+        amax = mag_max(amax, fabsf(f));
       }
     }
   }
   amax = block_max256(amax, red);
   float scale = 0.f, inv = 0.f;
-  if (amax > 0.f) {
+  if (amax != 0.f) {  // a NaN or +inf block too: scale NaN / +inf, inverse NaN / 0
     scale = amax / 127.0f;  // IEEE-correct binary32 division
     inv = 127.0f / amax;
   }
@@ -238,8 +243,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
     unsigned lo = 0, hi = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float q = __builtin_rintf(x[i][j] * inv);  // round to nearest even
-      q = fminf(fmaxf(q, -127.f), 127.f);
+      const float y = x[i][j] * inv;
+      float q = __builtin_rintf(y);  // round to nearest even
+      q = y != y ? 0.f : fminf(fmaxf(q, -127.f), 127.f);  // NaN (a NaN or +inf block) codes 0
       unsigned byte = (unsigned)((int)q) & 0xffu;
       if (j < 4)
         lo |= byte << (8 * j);
@@ -446,9 +452,9 @@ __global__ __launch_bounds__(D) void k_vmax_final(float* __restrict__ partial, i
 #pragma unroll
     for (int k = 0; k < 8; ++k) p[k] = partial[(bh * nchunk + i + k) * D + c];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, p[k]);
+    for (int k = 0; k < 8; ++k) m = mag_max(m, p[k]);
   }
-  for (; i < nchunk; ++i) m = fmaxf(m, partial[(bh * nchunk + i) * D + c]);
+  for (; i < nchunk; ++i) m = mag_max(m, partial[(bh * nchunk + i) * D + c]);
   partial[(bh * nchunk) * D + c] = m;
 }
 
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
   if (t < D) {
     const float m = a.vmax_partial[(bh * a.nchunk) * D + t];  // max over chunks (k_vmax_final)
     float sc = 0.f, inv = 0.f;
-    if (m > 0.f) {
+    if (m != 0.f) {  // NaN and +inf included, as for the INT8 blocks
       sc = m / 448.0f;
       inv = 448.0f / m;
     }
@@ -492,7 +498,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
     const float inv = inv_s[c];
     auto x = [&](int key) {
       float f = in_to_f32<IN>(tile[key][c]) * inv;
-      return fabsf(f) > 448.f ? copysignf(448.f, f) : f;  // saturate (NaN passes through)
+      f = f != f ? 0.f : f;                               // a NaN or +inf channel codes 0
+      return fabsf(f) > 448.f ? copysignf(448.f, f) : f;  // saturate
     };
     v4i o;
 #pragma unroll
