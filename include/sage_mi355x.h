@@ -61,17 +61,37 @@ typedef enum {
   SAGE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } sage_status;
 
+/* The input enums below span every 32-bit int (the *_MIN_ / *_MAX_ enumerators are not values to
+ * pass): whatever int a caller stores in one is a value of the type, and the entry points reject
+ * an unknown one with SAGE_ERR_INVALID_ARGUMENT. */
+
 /* Element type of Q, K, V (bf16 or fp16) and of the output O (any of the three; fp32 for partial
  * results that sage_merge_lse combines later). */
-typedef enum { SAGE_BF16 = 0, SAGE_FP16 = 1, SAGE_F32 = 2 } sage_dtype;
+typedef enum {
+  SAGE_BF16 = 0,
+  SAGE_FP16 = 1,
+  SAGE_F32 = 2,
+  SAGE_DTYPE_MIN_ = -0x7fffffff - 1,
+  SAGE_DTYPE_MAX_ = 0x7fffffff
+} sage_dtype;
 
 /* Attention mask element type (optional boolean or float32 mask: Triton INT8/FP16 kernel section).
  *   SAGE_MASK_BOOL: uint8, nonzero = attend, 0 = masked out.
  *   SAGE_MASK_F32:  fp32 added to the scaled score sm_scale * q.k (natural-log units) before the
  *                   softmax; -inf masks the key.  Entries must be finite or -inf. */
-typedef enum { SAGE_MASK_BOOL = 0, SAGE_MASK_F32 = 1 } sage_mask_dtype;
+typedef enum {
+  SAGE_MASK_BOOL = 0,
+  SAGE_MASK_F32 = 1,
+  SAGE_MASK_DTYPE_MIN_ = -0x7fffffff - 1,
+  SAGE_MASK_DTYPE_MAX_ = 0x7fffffff
+} sage_mask_dtype;
 
-typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_dtype;
+typedef enum {
+  SAGE_PV_FP16 = 0,
+  SAGE_PV_FP8_E4M3 = 1,
+  SAGE_PV_DTYPE_MIN_ = -0x7fffffff - 1,
+  SAGE_PV_DTYPE_MAX_ = 0x7fffffff
+} sage_pv_dtype;
 
 /* A Q, K or V tensor of shape [B, H, N, d] addressed as
  *   data + b*stride_b + h*stride_h + n*stride_n + c      (element offsets, c contiguous). */

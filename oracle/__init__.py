@@ -56,11 +56,24 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(out: str) -> str:
+    """The same sources built with AddressSanitizer and UndefinedBehaviorSanitizer (any finding
+    aborts), without OpenMP, into ``out``.  A process loads it through SAGE_ORACLE_LIB with gcc's
+    libasan preloaded."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-Wall",
+           "-Wno-unknown-pragmas", "-o", out, _SRC, _SRC_FP4, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("SAGE_ORACLE_LIB")
+        if not path:
+            path = build(force=False)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int64
         i32 = ctypes.c_int

@@ -59,6 +59,7 @@ def test_host_queries(L):
     with_mask = L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 1)
     assert with_mask - L.sage_fwd_workspace_bytes(2, 32, 8192, 8192, 128, 0, 0) >= 2 * 32 * 128
     assert L.sage_fwd_workspace_bytes(1, 1, 1, 1, 64, 7, 0) == 0
+    assert L.sage_fwd_workspace_bytes(1, 1, 1, 1, 64, -1, 0) == 0
     for s, txt in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace missing or too small")]:
         assert L.sage_status_string(s) == txt
 
@@ -92,7 +93,8 @@ def call_quant(L, q, k, out, ws=FAKE, wsb=1 << 20):
 
 @pytest.mark.parametrize("case,status", [
     ("null_q", INVALID), ("null_data", INVALID), ("zero_B", INVALID), ("neg_N", INVALID), ("d96", UNSUPPORTED),
-    ("qk_dtype_mismatch", INVALID), ("bad_dtype", INVALID), ("misaligned", INVALID), ("odd_stride", INVALID),
+    ("qk_dtype_mismatch", INVALID), ("bad_dtype", INVALID), ("neg_dtype", INVALID), ("max_dtype", INVALID),
+    ("misaligned", INVALID), ("odd_stride", INVALID),
     ("small_stride_n", INVALID), ("qk_mismatch_H", INVALID), ("out_null_ptr", INVALID), ("out_bad_pad", INVALID),
     ("out_wrong_N", INVALID), ("no_workspace", WORKSPACE), ("small_workspace", WORKSPACE),
     ("gqa_out_hkv", INVALID), ("gqa_not_divisor", INVALID),
@@ -114,6 +116,10 @@ def test_quantize_validation(L, case, status):
         q = desc(dtype=1)
     elif case == "bad_dtype":
         q = desc(dtype=9)
+    elif case == "neg_dtype":  # any int is a value of the C enum; unknown ones are rejected
+        q, k = desc(dtype=-1), desc(dtype=-1)
+    elif case == "max_dtype":
+        q, k = desc(dtype=0x7FFFFFFF), desc(dtype=0x7FFFFFFF)
     elif case == "misaligned":
         q = desc(data=FAKE + 2)
     elif case == "odd_stride":
