@@ -29,20 +29,21 @@ namespace sage {
 
 constexpr int kChunk = 256;  // tokens per column-reduction chunk
 constexpr int kPrepThreads = 256;
+constexpr int kColredThreads = 512;
 
 // ---------------------------------------------------------------------------------------------
 // Column reductions over token chunks.  MODE 0: fp64 sums of x; MODE 1: fp32 maxima of |x|.
 // x is bf16 (IN = 0) or fp16 (IN = 1).
-// grid = (nchunk, B*H), block = 256.  Thread t covers channels [8*(t % (D/8)), +8) of the rows
-// t / (D/8) + i * (256 / (D/8)) of the chunk.
+// grid = (nchunk, B*H), block = 512.  Thread t covers channels [8*(t % (D/8)), +8) of the rows
+// t / (D/8) + i * (512 / (D/8)) of the chunk; all of its loads are issued before the first is used.
 // ---------------------------------------------------------------------------------------------
 template <int D, int MODE, int IN>
-__global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned short* __restrict__ x, int64_t H,
+__global__ __launch_bounds__(kColredThreads) void k_colred_partial(const unsigned short* __restrict__ x, int64_t H,
                                                                  int64_t Nmax, int64_t sb, int64_t sh, int64_t sn,
                                                                  void* __restrict__ partial, int nchunk,
                                                                  const int* __restrict__ cu, int64_t total) {
   constexpr int CG = D / 8;               // threads per row
-  constexpr int RPI = kPrepThreads / CG;  // rows per iteration
+  constexpr int RPI = kColredThreads / CG;  // rows per iteration
   const int t = threadIdx.x, cg = t % CG, rs = t / CG;
   const int64_t bh = blockIdx.y, b = bh / H, h = bh % H;
   const SeqSpan sp = seq_span(cu, b, Nmax, total);
@@ -59,17 +60,19 @@ __global__ __launch_bounds__(kPrepThreads) void k_colred_partial(const unsigned 
   // all of the chunk's loads are issued before the first is used (zero rows past N add nothing)
   constexpr int TPT = kChunk / RPI;
   u16x8 v[TPT];
+  const int64_t nlast = N > 0 ? N - 1 : 0;  // rows past N read row N - 1 and count as zero; no loads if N = 0
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int64_t tok = t0 + rs + i * RPI;
     v[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (tok < N) v[i] = *reinterpret_cast<const u16x8*>(base + tok * sn);
+    if (N > 0) v[i] = *reinterpret_cast<const u16x8*>(base + (tok < N ? tok : nlast) * sn);
   }
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float f = in_to_f32<IN>(v[i][j]);
+      const int64_t tok = t0 + rs + i * RPI;
+      const float f = tok < N ? in_to_f32<IN>(v[i][j]) : 0.f;
       if constexpr (MODE == 0)
         sum[j] += (double)f;
       else
@@ -183,21 +186,25 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
   const bool pbm = !isq && a.kbmean != nullptr;  // uniform
   float x[RPB][8];
   float amax = 0.f;
+  u16x8 raw[RPB];
+#pragma unroll
+  for (int i = 0; i < RPB; ++i) {  // every load in flight first; rows past N read row N - 1 (N > r0)
+    const int64_t tok = r0 + rs + i * RPI;
+    raw[i] = *reinterpret_cast<const u16x8*>(src + (tok < N ? tok : N - 1) * sn);
+  }
+  float kmr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kmr[j] = km_s[cg * 8 + j];
 #pragma unroll
   for (int i = 0; i < RPB; ++i) {
-    int64_t tok = r0 + rs + i * RPI;
-    if (tok < N) {
-      u16x8 v = *reinterpret_cast<const u16x8*>(src + tok * sn);
+    const bool valid = r0 + rs + i * RPI < N;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float f = in_to_f32<IN>(v[j]);
-        if (!isq && !pbm) f = f - km_s[cg * 8 + j];  // one fp32 rounding
-        x[i][j] = f;
-        amax = mag_max(amax, fabsf(f));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[i][j] = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      float f = in_to_f32<IN>(raw[i][j]);
+      if (!isq && !pbm) f = f - kmr[j];  // one fp32 rounding
+      f = valid ? f : 0.f;
+      x[i][j] = f;
+      amax = mag_max(amax, fabsf(f));
     }
   }
   if (pbm) {  // the block's own column means, then the smoothed values and their amax
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_quant_qk(QuantArgs a) {
     for (int i = 0; i < RPB; ++i) {
       double s = 0.0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += (double)x[i][j] * (double)km_s[cg * 8 + j];
+      for (int j = 0; j < 8; ++j) s += (double)x[i][j] * (double)kmr[j];
 #pragma unroll
       for (int o = 1; o < CG; o <<= 1) s += __shfl_xor(s, o);
       int64_t tok = r0 + rs + i * RPI;
@@ -386,8 +393,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_block_corr(QuantArgs a, int ng
 }
 
 // ---------------------------------------------------------------------------------------------
-// V preparation.  grid = (Nk_pad/64, B*H), block = 256.  A 64-token x D tile is converted and
-// written transposed: row c of v_t holds the tile's 64 keys of channel c, in the MFMA key order.
+// V preparation.  Each 64-token x D tile is converted and written transposed: row c of v_t holds
+// the tile's 64 keys of channel c, in the MFMA key order.
 // ---------------------------------------------------------------------------------------------
 // position p (0..15) inside a 16-key group holds key ((p & 7) >> 2) * 8 + (p >> 3) * 4 + (p & 3)
 __device__ __forceinline__ int fp16_pos_to_key(int p) { return ((p & 7) >> 2) * 8 + (p >> 3) * 4 + (p & 3); }
@@ -398,44 +405,55 @@ __device__ __forceinline__ int fp8_pos_to_key(int p) {
   return kb * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
 }
 
+// Each thread converts 8 keys x 8 channels with no LDS: it loads the 8 keys that fill positions
+// [8 pg, 8 pg + 8) of the tile (keys 16 (pg / 2) + pos_to_key(8 (pg % 2) + e), e = 0..7), 16 bytes
+// of each key's row, and writes, per channel, the 16 bytes of those positions.  Two neighbouring
+// positions of one channel come out of one v_cvt_pk_f16_f32, which also transposes.  A workgroup
+// covers 256 / (8 * D/8) tiles of 64 keys; grid = (ceil(Nk_pad / 64 / tiles per workgroup), B*H).
 template <int D, int IN>
 __global__ __launch_bounds__(kPrepThreads) void k_prep_v16(PrepVArgs a) {
   constexpr int CG = D / 8;
-  constexpr int RPI = kPrepThreads / CG;
-  __shared__ _Float16 tile[64][D + 8];  // +8 halves of padding against bank conflicts
-  __shared__ float vm[D];
-  const int t = threadIdx.x, cg = t % CG, rs = t / CG;
+  constexpr int TT = 8 * CG;                // threads per 64-key tile
+  constexpr int TPW = kPrepThreads / TT;    // tiles per workgroup
+  // lanes next to each other take neighbouring position groups of one channel group, so a store
+  // instruction writes 128 contiguous bytes of each of 8 channel rows
+  const int t = threadIdx.x, tt = t % TT, pg = tt % 8, cg = tt / 8;
+  const int64_t kt = (int64_t)blockIdx.x * TPW + t / TT;
+  if (kt * 64 >= a.Nk_pad) return;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const int64_t k0 = kt * 64;
   const SeqSpan sp = seq_span(a.cu_k, b, a.Nk, a.total_k);
-  if (t < D) vm[t] = a.vmean ? a.vmean[bh * D + t] : 0.f;  // smooth_v: the channel means
-  __syncthreads();
   const unsigned short* src = a.v + b * a.v_sb + h * a.v_sh + sp.off * a.v_sn + cg * 8;
-  for (int r = rs; r < 64; r += RPI) {
-    int64_t tok = k0 + r;
-    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (tok < sp.len) v = *reinterpret_cast<const u16x8*>(src + tok * a.v_sn);
+  const int64_t nlast = sp.len > 0 ? sp.len - 1 : 0;
+  u16x8 raw[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float x = in_to_f32<IN>(v[j]);
-      if (a.vmean) x = x - vm[cg * 8 + j];  // one fp32 rounding
-      tile[r][cg * 8 + j] = tok < sp.len ? (_Float16)x : (_Float16)0.f;  // RNE (exact for fp16 V); pad keys 0
-    }
+  for (int e = 0; e < 8; ++e) {  // every load in flight first; keys past the sequence read its last key
+    const int64_t tok = k0 + 16 * (pg >> 1) + fp16_pos_to_key(8 * (pg & 1) + e);
+    raw[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (sp.len > 0) raw[e] = *reinterpret_cast<const u16x8*>(src + (tok < sp.len ? tok : nlast) * a.v_sn);
   }
-  __syncthreads();
-  // D rows x 8 chunks of 8 halves; chunk q holds positions [8q, 8q+8)
-  unsigned short* dst = static_cast<unsigned short*>(a.vt) + (bh * D) * a.Nk_pad + k0;
-  for (int i = t; i < D * 8; i += kPrepThreads) {
-    int c = i / 8, q = i % 8;
-    u16x8 o;
+  float vm[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int p = q * 8 + j;
-      int key = (p & ~15) + fp16_pos_to_key(p & 15);
-      _Float16 hv = tile[key][c];
-      o[j] = *reinterpret_cast<unsigned short*>(&hv);
+  for (int j = 0; j < 8; ++j) vm[j] = a.vmean ? a.vmean[bh * D + cg * 8 + j] : 0.f;  // smooth_v
+  unsigned short* dst = static_cast<unsigned short*>(a.vt) + (bh * D + cg * 8) * a.Nk_pad + k0 + 8 * pg;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v4i o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float x2[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * m + q;
+        const int64_t tok = k0 + 16 * (pg >> 1) + fp16_pos_to_key(8 * (pg & 1) + e);
+        float x = in_to_f32<IN>(raw[e][j]);
+        if (a.vmean) x = x - vm[j];  // one fp32 rounding
+        x2[q] = tok < sp.len ? x : 0.f;  // pad keys 0
+      }
+      // round to nearest even (exact for fp16 V)
+      o[m] = __builtin_bit_cast(int, __builtin_convertvector((v2f{x2[0], x2[1]}), v2h));
     }
-    *reinterpret_cast<u16x8*>(dst + (int64_t)c * a.Nk_pad + q * 8) = o;
+    *reinterpret_cast<v4i*>(dst + (int64_t)j * a.Nk_pad) = o;
   }
 }
 
@@ -588,7 +606,7 @@ static void launch_kmean_t(const QuantArgs& a, double* partial, int nchunk, hipS
     return;
   }
   dim3 g(nchunk, (unsigned)(a.B * a.Hkv));
-  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk,
+  k_colred_partial<D, 0, IN><<<g, kColredThreads, 0, s>>>(a.k, a.Hkv, a.Nk, a.k_sb, a.k_sh, a.k_sn, partial, nchunk,
                                                         a.cu_k, a.total_k);
   k_kmean_final<D><<<(unsigned)(a.B * a.Hkv), D, 0, s>>>(partial, nchunk, a.Hkv, a.Nk, a.cu_k, a.total_k, a.kmean);
 }
@@ -612,7 +630,7 @@ static void launch_token_mean_t(const unsigned short* x, int64_t B, int64_t H, i
                                 int64_t sn, double* partial, float* mean, hipStream_t s) {
   const int nchunk = (int)((N + kChunk - 1) / kChunk);
   dim3 g(nchunk, (unsigned)(B * H));
-  k_colred_partial<D, 0, IN><<<g, kPrepThreads, 0, s>>>(x, H, N, sb, sh, sn, partial, nchunk, nullptr, 0);
+  k_colred_partial<D, 0, IN><<<g, kColredThreads, 0, s>>>(x, H, N, sb, sh, sn, partial, nchunk, nullptr, 0);
   k_kmean_final<D><<<(unsigned)(B * H), D, 0, s>>>(partial, nchunk, H, N, nullptr, 0, mean);
 }
 
@@ -664,22 +682,24 @@ hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
 
 template <int D, int IN>
 static void launch_prep_v_t(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
-  dim3 g((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.H));
   if (!pv_fp8) {
+    constexpr int tpw = kPrepThreads / D;  // 64-key tiles per workgroup of k_prep_v16
+    const dim3 g16((unsigned)((a.Nk_pad / 64 + tpw - 1) / tpw), (unsigned)(a.B * a.H));
     if (a.vmean) {  // smooth_v: V's channel means first, exactly as K's
       dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
-      k_colred_partial<D, 0, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vsum_partial,
+      k_colred_partial<D, 0, IN><<<gr, kColredThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vsum_partial,
                                                             a.nchunk, a.cu_k, a.total_k);
       k_kmean_final<D><<<(unsigned)(a.B * a.H), D, 0, s>>>(a.vsum_partial, a.nchunk, a.H, a.Nk, a.cu_k, a.total_k,
                                                           a.vmean);
     }
-    k_prep_v16<D, IN><<<g, kPrepThreads, 0, s>>>(a);
+    k_prep_v16<D, IN><<<g16, kPrepThreads, 0, s>>>(a);
   } else {
     dim3 gr(a.nchunk, (unsigned)(a.B * a.H));
-    k_colred_partial<D, 1, IN><<<gr, kPrepThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
+    k_colred_partial<D, 1, IN><<<gr, kColredThreads, 0, s>>>(a.v, a.H, a.Nk, a.v_sb, a.v_sh, a.v_sn, a.vmax_partial,
                                                           a.nchunk, a.cu_k, a.total_k);
     k_vmax_final<D><<<(unsigned)(a.B * a.H), D, 0, s>>>(a.vmax_partial, a.nchunk);
-    k_prep_v8<D, IN><<<g, kPrepThreads, 0, s>>>(a);
+    const dim3 g8((unsigned)(a.Nk_pad / 64), (unsigned)(a.B * a.H));
+    k_prep_v8<D, IN><<<g8, kPrepThreads, 0, s>>>(a);
   }
 }
 
