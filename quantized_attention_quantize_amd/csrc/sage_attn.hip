@@ -595,8 +595,12 @@ __device__ __forceinline__ const T* kernarg_reload() {
   return p;
 }
 
-template <int D, int PV, int MF, int BM>
+// TT: the launch has a mask-tile table (a boolean or float mask; MF implies TT).  Without one the
+// tile walk is plain arithmetic: no tile is dropped and only the causal diagonal and ragged tail
+// take the per-element step.
+template <int D, int PV, int MF, int BM, int TT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
+  static_assert(TT || !MF, "a float mask comes with its tile table");
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
   __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     const int lim = (q0 + kBlockM + kBlockN - 1) / kBlockN;
     if (lim < kt_end) kt_end = lim;
   }
-  const int* mt = a.mtiles ? a.mtiles + ((b * a.Hm + (a.Hm == 1 ? 0 : h)) * a.nQT + qt) * a.nKT : nullptr;
+  const int* mt = TT ? a.mtiles + ((b * a.Hm + (a.Hm == 1 ? 0 : h)) * a.nQT + qt) * a.nKT : nullptr;
   constexpr int kMaskBytes = MF ? 4 : 1;  // bytes per mask element
   // the float-mask step reads rows past Nq at row Nq - 1 (never stored), so a tile's mask pointer
   // is null or not for the whole wave
@@ -656,8 +660,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
 
   Stager<D, PV, kWaves> st;
   st.init(k8h, vth, a.Nk_pad, w, lane);
-  auto dropped = [&](int t) { return mt != nullptr && scalar_ld(mt, t) == 0; };
+  auto dropped = [&](int t) { return TT && scalar_ld(mt, t) == 0; };
   auto next_tile = [&](int t) {
+    if constexpr (!TT) return t + 1 < kt_end ? t + 1 : kt_end;
     if (t >= kt_end) return kt_end;
     ++t;
     while (t < kt_end && dropped(t)) ++t;
@@ -701,7 +706,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     // The test runs on a vector-register copy of the tile index (v_mbcnt_lo with an empty mask
     // adds 0): the compiler then keeps the masked/unmasked step choice as a per-lane branch, which
     // it compiles without spills, and holds no row index in a vector register across the loop.
-    return (int)__builtin_amdgcn_mbcnt_lo(0u, t) >= first_part || (mt != nullptr && scalar_ld(mt, t) == 2);
+    return (int)__builtin_amdgcn_mbcnt_lo(0u, t) >= first_part || (TT && scalar_ld(mt, t) == 2);
   };
   auto visible = [&](int t, int& lim, const void*& mtile) {
     if (t >= kt_end) {
@@ -715,12 +720,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const int dr = row - j0;
       lim = dr < lim ? (dr < -1 ? -1 : dr) : lim;
     }
-    mtile = (mt != nullptr && scalar_ld(mt, t) == 2 && mrow) ? mrow + (int64_t)j0 * kMaskBytes : nullptr;
+    mtile = (TT && scalar_ld(mt, t) == 2 && mrow) ? mrow + (int64_t)j0 * kMaskBytes : nullptr;
   };
   // float-mask step: whether tile t reads its mask (uniform), and whether it may read it 16 bytes
   // at a time; the mask pointer is then formed for every lane
   auto fmask_of = [&](int t, bool& has_m, bool& full4) -> const void* {
-    has_m = t < kt_end && mt != nullptr && scalar_ld(mt, t) == 2;
+    has_m = t < kt_end && TT && scalar_ld(mt, t) == 2;
     full4 = a.mask_vec4 && (t + 1) * kBlockN <= nk;
     return mrow ? mrow + (int64_t)(t < kt_end ? t : 0) * kBlockN * kMaskBytes : nullptr;
   };
@@ -928,22 +933,36 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
 
 // Every variant instantiated explicitly: the launches below alone do not make hipcc's host pass
 // emit the launch stubs of the MF = 0 kernels.
-template __global__ void k_attn_fwd<128, 0, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 0, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 0, 0, 1>(AttnArgs);
-template __global__ void k_attn_fwd<128, 1, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 1, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<128, 1, 0, 1>(AttnArgs);
-template __global__ void k_attn_fwd<64, 0, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 0, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 0, 0, 1>(AttnArgs);
-template __global__ void k_attn_fwd<64, 1, 0, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 1, 1, 0>(AttnArgs);
-template __global__ void k_attn_fwd<64, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 0, 0, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 1, 0>(AttnArgs);
+template __global__ void k_attn_fwd<64, 1, 0, 1, 1>(AttnArgs);
 
+// a mask always comes with its tile table (the host classifies the tiles first)
 template <int D, int PV, int MF, int BM>
 static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
-  k_attn_fwd<D, PV, MF, BM><<<grid, kAttnThreads, 0, s>>>(a);
+  if constexpr (MF)
+    k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (a.mtiles)
+    k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
+  else
+    k_attn_fwd<D, PV, MF, BM, 0><<<grid, kAttnThreads, 0, s>>>(a);
 }
 
 // the float-mask and per_block_mean variants are not combined (the host rejects both at once)
