@@ -106,25 +106,60 @@ def valu_ceiling(workload: str, ops_per_launch: float, kernel: str = "k_attn_fwd
                      "instruction per SIMD at 8 waves/SIMD (bench_isa_rates.hip), over 1024 SIMDs"}
 
 
-def sample_clocks(out_path: str, stop_path: str):
-    """--sample-clocks: write one line of GFX clock readings (amd-smi, MHz) with a timestamp about
-    every 0.2 s until stop_path exists.  Started by the benchmark before it touches the GPU."""
+def _read_sclk(paths):
+    """Current shader clock(s) in MHz from the sysfs DPM tables (the line marked '*')."""
+    import re
+
+    mhz = []
+    for p in paths:
+        try:
+            for ln in open(p):
+                if ln.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", ln, flags=re.I)
+                    if m:
+                        mhz.append(int(m.group(1)))
+        except OSError:
+            pass
+    return mhz
+
+
+def _amdsmi_gfx_clocks():
+    """Current GFX clock of every XCD (MHz) from amd-smi: the CLK lines of the GFX_n sections only."""
     import re
     import subprocess
 
+    r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True, timeout=5)
+    mhz, in_gfx = [], False
+    for ln in r.stdout.splitlines():
+        sec = re.match(r"^\s+([A-Z]+)_\d+:\s*$", ln)
+        if sec:
+            in_gfx = sec.group(1) == "GFX"
+            continue
+        m = re.match(r"^\s+CLK:\s+(\d+) MHz", ln)
+        if m and in_gfx:
+            mhz.append(int(m.group(1)))
+    return mhz
+
+
+def sample_clocks(out_path: str, stop_path: str):
+    """--sample-clocks: write the shader clock (MHz) with a timestamp every 5 ms (sysfs pp_dpm_sclk;
+    amd-smi's GFX clocks every 0.1 s where sysfs has none) until stop_path exists.  Started by the
+    benchmark before it touches the GPU."""
+    import glob
+
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
     parent, t_end = os.getppid(), time.time() + 1800
     with open(out_path, "w") as out:
         # until told to stop, or the benchmark process is gone, or half an hour has passed
         while not os.path.exists(stop_path) and os.getppid() == parent and time.time() < t_end:
             t = time.time()
             try:
-                r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True, timeout=5)
-                mhz = [int(x) for x in re.findall(r"^\s+CLK:\s+(\d+) MHz", r.stdout, flags=re.M)]
+                mhz = _read_sclk(paths) if paths else _amdsmi_gfx_clocks()
             except Exception:
                 mhz = []
             out.write(json.dumps({"t": t, "mhz": mhz}) + "\n")
             out.flush()
-            time.sleep(0.2)
+            time.sleep(0.005 if paths else 0.1)
 
 
 def start_clock_sampler():
@@ -157,9 +192,55 @@ def start_clock_sampler():
             return None
         mhz.sort()
         return {"median_mhz": mhz[len(mhz) // 2], "min_mhz": mhz[0], "max_mhz": mhz[-1], "readings": len(mhz),
-                "source": "amd-smi metric -c (GFX clock of every XCD), sampled during the timed steps"}
+                "source": "current shader clock (sysfs pp_dpm_sclk, else amd-smi GFX clocks), sampled every "
+                          "5 ms during the timed steps"}
 
     return finish
+
+
+def accuracy_rows(q, k, v, out, causal: bool, mask, heads: int = 2, rows_per_head: int = 128, seed: int = 7):
+    """Output accuracy on sampled rows against plain PyTorch fp32 attention on the same bf16/fp16
+    inputs (exact softmax, no quantization), computed on the GPU after the timed steps.  q, out:
+    [B, H, Nq, d]; k, v: [B, Hkv, Nk, d]; mask: None or broadcastable [B, 1|H, Nq, Nk] (bool: True
+    attends; float: added)."""
+    import torch
+
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    g = torch.Generator().manual_seed(seed)
+    sm = 1.0 / (d ** 0.5)
+    num = den = dot = nq = no = 0.0
+    worst = 0.0
+    n = 0
+    for hh in torch.randperm(B * H, generator=g)[:heads].tolist():
+        b, h = divmod(hh, H)
+        hk = h // (H // Hkv)
+        rows = torch.randperm(Nq, generator=g)[:rows_per_head].sort().values.to(q.device)
+        qr = q[b, h].index_select(0, rows).float()
+        kt = k[b, hk].float().t().contiguous()
+        s = (qr @ kt) * sm
+        if causal:
+            s = s.masked_fill(torch.arange(Nk, device=q.device)[None, :] > rows[:, None], float("-inf"))
+        if mask is not None:
+            m = mask[b, 0 if mask.shape[1] == 1 else h]
+            m = m.expand(Nq, Nk) if m.shape[0] == 1 else m
+            m = m.index_select(0, rows)
+            s = s.masked_fill(~m, float("-inf")) if m.dtype == torch.bool else s + m.float()
+        p = torch.softmax(s, dim=-1).nan_to_num(0.0)
+        ref = p @ v[b, hk].float()
+        got = out[b, h].index_select(0, rows).float()
+        err = (got - ref).abs().sum(-1)
+        mag = ref.abs().sum(-1)
+        num += float(err.sum())
+        den += float(mag.sum())
+        worst = max(worst, float((err / mag.clamp_min(1e-30)).max()))
+        dot += float((got * ref).sum())
+        nq += float((got * got).sum())
+        no += float((ref * ref).sum())
+        n += int(rows.numel())
+    return {"rows": n, "rel_l1_vs_fp32": round(num / max(den, 1e-300), 6), "worst_row_rel_l1": round(worst, 6),
+            "cosine": round(dot / max((nq * no) ** 0.5, 1e-300), 6),
+            "reference": "plain PyTorch fp32 softmax attention on the same inputs, sampled rows of the last step"}
 
 
 def cpu_baseline(w, work_target: float, tau: float, lsum_rounded: bool):
@@ -256,7 +337,12 @@ def varlen_setup(w, dev):
         if ev is not None:
             ev[0][1].record(stream)
 
-    return step, 1, out.element_size()
+    def accuracy():  # the first sequence of the packed batch
+        n0 = w.seqlens[0]
+        hnd = lambda x: x[:n0].permute(1, 0, 2).unsqueeze(0)  # noqa: E731
+        return accuracy_rows(hnd(q), hnd(k), hnd(v), hnd(out), w.causal, None)
+
+    return step, 1, out.element_size(), accuracy
 
 
 def fp4_setup(w, dev):
@@ -285,17 +371,22 @@ def fp4_setup(w, dev):
         if ev is not None:
             ev[0][1].record(stream)
 
-    return step, 1, out.element_size()
+    return step, 1, out.element_size(), lambda: accuracy_rows(q, k, v, out, w.causal, None)
 
 
-def run_timed(args, w, step, S, out_esize, dev, clocks=None):
+def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
     """Warm-up, then exactly args.steps timed steps; prints the JSON line.  step(ev, mev) records
-    HIP events around each of its S attention launches (ev[s]) and around the merge (mev)."""
+    HIP events around each of its S attention launches (ev[s]) and around the merge (mev).
+    accuracy(): output accuracy of the last step on sampled rows.  With --scrub-mib N a buffer of N
+    MiB is overwritten before every step (outside that step's events), so each step starts with the
+    L2 and the 256 MB MALL holding none of its inputs; the time per step then comes from HIP events
+    around each step alone."""
     import torch
 
     import quantized_attention_quantize_amd as sage
 
     stream = torch.cuda.current_stream(dev)
+    scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev) if args.scrub_mib > 0 else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -305,13 +396,19 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None):
 
     evs = [[pair() for _ in range(S)] for _ in range(args.steps)]
     mevs = [pair() for _ in range(args.steps)] if S > 1 else [None] * args.steps
+    sevs = [pair() for _ in range(args.steps)] if scrub is not None else None
     g0, g1 = pair()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tw0 = time.time()
     g0.record(stream)
     for i in range(args.steps):
+        if scrub is not None:
+            scrub.fill_(i & 255)
+            sevs[i][0].record(stream)
         step(evs[i], mevs[i])
+        if scrub is not None:
+            sevs[i][1].record(stream)
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -319,6 +416,8 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None):
 
     ms_step = wall * 1e3 / args.steps
     gpu_ms_step = g0.elapsed_time(g1) / args.steps
+    if scrub is not None:  # the steps alone, each after the scrub
+        ms_step = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
     attn_ms = sorted(a.elapsed_time(b) for e in evs for a, b in e)  # one entry per attention launch
     attn_avg = sum(attn_ms) / len(attn_ms)
     ops = w.ops
@@ -360,7 +459,13 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None):
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
                      "min_ms": round(attn_ms[0], 4)},
         "sclk": sclk,
+        "accuracy": accuracy() if accuracy is not None else None,
     }
+    if scrub is not None:
+        line["config"]["cache_scrub_mib"] = args.scrub_mib
+        line["config"]["timing"] = "HIP events around each step, a cache scrub before each"
+        line["data"] = "synthetic, caches scrubbed before every step"
+
     vc = valu_ceiling(w.name, ops / S, "k_fp4_attn" if w.method == "fp4" else "k_attn_fwd")
     if vc is not None:
         vc["achieved"] = line["roofline"]["achieved"]
@@ -397,6 +502,9 @@ def main():
     ap.add_argument("--cpu-work", type=float, default=2.7e8,
                     help="query-row x key pairs in the CPU-baseline sample (oracle on the host)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scrub-mib", type=int, default=0,
+                    help="overwrite a buffer of this many MiB before every timed step (cold L2 and MALL); the "
+                         "time per step is then taken from HIP events around each step")
     ap.add_argument("--sample-clocks", nargs=2, metavar=("OUT", "STOP"), help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.sample_clocks:
@@ -431,10 +539,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sage.load_library()
-    if w.seqlens:
-        return run_timed(args, w, *varlen_setup(w, dev), dev, clocks)
-    if w.method == "fp4":
-        return run_timed(args, w, *fp4_setup(w, dev), dev, clocks)
+    if w.seqlens or w.method == "fp4":
+        step, S, esize, acc = (varlen_setup if w.seqlens else fp4_setup)(w, dev)
+        return run_timed(args, w, step, S, esize, dev, clocks, acc)
     inp = workload_inputs(w, seed=0)
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     mask = None if inp.mask is None else inp.mask.to(dev)
@@ -486,7 +593,11 @@ def main():
             if mev is not None:
                 mev[1].record(stream)
 
-    return run_timed(args, w, step, S, out.element_size(), dev, clocks)
+    def accuracy():
+        return accuracy_rows(q, kv[0][0] if S == 1 else torch.cat([a for a, _ in kv], 2),
+                             kv[0][1] if S == 1 else torch.cat([b for _, b in kv], 2), out, w.causal, mask)
+
+    return run_timed(args, w, step, S, out.element_size(), dev, clocks, accuracy)
 
 
 if __name__ == "__main__":
