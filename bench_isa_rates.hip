@@ -5,7 +5,8 @@
 // waves per SIMD (the pipe's throughput) and at 1 wave per SIMD (one wave's issue rate).  The clock
 // is measured in the same run: s_memtime (shader clock) against s_memrealtime (100 MHz) across a
 // probe kernel.  bench.py turns these rates and the attention kernel's instruction counts into the
-// VALU ceiling reported beside the MFMA ceiling.
+// VALU ceiling reported beside the MFMA ceiling.  Each probe's own clock is reported too: under the
+// MFMA probes the chip clocks down, so clocks per instruction = ns x that probe's MHz.
 //
 //   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //         -o bench_isa_rates bench_isa_rates.hip && ./bench_isa_rates
@@ -130,6 +131,7 @@ int main() {
   CHECK(hipEventCreate(&e1));
   printf("{\"device\": \"%s\", \"cus\": %d", prop.gcnArchName, ncu);
   double sclk_mhz = 0.0;
+  double kind_mhz[2][NKIND] = {};
   for (int wps : {8, 1}) {  // waves per SIMD: two 1024-thread workgroups per CU, or one 256-thread one
     const int threads = wps == 8 ? 1024 : 256, blocks = wps == 8 ? 2 * ncu : ncu;
     printf(", \"ns_per_wave_instr_per_simd_%dwps\": {", wps);
@@ -146,12 +148,16 @@ int main() {
       const double waves_per_simd = (double)blocks * threads / 64 / nsimd;
       const double instr = waves_per_simd * (double)(k >= MFMA_I8 ? kIter / 4 : kIter) * 16;
       printf("%s\"%s\": %.4f", k ? ", " : "", kName[k], ms / reps * 1e6 / instr);
-      if (wps == 8 && k == FMA) {
-        unsigned long long c[2];
-        CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
-        sclk_mhz = c[1] ? 100.0 * (double)c[0] / (double)c[1] : 0.0;
-      }
+      unsigned long long c[2];  // the shader clock across the last launch of this probe
+      CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+      kind_mhz[wps == 8 ? 0 : 1][k] = c[1] ? 100.0 * (double)c[0] / (double)c[1] : 0.0;
+      if (wps == 8 && k == FMA) sclk_mhz = kind_mhz[0][k];
     }
+    printf("}");
+  }
+  for (int i = 0; i < 2; ++i) {
+    printf(", \"sclk_mhz_per_probe_%dwps\": {", i == 0 ? 8 : 1);
+    for (int k = 0; k < NKIND; ++k) printf("%s\"%s\": %.0f", k ? ", " : "", kName[k], kind_mhz[i][k]);
     printf("}");
   }
   printf(", \"sclk_mhz_during_fma_probe\": %.0f}\n", sclk_mhz);

@@ -73,7 +73,7 @@ EXPORTS = ("sage_pad_tokens", "sage_block_n", "sage_softmax_tau", "sage_rowsum_r
            "sage_debug_qk_int32", "sage_status_string", "sage_fp4_q_blocks", "sage_fp4_softmax_tau",
            "sage_fp4_workspace_bytes",
            "sage_fp4_quantize_qkv", "sage_fp4_attn_fwd", "sage_fp4_debug_scores", "sage_qk_quant_bytes",
-           "sage_qk_quant_init", "sage_quantize_qk_noalloc")
+           "sage_qk_quant_init", "sage_quantize_qk_noalloc", "sage_sclk_probe")
 
 
 def lib_path() -> str:
@@ -141,6 +141,8 @@ def load_library():
     L.sage_quantize_qk_noalloc.restype = I
     L.sage_status_string.argtypes = [I]
     L.sage_status_string.restype = ctypes.c_char_p
+    L.sage_sclk_probe.argtypes = [I64, I64, P, P]
+    L.sage_sclk_probe.restype = I
     L.sage_fp4_q_blocks.argtypes = [I64, I]
     L.sage_fp4_q_blocks.restype = I64
     L.sage_fp4_softmax_tau.argtypes = []
@@ -460,6 +462,23 @@ def attn_fwd_prepared(qk: QuantizedQK, v_t: torch.Tensor, v_scale: torch.Tensor 
 
 def default_sm_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def sclk_probe(device=None, nblocks: int = 1024, iters: int = 20000) -> dict:
+    """The shader clock under an MFMA + VALU load (sage_sclk_probe): median, min and max MHz over
+    the probe's workgroups, and how long the probe ran."""
+    L = load_library()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    out = torch.zeros(4 * nblocks, dtype=torch.int64, device=dev)
+    _check(L.sage_sclk_probe(nblocks, iters, out.data_ptr(), _stream(out)), "sage_sclk_probe")
+    c = out.view(nblocks, 4).cpu().numpy().astype("float64")
+    dt, dr = c[:, 2] - c[:, 0], c[:, 3] - c[:, 1]
+    ok = dr > 0
+    mhz = sorted((100.0 * dt[ok] / dr[ok]).tolist())
+    if not mhz:
+        raise RuntimeError("sage_sclk_probe: no workgroup reported a duration")
+    return {"median_mhz": round(mhz[len(mhz) // 2], 1), "min_mhz": round(mhz[0], 1), "max_mhz": round(mhz[-1], 1),
+            "probe_ms": round(float(dr[ok].max()) / 1e5, 3), "workgroups": len(mhz)}
 
 
 def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out: torch.Tensor | None = None,

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsage_mi355x.so")
-SOURCES = ["sage_api.cpp", "sage_prep.hip", "sage_attn.hip", "sage_merge.hip", "sage_fp4.hip"]
+SOURCES = ["sage_api.cpp", "sage_prep.hip", "sage_attn.hip", "sage_merge.hip", "sage_fp4.hip", "sage_clock.hip"]
 ARCH = "gfx950"
 
 

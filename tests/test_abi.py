@@ -427,3 +427,14 @@ def test_noalloc_quantize_validation(L):
     big_q, big_k, big_out = desc(H=64, N=40000, d=128), desc(H=64, N=40000, d=128), quant(H=64, Nq=40000, Nk=40000,
                                                                                            d=128)
     assert call(big_q, big_k, big_out) == WORKSPACE
+
+
+def test_sclk_probe_validation(L):
+    """The clock probe rejects bad sizes and a misaligned or null buffer before anything runs."""
+    f = L.sage_sclk_probe
+    assert f(0, 10, FAKE, None) == INVALID
+    assert f(65537, 10, FAKE, None) == INVALID
+    assert f(8, 0, FAKE, None) == INVALID
+    assert f(8, (1 << 24) + 1, FAKE, None) == INVALID
+    assert f(8, 10, None, None) == INVALID
+    assert f(8, 10, FAKE + 4, None) == INVALID
