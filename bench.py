@@ -385,11 +385,23 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
 
     import quantized_attention_quantize_amd as sage
 
+    from quantized_attention_quantize_amd import api as _api
+
     stream = torch.cuda.current_stream(dev)
     scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev) if args.scrub_mib > 0 else None
+    warm_ms = None  # the fastest warm-up step, for sizing the clock probe below
     for _ in range(args.warmup):
+        tw = time.perf_counter()
         step()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - tw) * 1e3
+        warm_ms = dt if warm_ms is None else min(warm_ms, dt)
+    warm_ms = warm_ms or 1.0
+    # the shader clock during the timed steps: idle waves on a second stream read the clock counters
+    # over about half of the expected timed window (s_sleep trips of 8128 clocks, <= 3.4 us each)
+    side = torch.cuda.Stream(device=dev)
+    clk_buf = torch.zeros(4 * 8, dtype=torch.int64, device=dev)
+    clk_iters = max(1, min(int(0.5 * warm_ms * args.steps / 3.4e-3), 1 << 24))
 
     def pair():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,6 +414,10 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
     t0 = time.perf_counter()
     tw0 = time.time()
     g0.record(stream)
+    try:
+        _api.sclk_probe(dev, nblocks=8, iters=clk_iters, load=False, stream=side, out=clk_buf)
+    except Exception:
+        clk_buf = None
     for i in range(args.steps):
         if scrub is not None:
             scrub.fill_(i & 255)
@@ -413,11 +429,10 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sclk = clocks(tw0, time.time()) if clocks is not None else None
-    try:  # the shader clock measured on the GPU right after the timed steps
-        from quantized_attention_quantize_amd import api as _api
-        probe = _api.sclk_probe(dev)
-        probe["source"] = ("sage_sclk_probe right after the timed steps: s_memtime against the 100 MHz "
-                           "s_memrealtime across 1024 workgroups of FP16 MFMA + VALU work")
+    try:
+        probe = _api.sclk_result(clk_buf) if clk_buf is not None else {"error": "probe not launched"}
+        probe["source"] = ("sage_sclk_probe (idle form) on a second stream during the timed steps: s_memtime "
+                           "against the 100 MHz s_memrealtime over about half of the timed window")
     except Exception as e:  # the measurement aid must not stop the benchmark
         probe = {"error": str(e)}
 

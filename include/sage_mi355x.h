@@ -358,13 +358,16 @@ sage_status sage_merge_lse(int64_t S, int64_t B, int64_t H, int64_t Nq, int64_t 
 sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, int64_t row0, int64_t nrows,
                                 int64_t col0, int64_t ncols, int32_t* out, void* stream);
 
-/* Measurement aid: the shader clock under load.  Launches nblocks workgroups that keep their
- * SIMDs busy with FP16 MFMAs and VALU work for iters loop trips; the first wave of workgroup i
- * writes out[4i .. 4i+3] = shader clock counter (s_memtime) and 100 MHz counter (s_memrealtime)
- * at its start, then both at its end.  The clock in MHz is 100 * (out[4i+2] - out[4i]) /
- * (out[4i+3] - out[4i+1]).  out: device buffer of 4 * nblocks uint64 (8-byte aligned).
- * 1 <= nblocks <= 65536, 1 <= iters <= 2^24.  Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
-sage_status sage_sclk_probe(int64_t nblocks, int64_t iters, unsigned long long* out, void* stream);
+/* Measurement aid: the shader clock.  Launches nblocks workgroups; load = 1: each keeps its SIMDs
+ * busy with FP16 MFMAs and VALU work for iters loop trips (the clock under such a load); load = 0:
+ * one wave each sleeps iters times (s_sleep 127, about 8k clocks) and adds no load, so that,
+ * launched on a second stream beside other kernels, it measures the clock they run at.  The first
+ * wave of workgroup i writes out[4i .. 4i+3] = shader clock counter (s_memtime) and 100 MHz
+ * counter (s_memrealtime) at its start, then both at its end; the clock in MHz is
+ * 100 * (out[4i+2] - out[4i]) / (out[4i+3] - out[4i+1]).  out: device buffer of 4 * nblocks
+ * uint64 (8-byte aligned).  1 <= nblocks <= 65536, 1 <= iters <= 2^24, load 0 or 1.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+sage_status sage_sclk_probe(int64_t nblocks, int64_t iters, int load, unsigned long long* out, void* stream);
 
 /* Static description of a status code. Host only. */
 const char* sage_status_string(sage_status s);

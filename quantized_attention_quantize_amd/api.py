@@ -141,7 +141,7 @@ def load_library():
     L.sage_quantize_qk_noalloc.restype = I
     L.sage_status_string.argtypes = [I]
     L.sage_status_string.restype = ctypes.c_char_p
-    L.sage_sclk_probe.argtypes = [I64, I64, P, P]
+    L.sage_sclk_probe.argtypes = [I64, I64, I, P, P]
     L.sage_sclk_probe.restype = I
     L.sage_fp4_q_blocks.argtypes = [I64, I]
     L.sage_fp4_q_blocks.restype = I64
@@ -464,14 +464,24 @@ def default_sm_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def sclk_probe(device=None, nblocks: int = 1024, iters: int = 20000) -> dict:
-    """The shader clock under an MFMA + VALU load (sage_sclk_probe): median, min and max MHz over
-    the probe's workgroups, and how long the probe ran."""
+def sclk_probe(device=None, nblocks: int = 1024, iters: int = 20000, load: bool = True, stream=None,
+               out: torch.Tensor | None = None):
+    """The shader clock (sage_sclk_probe).  load=True: under the probe's own MFMA + VALU load, run
+    now and read back: returns median, min and max MHz over its workgroups and how long it ran.
+    load=False: the idle form is only enqueued on `stream` (a torch.cuda.Stream) into `out`
+    (int64 [4 * nblocks]); read it later with sclk_result(out)."""
     L = load_library()
     dev = torch.device("cuda") if device is None else torch.device(device)
-    out = torch.zeros(4 * nblocks, dtype=torch.int64, device=dev)
-    _check(L.sage_sclk_probe(nblocks, iters, out.data_ptr(), _stream(out)), "sage_sclk_probe")
-    c = out.view(nblocks, 4).cpu().numpy().astype("float64")
+    if out is None:
+        out = torch.zeros(4 * nblocks, dtype=torch.int64, device=dev)
+    st = _stream(out) if stream is None else stream.cuda_stream
+    _check(L.sage_sclk_probe(nblocks, iters, 1 if load else 0, out.data_ptr(), st), "sage_sclk_probe")
+    return sclk_result(out) if load else out
+
+
+def sclk_result(out: torch.Tensor) -> dict:
+    """MHz per workgroup from sage_sclk_probe's counters: median, min, max, and the window length."""
+    c = out.view(-1, 4).cpu().numpy().astype("float64")
     dt, dr = c[:, 2] - c[:, 0], c[:, 3] - c[:, 1]
     ok = dr > 0
     mhz = sorted((100.0 * dt[ok] / dr[ok]).tolist())

@@ -703,12 +703,12 @@ sage_status sage_debug_qk_int32(const sage_qk_quant* qk, int64_t b, int64_t h, i
   return hip_status(launch_debug_qk(a, (int)qk->d, qk->Nq_pad, static_cast<hipStream_t>(stream)));
 }
 
-sage_status sage_sclk_probe(int64_t nblocks, int64_t iters, unsigned long long* out, void* stream) {
+sage_status sage_sclk_probe(int64_t nblocks, int64_t iters, int load, unsigned long long* out, void* stream) {
   if (nblocks < 1 || nblocks > 65536 || iters < 1 || iters > ((int64_t)1 << 24)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!out || ((uintptr_t)out & 7u)) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((load != 0 && load != 1) || !out || ((uintptr_t)out & 7u)) return SAGE_ERR_INVALID_ARGUMENT;
   sage_status s;
   if ((s = check_device()) != SAGE_OK) return s;
-  return hip_status(launch_sclk_probe(out, (int)nblocks, (int)iters, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_sclk_probe(out, (int)nblocks, (int)iters, load, static_cast<hipStream_t>(stream)));
 }
 
 const char* sage_status_string(sage_status s) {

@@ -176,7 +176,7 @@ hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int d, int pv_fp8, hipStream_t s);
 hipError_t launch_debug_qk(const DebugQKArgs& a, int d, int64_t Nq_pad, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_sclk_probe(unsigned long long* out, int nblocks, int iters, hipStream_t s);
+hipError_t launch_sclk_probe(unsigned long long* out, int nblocks, int iters, int load, hipStream_t s);
 int64_t token_mean_partial_doubles(int64_t B, int64_t H, int64_t N, int64_t d);
 hipError_t launch_token_mean(const unsigned short* x, int in_fp16, int d, int64_t B, int64_t H, int64_t N, int64_t sb,
                              int64_t sh, int64_t sn, double* partial, float* mean, hipStream_t s);

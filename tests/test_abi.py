@@ -432,9 +432,10 @@ def test_noalloc_quantize_validation(L):
 def test_sclk_probe_validation(L):
     """The clock probe rejects bad sizes and a misaligned or null buffer before anything runs."""
     f = L.sage_sclk_probe
-    assert f(0, 10, FAKE, None) == INVALID
-    assert f(65537, 10, FAKE, None) == INVALID
-    assert f(8, 0, FAKE, None) == INVALID
-    assert f(8, (1 << 24) + 1, FAKE, None) == INVALID
-    assert f(8, 10, None, None) == INVALID
-    assert f(8, 10, FAKE + 4, None) == INVALID
+    assert f(0, 10, 1, FAKE, None) == INVALID
+    assert f(65537, 10, 1, FAKE, None) == INVALID
+    assert f(8, 0, 0, FAKE, None) == INVALID
+    assert f(8, (1 << 24) + 1, 1, FAKE, None) == INVALID
+    assert f(8, 10, 2, FAKE, None) == INVALID
+    assert f(8, 10, 1, None, None) == INVALID
+    assert f(8, 10, 0, FAKE + 4, None) == INVALID

@@ -21,3 +21,18 @@ def test_sclk_probe_reports_a_plausible_clock():
     assert r["workgroups"] == 256
     assert 300.0 <= r["min_mhz"] <= r["median_mhz"] <= r["max_mhz"] <= 3000.0
     assert r["probe_ms"] > 0
+
+
+def test_idle_sclk_probe_beside_a_kernel():
+    """The idle form on a second stream, beside a busy matrix product on the default stream, reports
+    a clock in range and covers its sleep window."""
+    sage.load_library()
+    side = torch.cuda.Stream()
+    a = torch.randn(4096, 4096, device="cuda")
+    out = api.sclk_probe("cuda", nblocks=8, iters=200, load=False, stream=side)
+    for _ in range(20):
+        a = (a @ a).clamp_(-1, 1)
+    torch.cuda.synchronize()
+    r = api.sclk_result(out)
+    say(f"idle sclk probe: {r}")
+    assert r["workgroups"] == 8 and 300.0 <= r["min_mhz"] <= r["max_mhz"] <= 3000.0 and r["probe_ms"] > 0.1
