@@ -660,16 +660,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
 
   Stager<D, PV, kWaves> st;
   st.init(k8h, vth, a.Nk_pad, w, lane);
-  auto dropped = [&](int t) { return TT && scalar_ld(mt, t) == 0; };
+  // mask-tile table entry: state in bits 0-1 (0 all masked, 1 all visible, 2 mixed), above them the
+  // next tile of this row block that is not all masked
+  auto tstate = [&](int t) { return TT ? scalar_ld(mt, t) & 3 : 1; };
+  auto dropped = [&](int t) { return tstate(t) == 0; };
   auto next_tile = [&](int t) {
     if constexpr (!TT) return t + 1 < kt_end ? t + 1 : kt_end;
     if (t >= kt_end) return kt_end;
-    ++t;
-    while (t < kt_end && dropped(t)) ++t;
-    return t;
+    const int nx = scalar_ld(mt, t) >> 2;
+    return nx < kt_end ? nx : kt_end;
   };
   int t0 = 0;
-  while (t0 < kt_end && dropped(t0)) ++t0;
+  if (TT && kt_end > 0 && dropped(0)) t0 = next_tile(0);
   const int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
   const int tstand = t0 < kt_end ? t0 : 0;  // a valid tile to stand in for loads past the end
   auto clampt = [&](int t) { return t < kt_end ? t : tstand; };
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     // The test runs on a vector-register copy of the tile index (v_mbcnt_lo with an empty mask
     // adds 0): the compiler then keeps the masked/unmasked step choice as a per-lane branch, which
     // it compiles without spills, and holds no row index in a vector register across the loop.
-    return (int)__builtin_amdgcn_mbcnt_lo(0u, t) >= first_part || (TT && scalar_ld(mt, t) == 2);
+    return (int)__builtin_amdgcn_mbcnt_lo(0u, t) >= first_part || (TT && tstate(t) == 2);
   };
   auto visible = [&](int t, int& lim, const void*& mtile) {
     if (t >= kt_end) {
@@ -720,12 +722,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const int dr = row - j0;
       lim = dr < lim ? (dr < -1 ? -1 : dr) : lim;
     }
-    mtile = (TT && scalar_ld(mt, t) == 2 && mrow) ? mrow + (int64_t)j0 * kMaskBytes : nullptr;
+    mtile = (TT && tstate(t) == 2 && mrow) ? mrow + (int64_t)j0 * kMaskBytes : nullptr;
   };
   // float-mask step: whether tile t reads its mask (uniform), and whether it may read it 16 bytes
   // at a time; the mask pointer is then formed for every lane
   auto fmask_of = [&](int t, bool& has_m, bool& full4) -> const void* {
-    has_m = t < kt_end && TT && scalar_ld(mt, t) == 2;
+    has_m = t < kt_end && TT && tstate(t) == 2;
     full4 = a.mask_vec4 && (t + 1) * kBlockN <= nk;
     return mrow ? mrow + (int64_t)(t < kt_end ? t : 0) * kBlockN * kMaskBytes : nullptr;
   };

@@ -61,7 +61,8 @@ struct MaskTileArgs {
   int64_t B, Hm, Nq, Nk;
   int nQT, nKT;
   int vec16;  // rows and base are 16-byte aligned: read 16 bytes at a time
-  int* state;  // [B*Hm][nQT][nKT]: 0 all masked, 1 all visible (fp32: all exactly 0), 2 mixed
+  int* state;  // [B*Hm][nQT][nKT]: bits 0-1: 0 all masked, 1 all visible (fp32: all exactly 0), 2 mixed;
+               // bits 2+: the row block's next tile that is not all masked (nKT if none), from k_mask_walk
 };
 
 struct AttnArgs {

@@ -11,6 +11,7 @@
 //   k_mask_tiles      classifies each (256-row x 64-key) tile of a boolean or fp32 additive mask
 //                     as all-masked, all-visible (fp32: all exactly 0) or mixed, so the attention
 //                     kernel skips a tile or reads no mask for it
+//   k_mask_walk       adds to each tile's state the next tile of its row block that is not skipped
 //
 // Non-finite inputs: every maximum that sets a scale keeps NaN (mag_max), so a Q or K block or an
 // FP8 V channel holding a NaN gets a NaN scale, and a NaN or +inf scale gives every code of its
@@ -596,6 +597,22 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
   if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = x || (z && o) ? 2 : (o ? 1 : 0);
 }
 
+// The walk over a row block's key tiles: each entry of the state table gets, above its state (bits
+// 0-1), the index of the next tile after it that is not all-masked (nKT if there is none), so the
+// attention kernel steps from tile to tile with one load instead of a loop over dropped tiles.  One
+// thread per (mask batch, head, row block) row of the table, scanning it from the end.
+__global__ __launch_bounds__(kPrepThreads) void k_mask_walk(int* __restrict__ state, int64_t rows, int nKT) {
+  const int64_t r = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  if (r >= rows) return;
+  int* row = state + r * nKT;
+  int nxt = nKT;
+  for (int kt = nKT - 1; kt >= 0; --kt) {
+    const int st = row[kt] & 3;
+    row[kt] = st | (nxt << 2);
+    if (st != 0) nxt = kt;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------------------------
@@ -717,6 +734,8 @@ hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s) {
     k_mask_tiles<true><<<g, kPrepThreads, 0, s>>>(a);
   else
     k_mask_tiles<false><<<g, kPrepThreads, 0, s>>>(a);
+  const int64_t rows = a.B * a.Hm * a.nQT;
+  k_mask_walk<<<(unsigned)((rows + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, s>>>(a.state, rows, a.nKT);
   return hipGetLastError();
 }
 
