@@ -316,6 +316,12 @@ CASES = [
     dict(name="fmask_fp8", B=1, H=2, Nq=300, Nk=450, d=128, pv="fp8", sigma=8.0, mask="f_rand_h"),
     dict(name="fmask_fp8_d64_causal", B=1, H=2, Nq=200, Nk=333, d=64, pv="fp8", causal=True, mask="f_rand_1"),
     dict(name="fmask_zero_inf_tiles", B=1, H=2, Nq=520, Nk=700, d=128, mask="f_tiles"),
+    # the skipped-tile walk: leading, alternating and trailing dropped key tiles per 256-row block
+    dict(name="mask_tile_walk", B=1, H=2, Nq=520, Nk=1000, d=128, mask="walk"),
+    dict(name="mask_tile_walk_fp8_d64", B=1, H=2, Nq=520, Nk=1000, d=64, pv="fp8", mask="walk"),
+    dict(name="mask_tile_walk_causal", B=1, H=2, Nq=1000, Nk=1000, d=128, causal=True, mask="walk"),
+    dict(name="fmask_tile_walk", B=1, H=2, Nq=520, Nk=1000, d=128, mask="f_walk"),
+    dict(name="fmask_tile_walk_fp8", B=1, H=2, Nq=520, Nk=1000, d=128, pv="fp8", mask="f_walk"),
     dict(name="fmask_gqa_fp16_in_nhd", B=1, H=4, Hkv=1, Nq=130, Nk=260, d=128, dtype="fp16", layout="NHD",
          mask="f_rand_h"),
     # smooth_v on values with a large channel bias
@@ -359,6 +365,25 @@ def case_mask(c, B, H, Nq, Nk):
         m = torch.zeros(B, 1, 1, Nk, dtype=torch.float32)
         m[..., Nk // 3:] = float("-inf")
         m[..., :40] = 0.7
+        return m
+    if kind in ("walk", "f_walk"):
+        # Per 256-row block, which 64-key tiles any of its rows sees: rows 0-255 every third tile
+        # from tile 2 (tiles 0-1 dropped, one of them partly masked), rows 256-511 tile 7 (partly)
+        # and the ragged last tile only, rows 512+ the first four tiles only.
+        vis = torch.zeros(Nq, Nk, dtype=torch.bool)
+        for t in range(2, (Nk + 63) // 64, 3):
+            vis[:256, 64 * t:64 * t + 64] = True
+        vis[:256, 64 * 8 + 10:64 * 8 + 30] = False
+        vis[256:512, 64 * 7:64 * 7 + 33] = True
+        vis[256:512, 64 * ((Nk - 1) // 64):] = True
+        vis[512:, :256] = True
+        vis[600:, 900:] = True  # later blocks (causal case): a visible run across the ragged tail
+        vis = vis[:Nq, :Nk].expand(B, 1, Nq, Nk)
+        if kind == "walk":
+            return vis.clone()
+        m = torch.where(vis, 0.0, float("-inf")).to(torch.float32)
+        m[..., :256, 64 * 5:64 * 6] += 0.5 * torch.randn(B, 1, min(Nq, 256), 64,
+                                                        generator=torch.Generator().manual_seed(8))
         return m
     if kind == "f_tiles":
         # whole 256 x 64 tiles that are all 0 (read no mask), all -inf (skipped) or mixed
