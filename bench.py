@@ -483,7 +483,11 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
                                     " for PV, each half of the counted ops"),
                      "ops_per_launch": ops * visible / S,
                      "traffic": traffic, "avg_ms": round(attn_avg, 4), "median_ms": round(attn_ms[len(attn_ms) // 2], 4),
-                     "min_ms": round(attn_ms[0], 4)},
+                     "min_ms": round(attn_ms[0], 4),
+                     "timed": ("HIP events around sage_fp4_attn_fwd (k_fp4_attn)" if w.method == "fp4" else
+                               "HIP events around sage_attn_fwd_prepared: the mask-tile classification (k_mask_tiles, "
+                               "k_mask_walk) and k_attn_fwd" if w.mask else
+                               "HIP events around sage_attn_fwd_prepared (k_attn_fwd alone)")},
         "sclk": probe,
         "sclk_sysfs": sclk,
         "accuracy": accuracy() if accuracy is not None else None,

@@ -21,6 +21,8 @@
 // Method sources (page title, section): SageAttention docs digest (context7 llms.txt) --
 // "sageattn_qk_int8_pv_fp16_triton" (per-block INT8 Q/K, smooth_k), "sageattn3_blackwell" usage
 // (smoothing by the global token mean), "sageattn_qk_int8_pv_fp8_cuda" (per-channel FP8 V).
+#include <limits.h>
+
 #include <type_traits>
 
 #include "sage_device.h"
@@ -600,16 +602,28 @@ __global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
 // The walk over a row block's key tiles: each entry of the state table gets, above its state (bits
 // 0-1), the index of the next tile after it that is not all-masked (nKT if there is none), so the
 // attention kernel steps from tile to tile with one load instead of a loop over dropped tiles.  One
-// thread per (mask batch, head, row block) row of the table, scanning it from the end.
-__global__ __launch_bounds__(kPrepThreads) void k_mask_walk(int* __restrict__ state, int64_t rows, int nKT) {
-  const int64_t r = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
-  if (r >= rows) return;
-  int* row = state + r * nKT;
-  int nxt = nKT;
-  for (int kt = nKT - 1; kt >= 0; --kt) {
-    const int st = row[kt] & 3;
-    row[kt] = st | (nxt << 2);
-    if (st != 0) nxt = kt;
+// wave per (mask batch, head, row block) row of the table takes it 64 entries at a time from the
+// end: a suffix minimum across the lanes gives each entry the first kept tile at or after it, and
+// the chunk's minimum carries over to the chunk before it.
+__global__ __launch_bounds__(64) void k_mask_walk(int* __restrict__ state, int nKT) {
+  int* row = state + (int64_t)blockIdx.x * nKT;
+  const int lane = threadIdx.x;
+  int carry = nKT;  // the first kept tile after this chunk
+  for (int base = ((nKT - 1) / 64) * 64; base >= 0; base -= 64) {
+    const int kt = base + lane;
+    const int st = kt < nKT ? row[kt] & 3 : 0;
+    int v = st != 0 ? kt : INT_MAX;  // (entries past nKT have st = 0)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_down(v, off);
+      if (lane + off < 64) v = v < o ? v : o;  // minimum over lanes [lane, 63] of this chunk
+    }
+    int nxt = __shfl_down(v, 1);
+    if (lane == 63) nxt = INT_MAX;
+    nxt = nxt < carry ? nxt : carry;
+    if (kt < nKT) row[kt] = st | (nxt << 2);
+    const int cmin = __shfl(v, 0);
+    carry = cmin < carry ? cmin : carry;
   }
 }
 
@@ -734,8 +748,8 @@ hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s) {
     k_mask_tiles<true><<<g, kPrepThreads, 0, s>>>(a);
   else
     k_mask_tiles<false><<<g, kPrepThreads, 0, s>>>(a);
-  const int64_t rows = a.B * a.Hm * a.nQT;
-  k_mask_walk<<<(unsigned)((rows + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, s>>>(a.state, rows, a.nKT);
+  const int64_t rows = a.B * a.Hm * a.nQT;  // one wave per row of the table
+  k_mask_walk<<<(unsigned)rows, 64, 0, s>>>(a.state, a.nKT);
   return hipGetLastError();
 }
 
