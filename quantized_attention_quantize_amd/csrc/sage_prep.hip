@@ -534,69 +534,107 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_v8(PrepVArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Mask tile classification.  grid = (nKT, nQT, B*Hm), block = 256 (one thread per tile row).
+// Mask tile classification.  grid = (nKT, nQT, B*Hm), block = 256.
 // state: 0 = every (valid) entry masked, 1 = every valid entry visible with nothing added (boolean:
 // nonzero; fp32: exactly +-0), 2 = anything else.  Entries beyond Nq / Nk do not count.  F32: the
-// mask is fp32 and additive, -inf masks.
+// mask is fp32 and additive, -inf masks.  A whole 16-byte-aligned tile is read in 16-byte chunks,
+// consecutive lanes along a row (4 lanes a row for a boolean tile row of 64 bytes, 16 for fp32's
+// 256 bytes), every load issued before the first is classified; a ragged or unaligned tile is read
+// one row per thread.
 // ---------------------------------------------------------------------------------------------
+// key tiles per classification workgroup: a boolean workgroup reads whole 128-byte lines of its rows
 template <bool F32>
-__global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
-  const int kt = blockIdx.x, qt = blockIdx.y;
-  const int64_t bm = blockIdx.z, b = bm / a.Hm, hm = bm % a.Hm;
-  const int64_t i = (int64_t)qt * kMaskTileRows + threadIdx.x;
-  const int64_t j0 = (int64_t)kt * kBlockN;
-  int any0 = 0, any1 = 0, anyx = 0;  // a masked entry / a plainly visible one / anything else
-  if (i < a.Nq) {
-    const int64_t off = b * a.sb + hm * a.sh + i * a.sq;
-    int64_t jn = a.Nk - j0 < kBlockN ? a.Nk - j0 : kBlockN;
+constexpr int kMaskTilesPerGroup = F32 ? 1 : 2;
+
+template <bool F32>
+__device__ __forceinline__ void mask_classify16(uint4 w, int& any0, int& any1, int& anyx) {
+  const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
     if constexpr (F32) {
-      const float* row = static_cast<const float*>(a.mask) + off + j0;
-      auto classify = [&](float v) {
-        any0 |= v == -INFINITY;
-        any1 |= v == 0.f;
-        anyx |= v != -INFINITY && v != 0.f;
-      };
-      if (a.vec16 && jn == kBlockN) {
-#pragma unroll
-        for (int c = 0; c < kBlockN / 4; ++c) {
-          const float4 w = *reinterpret_cast<const float4*>(row + 4 * c);
-          classify(w.x);
-          classify(w.y);
-          classify(w.z);
-          classify(w.w);
-        }
-      } else {
-        for (int64_t j = 0; j < jn; ++j) classify(row[j]);
-      }
+      const float v = __uint_as_float(ws[e]);
+      any0 |= v == -INFINITY;
+      any1 |= v == 0.f;
+      anyx |= v != -INFINITY && v != 0.f;
     } else {
-      const uint8_t* row = static_cast<const uint8_t*>(a.mask) + off;
-      if (a.vec16 && jn == kBlockN) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint4 w = *reinterpret_cast<const uint4*>(row + j0 + 16 * c);
-          unsigned ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            unsigned v = ws[e];
-            // per byte: zero -> any0, nonzero -> any1
-            unsigned nz = ((v & 0x7f7f7f7fu) + 0x7f7f7f7fu | v) & 0x80808080u;
-            any1 |= nz != 0u;
-            any0 |= nz != 0x80808080u;
-          }
-        }
-      } else {
-        for (int64_t j = 0; j < jn; ++j) {
-          uint8_t v = row[j0 + j];
-          any1 |= v != 0;
-          any0 |= v == 0;
-        }
-      }
+      const unsigned v = ws[e];
+      // per byte: zero -> any0, nonzero -> any1
+      const unsigned nz = ((v & 0x7f7f7f7fu) + 0x7f7f7f7fu | v) & 0x80808080u;
+      any1 |= nz != 0u;
+      any0 |= nz != 0x80808080u;
     }
   }
-  const int z = __syncthreads_or(any0);
-  const int o = __syncthreads_or(any1);
-  const int x = __syncthreads_or(anyx);
-  if (threadIdx.x == 0) a.state[(bm * a.nQT + qt) * a.nKT + kt] = x || (z && o) ? 2 : (o ? 1 : 0);
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kPrepThreads) void k_mask_tiles(MaskTileArgs a) {
+  constexpr int ESZ = F32 ? 4 : 1;
+  constexpr int TPW = kMaskTilesPerGroup<F32>;  // key tiles per workgroup
+  const int kt0 = (int)blockIdx.x * TPW, qt = blockIdx.y;
+  const int64_t bm = blockIdx.z, b = bm / a.Hm, hm = bm % a.Hm;
+  const int64_t i0 = (int64_t)qt * kMaskTileRows;
+  const int64_t j0 = (int64_t)kt0 * kBlockN;
+  const char* head = static_cast<const char*>(a.mask) + (b * a.sb + hm * a.sh) * ESZ;
+  unsigned flags = 0;  // for tile kt0 + t, bit 3t: a masked entry, 3t + 1: a plainly visible one, 3t + 2: other
+  if (a.vec16 && a.Nk - j0 >= (int64_t)TPW * kBlockN) {
+    constexpr int CPR = TPW * kBlockN * ESZ / 16;  // 16-byte chunks per row of the group's tiles
+    constexpr int RPP = kPrepThreads / CPR;        // rows per pass
+    constexpr int NP = kMaskTileRows / RPP;        // passes
+    const int c = threadIdx.x % CPR, r = threadIdx.x / CPR;
+    uint4 w[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t i = i0 + r + p * RPP;
+      w[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < a.Nq) w[p] = *reinterpret_cast<const uint4*>(head + (i * a.sq + j0) * ESZ + c * 16);
+    }
+    int any0 = 0, any1 = 0, anyx = 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (i0 + r + p * RPP < a.Nq) mask_classify16<F32>(w[p], any0, any1, anyx);
+    const int t = c / (CPR / TPW);
+    flags = (unsigned)(any0 | any1 << 1 | anyx << 2) << (3 * t);
+  } else {
+    const int64_t i = i0 + threadIdx.x;
+    for (int t = 0; t < TPW && kt0 + t < a.nKT; ++t) {
+      const int64_t jt = j0 + (int64_t)t * kBlockN;
+      const int64_t jn = a.Nk - jt < kBlockN ? a.Nk - jt : kBlockN;
+      int any0 = 0, any1 = 0, anyx = 0;
+      if (i < a.Nq) {
+        if constexpr (F32) {
+          const float* row = reinterpret_cast<const float*>(head) + i * a.sq + jt;
+          for (int64_t j = 0; j < jn; ++j) {
+            const float v = row[j];
+            any0 |= v == -INFINITY;
+            any1 |= v == 0.f;
+            anyx |= v != -INFINITY && v != 0.f;
+          }
+        } else {
+          const uint8_t* row = reinterpret_cast<const uint8_t*>(head) + i * a.sq + jt;
+          for (int64_t j = 0; j < jn; ++j) {
+            const uint8_t v = row[j];
+            any1 |= v != 0;
+            any0 |= v == 0;
+          }
+        }
+      }
+      flags |= (unsigned)(any0 | any1 << 1 | anyx << 2) << (3 * t);
+    }
+  }
+  // OR of the flags over the workgroup
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) flags |= __shfl_xor(flags, o);
+  __shared__ unsigned wflags[kPrepThreads / 64];
+  if ((threadIdx.x & 63) == 0) wflags[threadIdx.x >> 6] = flags;
+  __syncthreads();
+  if (threadIdx.x < TPW && kt0 + (int)threadIdx.x < a.nKT) {
+    unsigned f = 0;
+#pragma unroll
+    for (int wv = 0; wv < kPrepThreads / 64; ++wv) f |= wflags[wv];
+    f >>= 3 * threadIdx.x;
+    const bool z = f & 1u, o = f & 2u, x = f & 4u;
+    a.state[(bm * a.nQT + qt) * a.nKT + kt0 + threadIdx.x] = x || (z && o) ? 2 : (o ? 1 : 0);
+  }
 }
 
 // The walk over a row block's key tiles: each entry of the state table gets, above its state (bits
@@ -743,11 +781,14 @@ hipError_t launch_prep_v(const PrepVArgs& a, int pv_fp8, hipStream_t s) {
 }
 
 hipError_t launch_mask_tiles(const MaskTileArgs& a, hipStream_t s) {
-  dim3 g((unsigned)a.nKT, (unsigned)a.nQT, (unsigned)(a.B * a.Hm));
-  if (a.f32)
-    k_mask_tiles<true><<<g, kPrepThreads, 0, s>>>(a);
-  else
-    k_mask_tiles<false><<<g, kPrepThreads, 0, s>>>(a);
+  const unsigned gq = (unsigned)a.nQT, gb = (unsigned)(a.B * a.Hm);
+  if (a.f32) {
+    constexpr int T = kMaskTilesPerGroup<true>;
+    k_mask_tiles<true><<<dim3((unsigned)((a.nKT + T - 1) / T), gq, gb), kPrepThreads, 0, s>>>(a);
+  } else {
+    constexpr int T = kMaskTilesPerGroup<false>;
+    k_mask_tiles<false><<<dim3((unsigned)((a.nKT + T - 1) / T), gq, gb), kPrepThreads, 0, s>>>(a);
+  }
   const int64_t rows = a.B * a.Hm * a.nQT;  // one wave per row of the table
   k_mask_walk<<<(unsigned)rows, 64, 0, s>>>(a.state, a.nKT);
   return hipGetLastError();
