@@ -854,51 +854,85 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   // read again from the kernel-argument segment here, so they hold no SGPRs across the loop.
   const AttnArgs& ea = *kernarg_reload<AttnArgs>();
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
-  if (row < nq) {
-    const float* vsh = PV == 1 ? ea.vscale + bhk * D : nullptr;
-    // A row without a visible key (l = 0) stores O = 0 and LSE = -inf, whatever a zero
-    // probability times a NaN in V left in o; a NaN l (a NaN score) makes both NaN.
-    const bool live = l_tot != 0.f;
-    const float inv = live ? 1.f / l_tot : 0.f;
-    const float* vmh = (ea.vmean && live) ? ea.vmean + bhk * D : nullptr;  // smooth_v
-    const int64_t obase = b * ea.o_sb + h * ea.o_sh + (sq.off + row) * ea.o_sn;  // elements
+  const float* vsh = PV == 1 ? ea.vscale + bhk * D : nullptr;
+  // A row without a visible key (l = 0) stores O = 0 and LSE = -inf, whatever a zero
+  // probability times a NaN in V left in o; a NaN l (a NaN score) makes both NaN.
+  const bool live = l_tot != 0.f;
+  const float inv = live ? 1.f / l_tot : 0.f;
+  const float* vmh = (ea.vmean && live) ? ea.vmean + bhk * D : nullptr;  // smooth_v
+  // channels db*32 + rq*8 + 4g .. +3 of this lane's row, normalized
+  auto norm = [&](int db, int rq, float (&f)[4]) {
+    const int d0 = db * 32 + rq * 8 + g * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (PV == 1)
+        f[e] = o[db][rq * 4 + e] * (vsh[d0 + e] * inv);
+      else
+        f[e] = o[db][rq * 4 + e] * inv;
+      if (vmh) f[e] = f[e] + vmh[d0 + e];
+      f[e] = live ? f[e] : 0.f;
+    }
+  };
+  // O leaves through LDS: each wave writes its 32 rows into its own region of the idle ring (rows of
+  // RB = 2*D bytes, 16-byte chunks XOR-swizzled by the row) and reads them back so that consecutive
+  // lanes store consecutive 16-byte chunks of one row.  16-bit output is one pass; fp32 is two,
+  // of D/2 channels each.
+  constexpr int RB = 2 * D, CPR = RB / 16;  // region row bytes, chunks per row
+  __syncthreads();                          // every wave's last reads of the ring are done
+  char* const so = smem + w * (32 * RB);
+  const int64_t orow0 = b * ea.o_sb + h * ea.o_sh + (sq.off + r0w) * ea.o_sn;  // elements
+  auto store_region = [&](char* outp, int osz, int ch0) {
+    __syncthreads();  // the region is written
+#pragma unroll
+    for (int it = 0; it < CPR / 2; ++it) {
+      const int r = it * (64 / CPR) + lane / CPR, c = lane % CPR;
+      const v4i val = *reinterpret_cast<const v4i*>(so + r * RB + ((c ^ (r & (CPR - 1))) * 16));
+      if (r0w + r < nq)
+        *reinterpret_cast<v4i*>(outp + (orow0 + r * ea.o_sn + ch0) * osz + c * 16) = val;
+    }
+  };
+  if (ea.out_kind == 2) {  // fp32, e.g. partial results that are merged later
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass) __syncthreads();  // the previous pass's reads of the region are done
+#pragma unroll
+      for (int db = pass * D / 64; db < (pass + 1) * D / 64; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float f[4];
+          norm(db, rq, f);
+          const int c = (db - pass * D / 64) * 8 + rq * 2 + g;
+          *reinterpret_cast<float4*>(so + lr * RB + ((c ^ (lr & (CPR - 1))) * 16)) = make_float4(f[0], f[1], f[2], f[3]);
+        }
+      store_region(static_cast<char*>(ea.out), 4, pass * D / 2);
+    }
+  } else {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = db * 32 + rq * 8 + g * 4;
         float f[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (PV == 1)
-            f[e] = o[db][rq * 4 + e] * (vsh[d0 + e] * inv);
-          else
-            f[e] = o[db][rq * 4 + e] * inv;
-          if (vmh) f[e] = f[e] + vmh[d0 + e];
-          f[e] = live ? f[e] : 0.f;
-        }
-        if (ea.out_kind == 2) {  // fp32, e.g. partial results that are merged later
-          *reinterpret_cast<float4*>(static_cast<float*>(ea.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
+        norm(db, rq, f);
+        uint2 pk;
+        if (ea.out_kind == 1) {
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
         } else {
-          uint2 pk;
-          if (ea.out_kind == 1) {
-            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
-            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
-          } else {
-            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
-            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
-          }
-          *reinterpret_cast<uint2*>(static_cast<unsigned short*>(ea.out) + obase + d0) = pk;
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
         }
+        const int c = db * 4 + rq;
+        *reinterpret_cast<uint2*>(so + lr * RB + ((c ^ (lr & (CPR - 1))) * 16) + g * 8) = pk;
       }
-    if (g == 0 && ea.lse) {
-      float v = -INFINITY;
-      if (l_tot != 0.f) {
-        // l_tot sums 2^(s - pm) over the row (e4m3 P carries its scale 448 * 2^-tau inside pm)
-        v = (rs.pm + log2f(l_tot)) * kLn2 + ea.sm_scale * ea.corr[bh * ea.Nq + row];
-      }
-      ea.lse[b * ea.l_sb + h * ea.l_sh + sq.off + row] = v;
+    store_region(static_cast<char*>(ea.out), 2, 0);
+  }
+  if (row < nq && g == 0 && ea.lse) {
+    float v = -INFINITY;
+    if (l_tot != 0.f) {
+      // l_tot sums 2^(s - pm) over the row (e4m3 P carries its scale 448 * 2^-tau inside pm)
+      v = (rs.pm + log2f(l_tot)) * kLn2 + ea.sm_scale * ea.corr[bh * ea.Nq + row];
     }
+    ea.lse[b * ea.l_sb + h * ea.l_sh + sq.off + row] = v;
   }
 }
 
