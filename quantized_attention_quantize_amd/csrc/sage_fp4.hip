@@ -428,7 +428,9 @@ constexpr int kF4KB = kBlockN * 64;              // K tile: 64 keys x 64 bytes
 constexpr int kF4VB = 128 * kBlockN / 2;         // V^T tile: 128 channels x 32 bytes (64 rows of 64)
 constexpr int kF4CB = 2 * kBlockN * 4;           // correction values of the workgroup's two Q blocks
 constexpr int kF4SB = 256;                       // K scales (64 keys x 4) or V scales (2 x 128) of a tile
-constexpr int kF4Smem = kF4NS * (kF4KB + kF4VB + kF4CB + 2 * kF4SB);
+constexpr int kF4Ring = kF4NS * (kF4KB + kF4VB + kF4CB + 2 * kF4SB);
+constexpr int kF4OStage = (kF4AttnThreads / 64) * 32 * 256;  // the epilogue's output staging: 32 rows of 256 bytes a wave
+constexpr int kF4Smem = kF4Ring > kF4OStage ? kF4Ring : kF4OStage;
 
 // Chunk swizzle of the FP4 tiles' 64-byte LDS rows (64 rows per tile).  In one 16-lane LDS phase
 // the K fragment reads take rows 32 kb + 16 (l bit 2) + 4 (l >> 3) + (l & 3) and the V fragment
@@ -856,38 +858,65 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
     for (int db = 0; db < 4; ++db) f4_pv(o, db, *reinterpret_cast<const v4i*>(sV + lb.v[db]), P, vs);
   }
 
-  // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE
+  // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE.  O leaves through LDS: each wave
+  // writes its 32 rows into its own region (rows of 256 bytes, 16-byte chunks XOR-swizzled by the
+  // row) and reads them back so that consecutive lanes store consecutive 16-byte chunks of one row;
+  // fp32 output takes two passes of 64 channels.
   const float l_tot = rs.l + __shfl_xor(rs.l, 32);
-  if (row < nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t obase = b * a.o_sb + h * a.o_sh + (int64_t)row * a.o_sn;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int RB = 2 * D, CPR = RB / 16;  // region row bytes, chunks per row
+  __syncthreads();                          // every wave's last reads of the ring are done
+  char* const so = smem + w * (32 * RB);
+  const int64_t orow0 = b * a.o_sb + h * a.o_sh + (int64_t)r0w * a.o_sn;  // elements
+  auto store_region = [&](char* outp, int osz, int ch0) {
+    __syncthreads();  // the region is written
+#pragma unroll
+    for (int it = 0; it < CPR / 2; ++it) {
+      const int r = it * (64 / CPR) + lane / CPR, c = lane % CPR;
+      const v4i val = *reinterpret_cast<const v4i*>(so + r * RB + ((c ^ (r & (CPR - 1))) * 16));
+      if (r0w + r < nq)
+        *reinterpret_cast<v4i*>(outp + (orow0 + r * a.o_sn + ch0) * osz + c * 16) = val;
+    }
+  };
+  if (a.out_kind == 2) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass) __syncthreads();  // the previous pass's reads of the region are done
+#pragma unroll
+      for (int db = 2 * pass; db < 2 * pass + 2; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int c = (db - 2 * pass) * 8 + rq * 2 + g;
+          *reinterpret_cast<float4*>(so + lr * RB + ((c ^ (lr & (CPR - 1))) * 16)) =
+              make_float4(o[db][rq * 4] * inv, o[db][rq * 4 + 1] * inv, o[db][rq * 4 + 2] * inv, o[db][rq * 4 + 3] * inv);
+        }
+      store_region(static_cast<char*>(a.out), 4, pass * 64);
+    }
+  } else {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = db * 32 + rq * 8 + g * 4;
         float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = o[db][rq * 4 + e] * inv;
-        if (a.out_kind == 2) {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + obase + d0) = make_float4(f[0], f[1], f[2], f[3]);
+        uint2 pk;
+        if (a.out_kind == 1) {
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
         } else {
-          uint2 pk;
-          if (a.out_kind == 1) {
-            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2h));  // RNE
-            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2h));
-          } else {
-            pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
-            pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
-          }
-          *reinterpret_cast<uint2*>(static_cast<unsigned short*>(a.out) + obase + d0) = pk;
+          pk.x = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[0], f[1]}), v2bf));  // RNE
+          pk.y = __builtin_bit_cast(unsigned, __builtin_convertvector((v2f{f[2], f[3]}), v2bf));
         }
+        const int c = db * 4 + rq;
+        *reinterpret_cast<uint2*>(so + lr * RB + ((c ^ (lr & (CPR - 1))) * 16) + g * 8) = pk;
       }
-    if (g == 0 && a.lse) {
-      float v = -INFINITY;
-      if (l_tot > 0.f) v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.lse_corr[bh * a.Nq + row];
-      a.lse[bh * a.Nq + row] = v;
-    }
+    store_region(static_cast<char*>(a.out), 2, 0);
+  }
+  if (row < nq && g == 0 && a.lse) {
+    float v = -INFINITY;
+    if (l_tot > 0.f) v = (rs.pm + log2f(l_tot)) * kLn2 + a.sm_scale * a.lse_corr[bh * a.Nq + row];
+    a.lse[bh * a.Nq + row] = v;
   }
 }
 
