@@ -10,9 +10,11 @@
 //
 // Design (MI355X / CDNA4):
 //  * One workgroup = 8 waves = 256 query rows of one (b,h), two waves per SIMD; each wave owns one
-//    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  Inside a
-//    wave the key loop is software-pipelined (QK of the next tile, softmax of this tile and PV of
-//    the previous tile are interleaved), so MFMA and VALU work of one wave overlap.
+//    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  Unmasked
+//    launches split each step into a softmax phase and an MFMA phase, run in opposite orders by the
+//    two waves of a SIMD, so one wave's exponentials overlap the other's MFMA stream.  Masked
+//    launches software-pipeline the key loop inside each wave instead (QK of the next tile,
+//    softmax of this tile and PV of the previous tile interleaved).
 //  * S^T = K8 . Q8^T on v_mfma_i32_32x32x32_i8: the K tile (A operand) comes from LDS, the
 //    wave's Q8 rows (B operand) stay in registers for the whole key loop.  In the 32x32 output
 //    layout each lane holds one query row and 16 of every 32 keys, so the row max and row sum are
@@ -577,6 +579,103 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
     for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
 }
 
+// Phase-split schedule (PP) for launches without a mask table, float mask or per-block means.
+// The waves of a workgroup form two groups, one wave of each on every SIMD (waves 0-3 and 4-7).
+// Every step holds one softmax phase (VALU: a tile's row maxima, exponentials, row sums and
+// P) and one MFMA phase (QK of the next tile into the score registers, PV of the current tile
+// from P), in opposite orders in the two groups: group 0 runs softmax then MFMA, group 1 runs
+// MFMA then the softmax of the next tile.  So while one wave of a SIMD streams its MFMAs, the
+// other runs its softmax on the vector unit, and a wave holds one set of score registers, not two.
+
+// Softmax of one tile whose scores are in acc: masks them (SLOW), takes the row maxima, moves the
+// reference maximum, and writes P = exp2(s*c - pm) (fp16, or e4m3 of 448*2^-tau*p) with the row
+// sums.  Returns 2^(m_old - m_new), the factor O takes before this tile's PV.
+template <int D, int PV, bool SLOW>
+__device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, float c, RowState& rs, int g, int lim) {
+  constexpr bool MG = PV == 0;  // FP16 P: the QK accumulators start at the biased value (see tile_step)
+  if constexpr (SLOW) mask_scores(acc, g, lim, nullptr, false);
+  int ch[4];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) max_piece(acc, ch, p);
+  float pm_new;
+  const float alpha = finish_max<PV, SLOW, false, false, MG>(ch, c, rs, pm_new);
+  rs.pm = pm_new;
+  const float kk = MG ? __builtin_fmaf(-kMagic, c, -pm_new) : -pm_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = gi * 4 + e;
+      const int si = acc[idx >> 4][idx & 15];
+      float t;
+      if constexpr (MG)
+        t = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(si), c, kk));
+      else
+        t = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si, c, kk));
+      if constexpr (SLOW) t = si == INT_MIN ? 0.f : t;
+      x[e] = t;
+    }
+    psum += (x[0] + x[1]) + (x[2] + x[3]);  // the fp32 probabilities, before P's rounding
+    if constexpr (PV == 0) {
+      const int idx = gi * 4, kb = idx >> 4, r = idx & 15;
+      const int s2 = kb * 2 + (r >> 3), jj = (r & 7) >> 1;
+      const v2h h0 = __builtin_convertvector((v2f{x[0], x[1]}), v2h);  // round to nearest even
+      const v2h h1 = __builtin_convertvector((v2f{x[2], x[3]}), v2h);
+      P.s[s2][2 * jj] = h0[0];
+      P.s[s2][2 * jj + 1] = h0[1];
+      P.s[s2][2 * jj + 2] = h1[0];
+      P.s[s2][2 * jj + 3] = h1[1];
+    } else {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      P.b[gi] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    }
+  }
+  rs.l = alpha * rs.l + psum;
+  return alpha;
+}
+
+// Operands of the MFMA phase read from LDS ahead of its MFMA stream.
+constexpr int kPhaseLA = 3;
+
+// MFMA phase: the QK MFMAs of the next tile (K from sK) into acc, then the PV MFMAs of the
+// current tile (V from sV, P) into O.  Operand r < NQ is K fragment r, else V fragment r - NQ;
+// the first kPhaseLA K fragments arrive in pre, the rest are read kPhaseLA MFMAs ahead.
+template <int D, int PV>
+__device__ __forceinline__ void mfma_phase(const v4i (&pre)[kPhaseLA], const char* sK, const char* sV,
+                                           const PFrag<PV>& P, const v4i (&qf)[D / 32], v16f (&o)[D / 32],
+                                           v16i (&acc)[2], const LaneBases& lb, int g, const v16i& magic) {
+  using SG = StepGeom<D, PV>;
+  constexpr int NB = SG::NB, NQ = SG::NQ, NPV = SG::NPV, NM = NQ + NPV;
+  static_assert(NQ > kPhaseLA, "the preloaded operands are K fragments");
+  v4i kf[NQ];
+  typename SG::VFrag vf[NPV];
+#pragma unroll
+  for (int r = 0; r < kPhaseLA; ++r) kf[r] = pre[r];
+  auto read = [&](int r) {
+    if (r < NQ)
+      kf[r] = kfrag<D>(sK, lb, r);
+    else
+      vf[r - NQ] = vfrag<D, PV>(sV, lb, g, r - NQ);
+  };
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    if (k + kPhaseLA < NM) read(k + kPhaseLA);
+    if (k < NQ) {
+      qk_mfma<D, PV == 0>(kf[k], qf, k, acc, magic);
+    } else {
+      const int j = k - NQ;
+      if constexpr (PV == 0)
+        o[j % NB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, vf[j]), P.s[j / NB], o[j % NB], 0,
+                                                          0, 0);
+      else
+        o[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[j], P.b, o[j], 0, 0, 0, 127, 0, 127);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Main loop, software-pipelined inside each wave (see tile_step).  One workgroup = 8 waves = 256
 // query rows; wave w owns rows 32w..32w+31.  LDS holds a four-stage ring of K tiles and one of V
 // tiles; processed tiles are numbered T[0], T[1], ...: K of T[i] lives in kslot i%4, V of T[i] in
@@ -598,9 +697,12 @@ __device__ __forceinline__ const T* kernarg_reload() {
 // TT: the launch has a mask-tile table (a boolean or float mask; MF implies TT).  Without one the
 // tile walk is plain arithmetic: no tile is dropped and only the causal diagonal and ragged tail
 // take the per-element step.
-template <int D, int PV, int MF, int BM, int TT>
+// PP: the phase-split schedule (softmax_phase / mfma_phase) instead of tile_step; only without a
+// mask table, float mask or per-block means.
+template <int D, int PV, int MF, int BM, int TT, int PP = 0>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   static_assert(TT || !MF, "a float mask comes with its tile table");
+  static_assert(!PP || (!MF && !BM && !TT), "the phase-split schedule runs unmasked launches only");
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
   __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
@@ -610,6 +712,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   char* const kring = smem + kNS * G::V_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
+  // PP: waves 4-7 run their MFMA phase first.  Waves w and w + 4 share a SIMD (waves go round-robin
+  // over the four SIMDs), so every SIMD holds one wave of each group.
+  const int grp1 = __builtin_amdgcn_readfirstlane(w >= kWaves / 2 ? 1 : 0);
 
   int64_t bh;
   int qt;
@@ -757,7 +862,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const float cbs = a.sm_scale * kLog2e;
   auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
   float cb_cur = cb_of(t0);
-  {  // scores of T[0] and the row maxima of its first key block; the first PV operands
+  if constexpr (PP) {  // scores of T[0]; group 1 takes their softmax before its first step
+    qk_tile<D, PV == 0>(kring, qf, lb, acc, magic);
+    if (grp1) {
+      int lim;
+      const void* mtile;
+      visible(t0, lim, mtile);
+      if (part_cur)
+        softmax_phase<D, PV, true>(acc, P, c_cur, rs, g, lim);
+      else
+        softmax_phase<D, PV, false>(acc, P, c_cur, rs, g, kBlockN - 1);
+      // O is still zero: the factor returned (0) needs no application
+    }
+  } else {  // scores of T[0] and the row maxima of its first key block; the first PV operands
     qk_tile<D, (PV == 0 && !MF)>(kring, qf, lb, acc, magic);
     int lim;
     const void* mtile;
@@ -840,15 +957,69 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     ++n;
     return true;
   };
+  // Phase-split step n: both groups read K of T[n+1] and V of T[n] (slots (n+1)%4 and n%4), and
+  // issue the loads of V of T[n+2] and K of T[n+3] into slots last read two steps earlier.  Group
+  // 0: softmax of T[n], then QK of T[n+1] and PV of T[n].  Group 1 (T[n]'s softmax done a step
+  // earlier): QK of T[n+1] and PV of T[n], then the softmax of T[n+1].  The softmax past the last
+  // tile sees only masked scores (P = 0, factor 1).
+  auto pstep = [&](auto slot) -> bool {
+    constexpr int Q = decltype(slot)::value;
+    if (tc >= kt_end) return false;
+    asm volatile("s_barrier" ::: "memory");
+    st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
+    st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
+    const float ks_n2 = ks_load(tnn);
+    const char* sV = vring + Q * G::V_BYTES;                // V of T[n]
+    const char* sK = kring + ((Q + 1) % kNS) * G::K_BYTES;  // K of T[n+1]
+    v4i pre[kPhaseLA];
+#pragma unroll
+    for (int r = 0; r < kPhaseLA; ++r) pre[r] = kfrag<D>(sK, lb, r);
+    const float c_nxt = scale_from(tn, ks_n1);
+    if (grp1) mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+    const int ts = grp1 ? tn : tc;
+    const float cs = grp1 ? c_nxt : c_cur;
+    int lim;
+    const void* mtile;
+    visible(ts, lim, mtile);
+    float alpha;
+    if (partial(ts))
+      alpha = softmax_phase<D, PV, true>(acc, P, cs, rs, g, lim);
+    else
+      alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1);
+    if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
+    if (!grp1) mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+    switch (nload) {
+      case 0: wait_vmcnt<1>(); break;
+      case 1: wait_vmcnt<2>(); break;
+      case 2: wait_vmcnt<3>(); break;
+      case 3: wait_vmcnt<4>(); break;
+      case 4: wait_vmcnt<5>(); break;
+      case 5: wait_vmcnt<6>(); break;
+      default: wait_vmcnt<7>(); break;
+    }
+    c_cur = c_nxt;
+    ks_n1 = ks_n2;
+    tc = tn;
+    tn = tnn;
+    tnn = tnnn;
+    tnnn = next_tile(tnnn);
+    ++n;
+    return true;
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  while (step(I0{}) && step(I1{}) && step(I2{}) && step(I3{})) {
+  if constexpr (PP) {
+    while (pstep(I0{}) && pstep(I1{}) && pstep(I2{}) && pstep(I3{})) {
+    }
+  } else {
+    while (step(I0{}) && step(I1{}) && step(I2{}) && step(I3{})) {
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
-  if (n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
+  if (!PP && n > 0) pv_tile<D, PV>(vring + ((n - 1) % kNS) * G::V_BYTES, P, lb, g, o);
 
   // epilogue: normalize, store O (bf16, fp16 or fp32) and the LSE.  The arguments it needs are
   // read again from the kernel-argument segment here, so they hold no SGPRs across the loop.
@@ -970,6 +1141,8 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
 // Every variant instantiated explicitly: the launches below alone do not make hipcc's host pass
 // emit the launch stubs of the MF = 0 kernels.
 template __global__ void k_attn_fwd<128, 0, 0, 0, 0>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 1, 0>(AttnArgs);
@@ -990,6 +1163,13 @@ template __global__ void k_attn_fwd<64, 1, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 0>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 1>(AttnArgs);
 
+// Unmasked launches at d = 128 run the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
+// interleaved tile_step schedule everywhere, e.g. to compare the two).
+#ifndef SAGE_PHASE_SPLIT
+#define SAGE_PHASE_SPLIT 1
+#endif
+constexpr bool kPhaseSplit = SAGE_PHASE_SPLIT;
+
 // a mask always comes with its tile table (the host classifies the tiles first)
 template <int D, int PV, int MF, int BM>
 static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
@@ -997,6 +1177,8 @@ static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
     k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
   else if (a.mtiles)
     k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
+  else if constexpr (D == 128 && !BM && kPhaseSplit)
+    k_attn_fwd<D, PV, MF, BM, 0, 1><<<grid, kAttnThreads, 0, s>>>(a);
   else
     k_attn_fwd<D, PV, MF, BM, 0><<<grid, kAttnThreads, 0, s>>>(a);
 }
