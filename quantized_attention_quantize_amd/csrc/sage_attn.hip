@@ -10,11 +10,12 @@
 //
 // Design (MI355X / CDNA4):
 //  * One workgroup = 8 waves = 256 query rows of one (b,h), two waves per SIMD; each wave owns one
-//    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  Unmasked
-//    launches split each step into a softmax phase and an MFMA phase, run in opposite orders by the
-//    two waves of a SIMD, so one wave's exponentials overlap the other's MFMA stream.  Masked
-//    launches software-pipeline the key loop inside each wave instead (QK of the next tile,
-//    softmax of this tile and PV of the previous tile interleaved).
+//    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  At
+//    d = 128 (no float mask, no per-block means) each step is split into a softmax phase and an
+//    MFMA phase, run in opposite orders by the two waves of a SIMD, so one wave's exponentials
+//    overlap the other's MFMA stream.  The other launches software-pipeline the key loop inside
+//    each wave instead (QK of the next tile, softmax of this tile and PV of the previous tile
+//    interleaved).
 //  * S^T = K8 . Q8^T on v_mfma_i32_32x32x32_i8: the K tile (A operand) comes from LDS, the
 //    wave's Q8 rows (B operand) stay in registers for the whole key loop.  In the 32x32 output
 //    layout each lane holds one query row and 16 of every 32 keys, so the row max and row sum are
@@ -587,13 +588,15 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
 // MFMA then the softmax of the next tile.  So while one wave of a SIMD streams its MFMAs, the
 // other runs its softmax on the vector unit, and a wave holds one set of score registers, not two.
 
-// Softmax of one tile whose scores are in acc: masks them (SLOW), takes the row maxima, moves the
+// Softmax of one tile whose scores are in acc: masks them (SLOW; lim and the boolean mask row mtile
+// as in mask_scores), takes the row maxima, moves the
 // reference maximum, and writes P = exp2(s*c - pm) (fp16, or e4m3 of 448*2^-tau*p) with the row
 // sums.  Returns 2^(m_old - m_new), the factor O takes before this tile's PV.
 template <int D, int PV, bool SLOW>
-__device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, float c, RowState& rs, int g, int lim) {
+__device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, float c, RowState& rs, int g, int lim,
+                                               const uint8_t* mtile, bool mvec4) {
   constexpr bool MG = PV == 0;  // FP16 P: the QK accumulators start at the biased value (see tile_step)
-  if constexpr (SLOW) mask_scores(acc, g, lim, nullptr, false);
+  if constexpr (SLOW) mask_scores(acc, g, lim, mtile, mvec4);
   int ch[4];
 #pragma unroll
   for (int p = 0; p < 8; ++p) max_piece(acc, ch, p);
@@ -697,12 +700,12 @@ __device__ __forceinline__ const T* kernarg_reload() {
 // TT: the launch has a mask-tile table (a boolean or float mask; MF implies TT).  Without one the
 // tile walk is plain arithmetic: no tile is dropped and only the causal diagonal and ragged tail
 // take the per-element step.
-// PP: the phase-split schedule (softmax_phase / mfma_phase) instead of tile_step; only without a
-// mask table, float mask or per-block means.
+// PP: the phase-split schedule (softmax_phase / mfma_phase) instead of tile_step; not with a float
+// mask or per-block means.
 template <int D, int PV, int MF, int BM, int TT, int PP = 0>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   static_assert(TT || !MF, "a float mask comes with its tile table");
-  static_assert(!PP || (!MF && !BM && !TT), "the phase-split schedule runs unmasked launches only");
+  static_assert(!PP || (!MF && !BM), "the phase-split schedule takes no float mask or per-block means");
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
   __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
@@ -869,9 +872,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const void* mtile;
       visible(t0, lim, mtile);
       if (part_cur)
-        softmax_phase<D, PV, true>(acc, P, c_cur, rs, g, lim);
+        softmax_phase<D, PV, true>(acc, P, c_cur, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4);
       else
-        softmax_phase<D, PV, false>(acc, P, c_cur, rs, g, kBlockN - 1);
+        softmax_phase<D, PV, false>(acc, P, c_cur, rs, g, kBlockN - 1, nullptr, false);
       // O is still zero: the factor returned (0) needs no application
     }
   } else {  // scores of T[0] and the row maxima of its first key block; the first PV operands
@@ -983,9 +986,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     visible(ts, lim, mtile);
     float alpha;
     if (partial(ts))
-      alpha = softmax_phase<D, PV, true>(acc, P, cs, rs, g, lim);
+      alpha = softmax_phase<D, PV, true>(acc, P, cs, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4);
     else
-      alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1);
+      alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1, nullptr, false);
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
     if (!grp1) mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
     switch (nload) {
@@ -1143,6 +1146,8 @@ __global__ __launch_bounds__(64) void k_debug_qk(DebugQKArgs a, int64_t Nq_pad) 
 template __global__ void k_attn_fwd<128, 0, 0, 0, 0>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 1, 0, 0, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 0, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 0, 1, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 1, 0>(AttnArgs);
@@ -1163,7 +1168,7 @@ template __global__ void k_attn_fwd<64, 1, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 0>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 1>(AttnArgs);
 
-// Unmasked launches at d = 128 run the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
+// Launches at d = 128 without a float mask or per-block means run the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
 // interleaved tile_step schedule everywhere, e.g. to compare the two).
 #ifndef SAGE_PHASE_SPLIT
 #define SAGE_PHASE_SPLIT 1
@@ -1175,8 +1180,12 @@ template <int D, int PV, int MF, int BM>
 static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (MF)
     k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (a.mtiles)
-    k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (a.mtiles) {
+    if constexpr (D == 128 && !BM && kPhaseSplit)
+      k_attn_fwd<D, PV, MF, BM, 1, 1><<<grid, kAttnThreads, 0, s>>>(a);
+    else
+      k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
+  }
   else if constexpr (D == 128 && !BM && kPhaseSplit)
     k_attn_fwd<D, PV, MF, BM, 0, 1><<<grid, kAttnThreads, 0, s>>>(a);
   else
