@@ -19,8 +19,8 @@
 //    qmean_u . K_j - qmean_u . kmean on the bf16 MFMA from exact bf16 parts of qmean and K.
 //  * Attention: the INT8 kernel's organisation (8 waves x 32 query rows per workgroup, a
 //    four-stage LDS ring filled by direct buffer-to-LDS loads two tiles ahead, one barrier per
-//    64-key tile; in each wave the PV of tile n-1, the softmax of tile n and the QK of tile n+1
-//    are interleaved), with
+//    64-key tile; each step a softmax phase and an MFMA phase, in opposite orders in the two waves
+//    of a SIMD), with
 //    - S^T = K Q^T on the f8f6f4 MFMA with both operands e2m1 and their scales; the MFMA's C
 //      operand starts from the tile's correction values, so the accumulator holds the whole score;
 //    - operand layouts of the 32x32x64 f8f6f4 MFMA: an e4m3 operand gives lane group g (lanes
@@ -641,6 +641,84 @@ __device__ __forceinline__ float f4_step(v16f (&acc)[2], float (&ch)[4], v8i& P,
   return alpha;
 }
 
+// Phase-split form of the step (the INT8 kernel's phase-split schedule): waves 0-3 take a tile's
+// softmax and then the MFMA phase, waves 4-7 the MFMA phase and then the next tile's softmax, so
+// the two waves of a SIMD overlap one's exponentials with the other's MFMAs.
+// Softmax of the tile whose scores are in acc (SLOW: keys past lim masked): row maxima, reference
+// maximum, P = e4m3(448 * p) and the row sums.  Returns 2^(m_old - m_new), O's factor before this
+// tile's PV.
+template <bool SLOW>
+__device__ __forceinline__ float f4_softmax(v16f (&acc)[2], v8i& P, float c, F4Row& rs, int g, int lim) {
+  if constexpr (SLOW) f4_mask(acc, g, lim);
+  float ch[4];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) f4_max_piece(acc, ch, p);
+  const float alpha = f4_finish_max(ch, c, rs);
+  float psum = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = 4 * gi + e;
+      x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[idx >> 4][idx & 15], c, -rs.pm));  // -inf gives 0
+    }
+    psum += (x[0] + x[1]) + (x[2] + x[3]);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    P[gi] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);  // byte e: key f4_key(gi / 4, 4 (gi % 4) + e, g)
+  }
+  rs.l = alpha * rs.l + psum;
+  return alpha;
+}
+
+// MFMA phase: the QK of the next tile (K codes, correction values and K scales from sK / sC / sKS;
+// its first K fragment arrives in k0) into acc, then the PV of the current tile (V codes and scale
+// word from sV / sVS) from P into O.  Operands are read from LDS one MFMA ahead.
+__device__ __forceinline__ void f4_mfma(v4i k0, const char* sK, const char* sC, const char* sKS, const char* sV,
+                                        const char* sVS, const v8i (&qf)[2], int qsc, const v8i& P, v16f (&o)[4],
+                                        v16f (&acc)[2], const F4Lanes& lb) {
+  v4i kf[4], vf[4];
+  v16f cv[2];
+  int ks[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const float* cp = reinterpret_cast<const float*>(sC + lb.c) + 32 * kb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(cp + 4 * q);
+      cv[kb][4 * q] = f.x;
+      cv[kb][4 * q + 1] = f.y;
+      cv[kb][4 * q + 2] = f.z;
+      cv[kb][4 * q + 3] = f.w;
+    }
+    ks[kb] = *reinterpret_cast<const unsigned short*>(sKS + lb.ks[kb]);
+  }
+  const int vsc = *reinterpret_cast<const int*>(sVS + lb.vs);
+  kf[0] = k0;
+  auto read = [&](int r) {
+    if (r < 4) {
+      const int kb = r >> 1, cs = r & 1;
+      kf[r] = *reinterpret_cast<const v4i*>(sK + lb.k[cs] + 2048 * kb);
+    } else {
+      vf[r - 4] = *reinterpret_cast<const v4i*>(sV + lb.v[r - 4]);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k + 1 < 8) read(k + 1);
+    if (k < 4) {
+      const int kb = k >> 1, cs = k & 1;
+      if (cs == 0)
+        acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(kf[k]), qf[0], cv[kb], 4, 4, 0, ks[kb], 0, qsc);
+      else
+        acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(kf[k]), qf[1], acc[kb], 4, 4, 1, ks[kb], 1, qsc);
+    } else {
+      f4_pv(o, k - 4, vf[k - 4], P, vsc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // The workgroup's tile loads.  Waves 0-3 each fill one 1 KiB segment of a K tile (wave 3 also the
 // two correction rows with lanes 0-31, wave 2 the K scale bytes with lanes 0-15); waves 4-7 one
 // segment of a V tile (wave 7 also the V scale bytes with lanes 0-15).  A lane fetches the global
@@ -701,6 +779,8 @@ struct F4Stager {
   }
 };
 
+// PP: the phase-split schedule (f4_softmax / f4_mfma) instead of f4_step.
+template <int PP>
 __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) char smem[kF4Smem];
@@ -711,6 +791,8 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
   char* const vsring = ksring + kF4NS * kF4SB;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
+  // PP: waves 4-7 run their MFMA phase first; waves w and w + 4 share a SIMD
+  const int grp1 = __builtin_amdgcn_readfirstlane(w >= 4 ? 1 : 0);
 
   int64_t bh;
   int qt;
@@ -793,7 +875,16 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
   v4i vpre;
   int vsc;
   bool part_cur = partial(t0);
-  {  // scores of T[0] and the row maxima of its key block 0; the first PV operands (T[-1])
+  if constexpr (PP) {  // scores of T[0]; group 1 takes their softmax before its first step
+    f4_qk_tile(kring, cring, ksring, qf, qsc, lb, acc);
+    if (grp1) {
+      if (part_cur)
+        f4_softmax<true>(acc, P, c, rs, g, limit(t0));
+      else
+        f4_softmax<false>(acc, P, c, rs, g, kBlockN - 1);
+      // O is still zero: the factor returned needs no application
+    }
+  } else {  // scores of T[0] and the row maxima of its key block 0; the first PV operands (T[-1])
     f4_qk_tile(kring, cring, ksring, qf, qsc, lb, acc);
     if (part_cur) f4_mask(acc, g, limit(t0));
 #pragma unroll
@@ -842,15 +933,60 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
     ++n;
     return true;
   };
+  // Phase-split step n: both groups read K of T[n+1] and V of T[n]; group 0 takes T[n]'s softmax
+  // and then the MFMA phase, group 1 the MFMA phase and then T[n+1]'s softmax (past the last tile
+  // every score is masked: P = 0, factor 1).
+  auto pstep = [&](auto slot) -> bool {
+    constexpr int Q = decltype(slot)::value;  // n % 4
+    if (tc >= kt_end) return false;
+    __syncthreads();
+    st.load_v(clampt(tnn), vring + ((Q + 2) % kF4NS) * kF4VB, vsring + ((Q + 2) % kF4NS) * kF4SB);
+    st.load_k(clampt(tnnn), kring + ((Q + 3) % kF4NS) * kF4KB, cring + ((Q + 3) % kF4NS) * kF4CB,
+              ksring + ((Q + 3) % kF4NS) * kF4SB);
+    const char* sV = vring + Q * kF4VB;  // V of T[n]
+    const char* sVS = vsring + Q * kF4SB;
+    const int s1 = (Q + 1) % kF4NS;      // K side of T[n+1]
+    const char* sK = kring + s1 * kF4KB;
+    const v4i k0 = *reinterpret_cast<const v4i*>(sK + lb.k[0]);
+    if (grp1) f4_mfma(k0, sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf, qsc, P, o, acc, lb);
+    const int ts = grp1 ? tn : tc;
+    float alpha;
+    if (partial(ts))
+      alpha = f4_softmax<true>(acc, P, c, rs, g, limit(ts));
+    else
+      alpha = f4_softmax<false>(acc, P, c, rs, g, kBlockN - 1);
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    if (!grp1) f4_mfma(k0, sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf, qsc, P, o, acc, lb);
+    if (nl == 1)
+      wait_vmcnt<1>();
+    else
+      wait_vmcnt<2>();
+    tc = tn;
+    tn = tnn;
+    tnn = tnnn;
+    tnnn = tnnn + 1;
+    ++n;
+    return true;
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  while (step(I0{}) && step(I1{}) && step(I2{}) && step(I3{})) {
+  if constexpr (PP) {
+    while (pstep(I0{}) && pstep(I1{}) && pstep(I2{}) && pstep(I3{})) {
+    }
+  } else {
+    while (step(I0{}) && step(I1{}) && step(I2{}) && step(I3{})) {
+    }
   }
   wait_vmcnt<0>();
   __syncthreads();
-  if (n > 0) {  // PV of the last tile
+  if (!PP && n > 0) {  // PV of the last tile
     const int sl = (n - 1) % kF4NS;
     const char* sV = vring + sl * kF4VB;
     const int vs = *reinterpret_cast<const int*>(vsring + sl * kF4SB + lb.vs);
@@ -1008,8 +1144,18 @@ hipError_t launch_fp4_quant(const Fp4QuantArgs& a, double* partial, hipStream_t 
   return hipGetLastError();
 }
 
+// The attention kernel runs the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
+// interleaved f4_step schedule, e.g. to compare the two).
+#ifndef SAGE_PHASE_SPLIT
+#define SAGE_PHASE_SPLIT 1
+#endif
+constexpr bool kPhaseSplitF4 = SAGE_PHASE_SPLIT;
+
 hipError_t launch_fp4_attn(const Fp4AttnArgs& a, hipStream_t s) {
-  k_fp4_attn<<<(unsigned)(a.nQT * a.B * a.H), kF4AttnThreads, 0, s>>>(a);
+  if (kPhaseSplitF4)
+    k_fp4_attn<1><<<(unsigned)(a.nQT * a.B * a.H), kF4AttnThreads, 0, s>>>(a);
+  else
+    k_fp4_attn<0><<<(unsigned)(a.nQT * a.B * a.H), kF4AttnThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
