@@ -294,6 +294,13 @@ CASES = [
     dict(name="mask_keypad", B=2, H=2, Nq=300, Nk=417, d=128, mask="keypad"),
     dict(name="fmask_keypad_fp8_causal", B=2, H=2, Nq=260, Nk=260, d=64, pv="fp8", causal=True, mask="f_keypad"),
     dict(name="sm_scale", B=1, H=2, Nq=256, Nk=256, d=128, sm_scale=0.05),
+    # short key ranges at d = 128 (the phase-split step, whose second wave group takes the softmax
+    # of the tile after the current one: here past the last tile from the first step on)
+    dict(name="one_tile", B=1, H=2, Nq=300, Nk=40, d=128),
+    dict(name="one_key_d128_fp8", B=1, H=2, Nq=200, Nk=1, d=128, pv="fp8", sigma=8.0),
+    dict(name="two_tiles_ragged", B=1, H=2, Nq=257, Nk=65, d=128),
+    dict(name="causal_short", B=1, H=2, Nq=70, Nk=70, d=128, causal=True),
+    dict(name="fp8_causal_one_block", B=1, H=2, Nq=256, Nk=256, d=128, pv="fp8", causal=True),
     # peaked rows: most of a row's weight sits on a few keys, where e4m3 P = 448 * p reaches 448 and
     # FP16 P (under its lazy maximum) reaches 2^8 (e4m3 P and V on rows this peaked are at cosine
     # 0.9989 from exact attention in the emulation itself)
