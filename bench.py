@@ -37,6 +37,7 @@ FP16_PEAK_TOPS = 2500.0  # MI355X dense FP16 MFMA
 
 
 FP4_PEAK_TOPS = 10100.0  # MI355X dense FP4 MFMA
+SETTLE_S = 0.25  # seconds of back-to-back untimed steps before the timed region (see run_timed)
 FP8_PEAK_TOPS = 5000.0
 
 
@@ -389,27 +390,48 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
 
     stream = torch.cuda.current_stream(dev)
     scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device=dev) if args.scrub_mib > 0 else None
-    warm_ms = None  # the fastest warm-up step, for sizing the clock probe below
-    for _ in range(args.warmup):
-        tw = time.perf_counter()
-        step()
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - tw) * 1e3
-        warm_ms = dt if warm_ms is None else min(warm_ms, dt)
-    warm_ms = warm_ms or 1.0
-    # the shader clock during the timed steps: idle waves on a second stream read the clock counters
-    # over about half of the expected timed window (s_sleep trips of 8128 clocks, <= 3.4 us each)
-    side = torch.cuda.Stream(device=dev)
-    clk_buf = torch.zeros(4 * 8, dtype=torch.int64, device=dev)
-    clk_iters = max(1, min(int(0.5 * warm_ms * args.steps / 3.4e-3), 1 << 24))
 
     def pair():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
+    # Everything the timed region needs is made before the first warm-up step, so that from then on
+    # the GPU never waits on the host: an idle gap of a few tens of ms before the timed steps makes
+    # the chip's power management throttle the next launches (one measured n8k trace: 2.16 ms
+    # after a 20 ms gap, settling to 1.55 ms over about 50 ms of load).
+    side = torch.cuda.Stream(device=dev)
+    clk_buf = torch.zeros(4 * 8, dtype=torch.int64, device=dev)
     evs = [[pair() for _ in range(S)] for _ in range(args.steps)]
     mevs = [pair() for _ in range(args.steps)] if S > 1 else [None] * args.steps
     sevs = [pair() for _ in range(args.steps)] if scrub is not None else None
     g0, g1 = pair()
+    wevs = [pair() for _ in range(max(args.warmup, 1))]
+    # the clock probe's first launch loads its code (several ms with the GPU idle): done here, once
+    try:
+        _api.sclk_probe(dev, nblocks=8, iters=1, load=False, stream=side, out=clk_buf)
+    except Exception:
+        pass
+    torch.cuda.synchronize()
+    # Warm-up: the W steps back to back, then untimed steps until the loop has kept the GPU busy for
+    # SETTLE_S seconds (a synchronization every 8 steps leaves gaps of one launch latency only), so
+    # the timed steps start at the clock the chip holds under sustained load.
+    tw = time.perf_counter()
+    for i in range(args.warmup):
+        wevs[i][0].record(stream)
+        step()
+        wevs[i][1].record(stream)
+    settle = 0
+    torch.cuda.synchronize()
+    while time.perf_counter() - tw < SETTLE_S:
+        step()
+        settle += 1
+        if settle % 8 == 0:
+            torch.cuda.synchronize()
+    settle_s = time.perf_counter() - tw
+    # the fastest warm-up step, for sizing the clock probe below
+    warm_ms = min(a.elapsed_time(b) for a, b in wevs[:args.warmup]) if args.warmup > 0 else 1.0
+    # the shader clock during the timed steps: idle waves on a second stream read the clock counters
+    # over about half of the expected timed window (s_sleep trips of 8128 clocks, <= 3.4 us each)
+    clk_iters = max(1, min(int(0.5 * warm_ms * args.steps / 3.4e-3), 1 << 24))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tw0 = time.time()
@@ -457,6 +479,8 @@ def run_timed(args, w, step, S, out_esize, dev, clocks=None, accuracy=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"untimed_steps": settle, "seconds": round(settle_s, 3),
+                   "rule": f"after the W warm-up steps, untimed steps until the GPU has been busy {SETTLE_S} s"},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
