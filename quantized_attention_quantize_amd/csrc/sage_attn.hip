@@ -596,6 +596,7 @@ template <int D, int PV, bool SLOW>
 __device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, float c, RowState& rs, int g, int lim,
                                                const uint8_t* mtile, bool mvec4) {
   constexpr bool MG = PV == 0;  // FP16 P: the QK accumulators start at the biased value (see tile_step)
+  c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));  // the same in every lane: an SGPR operand
   if constexpr (SLOW) mask_scores(acc, g, lim, mtile, mvec4);
   int ch[4];
 #pragma unroll
@@ -969,16 +970,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     constexpr int Q = decltype(slot)::value;
     if (tc >= kt_end) return false;
     asm volatile("s_barrier" ::: "memory");
-    st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
-    st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
-    const float ks_n2 = ks_load(tnn);
     const char* sV = vring + Q * G::V_BYTES;                // V of T[n]
     const char* sK = kring + ((Q + 1) % kNS) * G::K_BYTES;  // K of T[n+1]
+    float ks_n2;
+    auto stage = [&] {  // this step's staging loads, then the k-scale of T[n+2]
+      st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
+      st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
+      ks_n2 = ks_load(tnn);
+    };
     v4i pre[kPhaseLA];
+    auto preload = [&] {
 #pragma unroll
-    for (int r = 0; r < kPhaseLA; ++r) pre[r] = kfrag<D>(sK, lb, r);
+      for (int r = 0; r < kPhaseLA; ++r) pre[r] = kfrag<D>(sK, lb, r);
+    };
     const float c_nxt = scale_from(tn, ks_n1);
-    if (grp1) mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+    // Group 1 reads its first operands and streams its MFMAs right after the barrier, and issues the
+    // loads after them; group 0 issues the loads first and reads its operands after its softmax, so
+    // group 1's reads are served first.
+    if (grp1) {
+      preload();
+      mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+      stage();
+    } else {
+      stage();
+    }
     const int ts = grp1 ? tn : tc;
     const float cs = grp1 ? c_nxt : c_cur;
     int lim;
@@ -990,7 +1005,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     else
       alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1, nullptr, false);
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
-    if (!grp1) mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+    if (!grp1) {
+      preload();
+      mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
+    }
     switch (nload) {
       case 0: wait_vmcnt<1>(); break;
       case 1: wait_vmcnt<2>(); break;

@@ -940,15 +940,24 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
     constexpr int Q = decltype(slot)::value;  // n % 4
     if (tc >= kt_end) return false;
     __syncthreads();
-    st.load_v(clampt(tnn), vring + ((Q + 2) % kF4NS) * kF4VB, vsring + ((Q + 2) % kF4NS) * kF4SB);
-    st.load_k(clampt(tnnn), kring + ((Q + 3) % kF4NS) * kF4KB, cring + ((Q + 3) % kF4NS) * kF4CB,
-              ksring + ((Q + 3) % kF4NS) * kF4SB);
+    auto stage = [&] {
+      st.load_v(clampt(tnn), vring + ((Q + 2) % kF4NS) * kF4VB, vsring + ((Q + 2) % kF4NS) * kF4SB);
+      st.load_k(clampt(tnnn), kring + ((Q + 3) % kF4NS) * kF4KB, cring + ((Q + 3) % kF4NS) * kF4CB,
+                ksring + ((Q + 3) % kF4NS) * kF4SB);
+    };
     const char* sV = vring + Q * kF4VB;  // V of T[n]
     const char* sVS = vsring + Q * kF4SB;
     const int s1 = (Q + 1) % kF4NS;      // K side of T[n+1]
     const char* sK = kring + s1 * kF4KB;
-    const v4i k0 = *reinterpret_cast<const v4i*>(sK + lb.k[0]);
-    if (grp1) f4_mfma(k0, sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf, qsc, P, o, acc, lb);
+    // group 1 streams its MFMAs right after the barrier and stages the loads after them; group 0
+    // stages first and reads its operands after its softmax
+    if (grp1) {
+      f4_mfma(*reinterpret_cast<const v4i*>(sK + lb.k[0]), sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf,
+              qsc, P, o, acc, lb);
+      stage();
+    } else {
+      stage();
+    }
     const int ts = grp1 ? tn : tc;
     float alpha;
     if (partial(ts))
@@ -961,7 +970,9 @@ __global__ __launch_bounds__(kF4AttnThreads) void k_fp4_attn(Fp4AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    if (!grp1) f4_mfma(k0, sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf, qsc, P, o, acc, lb);
+    if (!grp1)
+      f4_mfma(*reinterpret_cast<const v4i*>(sK + lb.k[0]), sK, cring + s1 * kF4CB, ksring + s1 * kF4SB, sV, sVS, qf,
+              qsc, P, o, acc, lb);
     if (nl == 1)
       wait_vmcnt<1>();
     else
