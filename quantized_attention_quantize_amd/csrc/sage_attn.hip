@@ -985,13 +985,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     };
     const float c_nxt = scale_from(tn, ks_n1);
     // Group 1 reads its first operands and streams its MFMAs right after the barrier, and issues the
-    // loads after them; group 0 issues the loads first and reads its operands after its softmax, so
-    // group 1's reads are served first.
+    // loads after them; group 0 starts its softmax at once and issues the loads and its operand reads
+    // after it, so group 1's reads are served first.
     if (grp1) {
       preload();
       mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
-      stage();
-    } else {
       stage();
     }
     const int ts = grp1 ? tn : tc;
@@ -1006,6 +1004,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1, nullptr, false);
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
     if (!grp1) {
+      stage();
       preload();
       mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
     }
