@@ -897,6 +897,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   int n = 0;
   int tc = t0, tn = t1, tnn = t2, tnnn = t3;  // T[n] .. T[n+3]
   float ks_n1 = scalar_ld(ksh, t1 < kt_end ? t1 : 0);  // k-scale of T[n+1]
+  // PP: the phase-split step takes T[n+1]'s scale at its start, where no LDS read is in flight, so
+  // the k-scales come by scalar loads issued three tiles ahead into a ring indexed by the step's slot
+  // (T[i]'s scale in ksr[i % 4]).  (A vector load there would be waited for by vmcnt, and the
+  // compiler's wait would also drain the staging loads.)
+  float ksr[4] = {0.f, ks_n1, PP ? scalar_ld(ksh, t2 < kt_end ? t2 : 0) : 0.f, 0.f};
   auto step = [&](auto slot) -> bool {
     constexpr int Q = decltype(slot)::value;  // n % kNS
     if (tc >= kt_end) return false;
@@ -972,18 +977,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     asm volatile("s_barrier" ::: "memory");
     const char* sV = vring + Q * G::V_BYTES;                // V of T[n]
     const char* sK = kring + ((Q + 1) % kNS) * G::K_BYTES;  // K of T[n+1]
-    float ks_n2;
-    auto stage = [&] {  // this step's staging loads, then the k-scale of T[n+2]
+    auto stage = [&] {  // this step's staging loads and the k-scale of T[n+3]
       st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
       st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
-      ks_n2 = ks_load(tnn);
+      ksr[(Q + 3) % kNS] = scalar_ld(ksh, tnnn < kt_end ? tnnn : 0);
     };
     v4i pre[kPhaseLA];
     auto preload = [&] {
 #pragma unroll
       for (int r = 0; r < kPhaseLA; ++r) pre[r] = kfrag<D>(sK, lb, r);
     };
-    const float c_nxt = scale_from(tn, ks_n1);
+    const float c_nxt = scale_from(tn, ksr[(Q + 1) % kNS]);
     // Group 1 reads its first operands and streams its MFMAs right after the barrier, and issues the
     // loads after them; group 0 starts its softmax at once and issues the loads and its operand reads
     // after it, so group 1's reads are served first.
@@ -1008,17 +1012,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       preload();
       mfma_phase<D, PV>(pre, sK, sV, P, qf, o, acc, lb, g, magic);
     }
-    switch (nload) {
-      case 0: wait_vmcnt<1>(); break;
-      case 1: wait_vmcnt<2>(); break;
-      case 2: wait_vmcnt<3>(); break;
-      case 3: wait_vmcnt<4>(); break;
-      case 4: wait_vmcnt<5>(); break;
-      case 5: wait_vmcnt<6>(); break;
-      default: wait_vmcnt<7>(); break;
-    }
+    // every wave issues the same loads per step at d = 128: a compile-time wait, so the compiler
+    // sees that the k-scale read at the next step's start has landed
+    static_assert(G::V_SEGS_ALL % kWaves == 0 && G::K_SEGS_ALL % kWaves == 0, "uniform staging");
+    wait_vmcnt<(G::V_SEGS_ALL + G::K_SEGS_ALL) / kWaves>();
     c_cur = c_nxt;
-    ks_n1 = ks_n2;
     tc = tn;
     tn = tnn;
     tnn = tnnn;
