@@ -11,7 +11,7 @@
 // Design (MI355X / CDNA4):
 //  * One workgroup = 8 waves = 256 query rows of one (b,h), two waves per SIMD; each wave owns one
 //    32-row MFMA block, and all eight read the K and V tiles the workgroup stages in LDS.  At
-//    d = 128 (no float mask, no per-block means) each step is split into a softmax phase and an
+//    d = 128 (no float mask) each step is split into a softmax phase and an
 //    MFMA phase, run in opposite orders by the two waves of a SIMD, so one wave's exponentials
 //    overlap the other's MFMA stream.  The other launches software-pipeline the key loop inside
 //    each wave instead (QK of the next tile, softmax of this tile and PV of the previous tile
@@ -588,13 +588,13 @@ __device__ __forceinline__ void scale_acc(v16f (&o)[D / 32], float alpha) {
 // MFMA then the softmax of the next tile.  So while one wave of a SIMD streams its MFMAs, the
 // other runs its softmax on the vector unit, and a wave holds one set of score registers, not two.
 
-// Softmax of one tile whose scores are in acc: masks them (SLOW; lim and the boolean mask row mtile
-// as in mask_scores), takes the row maxima, moves the
+// Softmax of one tile whose scores are in acc (BM: plus the row's per_block_mean term cb, log2
+// units): masks them (SLOW; lim and the boolean mask row mtile as in mask_scores), takes the row maxima, moves the
 // reference maximum, and writes P = exp2(s*c - pm) (fp16, or e4m3 of 448*2^-tau*p) with the row
 // sums.  Returns 2^(m_old - m_new), the factor O takes before this tile's PV.
-template <int D, int PV, bool SLOW>
+template <int D, int PV, bool SLOW, bool BM = false>
 __device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, float c, RowState& rs, int g, int lim,
-                                               const uint8_t* mtile, bool mvec4) {
+                                               const uint8_t* mtile, bool mvec4, float cb = 0.f) {
   constexpr bool MG = PV == 0;  // FP16 P: the QK accumulators start at the biased value (see tile_step)
   c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));  // the same in every lane: an SGPR operand
   if constexpr (SLOW) mask_scores(acc, g, lim, mtile, mvec4);
@@ -602,9 +602,10 @@ __device__ __forceinline__ float softmax_phase(v16i (&acc)[2], PFrag<PV>& P, flo
 #pragma unroll
   for (int p = 0; p < 8; ++p) max_piece(acc, ch, p);
   float pm_new;
-  const float alpha = finish_max<PV, SLOW, false, false, MG>(ch, c, rs, pm_new);
+  const float alpha = finish_max<PV, SLOW, false, BM, MG>(ch, c, rs, pm_new, cb);
   rs.pm = pm_new;
-  const float kk = MG ? __builtin_fmaf(-kMagic, c, -pm_new) : -pm_new;
+  const float nb = BM ? cb - pm_new : -pm_new;  // per_block_mean: the row's term of this key block
+  const float kk = MG ? __builtin_fmaf(-kMagic, c, nb) : nb;
   float psum = 0.f;
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi) {
@@ -702,18 +703,21 @@ __device__ __forceinline__ const T* kernarg_reload() {
 // tile walk is plain arithmetic: no tile is dropped and only the causal diagonal and ragged tail
 // take the per-element step.
 // PP: the phase-split schedule (softmax_phase / mfma_phase) instead of tile_step; not with a float
-// mask or per-block means.
+// mask.
 template <int D, int PV, int MF, int BM, int TT, int PP = 0>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   static_assert(TT || !MF, "a float mask comes with its tile table");
-  static_assert(!PP || (!MF && !BM), "the phase-split schedule takes no float mask or per-block means");
+  static_assert(!PP || !MF, "the phase-split schedule takes no float mask");
   using G = TileGeom<D, PV>;
   constexpr int kNS = 4;
-  __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES];
+  // PP with per_block_mean: a third ring holds each key tile's per-row score terms (4 B x 256 rows)
+  constexpr int kCB = PP && BM ? kBlockM * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[kNS * G::K_BYTES + kNS * G::V_BYTES + kNS * kCB];
   // V ring first: with at most 64 KiB of V slots every V fragment read is a lane base plus an
   // immediate ds_read offset
   char* const vring = smem;
   char* const kring = smem + kNS * G::V_BYTES;
+  char* const cbring = kring + kNS * G::K_BYTES;  // PP && BM only
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int w = tid >> 6;
   // PP: waves 4-7 run their MFMA phase first.  Waves w and w + 4 share a SIMD (waves go round-robin
@@ -784,10 +788,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const int t1 = next_tile(t0), t2 = next_tile(t1), t3 = next_tile(t2);
   const int tstand = t0 < kt_end ? t0 : 0;  // a valid tile to stand in for loads past the end
   auto clampt = [&](int t) { return t < kt_end ? t : tstand; };
+  // PP with per_block_mean: key tile t's terms of the workgroup's 256 rows (blk_corr[t][q0 ..], 4 B
+  // each) travel through their own ring slot beside its K tile.  Wave w loads the 64 rows of
+  // quarter w % 4, one dword a lane (the rows start at any 4-byte boundary): waves w and w + 4 write
+  // the same values to the same bytes, so every wave issues the same loads per step and the step's
+  // wait stays one compile-time count (a wave-dependent wait made the compiler spill).  Rows past
+  // the head's terms read 0.
+  const __amdgpu_buffer_rsrc_t cbrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(PP && BM ? a.blk_corr + bh * a.nbk * a.Nq : nullptr), (short)0, PP && BM ? (int)(a.nbk * a.Nq * 4) : 0,
+      kBufferWord3);
+  const int wq = __builtin_amdgcn_readfirstlane(w % (kWaves / 2));  // quarter of the rows
+  auto load_cb = [&](int t, int slot) {
+    if constexpr (PP && BM)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cbrs, (lds_void_t*)(cbring + slot * kCB + wq * 256), 4, (int)(lane * 4),
+                                               (int)(((int64_t)t * a.Nq + q0) * 4) + wq * 256, 0, 0);
+  };
   if (t0 < kt_end) {
     st.load_k(t0, kring);
     st.load_k(clampt(t1), kring + G::K_BYTES);
     st.load_k(clampt(t2), kring + 2 * G::K_BYTES);
+    load_cb(t0, 0);
+    load_cb(clampt(t1), 1);
+    load_cb(clampt(t2), 2);
     st.load_v(t0, vring);
     st.load_v(clampt(t1), vring + G::V_BYTES);
   }
@@ -866,6 +888,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
   const float cbs = a.sm_scale * kLog2e;
   auto cb_of = [&](int t) { return BM && t < kt_end ? cbh[(int64_t)t * a.Nq] * cbs : 0.f; };
   float cb_cur = cb_of(t0);
+  // PP with per_block_mean: this lane's row term of the key tile in ring slot `slot`, log2 units
+  auto cb_at = [&](int slot) -> float {
+    if constexpr (PP && BM)
+      return reinterpret_cast<const float*>(cbring + slot * kCB)[32 * w + lr] * cbs;
+    else
+      return 0.f;
+  };
   if constexpr (PP) {  // scores of T[0]; group 1 takes their softmax before its first step
     qk_tile<D, PV == 0>(kring, qf, lb, acc, magic);
     if (grp1) {
@@ -873,9 +902,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
       const void* mtile;
       visible(t0, lim, mtile);
       if (part_cur)
-        softmax_phase<D, PV, true>(acc, P, c_cur, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4);
+        softmax_phase<D, PV, true, BM>(acc, P, c_cur, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4,
+                                       cb_at(0));
       else
-        softmax_phase<D, PV, false>(acc, P, c_cur, rs, g, kBlockN - 1, nullptr, false);
+        softmax_phase<D, PV, false, BM>(acc, P, c_cur, rs, g, kBlockN - 1, nullptr, false, cb_at(0));
       // O is still zero: the factor returned (0) needs no application
     }
   } else {  // scores of T[0] and the row maxima of its first key block; the first PV operands
@@ -980,6 +1010,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     auto stage = [&] {  // this step's staging loads and the k-scale of T[n+3]
       st.load_v(clampt(tnn), vring + ((Q + 2) % kNS) * G::V_BYTES);
       st.load_k(clampt(tnnn), kring + ((Q + 3) % kNS) * G::K_BYTES);
+      load_cb(clampt(tnnn), (Q + 3) % kNS);
       ksr[(Q + 3) % kNS] = scalar_ld(ksh, tnnn < kt_end ? tnnn : 0);
     };
     v4i pre[kPhaseLA];
@@ -1002,10 +1033,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     const void* mtile;
     visible(ts, lim, mtile);
     float alpha;
+    const float cb = cb_at(grp1 ? (Q + 1) % kNS : Q);  // per_block_mean: T[n+1]'s or T[n]'s term
     if (partial(ts))
-      alpha = softmax_phase<D, PV, true>(acc, P, cs, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4);
+      alpha = softmax_phase<D, PV, true, BM>(acc, P, cs, rs, g, lim, static_cast<const uint8_t*>(mtile), a.mask_vec4,
+                                             cb);
     else
-      alpha = softmax_phase<D, PV, false>(acc, P, cs, rs, g, kBlockN - 1, nullptr, false);
+      alpha = softmax_phase<D, PV, false, BM>(acc, P, cs, rs, g, kBlockN - 1, nullptr, false, cb);
     if (__ballot(alpha != 1.f)) scale_acc<D>(o, alpha);
     if (!grp1) {
       stage();
@@ -1015,7 +1048,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_fwd(AttnArgs a) {
     // every wave issues the same loads per step at d = 128: a compile-time wait, so the compiler
     // sees that the k-scale read at the next step's start has landed
     static_assert(G::V_SEGS_ALL % kWaves == 0 && G::K_SEGS_ALL % kWaves == 0, "uniform staging");
-    wait_vmcnt<(G::V_SEGS_ALL + G::K_SEGS_ALL) / kWaves>();
+    constexpr int kNL = (G::V_SEGS_ALL + G::K_SEGS_ALL) / kWaves;
+    wait_vmcnt<kNL + (BM ? 1 : 0)>();  // (one load more with per_block_mean: the row terms)
     c_cur = c_nxt;
     tc = tn;
     tn = tnn;
@@ -1163,6 +1197,10 @@ template __global__ void k_attn_fwd<128, 0, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 1, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 0, 1, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 1, 0, 0, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 1, 0, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 0, 0, 1, 1, 1>(AttnArgs);
+template __global__ void k_attn_fwd<128, 1, 0, 1, 1, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<128, 0, 0, 1, 0>(AttnArgs);
@@ -1183,7 +1221,7 @@ template __global__ void k_attn_fwd<64, 1, 1, 0, 1>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 0>(AttnArgs);
 template __global__ void k_attn_fwd<64, 1, 0, 1, 1>(AttnArgs);
 
-// Launches at d = 128 without a float mask or per-block means run the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
+// Launches at d = 128 without a float mask run the phase-split schedule (build with -DSAGE_PHASE_SPLIT=0 for the
 // interleaved tile_step schedule everywhere, e.g. to compare the two).
 #ifndef SAGE_PHASE_SPLIT
 #define SAGE_PHASE_SPLIT 1
@@ -1196,12 +1234,12 @@ static void launch_attn_t(const AttnArgs& a, unsigned grid, hipStream_t s) {
   if constexpr (MF)
     k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
   else if (a.mtiles) {
-    if constexpr (D == 128 && !BM && kPhaseSplit)
+    if constexpr (D == 128 && kPhaseSplit)
       k_attn_fwd<D, PV, MF, BM, 1, 1><<<grid, kAttnThreads, 0, s>>>(a);
     else
       k_attn_fwd<D, PV, MF, BM, 1><<<grid, kAttnThreads, 0, s>>>(a);
   }
-  else if constexpr (D == 128 && !BM && kPhaseSplit)
+  else if constexpr (D == 128 && kPhaseSplit)
     k_attn_fwd<D, PV, MF, BM, 0, 1><<<grid, kAttnThreads, 0, s>>>(a);
   else
     k_attn_fwd<D, PV, MF, BM, 0><<<grid, kAttnThreads, 0, s>>>(a);
