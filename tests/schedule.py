@@ -11,8 +11,8 @@ TAU = {"fp16": 8.0, "fp8": 0.0}
 TAU_FP4 = 0
 ROWSUM_ROUNDED = False
 
-# Parity bars.  O against the emulation run with the schedule above: relative L1 <= 1e-3 (the
-# spec bar), and per row no more than ROW_TOL -- the kernel differs from the emulation only
+# Parity bars.  O against the emulation run with the schedule above: relative L1 <= 1e-3 (over
+# all compared rows), and per row no more than ROW_TOL -- the kernel differs from the emulation only
 # by fp32 rounding (v_exp_f32, MFMA summation order, fused products, and on the FP16 path the
 # fp32 rounding of each tile's exponent offset, below half an integer score unit), which can flip
 # the rounding of an fp16 or e4m3 P element now and then but cannot move a whole row.  O against the plain

@@ -23,7 +23,7 @@ from gpu_helpers import (DEV, TAU, assert_lse_close, bits, check_o, cosine, f32_
 
 pytestmark = pytest.mark.gpu
 
-QE_REL_L1 = 1e-3  # output vs quantized emulation (spec bar)
+QE_REL_L1 = 1e-3  # output vs quantized emulation: the relative-L1 parity bar
 QE_LSE = 1e-3
 EX_COS = 0.999
 EX_REL_L1 = 3e-2
