@@ -673,7 +673,7 @@ __device__ __forceinline__ float f4_softmax(v16f (&acc)[2], v8i& P, float c, F4R
 
 // MFMA phase: the QK of the next tile (K codes, correction values and K scales from sK / sC / sKS;
 // its first K fragment arrives in k0) into acc, then the PV of the current tile (V codes and scale
-// word from sV / sVS) from P into O.  Operands are read from LDS one MFMA ahead.
+// word from sV / sVS) from P into O.  Operands are read from LDS two MFMAs ahead.
 __device__ __forceinline__ void f4_mfma(v4i k0, const char* sK, const char* sC, const char* sKS, const char* sV,
                                         const char* sVS, const v8i (&qf)[2], int qsc, const v8i& P, v16f (&o)[4],
                                         v16f (&acc)[2], const F4Lanes& lb) {
@@ -705,7 +705,8 @@ __device__ __forceinline__ void f4_mfma(v4i k0, const char* sK, const char* sC, 
   };
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    if (k + 1 < 8) read(k + 1);
+    if (k == 0) read(1);  // operands two MFMAs ahead (k0 arrives read)
+    if (k + 2 < 8) read(k + 2);
     if (k < 4) {
       const int kb = k >> 1, cs = k & 1;
       if (cs == 0)
